@@ -1,0 +1,232 @@
+// C-ABI entry points of liblbca: host-side validation, then one launcher call.
+// Validation never touches the GPU, so every argument error is reported
+// (and testable) on a machine without one.
+#include <math.h>
+#include <stdint.h>
+
+#include "lbca_internal.h"
+
+namespace {
+
+bool is_dtype(int32_t d) { return d == LBCA_F32 || d == LBCA_BF16; }
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+constexpr int64_t kMaxElems = int64_t(1) << 46;  // guards products against overflow
+
+bool sane_product(std::initializer_list<int64_t> dims) {
+  int64_t p = 1;
+  for (int64_t d : dims) {
+    if (d < 0) return false;
+    if (d == 0) return true;
+    if (p > kMaxElems / d) return false;
+    p *= d;
+  }
+  return true;
+}
+
+int check_treatment(float eps, int32_t rope_dims, float rope_base, int64_t dim) {
+  if (isnan(eps) || isinf(eps)) return LBCA_ERR_INVALID_ARG;
+  if (rope_dims < 0 || rope_dims > dim) return LBCA_ERR_INVALID_ARG;
+  if (rope_dims > 0 && (rope_dims % 16 != 0)) return LBCA_ERR_UNSUPPORTED;
+  if (rope_dims > 0 && !(rope_base > 1.0f && isfinite(rope_base))) return LBCA_ERR_INVALID_ARG;
+  return LBCA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LBCA_OK : LBCA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int lbca_abi_version(void) { return LBCA_ABI_VERSION; }
+
+const char* lbca_status_string(int status) {
+  switch (status) {
+    case LBCA_OK: return "ok";
+    case LBCA_ERR_INVALID_ARG: return "invalid argument";
+    case LBCA_ERR_UNSUPPORTED: return "unsupported dtype, dimension or flag combination";
+    case LBCA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LBCA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int lbca_visible_range(int64_t t, int64_t m, int64_t W, int32_t mode, int64_t* n_pooled,
+                       int64_t* raw_begin) {
+  if (!n_pooled || !raw_begin || t < 0 || m < 1 || W < 1) return LBCA_ERR_INVALID_ARG;
+  if (mode == LBCA_EXCLUSIVE) {
+    const int64_t x = t + 1 - W;
+    *n_pooled = x > 0 ? x / m : 0;
+    *raw_begin = *n_pooled * m;
+  } else if (mode == LBCA_OVERLAP) {
+    *n_pooled = (t + 1) / m;
+    *raw_begin = t - W + 1 > 0 ? t - W + 1 : 0;
+  } else {
+    return LBCA_ERR_INVALID_ARG;
+  }
+  return LBCA_OK;
+}
+
+// ---------------------------------------------------------------------------
+int lbca_pool_blocks(const lbca_pool_args* a, void* stream) {
+  if (!a || !a->x || !a->z || !a->bias || !a->out_x) return LBCA_ERR_INVALID_ARG;
+  if ((a->v == nullptr) != (a->out_v == nullptr)) return LBCA_ERR_INVALID_ARG;
+  const bool dual = a->xb != nullptr || a->zb != nullptr || a->bias_b != nullptr;
+  if (dual && !(a->xb && a->zb && a->bias_b)) return LBCA_ERR_INVALID_ARG;
+  if (dual && a->v) return LBCA_ERR_UNSUPPORTED;
+  if (!is_dtype(a->x_dtype) || !is_dtype(a->z_dtype)) return LBCA_ERR_INVALID_ARG;
+  if (a->batch < 0 || a->heads < 1 || a->tokens < 0 || a->block < 1 || a->entries < 0)
+    return LBCA_ERR_INVALID_ARG;
+  if (!pow2(a->dim) || a->dim < 8) return a->dim > 0 ? LBCA_ERR_UNSUPPORTED : LBCA_ERR_INVALID_ARG;
+  if (a->dim > 512) return LBCA_ERR_UNSUPPORTED;
+  if (a->block_begin < 0 || a->block_end < a->block_begin || a->block_end > a->entries)
+    return LBCA_ERR_INVALID_ARG;
+  if (!sane_product({a->batch, a->heads, a->tokens, a->dim}) ||
+      !sane_product({a->batch, a->heads, a->entries, a->dim}) ||
+      !sane_product({a->heads, a->block, a->dim}) || a->block_end > kMaxElems / a->block)
+    return LBCA_ERR_INVALID_ARG;
+  const bool treat = a->rmsnorm_eps >= 0.f || a->rope_dims != 0;
+  int st = check_treatment(a->rmsnorm_eps, a->rope_dims, a->rope_base, a->dim);
+  if (st != LBCA_OK) return st;
+  if (treat && a->v) return LBCA_ERR_UNSUPPORTED;
+  if (!aligned16(a->x) || !aligned16(a->v) || !aligned16(a->z) || !aligned16(a->bias) ||
+      !aligned16(a->xb) || !aligned16(a->zb) || !aligned16(a->bias_b) || !aligned16(a->out_x) ||
+      !aligned16(a->out_v))
+    return LBCA_ERR_INVALID_ARG;
+  if (a->block_end > a->block_begin) {
+    const int64_t first_block = (dual && a->block_begin > 0) ? a->block_begin - 1 : a->block_begin;
+    const int64_t lo = first_block * a->block - a->pos_base;
+    const int64_t hi = a->block_end * a->block - a->pos_base;
+    if (lo < 0 || hi > a->tokens) return LBCA_ERR_INVALID_ARG;
+  }
+  if (a->batch == 0 || a->block_end == a->block_begin) return LBCA_OK;
+  return hip_status(lbca::launch_pool(*a, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+static int validate_decode(const lbca_decode_args* a) {
+  if (!a || !a->q || !a->pooled_k || !a->raw_k || !a->pos || !a->out) return LBCA_ERR_INVALID_ARG;
+  if ((a->pooled_v == nullptr) != (a->raw_v == nullptr)) return LBCA_ERR_INVALID_ARG;
+  if (!is_dtype(a->dtype)) return LBCA_ERR_INVALID_ARG;
+  if (a->batch < 0 || a->q_heads < 1 || a->kv_heads < 1 || a->q_heads % a->kv_heads != 0)
+    return LBCA_ERR_INVALID_ARG;
+  if (a->dim < 1 || a->entries < 0 || a->raw_rows < 1 || a->block < 1 || a->window < 1)
+    return LBCA_ERR_INVALID_ARG;
+  if (a->mode != LBCA_EXCLUSIVE && a->mode != LBCA_OVERLAP) return LBCA_ERR_INVALID_ARG;
+  if (a->sel_idx && a->k_sel < 1) return LBCA_ERR_INVALID_ARG;
+  if (!isfinite(a->scale)) return LBCA_ERR_INVALID_ARG;
+  if (!sane_product({a->batch, a->kv_heads, a->entries, a->dim}) ||
+      !sane_product({a->batch, a->kv_heads, a->raw_rows, a->dim}) ||
+      !sane_product({a->batch, a->q_heads, a->dim}) || !sane_product({a->batch, a->k_sel}))
+    return LBCA_ERR_INVALID_ARG;
+  const bool treat = a->rmsnorm_eps >= 0.f || a->rope_dims != 0;
+  int st = check_treatment(a->rmsnorm_eps, a->rope_dims, a->rope_base, a->dim);
+  if (st != LBCA_OK) return st;
+  if (treat && a->pooled_v) return LBCA_ERR_UNSUPPORTED;
+  const int64_t G = a->q_heads / a->kv_heads;
+  if (a->dtype == LBCA_BF16) {
+    if (!(a->dim == 64 || a->dim == 128 || a->dim == 256 || a->dim == 512)) return LBCA_ERR_UNSUPPORTED;
+    if (G > 64) return LBCA_ERR_UNSUPPORTED;
+    if (!(a->rope_dims == 0 || a->rope_dims == 64 || a->rope_dims == 128)) return LBCA_ERR_UNSUPPORTED;
+  } else {
+    if (a->dim % 64 != 0 || a->dim > 512) return LBCA_ERR_UNSUPPORTED;
+    if (treat) return LBCA_ERR_UNSUPPORTED;
+  }
+  if (!aligned16(a->q) || !aligned16(a->pooled_k) || !aligned16(a->pooled_v) ||
+      !aligned16(a->raw_k) || !aligned16(a->raw_v) || !aligned16(a->out))
+    return LBCA_ERR_INVALID_ARG;
+  return LBCA_OK;
+}
+
+int lbca_attend_decode_workspace(const lbca_decode_args* a, size_t* bytes) {
+  if (!bytes) return LBCA_ERR_INVALID_ARG;
+  int st = validate_decode(a);
+  if (st != LBCA_OK) return st;
+  *bytes = lbca::plan_decode(*a).ws_bytes;
+  return LBCA_OK;
+}
+
+int lbca_attend_decode(const lbca_decode_args* a, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  int st = validate_decode(a);
+  if (st != LBCA_OK) return st;
+  const lbca::DecodePlan plan = lbca::plan_decode(*a);
+  if (plan.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.ws_bytes || !aligned16(workspace)))
+    return LBCA_ERR_WORKSPACE;
+  if (a->batch == 0) return LBCA_OK;
+  return hip_status(lbca::launch_decode(*a, plan, workspace, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+int lbca_attend_prefill(const lbca_prefill_args* a, void* stream) {
+  if (!a || !a->q || !a->pooled_k || !a->raw_k || !a->out) return LBCA_ERR_INVALID_ARG;
+  if ((a->pooled_v == nullptr) != (a->raw_v == nullptr)) return LBCA_ERR_INVALID_ARG;
+  if (!is_dtype(a->dtype) || !is_dtype(a->out_dtype)) return LBCA_ERR_INVALID_ARG;
+  if (a->batch < 0 || a->q_len < 0 || a->q_heads < 1 || a->kv_heads < 1 ||
+      a->q_heads % a->kv_heads != 0)
+    return LBCA_ERR_INVALID_ARG;
+  if (a->dim < 1 || a->entries < 0 || a->raw_rows < 1 || a->block < 1 || a->window < 1 ||
+      a->q_pos0 < 0)
+    return LBCA_ERR_INVALID_ARG;
+  if (a->mode != LBCA_EXCLUSIVE && a->mode != LBCA_OVERLAP) return LBCA_ERR_INVALID_ARG;
+  if (!isfinite(a->scale)) return LBCA_ERR_INVALID_ARG;
+  if (!sane_product({a->batch, a->q_len, a->q_heads, a->dim}) ||
+      !sane_product({a->batch, a->kv_heads, a->entries, a->dim}) ||
+      !sane_product({a->batch, a->kv_heads, a->raw_rows, a->dim}) || a->q_pos0 > kMaxElems)
+    return LBCA_ERR_INVALID_ARG;
+  if (a->dtype == LBCA_BF16) {
+    if (!(a->dim == 64 || a->dim == 128)) return LBCA_ERR_UNSUPPORTED;
+  } else {
+    if (a->dim % 64 != 0 || a->dim > 512) return LBCA_ERR_UNSUPPORTED;
+  }
+  if (!aligned16(a->q) || !aligned16(a->pooled_k) || !aligned16(a->pooled_v) ||
+      !aligned16(a->raw_k) || !aligned16(a->raw_v) || !aligned16(a->out))
+    return LBCA_ERR_INVALID_ARG;
+  if (a->q_len > 0) {
+    // n_pooled(t) and raw_begin(t) never decrease with t: the extreme queries bound all.
+    int64_t np_last, rb_first, np0, rb_last;
+    lbca_visible_range(a->q_pos0 + a->q_len - 1, a->block, a->window, a->mode, &np_last, &rb_last);
+    lbca_visible_range(a->q_pos0, a->block, a->window, a->mode, &np0, &rb_first);
+    if (np_last > a->entries) return LBCA_ERR_INVALID_ARG;
+    if (rb_first - a->raw_pos_base < 0) return LBCA_ERR_INVALID_ARG;
+    if (a->q_pos0 + a->q_len - 1 - a->raw_pos_base >= a->raw_rows) return LBCA_ERR_INVALID_ARG;
+  }
+  if (a->batch == 0 || a->q_len == 0) return LBCA_OK;
+  return hip_status(lbca::launch_prefill(*a, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+static int validate_index(const csa_index_args* a) {
+  if (!a || !a->q_idx || !a->head_w || !a->keys || !a->pos || !a->out_idx) return LBCA_ERR_INVALID_ARG;
+  if (!is_dtype(a->dtype)) return LBCA_ERR_INVALID_ARG;
+  if (a->dtype != LBCA_BF16) return LBCA_ERR_UNSUPPORTED;
+  if (a->batch < 0 || a->heads < 1 || a->entries < 0 || a->block < 1 || a->k < 1)
+    return LBCA_ERR_INVALID_ARG;
+  if (!(a->dim == 32 || a->dim == 64 || a->dim == 128)) return a->dim > 0 ? LBCA_ERR_UNSUPPORTED : LBCA_ERR_INVALID_ARG;
+  if (a->heads > 16 || a->k > 2048 || a->entries > 65536) return LBCA_ERR_UNSUPPORTED;
+  if (!sane_product({a->batch, a->entries, a->dim})) return LBCA_ERR_INVALID_ARG;
+  if (!aligned16(a->q_idx) || !aligned16(a->keys) || !aligned16(a->head_w) ||
+      !aligned16(a->out_idx) || !aligned16(a->out_score))
+    return LBCA_ERR_INVALID_ARG;
+  return LBCA_OK;
+}
+
+int csa_index_topk_workspace(const csa_index_args* a, size_t* bytes) {
+  if (!bytes) return LBCA_ERR_INVALID_ARG;
+  int st = validate_index(a);
+  if (st != LBCA_OK) return st;
+  *bytes = lbca::index_workspace_bytes(*a);
+  return LBCA_OK;
+}
+
+int csa_index_topk(const csa_index_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = validate_index(a);
+  if (st != LBCA_OK) return st;
+  const size_t need = lbca::index_workspace_bytes(*a);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return LBCA_ERR_WORKSPACE;
+  if (a->batch == 0) return LBCA_OK;
+  return hip_status(lbca::launch_index_topk(*a, workspace, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// Device helpers shared by the liblbca kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lbca {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct bf16_t {  // storage tag for bfloat16 bit patterns
+  uint16_t bits;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = (__bf16)a, y = (__bf16)b;  // v_cvt_pk_bf16_f32, round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// 8 consecutive elements <-> 8 floats
+__device__ __forceinline__ void load8(const float* p, float* f) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  float4 b = *reinterpret_cast<const float4*>(p + 4);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+__device__ __forceinline__ void load8(const bf16_t* p, float* f) {
+  uint4 u = *reinterpret_cast<const uint4*>(p);
+  f[0] = lo_bf16(u.x); f[1] = hi_bf16(u.x); f[2] = lo_bf16(u.y); f[3] = hi_bf16(u.y);
+  f[4] = lo_bf16(u.z); f[5] = hi_bf16(u.z); f[6] = lo_bf16(u.w); f[7] = hi_bf16(u.w);
+}
+__device__ __forceinline__ void store8(float* p, const float* f) {
+  *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+}
+__device__ __forceinline__ void store8(bf16_t* p, const float* f) {
+  uint4 u;
+  u.x = pack_bf16x2(f[0], f[1]); u.y = pack_bf16x2(f[2], f[3]);
+  u.z = pack_bf16x2(f[4], f[5]); u.w = pack_bf16x2(f[6], f[7]);
+  *reinterpret_cast<uint4*>(p) = u;
+}
+
+// Rotation angle pos * base^(-2k/r), reduced to [-pi, pi] in double precision so
+// that positions up to 2^40 keep fp32-accurate sines; returns cos and sin.
+__device__ __forceinline__ void rope_cos_sin(double pos, int k, int r, double log2_base, float* c,
+                                             float* s) {
+  const double two_pi = 6.283185307179586476925286766559;
+  double theta = exp2(-(2.0 * (double)k / (double)r) * log2_base);
+  double a = pos * theta;
+  a -= rint(a * (1.0 / two_pi)) * two_pi;
+  float af = (float)a;
+  *c = cosf(af);
+  *s = sinf(af);
+}
+
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+template <int WIDTH>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Visibility rule on the device (same definition as lbca_visible_range).
+__device__ __forceinline__ void visible_range(int64_t t, int64_t m, int64_t W, int mode,
+                                              int64_t* n_pooled, int64_t* raw_begin) {
+  if (mode == 0) {
+    int64_t x = t + 1 - W;
+    *n_pooled = x > 0 ? x / m : 0;
+    *raw_begin = *n_pooled * m;
+  } else {
+    *n_pooled = (t + 1) / m;
+    int64_t rb = t - W + 1;
+    *raw_begin = rb > 0 ? rb : 0;
+  }
+}
+
+}  // namespace lbca

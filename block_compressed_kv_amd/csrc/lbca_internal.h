@@ -1,0 +1,29 @@
+// Internal launcher declarations of liblbca (host side).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "lbca.h"
+
+namespace lbca {
+
+// Host validation has already run when these are called; they only pick the
+// kernel instance and launch it on `stream`.
+hipError_t launch_pool(const lbca_pool_args& a, hipStream_t stream);
+
+struct DecodePlan {
+  int tile_rows;     // rows per wave tile
+  int head_groups;   // ceil(G / 16) for the MFMA path, G for the fp32 path
+  int splits;        // workgroups along the row range of one (sequence, KV head, head group)
+  size_t ws_bytes;   // partial (acc, max, sum) bytes
+};
+DecodePlan plan_decode(const lbca_decode_args& a);
+hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void* ws,
+                         hipStream_t stream);
+
+hipError_t launch_prefill(const lbca_prefill_args& a, hipStream_t stream);
+hipError_t launch_prefill_f32(const lbca_prefill_args& a, hipStream_t stream);
+
+size_t index_workspace_bytes(const csa_index_args& a);
+hipError_t launch_index_topk(const csa_index_args& a, void* ws, hipStream_t stream);
+
+}  // namespace lbca

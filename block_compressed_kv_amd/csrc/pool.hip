@@ -1,0 +1,226 @@
+// Block pooling kernels (single series, shared series, dual overlapped series).
+//
+// Method: "mSeek: learned KV-cache compression in a 3B model", section "How LBCA
+// works" (steps 2-3); "HCA: Heavily Compressed Attention (toy implementation)",
+// "What is implemented" (single-series pooling with a learnable positional
+// bias); "CSA: Compressed Sparse Attention (toy implementation)", "What is
+// implemented" (dual overlapped pooling, one joint softmax per channel).
+//
+// Design: pooling reads every token-channel once (8 B/element for bf16 K+V
+// with fp32 logits) and writes 1/m of that, so it is HBM-bound.  A group of
+// L = dim/8 lanes owns one output row; each lane owns 8 consecutive channels,
+// so every load is a 16-byte vector and a group's loads cover whole 128-byte
+// lines.  The softmax over the block is an online softmax in registers,
+// advanced four tokens at a time (one rescale exp per four data exps).  The
+// optional HCA/CSA entry treatment (RMSNorm, partial RoPE at the block start)
+// runs in the epilogue on the finished fp32 row, before the single rounding to
+// the storage type.
+#include "device_util.h"
+#include "lbca_internal.h"
+
+namespace lbca {
+
+struct PoolParams {
+  const void* x;
+  const void* v;
+  const void* z;
+  const float* bias;
+  const void* xb;
+  const void* zb;
+  const float* bias_b;
+  void* out_x;
+  void* out_v;
+  int64_t heads, tokens, dim, m, entries, block_begin, n_blocks, pos_base, total_rows;
+  int lanes_per_row;  // L = dim / 8, a power of two <= 64
+  int log2_lanes;
+  float eps;          // < 0: no RMSNorm
+  int rope_dims;      // 0: no RoPE
+  double log2_base;
+};
+
+template <typename TX, typename TZ, bool HAS_V>
+struct PoolAcc {
+  float mx[8], l[8], ax[8], av[8];
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) { mx[c] = kNegInf; l[c] = 0.f; ax[c] = 0.f; av[c] = 0.f; }
+  }
+
+  // Fold NT tokens (rows r0..r0+NT-1 of the series, bias rows b0..) into the state.
+  template <int NT>
+  __device__ __forceinline__ void fold(const TX* xs, const TX* vs, const TZ* zs, const float* bs,
+                                       int64_t dim) {
+    float a[NT][8];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      float zz[8], bb[8];
+      load8(zs + i * dim, zz);
+      load8(bs + i * dim, bb);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) a[i][c] = (zz[c] + bb[c]) * kLog2e;
+    }
+    float xv[NT][8], vv[NT][8];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      load8(xs + i * dim, xv[i]);
+      if (HAS_V) load8(vs + i * dim, vv[i]);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float g = a[0][c];
+#pragma unroll
+      for (int i = 1; i < NT; ++i) g = fmaxf(g, a[i][c]);
+      const float nm = fmaxf(mx[c], g);
+      const float corr = exp2f(mx[c] - nm);
+      float sl = 0.f, sx = 0.f, sv = 0.f;
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        const float p = exp2f(a[i][c] - nm);
+        sl += p;
+        sx = fmaf(p, xv[i][c], sx);
+        if (HAS_V) sv = fmaf(p, vv[i][c], sv);
+      }
+      l[c] = fmaf(l[c], corr, sl);
+      ax[c] = fmaf(ax[c], corr, sx);
+      if (HAS_V) av[c] = fmaf(av[c], corr, sv);
+      mx[c] = nm;
+    }
+  }
+
+  // Fold a run of `count` consecutive tokens.
+  __device__ __forceinline__ void run(const TX* xs, const TX* vs, const TZ* zs, const float* bs,
+                                      int64_t count, int64_t dim) {
+    int64_t i = 0;
+    for (; i + 4 <= count; i += 4)
+      fold<4>(xs + i * dim, HAS_V ? vs + i * dim : nullptr, zs + i * dim, bs + i * dim, dim);
+    for (; i < count; ++i)
+      fold<1>(xs + i * dim, HAS_V ? vs + i * dim : nullptr, zs + i * dim, bs + i * dim, dim);
+  }
+};
+
+template <typename TX, typename TZ, bool DUAL, bool HAS_V, bool TREAT>
+__global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int L = p.lanes_per_row;
+  const int gi = lane >> p.log2_lanes;  // row group inside the wave
+  const int li = lane & (L - 1);        // lane inside the group
+  const int groups = 64 >> p.log2_lanes;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + wave) * groups + gi;
+  const bool active = row < p.total_rows;
+  const int64_t rr = active ? row : 0;
+
+  const int64_t j = p.block_begin + rr % p.n_blocks;  // entry index
+  const int64_t bh = rr / p.n_blocks;                // sequence * heads + head
+  const int64_t h = bh % p.heads;
+  const int64_t dim = p.dim;
+  const int64_t c0 = (int64_t)li * 8;
+  const int64_t series = bh * p.tokens * dim + c0;
+  const float* bias_h = p.bias + h * p.m * dim + c0;
+
+  PoolAcc<TX, TZ, HAS_V> acc;
+  acc.init();
+  if (active) {
+    const int64_t r0 = j * p.m - p.pos_base;  // token row of the entry's own block
+    acc.run(static_cast<const TX*>(p.x) + series + r0 * dim,
+            HAS_V ? static_cast<const TX*>(p.v) + series + r0 * dim : nullptr,
+            static_cast<const TZ*>(p.z) + series + r0 * dim, bias_h, p.m, dim);
+    if (DUAL && j > 0) {
+      const int64_t rb = r0 - p.m;  // preceding block, b-series
+      acc.run(static_cast<const TX*>(p.xb) + series + rb * dim, nullptr,
+              static_cast<const TZ*>(p.zb) + series + rb * dim, p.bias_b + h * p.m * dim + c0,
+              p.m, dim);
+    }
+  }
+
+  float ox[8], ov[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float inv = active ? 1.f / acc.l[c] : 0.f;
+    ox[c] = acc.ax[c] * inv;
+    ov[c] = acc.av[c] * inv;
+  }
+
+  if (TREAT) {
+    if (p.eps >= 0.f) {
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) ss = fmaf(ox[c], ox[c], ss);
+      for (int o = L >> 1; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+      const float inv = 1.f / sqrtf(ss / (float)dim + p.eps);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) ox[c] *= inv;
+    }
+    if (p.rope_dims > 0) {
+      const int r = p.rope_dims, half = r >> 1;
+      const int64_t first = dim - r;
+      const bool lo_half = c0 >= first && c0 < first + half;
+      const bool hi_half = c0 >= first + half;
+      const int src = lo_half ? lane + (half >> 3) : (hi_half ? lane - (half >> 3) : lane);
+      float part[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) part[c] = __shfl(ox[c], src, 64);
+      if (lo_half || hi_half) {
+        const double pos = (double)(j * p.m);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int k = (int)(c0 + c - first) - (hi_half ? half : 0);
+          float cs, sn;
+          rope_cos_sin(pos, k, r, p.log2_base, &cs, &sn);
+          ox[c] = lo_half ? ox[c] * cs - part[c] * sn : ox[c] * cs + part[c] * sn;
+        }
+      }
+    }
+  }
+
+  if (active) {
+    const int64_t o = (bh * p.entries + j) * dim + c0;
+    store8(static_cast<TX*>(p.out_x) + o, ox);
+    if (HAS_V) store8(static_cast<TX*>(p.out_v) + o, ov);
+  }
+}
+
+template <typename TX, typename TZ>
+static hipError_t launch_typed(const PoolParams& p, bool dual, bool has_v, bool treat, dim3 grid,
+                               hipStream_t s) {
+  if (dual) {
+    if (treat) pool_kernel<TX, TZ, true, false, true><<<grid, 256, 0, s>>>(p);
+    else pool_kernel<TX, TZ, true, false, false><<<grid, 256, 0, s>>>(p);
+  } else if (has_v) {
+    pool_kernel<TX, TZ, false, true, false><<<grid, 256, 0, s>>>(p);
+  } else {
+    if (treat) pool_kernel<TX, TZ, false, false, true><<<grid, 256, 0, s>>>(p);
+    else pool_kernel<TX, TZ, false, false, false><<<grid, 256, 0, s>>>(p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pool(const lbca_pool_args& a, hipStream_t stream) {
+  PoolParams p;
+  p.x = a.x; p.v = a.v; p.z = a.z; p.bias = a.bias;
+  p.xb = a.xb; p.zb = a.zb; p.bias_b = a.bias_b;
+  p.out_x = a.out_x; p.out_v = a.out_v;
+  p.heads = a.heads; p.tokens = a.tokens; p.dim = a.dim; p.m = a.block; p.entries = a.entries;
+  p.block_begin = a.block_begin; p.n_blocks = a.block_end - a.block_begin;
+  p.pos_base = a.pos_base;
+  p.total_rows = a.batch * a.heads * p.n_blocks;
+  p.lanes_per_row = (int)(a.dim / 8);
+  p.log2_lanes = __builtin_ctz((unsigned)p.lanes_per_row);
+  p.eps = a.rmsnorm_eps;
+  p.rope_dims = a.rope_dims;
+  p.log2_base = a.rope_dims > 0 ? log2((double)a.rope_base) : 0.0;
+  if (p.total_rows == 0) return hipSuccess;
+  const int64_t rows_per_block = 4 * (64 / p.lanes_per_row);
+  dim3 grid((unsigned)((p.total_rows + rows_per_block - 1) / rows_per_block));
+  const bool dual = a.xb != nullptr, has_v = a.v != nullptr;
+  const bool treat = a.rmsnorm_eps >= 0.f || a.rope_dims > 0;
+  if (a.x_dtype == LBCA_BF16) {
+    if (a.z_dtype == LBCA_BF16) return launch_typed<bf16_t, bf16_t>(p, dual, has_v, treat, grid, stream);
+    return launch_typed<bf16_t, float>(p, dual, has_v, treat, grid, stream);
+  }
+  if (a.z_dtype == LBCA_BF16) return launch_typed<float, bf16_t>(p, dual, has_v, treat, grid, stream);
+  return launch_typed<float, float>(p, dual, has_v, treat, grid, stream);
+}
+
+}  // namespace lbca

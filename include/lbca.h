@@ -1,0 +1,276 @@
+/*
+ * liblbca: learned block-compressed attention on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only.  Device pointers are HIP device
+ * memory owned by the caller; the library allocates nothing, keeps no state
+ * between calls, never frees a caller buffer, and only enqueues work on the
+ * stream the caller passes (a hipStream_t, 0 = the null stream).  Every call is
+ * asynchronous with respect to the host unless stated otherwise.
+ *
+ * Errors: every entry point returns an int status.  Argument validation runs on
+ * the host BEFORE any device work is enqueued; an argument error returns
+ * LBCA_ERR_INVALID_ARG / LBCA_ERR_UNSUPPORTED / LBCA_ERR_WORKSPACE and leaves
+ * every output untouched.  LBCA_ERR_HIP means a HIP launch reported an error
+ * (outputs unspecified).  Nothing aborts or throws across the ABI.  Values the
+ * host cannot see (positions held in device memory) are checked by the
+ * kernels: a sequence whose position does not fit the buffers it was given
+ * gets NaN outputs instead of out-of-bounds accesses.
+ *
+ * Layout conventions: every tensor is dense row-major with the shape given
+ * (last dimension contiguous), element type given by a dtype field
+ * (LBCA_F32 = IEEE float32, LBCA_BF16 = bfloat16 bit patterns).  Device
+ * pointers to bf16/f32 data must be 16-byte aligned.  Positions are 0-based
+ * token indices (int64).
+ *
+ * Method (pages cited by title and section):
+ *  - "mSeek: learned KV-cache compression in a 3B model" (mSeek), section
+ *    "How LBCA works": each completed block of m old tokens is replaced by one
+ *    learned entry (per-channel softmax of content logits over the block,
+ *    weighted sum of its keys and values); a query attends over every visible
+ *    summary plus the exact raw local window; incomplete blocks stay raw.
+ *  - "HCA: Heavily Compressed Attention (toy implementation)" (HCA), section
+ *    "What is implemented": single-series pooling with a learnable positional
+ *    bias; dense attention over all causally visible compressed entries plus a
+ *    sliding-window branch; shared-KV MQA; RMSNorm; partial RoPE; sink.
+ *  - "CSA: Compressed Sparse Attention (toy implementation)" (CSA), section
+ *    "What is implemented": dual overlapped pooling; lightning indexer with
+ *    ReLU scores and learned head weights; top-k over causally visible entries;
+ *    shared-KV MQA core attention with the same treatment and a -t rotation
+ *    of the rotated output dims.
+ */
+#ifndef LBCA_H
+#define LBCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LBCA_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define LBCA_API __attribute__((visibility("default")))
+#else
+#define LBCA_API
+#endif
+
+/* status codes */
+#define LBCA_OK 0
+#define LBCA_ERR_INVALID_ARG (-1)  /* null required pointer, bad size, shape mismatch */
+#define LBCA_ERR_UNSUPPORTED (-2)  /* valid but not implemented (dtype, dim, flag mix) */
+#define LBCA_ERR_WORKSPACE (-3)    /* workspace missing or too small */
+#define LBCA_ERR_HIP (-4)          /* a HIP runtime call failed */
+
+/* element types */
+#define LBCA_F32 0
+#define LBCA_BF16 1
+
+/* visibility rules */
+#define LBCA_EXCLUSIVE 0 /* mSeek LBCA: a block is pooled once complete AND wholly
+                            older than the W-token window; raw span = first
+                            unpooled token .. t (W .. W+m-1 tokens). */
+#define LBCA_OVERLAP 1   /* HCA/CSA: every complete block is visible; the raw
+                            window is the last W tokens [max(0,t-W+1), t]. */
+
+LBCA_API int lbca_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+LBCA_API const char* lbca_status_string(int status);
+
+/*
+ * Host-only visibility rule for a query at position t (mSeek "How LBCA works",
+ * steps 4-5; HCA/CSA "What is implemented").  Writes the number of visible
+ * pooled entries (entries 0 .. n_pooled-1) and the first raw position; the raw
+ * span is [raw_begin, t].
+ *   EXCLUSIVE: n_pooled = floor(max(0, t+1-W) / m), raw_begin = n_pooled*m
+ *   OVERLAP:   n_pooled = floor((t+1) / m),         raw_begin = max(0, t-W+1)
+ * Errors: INVALID_ARG if t < 0, m < 1, W < 1, bad mode or a NULL output.
+ * The kernels apply the same rule on the device.
+ */
+LBCA_API int lbca_visible_range(int64_t t, int64_t m, int64_t W, int32_t mode,
+                       int64_t* n_pooled, int64_t* raw_begin);
+
+/* ------------------------------------------------------------------------ */
+/* Block pooling (mSeek "How LBCA works" steps 2-3; HCA "What is implemented"
+ * item 1; CSA "What is implemented" item 1).
+ *
+ * Single-series mode (xb == NULL): entry j pools tokens [j*m, (j+1)*m):
+ *   w[s,c]   = softmax over s in block j of (z[s,c] + bias[h, s-j*m, c])
+ *   out_x[j,c] = sum_s w[s,c] * x[s,c];  out_v[j,c] = sum_s w[s,c] * v[s,c]
+ * With v == NULL only out_x is written (HCA shared K=V series).
+ * Dual mode (xb != NULL, CSA): entry i takes ONE softmax per channel over the
+ * logits z[s]+bias[s-i*m] of block i and zb[s]+bias_b[s-(i-1)*m] of block i-1
+ * (block i alone for i = 0), and sums the matching rows of x and xb.
+ *
+ * Optional entry treatment (shared series only, v == NULL): with
+ * rmsnorm_eps >= 0 each pooled row is RMS-normalised (unit weight); with
+ * rope_dims > 0 its last rope_dims dims are then rotated at the entry's block
+ * start position j*m (rotate-half pairs (k, k+r/2), angle pos*base^(-2k/r),
+ * angles reduced in double precision).  This is the per-entry part of the
+ * HCA/CSA core-attention treatment, applied once when the entry is written;
+ * lbca_attend_decode reads stored entries as-is.
+ *
+ *   x, v, z, xb, zb   [batch, heads, tokens, dim]; row r holds position pos_base+r
+ *   bias, bias_b      [heads, block, dim] float32
+ *   out_x, out_v      [batch, heads, entries, dim]; entry j is row j
+ *   blocks [block_begin, block_end) are pooled; every other out row is left as is.
+ * Dtypes: x/v/xb/out in x_dtype, z/zb in z_dtype (each F32 or BF16); math in fp32.
+ * Constraints: dim a power of two in [8, 512]; rope_dims % 16 == 0, <= dim.
+ * Errors: INVALID_ARG if a token row needed is outside [0, tokens) or
+ * block_end > entries; UNSUPPORTED for treatment with v != NULL.
+ */
+typedef struct lbca_pool_args {
+  const void* x;
+  const void* v;
+  const void* z;
+  const float* bias;
+  const void* xb;
+  const void* zb;
+  const float* bias_b;
+  void* out_x;
+  void* out_v;
+  int64_t batch, heads, tokens, dim, block, entries;
+  int64_t block_begin, block_end;
+  int64_t pos_base;
+  int32_t x_dtype, z_dtype;
+  float rmsnorm_eps; /* < 0: off */
+  int32_t rope_dims; /* 0: off */
+  float rope_base;
+} lbca_pool_args;
+
+LBCA_API int lbca_pool_blocks(const lbca_pool_args* a, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention: one query per sequence (mSeek "How LBCA works" step 4;
+ * HCA "What is implemented" item 2; CSA "What is implemented" item 3).
+ *
+ * For query head h (KV head h / G, G = q_heads / kv_heads) of sequence b at
+ * position t = pos[b], the visible rows are the pooled entries j < n_pooled(t)
+ * (or, with sel_idx, the listed entries that are visible; -1 and invisible
+ * ids are skipped) followed by the raw span [raw_begin(t), t], read from the
+ * raw buffer row (position - raw_pos_base[b]).  One softmax over
+ *   logit = scale * q . k_row
+ * for all of them, plus exp(sink[h]) in the denominator when sink != NULL.
+ *   out[b,h,:] = sum softmax * v_row;  lse[b,h] = log(sum exp(logit) [+ exp(sink)])
+ * Shared series (pooled_v == raw_v == NULL): the row is both key and value.
+ * Treatment (shared series only): rmsnorm_eps >= 0 normalises q and every RAW
+ * row; rope_dims > 0 rotates q at t and every raw row at its position, and
+ * rotates the output's last rope_dims dims by -t.  Pooled entries are used as
+ * stored (write them with the same treatment through lbca_pool_blocks).
+ *
+ *   q            [batch, q_heads, dim]               dtype
+ *   pooled_k/v   [batch, kv_heads, entries, dim]     dtype
+ *   raw_k/v      [batch, kv_heads, raw_rows, dim]    dtype
+ *   pos          [batch] int64 (device)
+ *   raw_pos_base [batch] int64 (device) or NULL = 0
+ *   sel_idx      [batch, k_sel] int32 (device) or NULL
+ *   sink         [q_heads] float32 (device) or NULL
+ *   out          [batch, q_heads, dim] float32;  lse [batch, q_heads] float32 or NULL
+ * Supported: dtype BF16 with dim in {64,128,256,512}, G <= 64 and rope_dims in
+ * {0, 64, 128} (MFMA path); dtype F32 with dim % 64 == 0, dim <= 512 and no
+ * treatment.
+ * A sequence whose visible rows do not fit (n_pooled > entries, raw span
+ * outside the raw buffer, t < 0) gets NaN in out and lse.
+ * Workspace: lbca_attend_decode_workspace reports the bytes (split partials);
+ * pass at least that many bytes of device memory (16-byte aligned); contents
+ * on entry do not matter.  Calls sharing one workspace must not overlap.
+ */
+typedef struct lbca_decode_args {
+  const void* q;
+  const void* pooled_k;
+  const void* pooled_v;
+  const void* raw_k;
+  const void* raw_v;
+  const int64_t* pos;
+  const int64_t* raw_pos_base;
+  const int32_t* sel_idx;
+  const float* sink;
+  float* out;
+  float* lse;
+  int64_t batch, q_heads, kv_heads, dim, entries, raw_rows, k_sel;
+  int64_t block, window;
+  int32_t mode, dtype;
+  float scale;
+  float rmsnorm_eps; /* < 0: off */
+  int32_t rope_dims; /* 0: off */
+  float rope_base;
+} lbca_decode_args;
+
+LBCA_API int lbca_attend_decode_workspace(const lbca_decode_args* a, size_t* bytes);
+LBCA_API int lbca_attend_decode(const lbca_decode_args* a, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Prefill attention over a chunk of q_len consecutive queries (mSeek "How LBCA
+ * works" steps 4-5 and its chunked bounded-memory path): query i of the chunk
+ * sits at position t = q_pos0 + i and sees exactly what lbca_attend_decode
+ * would show it at t (per-query visibility), so chunked prefill equals
+ * one-shot prefill.  A chunked caller pools the blocks the chunk's last query
+ * may see before calling this.
+ *
+ *   q            [batch, q_len, q_heads, dim]            dtype
+ *   pooled_k/v   [batch, kv_heads, entries, dim]         dtype (v NULL: shared)
+ *   raw_k/v      [batch, kv_heads, raw_rows, dim]        row r = position raw_pos_base + r
+ *   sink         [q_heads] float32 or NULL
+ *   out          [batch, q_len, q_heads, dim]            out_dtype (F32 or BF16)
+ *   lse          [batch, q_len, q_heads] float32 or NULL
+ * Supported: BF16 with dim in {64,128} (MFMA path); F32 with dim % 64 == 0,
+ * dim <= 512.  Errors: INVALID_ARG if some query's pooled entries exceed
+ * `entries` or its raw span leaves the raw buffer (checked on the host).
+ */
+typedef struct lbca_prefill_args {
+  const void* q;
+  const void* pooled_k;
+  const void* pooled_v;
+  const void* raw_k;
+  const void* raw_v;
+  const float* sink;
+  void* out;
+  float* lse;
+  int64_t batch, q_len, q_heads, kv_heads, dim, entries, raw_rows;
+  int64_t q_pos0, raw_pos_base, block, window;
+  int32_t mode, dtype, out_dtype;
+  float scale;
+} lbca_prefill_args;
+
+LBCA_API int lbca_attend_prefill(const lbca_prefill_args* a, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* CSA lightning indexer + top-k (CSA "What is implemented" item 2).
+ * For sequence b at position t = pos[b], the visible compressed keys are
+ * j < n_vis = min(floor((t+1)/block), entries) (OVERLAP rule).  Score
+ *   I_j = sum_h head_w[b,h] * relu(q_idx[b,h,:] . keys[b,j,:])   (fp32)
+ * and select the k largest; ties go to the lower index; if n_vis < k all
+ * visible ids are selected and the rest of the row is -1.  out_idx holds the
+ * chosen ids in ascending order; out_score (optional) their scores (NaN where
+ * padded).  -0.0 and +0.0 compare equal; scores must not be NaN.
+ *
+ *   q_idx [batch, heads, dim] dtype;  head_w [batch, heads] float32
+ *   keys  [batch, entries, dim] dtype;  pos [batch] int64 (device)
+ *   out_idx [batch, k] int32;  out_score [batch, k] float32 or NULL
+ * Supported: dtype BF16; dim in {32, 64, 128}; heads <= 16;
+ * 1 <= k <= 2048; entries <= 65536.  Workspace: csa_index_topk_workspace.
+ * Sequences with t < 0 get an all -1 row.
+ */
+typedef struct csa_index_args {
+  const void* q_idx;
+  const float* head_w;
+  const void* keys;
+  const int64_t* pos;
+  int32_t* out_idx;
+  float* out_score;
+  int64_t batch, heads, dim, entries, k, block;
+  int32_t dtype;
+} csa_index_args;
+
+LBCA_API int csa_index_topk_workspace(const csa_index_args* a, size_t* bytes);
+LBCA_API int csa_index_topk(const csa_index_args* a, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LBCA_H */

@@ -1,0 +1,206 @@
+"""C-ABI boundary tests that need no GPU.
+
+* liblbca.so loads and exports every entry point include/lbca.h declares;
+* the host visibility rule equals the oracle's bit for bit;
+* every argument error returns its documented status before any device work
+  (fake, never dereferenced pointers are used; each case fails validation).
+"""
+import ctypes
+import subprocess
+
+import pytest
+
+from block_compressed_kv_amd import lbca
+from oracle import lbca_oracle as O
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced (validation fails first)
+
+try:
+    import torch
+
+    _GPU = torch.cuda.is_available()
+except Exception:  # pragma: no cover
+    _GPU = False
+# The fake-pointer cases are host-validation tests; on a machine with a GPU a
+# case that slipped through validation would launch a kernel on fake pointers.
+fake_ptr = pytest.mark.skipif(_GPU, reason="fake-pointer validation cases run on CPU-only machines")
+
+
+def test_every_declared_symbol_is_exported():
+    names = lbca.exported_names()
+    assert {"lbca_pool_blocks", "lbca_attend_decode", "lbca_attend_prefill", "csa_index_topk",
+            "lbca_visible_range", "lbca_attend_decode_workspace", "csa_index_topk_workspace",
+            "lbca_status_string", "lbca_abi_version"} <= set(names)
+    L = lbca.lib()
+    for n in names:
+        assert hasattr(L, n)
+    out = subprocess.run(["nm", "-D", "--defined-only", lbca.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(names) <= exported
+    # nothing but the C ABI leaks out of the library
+    assert all(s.startswith(("lbca_", "csa_")) or s in ("_init", "_fini") for s in exported), exported
+
+
+def test_status_strings():
+    L = lbca.lib()
+    for code in (0, -1, -2, -3, -4, 7):
+        assert L.lbca_status_string(code)
+
+
+@pytest.mark.parametrize("mode", [O.EXCLUSIVE, O.OVERLAP])
+def test_host_visibility_matches_oracle(mode):
+    for m in (1, 3, 4, 16, 64, 128):
+        for W in (1, 7, 128):
+            for t in list(range(0, 300)) + [32767, 2 ** 20 - 1, 2 ** 17 - 1, 10 ** 9]:
+                assert lbca.visible_range(t, m, W, mode) == O.visible_range(t, m, W, mode)
+
+
+def test_visibility_errors():
+    for args in [(-1, 4, 8, 0), (3, 0, 8, 0), (3, 4, 0, 0), (3, 4, 8, 2)]:
+        with pytest.raises(lbca.LbcaError) as e:
+            lbca.visible_range(*args)
+        assert e.value.status == lbca.ERR_INVALID_ARG
+
+
+def _pool(**kw):
+    a = dict(x=FAKE, v=None, z=FAKE, bias=FAKE, xb=None, zb=None, bias_b=None, out_x=FAKE, out_v=None,
+             batch=1, heads=2, tokens=64, dim=128, block=16, entries=4, block_begin=0, block_end=4,
+             pos_base=0, x_dtype=1, z_dtype=0, rmsnorm_eps=-1.0, rope_dims=0, rope_base=10000.0)
+    a.update(kw)
+    s = lbca.PoolArgs(**a)
+    return lbca.lib().lbca_pool_blocks(ctypes.byref(s), None)
+
+
+@fake_ptr
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), -1), (dict(z=None), -1), (dict(bias=None), -1), (dict(out_x=None), -1),
+    (dict(v=FAKE), -1),                                   # v without out_v
+    (dict(xb=FAKE), -1),                                  # partial dual args
+    (dict(xb=FAKE, zb=FAKE, bias_b=FAKE, v=FAKE, out_v=FAKE), -2),  # dual with values
+    (dict(x_dtype=5), -1), (dict(heads=0), -1), (dict(block=0), -1),
+    (dict(dim=96), -2), (dict(dim=1024), -2), (dict(dim=0), -1),
+    (dict(block_end=5), -1), (dict(block_begin=3, block_end=2), -1),
+    (dict(tokens=63), -1), (dict(pos_base=16), -1),       # token rows outside the buffer
+    (dict(rope_dims=24), -2), (dict(rope_dims=256), -1), (dict(rmsnorm_eps=float("nan")), -1),
+    (dict(rope_dims=64, rope_base=0.5), -1),
+    (dict(v=FAKE, out_v=FAKE, rmsnorm_eps=1e-6), -2),     # treatment needs a shared series
+    (dict(x=FAKE + 8), -1),                               # misaligned
+    (dict(xb=FAKE, zb=FAKE, bias_b=FAKE, block_begin=1, pos_base=16), -1),  # dual needs block i-1
+])
+def test_pool_validation(kw, code):
+    assert _pool(**kw) == code
+
+
+@fake_ptr
+def test_pool_empty_range_is_ok_without_gpu():
+    assert _pool(block_begin=2, block_end=2) == 0
+    assert _pool(batch=0) == 0
+
+
+def _decode(ws=None, ws_bytes=0, **kw):
+    a = dict(q=FAKE, pooled_k=FAKE, pooled_v=FAKE, raw_k=FAKE, raw_v=FAKE, pos=FAKE, raw_pos_base=None,
+             sel_idx=None, sink=None, out=FAKE, lse=None, batch=2, q_heads=24, kv_heads=8, dim=128,
+             entries=510, raw_rows=256, k_sel=0, block=64, window=128, mode=0, dtype=1, scale=0.08,
+             rmsnorm_eps=-1.0, rope_dims=0, rope_base=10000.0)
+    a.update(kw)
+    s = lbca.DecodeArgs(**a)
+    L = lbca.lib()
+    n = ctypes.c_size_t()
+    st = L.lbca_attend_decode_workspace(ctypes.byref(s), ctypes.byref(n))
+    st2 = L.lbca_attend_decode(ctypes.byref(s), ws, ws_bytes, None)
+    return st, st2, n.value
+
+
+@fake_ptr
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(pos=None), -1), (dict(out=None), -1), (dict(raw_v=None), -1),
+    (dict(q_heads=25), -1), (dict(kv_heads=0), -1), (dict(raw_rows=0), -1), (dict(window=0), -1),
+    (dict(mode=3), -1), (dict(dtype=9), -1), (dict(scale=float("inf")), -1),
+    (dict(sel_idx=FAKE, k_sel=0), -1),
+    (dict(dim=96), -2), (dict(dim=1024), -2), (dict(q_heads=8 * 65), -2),
+    (dict(rmsnorm_eps=1e-6), -2),                              # treatment with separate V
+    (dict(pooled_v=None, raw_v=None, rope_dims=32), -2),       # MFMA path rope dims
+    (dict(dtype=0, dim=96), -2),
+    (dict(dtype=0, pooled_v=None, raw_v=None, rmsnorm_eps=1e-6), -2),
+    (dict(out=FAKE + 4), -1),
+])
+def test_decode_validation(kw, code):
+    st, st2, _ = _decode(**kw)
+    assert st == code and st2 == code
+
+
+@fake_ptr
+def test_decode_workspace_required():
+    st, st2, need = _decode()
+    assert st == 0 and need > 0
+    assert st2 == lbca.ERR_WORKSPACE                    # no workspace given
+    _, st3, _ = _decode(ws=FAKE, ws_bytes=need - 1)
+    assert st3 == lbca.ERR_WORKSPACE
+    _, st4, _ = _decode(ws=FAKE + 8, ws_bytes=need)
+    assert st4 == lbca.ERR_WORKSPACE                    # misaligned workspace
+
+
+def _prefill(**kw):
+    a = dict(q=FAKE, pooled_k=FAKE, pooled_v=FAKE, raw_k=FAKE, raw_v=FAKE, sink=None, out=FAKE,
+             lse=None, batch=1, q_len=2048, q_heads=24, kv_heads=8, dim=128, entries=1016,
+             raw_rows=16384, q_pos0=14336, raw_pos_base=0, block=16, window=128, mode=0, dtype=1,
+             out_dtype=1, scale=0.08)
+    a.update(kw)
+    return lbca.lib().lbca_attend_prefill(ctypes.byref(lbca.PrefillArgs(**a)), None)
+
+
+@fake_ptr
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(out=None), -1), (dict(pooled_v=None), -1),
+    (dict(q_heads=23), -1), (dict(q_pos0=-1), -1), (dict(mode=2), -1), (dict(out_dtype=4), -1),
+    (dict(entries=1015), -1),                 # last query needs 1016 pooled entries
+    (dict(raw_rows=16383), -1),               # last query's position leaves the raw buffer
+    (dict(raw_pos_base=14300), -1),           # first query's raw span (from 14208) starts before the buffer
+    (dict(dim=256), -2), (dict(dtype=0, dim=96), -2),
+])
+def test_prefill_validation(kw, code):
+    assert _prefill(**kw) == code
+
+
+@fake_ptr
+def test_prefill_empty_is_ok_without_gpu():
+    assert _prefill(q_len=0) == 0
+    assert _prefill(batch=0) == 0
+
+
+def _index(ws=None, ws_bytes=0, **kw):
+    a = dict(q_idx=FAKE, head_w=FAKE, keys=FAKE, pos=FAKE, out_idx=FAKE, out_score=None, batch=2,
+             heads=8, dim=64, entries=32768, k=512, block=4, dtype=1)
+    a.update(kw)
+    s = lbca.IndexArgs(**a)
+    n = ctypes.c_size_t()
+    L = lbca.lib()
+    return (L.csa_index_topk_workspace(ctypes.byref(s), ctypes.byref(n)),
+            L.csa_index_topk(ctypes.byref(s), ws, ws_bytes, None), n.value)
+
+
+@fake_ptr
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_idx=None), -1), (dict(head_w=None), -1), (dict(pos=None), -1), (dict(out_idx=None), -1),
+    (dict(k=0), -1), (dict(block=0), -1), (dict(heads=0), -1), (dict(dtype=7), -1),
+    (dict(dim=48), -2), (dict(heads=17), -2), (dict(k=4096), -2), (dict(entries=1 << 17), -2),
+    (dict(dtype=0), -2),
+])
+def test_index_validation(kw, code):
+    st, st2, _ = _index(**kw)
+    assert st == code and st2 == code
+
+
+@fake_ptr
+def test_index_workspace_required():
+    st, st2, need = _index()
+    assert st == 0 and need == 2 * 32768 * 4
+    assert st2 == lbca.ERR_WORKSPACE
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(lbca, "LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(lbca, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        lbca.lib()

@@ -1,0 +1,312 @@
+"""GPU parity: every entry point of liblbca against the fp64 oracle, through the C ABI.
+
+Sizes span several tiles plus a ragged tail and finish in seconds on the oracle;
+the full workload sizes are in test_gpu_fullsize.py.  Inputs come from the
+seeded generators (block_compressed_kv_amd.synth) and are copied exactly to the
+oracle.  Tolerances: see tests/parity_util.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_compressed_kv_amd import synth
+from oracle import lbca_oracle as O
+
+from parity_util import check, check_bf16, check_f32_rows, host, say, topk_matches
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _dev(d):
+    return {k: v.to(DEV) for k, v in d.items()}
+
+
+# ---------------------------------------------------------------------------
+# pooling
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kv,zt,B,H,T,d,m,b0,b1", [
+    ("f32", "f32", 1, 1, 1025, 64, 16, 0, 64),       # tiny fp32 layer (all complete blocks)
+    ("bf16", "f32", 2, 8, 4096, 128, 64, 3, 61),     # Llama-shaped GQA layer, ragged range
+    ("bf16", "bf16", 1, 2, 640, 256, 16, 0, 40),
+    ("f32", "bf16", 2, 3, 300, 32, 7, 1, 42),        # odd block size (m % 4 != 0)
+])
+def test_pool_single(lib, kv, zt, B, H, T, d, m, b0, b1):
+    say(f"pool {kv}/{zt} B={B} H={H} T={T} d={d} m={m} blocks [{b0},{b1})")
+    L = _dev(synth.lbca_layer(f"pool-{kv}-{d}-{m}", B, H, H, T, d, m, kv, zt))
+    N = T // m
+    ok = torch.full((B, H, N, d), 7.0, dtype=L["k"].dtype, device=DEV)
+    ov = torch.full_like(ok, 7.0)
+    lib.pool_blocks(L["k"], L["z"], L["bias"], m, b0, b1, ok, v=L["v"], out_v=ov)
+    torch.cuda.synchronize()
+    rk, rv = O.pool_single(host(L["k"]), host(L["z"]), host(L["bias"]), m, b0, b1, values=host(L["v"]))
+    check(kv, host(ok[:, :, b0:b1]), rk, "pooled K")
+    check(kv, host(ov[:, :, b0:b1]), rv, "pooled V")
+    # rows outside the range are untouched
+    assert (ok[:, :, :b0] == 7.0).all() and (ok[:, :, b1:] == 7.0).all()
+
+
+def test_pool_pos_base_window(lib):
+    # token buffer that starts at position 640: pool blocks 10..19 (m=64) from it
+    B, H, T, d, m = 1, 2, 2048, 128, 64
+    L = _dev(synth.lbca_layer("pool-base", B, H, H, T, d, m, "bf16", "f32"))
+    base = 640
+    sub = {k: L[k][:, :, base:].contiguous() for k in ("k", "v", "z")}
+    ok = torch.zeros((B, H, 32, d), dtype=torch.bfloat16, device=DEV)
+    ov = torch.zeros_like(ok)
+    lib.pool_blocks(sub["k"], sub["z"], L["bias"], m, 10, 20, ok, v=sub["v"], out_v=ov, pos_base=base)
+    rk, rv = O.pool_single(host(L["k"]), host(L["z"]), host(L["bias"]), m, 10, 20, values=host(L["v"]))
+    check_bf16(host(ok[:, :, 10:20]), rk, "pooled K (pos_base)")
+    check_bf16(host(ov[:, :, 10:20]), rv, "pooled V (pos_base)")
+
+
+@pytest.mark.parametrize("treat", [False, True])
+def test_pool_shared_hca(lib, treat):
+    B, T, d, m = 2, 128 * 9 + 50, 512, 128
+    H = _dev(synth.hca_layer(f"pool-hca-{treat}", B, 4, T, d, m))
+    N = T // m
+    out = torch.zeros((B, 1, N, d), dtype=torch.bfloat16, device=DEV)
+    kw = dict(rmsnorm_eps=1e-6, rope_dims=64, rope_base=10000.0) if treat else {}
+    lib.pool_blocks(H["c"], H["z"], H["bias"], m, 0, N, out, **kw)
+    ref = O.pool_single(host(H["c"]), host(H["z"]), host(H["bias"]), m, 0, N)
+    if treat:
+        ref = O.rope(O.rmsnorm(ref, 1e-6), (np.arange(N) * m)[None, None], 64, 10000.0)
+    check_bf16(host(out), ref, f"HCA entries treat={treat}")
+
+
+@pytest.mark.parametrize("d,treat", [(512, False), (512, True), (64, False)])
+def test_pool_dual_csa(lib, d, treat):
+    B, m, T = 2, 4, 4 * 301
+    C = _dev(synth.csa_layer(f"pool-dual-{d}", B, 4, T, d, m, 8, 64))
+    N = T // m
+    out = torch.zeros((B, 1, N, d), dtype=torch.bfloat16, device=DEV)
+    kw = dict(rmsnorm_eps=1e-6, rope_dims=64, rope_base=10000.0) if treat else {}
+    lib.pool_blocks(C["ca"], C["za"], C["bias_a"], m, 0, N, out, xb=C["cb"], zb=C["zb"],
+                    bias_b=C["bias_b"], **kw)
+    ref = O.pool_dual(host(C["ca"]), host(C["za"]), host(C["bias_a"][0]), host(C["cb"]), host(C["zb"]),
+                      host(C["bias_b"][0]), m, 0, N)
+    if treat:
+        ref = O.rope(O.rmsnorm(ref, 1e-6), (np.arange(N) * m)[None, None], 64, 10000.0)
+    check_bf16(host(out), ref, f"CSA dual entries d={d} treat={treat}")
+    # a sub-range starting mid-sequence reads block i-1 of the b-series
+    out2 = torch.zeros_like(out)
+    lib.pool_blocks(C["ca"], C["za"], C["bias_a"], m, 17, 90, out2, xb=C["cb"], zb=C["zb"],
+                    bias_b=C["bias_b"], **kw)
+    assert torch.equal(out2[:, :, 17:90], out[:, :, 17:90])
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+def test_decode_tiny_fp32_layer(lib):
+    # seq_len 1024 fp32 layer, decode at position 1024 (its own K/V cached): 56 pooled + 129 raw
+    T, t, m, W = 1025, 1024, 16, 128
+    L = _dev(synth.lbca_layer("c1", 1, 2, 1, T, 64, m, "f32", "f32", q_len=1))
+    n_p, _ = O.visible_range(t, m, W, O.EXCLUSIVE)
+    assert n_p == 56
+    pk = torch.zeros((1, 1, 64, 64), device=DEV)
+    pv = torch.zeros_like(pk)
+    lib.pool_blocks(L["k"], L["z"], L["bias"], m, 0, n_p, pk, v=L["v"], out_v=pv)
+    q = L["q"][:, 0].contiguous()
+    pos = torch.tensor([t], device=DEV)
+    for sink in (None, torch.tensor([0.3, -1.1], device=DEV)):
+        o, lse = lib.attend_decode(q, pk, L["k"], pos, m, W, O.EXCLUSIVE, pooled_v=pv, raw_v=L["v"],
+                                   sink=sink)
+        rpk, rpv = O.pool_single(host(L["k"]), host(L["z"]), host(L["bias"]), m, 0, n_p, values=host(L["v"]))
+        ro, rl = O.attend_decode(host(q), rpk, rpv, host(L["k"]), host(L["v"]), [t], m, W, O.EXCLUSIVE,
+                                 1 / 8, sink=None if sink is None else host(sink))
+        check_f32_rows(host(o), ro, f"tiny decode sink={sink is not None}")
+        check_f32_rows(host(lse)[..., None], rl[..., None], "tiny decode lse")
+
+
+@pytest.mark.parametrize("t_list", [[4095, 1000, 130, 0], [127, 128, 191, 192]])
+def test_decode_gqa_bf16(lib, t_list):
+    # Llama-shaped GQA decode (24 q heads over 8 KV heads, d=128), ragged positions
+    B, Hq, Hkv, d, m, W, T = len(t_list), 24, 8, 128, 64, 128, 4096
+    g = lambda n, shape: synth.normal(shape, synth.seed_of("dec-gqa", n, tuple(t_list)), dtype="bf16",
+                                      device=DEV)
+    q = g("q", (B, Hq, d))
+    pk, pv = g("pk", (B, Hkv, 64, d)), g("pv", (B, Hkv, 64, d))
+    rk, rv = g("rk", (B, Hkv, T, d)), g("rv", (B, Hkv, T, d))
+    pos = torch.tensor(t_list, device=DEV)
+    sink = synth.normal((Hq,), 5, device=DEV)
+    o, lse = lib.attend_decode(q, pk, rk, pos, m, W, O.EXCLUSIVE, pooled_v=pv, raw_v=rv, sink=sink)
+    ro, rl = O.attend_decode(host(q), host(pk), host(pv), host(rk), host(rv), t_list, m, W, O.EXCLUSIVE,
+                             1 / math.sqrt(d), sink=host(sink))
+    check_bf16(host(o), ro, "GQA decode out")
+    check_bf16(host(lse), rl, "GQA decode lse")
+    # bitwise reproducible
+    o2, lse2 = lib.attend_decode(q, pk, rk, pos, m, W, O.EXCLUSIVE, pooled_v=pv, raw_v=rv, sink=sink)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+def test_decode_raw_pos_base_and_overlap(lib):
+    B, Hq, Hkv, d, m, W = 3, 8, 2, 64, 16, 40
+    t_list, base = [700, 333, 45], [600, 290, 0]
+    g = lambda n, shape: synth.normal(shape, synth.seed_of("dec-base", n), dtype="bf16", device=DEV)
+    q = g("q", (B, Hq, d))
+    pk, pv = g("pk", (B, Hkv, 50, d)), g("pv", (B, Hkv, 50, d))
+    rk, rv = g("rk", (B, Hkv, 128, d)), g("rv", (B, Hkv, 128, d))
+    pos = torch.tensor(t_list, device=DEV)
+    rpb = torch.tensor(base, device=DEV)
+    o, lse = lib.attend_decode(q, pk, rk, pos, m, W, O.OVERLAP, pooled_v=pv, raw_v=rv, raw_pos_base=rpb)
+    ro, rl = O.attend_decode(host(q), host(pk), host(pv), host(rk), host(rv), t_list, m, W, O.OVERLAP,
+                             1 / 8, raw_pos_base=base)
+    check_bf16(host(o), ro, "decode OVERLAP + raw_pos_base")
+    check_bf16(host(lse), rl, "lse")
+
+
+def test_decode_invalid_sequence_gets_nan(lib):
+    B, Hq, Hkv, d, m, W = 3, 4, 1, 64, 16, 32
+    q = synth.normal((B, Hq, d), 1, dtype="bf16", device=DEV)
+    pk = synth.normal((B, Hkv, 8, d), 2, dtype="bf16", device=DEV)
+    rk = synth.normal((B, Hkv, 256, d), 3, dtype="bf16", device=DEV)
+    # seq 0 fine; seq 1 needs 13 pooled entries (> 8); seq 2 position beyond the raw buffer
+    pos = torch.tensor([100, 240, 300], device=DEV)
+    o, lse = lib.attend_decode(q, pk, rk, pos, m, W, O.OVERLAP)
+    assert torch.isfinite(o[0]).all() and torch.isfinite(lse[0]).all()
+    assert torch.isnan(o[1]).all() and torch.isnan(lse[1]).all()
+    assert torch.isnan(o[2]).all() and torch.isnan(lse[2]).all()
+
+
+@pytest.mark.parametrize("rd", [0, 64])
+def test_decode_hca_treated(lib, rd):
+    # HCA-style MQA: shared series, 64 heads, d=512, m'=128, RMSNorm, partial RoPE, sink
+    B, Hq, d, m, W = 2, 64, 512, 128, 128
+    T = 128 * 12 + 77
+    H = _dev(synth.hca_layer(f"dec-hca-{rd}", B, Hq, T, d, m))
+    t_list = [T - 1, 128 * 5 + 3]
+    N = T // m
+    entries = torch.zeros((B, 1, N, d), dtype=torch.bfloat16, device=DEV)
+    lib.pool_blocks(H["c"], H["z"], H["bias"], m, 0, N, entries, rmsnorm_eps=1e-6, rope_dims=rd)
+    pos = torch.tensor(t_list, device=DEV)
+    o, lse = lib.attend_decode(H["q"], entries, H["c"], pos, m, W, O.OVERLAP, sink=H["sink"],
+                               rmsnorm_eps=1e-6, rope_dims=rd)
+    pooled = O.pool_single(host(H["c"]), host(H["z"]), host(H["bias"]), m, 0, N)
+    ro, rl = O.attend_decode(host(H["q"]), pooled, None, host(H["c"]), None, t_list, m, W, O.OVERLAP,
+                             1 / math.sqrt(d), sink=host(H["sink"]), rmsnorm_eps=1e-6, rope_dims=rd)
+    check_bf16(host(o), ro, f"HCA decode rope={rd}")
+    check_bf16(host(lse), rl, "HCA lse")
+
+
+def test_decode_selected_entries(lib):
+    # CSA-style: dual-pooled treated entries, a selection with -1 padding and invisible
+    # ids, plus the 128-token window; MQA 64 heads, d=512
+    B, Hq, d, m, W, k = 2, 64, 512, 4, 128, 40
+    T = 4 * 300
+    C = _dev(synth.csa_layer("dec-sel", B, Hq, T, d, m, 8, 64))
+    N = T // m
+    entries = torch.zeros((B, 1, N, d), dtype=torch.bfloat16, device=DEV)
+    treat = dict(rmsnorm_eps=1e-6, rope_dims=64, rope_base=10000.0)
+    lib.pool_blocks(C["ca"], C["za"], C["bias_a"], m, 0, N, entries, xb=C["cb"], zb=C["zb"],
+                    bias_b=C["bias_b"], **treat)
+    t_list = [T - 1, 4 * 100 + 2]
+    rng = np.random.default_rng(3)
+    sel = np.stack([np.sort(rng.choice(300, k, replace=False)), np.sort(rng.choice(150, k, replace=False))])
+    sel[0, -3:] = -1                 # empty slots
+    sel_t = torch.tensor(sel, dtype=torch.int32, device=DEV)   # seq 1 also lists ids >= 100 (invisible)
+    pos = torch.tensor(t_list, device=DEV)
+    o, lse = lib.attend_decode(C["q"], entries, C["ca"], pos, m, W, O.OVERLAP, sel_idx=sel_t,
+                               sink=C["sink"], **treat)
+    pooled = O.pool_dual(host(C["ca"]), host(C["za"]), host(C["bias_a"][0]), host(C["cb"]),
+                         host(C["zb"]), host(C["bias_b"][0]), m, 0, N)
+    ro, rl = O.attend_decode(host(C["q"]), pooled, None, host(C["ca"]), None, t_list, m, W, O.OVERLAP,
+                             1 / math.sqrt(d), sel_idx=sel, sink=host(C["sink"]), **treat)
+    check_bf16(host(o), ro, "selected decode")
+    check_bf16(host(lse), rl, "selected lse")
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+def test_prefill_tiny_fp32_layer(lib):
+    T, m, W = 1024, 16, 128
+    L = _dev(synth.lbca_layer("c1", 1, 2, 1, T + 1, 64, m, "f32", "f32", q_len=T))
+    n_p, _ = O.visible_range(T - 1, m, W, O.EXCLUSIVE)
+    pk = torch.zeros((1, 1, 64, 64), device=DEV)
+    pv = torch.zeros_like(pk)
+    lib.pool_blocks(L["k"], L["z"], L["bias"], m, 0, n_p, pk, v=L["v"], out_v=pv)
+    o, lse = lib.attend_prefill(L["q"], 0, pk, L["k"], 0, m, W, O.EXCLUSIVE, pooled_v=pv, raw_v=L["v"])
+    k, v, z, bias = (host(L[n]) for n in ("k", "v", "z", "bias"))
+    ro, rl = O.prefill_chunked(host(L["q"]), k[:, :, :T], v[:, :, :T], z[:, :, :T], bias, m, W, T, 1 / 8)
+    check_f32_rows(host(o), ro, "tiny prefill")
+    check_f32_rows(host(lse)[..., None], rl[..., None], "tiny prefill lse")
+
+
+@pytest.mark.parametrize("chunk", [256, 300])
+def test_prefill_chunked_bf16(lib, chunk):
+    # Llama-shaped GQA layer, m=16, W=128, chunked: pool the chunk's newly visible blocks, attend
+    B, Hq, Hkv, d, m, W, T = 1, 24, 8, 128, 16, 128, 1200
+    L = _dev(synth.lbca_layer("prefill-bf16", B, Hq, Hkv, T, d, m, "bf16", "f32", q_len=T))
+    pk = torch.zeros((B, Hkv, T // m, d), dtype=torch.bfloat16, device=DEV)
+    pv = torch.zeros_like(pk)
+    out = torch.empty((B, T, Hq, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device=DEV)
+    done = 0
+    for c0 in range(0, T, chunk):
+        c1 = min(T, c0 + chunk)
+        need, _ = O.visible_range(c1 - 1, m, W, O.EXCLUSIVE)
+        if need > done:
+            lib.pool_blocks(L["k"], L["z"], L["bias"], m, done, need, pk, v=L["v"], out_v=pv)
+            done = need
+        lib.attend_prefill(L["q"][:, c0:c1].contiguous(), c0, pk, L["k"], 0, m, W, O.EXCLUSIVE,
+                           out=out[:, c0:c1], lse=lse[:, c0:c1], pooled_v=pv, raw_v=L["v"])
+    ro, rl = O.prefill_chunked(host(L["q"]), host(L["k"]), host(L["v"]), host(L["z"]), host(L["bias"]),
+                               m, W, 400, 1 / math.sqrt(d))
+    check_bf16(host(out), ro, f"chunked prefill chunk={chunk}")
+    check_bf16(host(lse), rl, "prefill lse")
+
+
+def test_prefill_overlap_shared_sink(lib):
+    # OVERLAP visibility, shared K=V series, sink, fp32 output, MQA-like 8 heads over 1 KV head, d=64
+    B, Hq, d, m, W, T = 2, 8, 64, 8, 24, 333
+    g = lambda n, shape: synth.normal(shape, synth.seed_of("prefill-ov", n), dtype="bf16", device=DEV)
+    q = g("q", (B, 100, Hq, d))
+    pooled, raw = g("p", (B, 1, T // m, d)), g("r", (B, 1, T, d))
+    sink = synth.normal((Hq,), 9, device=DEV)
+    o, lse = lib.attend_prefill(q, T - 100, pooled, raw, 0, m, W, O.OVERLAP, sink=sink,
+                                out_dtype=torch.float32)
+    ro, rl = O.attend_prefill(host(q), T - 100, host(pooled), None, host(raw), None, 0, m, W, O.OVERLAP,
+                              1 / 8, sink=host(sink))
+    check_bf16(host(o), ro, "prefill overlap shared")
+    check_bf16(host(lse), rl, "lse")
+
+
+# ---------------------------------------------------------------------------
+# indexer + top-k
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("N,k,t_list", [(2000, 64, [7999, 3001]), (700, 512, [2799, 100]),
+                                        (5000, 2048, [19999, 19999])])
+def test_index_topk(lib, N, k, t_list):
+    B, HI, dI, m = len(t_list), 8, 64, 4
+    g = lambda n, shape: synth.normal(shape, synth.seed_of("idx", N, n), dtype="bf16", device=DEV)
+    qi, keys = g("qi", (B, HI, dI)), g("k", (B, N, dI))
+    w = synth.uniform((B, HI), synth.seed_of("idx", N, "w"), device=DEV)
+    pos = torch.tensor(t_list, device=DEV)
+    idx, score = lib.csa_index_topk(qi, w, keys, pos, m, k)
+    idx, score = idx.cpu().numpy(), score.cpu().numpy()
+    for b, t in enumerate(t_list):
+        n_vis = min((t + 1) // m, N)
+        s = O.index_scores(host(qi[b]), host(w[b]), host(keys[b]), n_vis)
+        margin = topk_matches(idx[b], s, k, f"top-k seq {b}")
+        say(f"top-k seq {b}: n_vis={n_vis} k={k} margin={margin:.3e}")
+        sel = idx[b][idx[b] >= 0]
+        np.testing.assert_allclose(score[b][:sel.size], s[sel], rtol=1e-5, atol=1e-5)
+        assert np.isnan(score[b][sel.size:]).all()
+
+
+def test_topk_ties_and_zero_scores(lib):
+    # planted exact ties: small-integer data makes every score exact in fp32 and fp64
+    B, HI, dI, N, m, k = 1, 2, 32, 96, 1, 10
+    qi = torch.zeros((B, HI, dI), dtype=torch.bfloat16, device=DEV)
+    qi[0, 0, 0] = 1.0
+    keys = torch.zeros((B, N, dI), dtype=torch.bfloat16, device=DEV)
+    vals = [3, 5, 5, 1, 5, 2, 2, 7, -4, 2] * 9 + [0] * 6
+    keys[0, :, 0] = torch.tensor(vals, dtype=torch.bfloat16)
+    w = torch.tensor([[1.0, 0.5]], device=DEV)
+    idx, score = lib.csa_index_topk(qi, w, keys, torch.tensor([N - 1], device=DEV), m, k)
+    s = np.maximum(np.array(vals, dtype=np.float64), 0)
+    ref = O.topk_select(s, k)
+    assert list(idx[0].cpu().numpy()) == list(ref)
