@@ -1,0 +1,323 @@
+"""Benchmark: LBCA decode at 32K context on one MI355X (plus prefill and pooling lines).
+
+Headline workload: Llama-3.2-3B-shaped LBCA layers (24 query heads over 8 KV
+heads, head dim 128, bf16 K/V/Q, fp32 pooling logits, 64-token blocks, 128-token
+raw window), 14 grafted layers with independent seeded inputs, batch 16, one
+decode step at position t = 32767 (510 pooled entries + 128 raw tokens per KV
+head).  At that position block 509 leaves the window, so the step is, per layer:
+pool block 509 of every sequence and KV head, then decode attention.
+``value`` = layer-steps per second (14 per step).
+
+Inputs are resident in HBM before timing.  Each layer keeps only what a decode
+step touches (pooled cache, the last 192 raw tokens, the due block's logits);
+the 14 layers together exceed the 256 MB Infinity Cache, so every step streams
+from HBM.  The step is captured once as a HIP graph (launch-bound otherwise) and
+replayed; HIP events on the launch stream bracket the timed region.
+
+Also reported: decode launch duration and its HBM roofline fraction, the
+oracle on the host cores (cpu_baseline), batch 1 and 4, full-history pooling
+GB/s, and chunked prefill (16K context in 2048-token chunks) TFLOP/s.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--all]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+from block_compressed_kv_amd import lbca, synth
+
+METRIC = "LBCA decode layer-steps/s + achieved HBM GB/s at 32K ctx; prefill TFLOP/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+EXCL, OVER = lbca.EXCLUSIVE, lbca.OVERLAP
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def ev():
+    return torch.cuda.Event(enable_timing=True)
+
+
+# ---------------------------------------------------------------------------
+# 32K decode layers
+# ---------------------------------------------------------------------------
+CTX, HQ, HKV, D, M, W, LAYERS = 32768, 24, 8, 128, 64, 128, 14
+T_POS = CTX - 1                        # query position
+N_POOLED = 510                         # visible pooled entries at T_POS
+RAW0 = 509 * M                         # first token kept raw: block 509 (due) + window
+RAW_ROWS = CTX - RAW0                  # 192
+
+
+def decode_bytes_per_seq_layer():
+    # K and V of every visible row (pooled + raw window) in bf16, q in bf16, out in fp32
+    n_rows = N_POOLED + (T_POS - (N_POOLED * M) + 1)
+    return n_rows * HKV * D * 2 * 2 + HQ * D * 2 + HQ * D * 4
+
+
+class DecodeLayer:
+    def __init__(self, layer, B, pool_timer=None):
+        tag = ("bench-32k", layer, B)
+        dev = "cuda"
+        full = synth.lbca_layer(tag, B, HQ, HKV, CTX, D, M, "bf16", "f32", device=dev)
+        self.bias = full["bias"]
+        self.pk = torch.empty((B, HKV, N_POOLED, D), dtype=torch.bfloat16, device=dev)
+        self.pv = torch.empty_like(self.pk)
+        # prefill-time pooling of blocks 0..508 from the whole history (timed as pooling GB/s)
+        e0, e1 = ev(), ev()
+        e0.record()
+        lbca.pool_blocks(full["k"], full["z"], self.bias, M, 0, N_POOLED - 1, self.pk, v=full["v"],
+                         out_v=self.pv)
+        e1.record()
+        if pool_timer is not None:
+            pool_timer.append((e0, e1, B * HKV * (N_POOLED - 1) * M * D * (2 + 2 + 4)))
+        self.rk = full["k"][:, :, RAW0:].contiguous()
+        self.rv = full["v"][:, :, RAW0:].contiguous()
+        self.z = full["z"][:, :, RAW0:].contiguous()
+        del full
+        self.q = synth.normal((B, HQ, D), synth.seed_of(*tag, "q1"), dtype="bf16", device=dev)
+        self.pos = torch.full((B,), T_POS, dtype=torch.int64, device=dev)
+        self.rpb = torch.full((B,), RAW0, dtype=torch.int64, device=dev)
+        self.out = torch.empty((B, HQ, D), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, HQ), dtype=torch.float32, device=dev)
+        nbytes = lbca.decode_workspace_bytes(self.q, self.pk, self.rk, self.pos, M, W, EXCL,
+                                             pooled_v=self.pv, raw_v=self.rv, raw_pos_base=self.rpb)
+        self.ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
+
+    def pool_due(self):
+        lbca.pool_blocks(self.rk, self.z, self.bias, M, N_POOLED - 1, N_POOLED, self.pk, v=self.rv,
+                         out_v=self.pv, pos_base=RAW0)
+
+    def decode(self):
+        lbca.attend_decode(self.q, self.pk, self.rk, self.pos, M, W, EXCL, out=self.out, lse=self.lse,
+                           pooled_v=self.pv, raw_v=self.rv, raw_pos_base=self.rpb, workspace=self.ws)
+
+
+def capture(fn):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm the allocator / module loading outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, reps):
+    e0, e1 = ev(), ev()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps  # ms
+
+
+def run_decode(B, steps, warmup, pool_timer=None):
+    layers = [DecodeLayer(l, B, pool_timer) for l in range(LAYERS)]
+    torch.cuda.synchronize()
+
+    def step():
+        for L in layers:
+            L.pool_due()
+            L.decode()
+
+    def dec_only():
+        for L in layers:
+            L.decode()
+
+    # eager reference of the step, then check graph replays reproduce it bitwise
+    step()
+    torch.cuda.synchronize()
+    ref = [L.out.clone() for L in layers]
+    g_step = capture(step)
+    g_dec = capture(dec_only)
+    for _ in range(max(1, warmup)):
+        g_step.replay()
+    torch.cuda.synchronize()
+    for L, r in zip(layers, ref):
+        if not torch.equal(L.out, r):
+            raise RuntimeError("graph replay differs from the eager step")
+    ms_step = time_graph(g_step, steps)
+    ms_dec = time_graph(g_dec, steps) / LAYERS
+    return layers, ms_step, ms_dec
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill, 16K context
+# ---------------------------------------------------------------------------
+P_CTX, P_M, P_CHUNK = 16384, 16, 2048
+
+
+def prefill_flops():
+    tot = 0
+    for t in range(P_CTX):
+        n_p, rb = lbca.visible_range(t, P_M, W, EXCL)
+        tot += 4 * HQ * D * (n_p + t - rb + 1)
+    return tot
+
+
+def run_prefill(reps):
+    dev = "cuda"
+    L = synth.lbca_layer(("bench-prefill-16k",), 1, HQ, HKV, P_CTX, D, P_M, "bf16", "f32", device=dev,
+                         q_len=P_CTX)
+    pk = torch.zeros((1, HKV, P_CTX // P_M, D), dtype=torch.bfloat16, device=dev)
+    pv = torch.zeros_like(pk)
+    out = torch.empty((1, P_CTX, HQ, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((1, P_CTX, HQ), dtype=torch.float32, device=dev)
+    qs = [L["q"][:, c:c + P_CHUNK].contiguous() for c in range(0, P_CTX, P_CHUNK)]
+    plan = []
+    done = 0
+    for i, c0 in enumerate(range(0, P_CTX, P_CHUNK)):
+        need, _ = lbca.visible_range(c0 + P_CHUNK - 1, P_M, W, EXCL)
+        plan.append((i, c0, done, need))
+        done = need
+
+    def attend(i, c0):
+        lbca.attend_prefill(qs[i], c0, pk, L["k"], 0, P_M, W, EXCL, out=out[:, c0:c0 + P_CHUNK],
+                            lse=lse[:, c0:c0 + P_CHUNK], pooled_v=pv, raw_v=L["v"])
+
+    def full():
+        for i, c0, b0, b1 in plan:
+            lbca.pool_blocks(L["k"], L["z"], L["bias"], P_M, b0, b1, pk, v=L["v"], out_v=pv)
+            attend(i, c0)
+
+    def attn_only():
+        for i, c0, _, _ in plan:
+            attend(i, c0)
+
+    g_full = capture(full)
+    g_attn = capture(attn_only)
+    g_full.replay()
+    ms_full = time_graph(g_full, reps)
+    ms_attn = time_graph(g_attn, reps)
+    return ms_full, ms_attn
+
+
+# ---------------------------------------------------------------------------
+# oracle on the host
+# ---------------------------------------------------------------------------
+def cpu_baseline(layer, budget_s=12.0):
+    import numpy as np
+
+    from oracle import lbca_oracle as O
+
+    host = lambda t: t.detach().cpu().to(torch.float64).numpy()
+    B = layer.q.shape[0]
+    q, pk, pv = host(layer.q), host(layer.pk), host(layer.pv)
+    rk, rv, z, bias = host(layer.rk), host(layer.rv), host(layer.z), host(layer.bias)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        # due block 509 from the raw buffer (positions RAW0.. are rows 0..), then attention
+        due_k, due_v = O.pool_single(rk, z, bias, M, 0, 1, values=rv)
+        pk[:, :, N_POOLED - 1] = due_k[:, :, 0]
+        pv[:, :, N_POOLED - 1] = due_v[:, :, 0]
+        O.attend_decode(q, pk, pv, rk, rv, [T_POS] * B, M, W, O.EXCLUSIVE, 1 / math.sqrt(D),
+                        raw_pos_base=[RAW0] * B)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": n / el, "unit": "layer-steps/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"{n} oracle layer-steps (pool the due block + decode attention, batch {B}, "
+                      f"32K context, fp64 NumPy) in {el:.1f} s; torch threads {torch.get_num_threads()}"}
+
+
+# ---------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--batch", type=int, default=16)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the host oracle timing")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-small-batch", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the decode/prefill hot path here has no multi-GPU "
+              f"path (requested --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    lbca.lib()  # fail loudly if the library is missing
+
+    B = args.batch
+    log(f"[bench] decode 32K: building {LAYERS} layers at batch {B}")
+    pool_timer = []
+    layers, ms_step, ms_dec = run_decode(B, args.steps, args.warmup, pool_timer)
+    torch.cuda.synchronize()
+    pool_ms = sum(a.elapsed_time(b) for a, b, _ in pool_timer)
+    pool_bytes = sum(n for _, _, n in pool_timer)
+    log(f"[bench] step {ms_step * 1e3:.1f} us ({LAYERS} layers), decode launch {ms_dec * 1e3:.2f} us")
+
+    per_launch_bytes = decode_bytes_per_seq_layer() * B
+    achieved = per_launch_bytes / (ms_dec * 1e-3) / 1e9
+    value = LAYERS / (ms_step * 1e-3)
+    extra = {
+        "decode_only_layer_steps_per_s": 1e3 / ms_dec,
+        "decode_launch_us": ms_dec * 1e3,
+        "decode_algorithmic_bytes_per_launch": per_launch_bytes,
+        "history_pool_GBps": pool_bytes / (pool_ms * 1e-3) / 1e9,
+        "history_pool_bytes": pool_bytes,
+    }
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] oracle on host cores (bounded sample)")
+        cpu = cpu_baseline(layers[0])
+    del layers
+    torch.cuda.empty_cache()
+
+    if not args.no_small_batch:
+        for b in (1, 4):
+            log(f"[bench] decode 32K batch {b}")
+            ls, st, dc = run_decode(b, args.steps, args.warmup)
+            by = decode_bytes_per_seq_layer() * b
+            extra[f"b{b}"] = {"layer_steps_per_s": LAYERS / (st * 1e-3), "decode_launch_us": dc * 1e3,
+                              "decode_GBps": by / (dc * 1e-3) / 1e9}
+            del ls
+            torch.cuda.empty_cache()
+
+    if not args.no_prefill:
+        log("[bench] chunked prefill 16K (8 x 2048)")
+        ms_full, ms_attn = run_prefill(max(5, args.steps // 10))
+        fl = prefill_flops()
+        extra["prefill"] = {"tflops": fl / (ms_attn * 1e-3) / 1e12, "attention_ms": ms_attn,
+                            "with_pooling_ms": ms_full, "algorithmic_flops": fl,
+                            "frac_of_bf16_peak": fl / (ms_attn * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "layer-steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"lbca-decode-32k-b{B}-14layers", "batch": B, "context": CTX,
+                   "q_heads": HQ, "kv_heads": HKV, "head_dim": D, "block": M, "window": W,
+                   "layers": LAYERS, "step": "pool due block 509 + decode attention, per layer"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "lbca_attend_decode launch (split-K partial + merge)"},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

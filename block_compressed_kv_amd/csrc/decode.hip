@@ -7,29 +7,39 @@
 // RMSNorm on queries and entries, partial RoPE with the -t output rotation,
 // attention sink, selected entries plus the sliding window).
 //
-// bf16 path (MFMA).  One wave per workgroup.  A wave owns 16 query heads of one
-// KV head (GQA groups are padded to 16; MQA with 64 heads uses 4 head groups)
-// and a contiguous range of R-row tiles of the visible-row list (pooled or
-// selected entries, then the raw span).  Scores are computed transposed,
-// S^T[row, head] = K[row, :] . Q[head, :], with v_mfma_f32_16x16x32_bf16 whose
-// A operand is read straight from global memory in row-major K layout, so
-// every lane holds all scores of one head and the softmax max/sum need only
-// two cross-lane steps.  P^T is already the B-operand layout of
-// v_mfma_f32_16x16x16_bf16 for O^T = V^T P^T; V rows go through LDS so the
-// A operand (8 rows of one dim per lane) can be gathered.  Each wave writes an
-// unnormalised partial (acc, running max, running sum); a merge kernel combines
-// the splits in a fixed order (bitwise reproducible), adds the sink and
-// applies the -t rotation.
+// Work unit = (sequence, KV head, group of 16 query heads).  GQA groups are
+// padded to 16 heads; MQA with 64 heads is 4 units per KV head, whose
+// workgroups read the same rows (L2 hits after the first).
 //
-// fp32 path (VALU).  One wave per (query, head): lanes score 64 rows at a time,
-// then broadcast each probability to accumulate V.  Used for fp32 decode and
-// fp32 prefill.
+// A workgroup (NW waves) owns a contiguous range of the unit's visible-row
+// list (pooled or selected entries, then the raw span) cut into R-row tiles;
+// wave w takes tiles w, w+NW, ... and, where registers allow, keeps the next
+// tile's global loads in flight (two tile buffers used in turn) while it
+// computes the current one.  Scores are computed transposed,
+// S^T[row, head] = K[row, :] . Q[head, :], with v_mfma_f32_16x16x32_bf16 whose
+// A operand is loaded straight from global memory in row-major K layout: every
+// lane holds scores of one head, and the softmax max/sum need one 16-lane and
+// one 32-lane swap.  P^T is already the B operand of v_mfma_f32_16x16x16_bf16
+// for O^T = V^T P^T; V rows are staged row-major in a per-wave LDS tile and
+// each A operand is one transposing LDS read (ds_read_b64_tr_b16).
+//
+// Small decodes are bound by each wave's instruction chain, not by bytes, so
+// the per-tile path is kept short: raw v_exp_f32, lane swaps instead of LDS
+// permutes, the accumulator rescale skipped when no running max moved, 32-bit
+// index arithmetic, and a single-barrier merge of the waves.  With one split
+// the workgroup finishes its heads (sink, normalisation, -t rotation, LSE);
+// with several, each workgroup writes an unnormalised partial (acc, max, sum)
+// and decode_merge_kernel combines them in a fixed order (bitwise
+// reproducible).  No device-scope fence is used anywhere: on this multi-XCD
+// part a device-scope release/acquire writes back and invalidates the XCD's L2.
 #include "device_util.h"
 #include "lbca_internal.h"
 
-namespace lbca {
+#ifndef LBCA_DECODE_TARGET_WAVES
+#define LBCA_DECODE_TARGET_WAVES 1024  // waves a decode launch aims for (256 CUs x 4 SIMDs)
+#endif
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+namespace lbca {
 
 struct DecodeParams {
   const bf16_t* q;
@@ -43,10 +53,10 @@ struct DecodeParams {
   const float* sink;
   float* out;
   float* lse;
-  float* ws_acc;  // [wg][16][D]
-  float* ws_ml;   // [wg][16][2]
+  float* ws_ml;    // [units * splits][16][2]
+  float* ws_acc;   // [units * splits][16][D]
   int64_t hq, hkv, G, entries, raw_rows, k_sel, m, W;
-  int mode, splits, head_groups, dim;
+  int mode, splits, head_groups;
   float scale_log2;
   float eps;
   int rope_dims;
@@ -54,7 +64,8 @@ struct DecodeParams {
 };
 
 struct SeqView {
-  int64_t t, n_pooled, n_sel, n_raw, raw_begin, raw_row0;
+  int64_t t, raw_begin, raw_row0;
+  int n_pooled, n_sel, n_raw;
   bool ok;
 };
 
@@ -67,9 +78,9 @@ __device__ __forceinline__ SeqView seq_view(const DecodeParams& p, int64_t b) {
   if (ok) visible_range(v.t, p.m, p.W, p.mode, &np, &rb);
   ok = ok && np <= p.entries && rb - base >= 0 && v.t - base < p.raw_rows;
   v.ok = ok;
-  v.n_pooled = np;
-  v.n_sel = ok ? (p.sel ? p.k_sel : np) : 0;
-  v.n_raw = ok ? v.t - rb + 1 : 0;
+  v.n_pooled = (int)np;
+  v.n_sel = ok ? (int)(p.sel ? p.k_sel : np) : 0;
+  v.n_raw = ok ? (int)(v.t - rb + 1) : 0;
   v.raw_begin = rb;
   v.raw_row0 = rb - base;
   return v;
@@ -86,11 +97,18 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
   return u;
 }
 
+// A wave reads back LDS its own lanes wrote: order the accesses at wave scope.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // HCA/CSA treatment of one row held in MFMA operand layout: lane (., kq) holds
 // dims 32*s + 8*kq + i of the row (s < D/32, i < 8); the 4 lanes of a row are
 // lane, lane^16, lane^32, lane^48.  RMSNorm over all D dims, then RoPE on the
 // last RD dims (rotate-half pairs (k, k+RD/2) sit in the same lane, RD/64 steps
-// apart).  Every lane of the wave must call this (it shuffles).
+// apart).  Every lane of the wave must call this (it uses lane swaps).
 template <int D, int RD>
 __device__ __forceinline__ void treat_row(uint4 (&r)[D / 32], double pos, bool ok, float eps,
                                           double log2_base) {
@@ -105,8 +123,8 @@ __device__ __forceinline__ void treat_row(uint4 (&r)[D / 32], double pos, bool o
 #pragma unroll
       for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
     }
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
+    ss = xor16_sum(ss);
+    ss = xor32_sum(ss);
     const float inv = ok ? 1.f / sqrtf(ss / (float)D + eps) : 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -117,7 +135,7 @@ __device__ __forceinline__ void treat_row(uint4 (&r)[D / 32], double pos, bool o
       r[s] = pack8(f);
     }
   }
-  if (RD > 0) {
+  if constexpr (RD > 0) {
     constexpr int SH = RD / 64;       // steps between pair partners
     constexpr int S0 = KS - 2 * SH;   // first rotated step
 #pragma unroll
@@ -140,87 +158,139 @@ __device__ __forceinline__ void treat_row(uint4 (&r)[D / 32], double pos, bool o
   }
 }
 
-template <int D, int R, bool SHARED, int RD, bool TREAT>
-__global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
-  constexpr int KS = D / 32, NH = R / 16, DT = D / 16, PITCH = D + 8;
-  __shared__ __attribute__((aligned(16))) bf16_t vtile[R * PITCH];
+template <int D, int R, bool SHARED>
+struct Tile {
+  uint4 k[R / 16][D / 32];
+  uint4 v[SHARED ? 1 : R / 16][SHARED ? 1 : D / 32];
+  unsigned valid[R / 16];
+};
 
-  const int lane = threadIdx.x, n = lane & 15, kq = lane >> 4;
-  int64_t id = blockIdx.x;
-  const int split = (int)(id % p.splits);
-  id /= p.splits;
-  const int hg = (int)(id % p.head_groups);
-  id /= p.head_groups;
-  const int64_t kvh = id % p.hkv;
-  const int64_t b = id / p.hkv;
-  const SeqView sv = seq_view(p, b);
-
-  const int64_t tiles_p = (sv.n_sel + R - 1) / R;
-  const int64_t tiles_total = tiles_p + (sv.n_raw + R - 1) / R;
-  const int64_t per = (tiles_total + p.splits - 1) / p.splits;
-  const int64_t t0 = split * per;
-  const int64_t t1 = t0 + per < tiles_total ? t0 + per : tiles_total;
-
-  // queries of this head group as B operands (zero for padded heads)
-  const int64_t slot = (int64_t)hg * 16 + n;
-  const bool head_ok = slot < p.G;
-  const bf16_t* qrow = p.q + ((b * p.hkv + kvh) * p.G + slot) * D + 8 * kq;
-  uint4 qr[KS];
+// Issue the global loads of one tile (rows beyond the list or unusable
+// selected ids are zero and marked invalid).
+template <int D, int R, bool SHARED>
+__device__ __forceinline__ void load_tile(Tile<D, R, SHARED>& T, const DecodeParams& p,
+                                          const SeqView& sv, int64_t b, int64_t kv_pool,
+                                          int64_t kv_raw, int tiles_p, int tile, int n, int kq) {
+  constexpr int KS = D / 32, NH = R / 16;
+  const bool is_raw = tile >= tiles_p;
+  const int v0 = is_raw ? (tile - tiles_p) * R : tile * R;
+  const int count = is_raw ? sv.n_raw : sv.n_sel;
+  // base addresses selected as integers (a pointer select from the argument
+  // block otherwise becomes a private-memory lookup)
+  const uintptr_t kbase = is_raw ? reinterpret_cast<uintptr_t>(p.rk) : reinterpret_cast<uintptr_t>(p.pk);
+  const uintptr_t vbase = is_raw ? reinterpret_cast<uintptr_t>(p.rv) : reinterpret_cast<uintptr_t>(p.pv);
 #pragma unroll
-  for (int s = 0; s < KS; ++s)
-    qr[s] = head_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s) : make_uint4(0, 0, 0, 0);
-  if (TREAT) treat_row<D, RD>(qr, (double)sv.t, head_ok, p.eps, p.log2_base);
+  for (int h = 0; h < NH; ++h) {
+    const int v = v0 + 16 * h + n;
+    bool ok = v < count;
+    int64_t row;
+    if (is_raw) {
+      row = kv_raw + v;
+    } else {
+      int64_t e = v;
+      if (p.sel) e = ok ? (int64_t)p.sel[b * p.k_sel + v] : -1;
+      ok = ok && e >= 0 && e < sv.n_pooled;
+      row = kv_pool + e;
+    }
+    const bf16_t* kp = reinterpret_cast<const bf16_t*>(kbase) + row * D + 8 * kq;
+    if (ok) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) T.k[h][s] = *reinterpret_cast<const uint4*>(kp + 32 * s);
+      if constexpr (!SHARED) {
+        const bf16_t* vp = reinterpret_cast<const bf16_t*>(vbase) + row * D + 8 * kq;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) T.v[h][s] = *reinterpret_cast<const uint4*>(vp + 32 * s);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        T.k[h][s] = make_uint4(0, 0, 0, 0);
+        if constexpr (!SHARED) T.v[h][s] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    T.valid[h] = (unsigned)(__ballot(ok) & 0xffffull);
+  }
+}
+
+template <int D, int R, int NW, bool SHARED, int RD, bool TREAT>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
+  constexpr int KS = D / 32, NH = R / 16, DT = D / 16, PITCH = D + 16;
+  constexpr int STAGE = R * PITCH;                   // bf16 elements of one wave's value stage
+  constexpr bool PREFETCH = D <= 128;                // second tile buffer fits in registers
+  constexpr bool PAR_MERGE = NW * 16 * D * 4 <= NW * STAGE * 2;
+  static_assert(NW * STAGE * 2 >= 16 * D * 4, "merge buffer must fit in the stages");
+  __shared__ __attribute__((aligned(16))) bf16_t lds[NW * STAGE];
+  __shared__ float s_ml[NW][16][2];
+  __shared__ float s_w[NW][16];
+  __shared__ float s_M[16], s_L[16], s_inv[16], s_lse[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, kq = lane >> 4;
+  const int split = blockIdx.x;
+  const int hg = (int)(blockIdx.y % (unsigned)p.head_groups);
+  const int64_t kvh = blockIdx.y / (unsigned)p.head_groups;
+  const int64_t b = blockIdx.z;
+  const int64_t unit = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
+  const int slot0 = hg * 16;
+  const int nvalid = (int)(p.G - slot0 < 16 ? p.G - slot0 : 16);
+  const int64_t head0 = kvh * p.G + slot0;  // first query head of the unit
+  const bool head_ok = n < nvalid;
+
+  // queries of this head group as B operands (zero for padded heads); their
+  // addresses do not depend on the position, so they load alongside it
+  uint4 qr[KS];
+  {
+    const bf16_t* qrow = p.q + (b * p.hq + head0 + n) * D + 8 * kq;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qr[s] = head_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s) : make_uint4(0, 0, 0, 0);
+  }
+  const SeqView sv = seq_view(p, b);
+  if (!sv.ok) {  // rows do not fit the buffers: NaN, written once per unit
+    if (split == 0) {
+      for (int i = tid; i < nvalid * D; i += blockDim.x)
+        p.out[(b * p.hq + head0 + i / D) * D + i % D] = __builtin_nanf("");
+      if (p.lse && tid < nvalid) p.lse[b * p.hq + head0 + tid] = __builtin_nanf("");
+    }
+    return;
+  }
+  if constexpr (TREAT) treat_row<D, RD>(qr, (double)sv.t, head_ok, p.eps, p.log2_base);
+
+  const int tiles_p = (sv.n_sel + R - 1) / R;
+  const int tiles_total = tiles_p + (sv.n_raw + R - 1) / R;
+  const int per = (tiles_total + p.splits - 1) / p.splits;
+  const int t0 = split * per;
+  const int t1 = t0 + per < tiles_total ? t0 + per : tiles_total;
+  const int64_t kv_pool = (b * p.hkv + kvh) * p.entries;
+  const int64_t kv_raw = (b * p.hkv + kvh) * p.raw_rows + sv.raw_row0;
 
   float m_run = kNegInf, l_run = 0.f;
   f32x4 acc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16_t* vt = lds + wave * STAGE;
+  // transposing-read base of this lane: row 4*kq + n/4, column 4*(n%4)
+  const bf16_t* trb = vt + (4 * kq + (n >> 2)) * PITCH + 4 * (n & 3);
 
-  const int64_t kv_pool = (b * p.hkv + kvh) * p.entries;
-  const int64_t kv_raw = (b * p.hkv + kvh) * p.raw_rows + sv.raw_row0;
-
-  for (int64_t tile = t0; tile < t1; ++tile) {
-    const bool is_raw = tile >= tiles_p;
-    const int64_t v0 = is_raw ? (tile - tiles_p) * R : tile * R;
-    const int64_t count = is_raw ? sv.n_raw : sv.n_sel;
-    uint4 kr[NH][KS];
-    uint4 vr[SHARED ? 1 : NH][SHARED ? 1 : KS];
-    unsigned valid[NH];
+  auto process = [&](Tile<D, R, SHARED>& T, int tile) {
+    if constexpr (TREAT) {
+      if (tile >= tiles_p) {
+        const int v0 = (tile - tiles_p) * R;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      const int64_t v = v0 + 16 * h + n;
-      bool ok = v < count;
-      int64_t row = 0;
-      if (is_raw) {
-        row = kv_raw + v;
-      } else {
-        int64_t e = v;
-        if (p.sel) e = ok ? (int64_t)p.sel[b * p.k_sel + v] : -1;
-        ok = ok && e >= 0 && e < sv.n_pooled;
-        row = kv_pool + e;
+        for (int h = 0; h < NH; ++h)
+          treat_row<D, RD>(T.k[h], (double)(sv.raw_begin + v0 + 16 * h + n), (T.valid[h] >> n) & 1u,
+                           p.eps, p.log2_base);
       }
-      const bf16_t* kp = (is_raw ? p.rk : p.pk) + row * D + 8 * kq;
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        kr[h][s] = ok ? *reinterpret_cast<const uint4*>(kp + 32 * s) : make_uint4(0, 0, 0, 0);
-      if (!SHARED) {
-        const bf16_t* vp = (is_raw ? p.rv : p.pv) + row * D + 8 * kq;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          vr[h][s] = ok ? *reinterpret_cast<const uint4*>(vp + 32 * s) : make_uint4(0, 0, 0, 0);
-      }
-      if (TREAT && is_raw) treat_row<D, RD>(kr[h], (double)(sv.raw_begin + v), ok, p.eps, p.log2_base);
-      valid[h] = (unsigned)(__ballot(ok) & 0xffffull);
     }
-    // value rows to LDS (row-major) for the transposed A-operand gather
+    // value rows to this wave's LDS stage (row-major)
+    wave_lds_sync();
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        *reinterpret_cast<uint4*>(&vtile[(16 * h + n) * PITCH + 32 * s + 8 * kq]) =
-            SHARED ? kr[h][s] : vr[h][s];
-
-    // S^T = K Q^T (16 rows x 16 heads per half)
+        *reinterpret_cast<uint4*>(&vt[(16 * h + n) * PITCH + 32 * s + 8 * kq]) =
+            SHARED ? T.k[h][s] : T.v[h][s];
+    // S^T = K Q^T, 16 rows x 16 heads per half
     float sc[NH][4];
     float tmax = kNegInf;
 #pragma unroll
@@ -228,20 +298,20 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[h][s]),
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T.k[h][s]),
                                                      __builtin_bit_cast(bf16x8, qr[s]), c, 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bool vok = (valid[h] >> (4 * kq + j)) & 1u;
+        const bool vok = (T.valid[h] >> (4 * kq + j)) & 1u;
         sc[h][j] = vok ? c[j] * p.scale_log2 : kNegInf;
         tmax = fmaxf(tmax, sc[h][j]);
       }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = xor16_max(tmax);
+    tmax = xor32_max(tmax);
     const float nm = fmaxf(m_run, tmax);
     const float mu = nm == kNegInf ? 0.f : nm;
-    const float corr = exp2f(m_run - mu);
+    const float corr = fast_exp2(m_run - mu);
     float psum = 0.f;
     s16x4 pop[NH];
 #pragma unroll
@@ -249,309 +319,295 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
       float pj[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        pj[j] = exp2f(sc[h][j] - mu);
+        pj[j] = fast_exp2(sc[h][j] - mu);
         psum += pj[j];
       }
       const uint32_t w0 = pack_bf16x2(pj[0], pj[1]), w1 = pack_bf16x2(pj[2], pj[3]);
       pop[h] = s16x4{(short)(w0 & 0xffff), (short)(w0 >> 16), (short)(w1 & 0xffff), (short)(w1 >> 16)};
     }
     l_run = fmaf(l_run, corr, psum);
+    if (__ballot(corr != 1.f)) {  // some head's running max moved
 #pragma unroll
-    for (int t = 0; t < DT; ++t) acc[t] *= corr;
+      for (int t = 0; t < DT; ++t) acc[t] *= corr;
+    }
     m_run = nm;
-    __syncthreads();
-    // O^T += V^T P^T
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      const bf16_t* vb = &vtile[(16 * h + 4 * kq) * PITCH + n];
+    wave_lds_sync();
+    // O^T += V^T P^T.  With two 16-row halves the k=32 MFMA takes this lane's 8
+    // probabilities (rows 4kq+j of both halves) as its B operand and two
+    // transposing reads (the same rows of one dim) as its A operand.
+    if constexpr (NH == 2) {
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(
+          (uint16_t)pop[0][0] | ((uint32_t)(uint16_t)pop[0][1] << 16),
+          (uint16_t)pop[0][2] | ((uint32_t)(uint16_t)pop[0][3] << 16),
+          (uint16_t)pop[1][0] | ((uint32_t)(uint16_t)pop[1][1] << 16),
+          (uint16_t)pop[1][2] | ((uint32_t)(uint16_t)pop[1][3] << 16)));
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        s16x4 a;
-        a[0] = (short)vb[16 * t].bits;
-        a[1] = (short)vb[PITCH + 16 * t].bits;
-        a[2] = (short)vb[2 * PITCH + 16 * t].bits;
-        a[3] = (short)vb[3 * PITCH + 16 * t].bits;
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pop[h], acc[t], 0, 0, 0);
+        const s16x4 a0 = lds_read_tr16(trb + 16 * t), a1 = lds_read_tr16(trb + 16 * PITCH + 16 * t);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, s16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc[t], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr16(trb + 16 * h * PITCH + 16 * t),
+                                                              pop[h], acc[t], 0, 0, 0);
+    }
+  };
+
+  int tile = t0 + wave;
+  if constexpr (PREFETCH) {
+    if (tile < t1) {
+      Tile<D, R, SHARED> ta, tb;
+      load_tile<D, R, SHARED>(ta, p, sv, b, kv_pool, kv_raw, tiles_p, tile, n, kq);
+      while (true) {  // two buffers used in turn: no register copies between tiles
+        int nt = tile + NW;
+        if (nt < t1) load_tile<D, R, SHARED>(tb, p, sv, b, kv_pool, kv_raw, tiles_p, nt, n, kq);
+        process(ta, tile);
+        if (nt >= t1) break;
+        tile = nt;
+        nt = tile + NW;
+        if (nt < t1) load_tile<D, R, SHARED>(ta, p, sv, b, kv_pool, kv_raw, tiles_p, nt, n, kq);
+        process(tb, tile);
+        if (nt >= t1) break;
+        tile = nt;
       }
     }
-    __syncthreads();
+  } else {
+    Tile<D, R, SHARED> tt;
+    for (; tile < t1; tile += NW) {
+      load_tile<D, R, SHARED>(tt, p, sv, b, kv_pool, kv_raw, tiles_p, tile, n, kq);
+      process(tt, tile);
+    }
   }
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run = xor16_sum(l_run);
+  l_run = xor32_sum(l_run);
 
-  if (head_ok) {
-    const int64_t wg = blockIdx.x;
-    float* dst = p.ws_acc + (wg * 16 + n) * D + 4 * kq;
+  // ---- merge the NW waves (fixed order) ----
+  if (kq == 0) {
+    s_ml[wave][n][0] = m_run;
+    s_ml[wave][n][1] = l_run;
+  }
+  __syncthreads();  // every wave is done with its stage: the LDS is free
+  if (tid < 16) {
+    float M = kNegInf;
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
-      *reinterpret_cast<float4*>(dst + 16 * t) = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
-    if (kq == 0) {
-      p.ws_ml[(wg * 16 + n) * 2] = m_run;
-      p.ws_ml[(wg * 16 + n) * 2 + 1] = l_run;
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][tid][0]);
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float sw = s_ml[w][tid][0] == kNegInf ? 0.f : fast_exp2(s_ml[w][tid][0] - M);
+      s_w[w][tid] = sw;
+      L = fmaf(s_ml[w][tid][1], sw, L);
     }
-  }
-}
-
-// Combine the splits of one (sequence, query head): fixed order, then sink,
-// normalisation, LSE and the -t rotation of the last rope_dims dims.
-__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
-  __shared__ float orow[512];
-  const int64_t bh = blockIdx.x;
-  const int64_t b = bh / p.hq, h = bh % p.hq;
-  const int64_t kvh = h / p.G, g = h % p.G;
-  const int64_t hg = g / 16, n = g % 16;
-  const int D = p.dim;
-  const SeqView sv = seq_view(p, b);
-  float* out = p.out + bh * D;
-  if (!sv.ok) {
-    for (int d = threadIdx.x; d < D; d += blockDim.x) out[d] = __builtin_nanf("");
-    if (threadIdx.x == 0 && p.lse) p.lse[bh] = __builtin_nanf("");
-    return;
-  }
-  const int64_t wg0 = ((b * p.hkv + kvh) * p.head_groups + hg) * p.splits;
-  float M = kNegInf;
-  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.ws_ml[((wg0 + s) * 16 + n) * 2]);
-  float L = 0.f;
-  for (int s = 0; s < p.splits; ++s) {
-    const float* ml = p.ws_ml + ((wg0 + s) * 16 + n) * 2;
-    L += ml[1] * exp2f(ml[0] - M);
-  }
-  if (p.sink) L += exp2f(p.sink[h] * kLog2e - M);
-  const float invL = 1.f / L;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float o = 0.f;
-    for (int s = 0; s < p.splits; ++s) {
-      const float w = exp2f(p.ws_ml[((wg0 + s) * 16 + n) * 2] - M);
-      o = fmaf(p.ws_acc[((wg0 + s) * 16 + n) * D + d], w, o);
-    }
-    orow[d] = o * invL;
+    s_M[tid] = M;
+    s_L[tid] = L;
   }
   __syncthreads();
-  const int r = p.rope_dims, half = r / 2;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float o = orow[d];
-    if (r > 0 && d >= D - r) {
-      const bool lo = d < D - half;
-      const int k = lo ? d - (D - r) : d - (D - half);
+  float* buf = reinterpret_cast<float*>(lds);
+  if constexpr (PAR_MERGE) {  // every wave writes its scaled acc to its own slice
+    if (head_ok) {
+      const float sw = s_w[wave][n];
+      float* dst = buf + (wave * 16 + n) * D + 4 * kq;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+        *reinterpret_cast<float4*>(dst + 16 * t) =
+            make_float4(acc[t][0] * sw, acc[t][1] * sw, acc[t][2] * sw, acc[t][3] * sw);
+    }
+    __syncthreads();
+  } else {  // accumulate into one buffer, wave after wave
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (wave == w && head_ok) {
+        const float sw = s_w[w][n];
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          float4* dst = reinterpret_cast<float4*>(&buf[n * D + 16 * t + 4 * kq]);
+          float4 v = make_float4(acc[t][0] * sw, acc[t][1] * sw, acc[t][2] * sw, acc[t][3] * sw);
+          if (w > 0) {
+            const float4 o = *dst;
+            v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+          }
+          *dst = v;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  auto merged = [&](int sl, int d) {  // combined unnormalised acc of slot sl, dim d
+    if constexpr (PAR_MERGE) {
+      float o = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) o += buf[(w * 16 + sl) * D + d];
+      return o;
+    } else {
+      return buf[sl * D + d];
+    }
+  };
+
+  constexpr int r = RD, half = RD / 2;
+  if (p.splits == 1) {
+    if (tid < nvalid) {
+      float L = s_L[tid];
+      const float M = s_M[tid];
+      if (p.sink) L += exp2f(p.sink[head0 + tid] * kLog2e - M);
+      s_inv[tid] = 1.f / L;
+      s_lse[tid] = (M + log2f(L)) * 0.69314718055994531f;
+    }
+    __syncthreads();
+    const int items = nvalid * (D - half);  // plain dims, then rotate-half pairs
+    for (int i = tid; i < items; i += blockDim.x) {
+      const int sl = i / (D - half), d = i % (D - half);
+      float* o = p.out + (b * p.hq + head0 + sl) * D;
+      const float inv = s_inv[sl];
+      if (d < D - r) {
+        o[d] = merged(sl, d) * inv;
+      } else if constexpr (RD > 0) {
+        const int k = d - (D - r);
+        const float x1 = merged(sl, d) * inv, x2 = merged(sl, d + half) * inv;
+        float c, sn;
+        rope_cos_sin(-(double)sv.t, k, r, p.log2_base, &c, &sn);
+        o[d] = x1 * c - x2 * sn;
+        o[d + half] = x2 * c + x1 * sn;
+      }
+    }
+    if (p.lse && tid < nvalid) p.lse[b * p.hq + head0 + tid] = s_lse[tid];
+    return;
+  }
+  // ---- split partial to the workspace; decode_merge_kernel combines the splits ----
+  const int64_t part = unit * p.splits + split;
+  for (int i = tid; i < nvalid * D; i += blockDim.x)
+    p.ws_acc[(part * 16) * D + i] = merged(i / D, i % D);
+  if (tid < nvalid) {
+    p.ws_ml[(part * 16 + tid) * 2] = s_M[tid];
+    p.ws_ml[(part * 16 + tid) * 2 + 1] = s_L[tid];
+  }
+}
+
+// Combine the splits of one unit (16 query-head slots): every split's partial
+// is loaded at once (no dependent chain), weights exp2(m_s - M) in a fixed
+// order, then sink, normalisation, LSE and the -t rotation.
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D) {
+  __shared__ float s_m[64][16], s_l[64][16];
+  __shared__ float s_w[64][16];
+  __shared__ float s_inv[16], s_lse[16];
+  const int tid = threadIdx.x;
+  const int64_t unit = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const int hg = (int)(blockIdx.x % (unsigned)p.head_groups);
+  const int64_t kvh = blockIdx.x / (unsigned)p.head_groups;
+  const int64_t b = blockIdx.y;
+  const int slot0 = hg * 16;
+  const int nvalid = (int)(p.G - slot0 < 16 ? p.G - slot0 : 16);
+  const int64_t head0 = kvh * p.G + slot0;
+  const SeqView sv = seq_view(p, b);
+  if (!sv.ok) return;  // the decode kernel already wrote NaN for this unit
+  const int S = p.splits;
+  const int64_t part0 = unit * S;
+  for (int i = tid; i < S * 16; i += blockDim.x) {
+    const int s = i >> 4, slot = i & 15;
+    if (slot < nvalid) {
+      s_m[s][slot] = p.ws_ml[((part0 + s) * 16 + slot) * 2];
+      s_l[s][slot] = p.ws_ml[((part0 + s) * 16 + slot) * 2 + 1];
+    }
+  }
+  __syncthreads();
+  if (tid < nvalid) {
+    float M = kNegInf;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, s_m[s][tid]);
+    float L = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float sw = s_m[s][tid] == kNegInf ? 0.f : exp2f(s_m[s][tid] - M);
+      s_w[s][tid] = sw;
+      L = fmaf(s_l[s][tid], sw, L);
+    }
+    if (p.sink) L += exp2f(p.sink[head0 + tid] * kLog2e - M);
+    s_inv[tid] = 1.f / L;
+    s_lse[tid] = (M + log2f(L)) * 0.69314718055994531f;
+  }
+  __syncthreads();
+  const float* pa = p.ws_acc + part0 * 16 * D;
+  auto combined = [&](int sl, int d) {
+    float o = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < S; ++s) o = fmaf(pa[(s * 16 + sl) * D + d], s_w[s][sl], o);
+    return o * s_inv[sl];
+  };
+  const int r = p.rope_dims, half = r >> 1;
+  const int items = nvalid * (D - half);
+  for (int i = tid; i < items; i += blockDim.x) {
+    const int sl = i / (D - half), d = i % (D - half);
+    float* o = p.out + (b * p.hq + head0 + sl) * D;
+    if (d < D - r) {
+      o[d] = combined(sl, d);
+    } else {
+      const int k = d - (D - r);
+      const float x1 = combined(sl, d), x2 = combined(sl, d + half);
       float c, sn;
       rope_cos_sin(-(double)sv.t, k, r, p.log2_base, &c, &sn);
-      const float other = lo ? orow[d + half] : orow[d - half];
-      o = lo ? o * c - other * sn : o * c + other * sn;
+      o[d] = x1 * c - x2 * sn;
+      o[d + half] = x2 * c + x1 * sn;
     }
-    out[d] = o;
   }
-  if (threadIdx.x == 0 && p.lse) p.lse[bh] = (M + log2f(L)) * 0.69314718055994531f;
-}
-
-// ---------------------------------------------------------------------------
-// fp32 path: one wave per (sequence, query, head); decode and prefill.
-struct RowsParams {
-  const float* q;
-  const float* pk;
-  const float* pv;
-  const float* rk;
-  const float* rv;
-  const int64_t* pos;      // device positions (decode) or null
-  int64_t q_pos0;          // first query position (prefill)
-  const int64_t* rpb_dev;  // device raw_pos_base (decode) or null
-  int64_t rpb_host;
-  const int32_t* sel;
-  const float* sink;
-  void* out;
-  int out_bf16;
-  float* lse;
-  int64_t q_len, hq, hkv, G, entries, raw_rows, k_sel, m, W;
-  int mode;
-  float scale;
-};
-
-template <int D>
-__global__ __launch_bounds__(64) void rows_f32_kernel(RowsParams p) {
-  constexpr int DPL = D / 64;
-  __shared__ float qs[D];
-  const int lane = threadIdx.x;
-  const int64_t id = blockIdx.x;  // ((b * q_len + i) * hq + h)
-  const int64_t h = id % p.hq;
-  const int64_t bi = id / p.hq;
-  const int64_t i = bi % p.q_len;
-  const int64_t b = bi / p.q_len;
-  const int64_t kvh = h / p.G;
-  const int64_t t = p.pos ? p.pos[b] : p.q_pos0 + i;
-  const int64_t base = p.rpb_dev ? p.rpb_dev[b] : p.rpb_host;
-  int64_t np = 0, rb = 0;
-  bool ok = t >= 0;
-  if (ok) visible_range(t, p.m, p.W, p.mode, &np, &rb);
-  ok = ok && np <= p.entries && rb - base >= 0 && t - base < p.raw_rows;
-  float o[DPL];
-  const int64_t orow = id * D + lane * DPL;
-  if (!ok) {
-    for (int c = 0; c < DPL; ++c) o[c] = __builtin_nanf("");
-  } else {
-    const float* qrow = p.q + id * D;
-    for (int d = lane; d < D; d += 64) qs[d] = qrow[d];
-    __syncthreads();
-    const int64_t n_sel = p.sel ? p.k_sel : np;
-    const int64_t n_raw = t - rb + 1;
-    const int64_t n_tot = n_sel + n_raw;
-    const int64_t kv_pool = (b * p.hkv + kvh) * p.entries;
-    const int64_t kv_raw = (b * p.hkv + kvh) * p.raw_rows + (rb - base);
-    const float* vpool = p.pv ? p.pv : p.pk;
-    const float* vraw = p.rv ? p.rv : p.rk;
-    float m_run = kNegInf, l_run = 0.f;
-    for (int c = 0; c < DPL; ++c) o[c] = 0.f;
-    for (int64_t g0 = 0; g0 < n_tot; g0 += 64) {
-      // each lane scores one row
-      const int64_t v = g0 + lane;
-      bool rok = v < n_tot;
-      const float* krow = nullptr;
-      if (rok) {
-        if (v < n_sel) {
-          const int64_t e = p.sel ? (int64_t)p.sel[b * p.k_sel + v] : v;
-          rok = e >= 0 && e < np;
-          krow = p.pk + (kv_pool + e) * D;
-        } else {
-          krow = p.rk + (kv_raw + (v - n_sel)) * D;
-        }
-      }
-      float s = kNegInf;
-      if (rok) {
-        float dot = 0.f;
-        for (int d = 0; d < D; d += 4) {
-          const float4 k4 = *reinterpret_cast<const float4*>(krow + d);
-          dot = fmaf(qs[d], k4.x, dot);
-          dot = fmaf(qs[d + 1], k4.y, dot);
-          dot = fmaf(qs[d + 2], k4.z, dot);
-          dot = fmaf(qs[d + 3], k4.w, dot);
-        }
-        s = dot * p.scale;
-      }
-      const float gmax = group_max<64>(s);
-      const float nm = fmaxf(m_run, gmax);
-      const float mu = nm == kNegInf ? 0.f : nm;
-      const float corr = expf(m_run - mu);
-      const float pr = expf(s - mu);
-      l_run = l_run * corr + group_sum<64>(pr);
-      for (int c = 0; c < DPL; ++c) o[c] *= corr;
-      m_run = nm;
-      const int cnt = (int)(n_tot - g0 < 64 ? n_tot - g0 : 64);
-      for (int r = 0; r < cnt; ++r) {
-        const float pw = __shfl(pr, r, 64);
-        if (pw == 0.f) continue;  // masked row (uniform across the wave)
-        const int64_t vv = g0 + r;
-        const float* vrow;
-        if (vv < n_sel) {
-          const int64_t e = p.sel ? (int64_t)p.sel[b * p.k_sel + vv] : vv;
-          vrow = vpool + (kv_pool + e) * D;
-        } else {
-          vrow = vraw + (kv_raw + (vv - n_sel)) * D;
-        }
-        for (int c = 0; c < DPL; ++c) o[c] = fmaf(pw, vrow[lane * DPL + c], o[c]);
-      }
-    }
-    float den = l_run;
-    if (p.sink) den += expf(p.sink[h] - m_run);
-    const float inv = 1.f / den;
-    for (int c = 0; c < DPL; ++c) o[c] *= inv;
-    if (lane == 0 && p.lse) p.lse[id] = m_run + logf(den);
-  }
-  if (!ok && lane == 0 && p.lse) p.lse[id] = __builtin_nanf("");
-  if (p.out_bf16) {
-    bf16_t* out = static_cast<bf16_t*>(p.out) + orow;
-    for (int c = 0; c < DPL; ++c) out[c].bits = (uint16_t)(pack_bf16x2(o[c], 0.f) & 0xffff);
-  } else {
-    float* out = static_cast<float*>(p.out) + orow;
-    for (int c = 0; c < DPL; ++c) out[c] = o[c];
-  }
-}
-
-hipError_t launch_rows_f32(const RowsParams& rp, int64_t dim, int64_t batch, hipStream_t s) {
-  const dim3 grid((unsigned)(batch * rp.q_len * rp.hq));
-  switch (dim) {
-    case 64: rows_f32_kernel<64><<<grid, 64, 0, s>>>(rp); break;
-    case 128: rows_f32_kernel<128><<<grid, 64, 0, s>>>(rp); break;
-    case 192: rows_f32_kernel<192><<<grid, 64, 0, s>>>(rp); break;
-    case 256: rows_f32_kernel<256><<<grid, 64, 0, s>>>(rp); break;
-    case 320: rows_f32_kernel<320><<<grid, 64, 0, s>>>(rp); break;
-    case 384: rows_f32_kernel<384><<<grid, 64, 0, s>>>(rp); break;
-    case 448: rows_f32_kernel<448><<<grid, 64, 0, s>>>(rp); break;
-    case 512: rows_f32_kernel<512><<<grid, 64, 0, s>>>(rp); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_prefill_f32(const lbca_prefill_args& a, hipStream_t stream) {
-  RowsParams rp{};
-  rp.q = static_cast<const float*>(a.q);
-  rp.pk = static_cast<const float*>(a.pooled_k);
-  rp.pv = static_cast<const float*>(a.pooled_v);
-  rp.rk = static_cast<const float*>(a.raw_k);
-  rp.rv = static_cast<const float*>(a.raw_v);
-  rp.pos = nullptr;
-  rp.q_pos0 = a.q_pos0;
-  rp.rpb_dev = nullptr;
-  rp.rpb_host = a.raw_pos_base;
-  rp.sel = nullptr;
-  rp.sink = a.sink;
-  rp.out = a.out;
-  rp.out_bf16 = a.out_dtype == LBCA_BF16;
-  rp.lse = a.lse;
-  rp.q_len = a.q_len;
-  rp.hq = a.q_heads; rp.hkv = a.kv_heads; rp.G = a.q_heads / a.kv_heads;
-  rp.entries = a.entries; rp.raw_rows = a.raw_rows; rp.k_sel = 0;
-  rp.m = a.block; rp.W = a.window; rp.mode = a.mode; rp.scale = a.scale;
-  return launch_rows_f32(rp, a.dim, a.batch, stream);
+  if (p.lse && tid < nvalid) p.lse[b * p.hq + head0 + tid] = s_lse[tid];
 }
 
 // ---------------------------------------------------------------------------
 static int rows_per_tile(int64_t dim) { return dim >= 512 ? 16 : 32; }
+static int waves_per_wg(int64_t dim) { return dim <= 128 ? 8 : 4; }
 
 DecodePlan plan_decode(const lbca_decode_args& a) {
   DecodePlan pl{};
-  if (a.dtype != LBCA_BF16) {
-    pl.tile_rows = 64;
-    pl.head_groups = 1;
-    pl.splits = 1;
-    pl.ws_bytes = 0;
-    return pl;
-  }
+  if (a.dtype != LBCA_BF16) return pl;  // fp32 path needs no workspace
   const int64_t G = a.q_heads / a.kv_heads;
   pl.tile_rows = rows_per_tile(a.dim);
   pl.head_groups = (int)((G + 15) / 16);
-  // Upper bound of visible rows from the buffer capacities.
+  const int nw = waves_per_wg(a.dim);
+  // upper bound of the visible-row list from the buffer capacities
   const int64_t sel_max = a.sel_idx ? a.k_sel : a.entries;
   const int64_t raw_span = a.mode == LBCA_EXCLUSIVE ? a.window + a.block - 1 : a.window;
   const int64_t raw_max = raw_span < a.raw_rows ? raw_span : a.raw_rows;
+  const int64_t rows = sel_max + raw_max;
   const int64_t tiles = (sel_max + pl.tile_rows - 1) / pl.tile_rows + (raw_max + pl.tile_rows - 1) / pl.tile_rows;
-  // Aim for ~4 waves per CU over 256 CUs, never more splits than tiles.
   const int64_t units = a.batch * a.kv_heads * pl.head_groups;
-  int64_t splits = units > 0 ? (1024 + units - 1) / units : 1;
-  if (splits > tiles) splits = tiles;
-  if (splits < 1) splits = 1;
-  pl.splits = (int)splits;
-  const size_t wgs = (size_t)(units > 0 ? units : 1) * (size_t)splits;
-  pl.ws_bytes = wgs * 16 * (size_t)a.dim * sizeof(float) + wgs * 16 * 2 * sizeof(float);
+  // waves per unit: enough for ~LBCA_DECODE_TARGET_WAVES in total, never more
+  // than there are tiles; split partials (16 heads x dim fp32 per workgroup, for
+  // every head group of a KV head) kept under a quarter of the K/V bytes.
+  int64_t wpu = units > 0 ? (LBCA_DECODE_TARGET_WAVES + units - 1) / units : 1;
+  if (wpu > tiles) wpu = tiles;
+  int64_t s = (wpu + nw - 1) / nw;
+  const int64_t kv_bytes = rows * a.dim * 2 * (a.pooled_v ? 2 : 1);
+  const int64_t part_bytes = (int64_t)pl.head_groups * 16 * (a.dim + 2) * 4;
+  const int64_t by_traffic = kv_bytes / (4 * part_bytes) > 0 ? kv_bytes / (4 * part_bytes) : 1;
+  if (s > by_traffic) s = by_traffic;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  pl.splits = (int)s;
+  if (s == 1) return pl;
+  const size_t u = (size_t)units;
+  pl.ws_bytes = u * s * 16 * 2 * sizeof(float) + u * s * 16 * (size_t)a.dim * sizeof(float);
   return pl;
 }
 
-template <int D, int R>
-static hipError_t launch_partial_d(const DecodeParams& p, bool shared, int rd, bool treat, dim3 g,
-                                   hipStream_t s) {
+template <int D, int R, int NW>
+static hipError_t launch_d(const DecodeParams& p, bool shared, int rd, bool treat, dim3 g,
+                           hipStream_t s) {
+  const dim3 blk(NW * 64);
   if (!treat) {
-    if (shared) decode_partial_kernel<D, R, true, 0, false><<<g, 64, 0, s>>>(p);
-    else decode_partial_kernel<D, R, false, 0, false><<<g, 64, 0, s>>>(p);
+    if (shared) decode_kernel<D, R, NW, true, 0, false><<<g, blk, 0, s>>>(p);
+    else decode_kernel<D, R, NW, false, 0, false><<<g, blk, 0, s>>>(p);
     return hipGetLastError();
   }
   if (!shared) return hipErrorInvalidValue;
   switch (rd) {
-    case 0: decode_partial_kernel<D, R, true, 0, true><<<g, 64, 0, s>>>(p); break;
+    case 0: decode_kernel<D, R, NW, true, 0, true><<<g, blk, 0, s>>>(p); break;
     case 64:
-      if (D < 64) return hipErrorInvalidValue;
-      decode_partial_kernel<D, R, true, (D >= 64 ? 64 : 0), true><<<g, 64, 0, s>>>(p);
+      if constexpr (D >= 64) decode_kernel<D, R, NW, true, 64, true><<<g, blk, 0, s>>>(p);
       break;
     case 128:
-      if (D < 128) return hipErrorInvalidValue;
-      decode_partial_kernel<D, R, true, (D >= 128 ? 128 : 0), true><<<g, 64, 0, s>>>(p);
+      if constexpr (D >= 128) decode_kernel<D, R, NW, true, 128, true><<<g, blk, 0, s>>>(p);
+      else return hipErrorInvalidValue;
       break;
     default: return hipErrorInvalidValue;
   }
@@ -560,29 +616,8 @@ static hipError_t launch_partial_d(const DecodeParams& p, bool shared, int rd, b
 
 hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void* ws,
                          hipStream_t stream) {
+  if (a.dtype != LBCA_BF16) return launch_decode_f32(a, stream);
   const int64_t G = a.q_heads / a.kv_heads;
-  if (a.dtype != LBCA_BF16) {
-    RowsParams rp{};
-    rp.q = static_cast<const float*>(a.q);
-    rp.pk = static_cast<const float*>(a.pooled_k);
-    rp.pv = static_cast<const float*>(a.pooled_v);
-    rp.rk = static_cast<const float*>(a.raw_k);
-    rp.rv = static_cast<const float*>(a.raw_v);
-    rp.pos = a.pos;
-    rp.q_pos0 = 0;
-    rp.rpb_dev = a.raw_pos_base;
-    rp.rpb_host = 0;
-    rp.sel = a.sel_idx;
-    rp.sink = a.sink;
-    rp.out = a.out;
-    rp.out_bf16 = 0;
-    rp.lse = a.lse;
-    rp.q_len = 1;
-    rp.hq = a.q_heads; rp.hkv = a.kv_heads; rp.G = G;
-    rp.entries = a.entries; rp.raw_rows = a.raw_rows; rp.k_sel = a.sel_idx ? a.k_sel : 0;
-    rp.m = a.block; rp.W = a.window; rp.mode = a.mode; rp.scale = a.scale;
-    return launch_rows_f32(rp, a.dim, a.batch, stream);
-  }
   DecodeParams p{};
   p.q = static_cast<const bf16_t*>(a.q);
   p.pk = static_cast<const bf16_t*>(a.pooled_k);
@@ -591,30 +626,33 @@ hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void
   p.rv = static_cast<const bf16_t*>(a.raw_v);
   p.pos = a.pos; p.rpb = a.raw_pos_base; p.sel = a.sel_idx; p.sink = a.sink;
   p.out = a.out; p.lse = a.lse;
-  const size_t wgs = (size_t)a.batch * a.kv_heads * plan.head_groups * plan.splits;
-  p.ws_acc = static_cast<float*>(ws);
-  p.ws_ml = static_cast<float*>(ws) + wgs * 16 * a.dim;
+  const size_t units = (size_t)a.batch * a.kv_heads * plan.head_groups;
+  if (plan.splits > 1) {
+    p.ws_ml = static_cast<float*>(ws);
+    p.ws_acc = p.ws_ml + units * plan.splits * 16 * 2;
+  }
   p.hq = a.q_heads; p.hkv = a.kv_heads; p.G = G;
   p.entries = a.entries; p.raw_rows = a.raw_rows; p.k_sel = a.sel_idx ? a.k_sel : 0;
   p.m = a.block; p.W = a.window; p.mode = a.mode;
-  p.splits = plan.splits; p.head_groups = plan.head_groups; p.dim = (int)a.dim;
+  p.splits = plan.splits; p.head_groups = plan.head_groups;
   p.scale_log2 = a.scale * kLog2e;
   p.eps = a.rmsnorm_eps;
   p.rope_dims = a.rope_dims;
   p.log2_base = a.rope_dims > 0 ? log2((double)a.rope_base) : 0.0;
   const bool shared = a.pooled_v == nullptr;
   const bool treat = a.rmsnorm_eps >= 0.f || a.rope_dims > 0;
-  const dim3 g((unsigned)wgs);
+  const dim3 g((unsigned)plan.splits, (unsigned)(a.kv_heads * plan.head_groups), (unsigned)a.batch);
   hipError_t e;
   switch (a.dim) {
-    case 64: e = launch_partial_d<64, 32>(p, shared, a.rope_dims, treat, g, stream); break;
-    case 128: e = launch_partial_d<128, 32>(p, shared, a.rope_dims, treat, g, stream); break;
-    case 256: e = launch_partial_d<256, 32>(p, shared, a.rope_dims, treat, g, stream); break;
-    case 512: e = launch_partial_d<512, 16>(p, shared, a.rope_dims, treat, g, stream); break;
+    case 64: e = launch_d<64, 32, 8>(p, shared, a.rope_dims, treat, g, stream); break;
+    case 128: e = launch_d<128, 32, 8>(p, shared, a.rope_dims, treat, g, stream); break;
+    case 256: e = launch_d<256, 32, 4>(p, shared, a.rope_dims, treat, g, stream); break;
+    case 512: e = launch_d<512, 16, 4>(p, shared, a.rope_dims, treat, g, stream); break;
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess) return e;
-  decode_merge_kernel<<<dim3((unsigned)(a.batch * a.q_heads)), 128, 0, stream>>>(p);
+  if (e != hipSuccess || plan.splits == 1) return e;
+  decode_merge_kernel<<<dim3((unsigned)(a.kv_heads * plan.head_groups), (unsigned)a.batch), 256, 0,
+                        stream>>>(p, (int)a.dim);
   return hipGetLastError();
 }
 

@@ -47,17 +47,17 @@ __device__ __forceinline__ void store8(bf16_t* p, const float* f) {
   *reinterpret_cast<uint4*>(p) = u;
 }
 
-// Rotation angle pos * base^(-2k/r), reduced to [-pi, pi] in double precision so
-// that positions up to 2^40 keep fp32-accurate sines; returns cos and sin.
+// Rotation angle pos * base^(-2k/r) in turns (angle / 2pi), reduced to
+// [-1/2, 1/2] in double precision so that positions up to 2^40 keep an exact
+// phase; the hardware sine/cosine (argument in turns) then act on the small
+// reduced value.  Returns cos and sin.
 __device__ __forceinline__ void rope_cos_sin(double pos, int k, int r, double log2_base, float* c,
                                              float* s) {
-  const double two_pi = 6.283185307179586476925286766559;
-  double theta = exp2(-(2.0 * (double)k / (double)r) * log2_base);
-  double a = pos * theta;
-  a -= rint(a * (1.0 / two_pi)) * two_pi;
-  float af = (float)a;
-  *c = cosf(af);
-  *s = sinf(af);
+  const double inv_two_pi = 0.15915494309189533576888376337251;
+  const double turns = pos * exp2(-(2.0 * (double)k / (double)r) * log2_base) * inv_two_pi;
+  const float f = (float)(turns - rint(turns));
+  *c = __builtin_amdgcn_cosf(f);
+  *s = __builtin_amdgcn_sinf(f);
 }
 
 template <int WIDTH>
@@ -73,18 +73,63 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// a / b for a >= 0, b >= 1: 32-bit division when both fit (the 64-bit one is a
+// long software sequence on this ISA).
+__device__ __forceinline__ int64_t div_nonneg(int64_t a, int64_t b) {
+  if (((a | b) >> 31) == 0) return (int64_t)((uint32_t)a / (uint32_t)b);
+  return a / b;
+}
+
 // Visibility rule on the device (same definition as lbca_visible_range).
 __device__ __forceinline__ void visible_range(int64_t t, int64_t m, int64_t W, int mode,
                                               int64_t* n_pooled, int64_t* raw_begin) {
   if (mode == 0) {
     int64_t x = t + 1 - W;
-    *n_pooled = x > 0 ? x / m : 0;
+    *n_pooled = x > 0 ? div_nonneg(x, m) : 0;
     *raw_begin = *n_pooled * m;
   } else {
-    *n_pooled = (t + 1) / m;
+    *n_pooled = div_nonneg(t + 1, m);
     int64_t rb = t - W + 1;
     *raw_begin = rb > 0 ? rb : 0;
   }
+}
+
+// Cross-row reductions with the gfx950 lane swaps: after a 32-lane (16-lane)
+// swap of x with itself, the two results hold x[l] and x[l^32] (x[l^16]) in
+// some order on every lane.
+__device__ __forceinline__ float xor32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 2^x on the hardware exp unit (inputs here are <= 0 or -inf; results that
+// would be denormal flush to zero, which only drops weights below 2^-126).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ds_read_b64_tr_b16: in each 16-lane group the lanes' 8-byte chunks form 64
+// elements in source order e = 4*lane + i; lane i receives e = i, 16+i, 32+i,
+// 48+i.  With lane (j, g) pointing at row 4g + j/4, column c0 + 4*(j%4) of a
+// row-major tile, lane (j, g) receives rows 4g..4g+3 of column c0 + j: the
+// A operand of v_mfma_f32_16x16x16_bf16 for O^T = V^T P^T.
+__device__ __forceinline__ s16x4 lds_read_tr16(const bf16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)(p)));
 }
 
 }  // namespace lbca

@@ -12,9 +12,9 @@ hipError_t launch_pool(const lbca_pool_args& a, hipStream_t stream);
 
 struct DecodePlan {
   int tile_rows;     // rows per wave tile
-  int head_groups;   // ceil(G / 16) for the MFMA path, G for the fp32 path
-  int splits;        // workgroups along the row range of one (sequence, KV head, head group)
-  size_t ws_bytes;   // partial (acc, max, sum) bytes
+  int head_groups;   // ceil(G / 16): 16-head groups per KV head (MFMA path)
+  int splits;        // workgroups along the row list of one (sequence, KV head, head group)
+  size_t ws_bytes;   // split partials (acc, max, sum); 0 with one split
 };
 DecodePlan plan_decode(const lbca_decode_args& a);
 hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void* ws,
@@ -22,6 +22,7 @@ hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void
 
 hipError_t launch_prefill(const lbca_prefill_args& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const lbca_prefill_args& a, hipStream_t stream);
+hipError_t launch_decode_f32(const lbca_decode_args& a, hipStream_t stream);
 
 size_t index_workspace_bytes(const csa_index_args& a);
 hipError_t launch_index_topk(const csa_index_args& a, void* ws, hipStream_t stream);

@@ -8,15 +8,24 @@
 //
 // Design: pooling reads every token-channel once (8 B/element for bf16 K+V
 // with fp32 logits) and writes 1/m of that, so it is HBM-bound.  A group of
-// L = dim/8 lanes owns one output row; each lane owns 8 consecutive channels,
+// L = dim/8 lanes covers one token row; each lane owns 8 consecutive channels,
 // so every load is a 16-byte vector and a group's loads cover whole 128-byte
 // lines.  The softmax over the block is an online softmax in registers,
-// advanced four tokens at a time (one rescale exp per four data exps).  The
-// optional HCA/CSA entry treatment (RMSNorm, partial RoPE at the block start)
-// runs in the epilogue on the finished fp32 row, before the single rounding to
-// the storage type.
+// advanced four tokens at a time (one rescale exp per four data exps).
+// An output row may be split over P token phases (groups that take tokens
+// phase, phase+P, ...): with many rows (pooling a whole history) P = 1 and
+// every group streams its own block; with few rows (the single block that
+// falls out of the window at a decode step) P grows so that every lane has
+// one short burst of loads in flight, and the P partial states are merged in
+// LDS in a fixed order.  The optional HCA/CSA entry treatment (RMSNorm, partial
+// RoPE at the block start) runs on the finished fp32 row before the single
+// rounding to the storage type.
 #include "device_util.h"
 #include "lbca_internal.h"
+
+#ifndef LBCA_POOL_MAX_PHASES
+#define LBCA_POOL_MAX_PHASES 64  // upper bound on token phases per output row
+#endif
 
 namespace lbca {
 
@@ -33,6 +42,7 @@ struct PoolParams {
   int64_t heads, tokens, dim, m, entries, block_begin, n_blocks, pos_base, total_rows;
   int lanes_per_row;  // L = dim / 8, a power of two <= 64
   int log2_lanes;
+  int log2_phases;    // P = token phases per output row
   float eps;          // < 0: no RMSNorm
   int rope_dims;      // 0: no RoPE
   double log2_base;
@@ -47,24 +57,24 @@ struct PoolAcc {
     for (int c = 0; c < 8; ++c) { mx[c] = kNegInf; l[c] = 0.f; ax[c] = 0.f; av[c] = 0.f; }
   }
 
-  // Fold NT tokens (rows r0..r0+NT-1 of the series, bias rows b0..) into the state.
+  // Fold NT tokens, `stride` rows apart, into the state (bias rows stride apart too).
   template <int NT>
   __device__ __forceinline__ void fold(const TX* xs, const TX* vs, const TZ* zs, const float* bs,
-                                       int64_t dim) {
+                                       int64_t stride) {
     float a[NT][8];
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       float zz[8], bb[8];
-      load8(zs + i * dim, zz);
-      load8(bs + i * dim, bb);
+      load8(zs + i * stride, zz);
+      load8(bs + i * stride, bb);
 #pragma unroll
       for (int c = 0; c < 8; ++c) a[i][c] = (zz[c] + bb[c]) * kLog2e;
     }
     float xv[NT][8], vv[NT][8];
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      load8(xs + i * dim, xv[i]);
-      if (HAS_V) load8(vs + i * dim, vv[i]);
+      load8(xs + i * stride, xv[i]);
+      if constexpr (HAS_V) load8(vs + i * stride, vv[i]);
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -79,35 +89,56 @@ struct PoolAcc {
         const float p = exp2f(a[i][c] - nm);
         sl += p;
         sx = fmaf(p, xv[i][c], sx);
-        if (HAS_V) sv = fmaf(p, vv[i][c], sv);
+        if constexpr (HAS_V) sv = fmaf(p, vv[i][c], sv);
       }
       l[c] = fmaf(l[c], corr, sl);
       ax[c] = fmaf(ax[c], corr, sx);
-      if (HAS_V) av[c] = fmaf(av[c], corr, sv);
+      if constexpr (HAS_V) av[c] = fmaf(av[c], corr, sv);
       mx[c] = nm;
     }
   }
 
-  // Fold a run of `count` consecutive tokens.
+  // Fold tokens first, first+P, ... (< count) of a block whose token 0 is at
+  // xs/vs/zs (row pitch dim) and whose bias row 0 is at bs.
   __device__ __forceinline__ void run(const TX* xs, const TX* vs, const TZ* zs, const float* bs,
-                                      int64_t count, int64_t dim) {
-    int64_t i = 0;
-    for (; i + 4 <= count; i += 4)
-      fold<4>(xs + i * dim, HAS_V ? vs + i * dim : nullptr, zs + i * dim, bs + i * dim, dim);
-    for (; i < count; ++i)
-      fold<1>(xs + i * dim, HAS_V ? vs + i * dim : nullptr, zs + i * dim, bs + i * dim, dim);
+                                      int64_t first, int64_t P, int64_t count, int64_t dim) {
+    const int64_t stride = P * dim;
+    int64_t i = first;
+    for (; i + 3 * P < count; i += 4 * P)
+      fold<4>(xs + i * dim, HAS_V ? vs + i * dim : nullptr, zs + i * dim, bs + i * dim, stride);
+    for (; i < count; i += P)
+      fold<1>(xs + i * dim, HAS_V ? vs + i * dim : nullptr, zs + i * dim, bs + i * dim, stride);
+  }
+
+  // Merge another partial state (same channels) into this one.
+  __device__ __forceinline__ void merge(const float* omx, const float* ol, const float* oax,
+                                        const float* oav) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float nm = fmaxf(mx[c], omx[c]);
+      if (nm == kNegInf) continue;
+      const float a = exp2f(mx[c] - nm), b = exp2f(omx[c] - nm);
+      l[c] = l[c] * a + ol[c] * b;
+      ax[c] = ax[c] * a + oax[c] * b;
+      if constexpr (HAS_V) av[c] = av[c] * a + oav[c] * b;
+      mx[c] = nm;
+    }
   }
 };
 
 template <typename TX, typename TZ, bool DUAL, bool HAS_V, bool TREAT>
 __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  __shared__ float part[32][256];  // [state value][thread], used when P > 1
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int L = p.lanes_per_row;
-  const int gi = lane >> p.log2_lanes;  // row group inside the wave
-  const int li = lane & (L - 1);        // lane inside the group
-  const int groups = 64 >> p.log2_lanes;
-  const int64_t row = ((int64_t)blockIdx.x * 4 + wave) * groups + gi;
+  const int li = lane & (L - 1);                 // lane inside the group
+  const int gb = tid >> p.log2_lanes;            // group inside the workgroup
+  const int P = 1 << p.log2_phases;
+  const int phase = gb & (P - 1);
+  const int groups = 256 >> p.log2_lanes;
+  const int64_t rows_per_wg = groups >> p.log2_phases;
+  const int64_t row = (int64_t)blockIdx.x * rows_per_wg + (gb >> p.log2_phases);
   const bool active = row < p.total_rows;
   const int64_t rr = active ? row : 0;
 
@@ -125,12 +156,37 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
     const int64_t r0 = j * p.m - p.pos_base;  // token row of the entry's own block
     acc.run(static_cast<const TX*>(p.x) + series + r0 * dim,
             HAS_V ? static_cast<const TX*>(p.v) + series + r0 * dim : nullptr,
-            static_cast<const TZ*>(p.z) + series + r0 * dim, bias_h, p.m, dim);
+            static_cast<const TZ*>(p.z) + series + r0 * dim, bias_h, phase, P, p.m, dim);
     if (DUAL && j > 0) {
       const int64_t rb = r0 - p.m;  // preceding block, b-series
       acc.run(static_cast<const TX*>(p.xb) + series + rb * dim, nullptr,
               static_cast<const TZ*>(p.zb) + series + rb * dim, p.bias_b + h * p.m * dim + c0,
-              p.m, dim);
+              phase, P, p.m, dim);
+    }
+  }
+
+  if (P > 1) {  // fixed-order merge of the phases through LDS
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      part[c][tid] = acc.mx[c];
+      part[8 + c][tid] = acc.l[c];
+      part[16 + c][tid] = acc.ax[c];
+      part[24 + c][tid] = acc.av[c];
+    }
+    __syncthreads();
+    if (phase == 0) {
+      for (int ph = 1; ph < P; ++ph) {
+        const int src = tid + ph * L;
+        float omx[8], ol[8], oax[8], oav[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          omx[c] = part[c][src];
+          ol[c] = part[8 + c][src];
+          oax[c] = part[16 + c][src];
+          oav[c] = part[24 + c][src];
+        }
+        acc.merge(omx, ol, oax, oav);
+      }
     }
   }
 
@@ -142,7 +198,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
     ov[c] = acc.av[c] * inv;
   }
 
-  if (TREAT) {
+  if constexpr (TREAT) {
     if (p.eps >= 0.f) {
       float ss = 0.f;
 #pragma unroll
@@ -158,9 +214,9 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
       const bool lo_half = c0 >= first && c0 < first + half;
       const bool hi_half = c0 >= first + half;
       const int src = lo_half ? lane + (half >> 3) : (hi_half ? lane - (half >> 3) : lane);
-      float part[8];
+      float prt[8];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) part[c] = __shfl(ox[c], src, 64);
+      for (int c = 0; c < 8; ++c) prt[c] = __shfl(ox[c], src, 64);
       if (lo_half || hi_half) {
         const double pos = (double)(j * p.m);
 #pragma unroll
@@ -168,16 +224,16 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
           const int k = (int)(c0 + c - first) - (hi_half ? half : 0);
           float cs, sn;
           rope_cos_sin(pos, k, r, p.log2_base, &cs, &sn);
-          ox[c] = lo_half ? ox[c] * cs - part[c] * sn : ox[c] * cs + part[c] * sn;
+          ox[c] = lo_half ? ox[c] * cs - prt[c] * sn : ox[c] * cs + prt[c] * sn;
         }
       }
     }
   }
 
-  if (active) {
+  if (active && phase == 0) {
     const int64_t o = (bh * p.entries + j) * dim + c0;
     store8(static_cast<TX*>(p.out_x) + o, ox);
-    if (HAS_V) store8(static_cast<TX*>(p.out_v) + o, ov);
+    if constexpr (HAS_V) store8(static_cast<TX*>(p.out_v) + o, ov);
   }
 }
 
@@ -211,8 +267,15 @@ hipError_t launch_pool(const lbca_pool_args& a, hipStream_t stream) {
   p.rope_dims = a.rope_dims;
   p.log2_base = a.rope_dims > 0 ? log2((double)a.rope_base) : 0.0;
   if (p.total_rows == 0) return hipSuccess;
-  const int64_t rows_per_block = 4 * (64 / p.lanes_per_row);
-  dim3 grid((unsigned)((p.total_rows + rows_per_block - 1) / rows_per_block));
+  // token phases: grow P (<= groups per workgroup, <= m) until ~8K groups are busy
+  const int groups = 256 / p.lanes_per_row;
+  int lp = 0;
+  while ((1 << (lp + 1)) <= groups && (1 << (lp + 1)) <= a.block && (1 << (lp + 1)) <= LBCA_POOL_MAX_PHASES &&
+         p.total_rows * (int64_t(1) << lp) < 8192)
+    ++lp;
+  p.log2_phases = lp;
+  const int64_t rows_per_wg = groups >> lp;
+  dim3 grid((unsigned)((p.total_rows + rows_per_wg - 1) / rows_per_wg));
   const bool dual = a.xb != nullptr, has_v = a.v != nullptr;
   const bool treat = a.rmsnorm_eps >= 0.f || a.rope_dims > 0;
   if (a.x_dtype == LBCA_BF16) {

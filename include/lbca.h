@@ -173,9 +173,11 @@ LBCA_API int lbca_pool_blocks(const lbca_pool_args* a, void* stream);
  * treatment.
  * A sequence whose visible rows do not fit (n_pooled > entries, raw span
  * outside the raw buffer, t < 0) gets NaN in out and lse.
- * Workspace: lbca_attend_decode_workspace reports the bytes (split partials);
- * pass at least that many bytes of device memory (16-byte aligned); contents
- * on entry do not matter.  Calls sharing one workspace must not overlap.
+ * Workspace: lbca_attend_decode_workspace reports the bytes (0 when the rows
+ * of a sequence are not split across workgroups; otherwise the split
+ * partials).  Pass at least that many bytes of device memory, 16-byte
+ * aligned; contents on entry do not matter.  Calls sharing one workspace must
+ * not overlap.
  */
 typedef struct lbca_decode_args {
   const void* q;

@@ -142,6 +142,47 @@ def test_decode_gqa_bf16(lib, t_list):
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
 
 
+def test_decode_workspace_reuse_and_graph_replay(lib):
+    # split path: one workspace reused by many calls, eager and replayed from a graph,
+    # with other work in between, always reproduces the first result bit for bit
+    B, Hq, Hkv, d, m, W, T = 2, 24, 8, 128, 64, 128, 512 * 64 + 192
+    g = lambda n, shape: synth.normal(shape, synth.seed_of("dec-reuse", n), dtype="bf16", device=DEV)
+    q, q2 = g("q", (B, Hq, d)), g("q2", (B, Hq, d))
+    pk, pv = g("pk", (B, Hkv, 512, d)), g("pv", (B, Hkv, 512, d))
+    rk, rv = g("rk", (B, Hkv, T, d)), g("rv", (B, Hkv, T, d))
+    pos = torch.tensor([512 * 64 + 127, 300 * 64 + 77], device=DEV)   # 512 and 300 pooled entries
+    kw = dict(pooled_v=pv, raw_v=rv)
+    need = lib.decode_workspace_bytes(q, pk, rk, pos, m, W, O.EXCLUSIVE, **kw)
+    assert need > 0, "this shape should split the rows across workgroups"
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=DEV)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+    ref_o, ref_l = lib.attend_decode(q, pk, rk, pos, m, W, O.EXCLUSIVE, **kw)
+    ro, _ = O.attend_decode(host(q), host(pk), host(pv), host(rk), host(rv), pos.tolist(), m, W,
+                            O.EXCLUSIVE, 1 / math.sqrt(d))
+    check_bf16(host(ref_o), ro, "reference call")
+    for _ in range(5):
+        lib.attend_decode(q, pk, rk, pos, m, W, O.EXCLUSIVE, out=out, lse=lse, workspace=ws, **kw)
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+    torch.cuda.synchronize()
+    # graph of the same call on the same workspace
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        lib.attend_decode(q, pk, rk, pos, m, W, O.EXCLUSIVE, out=out, lse=lse, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    other = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for i in range(4):
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {i}"
+        # eager work in between, on another workspace and other queries
+        lib.attend_decode(q2, pk, rk, pos, m, W, O.EXCLUSIVE, workspace=other, **kw)
+        torch.cuda.synchronize()
+
+
 def test_decode_raw_pos_base_and_overlap(lib):
     B, Hq, Hkv, d, m, W = 3, 8, 2, 64, 16, 40
     t_list, base = [700, 333, 45], [600, 290, 0]
