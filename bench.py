@@ -64,7 +64,7 @@ def decode_bytes_per_seq_layer():
 
 
 class DecodeLayer:
-    def __init__(self, layer, B, pool_timer=None):
+    def __init__(self, layer, B, pos, rpb, pool_timer=None):
         tag = ("bench-32k", layer, B)
         dev = "cuda"
         full = synth.lbca_layer(tag, B, HQ, HKV, CTX, D, M, "bf16", "f32", device=dev)
@@ -84,8 +84,7 @@ class DecodeLayer:
         self.z = full["z"][:, :, RAW0:].contiguous()
         del full
         self.q = synth.normal((B, HQ, D), synth.seed_of(*tag, "q1"), dtype="bf16", device=dev)
-        self.pos = torch.full((B,), T_POS, dtype=torch.int64, device=dev)
-        self.rpb = torch.full((B,), RAW0, dtype=torch.int64, device=dev)
+        self.pos, self.rpb = pos, rpb  # one positions tensor for every layer, as in a model
         self.out = torch.empty((B, HQ, D), dtype=torch.float32, device=dev)
         self.lse = torch.empty((B, HQ), dtype=torch.float32, device=dev)
         nbytes = lbca.decode_workspace_bytes(self.q, self.pk, self.rk, self.pos, M, W, EXCL,
@@ -127,7 +126,9 @@ def time_graph(g, reps):
 
 
 def run_decode(B, steps, warmup, pool_timer=None):
-    layers = [DecodeLayer(l, B, pool_timer) for l in range(LAYERS)]
+    pos = torch.full((B,), T_POS, dtype=torch.int64, device="cuda")
+    rpb = torch.full((B,), RAW0, dtype=torch.int64, device="cuda")
+    layers = [DecodeLayer(l, B, pos, rpb, pool_timer) for l in range(LAYERS)]
     torch.cuda.synchronize()
 
     def step():

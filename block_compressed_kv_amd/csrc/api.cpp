@@ -128,9 +128,10 @@ static int validate_decode(const lbca_decode_args* a) {
     if (!(a->dim == 64 || a->dim == 128 || a->dim == 256 || a->dim == 512)) return LBCA_ERR_UNSUPPORTED;
     if (G > 64) return LBCA_ERR_UNSUPPORTED;
     if (!(a->rope_dims == 0 || a->rope_dims == 64 || a->rope_dims == 128)) return LBCA_ERR_UNSUPPORTED;
-    // row counts are 32-bit on the device; grid y/z carry (KV head, head group) and batch
-    if (a->entries >= (int64_t(1) << 31) || a->raw_rows >= (int64_t(1) << 31) ||
-        a->k_sel >= (int64_t(1) << 31) || a->batch > 65535 || a->kv_heads * ((G + 15) / 16) > 65535)
+    // rows are addressed by 32-bit byte offsets within one (sequence, KV head)
+    // slice; the merge grid's y/x carry batch and (KV head, head group)
+    if (a->entries * a->dim * 2 >= (int64_t(1) << 31) || a->raw_rows * a->dim * 2 >= (int64_t(1) << 31) ||
+        a->k_sel >= (int64_t(1) << 29) || a->batch > 65535 || a->kv_heads * ((G + 15) / 16) > 65535)
       return LBCA_ERR_UNSUPPORTED;
   } else {
     if (a->dim % 64 != 0 || a->dim > 512) return LBCA_ERR_UNSUPPORTED;

@@ -13,25 +13,33 @@
 //
 // A workgroup (NW waves) owns a contiguous range of the unit's visible-row
 // list (pooled or selected entries, then the raw span) cut into R-row tiles;
-// wave w takes tiles w, w+NW, ... and, where registers allow, keeps the next
-// tile's global loads in flight (two tile buffers used in turn) while it
-// computes the current one.  Scores are computed transposed,
+// wave w takes tiles w, w+NW, ... and keeps up to three tiles' global loads
+// in flight (register buffers refilled as soon as they are consumed); with one
+// split the first pooled tiles are requested before the position is read.
+// Scores are computed transposed,
 // S^T[row, head] = K[row, :] . Q[head, :], with v_mfma_f32_16x16x32_bf16 whose
 // A operand is loaded straight from global memory in row-major K layout: every
 // lane holds scores of one head, and the softmax max/sum need one 16-lane and
-// one 32-lane swap.  P^T is already the B operand of v_mfma_f32_16x16x16_bf16
-// for O^T = V^T P^T; V rows are staged row-major in a per-wave LDS tile and
-// each A operand is one transposing LDS read (ds_read_b64_tr_b16).
+// one 32-lane swap.  P^T is already the B operand of the MFMA for
+// O^T = V^T P^T; V rows are staged row-major in a per-wave LDS tile and each
+// A operand is gathered with transposing LDS reads (ds_read_b64_tr_b16).
 //
-// Small decodes are bound by each wave's instruction chain, not by bytes, so
-// the per-tile path is kept short: raw v_exp_f32, lane swaps instead of LDS
-// permutes, the accumulator rescale skipped when no running max moved, 32-bit
-// index arithmetic, and a single-barrier merge of the waves.  With one split
-// the workgroup finishes its heads (sink, normalisation, -t rotation, LSE);
-// with several, each workgroup writes an unnormalised partial (acc, max, sum)
-// and decode_merge_kernel combines them in a fixed order (bitwise
-// reproducible).  No device-scope fence is used anywhere: on this multi-XCD
-// part a device-scope release/acquire writes back and invalidates the XCD's L2.
+// When there are too few units to occupy every CU, DS "twin" workgroups share
+// a unit: each computes the full Q.K scores (identical softmax state, so no
+// merge is needed) but only 1/DS of the output dims, loading all K rows and
+// only its slice of V.  Twins get linear workgroup ids 8 apart, which the
+// dispatcher places on the same XCD, so the second read of K hits its L2.
+//
+// Small decodes are bound by each wave's instruction chain and by memory
+// latency rather than by bytes, so the per-tile path is kept short: raw
+// v_exp_f32, lane swaps instead of LDS permutes, the accumulator rescale
+// skipped when no running max moved, 32-bit index arithmetic, and a
+// single-barrier merge of the waves.  With one split the workgroup finishes
+// its heads (sink, normalisation, -t rotation, LSE); with several, each
+// workgroup writes an unnormalised partial (acc, max, sum) and
+// decode_merge_kernel combines them in a fixed order (bitwise reproducible).
+// No device-scope fence is used anywhere: on this multi-XCD part a
+// device-scope release/acquire writes back and invalidates the XCD's L2.
 #include "device_util.h"
 #include "lbca_internal.h"
 
@@ -57,6 +65,7 @@ struct DecodeParams {
   float* ws_acc;   // [units * splits][16][D]
   int64_t hq, hkv, G, entries, raw_rows, k_sel, m, W;
   int mode, splits, head_groups;
+  int units;       // batch * kv_heads * head_groups
   float scale_log2;
   float eps;
   int rope_dims;
@@ -108,10 +117,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 // dims 32*s + 8*kq + i of the row (s < D/32, i < 8); the 4 lanes of a row are
 // lane, lane^16, lane^32, lane^48.  RMSNorm over all D dims, then RoPE on the
 // last RD dims (rotate-half pairs (k, k+RD/2) sit in the same lane, RD/64 steps
-// apart).  Every lane of the wave must call this (it uses lane swaps).
+// apart).  freq[k] = turns per position of pair k (an LDS table, so the
+// double-precision frequencies are not held in registers through the tile
+// loop).  Every lane of the wave must call this (it uses lane swaps).
 template <int D, int RD>
 __device__ __forceinline__ void treat_row(uint4 (&r)[D / 32], double pos, bool ok, float eps,
-                                          double log2_base) {
+                                          const double* freq) {
   constexpr int KS = D / 32;
   const int kq = (threadIdx.x & 63) >> 4;
   if (eps >= 0.f) {
@@ -147,7 +158,7 @@ __device__ __forceinline__ void treat_row(uint4 (&r)[D / 32], double pos, bool o
       for (int i = 0; i < 8; ++i) {
         const int k = 32 * (s - S0) + 8 * kq + i;
         float c, sn;
-        rope_cos_sin(pos, k, RD, log2_base, &c, &sn);
+        rope_cos_sin_turns(pos * freq[k], &c, &sn);
         const float x1 = a[i], x2 = b[i];
         a[i] = x1 * c - x2 * sn;
         b[i] = x2 * c + x1 * sn;
@@ -158,79 +169,116 @@ __device__ __forceinline__ void treat_row(uint4 (&r)[D / 32], double pos, bool o
   }
 }
 
-template <int D, int R, bool SHARED>
+// One R-row tile in registers: all D dims of K (MFMA A operands) and this
+// workgroup's slice of V (DV dims) when V is a separate series.
+template <int D, int R, int DS, bool SHARED>
 struct Tile {
   uint4 k[R / 16][D / 32];
-  uint4 v[SHARED ? 1 : R / 16][SHARED ? 1 : D / 32];
+  uint4 v[SHARED ? 1 : R / 16][SHARED ? 1 : D / 32 / DS];
   unsigned valid[R / 16];
 };
 
-// Issue the global loads of one tile (rows beyond the list or unusable
-// selected ids are zero and marked invalid).
-template <int D, int R, bool SHARED>
-__device__ __forceinline__ void load_tile(Tile<D, R, SHARED>& T, const DecodeParams& p,
-                                          const SeqView& sv, int64_t b, int64_t kv_pool,
-                                          int64_t kv_raw, int tiles_p, int tile, int n, int kq) {
-  constexpr int KS = D / 32, NH = R / 16;
-  const bool is_raw = tile >= tiles_p;
-  const int v0 = is_raw ? (tile - tiles_p) * R : tile * R;
-  const int count = is_raw ? sv.n_raw : sv.n_sel;
-  // base addresses selected as integers (a pointer select from the argument
-  // block otherwise becomes a private-memory lookup)
-  const uintptr_t kbase = is_raw ? reinterpret_cast<uintptr_t>(p.rk) : reinterpret_cast<uintptr_t>(p.pk);
-  const uintptr_t vbase = is_raw ? reinterpret_cast<uintptr_t>(p.rv) : reinterpret_cast<uintptr_t>(p.pv);
+// Byte addresses of one (sequence, KV head) slice: the pooled and raw rows of
+// K and V (V aliases K for a shared series), and a stand-in row that rows
+// outside the list read instead (this head group's first query row: always
+// valid memory and already in cache, so such loads cost no HBM traffic).
+struct Slices {
+  uintptr_t pk, pv, rk, rv, dummy;
+};
+
+// Selected ids of one workgroup's range are staged in LDS (a global load of
+// an id right before the rows it names would make every wait on it a wait
+// for all older loads of the wave).
+constexpr int kSelLds = 1024;
+
+template <int D, int R, int DS, bool SHARED>
+__device__ __forceinline__ void clear_valid(Tile<D, R, DS, SHARED>& T) {
+#pragma unroll
+  for (int h = 0; h < R / 16; ++h) T.valid[h] = 0;
+}
+
+// Issue the loads of one tile of the visible-row list.  Tile ids: [0, tiles_p)
+// pooled or selected rows, [tiles_p, pad_p) empty, [pad_p, ...) raw rows.  A
+// tile that is not live (outside this workgroup's range) has no rows.  Rows
+// not in the list read the stand-in row and get a clear valid bit (their
+// scores are masked and their values zeroed when staged): the loads of a tile
+// carry no branch, since a load that may be skipped makes the compiler wait
+// for every older load before the next use of any.  Tiles past the range are
+// not loaded at all: each load instruction costs address-unit time even when
+// its data is cached, and a wave cannot end before its loads return.
+// ids: the selected ids of list positions r0, r0+1, ... (LDS).
+template <int D, int R, int DS, bool SHARED>
+__device__ __forceinline__ void load_tile(Tile<D, R, DS, SHARED>& T, const int* ids, int r0,
+                                          bool sel, const Slices& sl, const SeqView& sv,
+                                          int tiles_p, int pad_p, int tile, bool live, int n,
+                                          int kq, int dv0) {
+  constexpr int KS = D / 32, NH = R / 16, KV = KS / DS;
+  const bool is_raw = tile >= pad_p;
+  const bool empty = !is_raw && tile >= tiles_p;
+  const int v0 = is_raw ? (tile - pad_p) * R : tile * R;
+  const int count = (!live || empty) ? 0 : is_raw ? sv.n_raw : sv.n_sel;
+  const uintptr_t kb = is_raw ? sl.rk : sl.pk;  // wave-uniform selects
+  const uintptr_t vb = is_raw ? sl.rv : sl.pv;
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     const int v = v0 + 16 * h + n;
     bool ok = v < count;
-    int64_t row;
+    int row;
     if (is_raw) {
-      row = kv_raw + v;
+      row = (int)sv.raw_row0 + v;
     } else {
-      int64_t e = v;
-      if (p.sel) e = ok ? (int64_t)p.sel[b * p.k_sel + v] : -1;
-      ok = ok && e >= 0 && e < sv.n_pooled;
-      row = kv_pool + e;
+      row = v;
+      if (sel) row = ids[ok ? min(v - r0, kSelLds - 1) : 0];
+      ok = ok && row >= 0 && row < sv.n_pooled;
     }
-    const bf16_t* kp = reinterpret_cast<const bf16_t*>(kbase) + row * D + 8 * kq;
-    if (ok) {
+    const uint64_t off = (uint64_t)(uint32_t)row * (D * 2) + 16u * kq;
+    const uintptr_t kp = ok ? kb + off : sl.dummy + 16u * kq;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) T.k[h][s] = *reinterpret_cast<const uint4*>(kp + 32 * s);
-      if constexpr (!SHARED) {
-        const bf16_t* vp = reinterpret_cast<const bf16_t*>(vbase) + row * D + 8 * kq;
+    for (int s = 0; s < KS; ++s) T.k[h][s] = ldg16(kp + 64u * s);
+    if constexpr (!SHARED) {
+      const uintptr_t vp = (ok ? vb + off : sl.dummy + 16u * kq) + 2u * dv0;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) T.v[h][s] = *reinterpret_cast<const uint4*>(vp + 32 * s);
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        T.k[h][s] = make_uint4(0, 0, 0, 0);
-        if constexpr (!SHARED) T.v[h][s] = make_uint4(0, 0, 0, 0);
-      }
+      for (int s = 0; s < KV; ++s) T.v[h][s] = ldg16(vp + 64u * s);
     }
     T.valid[h] = (unsigned)(__ballot(ok) & 0xffffull);
   }
 }
 
-template <int D, int R, int NW, bool SHARED, int RD, bool TREAT>
+template <int D, int R, int NW, int DS, bool SHARED, int RD, bool TREAT, bool SPEC>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
-  constexpr int KS = D / 32, NH = R / 16, DT = D / 16, PITCH = D + 16;
+  constexpr int KS = D / 32, NH = R / 16;
+  constexpr int DV = D / DS;                         // output dims of this workgroup
+  constexpr int KV = DV / 32, DT = DV / 16, PITCH = DV + 16;
   constexpr int STAGE = R * PITCH;                   // bf16 elements of one wave's value stage
-  constexpr bool PREFETCH = D <= 128;                // second tile buffer fits in registers
-  constexpr bool PAR_MERGE = NW * 16 * D * 4 <= NW * STAGE * 2;
-  static_assert(NW * STAGE * 2 >= 16 * D * 4, "merge buffer must fit in the stages");
+  constexpr bool PAR_MERGE = NW * 16 * DV * 4 <= NW * STAGE * 2;
+  static_assert(NW * STAGE * 2 >= 16 * DV * 4, "merge buffer must fit in the stages");
+  static_assert(RD <= DV, "rotated dims must lie in one dim slice");
   __shared__ __attribute__((aligned(16))) bf16_t lds[NW * STAGE];
   __shared__ float s_ml[NW][16][2];
   __shared__ float s_w[NW][16];
   __shared__ float s_M[16], s_L[16], s_inv[16], s_lse[16];
+  __shared__ double s_freq[RD > 0 ? RD / 2 : 1];  // RoPE turns per position, pair k
+  __shared__ int s_ids[SPEC ? 1 : kSelLds];        // selected ids of this workgroup's range
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile choices stay scalar
   const int n = lane & 15, kq = lane >> 4;
-  const int split = blockIdx.x;
-  const int hg = (int)(blockIdx.y % (unsigned)p.head_groups);
-  const int64_t kvh = blockIdx.y / (unsigned)p.head_groups;
-  const int64_t b = blockIdx.z;
-  const int64_t unit = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
+  // linear id -> (unit, split, dim slice); twins of a unit sit 8 ids apart (same XCD)
+  unsigned u = blockIdx.x, dh = 0;
+  if constexpr (DS > 1) {
+    const unsigned rest = blockIdx.x >> 3;
+    dh = rest % DS;
+    u = (rest / DS) * 8 + (blockIdx.x & 7);
+  }
+  if (u >= (unsigned)p.units * (unsigned)p.splits) return;  // padding of the XCD mapping
+  const int split = (int)(u % (unsigned)p.splits);
+  const unsigned unit = u / (unsigned)p.splits;
+  const unsigned uy = (unsigned)(p.hkv * p.head_groups);
+  const int64_t b = unit / uy;
+  const unsigned y = unit % uy;
+  const int hg = (int)(y % (unsigned)p.head_groups);
+  const int64_t kvh = y / (unsigned)p.head_groups;
+  const int dv0 = (int)dh * DV;                      // first output dim of this workgroup
   const int slot0 = hg * 16;
   const int nvalid = (int)(p.G - slot0 < 16 ? p.G - slot0 : 16);
   const int64_t head0 = kvh * p.G + slot0;  // first query head of the unit
@@ -245,24 +293,69 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     for (int s = 0; s < KS; ++s)
       qr[s] = head_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s) : make_uint4(0, 0, 0, 0);
   }
+  // Addresses of this (sequence, KV head) slice (none depends on the position).
+  Slices sl;
+  {
+    const uint64_t sp = (uint64_t)((b * p.hkv + kvh) * p.entries) * (D * 2);
+    const uint64_t sr = (uint64_t)((b * p.hkv + kvh) * p.raw_rows) * (D * 2);
+    sl.pk = reinterpret_cast<uintptr_t>(p.pk) + sp;
+    sl.rk = reinterpret_cast<uintptr_t>(p.rk) + sr;
+    sl.pv = SHARED ? sl.pk : reinterpret_cast<uintptr_t>(p.pv) + sp;
+    sl.rv = SHARED ? sl.rk : reinterpret_cast<uintptr_t>(p.rv) + sr;
+    sl.dummy = reinterpret_cast<uintptr_t>(p.q + (b * p.hq + head0) * D);
+  }
+  // Each wave keeps TMAX tiles in flight.  SPEC instances (one split, no
+  // selection, launched as such by the host) request their first TMAX tiles,
+  // the pooled tiles w, w+NW, ..., now, before the position arrives
+  // (visibility is applied once the position is known), and move the raw
+  // tiles past slot TMAX*NW of the list.
+  constexpr int TMAX = D <= 64 ? 4 : D <= 128 ? (DS > 1 ? 3 : 2) : 1;
+  static_assert(!SPEC || D <= 128, "early tiles of wide rows would spill");
+  Tile<D, R, DS, SHARED> T[TMAX];
+  constexpr bool spec = SPEC;
+  if constexpr (SPEC) {
+#pragma unroll
+    for (int i = 0; i < TMAX; ++i) {
+      if ((wave + i * NW) * R >= p.entries) break;  // no buffer rows left
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const int e = (wave + i * NW) * R + 16 * h + n;
+        const uint64_t off = (uint64_t)e * (D * 2) + 16u * kq;
+        const bool in = e < p.entries;  // rows past the buffer read the stand-in row
+        const uintptr_t kp = in ? sl.pk + off : sl.dummy + 16u * kq;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) T[i].k[h][s] = ldg16(kp + 64u * s);
+        if constexpr (!SHARED) {
+          const uintptr_t vp = (in ? sl.pv + off : sl.dummy + 16u * kq) + 2u * dv0;
+#pragma unroll
+          for (int s = 0; s < KV; ++s) T[i].v[h][s] = ldg16(vp + 64u * s);
+        }
+      }
+    }
+  }
   const SeqView sv = seq_view(p, b);
-  if (!sv.ok) {  // rows do not fit the buffers: NaN, written once per unit
+  if (!sv.ok) {  // rows do not fit the buffers: NaN, written once per unit and slice
     if (split == 0) {
-      for (int i = tid; i < nvalid * D; i += blockDim.x)
-        p.out[(b * p.hq + head0 + i / D) * D + i % D] = __builtin_nanf("");
-      if (p.lse && tid < nvalid) p.lse[b * p.hq + head0 + tid] = __builtin_nanf("");
+      for (int i = tid; i < nvalid * DV; i += blockDim.x)
+        p.out[(b * p.hq + head0 + i / DV) * D + dv0 + i % DV] = __builtin_nanf("");
+      if (p.lse && dh == 0 && tid < nvalid) p.lse[b * p.hq + head0 + tid] = __builtin_nanf("");
     }
     return;
   }
-  if constexpr (TREAT) treat_row<D, RD>(qr, (double)sv.t, head_ok, p.eps, p.log2_base);
+  if constexpr (TREAT) {
+    if constexpr (RD > 0) {
+      if (tid < RD / 2) s_freq[tid] = rope_turns_per_pos(tid, RD, p.log2_base);
+      __syncthreads();
+    }
+    treat_row<D, RD>(qr, (double)sv.t, head_ok, p.eps, s_freq);
+  }
 
   const int tiles_p = (sv.n_sel + R - 1) / R;
-  const int tiles_total = tiles_p + (sv.n_raw + R - 1) / R;
+  const int pad_p = spec && tiles_p < TMAX * NW ? TMAX * NW : tiles_p;  // first raw tile
+  const int tiles_total = pad_p + (sv.n_raw + R - 1) / R;
   const int per = (tiles_total + p.splits - 1) / p.splits;
   const int t0 = split * per;
   const int t1 = t0 + per < tiles_total ? t0 + per : tiles_total;
-  const int64_t kv_pool = (b * p.hkv + kvh) * p.entries;
-  const int64_t kv_raw = (b * p.hkv + kvh) * p.raw_rows + sv.raw_row0;
 
   float m_run = kNegInf, l_run = 0.f;
   f32x4 acc[DT];
@@ -272,24 +365,40 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
   // transposing-read base of this lane: row 4*kq + n/4, column 4*(n%4)
   const bf16_t* trb = vt + (4 * kq + (n >> 2)) * PITCH + 4 * (n & 3);
 
-  auto process = [&](Tile<D, R, SHARED>& T, int tile) {
+  auto process = [&](Tile<D, R, DS, SHARED>& T, int tile) {
     if constexpr (TREAT) {
-      if (tile >= tiles_p) {
-        const int v0 = (tile - tiles_p) * R;
+      if (tile >= pad_p) {
+        const int v0 = (tile - pad_p) * R;
 #pragma unroll
         for (int h = 0; h < NH; ++h)
           treat_row<D, RD>(T.k[h], (double)(sv.raw_begin + v0 + 16 * h + n), (T.valid[h] >> n) & 1u,
-                           p.eps, p.log2_base);
+                           p.eps, s_freq);
       }
     }
-    // value rows to this wave's LDS stage (row-major)
+    // this workgroup's slice of the value rows to the wave's LDS stage (row-major)
     wave_lds_sync();
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        *reinterpret_cast<uint4*>(&vt[(16 * h + n) * PITCH + 32 * s + 8 * kq]) =
-            SHARED ? T.k[h][s] : T.v[h][s];
+      for (int s = 0; s < KV; ++s) {
+        uint4 val;
+        if constexpr (SHARED) {  // shared series: V is the (treated) K row, slice dh
+          // bitwise select: a conditional pick between array elements would be
+          // turned into a dynamically indexed (private memory) array
+          val = T.k[h][s];
+#pragma unroll
+          for (int q = 1; q < DS; ++q) {
+            const uint32_t mk = (int)dh == q ? 0xffffffffu : 0u;
+            const uint4 w = T.k[h][q * KV + s];
+            val = make_uint4((val.x & ~mk) | (w.x & mk), (val.y & ~mk) | (w.y & mk),
+                             (val.z & ~mk) | (w.z & mk), (val.w & ~mk) | (w.w & mk));
+          }
+        } else {
+          val = T.v[h][s];
+        }
+        if (!((T.valid[h] >> n) & 1u)) val = make_uint4(0, 0, 0, 0);  // rows past the list may hold anything
+        *reinterpret_cast<uint4*>(&vt[(16 * h + n) * PITCH + 32 * s + 8 * kq]) = val;
+      }
     // S^T = K Q^T, 16 rows x 16 heads per half
     float sc[NH][4];
     float tmax = kNegInf;
@@ -313,7 +422,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     const float mu = nm == kNegInf ? 0.f : nm;
     const float corr = fast_exp2(m_run - mu);
     float psum = 0.f;
-    s16x4 pop[NH];
+    uint32_t pw[NH][2];
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       float pj[4];
@@ -322,8 +431,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
         pj[j] = fast_exp2(sc[h][j] - mu);
         psum += pj[j];
       }
-      const uint32_t w0 = pack_bf16x2(pj[0], pj[1]), w1 = pack_bf16x2(pj[2], pj[3]);
-      pop[h] = s16x4{(short)(w0 & 0xffff), (short)(w0 >> 16), (short)(w1 & 0xffff), (short)(w1 >> 16)};
+      pw[h][0] = pack_bf16x2(pj[0], pj[1]);
+      pw[h][1] = pack_bf16x2(pj[2], pj[3]);
     }
     l_run = fmaf(l_run, corr, psum);
     if (__ballot(corr != 1.f)) {  // some head's running max moved
@@ -336,11 +445,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     // probabilities (rows 4kq+j of both halves) as its B operand and two
     // transposing reads (the same rows of one dim) as its A operand.
     if constexpr (NH == 2) {
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(
-          (uint16_t)pop[0][0] | ((uint32_t)(uint16_t)pop[0][1] << 16),
-          (uint16_t)pop[0][2] | ((uint32_t)(uint16_t)pop[0][3] << 16),
-          (uint16_t)pop[1][0] | ((uint32_t)(uint16_t)pop[1][1] << 16),
-          (uint16_t)pop[1][2] | ((uint32_t)(uint16_t)pop[1][3] << 16)));
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]));
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         const s16x4 a0 = lds_read_tr16(trb + 16 * t), a1 = lds_read_tr16(trb + 16 * PITCH + 16 * t);
@@ -349,37 +454,71 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
       }
     } else {
 #pragma unroll
-      for (int h = 0; h < NH; ++h)
+      for (int h = 0; h < NH; ++h) {
+        const s16x4 pb = __builtin_bit_cast(s16x4, make_uint2(pw[h][0], pw[h][1]));
 #pragma unroll
         for (int t = 0; t < DT; ++t)
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr16(trb + 16 * h * PITCH + 16 * t),
-                                                              pop[h], acc[t], 0, 0, 0);
+                                                              pb, acc[t], 0, 0, 0);
+      }
     }
   };
 
-  int tile = t0 + wave;
-  if constexpr (PREFETCH) {
-    if (tile < t1) {
-      Tile<D, R, SHARED> ta, tb;
-      load_tile<D, R, SHARED>(ta, p, sv, b, kv_pool, kv_raw, tiles_p, tile, n, kq);
-      while (true) {  // two buffers used in turn: no register copies between tiles
-        int nt = tile + NW;
-        if (nt < t1) load_tile<D, R, SHARED>(tb, p, sv, b, kv_pool, kv_raw, tiles_p, nt, n, kq);
-        process(ta, tile);
-        if (nt >= t1) break;
-        tile = nt;
-        nt = tile + NW;
-        if (nt < t1) load_tile<D, R, SHARED>(ta, p, sv, b, kv_pool, kv_raw, tiles_p, nt, n, kq);
-        process(tb, tile);
-        if (nt >= t1) break;
-        tile = nt;
-      }
+  // Tile loop: buffer i is computed, then refilled with the tile TMAX*NW
+  // further on, so up to TMAX tiles' loads overlap the computation; selected
+  // ids are fetched one refill ahead.  Tiles without a visible row (empty
+  // padding, past the range) are not computed.
+  // selected ids of this range to LDS (the host sizes ranges to fit)
+  const bool sel = !SPEC && p.sel != nullptr;  // SPEC instances are launched without a selection
+  const int r0 = t0 * R;
+  if (sel) {
+    int nr = (t1 < tiles_p ? t1 : tiles_p) * R;
+    nr = (nr < sv.n_sel ? nr : sv.n_sel) - r0;
+    nr = nr < kSelLds ? nr : kSelLds;
+    const int32_t* src = p.sel + b * p.k_sel + r0;
+    for (int i = tid; i < nr; i += NW * 64) s_ids[i] = src[i];
+    __syncthreads();
+  }
+  if constexpr (TMAX == 1) {
+    // wide rows: one buffer, loaded then computed (a refill issued during the
+    // computation would need a second buffer and spill)
+#pragma unroll 1
+    for (int ti = t0 + wave; ti < t1; ti += NW) {
+      load_tile<D, R, DS, SHARED>(T[0], s_ids, r0, sel, sl, sv, tiles_p, pad_p, ti, true, n, kq, dv0);
+      unsigned any = 0;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) any |= T[0].valid[h];
+      if (any) process(T[0], ti);
     }
   } else {
-    Tile<D, R, SHARED> tt;
-    for (; tile < t1; tile += NW) {
-      load_tile<D, R, SHARED>(tt, p, sv, b, kv_pool, kv_raw, tiles_p, tile, n, kq);
-      process(tt, tile);
+    const int step = TMAX * NW;
+    if constexpr (SPEC) {  // first tiles already requested: set their valid bits
+#pragma unroll
+      for (int i = 0; i < TMAX; ++i)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          T[i].valid[h] = (unsigned)(__ballot((wave + i * NW) * R + 16 * h + n < sv.n_sel) & 0xffffull);
+    } else {
+#pragma unroll
+      for (int i = 0; i < TMAX; ++i) {
+        const int ti = t0 + wave + i * NW;
+        if (ti < t1) load_tile<D, R, DS, SHARED>(T[i], s_ids, r0, sel, sl, sv, tiles_p, pad_p, ti, true, n, kq, dv0);
+        else clear_valid(T[i]);
+      }
+    }
+#pragma unroll 1
+    for (int g0 = t0 + wave; g0 < t1; g0 += step) {
+#pragma unroll
+      for (int i = 0; i < TMAX; ++i) {
+        const int ti = g0 + i * NW;
+        unsigned any = 0;
+#pragma unroll
+        for (int h = 0; h < NH; ++h) any |= T[i].valid[h];
+        if (any) process(T[i], ti);
+        const int nt = ti + step;
+        if (nt < t1) load_tile<D, R, DS, SHARED>(T[i], s_ids, r0, sel, sl, sv, tiles_p, pad_p, nt, true, n, kq, dv0);
+        else clear_valid(T[i]);
+      }
     }
   }
   l_run = xor16_sum(l_run);
@@ -410,7 +549,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
   if constexpr (PAR_MERGE) {  // every wave writes its scaled acc to its own slice
     if (head_ok) {
       const float sw = s_w[wave][n];
-      float* dst = buf + (wave * 16 + n) * D + 4 * kq;
+      float* dst = buf + (wave * 16 + n) * DV + 4 * kq;
 #pragma unroll
       for (int t = 0; t < DT; ++t)
         *reinterpret_cast<float4*>(dst + 16 * t) =
@@ -424,7 +563,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
         const float sw = s_w[w][n];
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
-          float4* dst = reinterpret_cast<float4*>(&buf[n * D + 16 * t + 4 * kq]);
+          float4* dst = reinterpret_cast<float4*>(&buf[n * DV + 16 * t + 4 * kq]);
           float4 v = make_float4(acc[t][0] * sw, acc[t][1] * sw, acc[t][2] * sw, acc[t][3] * sw);
           if (w > 0) {
             const float4 o = *dst;
@@ -436,18 +575,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
       __syncthreads();
     }
   }
-  auto merged = [&](int sl, int d) {  // combined unnormalised acc of slot sl, dim d
+  auto merged = [&](int sl, int dl) {  // combined unnormalised acc of slot sl, local dim dl
     if constexpr (PAR_MERGE) {
       float o = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) o += buf[(w * 16 + sl) * D + d];
+      for (int w = 0; w < NW; ++w) o += buf[(w * 16 + sl) * DV + dl];
       return o;
     } else {
-      return buf[sl * D + d];
+      return buf[sl * DV + dl];
     }
   };
 
-  constexpr int r = RD, half = RD / 2;
   if (p.splits == 1) {
     if (tid < nvalid) {
       float L = s_L[tid];
@@ -457,30 +595,36 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
       s_lse[tid] = (M + log2f(L)) * 0.69314718055994531f;
     }
     __syncthreads();
-    const int items = nvalid * (D - half);  // plain dims, then rotate-half pairs
+    // local dims: plain ones, and for the slice holding the rotated dims one
+    // item per rotate-half pair (k, k + RD/2)
+    constexpr int r = RD, half = RD / 2;
+    const bool rot = RD > 0 && (int)dh == DS - 1;
+    const int per_slot = rot ? DV - half : DV;
+    const int items = nvalid * per_slot;
     for (int i = tid; i < items; i += blockDim.x) {
-      const int sl = i / (D - half), d = i % (D - half);
+      const int sl = i / per_slot, dl = i % per_slot;
+      const int d = dv0 + dl;
       float* o = p.out + (b * p.hq + head0 + sl) * D;
       const float inv = s_inv[sl];
-      if (d < D - r) {
-        o[d] = merged(sl, d) * inv;
+      if (!rot || d < D - r) {
+        o[d] = merged(sl, dl) * inv;
       } else if constexpr (RD > 0) {
         const int k = d - (D - r);
-        const float x1 = merged(sl, d) * inv, x2 = merged(sl, d + half) * inv;
+        const float x1 = merged(sl, dl) * inv, x2 = merged(sl, dl + half) * inv;
         float c, sn;
-        rope_cos_sin(-(double)sv.t, k, r, p.log2_base, &c, &sn);
+        rope_cos_sin_turns(-(double)sv.t * s_freq[k], &c, &sn);
         o[d] = x1 * c - x2 * sn;
         o[d + half] = x2 * c + x1 * sn;
       }
     }
-    if (p.lse && tid < nvalid) p.lse[b * p.hq + head0 + tid] = s_lse[tid];
+    if (p.lse && dh == 0 && tid < nvalid) p.lse[b * p.hq + head0 + tid] = s_lse[tid];
     return;
   }
   // ---- split partial to the workspace; decode_merge_kernel combines the splits ----
-  const int64_t part = unit * p.splits + split;
-  for (int i = tid; i < nvalid * D; i += blockDim.x)
-    p.ws_acc[(part * 16) * D + i] = merged(i / D, i % D);
-  if (tid < nvalid) {
+  const int64_t part = (int64_t)unit * p.splits + split;
+  for (int i = tid; i < nvalid * DV; i += blockDim.x)
+    p.ws_acc[(part * 16 + i / DV) * D + dv0 + i % DV] = merged(i / DV, i % DV);
+  if (dh == 0 && tid < nvalid) {
     p.ws_ml[(part * 16 + tid) * 2] = s_M[tid];
     p.ws_ml[(part * 16 + tid) * 2 + 1] = s_L[tid];
   }
@@ -583,30 +727,44 @@ DecodePlan plan_decode(const lbca_decode_args& a) {
   if (s > by_traffic) s = by_traffic;
   if (s > 64) s = 64;
   if (s < 1) s = 1;
+  // a workgroup's range of selected ids must fit its LDS stage
+  const int64_t tiles_per_ids = kSelLds / pl.tile_rows;
+  if (a.sel_idx && s < (tiles + tiles_per_ids - 1) / tiles_per_ids) s = (tiles + tiles_per_ids - 1) / tiles_per_ids;
   pl.splits = (int)s;
+  // dim-split twins when the workgroups would not cover the 256 CUs, and
+  // always for 512 dims (a full-width accumulator does not fit beside a tile)
+  pl.dim_splits = ((a.dim == 512 || (a.dim >= 128 && units * s < 256)) && a.rope_dims <= a.dim / 2) ? 2 : 1;
   if (s == 1) return pl;
   const size_t u = (size_t)units;
   pl.ws_bytes = u * s * 16 * 2 * sizeof(float) + u * s * 16 * (size_t)a.dim * sizeof(float);
   return pl;
 }
 
-template <int D, int R, int NW>
+template <int D, int R, int NW, int DS>
 static hipError_t launch_d(const DecodeParams& p, bool shared, int rd, bool treat, dim3 g,
                            hipStream_t s) {
   const dim3 blk(NW * 64);
   if (!treat) {
-    if (shared) decode_kernel<D, R, NW, true, 0, false><<<g, blk, 0, s>>>(p);
-    else decode_kernel<D, R, NW, false, 0, false><<<g, blk, 0, s>>>(p);
+    if constexpr (D <= 128) {  // early-request instances for one split without selection
+      if (p.splits == 1 && p.sel == nullptr) {
+        if (shared) decode_kernel<D, R, NW, DS, true, 0, false, true><<<g, blk, 0, s>>>(p);
+        else decode_kernel<D, R, NW, DS, false, 0, false, true><<<g, blk, 0, s>>>(p);
+        return hipGetLastError();
+      }
+    }
+    if (shared) decode_kernel<D, R, NW, DS, true, 0, false, false><<<g, blk, 0, s>>>(p);
+    else decode_kernel<D, R, NW, DS, false, 0, false, false><<<g, blk, 0, s>>>(p);
     return hipGetLastError();
   }
   if (!shared) return hipErrorInvalidValue;
   switch (rd) {
-    case 0: decode_kernel<D, R, NW, true, 0, true><<<g, blk, 0, s>>>(p); break;
+    case 0: decode_kernel<D, R, NW, DS, true, 0, true, false><<<g, blk, 0, s>>>(p); break;
     case 64:
-      if constexpr (D >= 64) decode_kernel<D, R, NW, true, 64, true><<<g, blk, 0, s>>>(p);
+      if constexpr (D / DS >= 64) decode_kernel<D, R, NW, DS, true, 64, true, false><<<g, blk, 0, s>>>(p);
+      else return hipErrorInvalidValue;
       break;
     case 128:
-      if constexpr (D >= 128) decode_kernel<D, R, NW, true, 128, true><<<g, blk, 0, s>>>(p);
+      if constexpr (D / DS >= 128) decode_kernel<D, R, NW, DS, true, 128, true, false><<<g, blk, 0, s>>>(p);
       else return hipErrorInvalidValue;
       break;
     default: return hipErrorInvalidValue;
@@ -635,19 +793,24 @@ hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void
   p.entries = a.entries; p.raw_rows = a.raw_rows; p.k_sel = a.sel_idx ? a.k_sel : 0;
   p.m = a.block; p.W = a.window; p.mode = a.mode;
   p.splits = plan.splits; p.head_groups = plan.head_groups;
+  p.units = (int)units;
   p.scale_log2 = a.scale * kLog2e;
   p.eps = a.rmsnorm_eps;
   p.rope_dims = a.rope_dims;
   p.log2_base = a.rope_dims > 0 ? log2((double)a.rope_base) : 0.0;
   const bool shared = a.pooled_v == nullptr;
   const bool treat = a.rmsnorm_eps >= 0.f || a.rope_dims > 0;
-  const dim3 g((unsigned)plan.splits, (unsigned)(a.kv_heads * plan.head_groups), (unsigned)a.batch);
+  const size_t pairs = units * plan.splits;  // (unit, split) pairs
+  const int ds = plan.dim_splits;
+  const dim3 g((unsigned)(ds == 1 ? pairs : (pairs + 7) / 8 * 8 * ds));
   hipError_t e;
-  switch (a.dim) {
-    case 64: e = launch_d<64, 32, 8>(p, shared, a.rope_dims, treat, g, stream); break;
-    case 128: e = launch_d<128, 32, 8>(p, shared, a.rope_dims, treat, g, stream); break;
-    case 256: e = launch_d<256, 32, 4>(p, shared, a.rope_dims, treat, g, stream); break;
-    case 512: e = launch_d<512, 16, 4>(p, shared, a.rope_dims, treat, g, stream); break;
+  switch (a.dim * 4 + ds) {
+    case 64 * 4 + 1: e = launch_d<64, 32, 8, 1>(p, shared, a.rope_dims, treat, g, stream); break;
+    case 128 * 4 + 1: e = launch_d<128, 32, 8, 1>(p, shared, a.rope_dims, treat, g, stream); break;
+    case 128 * 4 + 2: e = launch_d<128, 32, 8, 2>(p, shared, a.rope_dims, treat, g, stream); break;
+    case 256 * 4 + 1: e = launch_d<256, 32, 4, 1>(p, shared, a.rope_dims, treat, g, stream); break;
+    case 256 * 4 + 2: e = launch_d<256, 32, 4, 2>(p, shared, a.rope_dims, treat, g, stream); break;
+    case 512 * 4 + 2: e = launch_d<512, 16, 4, 2>(p, shared, a.rope_dims, treat, g, stream); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || plan.splits == 1) return e;

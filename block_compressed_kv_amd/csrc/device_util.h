@@ -51,13 +51,18 @@ __device__ __forceinline__ void store8(bf16_t* p, const float* f) {
 // [-1/2, 1/2] in double precision so that positions up to 2^40 keep an exact
 // phase; the hardware sine/cosine (argument in turns) then act on the small
 // reduced value.  Returns cos and sin.
-__device__ __forceinline__ void rope_cos_sin(double pos, int k, int r, double log2_base, float* c,
-                                             float* s) {
+__device__ __forceinline__ double rope_turns_per_pos(int k, int r, double log2_base) {
   const double inv_two_pi = 0.15915494309189533576888376337251;
-  const double turns = pos * exp2(-(2.0 * (double)k / (double)r) * log2_base) * inv_two_pi;
+  return exp2(-(2.0 * (double)k / (double)r) * log2_base) * inv_two_pi;
+}
+__device__ __forceinline__ void rope_cos_sin_turns(double turns, float* c, float* s) {
   const float f = (float)(turns - rint(turns));
   *c = __builtin_amdgcn_cosf(f);
   *s = __builtin_amdgcn_sinf(f);
+}
+__device__ __forceinline__ void rope_cos_sin(double pos, int k, int r, double log2_base, float* c,
+                                             float* s) {
+  rope_cos_sin_turns(pos * rope_turns_per_pos(k, r, log2_base), c, s);
 }
 
 template <int WIDTH>
@@ -130,6 +135,14 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 __device__ __forceinline__ s16x4 lds_read_tr16(const bf16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)(p)));
+}
+
+// 16-byte load from a global-memory byte address (global, not flat: a flat
+// access would also count against the LDS wait counter).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 gbl_u32x4;
+__device__ __forceinline__ uint4 ldg16(uintptr_t a) {
+  return __builtin_bit_cast(uint4, *reinterpret_cast<gbl_u32x4*>(a));
 }
 
 }  // namespace lbca

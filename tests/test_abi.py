@@ -124,6 +124,9 @@ def _decode(ws=None, ws_bytes=0, **kw):
     (dict(dtype=0, dim=96), -2),
     (dict(dtype=0, pooled_v=None, raw_v=None, rmsnorm_eps=1e-6), -2),
     (dict(out=FAKE + 4), -1),
+    (dict(entries=1 << 23), -2),                               # pooled slice of 2 GiB at 128 dims
+    (dict(raw_rows=1 << 23), -2),
+    (dict(batch=65536), -2),
 ])
 def test_decode_validation(kw, code):
     st, st2, _ = _decode(**kw)

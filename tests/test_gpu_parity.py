@@ -183,6 +183,43 @@ def test_decode_workspace_reuse_and_graph_replay(lib):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("d,Hq,Hkv,shared", [(128, 24, 8, False), (128, 16, 8, True), (64, 8, 8, False)])
+def test_decode_one_split_rows_past_the_list(lib, d, Hq, Hkv, shared):
+    # 16 sequences x 8 KV heads: one workgroup (group) per unit, the path that
+    # requests the first pooled rows before reading the position.  Every row
+    # outside a sequence's visible list (pooled capacity past n_pooled, raw rows
+    # past t) holds NaN and must not reach the output.
+    m, W, cap = 64, 128, 520
+    t_list = [33000, 32767, 32768 + 63, 200, 0, 127, 128, 191, 192, 5000, 20000, 33407, 1000,
+              64 * 300 + 5, 64 * 17, 64 * 23 + 127]
+    B = len(t_list)
+    g = lambda n, shape: synth.normal(shape, synth.seed_of("dec-1split", n, d, shared), dtype="bf16",
+                                      device=DEV)
+    q = g("q", (B, Hq, d))
+    pk, rk = g("pk", (B, Hkv, cap, d)), g("rk", (B, Hkv, 256, d))
+    pv, rv = (None, None) if shared else (g("pv", (B, Hkv, cap, d)), g("rv", (B, Hkv, 256, d)))
+    base = []
+    for b, t in enumerate(t_list):
+        n_p, rb = O.visible_range(t, m, W, O.EXCLUSIVE)
+        base.append(rb)
+        for x in (pk, pv):
+            if x is not None:
+                x[b, :, n_p:] = float("nan")
+        for x in (rk, rv):
+            if x is not None:
+                x[b, :, t - rb + 1:] = float("nan")
+    pos, rpb = torch.tensor(t_list, device=DEV), torch.tensor(base, device=DEV)
+    kw = dict(pooled_v=pv, raw_v=rv, raw_pos_base=rpb)
+    assert lib.decode_workspace_bytes(q, pk, rk, pos, m, W, O.EXCLUSIVE, **kw) == 0, "expected one split"
+    o, lse = lib.attend_decode(q, pk, rk, pos, m, W, O.EXCLUSIVE, **kw)
+    hv = lambda x: None if x is None else host(x)
+    ro, rl = O.attend_decode(host(q), host(pk), hv(pv), host(rk), hv(rv), t_list, m, W, O.EXCLUSIVE,
+                             1 / math.sqrt(d), raw_pos_base=base)
+    say(f"one-split decode d={d} Hq={Hq} Hkv={Hkv} shared={shared}")
+    check_bf16(host(o), ro, "one-split decode out")
+    check_bf16(host(lse), rl, "one-split decode lse")
+
+
 def test_decode_raw_pos_base_and_overlap(lib):
     B, Hq, Hkv, d, m, W = 3, 8, 2, 64, 16, 40
     t_list, base = [700, 333, 45], [600, 290, 0]
