@@ -43,8 +43,8 @@
 #include "device_util.h"
 #include "lbca_internal.h"
 
-#ifndef LBCA_DECODE_TARGET_WAVES
-#define LBCA_DECODE_TARGET_WAVES 1024  // waves a decode launch aims for (256 CUs x 4 SIMDs)
+#ifndef LBCA_DECODE_TILES_PER_WAVE
+#define LBCA_DECODE_TILES_PER_WAVE 4  // tiles per wave above which a unit's rows are split
 #endif
 
 namespace lbca {
@@ -715,12 +715,13 @@ DecodePlan plan_decode(const lbca_decode_args& a) {
   const int64_t rows = sel_max + raw_max;
   const int64_t tiles = (sel_max + pl.tile_rows - 1) / pl.tile_rows + (raw_max + pl.tile_rows - 1) / pl.tile_rows;
   const int64_t units = a.batch * a.kv_heads * pl.head_groups;
-  // waves per unit: enough for ~LBCA_DECODE_TARGET_WAVES in total, never more
-  // than there are tiles; split partials (16 heads x dim fp32 per workgroup, for
-  // every head group of a KV head) kept under a quarter of the K/V bytes.
-  int64_t wpu = units > 0 ? (LBCA_DECODE_TARGET_WAVES + units - 1) / units : 1;
-  if (wpu > tiles) wpu = tiles;
-  int64_t s = (wpu + nw - 1) / nw;
+  // Splits: only when a unit's tiles would give its waves more than
+  // LBCA_DECODE_TILES_PER_WAVE each (one workgroup per unit keeps every tile's
+  // loads in flight at once and needs no merge launch, which costs more than
+  // the few extra tiles per wave); split partials (16 heads x dim fp32 per
+  // workgroup, for every head group of a KV head) kept under a quarter of the
+  // K/V bytes.
+  int64_t s = (tiles + nw * LBCA_DECODE_TILES_PER_WAVE - 1) / (nw * LBCA_DECODE_TILES_PER_WAVE);
   const int64_t kv_bytes = rows * a.dim * 2 * (a.pooled_v ? 2 : 1);
   const int64_t part_bytes = (int64_t)pl.head_groups * 16 * (a.dim + 2) * 4;
   const int64_t by_traffic = kv_bytes / (4 * part_bytes) > 0 ? kv_bytes / (4 * part_bytes) : 1;

@@ -135,13 +135,16 @@ def test_decode_validation(kw, code):
 
 @fake_ptr
 def test_decode_workspace_required():
-    st, st2, need = _decode()
+    big = dict(entries=8192)                            # long row lists are split over workgroups
+    st, st2, need = _decode(**big)
     assert st == 0 and need > 0
     assert st2 == lbca.ERR_WORKSPACE                    # no workspace given
-    _, st3, _ = _decode(ws=FAKE, ws_bytes=need - 1)
+    _, st3, _ = _decode(ws=FAKE, ws_bytes=need - 1, **big)
     assert st3 == lbca.ERR_WORKSPACE
-    _, st4, _ = _decode(ws=FAKE + 8, ws_bytes=need)
+    _, st4, _ = _decode(ws=FAKE + 8, ws_bytes=need, **big)
     assert st4 == lbca.ERR_WORKSPACE                    # misaligned workspace
+    st5, _, need5 = _decode()                           # 510 entries: one workgroup per unit
+    assert st5 == 0 and need5 == 0
 
 
 def _prefill(**kw):

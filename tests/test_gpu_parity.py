@@ -145,21 +145,23 @@ def test_decode_gqa_bf16(lib, t_list):
 def test_decode_workspace_reuse_and_graph_replay(lib):
     # split path: one workspace reused by many calls, eager and replayed from a graph,
     # with other work in between, always reproduces the first result bit for bit
-    B, Hq, Hkv, d, m, W, T = 2, 24, 8, 128, 64, 128, 512 * 64 + 192
+    B, Hq, Hkv, d, m, W = 2, 24, 8, 128, 64, 128
     g = lambda n, shape: synth.normal(shape, synth.seed_of("dec-reuse", n), dtype="bf16", device=DEV)
     q, q2 = g("q", (B, Hq, d)), g("q2", (B, Hq, d))
-    pk, pv = g("pk", (B, Hkv, 512, d)), g("pv", (B, Hkv, 512, d))
-    rk, rv = g("rk", (B, Hkv, T, d)), g("rv", (B, Hkv, T, d))
-    pos = torch.tensor([512 * 64 + 127, 300 * 64 + 77], device=DEV)   # 512 and 300 pooled entries
-    kw = dict(pooled_v=pv, raw_v=rv)
+    pk, pv = g("pk", (B, Hkv, 2048, d)), g("pv", (B, Hkv, 2048, d))
+    rk, rv = g("rk", (B, Hkv, 256, d)), g("rv", (B, Hkv, 256, d))
+    t_list = [2048 * 64 + 127, 1300 * 64 + 77]                        # 2048 and 1299 pooled entries
+    base = [O.visible_range(t, m, W, O.EXCLUSIVE)[1] for t in t_list]
+    pos, rpb = torch.tensor(t_list, device=DEV), torch.tensor(base, device=DEV)
+    kw = dict(pooled_v=pv, raw_v=rv, raw_pos_base=rpb)
     need = lib.decode_workspace_bytes(q, pk, rk, pos, m, W, O.EXCLUSIVE, **kw)
     assert need > 0, "this shape should split the rows across workgroups"
     ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=DEV)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
     ref_o, ref_l = lib.attend_decode(q, pk, rk, pos, m, W, O.EXCLUSIVE, **kw)
-    ro, _ = O.attend_decode(host(q), host(pk), host(pv), host(rk), host(rv), pos.tolist(), m, W,
-                            O.EXCLUSIVE, 1 / math.sqrt(d))
+    ro, _ = O.attend_decode(host(q), host(pk), host(pv), host(rk), host(rv), t_list, m, W,
+                            O.EXCLUSIVE, 1 / math.sqrt(d), raw_pos_base=base)
     check_bf16(host(ref_o), ro, "reference call")
     for _ in range(5):
         lib.attend_decode(q, pk, rk, pos, m, W, O.EXCLUSIVE, out=out, lse=lse, workspace=ws, **kw)
@@ -249,12 +251,13 @@ def test_decode_invalid_sequence_gets_nan(lib):
     assert torch.isnan(o[2]).all() and torch.isnan(lse[2]).all()
 
 
-@pytest.mark.parametrize("rd", [0, 64])
-def test_decode_hca_treated(lib, rd):
-    # HCA-style MQA: shared series, 64 heads, d=512, m'=128, RMSNorm, partial RoPE, sink
+@pytest.mark.parametrize("rd,nb", [(0, 12), (64, 12), (64, 300)])
+def test_decode_hca_treated(lib, rd, nb):
+    # HCA-style MQA: shared series, 64 heads, d=512, m'=128, RMSNorm, partial RoPE, sink;
+    # 300 blocks split each sequence's rows over several workgroups
     B, Hq, d, m, W = 2, 64, 512, 128, 128
-    T = 128 * 12 + 77
-    H = _dev(synth.hca_layer(f"dec-hca-{rd}", B, Hq, T, d, m))
+    T = 128 * nb + 77
+    H = _dev(synth.hca_layer(f"dec-hca-{rd}-{nb}", B, Hq, T, d, m))
     t_list = [T - 1, 128 * 5 + 3]
     N = T // m
     entries = torch.zeros((B, 1, N, d), dtype=torch.bfloat16, device=DEV)
