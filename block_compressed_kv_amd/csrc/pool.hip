@@ -17,7 +17,9 @@
 // every group streams its own block; with few rows (the single block that
 // falls out of the window at a decode step) P grows so that every lane has
 // one short burst of loads in flight, and the P partial states are merged in
-// LDS in a fixed order.  The optional HCA/CSA entry treatment (RMSNorm, partial
+// a fixed tree order, by lane exchanges inside a wave and through LDS across
+// waves (a sequential merge by one group costs more than the loads).  The
+// optional HCA/CSA entry treatment (RMSNorm, partial
 // RoPE at the block start) runs on the finished fp32 row before the single
 // rounding to the storage type.
 #include "device_util.h"
@@ -110,18 +112,29 @@ struct PoolAcc {
       fold<1>(xs + i * dim, HAS_V ? vs + i * dim : nullptr, zs + i * dim, bs + i * dim, stride);
   }
 
-  // Merge another partial state (same channels) into this one.
-  __device__ __forceinline__ void merge(const float* omx, const float* ol, const float* oax,
-                                        const float* oav) {
+  // Combine channel c of two partial states, lower token phase first
+  // (branch-free; two empty states stay empty).
+  __device__ __forceinline__ void combine1(int c, float lmx, float ll, float lax, float lav,
+                                           float hmx, float hl, float hax, float hav) {
+    const float nm = fmaxf(lmx, hmx);
+    const bool none = nm == kNegInf;
+    const float a = none ? 0.f : exp2f(lmx - nm), b = none ? 0.f : exp2f(hmx - nm);
+    l[c] = ll * a + hl * b;
+    ax[c] = lax * a + hax * b;
+    av[c] = HAS_V ? lav * a + hav * b : 0.f;
+    mx[c] = nm;
+  }
+
+  // Merge with the state of lane (lane ^ off); `lower`: this lane holds the
+  // lower phase.  Both lanes of a pair evaluate the same expression.
+  __device__ __forceinline__ void merge_xor(int off, bool lower) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const float nm = fmaxf(mx[c], omx[c]);
-      if (nm == kNegInf) continue;
-      const float a = exp2f(mx[c] - nm), b = exp2f(omx[c] - nm);
-      l[c] = l[c] * a + ol[c] * b;
-      ax[c] = ax[c] * a + oax[c] * b;
-      if constexpr (HAS_V) av[c] = av[c] * a + oav[c] * b;
-      mx[c] = nm;
+      const float omx = __shfl_xor(mx[c], off, 64), ol = __shfl_xor(l[c], off, 64);
+      const float oax = __shfl_xor(ax[c], off, 64);
+      const float oav = HAS_V ? __shfl_xor(av[c], off, 64) : 0.f;
+      combine1(c, lower ? mx[c] : omx, lower ? l[c] : ol, lower ? ax[c] : oax, lower ? av[c] : oav,
+               lower ? omx : mx[c], lower ? ol : l[c], lower ? oax : ax[c], lower ? oav : av[c]);
     }
   }
 };
@@ -165,27 +178,32 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
     }
   }
 
-  if (P > 1) {  // fixed-order merge of the phases through LDS
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      part[c][tid] = acc.mx[c];
-      part[8 + c][tid] = acc.l[c];
-      part[16 + c][tid] = acc.ax[c];
-      part[24 + c][tid] = acc.av[c];
-    }
-    __syncthreads();
-    if (phase == 0) {
-      for (int ph = 1; ph < P; ++ph) {
-        const int src = tid + ph * L;
-        float omx[8], ol[8], oax[8], oav[8];
+  // Merge the P phases of a row in a fixed order: inside a wave by lane
+  // exchanges (phases of a row sit in consecutive groups), then across the
+  // row's waves through LDS, read by the row's first wave.
+  if (P > 1) {
+    const int span = L * P;  // lanes of one row
+    for (int off = L; off < 64 && off < span; off <<= 1) acc.merge_xor(off, (lane & off) == 0);
+    if (span > 64) {
+      const int wave = tid >> 6, waves_per_row = span >> 6;
+      if (lane < L) {  // the wave's lowest phase group holds its merge
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          omx[c] = part[c][src];
-          ol[c] = part[8 + c][src];
-          oax[c] = part[16 + c][src];
-          oav[c] = part[24 + c][src];
+          part[c][tid] = acc.mx[c];
+          part[8 + c][tid] = acc.l[c];
+          part[16 + c][tid] = acc.ax[c];
+          part[24 + c][tid] = acc.av[c];
         }
-        acc.merge(omx, ol, oax, oav);
+      }
+      __syncthreads();
+      if ((wave & (waves_per_row - 1)) == 0) {
+        for (int w = 1; w < waves_per_row; ++w) {
+          const int src = tid + 64 * w;
+#pragma unroll
+          for (int c = 0; c < 8; ++c)
+            acc.combine1(c, acc.mx[c], acc.l[c], acc.ax[c], acc.av[c], part[c][src], part[8 + c][src],
+                         part[16 + c][src], part[24 + c][src]);
+        }
       }
     }
   }
