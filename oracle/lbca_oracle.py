@@ -12,7 +12,7 @@ Pages cited (title, then section):
   [CSA]   "CSA: Compressed Sparse Attention (toy implementation)"
           (mailtotanvir.github.io/mastering-deepseek-v4-architecture/architecture/csa/)
 
-Readings where the pages are silent or garbled (all listed in the design doc):
+Readings where the pages are silent or garbled:
   * Two visibility rules.  LBCA ([mSeek] "How LBCA works", steps 4-5, and the
     "Results" table) pools a block only once it is complete AND wholly older
     than the W-token window; the raw span runs from the first unpooled block to
