@@ -203,9 +203,8 @@ def attend_decode(q, pooled_k, raw_k, pos, block, window, mode, out=None, lse=No
     need = ctypes.c_size_t()
     _check(lib().lbca_attend_decode_workspace(ctypes.byref(a), ctypes.byref(need)),
            "lbca_attend_decode_workspace")
-    if workspace is None and need.value > 0:
-        # arrival counters at the start must be zero before first use (calls leave them zero)
-        workspace = torch.zeros(need.value, dtype=torch.uint8, device=q.device)
+    if workspace is None and need.value > 0:  # split partials; contents on entry do not matter
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().lbca_attend_decode(ctypes.byref(a), _p(workspace), ws_bytes, _stream(stream)),
            "lbca_attend_decode")

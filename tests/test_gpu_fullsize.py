@@ -1,0 +1,177 @@
+"""GPU parity at the workloads' full sizes, in the launch shapes bench.py times.
+
+The GPU runs every call at full size; the fp64 oracle recomputes sampled
+outputs (whole units, query positions or sequences) one by one, from the same
+seeded inputs copied exactly to the host.  Tolerances: tests/parity_util.py.
+
+  * Llama-3.2-3B decode at 32K, batch 16: all 510 blocks pooled, one decode
+    launch; three (sequence, KV head) units checked (pooled entries and the
+    three query heads of each).
+  * Chunked prefill at 16K in 2048-token chunks: every chunk pools its new
+    blocks then attends; all pooled entries and 16 query positions (chunk
+    edges, window edges, random) checked for all 24 heads.
+  * HCA at 1M context, batch 4: 8192 treated entries pooled, decode with
+    RMSNorm, partial RoPE and a sink; one sequence recomputed by the oracle,
+    which streams its 2^20 tokens block range by block range.
+  * CSA at 128K, batch 2: dual pooling of 32768 treated entries, indexer
+    top-512 over 32768 keys (sets compared exactly), decode over the selection
+    plus the window.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_compressed_kv_amd import synth
+from oracle import lbca_oracle as O
+
+from parity_util import check_bf16, host, say, topk_matches
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+EPS, RD, BASE = 1e-6, 64, 10000.0
+
+
+def _cpu(t):
+    return t.detach().to("cpu")
+
+
+def test_llama_decode_32k_batch16(lib):
+    B, Hq, Hkv, d, m, W, T, N = 16, 24, 8, 128, 64, 128, 32768, 510
+    G = Hq // Hkv
+    say(f"full-size LBCA decode B={B} T={T}: generating")
+    L = synth.lbca_layer(("full-llama-32k",), B, Hq, Hkv, T, d, m, "bf16", "f32", device=DEV)
+    pk = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=DEV)
+    pv = torch.empty_like(pk)
+    say("pool 510 blocks, decode at t=32767")
+    lib.pool_blocks(L["k"], L["z"], L["bias"], m, 0, N, pk, v=L["v"], out_v=pv)
+    q = L["q"][:, 0].contiguous()
+    pos = torch.full((B,), T - 1, dtype=torch.int64, device=DEV)
+    o, lse = lib.attend_decode(q, pk, L["k"], pos, m, W, O.EXCLUSIVE, pooled_v=pv, raw_v=L["v"])
+    torch.cuda.synchronize()
+    for b, kh in ((0, 0), (7, 5), (15, 7)):
+        say(f"oracle unit b={b} kv head={kh}")
+        ks, vs = _cpu(L["k"][b:b + 1, kh:kh + 1]), _cpu(L["v"][b:b + 1, kh:kh + 1])
+        zs, bias = _cpu(L["z"][b:b + 1, kh:kh + 1]), _cpu(L["bias"][kh:kh + 1])
+        rk, rv = O.pool_single(ks, zs, bias, m, 0, N, values=vs)
+        check_bf16(host(pk[b, kh]), rk[0, 0], f"pooled K b={b} h={kh}")
+        check_bf16(host(pv[b, kh]), rv[0, 0], f"pooled V b={b} h={kh}")
+        qh = _cpu(q[b:b + 1, kh * G:(kh + 1) * G])
+        ro, rl = O.attend_decode(qh, rk, rv, ks, vs, [T - 1], m, W, O.EXCLUSIVE, 1 / math.sqrt(d))
+        check_bf16(host(o[b, kh * G:(kh + 1) * G]), ro[0], f"decode out b={b} h={kh}")
+        check_bf16(host(lse[b, kh * G:(kh + 1) * G]), rl[0], f"decode lse b={b} h={kh}")
+
+
+def test_llama_chunked_prefill_16k(lib):
+    B, Hq, Hkv, d, m, W, T, chunk = 1, 24, 8, 128, 16, 128, 16384, 2048
+    say(f"full-size chunked prefill T={T} chunk={chunk}: generating")
+    L = synth.lbca_layer(("full-prefill-16k",), B, Hq, Hkv, T, d, m, "bf16", "f32", device=DEV, q_len=T)
+    N = T // m
+    pk = torch.zeros((B, Hkv, N, d), dtype=torch.bfloat16, device=DEV)
+    pv = torch.zeros_like(pk)
+    out = torch.empty((B, T, Hq, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device=DEV)
+    done = 0
+    for c0 in range(0, T, chunk):
+        need, _ = O.visible_range(c0 + chunk - 1, m, W, O.EXCLUSIVE)
+        lib.pool_blocks(L["k"], L["z"], L["bias"], m, done, need, pk, v=L["v"], out_v=pv)
+        done = need
+        qc = L["q"][:, c0:c0 + chunk].contiguous()
+        lib.attend_prefill(qc, c0, pk, L["k"], 0, m, W, O.EXCLUSIVE, out=out[:, c0:c0 + chunk],
+                            lse=lse[:, c0:c0 + chunk], pooled_v=pv, raw_v=L["v"])
+    torch.cuda.synchronize()
+    say("oracle pooling of every block")
+    ks, vs, zs, bias = _cpu(L["k"]), _cpu(L["v"]), _cpu(L["z"]), _cpu(L["bias"])
+    rk, rv = O.pool_single(ks, zs, bias, m, 0, done, values=vs)
+    check_bf16(host(pk[:, :, :done]), rk, "pooled K")
+    check_bf16(host(pv[:, :, :done]), rv, "pooled V")
+    rng = np.random.default_rng(16384)
+    ts = sorted({0, 1, 127, 128, 2047, 2048, 4095, 8191, 8192 + 77, 14335, 14336, 16383,
+                 *rng.integers(0, T, 4).tolist()})
+    q = _cpu(L["q"])
+    for t in ts:
+        ro, rl = O.attend_prefill(q[:, t:t + 1], t, rk, rv, ks, vs, 0, m, W, O.EXCLUSIVE,
+                                  1 / math.sqrt(d))
+        check_bf16(host(out[:, t:t + 1]), ro, f"prefill out t={t}")
+        check_bf16(host(lse[:, t:t + 1]), rl, f"prefill lse t={t}")
+
+
+def test_hca_decode_1m_batch4(lib):
+    B, Hq, d, m, W, T = 4, 64, 512, 128, 128, 1 << 20
+    N = T // m
+    say(f"full-size HCA decode B={B} T={T}: generating")
+    H = synth.hca_layer(("full-hca-1m",), B, Hq, T, d, m, device=DEV)
+    ent = torch.empty((B, 1, N, d), dtype=torch.bfloat16, device=DEV)
+    say("pool 8192 treated entries, decode at t=2^20-1")
+    lib.pool_blocks(H["c"], H["z"], H["bias"], m, 0, N, ent, rmsnorm_eps=EPS, rope_dims=RD, rope_base=BASE)
+    pos = torch.full((B,), T - 1, dtype=torch.int64, device=DEV)
+    o, lse = lib.attend_decode(H["q"], ent, H["c"], pos, m, W, O.OVERLAP, sink=H["sink"],
+                                rmsnorm_eps=EPS, rope_dims=RD, rope_base=BASE)
+    torch.cuda.synchronize()
+    b = 2
+    say(f"oracle: stream sequence {b} ({N} blocks)")
+    bias = _cpu(H["bias"])
+    parts = []
+    step = 1024
+    for j0 in range(0, N, step):
+        cs = _cpu(H["c"][b:b + 1, :, j0 * m:(j0 + step) * m])
+        zs = _cpu(H["z"][b:b + 1, :, j0 * m:(j0 + step) * m])
+        parts.append(O.pool_single(cs, zs, bias, m, 0, step))
+    pooled = np.concatenate(parts, axis=2)                       # [1, 1, N, d]
+    treated = O.rope(O.rmsnorm(pooled, EPS), np.arange(N) * m, RD, BASE)
+    check_bf16(host(ent[b:b + 1]), treated, "treated HCA entries")
+    raw = _cpu(H["c"][b:b + 1, :, T - W:])
+    ro, rl = O.attend_decode(_cpu(H["q"][b:b + 1]), pooled, None, raw, None, [T - 1], m, W, O.OVERLAP,
+                             1 / math.sqrt(d), raw_pos_base=[T - W], sink=_cpu(H["sink"]),
+                             rmsnorm_eps=EPS, rope_dims=RD, rope_base=BASE)
+    check_bf16(host(o[b:b + 1]), ro, "HCA decode out")
+    check_bf16(host(lse[b:b + 1]), rl, "HCA decode lse")
+
+
+def test_csa_decode_128k_batch2(lib):
+    B, Hq, d, m, W, T, HI, dI, k = 2, 64, 512, 4, 128, 1 << 17, 8, 64, 512
+    N = T // m
+    say(f"full-size CSA decode B={B} T={T}: generating")
+    C = synth.csa_layer(("full-csa-128k",), B, Hq, T, d, m, HI, dI, device=DEV)
+    # the indexer consumes compressed keys; both sides read these bf16 keys
+    keys = synth.normal((B, N, dI), synth.seed_of("full-csa-128k", "index-keys"), dtype="bf16", device=DEV)
+    ent = torch.empty((B, 1, N, d), dtype=torch.bfloat16, device=DEV)
+    treat = dict(rmsnorm_eps=EPS, rope_dims=RD, rope_base=BASE)
+    say("dual pooling of 32768 treated entries, indexer top-512, decode")
+    lib.pool_blocks(C["ca"], C["za"], C["bias_a"], m, 0, N, ent, xb=C["cb"], zb=C["zb"],
+                     bias_b=C["bias_b"], **treat)
+    pos = torch.full((B,), T - 1, dtype=torch.int64, device=DEV)
+    idx, _ = lib.csa_index_topk(C["qi"], C["w"], keys, pos, m, k)
+    o, lse = lib.attend_decode(C["q"], ent, C["ca"], pos, m, W, O.OVERLAP, sel_idx=idx, sink=C["sink"],
+                                **treat)
+    torch.cuda.synchronize()
+    gidx = _cpu(idx).numpy()
+    qi, w, kh = _cpu(C["qi"]), _cpu(C["w"]), _cpu(keys)
+    sel = np.zeros((B, k), dtype=np.int64)
+    for b in range(B):
+        say(f"oracle indexer sequence {b}")
+        s = O.index_scores(qi[b], w[b], kh[b], N)
+        topk_matches(gidx[b], s, k, f"CSA top-k b={b}")
+        sel[b] = O.topk_select(s, k)
+        assert (sel[b] == gidx[b]).all(), f"selection b={b}"
+    # oracle entries for the selected ids only (entry i: a-block i and b-block i-1)
+    pooled = np.zeros((B, 1, N, d))
+    ba, bb = _cpu(C["bias_a"][0]), _cpu(C["bias_b"][0])
+    for b in range(B):
+        say(f"oracle dual pooling of the selected entries, sequence {b}")
+        for i in sel[b]:
+            lo = max(0, i - 1) * m
+            sl = slice(lo, (i + 1) * m)
+            e = O.pool_dual(_cpu(C["ca"][b:b + 1, :, sl]), _cpu(C["za"][b:b + 1, :, sl]), ba,
+                            _cpu(C["cb"][b:b + 1, :, sl]), _cpu(C["zb"][b:b + 1, :, sl]), bb, m,
+                            i - lo // m, i - lo // m + 1)
+            pooled[b, 0, i] = e[0, 0, 0]
+        treated = O.rope(O.rmsnorm(pooled[b, 0, sel[b]], EPS), sel[b] * m, RD, BASE)
+        check_bf16(host(ent[b, 0, torch.as_tensor(sel[b], device=DEV)]), treated, f"treated CSA entries b={b}")
+    raw = _cpu(C["ca"][:, :, T - W:])
+    ro, rl = O.attend_decode(_cpu(C["q"]), pooled, None, raw, None, [T - 1] * B, m, W, O.OVERLAP,
+                             1 / math.sqrt(d), raw_pos_base=[T - W] * B, sel_idx=sel,
+                             sink=_cpu(C["sink"]), **treat)
+    check_bf16(host(o), ro, "CSA decode out")
+    check_bf16(host(lse), rl, "CSA decode lse")
