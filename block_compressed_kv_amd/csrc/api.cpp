@@ -181,6 +181,10 @@ int lbca_attend_prefill(const lbca_prefill_args* a, void* stream) {
     return LBCA_ERR_INVALID_ARG;
   if (a->dtype == LBCA_BF16) {
     if (!(a->dim == 64 || a->dim == 128)) return LBCA_ERR_UNSUPPORTED;
+    // positive scale (folded into the exponent after the row max); 32-bit rows and positions
+    if (!(a->scale > 0.f) || a->q_len * (a->q_heads / a->kv_heads) >= (int64_t(1) << 31) ||
+        a->q_pos0 + a->q_len >= (int64_t(1) << 31) || a->batch * a->kv_heads >= (int64_t(1) << 31))
+      return LBCA_ERR_UNSUPPORTED;
   } else {
     if (a->dim % 64 != 0 || a->dim > 512) return LBCA_ERR_UNSUPPORTED;
   }

@@ -19,9 +19,11 @@ constexpr float kNegInf = -__builtin_inff();
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32; a in the low half
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;  // v_cvt_pk_bf16_f32, round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2_t));
 }
 
 // 8 consecutive elements <-> 8 floats
@@ -136,6 +138,9 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const bf16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)(p)));
 }
+
+typedef __attribute__((address_space(1))) const void gbl_void;
+typedef __attribute__((address_space(3))) void lds_void;
 
 // 16-byte load from a global-memory byte address (global, not flat: a flat
 // access would also count against the LDS wait counter).

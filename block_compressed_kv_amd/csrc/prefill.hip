@@ -6,24 +6,31 @@
 // clear reference): a query sees every completed summary older than its
 // window plus its exact raw window, never a summary holding a later token.
 //
-// bf16 path (MFMA).  A workgroup of 4 waves owns one (sequence, KV head) and
-// 128 consecutive rows of the flattened (position, query head in the GQA group)
-// space; each wave holds 32 of those rows (two 16-row groups) as B operands.
-// The workgroup walks the union of its rows' visible rows in 32-row tiles:
-// first the pooled prefix [0, n_pooled(last position)), then the raw band
-// [raw_begin(first position), last position].  K and V tiles are staged in LDS
-// (double buffered, the next tile's global loads in flight during the current
-// tile's MFMAs, one barrier per tile).  Scores are computed transposed,
-// S^T = K Q^T (v_mfma_f32_16x16x32_bf16), so each lane owns one query row's
-// scores and the row max/sum need two cross-lane steps; O^T = V^T P^T uses
-// v_mfma_f32_16x16x16_bf16 with P^T straight from the score registers.  A
-// per-element mask applies each row's own visibility inside every tile.
+// bf16 path (MFMA, a dense contraction).  A workgroup of 8 waves (two per
+// SIMD, so one wave's softmax arithmetic runs beside the other's MFMAs) owns
+// one (sequence, KV head) and 256 consecutive rows of the flattened (position,
+// query head in the GQA group) space; each wave holds 32 of those rows (two
+// 16-row groups) as B operands.  The workgroup walks the union of its rows'
+// visible rows in tiles of 32 rows at 128 dims (64 at 64 dims): the pooled
+// prefix [0, n_pooled(last position)), then the raw band [raw_begin(first
+// position), last position].  K and V tiles go straight from global memory to
+// LDS (global_load_lds_dwordx4, no staging registers) in a chunk-swizzled
+// layout, so the 16-byte K reads and the transposing V reads of a 16-lane
+// group hit distinct banks; three buffers keep the next two tiles' loads in
+// flight during a tile's MFMAs, one barrier per tile.  Scores are computed
+// transposed, S^T = K Q^T with v_mfma_f32_16x16x32_bf16, so each lane owns one
+// query row's scores and the row max/sum need a 16- and a 32-lane swap; P^T
+// is then directly the B operand of O^T = V^T P^T (k = 32 keys: two 16-key
+// blocks), whose A operand comes from two transposing LDS reads
+// (ds_read_b64_tr_b16).  Tiles visible to every row skip the per-element mask;
+// a row's reference max moves only when a score exceeds it by 2^8, so the
+// accumulator rescale runs on few tiles.
+#include <type_traits>
+
 #include "device_util.h"
 #include "lbca_internal.h"
 
 namespace lbca {
-
-typedef short s16x4p __attribute__((ext_vector_type(4)));
 
 struct PrefillParams {
   const bf16_t* q;
@@ -39,207 +46,349 @@ struct PrefillParams {
   float scale_log2;
 };
 
-template <int D, bool SHARED>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
-  constexpr int KS = D / 32, DT = D / 16, KT = 32, PITCH = D + 8;
-  constexpr int CH = D / 8;                   // 16-byte chunks per row
-  constexpr int LOADS = (KT * CH) / 256;      // chunks per thread per tile
-  static_assert(LOADS >= 1 && (KT * CH) % 256 == 0, "tile must split evenly");
-  __shared__ __attribute__((aligned(16))) bf16_t ks[2][KT * PITCH];
-  __shared__ __attribute__((aligned(16))) bf16_t vs[SHARED ? 1 : 2][SHARED ? 16 : KT * PITCH];
+// Chunk swizzle of an LDS tile row (16-byte chunks): 8 consecutive rows read at
+// one chunk index, or 4 consecutive rows read at two adjacent chunks, hit
+// distinct banks.  Unchanged when the row moves by 16.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return (2 * r) & 15;
+  else return (2 * (r >> 1)) & 7;
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, kq = lane >> 4;
-  const int64_t bid = blockIdx.x;
-  const int64_t rblk = bid % p.row_blocks;
-  const int64_t bh = bid / p.row_blocks;
-  const int64_t kvh = bh % p.hkv, b = bh / p.hkv;
-  const int64_t rows_total = p.q_len * p.G;
-  const int64_t row0 = rblk * 128;
-  const int64_t row_last = (row0 + 127 < rows_total ? row0 + 127 : rows_total - 1);
-  const int64_t p_first = p.q_pos0 + row0 / p.G;
-  const int64_t p_last = p.q_pos0 + row_last / p.G;
+// Wait until at most N vector-memory operations of this wave are in flight
+// (other counters untouched).
+template <int N>
+__device__ __forceinline__ void vmcnt_wait() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
-  // my two 16-row query groups
-  uint4 qr[2][KS];
-  int64_t my_np[2], my_rb[2], my_pos[2], my_out[2];
-  bool my_ok[2];
+// All transposing V reads of one tile (16 ds_read_b64_tr_b16) in one block
+// that also waits for them.  Written as one asm block because the compiler
+// cannot tell which LDS buffer the intrinsic form reads and would wait for
+// every tile load still in flight; the block's outputs are early-clobber and
+// all used, and it ends with the wait for its own reads.  Slot o = (c*DT+t)*2+h
+// holds rows 32c + 16h + 4kq.. of column 16t + n (c: 32-key chunk, h: half).
+template <int D>
+__device__ __forceinline__ void read_v_tiles(s16x4 (&r)[16], const bf16_t* vt, int n, int kq, int swz_tr) {
+  constexpr int DT = D / 16;
+  const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) bf16_t*)(vt);
+  uint32_t ad[DT];
 #pragma unroll
-  for (int gq = 0; gq < 2; ++gq) {
-    const int64_t r = row0 + wave * 32 + gq * 16 + n;
+  for (int t = 0; t < DT; ++t)
+    ad[t] = base + 2u * (uint32_t)((4 * kq + (n >> 2)) * D + 4 * (n & 1) + 8 * ((2 * t + ((n & 3) >> 1)) ^ swz_tr));
+  if constexpr (D == 128) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16\n"
+        "ds_read_b64_tr_b16 %1, %16 offset:4096\n"
+        "ds_read_b64_tr_b16 %2, %17\n"
+        "ds_read_b64_tr_b16 %3, %17 offset:4096\n"
+        "ds_read_b64_tr_b16 %4, %18\n"
+        "ds_read_b64_tr_b16 %5, %18 offset:4096\n"
+        "ds_read_b64_tr_b16 %6, %19\n"
+        "ds_read_b64_tr_b16 %7, %19 offset:4096\n"
+        "ds_read_b64_tr_b16 %8, %20\n"
+        "ds_read_b64_tr_b16 %9, %20 offset:4096\n"
+        "ds_read_b64_tr_b16 %10, %21\n"
+        "ds_read_b64_tr_b16 %11, %21 offset:4096\n"
+        "ds_read_b64_tr_b16 %12, %22\n"
+        "ds_read_b64_tr_b16 %13, %22 offset:4096\n"
+        "ds_read_b64_tr_b16 %14, %23\n"
+        "ds_read_b64_tr_b16 %15, %23 offset:4096\n"
+        "s_waitcnt lgkmcnt(0)\n"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+          "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]),
+          "=&v"(r[14]), "=&v"(r[15])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
+        : "memory");
+  } else {
+    static_assert(D == 64, "transposing V reads are laid out for 64 or 128 dims");
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16\n"
+        "ds_read_b64_tr_b16 %1, %16 offset:2048\n"
+        "ds_read_b64_tr_b16 %2, %17\n"
+        "ds_read_b64_tr_b16 %3, %17 offset:2048\n"
+        "ds_read_b64_tr_b16 %4, %18\n"
+        "ds_read_b64_tr_b16 %5, %18 offset:2048\n"
+        "ds_read_b64_tr_b16 %6, %19\n"
+        "ds_read_b64_tr_b16 %7, %19 offset:2048\n"
+        "ds_read_b64_tr_b16 %8, %16 offset:4096\n"
+        "ds_read_b64_tr_b16 %9, %16 offset:6144\n"
+        "ds_read_b64_tr_b16 %10, %17 offset:4096\n"
+        "ds_read_b64_tr_b16 %11, %17 offset:6144\n"
+        "ds_read_b64_tr_b16 %12, %18 offset:4096\n"
+        "ds_read_b64_tr_b16 %13, %18 offset:6144\n"
+        "ds_read_b64_tr_b16 %14, %19 offset:4096\n"
+        "ds_read_b64_tr_b16 %15, %19 offset:6144\n"
+        "s_waitcnt lgkmcnt(0)\n"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+          "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]),
+          "=&v"(r[14]), "=&v"(r[15])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+        : "memory");
+  }
+}
+
+template <int D, bool SHARED>
+__global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
+  constexpr int NWV = 8;                 // waves per workgroup: two per SIMD
+  constexpr int NT = NWV * 64;
+  constexpr int QG = 2;                  // 16-row query groups per wave
+  constexpr int KT = D <= 64 ? 64 : 32;  // keys per tile (registers bound it at 128 dims)
+  constexpr int KB = KT / 16;            // 16-key blocks per tile
+  constexpr int KS = D / 32;             // 32-wide head-dim chunks (Q.K contraction)
+  constexpr int DT = D / 16;             // 16-wide output dim blocks
+  constexpr int CH = D / 8;              // 16-byte chunks per row
+  constexpr int CALLS = KT * CH / NT;    // LDS loads per thread per tile and series
+  constexpr int ROWS = NWV * QG * 16;    // query rows per workgroup
+  constexpr int LPT = CALLS * (SHARED ? 1 : 2);  // vector-memory ops per wave per tile
+  static_assert(KT * CH % NT == 0, "every thread loads whole chunks");
+  static_assert(ROWS == 256, "the launcher sizes the grid for 256 rows per workgroup");
+  // three tile buffers (two tiles of loads in flight), each its own array so
+  // the compiler can tell a read of one from the loads into another
+  constexpr int VSZ = SHARED ? 8 : KT * D;
+  __shared__ __attribute__((aligned(16))) bf16_t ks0[KT * D], ks1[KT * D], ks2[KT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t vs0[VSZ], vs1[VSZ], vs2[VSZ];
+  auto kbuf = [&](auto c) __attribute__((always_inline)) -> bf16_t* {
+    if constexpr (decltype(c)::value == 0) return ks0;
+    else if constexpr (decltype(c)::value == 1) return ks1;
+    else return ks2;
+  };
+  auto vbuf = [&](auto c) __attribute__((always_inline)) -> bf16_t* {
+    if constexpr (SHARED) return kbuf(c);
+    else if constexpr (decltype(c)::value == 0) return vs0;
+    else if constexpr (decltype(c)::value == 1) return vs1;
+    else return vs2;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (LDS load bases)
+  const int n = lane & 15, kq = lane >> 4;
+  const int swz_n = swz<D>(n), swz_tr = swz<D>(4 * kq + (n >> 2));  // (invariant under +16 rows)
+  const int bid = blockIdx.x;
+  const int rblk = bid % p.row_blocks;
+  const int bh = bid / p.row_blocks;
+  const int kvh = bh % (int)p.hkv, b = bh / (int)p.hkv;
+  const int G = (int)p.G;
+  const int rows_total = (int)p.q_len * G;
+  const int row0 = rblk * ROWS;
+  const int row_last = row0 + ROWS - 1 < rows_total ? row0 + ROWS - 1 : rows_total - 1;
+  const int q0 = (int)p.q_pos0;
+  const int p_first = q0 + row0 / G, p_last = q0 + row_last / G;
+
+  // this wave's 16-row query groups: B operands and per-row visibility
+  uint4 qr[QG][KS];
+  int my_np[QG], my_rb[QG], my_pos[QG];
+  int64_t my_out[QG];
+  bool my_ok[QG];
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    const int r = row0 + wave * (QG * 16) + g * 16 + n;
     const bool ok = r < rows_total;
-    const int64_t rr = ok ? r : rows_total - 1;
-    const int64_t pl = rr / p.G, g = rr % p.G;
-    const int64_t t = p.q_pos0 + pl;
-    visible_range(t, p.m, p.W, p.mode, &my_np[gq], &my_rb[gq]);
-    my_pos[gq] = t;
-    my_ok[gq] = ok;
-    my_out[gq] = ((b * p.q_len + pl) * p.hq + kvh * p.G + g) * D;
-    const bf16_t* qrow = p.q + my_out[gq] + 8 * kq;
+    const int rr = ok ? r : rows_total - 1;
+    const int pl = rr / G, hg = rr - pl * G;
+    int64_t np, rb;
+    visible_range(q0 + pl, p.m, p.W, p.mode, &np, &rb);
+    my_np[g] = (int)np;
+    my_rb[g] = (int)rb;
+    my_pos[g] = q0 + pl;
+    my_ok[g] = ok;
+    my_out[g] = (((int64_t)b * p.q_len + pl) * p.hq + (int64_t)kvh * G + hg) * D;
+    const bf16_t* qrow = p.q + my_out[g] + 8 * kq;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      qr[gq][s] = ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s) : make_uint4(0, 0, 0, 0);
+      qr[g][s] = ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s) : make_uint4(0, 0, 0, 0);
   }
 
-  int64_t NP, RB, dummy;
-  visible_range(p_last, p.m, p.W, p.mode, &NP, &dummy);
-  visible_range(p_first, p.m, p.W, p.mode, &dummy, &RB);
-  const int64_t T1 = (NP + KT - 1) / KT;
-  const int64_t T2 = (p_last - RB + 1 + KT - 1) / KT;
-  const int64_t T = T1 + T2;
-  const int64_t kv_pool = (b * p.hkv + kvh) * p.entries;
-  const int64_t kv_raw = (b * p.hkv + kvh) * p.raw_rows - p.raw_pos_base;
+  int64_t t64a, t64b;
+  visible_range(p_last, p.m, p.W, p.mode, &t64a, &t64b);
+  const int NP = (int)t64a, RBmax = (int)t64b;
+  visible_range(p_first, p.m, p.W, p.mode, &t64a, &t64b);
+  const int NPmin = (int)t64a, RB = (int)t64b;
+  const int T1 = (NP + KT - 1) / KT;
+  const int T = T1 + (p_last - RB + 1 + KT - 1) / KT;
+  // slice bases as integers (a pointer select from the argument block would
+  // become a private-memory lookup)
+  const uintptr_t pk_base = reinterpret_cast<uintptr_t>(p.pk) + ((int64_t)bh * p.entries) * (D * 2);
+  const uintptr_t pv_base = reinterpret_cast<uintptr_t>(SHARED ? p.pk : p.pv) + ((int64_t)bh * p.entries) * (D * 2);
+  const uintptr_t rk_base = reinterpret_cast<uintptr_t>(p.rk) + ((int64_t)bh * p.raw_rows - p.raw_pos_base) * (D * 2);
+  const uintptr_t rv_base = reinterpret_cast<uintptr_t>(SHARED ? p.rk : p.rv) + ((int64_t)bh * p.raw_rows - p.raw_pos_base) * (D * 2);
 
-  uint4 kreg[LOADS], vreg[SHARED ? 1 : LOADS];
-  auto load_tile = [&](int64_t tile) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / CH, col = c % CH;
-      int64_t row;
-      bool ok;
-      const bf16_t *kb, *vb;
-      if (tile < T1) {
-        const int64_t j = tile * KT + r;
-        ok = j < NP;
-        row = kv_pool + j;
-        kb = p.pk;
-        vb = p.pv;
-      } else {
-        const int64_t s = RB + (tile - T1) * KT + r;
-        ok = s <= p_last;
-        row = kv_raw + s;
-        kb = p.rk;
-        vb = p.rv;
-      }
-      kreg[i] = ok ? *reinterpret_cast<const uint4*>(kb + row * D + col * 8) : make_uint4(0, 0, 0, 0);
-      if (!SHARED)
-        vreg[i] = ok ? *reinterpret_cast<const uint4*>(vb + row * D + col * 8) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / CH, col = c % CH;
-      *reinterpret_cast<uint4*>(&ks[buf][r * PITCH + col * 8]) = kreg[i];
-      if (!SHARED) *reinterpret_cast<uint4*>(&vs[buf][r * PITCH + col * 8]) = vreg[i];
-    }
-  };
-
-  float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
-  f32x4 acc[2][DT];
-#pragma unroll
-  for (int gq = 0; gq < 2; ++gq)
-#pragma unroll
-    for (int t = 0; t < DT; ++t) acc[gq][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (T > 0) load_tile(0);
-  for (int64_t tile = 0; tile < T; ++tile) {
-    const int buf = (int)(tile & 1);
-    store_tile(buf);
-    __syncthreads();
-    if (tile + 1 < T) load_tile(tile + 1);
-    const bf16_t* kt = ks[buf];
-    const bf16_t* vt = SHARED ? ks[buf] : vs[buf];
+  // LDS layout: row r of a tile holds its 16-byte chunks in swizzled order,
+  // chunk c at position c ^ swz(r), so that the 16-byte K reads of 8 rows and
+  // the transposing V reads of 4 rows land on distinct banks without padding.
+  // Tile loads go straight to LDS (global_load_lds_dwordx4: lane i of a wave
+  // writes 16 bytes at the wave's LDS base + 16 i), so each lane loads the
+  // global chunk that belongs at its slot.  Rows past the list re-read its
+  // last row (finite data; their scores are masked, so their weights are 0).
+  auto load_tile = [&](int tile, auto bufc) __attribute__((always_inline)) {
     const bool pooled = tile < T1;
-    const int64_t base = pooled ? tile * KT : RB + (tile - T1) * KT;
-
-    float sc[2][2][4];  // [group][half][j]
+    const int x0 = pooled ? tile * KT : RB + (tile - T1) * KT;
+    const int lim = pooled ? NP : p_last + 1;
+    const uintptr_t kb = pooled ? pk_base : rk_base, vb = pooled ? pv_base : rv_base;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      uint4 kop[KS];
+    for (int i = 0; i < CALLS; ++i) {
+      const int slot = i * NT + tid;
+      const int r = slot / CH, pos = slot % CH;
+      const int x = x0 + r < lim ? x0 + r : lim - 1;
+      const uint64_t off = (uint64_t)(int64_t)x * (D * 2) + 16u * (pos ^ swz<D>(r));
+      const int dst = (i * NT + wave * 64) * 8;  // bf16 elements, wave-uniform
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(kb + off), (lds_void*)(kbuf(bufc) + dst), 16, 0, 0);
+      if constexpr (!SHARED)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(vb + off), (lds_void*)(vbuf(bufc) + dst), 16, 0, 0);
+    }
+  };
+
+  float m_run[QG], l_run[QG];
+  f32x4 acc[QG][DT];
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    m_run[g] = kNegInf;
+    l_run[g] = 0.f;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto compute = [&](int tile, const bf16_t* kt, const bf16_t* vt) __attribute__((always_inline)) {
+    const bool pooled = tile < T1;
+    const int x0 = pooled ? tile * KT : RB + (tile - T1) * KT;
+    const bool full = pooled ? (tile + 1) * KT <= NPmin : (x0 >= RBmax && x0 + KT - 1 <= p_first);
+
+    // S^T = K Q^T: 16 keys x 16 rows per MFMA; each K operand feeds QG MFMAs
+    f32x4 sc[KB][QG];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      uint4 ka[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        kop[s] = *reinterpret_cast<const uint4*>(&kt[(16 * hh + n) * PITCH + 32 * s + 8 * kq]);
+        ka[s] = *reinterpret_cast<const uint4*>(&kt[(16 * kb + n) * D + 8 * ((4 * s + kq) ^ swz_n)]);
 #pragma unroll
-      for (int gq = 0; gq < 2; ++gq) {
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+      for (int g = 0; g < QG; ++g) sc[kb][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // the QG accumulation chains interleaved: consecutive MFMAs are independent
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[s]),
-                                                       __builtin_bit_cast(bf16x8, qr[gq][s]), c, 0, 0, 0);
+      for (int s = 0; s < KS; ++s)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t x = base + 16 * hh + 4 * kq + j;  // entry id or position
-          const bool vis = pooled ? (x < my_np[gq]) : (x >= my_rb[gq] && x <= my_pos[gq]);
-          sc[gq][hh][j] = vis ? c[j] * p.scale_log2 : kNegInf;
-        }
-      }
+        for (int g = 0; g < QG; ++g)
+          sc[kb][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[s]),
+                                                               __builtin_bit_cast(bf16x8, qr[g][s]), sc[kb][g], 0, 0, 0);
     }
-    s16x4p pop[2][2];
+    // mask (only where some row does not see the whole tile), scale, softmax
+    uint4 pb[KB / 2][QG];
 #pragma unroll
-    for (int gq = 0; gq < 2; ++gq) {
+    for (int g = 0; g < QG; ++g) {
+      if (!full) {  // one uniform branch around the whole mask
+        // visible x: [lo, hi] (pooled: [0, n_pooled - 1]; raw: [raw_begin, t])
+        const int lo = pooled ? 0 : my_rb[g], hi = pooled ? my_np[g] - 1 : my_pos[g];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int x = x0 + 16 * kb + 4 * kq + j;
+            sc[kb][g][j] = (x >= lo && x <= hi) ? sc[kb][g][j] : kNegInf;
+          }
+      }
+      // Running max with lazy rescaling: the reference max of a row moves only
+      // when a score exceeds it by more than 2^8 (any reference gives the same
+      // softmax; weights stay below 2^8, far from fp32 or bf16 overflow), so
+      // the fp32 accumulators are rescaled on few tiles.  The scale is folded
+      // into the exponent: p = 2^(s * scale*log2(e) - m).
       float tmax = kNegInf;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, sc[gq][hh][j]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float nm = fmaxf(m_run[gq], tmax);
-      const float mu = nm == kNegInf ? 0.f : nm;
-      const float corr = exp2f(m_run[gq] - mu);
+        for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, sc[kb][g][j]);
+      tmax = xor16_max(tmax);
+      tmax = xor32_max(tmax) * p.scale_log2;
+      if (__ballot(tmax > m_run[g] + 8.f)) {
+        const float nm = fmaxf(m_run[g], tmax);
+        const float corr = nm == kNegInf ? 1.f : fast_exp2(m_run[g] - nm);
+        l_run[g] *= corr;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) acc[g][t] *= corr;
+        m_run[g] = nm;
+      }
+      const float mu = m_run[g] == kNegInf ? 0.f : m_run[g];
       float psum = 0.f;
+      uint32_t w[KB][2];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
+      for (int kb = 0; kb < KB; ++kb) {
         float pj[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          pj[j] = exp2f(sc[gq][hh][j] - mu);
+          pj[j] = fast_exp2(fmaf(sc[kb][g][j], p.scale_log2, -mu));
           psum += pj[j];
         }
-        const uint32_t w0 = pack_bf16x2(pj[0], pj[1]), w1 = pack_bf16x2(pj[2], pj[3]);
-        pop[gq][hh] = s16x4p{(short)(w0 & 0xffff), (short)(w0 >> 16), (short)(w1 & 0xffff), (short)(w1 >> 16)};
+        w[kb][0] = pack_bf16x2(pj[0], pj[1]);
+        w[kb][1] = pack_bf16x2(pj[2], pj[3]);
       }
-      l_run[gq] = fmaf(l_run[gq], corr, psum);
-      m_run[gq] = nm;
 #pragma unroll
-      for (int t = 0; t < DT; ++t) acc[gq][t] *= corr;
+      for (int c = 0; c < KB / 2; ++c) pb[c][g] = make_uint4(w[2 * c][0], w[2 * c][1], w[2 * c + 1][0], w[2 * c + 1][1]);
+      l_run[g] += psum;
     }
+    // O^T += V^T P^T: k = 32 keys (two 16-key blocks); A from two transposing reads,
+    // lane (n, kq) at row 4kq + n/4 (+16 per key block), column 16t + 4(n%4)
+    s16x4 va[16];
+    read_v_tiles<D>(va, vt, n, kq, swz_tr);
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const bf16_t* vb = &vt[(16 * hh + 4 * kq) * PITCH + n];
+    for (int c = 0; c < KB / 2; ++c)
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        s16x4p a;
-        a[0] = (short)vb[16 * t].bits;
-        a[1] = (short)vb[PITCH + 16 * t].bits;
-        a[2] = (short)vb[2 * PITCH + 16 * t].bits;
-        a[3] = (short)vb[3 * PITCH + 16 * t].bits;
+        const s16x4 a0 = va[(c * DT + t) * 2], a1 = va[(c * DT + t) * 2 + 1];
+        const bf16x8 a = __builtin_bit_cast(bf16x8, s16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
 #pragma unroll
-        for (int gq = 0; gq < 2; ++gq)
-          acc[gq][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pop[gq][hh], acc[gq][t], 0, 0, 0);
+        for (int g = 0; g < QG; ++g)
+          acc[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pb[c][g]), acc[g][t], 0, 0, 0);
       }
-    }
+
+  };
+
+  // Tile loop, unrolled by the three buffers: wait for this tile's loads (the
+  // next tile's may stay in flight), barrier (every wave's part has landed and
+  // the buffer of the previous tile is free), request the tile two ahead into
+  // that buffer, compute.
+  auto step = [&](int tile, auto bufc) __attribute__((always_inline)) {
+    constexpr int B = decltype(bufc)::value;
+    if (tile + 1 < T) vmcnt_wait<LPT>();
+    else vmcnt_wait<0>();
+    __builtin_amdgcn_s_barrier();
+    if (tile + 2 < T) load_tile(tile + 2, std::integral_constant<int, (B + 2) % 3>{});
+    compute(tile, kbuf(bufc), vbuf(bufc));
+  };
+  if (0 < T) load_tile(0, std::integral_constant<int, 0>{});
+  if (1 < T) load_tile(1, std::integral_constant<int, 1>{});
+  for (int tile = 0; tile < T; tile += 3) {
+    step(tile, std::integral_constant<int, 0>{});
+    if (tile + 1 >= T) break;
+    step(tile + 1, std::integral_constant<int, 1>{});
+    if (tile + 2 >= T) break;
+    step(tile + 2, std::integral_constant<int, 2>{});
   }
 
 #pragma unroll
-  for (int gq = 0; gq < 2; ++gq) {
-    float l = l_run[gq];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (!my_ok[gq]) continue;
-    const int64_t h = (my_out[gq] / D) % p.hq;
-    if (p.sink) l += exp2f(p.sink[h] * kLog2e - m_run[gq]);
+  for (int g = 0; g < QG; ++g) {
+    float l = xor16_sum(l_run[g]);
+    l = xor32_sum(l);
+    if (!my_ok[g]) continue;
+    const int64_t h = (my_out[g] / D) % p.hq;
+    if (p.sink) l += fast_exp2(p.sink[h] * kLog2e - m_run[g]);
     const float inv = 1.f / l;
     if (p.out_bf16) {
-      bf16_t* o = static_cast<bf16_t*>(p.out) + my_out[gq] + 4 * kq;
+      bf16_t* o = static_cast<bf16_t*>(p.out) + my_out[g] + 4 * kq;
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         uint2 w;
-        w.x = pack_bf16x2(acc[gq][t][0] * inv, acc[gq][t][1] * inv);
-        w.y = pack_bf16x2(acc[gq][t][2] * inv, acc[gq][t][3] * inv);
+        w.x = pack_bf16x2(acc[g][t][0] * inv, acc[g][t][1] * inv);
+        w.y = pack_bf16x2(acc[g][t][2] * inv, acc[g][t][3] * inv);
         *reinterpret_cast<uint2*>(o + 16 * t) = w;
       }
     } else {
-      float* o = static_cast<float*>(p.out) + my_out[gq] + 4 * kq;
+      float* o = static_cast<float*>(p.out) + my_out[g] + 4 * kq;
 #pragma unroll
       for (int t = 0; t < DT; ++t)
         *reinterpret_cast<float4*>(o + 16 * t) =
-            make_float4(acc[gq][t][0] * inv, acc[gq][t][1] * inv, acc[gq][t][2] * inv, acc[gq][t][3] * inv);
+            make_float4(acc[g][t][0] * inv, acc[g][t][1] * inv, acc[g][t][2] * inv, acc[g][t][3] * inv);
     }
-    if (p.lse && kq == 0) p.lse[my_out[gq] / D] = (m_run[gq] + log2f(l)) * 0.69314718055994531f;
+    if (p.lse && kq == 0) p.lse[my_out[g] / D] = (m_run[g] + log2f(l)) * 0.69314718055994531f;
   }
 }
 
@@ -259,17 +408,17 @@ hipError_t launch_prefill(const lbca_prefill_args& a, hipStream_t stream) {
   p.m = a.block; p.W = a.window; p.mode = a.mode;
   p.out_bf16 = a.out_dtype == LBCA_BF16;
   p.scale_log2 = a.scale * kLog2e;
-  p.row_blocks = (int)((a.q_len * p.G + 127) / 128);
+  p.row_blocks = (int)((a.q_len * p.G + 255) / 256);  // 256 query rows per workgroup
   const dim3 grid((unsigned)(a.batch * a.kv_heads * p.row_blocks));
   const bool shared = a.pooled_v == nullptr;
   switch (a.dim) {
     case 64:
-      if (shared) prefill_kernel<64, true><<<grid, 256, 0, stream>>>(p);
-      else prefill_kernel<64, false><<<grid, 256, 0, stream>>>(p);
+      if (shared) prefill_kernel<64, true><<<grid, 512, 0, stream>>>(p);
+      else prefill_kernel<64, false><<<grid, 512, 0, stream>>>(p);
       break;
     case 128:
-      if (shared) prefill_kernel<128, true><<<grid, 256, 0, stream>>>(p);
-      else prefill_kernel<128, false><<<grid, 256, 0, stream>>>(p);
+      if (shared) prefill_kernel<128, true><<<grid, 512, 0, stream>>>(p);
+      else prefill_kernel<128, false><<<grid, 512, 0, stream>>>(p);
       break;
     default: return hipErrorInvalidValue;
   }

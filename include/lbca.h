@@ -219,7 +219,8 @@ LBCA_API int lbca_attend_decode(const lbca_decode_args* a, void* workspace, size
  *   sink         [q_heads] float32 or NULL
  *   out          [batch, q_len, q_heads, dim]            out_dtype (F32 or BF16)
  *   lse          [batch, q_len, q_heads] float32 or NULL
- * Supported: BF16 with dim in {64,128} (MFMA path); F32 with dim % 64 == 0,
+ * Supported: BF16 with dim in {64,128}, scale > 0, positions and
+ * q_len * (q_heads / kv_heads) below 2^31 (MFMA path); F32 with dim % 64 == 0,
  * dim <= 512.  Errors: INVALID_ARG if some query's pooled entries exceed
  * `entries` or its raw span leaves the raw buffer (checked on the host).
  */

@@ -164,6 +164,7 @@ def _prefill(**kw):
     (dict(raw_rows=16383), -1),               # last query's position leaves the raw buffer
     (dict(raw_pos_base=14300), -1),           # first query's raw span (from 14208) starts before the buffer
     (dict(dim=256), -2), (dict(dtype=0, dim=96), -2),
+    (dict(scale=-0.1), -2), (dict(scale=0.0), -2),   # MFMA path folds a positive scale into the exponent
 ])
 def test_prefill_validation(kw, code):
     assert _prefill(**kw) == code
