@@ -16,8 +16,9 @@
 // position), last position].  K and V tiles go straight from global memory to
 // LDS (global_load_lds_dwordx4, no staging registers) in a chunk-swizzled
 // layout, so the 16-byte K reads and the transposing V reads of a 16-lane
-// group hit distinct banks; three buffers keep the next two tiles' loads in
-// flight during a tile's MFMAs, one barrier per tile.  Scores are computed
+// group hit distinct banks; four buffers keep two tiles' loads in flight, one
+// barrier per tile.  The loop is software-pipelined: a tile's softmax runs
+// while the next tile's Q.K MFMAs execute.  Scores are computed
 // transposed, S^T = K Q^T with v_mfma_f32_16x16x32_bf16, so each lane owns one
 // query row's scores and the row max/sum need a 16- and a 32-lane swap; P^T
 // is then directly the B operand of O^T = V^T P^T (k = 32 keys: two 16-key
@@ -144,21 +145,23 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
   constexpr int LPT = CALLS * (SHARED ? 1 : 2);  // vector-memory ops per wave per tile
   static_assert(KT * CH % NT == 0, "every thread loads whole chunks");
   static_assert(ROWS == 256, "the launcher sizes the grid for 256 rows per workgroup");
-  // three tile buffers (two tiles of loads in flight), each its own array so
-  // the compiler can tell a read of one from the loads into another
+  // four tile buffers, each its own array so the compiler can tell a read of
+  // one from the loads into another
   constexpr int VSZ = SHARED ? 8 : KT * D;
-  __shared__ __attribute__((aligned(16))) bf16_t ks0[KT * D], ks1[KT * D], ks2[KT * D];
-  __shared__ __attribute__((aligned(16))) bf16_t vs0[VSZ], vs1[VSZ], vs2[VSZ];
+  __shared__ __attribute__((aligned(16))) bf16_t ks0[KT * D], ks1[KT * D], ks2[KT * D], ks3[KT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t vs0[VSZ], vs1[VSZ], vs2[VSZ], vs3[VSZ];
   auto kbuf = [&](auto c) __attribute__((always_inline)) -> bf16_t* {
     if constexpr (decltype(c)::value == 0) return ks0;
     else if constexpr (decltype(c)::value == 1) return ks1;
-    else return ks2;
+    else if constexpr (decltype(c)::value == 2) return ks2;
+    else return ks3;
   };
   auto vbuf = [&](auto c) __attribute__((always_inline)) -> bf16_t* {
     if constexpr (SHARED) return kbuf(c);
     else if constexpr (decltype(c)::value == 0) return vs0;
     else if constexpr (decltype(c)::value == 1) return vs1;
-    else return vs2;
+    else if constexpr (decltype(c)::value == 2) return vs2;
+    else return vs3;
   };
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -249,13 +252,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
     for (int t = 0; t < DT; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto compute = [&](int tile, const bf16_t* kt, const bf16_t* vt) __attribute__((always_inline)) {
-    const bool pooled = tile < T1;
-    const int x0 = pooled ? tile * KT : RB + (tile - T1) * KT;
-    const bool full = pooled ? (tile + 1) * KT <= NPmin : (x0 >= RBmax && x0 + KT - 1 <= p_first);
-
-    // S^T = K Q^T: 16 keys x 16 rows per MFMA; each K operand feeds QG MFMAs
-    f32x4 sc[KB][QG];
+  // S^T = K Q^T: 16 keys x 16 rows per MFMA; each K operand feeds QG MFMAs
+  auto qk = [&](const bf16_t* kt, f32x4 (&sc)[KB][QG]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       uint4 ka[KS];
@@ -272,6 +270,12 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
           sc[kb][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[s]),
                                                                __builtin_bit_cast(bf16x8, qr[g][s]), sc[kb][g], 0, 0, 0);
     }
+  };
+
+  auto softmax_pv = [&](int tile, f32x4 (&sc)[KB][QG], const bf16_t* vt) __attribute__((always_inline)) {
+    const bool pooled = tile < T1;
+    const int x0 = pooled ? tile * KT : RB + (tile - T1) * KT;
+    const bool full = pooled ? (tile + 1) * KT <= NPmin : (x0 >= RBmax && x0 + KT - 1 <= p_first);
     // mask (only where some row does not see the whole tile), scale, softmax
     uint4 pb[KB / 2][QG];
 #pragma unroll
@@ -342,26 +346,39 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
 
   };
 
-  // Tile loop, unrolled by the three buffers: wait for this tile's loads (the
-  // next tile's may stay in flight), barrier (every wave's part has landed and
-  // the buffer of the previous tile is free), request the tile two ahead into
-  // that buffer, compute.
-  auto step = [&](int tile, auto bufc) __attribute__((always_inline)) {
+  // Tile loop, software-pipelined and unrolled by the four buffers: step
+  // `tile` waits for tile+1's loads (tile+2's may stay in flight), then a
+  // barrier (every wave's part has landed; the buffer of tile-1 is free),
+  // requests tile+3 into that buffer, issues tile+1's Q.K MFMAs and, beside
+  // them, the softmax of tile and its P.V MFMAs.
+  f32x4 s_a[KB][QG], s_b[KB][QG];  // scores of the current and the next tile, roles alternating
+  auto step = [&](int tile, auto bufc, f32x4 (&s_cur)[KB][QG], f32x4 (&s_next)[KB][QG]) __attribute__((always_inline)) {
     constexpr int B = decltype(bufc)::value;
-    if (tile + 1 < T) vmcnt_wait<LPT>();
-    else vmcnt_wait<0>();
+    if (tile + 1 < T) {
+      if (tile + 2 < T) vmcnt_wait<LPT>();
+      else vmcnt_wait<0>();
+    }
     __builtin_amdgcn_s_barrier();
-    if (tile + 2 < T) load_tile(tile + 2, std::integral_constant<int, (B + 2) % 3>{});
-    compute(tile, kbuf(bufc), vbuf(bufc));
+    if (tile + 3 < T) load_tile(tile + 3, std::integral_constant<int, (B + 3) % 4>{});
+    if (tile + 1 < T) qk(kbuf(std::integral_constant<int, (B + 1) % 4>{}), s_next);
+    softmax_pv(tile, s_cur, vbuf(bufc));
   };
   if (0 < T) load_tile(0, std::integral_constant<int, 0>{});
   if (1 < T) load_tile(1, std::integral_constant<int, 1>{});
-  for (int tile = 0; tile < T; tile += 3) {
-    step(tile, std::integral_constant<int, 0>{});
+  if (2 < T) load_tile(2, std::integral_constant<int, 2>{});
+  if (T > 2) vmcnt_wait<2 * LPT>();
+  else if (T > 1) vmcnt_wait<LPT>();
+  else vmcnt_wait<0>();
+  __builtin_amdgcn_s_barrier();
+  if (T > 0) qk(kbuf(std::integral_constant<int, 0>{}), s_a);
+  for (int tile = 0; tile < T; tile += 4) {
+    step(tile, std::integral_constant<int, 0>{}, s_a, s_b);
     if (tile + 1 >= T) break;
-    step(tile + 1, std::integral_constant<int, 1>{});
+    step(tile + 1, std::integral_constant<int, 1>{}, s_b, s_a);
     if (tile + 2 >= T) break;
-    step(tile + 2, std::integral_constant<int, 2>{});
+    step(tile + 2, std::integral_constant<int, 2>{}, s_a, s_b);
+    if (tile + 3 >= T) break;
+    step(tile + 3, std::integral_constant<int, 3>{}, s_b, s_a);
   }
 
 #pragma unroll
