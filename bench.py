@@ -209,6 +209,142 @@ def run_prefill(reps):
 
 
 # ---------------------------------------------------------------------------
+# HCA decode at 1M context and CSA decode at 128K (MQA, 64 query heads, dim 512)
+# ---------------------------------------------------------------------------
+X_HQ, X_D, X_RD, X_EPS, X_BASE = 64, 512, 64, 1e-6, 10000.0
+HCA_T, HCA_M, HCA_B = 1 << 20, 128, 4
+CSA_T, CSA_M, CSA_B, CSA_HI, CSA_DI, CSA_K = 1 << 17, 4, 2, 8, 64, 512
+ROTATE_BYTES = 600 << 20   # distinct bytes a timing loop cycles through (> 2 x Infinity Cache)
+
+
+def mqa_step_bytes(B, rows):
+    """Algorithmic bytes of one MQA decode call: every visible (or selected) row
+    read once in bf16 (K = V), the queries in bf16, out and LSE in fp32."""
+    return B * (rows * X_D * 2 + X_HQ * X_D * 2 + X_HQ * X_D * 4 + X_HQ * 4)
+
+
+def run_hca(reps):
+    """Pool the whole 1M history once (timed, GB/s), then time decode at t = 2^20 - 1
+    over instances that rotate through more than the Infinity Cache holds."""
+    dev = "cuda"
+    B, T, m = HCA_B, HCA_T, HCA_M
+    N = T // m
+    treat = dict(rmsnorm_eps=X_EPS, rope_dims=X_RD, rope_base=X_BASE)
+    H = synth.hca_layer(("bench-hca-1m",), B, X_HQ, T, X_D, m, device=dev)
+    ent = torch.empty((B, 1, N, X_D), dtype=torch.bfloat16, device=dev)
+    pool = lambda: lbca.pool_blocks(H["c"], H["z"], H["bias"], m, 0, N, ent, **treat)
+    pool()
+    g_pool = capture(pool)
+    ms_pool = time_graph(g_pool, 3)
+    pool_bytes = B * T * X_D * 2 * 2 + B * N * X_D * 2
+    raw = H["c"][:, :, T - W:].contiguous()
+    pos = torch.full((B,), T - 1, dtype=torch.int64, device=dev)
+    rpb = torch.full((B,), T - W, dtype=torch.int64, device=dev)
+    sink = H["sink"]
+    del H, g_pool
+    torch.cuda.empty_cache()
+    per_inst = ent.numel() * 2 + raw.numel() * 2
+    n_inst = max(2, -(-ROTATE_BYTES // per_inst))
+    inst = []
+    for i in range(n_inst):
+        inst.append(dict(ent=ent.clone(), raw=raw.clone(),
+                         q=synth.normal((B, X_HQ, X_D), synth.seed_of("bench-hca-1m", "q", i), dtype="bf16",
+                                        device=dev),
+                         out=torch.empty((B, X_HQ, X_D), device=dev), lse=torch.empty((B, X_HQ), device=dev)))
+    kw = dict(raw_pos_base=rpb, sink=sink, **treat)
+    x = inst[0]
+    nws = lbca.decode_workspace_bytes(x["q"], x["ent"], x["raw"], pos, m, W, OVER, **kw)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+
+    def step():
+        for x in inst:
+            lbca.attend_decode(x["q"], x["ent"], x["raw"], pos, m, W, OVER, out=x["out"], lse=x["lse"],
+                               workspace=ws, **kw)
+
+    g = capture(step)
+    g.replay()
+    us = time_graph(g, reps) * 1e3 / n_inst
+    rows = N + W
+    by = mqa_step_bytes(B, rows)
+    fl = B * X_HQ * rows * X_D * 4
+    return {"decode_us": us, "decode_GBps": by / (us * 1e-6) / 1e9,
+            "decode_frac_of_hbm_peak": by / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "decode_tflops": fl / (us * 1e-6) / 1e12, "decode_algorithmic_bytes": by,
+            "decode_workspace_bytes": nws, "instances": n_inst,
+            "pool_ms": ms_pool, "pool_GBps": pool_bytes / (ms_pool * 1e-3) / 1e9, "pool_bytes": pool_bytes,
+            "workload": f"HCA batch {B}, t = 2^20 - 1: {N} treated entries + {W} raw, 64 query heads x 512"}
+
+
+def run_csa(reps):
+    """Dual-pool the 128K history once (timed), then time indexer top-512 and decode over
+    the selection at t = 2^17 - 1, rotating through instances with their own keys."""
+    dev = "cuda"
+    B, T, m, k = CSA_B, CSA_T, CSA_M, CSA_K
+    N = T // m
+    treat = dict(rmsnorm_eps=X_EPS, rope_dims=X_RD, rope_base=X_BASE)
+    C = synth.csa_layer(("bench-csa-128k",), B, X_HQ, T, X_D, m, CSA_HI, CSA_DI, device=dev)
+    ent = torch.empty((B, 1, N, X_D), dtype=torch.bfloat16, device=dev)
+    pool = lambda: lbca.pool_blocks(C["ca"], C["za"], C["bias_a"], m, 0, N, ent, xb=C["cb"], zb=C["zb"],
+                                    bias_b=C["bias_b"], **treat)
+    pool()
+    g_pool = capture(pool)
+    ms_pool = time_graph(g_pool, 3)
+    pool_bytes = B * T * X_D * 2 * 4 + B * N * X_D * 2
+    raw = C["ca"][:, :, T - W:].contiguous()
+    sink = C["sink"]
+    del C, g_pool
+    torch.cuda.empty_cache()
+    pos = torch.full((B,), T - 1, dtype=torch.int64, device=dev)
+    rpb = torch.full((B,), T - W, dtype=torch.int64, device=dev)
+    tag = "bench-csa-128k"
+    # distinct bytes per instance that one step touches: keys + the gathered rows + window
+    per_inst = B * (N * CSA_DI * 2 + (k + W) * X_D * 2)
+    n_inst = max(2, -(-ROTATE_BYTES // per_inst))
+    inst = []
+    for i in range(n_inst):
+        inst.append(dict(
+            ent=ent.clone(), raw=raw.clone(),
+            keys=synth.normal((B, N, CSA_DI), synth.seed_of(tag, "keys", i), dtype="bf16", device=dev),
+            qi=synth.normal((B, CSA_HI, CSA_DI), synth.seed_of(tag, "qi", i), dtype="bf16", device=dev),
+            w=synth.uniform((B, CSA_HI), synth.seed_of(tag, "w", i), device=dev),
+            q=synth.normal((B, X_HQ, X_D), synth.seed_of(tag, "q", i), dtype="bf16", device=dev),
+            idx=torch.empty((B, k), dtype=torch.int32, device=dev),
+            sc=torch.empty((B, k), dtype=torch.float32, device=dev),
+            out=torch.empty((B, X_HQ, X_D), device=dev), lse=torch.empty((B, X_HQ), device=dev)))
+    kw = dict(raw_pos_base=rpb, sink=sink, **treat)
+    ws_i = torch.empty(B * N * 4, dtype=torch.uint8, device=dev)
+    x = inst[0]
+    nws = lbca.decode_workspace_bytes(x["q"], x["ent"], x["raw"], pos, m, W, OVER, sel_idx=x["idx"], **kw)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+
+    def index(x):
+        lbca.csa_index_topk(x["qi"], x["w"], x["keys"], pos, m, k, out_idx=x["idx"], out_score=x["sc"],
+                            workspace=ws_i)
+
+    def decode(x):
+        lbca.attend_decode(x["q"], x["ent"], x["raw"], pos, m, W, OVER, out=x["out"], lse=x["lse"],
+                           sel_idx=x["idx"], workspace=ws, **kw)
+
+    g_both = capture(lambda: [(index(x), decode(x)) for x in inst])
+    g_idx = capture(lambda: [index(x) for x in inst])
+    g_dec = capture(lambda: [decode(x) for x in inst])
+    g_both.replay()
+    us_both = time_graph(g_both, reps) * 1e3 / n_inst
+    us_idx = time_graph(g_idx, reps) * 1e3 / n_inst
+    us_dec = time_graph(g_dec, reps) * 1e3 / n_inst
+    by_idx = B * (N * CSA_DI * 2 + CSA_HI * CSA_DI * 2 + CSA_HI * 4 + k * 8)
+    by_dec = mqa_step_bytes(B, k + W)
+    by = by_idx + by_dec
+    return {"step_us": us_both, "step_GBps": by / (us_both * 1e-6) / 1e9, "step_algorithmic_bytes": by,
+            "index_topk_us": us_idx, "index_GBps": by_idx / (us_idx * 1e-6) / 1e9,
+            "decode_us": us_dec, "decode_GBps": by_dec / (us_dec * 1e-6) / 1e9,
+            "decode_workspace_bytes": nws, "instances": n_inst,
+            "pool_ms": ms_pool, "pool_GBps": pool_bytes / (ms_pool * 1e-3) / 1e9, "pool_bytes": pool_bytes,
+            "workload": f"CSA batch {B}, t = 2^17 - 1: top-{k} of {N} entries (8 x 64 indexer) + {W} raw, "
+                        f"64 query heads x 512"}
+
+
+# ---------------------------------------------------------------------------
 # oracle on the host
 # ---------------------------------------------------------------------------
 def cpu_baseline(layer, budget_s=12.0):
@@ -248,6 +384,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the host oracle timing")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-small-batch", action="store_true")
+    ap.add_argument("--no-mqa", action="store_true", help="skip the HCA 1M and CSA 128K lines")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the decode/prefill hot path here has no multi-GPU "
@@ -309,6 +446,14 @@ def main():
         extra["prefill"] = {"tflops": fl / (ms_attn * 1e-3) / 1e12, "attention_ms": ms_attn,
                             "with_pooling_ms": ms_full, "algorithmic_flops": fl,
                             "frac_of_bf16_peak": fl / (ms_attn * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+
+    if not args.no_mqa:
+        log("[bench] HCA decode 1M (batch 4)")
+        extra["hca_1m"] = run_hca(max(5, args.steps // 4))
+        torch.cuda.empty_cache()
+        log("[bench] CSA index top-512 + decode 128K (batch 2)")
+        extra["csa_128k"] = run_csa(max(5, args.steps // 4))
+        torch.cuda.empty_cache()
 
     line = {
         "metric": METRIC, "value": value, "unit": "layer-steps/s", "n_gpus": 1, "steps": args.steps,

@@ -131,7 +131,7 @@ static int validate_decode(const lbca_decode_args* a) {
     // rows are addressed by 32-bit byte offsets within one (sequence, KV head)
     // slice; the merge grid's y/x carry batch and (KV head, head group)
     if (a->entries * a->dim * 2 >= (int64_t(1) << 31) || a->raw_rows * a->dim * 2 >= (int64_t(1) << 31) ||
-        a->k_sel >= (int64_t(1) << 29) || a->batch > 65535 || a->kv_heads * ((G + 15) / 16) > 65535)
+        a->k_sel > 32768 || a->batch > 65535 || a->kv_heads * ((G + 15) / 16) > 65535)
       return LBCA_ERR_UNSUPPORTED;
   } else {
     if (a->dim % 64 != 0 || a->dim > 512) return LBCA_ERR_UNSUPPORTED;

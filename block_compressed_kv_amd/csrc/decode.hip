@@ -40,60 +40,13 @@
 // decode_merge_kernel combines them in a fixed order (bitwise reproducible).
 // No device-scope fence is used anywhere: on this multi-XCD part a
 // device-scope release/acquire writes back and invalidates the XCD's L2.
-#include "device_util.h"
-#include "lbca_internal.h"
+#include "decode_common.h"
 
 #ifndef LBCA_DECODE_TILES_PER_WAVE
 #define LBCA_DECODE_TILES_PER_WAVE 4  // tiles per wave above which a unit's rows are split
 #endif
 
 namespace lbca {
-
-struct DecodeParams {
-  const bf16_t* q;
-  const bf16_t* pk;
-  const bf16_t* pv;
-  const bf16_t* rk;
-  const bf16_t* rv;
-  const int64_t* pos;
-  const int64_t* rpb;
-  const int32_t* sel;
-  const float* sink;
-  float* out;
-  float* lse;
-  float* ws_ml;    // [units * splits][16][2]
-  float* ws_acc;   // [units * splits][16][D]
-  int64_t hq, hkv, G, entries, raw_rows, k_sel, m, W;
-  int mode, splits, head_groups;
-  int units;       // batch * kv_heads * head_groups
-  float scale_log2;
-  float eps;
-  int rope_dims;
-  double log2_base;
-};
-
-struct SeqView {
-  int64_t t, raw_begin, raw_row0;
-  int n_pooled, n_sel, n_raw;
-  bool ok;
-};
-
-__device__ __forceinline__ SeqView seq_view(const DecodeParams& p, int64_t b) {
-  SeqView v;
-  v.t = p.pos[b];
-  const int64_t base = p.rpb ? p.rpb[b] : 0;
-  int64_t np = 0, rb = 0;
-  bool ok = v.t >= 0;
-  if (ok) visible_range(v.t, p.m, p.W, p.mode, &np, &rb);
-  ok = ok && np <= p.entries && rb - base >= 0 && v.t - base < p.raw_rows;
-  v.ok = ok;
-  v.n_pooled = (int)np;
-  v.n_sel = ok ? (int)(p.sel ? p.k_sel : np) : 0;
-  v.n_raw = ok ? (int)(v.t - rb + 1) : 0;
-  v.raw_begin = rb;
-  v.raw_row0 = rb - base;
-  return v;
-}
 
 __device__ __forceinline__ void unpack8(const uint4& u, float* f) {
   f[0] = lo_bf16(u.x); f[1] = hi_bf16(u.x); f[2] = lo_bf16(u.y); f[3] = hi_bf16(u.y);
@@ -630,11 +583,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
   }
 }
 
-// Combine the splits of one unit (16 query-head slots): every split's partial
-// is loaded at once (no dependent chain), weights exp2(m_s - M) in a fixed
-// order, then sink, normalisation, LSE and the -t rotation.
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D) {
-  __shared__ float s_m[64][16], s_l[64][16];
+// Combine the splits of one unit (16 query-head slots) over one chunk of CK
+// output dims (blockIdx.z): weights exp2(m_s - M) in a fixed order, then
+// sink, normalisation, LSE and the -t rotation.  CK is the rotated width when
+// dims rotate (the last chunk is then exactly the rotated dims), so thread
+// (slot, u) takes the float4s at dims c0 + 4u and c0 + 4u + CK/2: a
+// rotate-half pair in the last chunk.  Every split's float4 is an independent
+// load.
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D, int CK) {
   __shared__ float s_w[64][16];
   __shared__ float s_inv[16], s_lse[16];
   const int tid = threadIdx.x;
@@ -649,62 +605,112 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D
   if (!sv.ok) return;  // the decode kernel already wrote NaN for this unit
   const int S = p.splits;
   const int64_t part0 = unit * S;
-  for (int i = tid; i < S * 16; i += blockDim.x) {
-    const int s = i >> 4, slot = i & 15;
-    if (slot < nvalid) {
-      s_m[s][slot] = p.ws_ml[((part0 + s) * 16 + slot) * 2];
-      s_l[s][slot] = p.ws_ml[((part0 + s) * 16 + slot) * 2 + 1];
-    }
-  }
-  __syncthreads();
   if (tid < nvalid) {
     float M = kNegInf;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, s_m[s][tid]);
+    for (int s = 0; s < S; ++s) M = fmaxf(M, p.ws_ml[((part0 + s) * 16 + tid) * 2]);
     float L = 0.f;
     for (int s = 0; s < S; ++s) {
-      const float sw = s_m[s][tid] == kNegInf ? 0.f : exp2f(s_m[s][tid] - M);
+      const float ms = p.ws_ml[((part0 + s) * 16 + tid) * 2];
+      const float sw = ms == kNegInf ? 0.f : exp2f(ms - M);
       s_w[s][tid] = sw;
-      L = fmaf(s_l[s][tid], sw, L);
+      L = fmaf(p.ws_ml[((part0 + s) * 16 + tid) * 2 + 1], sw, L);
     }
     if (p.sink) L += exp2f(p.sink[head0 + tid] * kLog2e - M);
     s_inv[tid] = 1.f / L;
     s_lse[tid] = (M + log2f(L)) * 0.69314718055994531f;
   }
   __syncthreads();
-  const float* pa = p.ws_acc + part0 * 16 * D;
-  auto combined = [&](int sl, int d) {
-    float o = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < S; ++s) o = fmaf(pa[(s * 16 + sl) * D + d], s_w[s][sl], o);
-    return o * s_inv[sl];
-  };
-  const int r = p.rope_dims, half = r >> 1;
-  const int items = nvalid * (D - half);
-  for (int i = tid; i < items; i += blockDim.x) {
-    const int sl = i / (D - half), d = i % (D - half);
-    float* o = p.out + (b * p.hq + head0 + sl) * D;
-    if (d < D - r) {
-      o[d] = combined(sl, d);
-    } else {
-      const int k = d - (D - r);
-      const float x1 = combined(sl, d), x2 = combined(sl, d + half);
-      float c, sn;
-      rope_cos_sin(-(double)sv.t, k, r, p.log2_base, &c, &sn);
-      o[d] = x1 * c - x2 * sn;
-      o[d + half] = x2 * c + x1 * sn;
+  const int per = CK / 8;  // threads per slot
+  const int sl = tid / per, u = tid % per;
+  if (sl < nvalid) {
+    const int c0 = (int)blockIdx.z * CK;
+    const int d1 = c0 + 4 * u, d2 = d1 + CK / 2;
+    const float* pa = p.ws_acc + (part0 * 16 + sl) * D;
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
+#pragma unroll 4
+    for (int s = 0; s < S; ++s) {
+      const float w = s_w[s][sl];
+      const float4 a = *reinterpret_cast<const float4*>(pa + (int64_t)s * 16 * D + d1);
+      const float4 c = *reinterpret_cast<const float4*>(pa + (int64_t)s * 16 * D + d2);
+      x.x = fmaf(a.x, w, x.x); x.y = fmaf(a.y, w, x.y); x.z = fmaf(a.z, w, x.z); x.w = fmaf(a.w, w, x.w);
+      y.x = fmaf(c.x, w, y.x); y.y = fmaf(c.y, w, y.y); y.z = fmaf(c.z, w, y.z); y.w = fmaf(c.w, w, y.w);
     }
+    const float inv = s_inv[sl];
+    float o1[4] = {x.x * inv, x.y * inv, x.z * inv, x.w * inv};
+    float o2[4] = {y.x * inv, y.y * inv, y.z * inv, y.w * inv};
+    const int r = p.rope_dims;
+    if (r > 0 && c0 == D - r) {  // rotate-half pairs (d1 + e, d2 + e) by -t
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float cs, sn;
+        rope_cos_sin(-(double)sv.t, d1 + e - c0, r, p.log2_base, &cs, &sn);
+        const float x1 = o1[e], x2 = o2[e];
+        o1[e] = x1 * cs - x2 * sn;
+        o2[e] = x2 * cs + x1 * sn;
+      }
+    }
+    float* o = p.out + (b * p.hq + head0 + sl) * D;
+    *reinterpret_cast<float4*>(o + d1) = make_float4(o1[0], o1[1], o1[2], o1[3]);
+    *reinterpret_cast<float4*>(o + d2) = make_float4(o2[0], o2[1], o2[2], o2[3]);
   }
-  if (p.lse && tid < nvalid) p.lse[b * p.hq + head0 + tid] = s_lse[tid];
+  if (p.lse && blockIdx.z == 0 && tid < nvalid) p.lse[b * p.hq + head0 + tid] = s_lse[tid];
+}
+
+void launch_decode_merge(const DecodeParams& p, int64_t batch, int64_t dim, hipStream_t stream) {
+  // chunks of the rotated width when dims rotate, else of min(dim, 64)
+  const int ck = p.rope_dims > 0 ? p.rope_dims : (dim < 64 ? (int)dim : 64);
+  decode_merge_kernel<<<dim3((unsigned)(p.hkv * p.head_groups), (unsigned)batch, (unsigned)(dim / ck)),
+                        (unsigned)(2 * ck), 0, stream>>>(p, (int)dim, ck);
 }
 
 // ---------------------------------------------------------------------------
 static int rows_per_tile(int64_t dim) { return dim >= 512 ? 16 : 32; }
 static int waves_per_wg(int64_t dim) { return dim <= 128 ? 8 : 4; }
 
+// Wide-row MQA path (512 dims, shared series, query heads in 32-head blocks):
+// workgroups per (sequence, KV head) along the row list.  Enough splits to
+// give about LBCA_WIDE_TARGET_WGS workgroups (one CU streams only about
+// 40 GB/s), but at least LBCA_WIDE_MIN_TILES 32-row tiles per workgroup (a
+// split's partial, 64 KB per head block, stays below the rows it reads), and
+// enough that each range's selected ids fit the LDS stage.
+#ifndef LBCA_WIDE_TARGET_WGS
+#define LBCA_WIDE_TARGET_WGS 128
+#endif
+#ifndef LBCA_WIDE_MIN_TILES
+#define LBCA_WIDE_MIN_TILES 4
+#endif
+constexpr int kWideSelLds = 1024;  // matches the wide kernel's id stage
+
+static DecodePlan plan_decode_wide(const lbca_decode_args& a, int64_t G) {
+  DecodePlan pl{};
+  pl.tile_rows = 32;
+  pl.head_groups = (int)(G / 16);
+  pl.dim_splits = 1;
+  pl.wide_blocks = (int)(G / 32);
+  const int64_t sel_max = a.sel_idx ? a.k_sel : a.entries;
+  const int64_t raw_span = a.mode == LBCA_EXCLUSIVE ? a.window + a.block - 1 : a.window;
+  const int64_t raw_max = raw_span < a.raw_rows ? raw_span : a.raw_rows;
+  const int64_t tiles = (sel_max + 31) / 32 + (raw_max + 31) / 32;
+  const int64_t per_split = a.batch * a.kv_heads;  // workgroups per split
+  int64_t s = (LBCA_WIDE_TARGET_WGS + per_split - 1) / per_split;
+  const int64_t by_rows = (tiles + LBCA_WIDE_MIN_TILES - 1) / LBCA_WIDE_MIN_TILES;
+  if (s > by_rows) s = by_rows;
+  if (a.sel_idx && s < (tiles + kWideSelLds / 32 - 1) / (kWideSelLds / 32))
+    s = (tiles + kWideSelLds / 32 - 1) / (kWideSelLds / 32);
+  if (s < 1) s = 1;
+  if (s > 64) s = 64;  // k_sel <= 32768 keeps the id constraint within this
+  pl.splits = (int)s;
+  if (s == 1) return pl;
+  const size_t u = (size_t)(a.batch * a.kv_heads * pl.head_groups);
+  pl.ws_bytes = u * s * 16 * 2 * sizeof(float) + u * s * 16 * (size_t)a.dim * sizeof(float);
+  return pl;
+}
+
 DecodePlan plan_decode(const lbca_decode_args& a) {
   DecodePlan pl{};
   if (a.dtype != LBCA_BF16) return pl;  // fp32 path needs no workspace
   const int64_t G = a.q_heads / a.kv_heads;
+  if (a.dim == 512 && a.pooled_v == nullptr && G % 32 == 0) return plan_decode_wide(a, G);
   pl.tile_rows = rows_per_tile(a.dim);
   pl.head_groups = (int)((G + 15) / 16);
   const int nw = waves_per_wg(a.dim);
@@ -801,6 +807,12 @@ hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void
   p.log2_base = a.rope_dims > 0 ? log2((double)a.rope_base) : 0.0;
   const bool shared = a.pooled_v == nullptr;
   const bool treat = a.rmsnorm_eps >= 0.f || a.rope_dims > 0;
+  if (plan.wide_blocks > 0) {
+    hipError_t e = launch_decode_wide(p, a.rope_dims, treat, plan.wide_blocks, stream);
+    if (e != hipSuccess || plan.splits == 1) return e;
+    launch_decode_merge(p, a.batch, a.dim, stream);
+    return hipGetLastError();
+  }
   const size_t pairs = units * plan.splits;  // (unit, split) pairs
   const int ds = plan.dim_splits;
   const dim3 g((unsigned)(ds == 1 ? pairs : (pairs + 7) / 8 * 8 * ds));
@@ -815,8 +827,7 @@ hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || plan.splits == 1) return e;
-  decode_merge_kernel<<<dim3((unsigned)(a.kv_heads * plan.head_groups), (unsigned)a.batch), 256, 0,
-                        stream>>>(p, (int)a.dim);
+  launch_decode_merge(p, a.batch, a.dim, stream);
   return hipGetLastError();
 }
 

@@ -1,0 +1,60 @@
+// Decode parameters and per-sequence visibility shared by the decode kernels.
+#pragma once
+#include "device_util.h"
+#include "lbca_internal.h"
+
+namespace lbca {
+
+struct DecodeParams {
+  const bf16_t* q;
+  const bf16_t* pk;
+  const bf16_t* pv;
+  const bf16_t* rk;
+  const bf16_t* rv;
+  const int64_t* pos;
+  const int64_t* rpb;
+  const int32_t* sel;
+  const float* sink;
+  float* out;
+  float* lse;
+  float* ws_ml;    // [units * splits][16][2]
+  float* ws_acc;   // [units * splits][16][D]
+  int64_t hq, hkv, G, entries, raw_rows, k_sel, m, W;
+  int mode, splits, head_groups;
+  int units;       // batch * kv_heads * head_groups
+  float scale_log2;
+  float eps;
+  int rope_dims;
+  double log2_base;
+};
+
+struct SeqView {
+  int64_t t, raw_begin, raw_row0;
+  int n_pooled, n_sel, n_raw;
+  bool ok;
+};
+
+__device__ __forceinline__ SeqView seq_view(const DecodeParams& p, int64_t b) {
+  SeqView v;
+  v.t = p.pos[b];
+  const int64_t base = p.rpb ? p.rpb[b] : 0;
+  int64_t np = 0, rb = 0;
+  bool ok = v.t >= 0;
+  if (ok) visible_range(v.t, p.m, p.W, p.mode, &np, &rb);
+  ok = ok && np <= p.entries && rb - base >= 0 && v.t - base < p.raw_rows;
+  v.ok = ok;
+  v.n_pooled = (int)np;
+  v.n_sel = ok ? (int)(p.sel ? p.k_sel : np) : 0;
+  v.n_raw = ok ? (int)(v.t - rb + 1) : 0;
+  v.raw_begin = rb;
+  v.raw_row0 = rb - base;
+  return v;
+}
+
+// Wide-row MQA decode (512 dims, shared series, query heads in blocks of 32
+// per KV head): launched by launch_decode when the plan selects it.
+hipError_t launch_decode_wide(const DecodeParams& p, int rope_dims, bool treat, int head_blocks,
+                              hipStream_t stream);
+void launch_decode_merge(const DecodeParams& p, int64_t batch, int64_t dim, hipStream_t stream);
+
+}  // namespace lbca

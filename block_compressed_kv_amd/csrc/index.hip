@@ -13,9 +13,10 @@
 // workspace in fp32.
 //
 // Selection is exact and deterministic: an MSB-first radix select over the
-// order-preserving 32-bit image of the fp32 scores finds the k-th largest key,
-// then a block-wide scan in index order takes every larger score and the
-// lowest-index ties, writing the chosen ids in ascending order.
+// order-preserving 32-bit image of the fp32 scores (held in registers) finds
+// the k-th largest key, then block-wide scans in index order take every
+// larger score and the lowest-index ties, writing the chosen ids in ascending
+// order.
 #include "device_util.h"
 #include "lbca_internal.h"
 
@@ -118,20 +119,30 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_sums, int* 
   return r;
 }
 
+// One workgroup per sequence; every thread keeps KPT scores (as order-preserving
+// 32-bit keys) of entries r * 1024 + tid in registers.  The k-th largest key is
+// found by a radix select over 12 + 10 + 10 bits: each pass counts the keys
+// that still match the digits chosen so far into an LDS histogram, and a
+// block-wide scan from the top bin finds the bin holding the k-th largest.
+// The selection then takes every key above it and the lowest-index keys equal
+// to it: each element's output slot is the number of selected elements before
+// it in index order, from per-(round, wave) counts scanned across the block.
+template <int KPT>
 __global__ __launch_bounds__(1024) void topk_kernel(IndexParams p) {
-  __shared__ int hist[256];
+  __shared__ int hist[4096];
   __shared__ int scan_buf[32];
-  __shared__ uint32_t s_prefix, s_remaining;
-  const int tid = threadIdx.x;
+  __shared__ int s_gt[KPT * 16], s_eq[KPT * 16];
+  __shared__ int s_pick[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t b = blockIdx.x;
-  const int64_t nv = n_visible(p, b);
-  const int64_t K = p.k;
+  const int nv = (int)n_visible(p, b);
+  const int K = (int)p.k;
   const float* sc = p.scores + b * p.entries;
   int32_t* oi = p.out_idx + b * K;
   float* os = p.out_score ? p.out_score + b * K : nullptr;
 
   if (nv <= K) {
-    for (int64_t i = tid; i < K; i += blockDim.x) {
+    for (int i = tid; i < K; i += blockDim.x) {
       const bool in = i < nv;
       oi[i] = in ? (int32_t)i : -1;
       if (os) os[i] = in ? sc[i] : __builtin_nanf("");
@@ -139,62 +150,98 @@ __global__ __launch_bounds__(1024) void topk_kernel(IndexParams p) {
     return;
   }
 
-  uint32_t prefix = 0, mask = 0;
-  uint32_t remaining = (uint32_t)K;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
-    for (int64_t i = tid; i < nv; i += blockDim.x) {
-      const uint32_t key = order_key(sc[i]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t above = 0;
-      int d = 255;
-      for (; d > 0; --d) {
-        const uint32_t h = (uint32_t)hist[d];
-        if (above + h >= remaining) break;
-        above += h;
-      }
-      s_prefix = prefix | ((uint32_t)d << shift);
-      s_remaining = remaining - above;
-    }
-    __syncthreads();
-    prefix = s_prefix;
-    remaining = s_remaining;
-    mask |= 0xffu << shift;
-    __syncthreads();
+  uint32_t key[KPT];
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) {
+    const int i = r * 1024 + tid;
+    key[r] = i < nv ? order_key(sc[i]) : 0u;
   }
-  const uint32_t thr = prefix;        // key of the k-th largest score
-  const int need_eq = (int)remaining; // ties at thr to take, lowest index first
 
-  const int64_t chunk = (nv + blockDim.x - 1) / blockDim.x;
-  const int64_t c0 = tid * chunk;
-  const int64_t c1 = c0 + chunk < nv ? c0 + chunk : nv;
-  int n_gt = 0, n_eq = 0;
-  for (int64_t i = c0; i < c1; ++i) {
-    const uint32_t key = order_key(sc[i]);
-    n_gt += key > thr;
-    n_eq += key == thr;
-  }
-  const int eq_off = block_exclusive_scan(n_eq, scan_buf, nullptr);
-  int take_eq = need_eq - eq_off;
-  take_eq = take_eq < 0 ? 0 : (take_eq > n_eq ? n_eq : take_eq);
-  int out = block_exclusive_scan(n_gt + take_eq, scan_buf, nullptr);
-  int eq_seen = 0;
-  for (int64_t i = c0; i < c1; ++i) {
-    const float f = sc[i];
-    const uint32_t key = order_key(f);
-    bool pick = key > thr;
-    if (key == thr) {
-      pick = eq_seen < take_eq;
-      ++eq_seen;
+  uint32_t prefix = 0, pmask = 0;
+  int remaining = K;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
+    const int nb = pass == 0 ? 4096 : 1024;
+    for (int i = tid; i < nb; i += 1024) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const bool in = r * 1024 + tid < nv && (key[r] & pmask) == prefix;
+      if (in) atomicAdd(&hist[(key[r] >> shift) & (uint32_t)(nb - 1)], 1);
     }
-    if (pick) {
-      oi[out] = (int32_t)i;
-      if (os) os[out] = f;
-      ++out;
+    __syncthreads();
+    // bins from the top: thread t holds bins nb-1-t*per .. nb-per-t*per
+    const int per = nb / 1024;
+    int local = 0;
+    for (int j = 0; j < per; ++j) local += hist[nb - 1 - tid * per - j];
+    const int above = block_exclusive_scan(local, scan_buf, nullptr);
+    if (above < remaining && remaining <= above + local) {
+      int c = above;
+      for (int j = 0; j < per; ++j) {
+        const int bin = nb - 1 - tid * per - j;
+        const int h = hist[bin];
+        if (c + h >= remaining) {
+          s_pick[0] = bin;
+          s_pick[1] = remaining - c;
+          break;
+        }
+        c += h;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s_pick[0] << shift;
+    pmask |= (uint32_t)(nb - 1) << shift;
+    remaining = s_pick[1];
+    __syncthreads();
+  }
+  const uint32_t thr = prefix;       // key of the k-th largest score
+  const int need_eq = remaining;     // keys equal to it to take, lowest index first
+
+  // counts above / equal to the threshold per (round, wave), scanned in index order
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) {
+    const bool in = r * 1024 + tid < nv;
+    const uint64_t gm = __ballot(in && key[r] > thr), em = __ballot(in && key[r] == thr);
+    if (lane == 0) {
+      s_gt[r * 16 + wave] = __popcll(gm);
+      s_eq[r * 16 + wave] = __popcll(em);
+    }
+  }
+  __syncthreads();
+  for (int e0 = 0; e0 < KPT * 16; e0 += 1024) {  // entries in index order (round-major)
+    const int e = e0 + tid;
+    const bool ok = e < KPT * 16;
+    int gt_tot, eq_tot;
+    const int g = ok ? s_gt[e] : 0, q = ok ? s_eq[e] : 0;
+    const int gp = block_exclusive_scan(g, scan_buf, &gt_tot);
+    const int qp = block_exclusive_scan(q, scan_buf, &eq_tot);
+    if (ok) {
+      s_gt[e] = gp + (e0 > 0 ? hist[0] : 0);
+      s_eq[e] = qp + (e0 > 0 ? hist[1] : 0);
+    }
+    __syncthreads();
+    if (tid == 0) {  // running totals for the next 1024 entries
+      hist[0] = (e0 > 0 ? hist[0] : 0) + gt_tot;
+      hist[1] = (e0 > 0 ? hist[1] : 0) + eq_tot;
+    }
+    __syncthreads();
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) {
+    const int i = r * 1024 + tid;
+    const bool in = i < nv;
+    const bool gt = in && key[r] > thr, eq = in && key[r] == thr;
+    const uint64_t gm = __ballot(gt), em = __ballot(eq);
+    const int gb = s_gt[r * 16 + wave] + __popcll(gm & below);
+    const int eb = s_eq[r * 16 + wave] + __popcll(em & below);
+    int slot = -1;
+    if (gt) slot = gb + (eb < need_eq ? eb : need_eq);
+    else if (eq && eb < need_eq) slot = gb + eb;
+    if (slot >= 0) {
+      oi[slot] = (int32_t)i;
+      if (os) os[slot] = sc[i];
     }
   }
 }
@@ -224,7 +271,11 @@ hipError_t launch_index_topk(const csa_index_args& a, void* ws, hipStream_t stre
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  topk_kernel<<<dim3((unsigned)a.batch), 1024, 0, stream>>>(p);
+  const dim3 g((unsigned)a.batch);
+  if (a.entries <= 4096) topk_kernel<4><<<g, 1024, 0, stream>>>(p);
+  else if (a.entries <= 16384) topk_kernel<16><<<g, 1024, 0, stream>>>(p);
+  else if (a.entries <= 32768) topk_kernel<32><<<g, 1024, 0, stream>>>(p);
+  else topk_kernel<64><<<g, 1024, 0, stream>>>(p);
   return hipGetLastError();
 }
 

@@ -170,7 +170,7 @@ LBCA_API int lbca_pool_blocks(const lbca_pool_args* a, void* stream);
  *   out          [batch, q_heads, dim] float32;  lse [batch, q_heads] float32 or NULL
  * Supported: dtype BF16 with dim in {64,128,256,512}, G <= 64, rope_dims in
  * {0, 64, 128}, pooled and raw slices of one (sequence, KV head) below 2 GiB
- * (entries * dim and raw_rows * dim < 2^30), k_sel < 2^29, batch <= 65535
+ * (entries * dim and raw_rows * dim < 2^30), k_sel <= 32768, batch <= 65535
  * (MFMA path); dtype F32 with dim % 64 == 0, dim <= 512 and no treatment.
  * A sequence whose visible rows do not fit (n_pooled > entries, raw span
  * outside the raw buffer, t < 0) gets NaN in out and lse.
