@@ -584,15 +584,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
 }
 
 // Combine the splits of one unit (16 query-head slots) over one chunk of CK
-// output dims (blockIdx.z): weights exp2(m_s - M) in a fixed order, then
-// sink, normalisation, LSE and the -t rotation.  CK is the rotated width when
-// dims rotate (the last chunk is then exactly the rotated dims), so thread
-// (slot, u) takes the float4s at dims c0 + 4u and c0 + 4u + CK/2: a
-// rotate-half pair in the last chunk.  Every split's float4 is an independent
-// load.
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D, int CK) {
-  __shared__ float s_w[64][16];
+// output dims (blockIdx.z): weights exp2(m_s - M), sink, normalisation, LSE
+// and the -t rotation.  CK is the rotated width when dims rotate (the last
+// chunk is then exactly the rotated dims).  1024 threads: thread (sg, slot, u),
+// u < CK/4, sums the float4 at dims c0 + 4u over splits s = sg, sg + NG, ...
+// (NG = 256 / CK split groups; all loads independent); the groups are added
+// in LDS in a fixed order, and thread (slot, u < CK/8) finishes the pair of
+// float4s at c0 + 4u and c0 + 4u + CK/2 (a rotate-half pair in the last chunk).
+constexpr int kMergeGroups = 4;  // for 64-dim chunks
+__global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeParams p, int D, int CK) {
+  __shared__ float s_w[64][16], s_l[64][16];  // split maxima (then weights) and sums
   __shared__ float s_inv[16], s_lse[16];
+  __shared__ float4 s_part[kMergeGroups][16][32];  // [group][slot][float4 of the chunk], CK <= 128
   const int tid = threadIdx.x;
   const int64_t unit = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
   const int hg = (int)(blockIdx.x % (unsigned)p.head_groups);
@@ -605,39 +608,61 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D
   if (!sv.ok) return;  // the decode kernel already wrote NaN for this unit
   const int S = p.splits;
   const int64_t part0 = unit * S;
+  // every split's (max, sum) of the 16 slots to LDS at once (one load per thread)
+  for (int i = tid; i < S * 16; i += blockDim.x) {
+    const float2 ml = *reinterpret_cast<const float2*>(&p.ws_ml[(part0 * 16 + i) * 2]);
+    s_w[i >> 4][i & 15] = ml.x;
+    s_l[i >> 4][i & 15] = ml.y;
+  }
+  __syncthreads();
   if (tid < nvalid) {
     float M = kNegInf;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, p.ws_ml[((part0 + s) * 16 + tid) * 2]);
+    for (int s = 0; s < S; ++s) M = fmaxf(M, s_w[s][tid]);
     float L = 0.f;
     for (int s = 0; s < S; ++s) {
-      const float ms = p.ws_ml[((part0 + s) * 16 + tid) * 2];
+      const float ms = s_w[s][tid];
       const float sw = ms == kNegInf ? 0.f : exp2f(ms - M);
       s_w[s][tid] = sw;
-      L = fmaf(p.ws_ml[((part0 + s) * 16 + tid) * 2 + 1], sw, L);
+      L = fmaf(s_l[s][tid], sw, L);
     }
     if (p.sink) L += exp2f(p.sink[head0 + tid] * kLog2e - M);
     s_inv[tid] = 1.f / L;
     s_lse[tid] = (M + log2f(L)) * 0.69314718055994531f;
   }
   __syncthreads();
-  const int per = CK / 8;  // threads per slot
-  const int sl = tid / per, u = tid % per;
-  if (sl < nvalid) {
-    const int c0 = (int)blockIdx.z * CK;
-    const int d1 = c0 + 4 * u, d2 = d1 + CK / 2;
-    const float* pa = p.ws_acc + (part0 * 16 + sl) * D;
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
+  const int nf = CK / 4;   // float4s per slot in the chunk
+  const int NG = 256 / CK;  // split groups
+  const int c0 = (int)blockIdx.z * CK;
+  {
+    const int u = tid % nf, sl = (tid / nf) % 16, sg = tid / (nf * 16);
+    if (sg < NG && sl < nvalid) {
+      const float* pa = p.ws_acc + (part0 * 16 + sl) * D + c0 + 4 * u;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
-    for (int s = 0; s < S; ++s) {
-      const float w = s_w[s][sl];
-      const float4 a = *reinterpret_cast<const float4*>(pa + (int64_t)s * 16 * D + d1);
-      const float4 c = *reinterpret_cast<const float4*>(pa + (int64_t)s * 16 * D + d2);
-      x.x = fmaf(a.x, w, x.x); x.y = fmaf(a.y, w, x.y); x.z = fmaf(a.z, w, x.z); x.w = fmaf(a.w, w, x.w);
-      y.x = fmaf(c.x, w, y.x); y.y = fmaf(c.y, w, y.y); y.z = fmaf(c.z, w, y.z); y.w = fmaf(c.w, w, y.w);
+      for (int s = sg; s < S; s += NG) {
+        const float w = s_w[s][sl];
+        const float4 a = *reinterpret_cast<const float4*>(pa + (int64_t)s * 16 * D);
+        x.x = fmaf(a.x, w, x.x); x.y = fmaf(a.y, w, x.y); x.z = fmaf(a.z, w, x.z); x.w = fmaf(a.w, w, x.w);
+      }
+      s_part[sg][sl][u] = x;
     }
+  }
+  __syncthreads();
+  const int sl = tid / (nf / 2), u = tid % (nf / 2);
+  if (sl < nvalid) {
     const float inv = s_inv[sl];
-    float o1[4] = {x.x * inv, x.y * inv, x.z * inv, x.w * inv};
-    float o2[4] = {y.x * inv, y.y * inv, y.z * inv, y.w * inv};
+    float o1[4], o2[4];
+    {
+      float4 x = s_part[0][sl][u], y = s_part[0][sl][u + nf / 2];
+      for (int g = 1; g < NG; ++g) {
+        const float4 a = s_part[g][sl][u], c = s_part[g][sl][u + nf / 2];
+        x.x += a.x; x.y += a.y; x.z += a.z; x.w += a.w;
+        y.x += c.x; y.y += c.y; y.z += c.z; y.w += c.w;
+      }
+      o1[0] = x.x * inv; o1[1] = x.y * inv; o1[2] = x.z * inv; o1[3] = x.w * inv;
+      o2[0] = y.x * inv; o2[1] = y.y * inv; o2[2] = y.z * inv; o2[3] = y.w * inv;
+    }
+    const int d1 = c0 + 4 * u, d2 = d1 + CK / 2;
     const int r = p.rope_dims;
     if (r > 0 && c0 == D - r) {  // rotate-half pairs (d1 + e, d2 + e) by -t
 #pragma unroll
@@ -660,7 +685,7 @@ void launch_decode_merge(const DecodeParams& p, int64_t batch, int64_t dim, hipS
   // chunks of the rotated width when dims rotate, else of min(dim, 64)
   const int ck = p.rope_dims > 0 ? p.rope_dims : (dim < 64 ? (int)dim : 64);
   decode_merge_kernel<<<dim3((unsigned)(p.hkv * p.head_groups), (unsigned)batch, (unsigned)(dim / ck)),
-                        (unsigned)(2 * ck), 0, stream>>>(p, (int)dim, ck);
+                        1024, 0, stream>>>(p, (int)dim, ck);
 }
 
 // ---------------------------------------------------------------------------
@@ -677,7 +702,7 @@ static int waves_per_wg(int64_t dim) { return dim <= 128 ? 8 : 4; }
 #define LBCA_WIDE_TARGET_WGS 128
 #endif
 #ifndef LBCA_WIDE_MIN_TILES
-#define LBCA_WIDE_MIN_TILES 4
+#define LBCA_WIDE_MIN_TILES 2
 #endif
 constexpr int kWideSelLds = 1024;  // matches the wide kernel's id stage
 

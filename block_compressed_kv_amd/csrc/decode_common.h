@@ -34,10 +34,10 @@ struct SeqView {
   bool ok;
 };
 
-__device__ __forceinline__ SeqView seq_view(const DecodeParams& p, int64_t b) {
+// t: the sequence's position, base: position of raw row 0.
+__device__ __forceinline__ SeqView seq_view(const DecodeParams& p, int64_t b, int64_t t, int64_t base) {
   SeqView v;
-  v.t = p.pos[b];
-  const int64_t base = p.rpb ? p.rpb[b] : 0;
+  v.t = t;
   int64_t np = 0, rb = 0;
   bool ok = v.t >= 0;
   if (ok) visible_range(v.t, p.m, p.W, p.mode, &np, &rb);
@@ -49,6 +49,9 @@ __device__ __forceinline__ SeqView seq_view(const DecodeParams& p, int64_t b) {
   v.raw_begin = rb;
   v.raw_row0 = rb - base;
   return v;
+}
+__device__ __forceinline__ SeqView seq_view(const DecodeParams& p, int64_t b) {
+  return seq_view(p, b, p.pos[b], p.rpb ? p.rpb[b] : 0);
 }
 
 // Wide-row MQA decode (512 dims, shared series, query heads in blocks of 32

@@ -60,11 +60,11 @@ constexpr int WDB = WQ / 32;       // 32-dim output blocks of one wave
 constexpr int WQB = WTR * WQ * 2;  // bytes of one wave's quarter tile
 constexpr int WSLOTS = 3;          // ring depth (tiles)
 
-// 16-byte chunk swizzle of tile row r (16 chunks per quarter row): 8
-// consecutive rows at one chunk, and 4 rows (from a multiple of 4) at two
-// adjacent chunks (even first), fall on distinct bank groups.  Rows 16 apart
-// differ by 4.
-__device__ __forceinline__ int wswz(int r) { return (2 * r + (r >> 2)) & 7; }
+// 16-byte chunk swizzle of tile row r (16 chunks per quarter row; the LDS
+// serves 16 chunks per cycle): 16 consecutive rows read at one chunk, and 4
+// rows (from a multiple of 4) read at 4 chunks of an aligned group, fall on 16
+// distinct bank groups.  Rows 16 apart share the swizzle.
+__device__ __forceinline__ int wswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // Workgroup barrier for LDS traffic between waves: this wave's LDS accesses
 // complete, then s_barrier; the asm's memory clobber keeps the compiler from
@@ -83,66 +83,81 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// The 8 score A operands of one quarter tile (row n, chunk (2ks + g) ^ swz(n)
-// = 8*(ks/4) + ((2*(ks%4) + g) ^ swz(n))): four per-lane addresses, the
-// k-steps 4..7 128 bytes further.
-__device__ __forceinline__ void wide_k_reads(uint4 (&r)[WKST], const uint32_t (&a)[4]) {
+// The 8 score A operands of one quarter tile (row n, chunk (2ks + g) ^ swz(n)):
+// one per-lane address per k-step.
+__device__ __forceinline__ void wide_k_reads(uint4 (&r)[WKST], const uint32_t (&a)[WKST]) {
   asm volatile(
       "ds_read_b128 %0, %8\n"
       "ds_read_b128 %1, %9\n"
       "ds_read_b128 %2, %10\n"
       "ds_read_b128 %3, %11\n"
-      "ds_read_b128 %4, %8 offset:128\n"
-      "ds_read_b128 %5, %9 offset:128\n"
-      "ds_read_b128 %6, %10 offset:128\n"
-      "ds_read_b128 %7, %11 offset:128\n"
+      "ds_read_b128 %4, %12\n"
+      "ds_read_b128 %5, %13\n"
+      "ds_read_b128 %6, %14\n"
+      "ds_read_b128 %7, %15\n"
       "s_waitcnt lgkmcnt(0)\n"
       : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
         "=&v"(r[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
       : "memory");
 }
 
-// The A operands of O^T += V^T P^T for one 16-row block of a quarter tile and
-// the wave's 4 output blocks: lane (i, mq, g) reads rows rb + 4g + i/4 and
-// rb + 8 + 4g + i/4 at dims 32*db + 16*mq + 4*(i%4); the transposing reads
-// give lane (m, g) dims 32*db + m of rows {rb+4g.., rb+8+4g..}.  The swizzled
-// chunk of block db is 8*(db/2) + (chunk of db%2), so four per-lane addresses
-// (two rows x db parity) and an immediate offset cover the 8 reads.
-// a: (row 1, even db), (row 1, odd db), (row 2, even db), (row 2, odd db).
-__device__ __forceinline__ void wide_tr_reads(s16x4 (&r)[8], const uint32_t (&a)[4]) {
+// The A operands of O^T += V^T P^T for both 16-row blocks of a quarter tile
+// and the wave's 4 output blocks: lane (i, mq, g) reads rows 16kb + 4g + i/4
+// and 16kb + 8 + 4g + i/4 at dims 32*db + 16*mq + 4*(i%4); the transposing
+// reads give lane (m, g) dims 32*db + m of rows {4g.., 8+4g..} of block kb.
+// a[2*db + h]: address of (row r1 + 8h, block db) in block 0; block 1 is
+// 4096 bytes on (same swizzle).  r[kb][2*db + h].
+__device__ __forceinline__ void wide_tr_reads(s16x4 (&r)[2][8], const uint32_t (&a)[8]) {
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n"
-      "ds_read_b64_tr_b16 %1, %10\n"
-      "ds_read_b64_tr_b16 %2, %9\n"
-      "ds_read_b64_tr_b16 %3, %11\n"
-      "ds_read_b64_tr_b16 %4, %8 offset:128\n"
-      "ds_read_b64_tr_b16 %5, %10 offset:128\n"
-      "ds_read_b64_tr_b16 %6, %9 offset:128\n"
-      "ds_read_b64_tr_b16 %7, %11 offset:128\n"
+      "ds_read_b64_tr_b16 %0, %16\n"
+      "ds_read_b64_tr_b16 %1, %17\n"
+      "ds_read_b64_tr_b16 %2, %18\n"
+      "ds_read_b64_tr_b16 %3, %19\n"
+      "ds_read_b64_tr_b16 %4, %20\n"
+      "ds_read_b64_tr_b16 %5, %21\n"
+      "ds_read_b64_tr_b16 %6, %22\n"
+      "ds_read_b64_tr_b16 %7, %23\n"
+      "ds_read_b64_tr_b16 %8, %16 offset:4096\n"
+      "ds_read_b64_tr_b16 %9, %17 offset:4096\n"
+      "ds_read_b64_tr_b16 %10, %18 offset:4096\n"
+      "ds_read_b64_tr_b16 %11, %19 offset:4096\n"
+      "ds_read_b64_tr_b16 %12, %20 offset:4096\n"
+      "ds_read_b64_tr_b16 %13, %21 offset:4096\n"
+      "ds_read_b64_tr_b16 %14, %22 offset:4096\n"
+      "ds_read_b64_tr_b16 %15, %23 offset:4096\n"
       "s_waitcnt lgkmcnt(0)\n"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
-        "=&v"(r[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[0][2]), "=&v"(r[0][3]), "=&v"(r[0][4]), "=&v"(r[0][5]),
+        "=&v"(r[0][6]), "=&v"(r[0][7]), "=&v"(r[1][0]), "=&v"(r[1][1]), "=&v"(r[1][2]), "=&v"(r[1][3]),
+        "=&v"(r[1][4]), "=&v"(r[1][5]), "=&v"(r[1][6]), "=&v"(r[1][7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
       : "memory");
 }
 
-// Two 16-byte rows of every wave's partial scores (float4 j0 and j0+1 of
-// this lane; the waves' partials are 4 KB apart).  An asm block like the tile
-// reads: a plain read would make the compiler wait for the copies in flight.
-__device__ __forceinline__ void wide_x_reads(float4 (&r)[8], uint32_t a) {
+// This lane's float4 j of the head block's four partials (4 KB apart): the
+// rows 8j + 4g + i this wave finishes.
+__device__ __forceinline__ void wide_x4_reads(float4 (&r)[4], uint32_t a) {
   asm volatile(
-      "ds_read_b128 %0, %8\n"
-      "ds_read_b128 %1, %8 offset:4096\n"
-      "ds_read_b128 %2, %8 offset:8192\n"
-      "ds_read_b128 %3, %8 offset:12288\n"
-      "ds_read_b128 %4, %8 offset:1024\n"
-      "ds_read_b128 %5, %8 offset:5120\n"
-      "ds_read_b128 %6, %8 offset:9216\n"
-      "ds_read_b128 %7, %8 offset:13312\n"
+      "ds_read_b128 %0, %4\n"
+      "ds_read_b128 %1, %4 offset:4096\n"
+      "ds_read_b128 %2, %4 offset:8192\n"
+      "ds_read_b128 %3, %4 offset:12288\n"
       "s_waitcnt lgkmcnt(0)\n"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
-        "=&v"(r[7])
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a)
+      : "memory");
+}
+
+// The P^T B operands of this lane for both 16-row blocks: the 8-byte words of
+// the waves that finished rows j = 0..3 (512 bytes apart).
+__device__ __forceinline__ void wide_p_reads(uint2 (&r)[4], uint32_t a) {
+  asm volatile(
+      "ds_read_b64 %0, %4\n"
+      "ds_read_b64 %1, %4 offset:512\n"
+      "ds_read_b64 %2, %4 offset:1024\n"
+      "ds_read_b64 %3, %4 offset:1536\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
       : "v"(a)
       : "memory");
 }
@@ -169,6 +184,8 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) float xs[HB][4][16 * 64];      // partial scores per wave
   __shared__ float ts[4][WTR];                                           // raw rows: partial sums of squares
   __shared__ float tq[HB][4][32];                                        // queries: partial sums of squares
+  __shared__ float s_mx[HB][4][32];                                      // row-slice maxima / sums per head
+  __shared__ __attribute__((aligned(16))) uint2 s_p[HB][4][64];          // P (bf16) of rows 8j.. per lane
   __shared__ int s_ids[SEL ? kWideSel : 1];
   __shared__ double s_freq[RD > 0 ? RD / 2 : 1];
 
@@ -184,6 +201,8 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
   const int64_t b = bk / (unsigned)p.hkv;
   const int64_t head0 = kvh * p.G + 32 * hb;  // first query head of this wave's block
 
+  const int64_t t_pos = p.pos[b];                     // requested first, used after the first copies
+  const int64_t t_base = p.rpb ? p.rpb[b] : 0;
   // query B operands (head n, dims 128q + 16ks + 8g ..); their addresses do
   // not depend on the position, so they load alongside it
   uint4 qb[WKST];
@@ -192,18 +211,15 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
 #pragma unroll
     for (int ks = 0; ks < WKST; ++ks) qb[ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks);
   }
-  const SeqView sv = seq_view(p, b);
-  if (!sv.ok) {  // rows do not fit the buffers: NaN, written once
-    if (split == 0) {
-      const int64_t h0 = kvh * p.G;
-      for (int i = tid; i < 32 * HB * WD; i += 256 * HB) p.out[(b * p.hq + h0) * WD + i] = __builtin_nanf("");
-      if (p.lse && tid < 32 * HB) p.lse[b * p.hq + h0 + tid] = __builtin_nanf("");
-    }
-    return;
-  }
-
-  const int tiles_p = (sv.n_sel + WTR - 1) / WTR;
-  const int tiles = tiles_p + (sv.n_raw + WTR - 1) / WTR;
+  // Tile range of this split from the buffer capacities (no position needed,
+  // so the first copies go out before it arrives): list positions [0, cap_sel)
+  // of pooled or selected entries, then [0, cap_raw) of the raw span.  Rows
+  // outside the runtime list are masked.
+  const int cap_sel = (int)(p.sel ? p.k_sel : p.entries);
+  const int64_t raw_span = p.mode == 0 ? p.W + p.m - 1 : p.W;
+  const int cap_raw = (int)(raw_span < p.raw_rows ? raw_span : p.raw_rows);
+  const int tiles_p = (cap_sel + WTR - 1) / WTR;
+  const int tiles = tiles_p + (cap_raw + WTR - 1) / WTR;
   const int per = (tiles + S - 1) / S;
   const int t0 = split * per < tiles ? split * per : tiles;
   const int t1 = t0 + per < tiles ? t0 + per : tiles;
@@ -211,15 +227,13 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
 
   if constexpr (SEL) {  // selected ids of this range (the host sizes ranges to fit)
     int nr = (t1 < tiles_p ? t1 : tiles_p) * WTR;
-    nr = (nr < sv.n_sel ? nr : sv.n_sel) - r0;
+    nr = (nr < cap_sel ? nr : cap_sel) - r0;
     nr = nr < kWideSel ? nr : kWideSel;
     const int32_t* src = p.sel + b * p.k_sel + r0;
     for (int i = tid; i < nr; i += 256 * HB) s_ids[i] = src[i];
   }
-  if constexpr (RD > 0) {
-    if (tid < RD / 2) s_freq[tid] = rope_turns_per_pos(tid, RD, p.log2_base);
-  }
-  if constexpr (SEL || RD > 0) lds_barrier();
+  if constexpr (SEL) lds_barrier();
+  SeqView sv;  // filled once the position arrives (after the first copies)
 
   // ---- tile copies: the waves of quarter q copy its 32 rows between them ----
   const uintptr_t pk_slice = reinterpret_cast<uintptr_t>(p.pk) + (uint64_t)((b * p.hkv + kvh) * p.entries) * (WD * 2);
@@ -242,12 +256,31 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
     row = id;
     return ok;
   };
+  // Whether every row of the tile is in the list and its rows are consecutive.
+  auto tile_full = [&](bool raw, int v0) __attribute__((always_inline)) {
+    return raw ? v0 + WTR <= sv.n_raw : (!SEL && v0 + WTR <= sv.n_sel);
+  };
+  // byte offset within a row run of this lane's copy j (row 4(hb*NI + j) + rq)
+  uint32_t lane_off[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int r = 4 * (hb * NI + j) + rq;
+    lane_off[j] = (uint32_t)(r * WD * 2 + WQ * 2 * q) + 16u * (uint32_t)(c_lane ^ wswz(r));
+  }
   // Issues this wave's NI copies of `tile` into ring slot `slot`.
   auto issue = [&](int tile, int slot) __attribute__((always_inline)) {
     const bool raw = tile >= tiles_p;
     const int v0 = raw ? (tile - tiles_p) * WTR : tile * WTR;
     const uintptr_t sb = raw ? rk_slice : pk_slice;
     uint8_t* dst0 = ring + slot * (4 * WQB) + q * WQB + hb * NI * 1024;
+    if (tile_full(raw, v0)) {  // consecutive rows, all in the list
+      const uintptr_t base = sb + (uint64_t)(raw ? sv.raw_row0 + v0 : (int64_t)v0) * (WD * 2);
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(base + lane_off[j]), (lds_void*)(dst0 + j * 1024),
+                                         16, 0, 0);
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int r = 4 * (hb * NI + j) + rq;
@@ -258,10 +291,57 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
       __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(ga), (lds_void*)(dst0 + j * 1024), 16, 0, 0);
     }
   };
-  if (t0 < t1) issue(t0, 0);
-  if (t0 + 1 < t1) issue(t0 + 1, 1);
+  // Copies of a pooled or selected tile before the position is known: rows
+  // within the buffer capacities (the list bounds are applied by the mask).
+  auto issue_early = [&](int tile, int slot) __attribute__((always_inline)) {
+    const int v0 = tile * WTR;
+    uint8_t* dst0 = ring + slot * (4 * WQB) + q * WQB + hb * NI * 1024;
+    if (!SEL && v0 + WTR <= cap_sel) {
+      const uintptr_t base = pk_slice + (uint64_t)v0 * (WD * 2);
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(base + lane_off[j]), (lds_void*)(dst0 + j * 1024),
+                                         16, 0, 0);
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int r = 4 * (hb * NI + j) + rq;
+      const int v = v0 + r;
+      bool ok = v < cap_sel;
+      int id = v;
+      if constexpr (SEL) {
+        const int li = v - r0;
+        id = s_ids[ok ? (li < kWideSel ? li : kWideSel - 1) : 0];
+        ok = ok && id >= 0 && id < p.entries;
+      }
+      const uint32_t coff = (uint32_t)(WQ * 2 * q) + 16u * (uint32_t)(c_lane ^ wswz(r));
+      const uintptr_t ga = (ok ? pk_slice + (uint64_t)id * (WD * 2) : dummy) + coff;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(ga), (lds_void*)(dst0 + j * 1024), 16, 0, 0);
+    }
+  };
+  // the first two tiles: pooled ones now, raw ones once the position is known
+  // (raw tiles come last, so the copies stay in tile order)
+  if (t0 < t1 && t0 < tiles_p) issue_early(t0, 0);
+  if (t0 + 1 < t1 && t0 + 1 < tiles_p) issue_early(t0 + 1, 1);
+  if constexpr (RD > 0) {  // RoPE turns per position (published by the barrier below)
+    if (tid < RD / 2) s_freq[tid] = rope_turns_per_pos(tid, RD, p.log2_base);
+  }
+  sv = seq_view(p, b, t_pos, t_base);
+  if (!sv.ok) {  // rows do not fit the buffers: NaN, written once
+    vm_wait<0>();
+    if (split == 0) {
+      const int64_t h0 = kvh * p.G;
+      for (int i = tid; i < 32 * HB * WD; i += 256 * HB) p.out[(b * p.hq + h0) * WD + i] = __builtin_nanf("");
+      if (p.lse && tid < 32 * HB) p.lse[b * p.hq + h0 + tid] = __builtin_nanf("");
+    }
+    return;
+  }
+  if (t0 < t1 && t0 >= tiles_p) issue(t0, 0);
+  if (t0 + 1 < t1 && t0 + 1 >= tiles_p) issue(t0 + 1, 1);
 
   // ---- query treatment in registers: RMSNorm over all 512 dims, RoPE on the last RD ----
+  if constexpr (RD > 0) lds_barrier();  // s_freq
   if constexpr (TREAT) {
     float inv = 1.f;
     if (p.eps >= 0.f) {
@@ -307,42 +387,52 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
   }
 
   // per-lane LDS byte offsets within a quarter tile.  Score A operands: row n,
-  // chunk 8*(ks/4) + ((2*(ks%4) + g) ^ swz(n)).
-  uint32_t koff[4];
+  // chunk (2ks + g) ^ swz(n).
+  uint32_t koff[WKST];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) koff[k] = (uint32_t)(n * WQ * 2 + 16 * ((2 * k + g) ^ wswz(n)));
-  // Transposing reads of rows r1 = 4g + i/4 and r1 + 8 (block 0); block 1 is
-  // 16 rows on, whose swizzle differs by 4, i.e. the db parities swap.
-  uint32_t toff[4];
+  for (int ks = 0; ks < WKST; ++ks) koff[ks] = (uint32_t)(n * WQ * 2 + 16 * ((2 * ks + g) ^ wswz(n)));
+  // Transposing reads of rows r1 = 4g + i/4 and r1 + 8, chunk 4db + 2mq + (i%4)/2
+  // (swizzled), 8-byte half i%2.
+  uint32_t toff[8];
   {
     const int i = lane & 15, mq = (lane >> 4) & 1;
     const int r1 = 4 * g + (i >> 2), cl = 2 * mq + ((i & 3) >> 1);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int r = r1 + 8 * (k >> 1), par = k & 1;
-      toff[k] = (uint32_t)(r * WQ * 2 + 16 * ((4 * par + cl) ^ wswz(r)) + 8 * (i & 1));
-    }
+    for (int db = 0; db < WDB; ++db)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = r1 + 8 * h;
+        toff[2 * db + h] = (uint32_t)(r * WQ * 2 + 16 * ((4 * db + cl) ^ wswz(r)) + 8 * (i & 1));
+      }
   }
   const uint32_t ring_a = (uint32_t)(uintptr_t)(lds_u8*)(ring) + (uint32_t)(q * WQB);
-  const uint32_t xs_a = (uint32_t)(uintptr_t)(lds_u8*)(reinterpret_cast<uint8_t*>(&xs[hb][0][0])) + 16u * lane;
+  // this wave finishes rows 8q + 4g + i of its head block: its float4 of each partial
+  const uint32_t xs_a = (uint32_t)(uintptr_t)(lds_u8*)(reinterpret_cast<uint8_t*>(&xs[hb][0][0])) + 16u * (q * 64 + lane);
+  const uint32_t p_a = (uint32_t)(uintptr_t)(lds_u8*)(reinterpret_cast<uint8_t*>(&s_p[hb][0][0])) + 8u * lane;
 
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kNegInf, l_run = 0.f;  // running max (this head block) and row-slice sum
+  float m_oth = kNegInf;                // running max of the other head block (for the decision)
   f32x16 acc[WDB];
 #pragma unroll
   for (int db = 0; db < WDB; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[db][e] = 0.f;
 
+  // Per tile two barriers: A after the partial scores are written (it also
+  // ends every wave's reads of the previous tile, whose slot then receives the
+  // copy of tile + 2), and C after P and the row-slice maxima are written; each
+  // wave waits for its copies of the next tile before C, so C also publishes
+  // that tile.  P is computed against the running max; when a score exceeds it
+  // by more than 2^8 (the first tile, and rarely after), every wave takes the
+  // rescaling path, which recomputes P and adds one barrier.
+  if (t0 < t1) {
+    if (t0 + 1 < t1) vm_wait<NI>();
+    else vm_wait<0>();
+  }
+  lds_barrier();  // the first tile landed
   int slot = 0;
 #pragma unroll 1
   for (int tile = t0; tile < t1; ++tile) {
-    // this wave's copies of the tile landed (the next tile's may stay in flight) ...
-    if (tile + 1 < t1) vm_wait<NI>();
-    else vm_wait<0>();
-    // ... and every wave's: the tile is complete, the previous tile's slot and
-    // the partial-score buffers are free
-    lds_barrier();
-    if (tile + 2 < t1) issue(tile + 2, slot == 0 ? 2 : slot - 1);
     const uint32_t sa = ring_a + (uint32_t)(slot * 4 * WQB);  // this wave's quarter tile (LDS address)
     const bool raw = tile >= tiles_p;
     const int v0 = raw ? (tile - tiles_p) * WTR : tile * WTR;
@@ -403,8 +493,8 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
       }
     }
     // valid rows of the tile (lane n: row n)
-    uint32_t mk;
-    {
+    uint32_t mk = 0xffffffffu;
+    if (!tile_full(raw, v0)) {
       int64_t row;
       const bool ok = locate(raw, v0 + n, row);
       mk = (uint32_t)(__ballot(ok) & 0xffffffffull);
@@ -413,7 +503,9 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
     f32x16 sc;
     {
       uint4 ka[WKST];
-      const uint32_t kad[4] = {sa + koff[0], sa + koff[1], sa + koff[2], sa + koff[3]};
+      uint32_t kad[WKST];
+#pragma unroll
+      for (int ks = 0; ks < WKST; ++ks) kad[ks] = sa + koff[ks];
       wide_k_reads(ka, kad);
       f32x16 s2;
 #pragma unroll
@@ -432,78 +524,102 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
     for (int j = 0; j < 4; ++j)
       *reinterpret_cast<float4*>(&xw[(j * 64 + lane) * 4]) =
           make_float4(sc[4 * j], sc[4 * j + 1], sc[4 * j + 2], sc[4 * j + 3]);
-    lds_barrier();
-    // full scores: the head block's four partials in a fixed order (identical in its waves)
+    lds_barrier();  // A
+    if (tile + 2 < t1) issue(tile + 2, slot == 0 ? 2 : slot - 1);
+    // Rows 8q + 4g + i (i < 4) are finished here: the four partials summed in a
+    // fixed order, masked, scaled into the exponent's units.
+    float s4[4];
+    {
+      float4 xr[4];
+      wide_x4_reads(xr, xs_a);
+      float4 t = xr[0];
 #pragma unroll
-    for (int jh = 0; jh < 2; ++jh) {
-      float4 xr[8];  // [j - 2jh][quarter]
-      wide_x_reads(xr, xs_a + 2048u * jh);
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        float4 t = xr[4 * jj];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) {
-          const float4 o = xr[4 * jj + w];
-          t.x += o.x; t.y += o.y; t.z += o.z; t.w += o.w;
-        }
-        const int j = 2 * jh + jj;
-        sc[4 * j] = t.x; sc[4 * j + 1] = t.y; sc[4 * j + 2] = t.z; sc[4 * j + 3] = t.w;
+      for (int w = 1; w < 4; ++w) {
+        t.x += xr[w].x; t.y += xr[w].y; t.z += xr[w].z; t.w += xr[w].w;
       }
+      s4[0] = t.x * p.scale_log2; s4[1] = t.y * p.scale_log2;
+      s4[2] = t.z * p.scale_log2; s4[3] = t.w * p.scale_log2;
     }
-    // mask, scale into the exponent's units, running max (moves lazily)
-    float tmax = kNegInf;
+    if (mk != 0xffffffffu) {  // a tile with rows outside the list
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int e = 0; e < 4; ++e)
+        if (!((mk >> (8 * q + 4 * g + e)) & 1u)) s4[e] = kNegInf;
+    }
+    // P against the running max; this wave's row-slice max for the check
+    float pj[4];
+    {
+      const float mu = m_run == kNegInf ? 0.f : m_run;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 8 * j + 4 * g + e;
-        const float v = ((mk >> row) & 1u) ? sc[4 * j + e] * p.scale_log2 : kNegInf;
-        sc[4 * j + e] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = xor32_max(tmax);
-    if (__ballot(tmax > m_run + 8.f)) {
-      const float nm = fmaxf(m_run, tmax);
+      for (int e = 0; e < 4; ++e) pj[e] = fast_exp2(s4[e] - mu);
+    }
+    s_p[hb][q][lane] = make_uint2(pack_bf16x2(pj[0], pj[1]), pack_bf16x2(pj[2], pj[3]));
+    {
+      const float lm = xor32_max(fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3])));
+      if (g == 0) s_mx[hb][q][n] = lm;
+    }
+    if (tile + 1 < t1) {  // this wave's copies of the next tile landed
+      if (tile + 2 < t1) vm_wait<NI>();
+      else vm_wait<0>();
+    }
+    lds_barrier();  // C
+    // tile max of head n in both head blocks; every wave tracks both running
+    // maxima, so the rescale decision is the same in all waves
+    const float tm = fmaxf(fmaxf(s_mx[hb][0][n], s_mx[hb][1][n]), fmaxf(s_mx[hb][2][n], s_mx[hb][3][n]));
+    float tm_o = kNegInf;
+    if constexpr (HB > 1)
+      tm_o = fmaxf(fmaxf(s_mx[hb ^ 1][0][n], s_mx[hb ^ 1][1][n]), fmaxf(s_mx[hb ^ 1][2][n], s_mx[hb ^ 1][3][n]));
+    if (__ballot(tm > m_run + 8.f || tm_o > m_oth + 8.f)) {  // rescale to the tile max, recompute P
+      const float nm = fmaxf(m_run, tm);
       const float corr = nm == kNegInf ? 1.f : fast_exp2(m_run - nm);
       l_run *= corr;
 #pragma unroll
       for (int db = 0; db < WDB; ++db) acc[db] *= corr;
       m_run = nm;
+      m_oth = fmaxf(m_oth, tm_o);
+      const float mu = m_run == kNegInf ? 0.f : m_run;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pj[e] = fast_exp2(s4[e] - mu);
+      s_p[hb][q][lane] = make_uint2(pack_bf16x2(pj[0], pj[1]), pack_bf16x2(pj[2], pj[3]));
+      lds_barrier();  // nobody has read the first P yet
     }
-    const float mu = m_run == kNegInf ? 0.f : m_run;
-    float psum = 0.f;
+    l_run += (pj[0] + pj[1]) + (pj[2] + pj[3]);
+    uint2 pr[4];  // P of rows j = 0..3 (this lane's g half)
+    wide_p_reads(pr, p_a);
     uint32_t pw[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float pj[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pj[e] = fast_exp2(sc[4 * j + e] - mu);
-        psum += pj[e];
-      }
-      pw[2 * j] = pack_bf16x2(pj[0], pj[1]);
-      pw[2 * j + 1] = pack_bf16x2(pj[2], pj[3]);
+      pw[2 * j] = pr[j].x;
+      pw[2 * j + 1] = pr[j].y;
     }
-    l_run += psum;
     // O^T += V^T P^T, two 16-row blocks: P^T of block kb is this lane's rows of j = 2kb, 2kb+1
+    {
+      s16x4 va[2][8];
+      uint32_t ta[8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s16x4 va[8];
-      const uint32_t o = sa + 4096u * kb;
-      const uint32_t ta[4] = {o + toff[kb], o + toff[1 - kb], o + toff[2 + kb], o + toff[3 - kb]};
+      for (int k = 0; k < 8; ++k) ta[k] = sa + toff[k];
       wide_tr_reads(va, ta);
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pw[4 * kb], pw[4 * kb + 1], pw[4 * kb + 2], pw[4 * kb + 3]));
 #pragma unroll
-      for (int db = 0; db < WDB; ++db) {
-        const s16x4 a0 = va[2 * db], a1 = va[2 * db + 1];
-        const bf16x8 a = __builtin_bit_cast(bf16x8, s16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pw[4 * kb], pw[4 * kb + 1], pw[4 * kb + 2], pw[4 * kb + 3]));
+#pragma unroll
+        for (int db = 0; db < WDB; ++db) {
+          const s16x4 a0 = va[kb][2 * db], a1 = va[kb][2 * db + 1];
+          const bf16x8 a = __builtin_bit_cast(bf16x8, s16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
+        }
       }
     }
     slot = slot == WSLOTS - 1 ? 0 : slot + 1;
   }
   const float M = m_run;
-  float L = xor32_sum(l_run);
+  float L;
+  {  // the row sums of the four slices (same scale in every wave), fixed order
+    const float lw = xor32_sum(l_run);
+    lds_barrier();  // every wave is past its last read of s_mx
+    if (g == 0) s_mx[hb][q][n] = lw;
+    lds_barrier();
+    L = ((s_mx[hb][0][n] + s_mx[hb][1][n]) + s_mx[hb][2][n]) + s_mx[hb][3][n];
+  }
 
   const int64_t head = head0 + n;
   if (S == 1) {

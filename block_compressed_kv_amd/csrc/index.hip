@@ -29,8 +29,8 @@ struct IndexParams {
   const int64_t* pos;
   int32_t* out_idx;
   float* out_score;
-  float* scores;  // [B][entries]
-  int64_t heads, entries, k, m;
+  float* scores;  // [B][stride]
+  int64_t heads, entries, k, m, stride;  // stride: entries rounded up to 4 (16-byte rows)
 };
 
 __device__ __forceinline__ int64_t n_visible(const IndexParams& p, int64_t b) {
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexParams p) {
       for (int j = 0; j < 4; ++j) v[j] += __shfl_xor(v[j], o, 64);
     const int64_t kbase = key0 + 16 * hh + 4 * kq;  // keys of lane (., kq): kbase .. kbase+3
     if (n == 0) {
-      float* dst = p.scores + b * p.entries + kbase;
+      float* dst = p.scores + b * p.stride + kbase;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (kbase + j < nv) dst[j] = v[j];
@@ -91,32 +91,28 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive scan of one value per thread over a 1024-thread block.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_sums, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wave_sums[wave] = x;
-  __syncthreads();
-  if (wave == 0) {
-    int s = lane < 16 ? wave_sums[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int y = __shfl_up(s, o, 64);
-      if (lane >= o) s += y;
-    }
-    if (lane < 16) wave_sums[16 + lane] = s;  // inclusive prefix of wave totals
-  }
-  __syncthreads();
-  const int before = wave > 0 ? wave_sums[16 + wave - 1] : 0;
-  if (total) *total = wave_sums[16 + 15];
-  const int r = before + x - v;
-  __syncthreads();
-  return r;
+// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS round trips):
+// shifts by 1, 2, 4, 8 within each 16-lane row, then lane 15 of a row added
+// to the next row, then lane 31 added to the upper half.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// Over the wave's lanes in order, with values v (>= 0) and a running count
+// `before` ahead of lane 0: the first lane where before + (inclusive sum)
+// reaches `target`; *base gets before + the sum of the lanes ahead of it.
+__device__ __forceinline__ int wave_crossing(int v, int target, int before, int* base) {
+  const int x = wave_incl_scan(v);
+  const uint64_t hit = __ballot(before + x >= target);
+  const int L = hit ? (int)__builtin_ctzll(hit) : 63;
+  *base = before + __builtin_amdgcn_readlane(x - v, L);
+  return L;
 }
 
 // One workgroup per sequence; every thread keeps KPT scores (as order-preserving
@@ -129,15 +125,22 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_sums, int* 
 // it in index order, from per-(round, wave) counts scanned across the block.
 template <int KPT>
 __global__ __launch_bounds__(1024) void topk_kernel(IndexParams p) {
-  __shared__ int hist[4096];
-  __shared__ int scan_buf[32];
+  // LDS: first the scores (copied straight from global memory), then the
+  // histograms (4 interleaved copies per bin, so lanes of one wave that hit
+  // the same bin mostly hit different words)
+  constexpr int STAGE = KPT <= 32 ? KPT * 1024 : 0;
+  constexpr int LDS_WORDS = STAGE > 4096 * 5 ? STAGE : 4096 * 5;  // histogram + candidate list
+  __shared__ __attribute__((aligned(16))) int lds_words[LDS_WORDS];
+  int* hist = lds_words;
   __shared__ int s_gt[KPT * 16], s_eq[KPT * 16];
+  __shared__ int s_part[1024];
+  __shared__ int s_nc;
   __shared__ int s_pick[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t b = blockIdx.x;
   const int nv = (int)n_visible(p, b);
   const int K = (int)p.k;
-  const float* sc = p.scores + b * p.entries;
+  const float* sc = p.scores + b * p.stride;
   int32_t* oi = p.out_idx + b * K;
   float* os = p.out_score ? p.out_score + b * K : nullptr;
 
@@ -151,54 +154,121 @@ __global__ __launch_bounds__(1024) void topk_kernel(IndexParams p) {
   }
 
   uint32_t key[KPT];
+  if constexpr (STAGE > 0) {
+    // 16-byte copies of the visible scores to LDS (lane i of a wave writes
+    // bytes 16 i of the wave's 1 KB), the last nv % 4 scores one by one
+    const int nc = nv >> 2;
+    float* stage = reinterpret_cast<float*>(lds_words);
+    for (int c0 = wave * 64; c0 < nc; c0 += 1024) {
+      if (c0 + lane < nc)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(reinterpret_cast<uintptr_t>(sc + 4 * (c0 + lane))),
+                                         (lds_void*)(stage + 4 * c0), 16, 0, 0);
+    }
+    if (tid < nv - 4 * nc) stage[4 * nc + tid] = sc[4 * nc + tid];
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies landed
+    __syncthreads();
 #pragma unroll
-  for (int r = 0; r < KPT; ++r) {
-    const int i = r * 1024 + tid;
-    key[r] = i < nv ? order_key(sc[i]) : 0u;
+    for (int r = 0; r < KPT; ++r) {
+      const int i = r * 1024 + tid;
+      key[r] = i < nv ? order_key(stage[i]) : 0u;
+    }
+    __syncthreads();  // the LDS becomes the histogram
+  } else {
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const int i = r * 1024 + tid;
+      key[r] = i < nv ? order_key(sc[i]) : 0u;
+    }
   }
 
   uint32_t prefix = 0, pmask = 0;
   int remaining = K;
+  // candidate list (keys of the chosen first-pass bin) in the LDS past the histogram
+  constexpr int kCandMax = (LDS_WORDS - 4 * 4096) > 4096 ? 4096 : (LDS_WORDS - 4 * 4096);
+  uint32_t* cand = reinterpret_cast<uint32_t*>(lds_words + 4 * 4096);
+  int n_cand = -1;
+  auto count = [&](int bin) {
+    const int4 h = *reinterpret_cast<const int4*>(&hist[4 * bin]);
+    return h.x + h.y + h.z + h.w;
+  };
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
     const int nb = pass == 0 ? 4096 : 1024;
-    for (int i = tid; i < nb; i += 1024) hist[i] = 0;
+    for (int i = tid; i < nb; i += 1024) *reinterpret_cast<int4*>(&hist[4 * i]) = make_int4(0, 0, 0, 0);
     __syncthreads();
+    // Keys past the visible entries are 0 and every visible key is at least
+    // 2^23 (order image of a finite float), so they fall in bin 0 of the first
+    // pass (never the chosen one) and never match a later prefix.
+    if (pass > 0 && n_cand >= 0) {  // the chosen first-pass bin's keys, compacted
+      for (int c = tid; c < n_cand; c += 1024) {
+        const uint32_t k = cand[c];
+        if ((k & pmask) == prefix) atomicAdd(&hist[4 * ((k >> shift) & (uint32_t)(nb - 1)) + (lane & 3)], 1);
+      }
+    } else {
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const bool in = r * 1024 + tid < nv && (key[r] & pmask) == prefix;
-      if (in) atomicAdd(&hist[(key[r] >> shift) & (uint32_t)(nb - 1)], 1);
+      for (int r = 0; r < KPT; ++r)
+        if ((key[r] & pmask) == prefix)
+          atomicAdd(&hist[4 * ((key[r] >> shift) & (uint32_t)(nb - 1)) + (lane & 3)], 1);
     }
     __syncthreads();
-    // bins from the top: thread t holds bins nb-1-t*per .. nb-per-t*per
+    // find the bin holding the remaining-th largest key: thread t sums bins
+    // nb-1-t*per .. nb-(t+1)*per (per = nb/1024) into s_part[t]; then one wave
+    // narrows it down: 16 threads per lane, then the thread, then its bins
     const int per = nb / 1024;
-    int local = 0;
-    for (int j = 0; j < per; ++j) local += hist[nb - 1 - tid * per - j];
-    const int above = block_exclusive_scan(local, scan_buf, nullptr);
-    if (above < remaining && remaining <= above + local) {
-      int c = above;
-      for (int j = 0; j < per; ++j) {
-        const int bin = nb - 1 - tid * per - j;
-        const int h = hist[bin];
-        if (c + h >= remaining) {
-          s_pick[0] = bin;
-          s_pick[1] = remaining - c;
-          break;
-        }
-        c += h;
+    {
+      int local = 0;
+      for (int j = 0; j < per; ++j) local += count(nb - 1 - tid * per - j);
+      s_part[tid] = local;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int l16 = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) l16 += s_part[16 * lane + j];
+      int base;
+      const int L = wave_crossing(l16, remaining, 0, &base);  // lane holding the crossing
+      const int tv = lane < 16 ? s_part[16 * L + lane] : 0;
+      const int J = wave_crossing(tv, remaining, base, &base);
+      const int t = 16 * L + J;
+      const int bv = lane < per ? count(nb - 1 - t * per - lane) : 0;
+      const int jb = wave_crossing(bv, remaining, base, &base);
+      if (lane == 0) {
+        s_pick[0] = nb - 1 - t * per - jb;
+        s_pick[1] = remaining - base;
       }
     }
     __syncthreads();
     prefix |= (uint32_t)s_pick[0] << shift;
     pmask |= (uint32_t)(nb - 1) << shift;
     remaining = s_pick[1];
-    __syncthreads();
+    if (pass == 0) {  // compact the chosen bin's keys (if they fit) for the later passes
+      const int nbin = count(s_pick[0]);
+      __syncthreads();  // every wave has read the count; the list may overwrite LDS past the histogram
+      if (nbin <= kCandMax) {
+        if (tid == 0) s_nc = 0;
+        __syncthreads();
+        // one LDS atomic per wave: lane offsets from a scan of per-thread counts
+        int mine = 0;
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) mine += (key[r] & pmask) == prefix;
+        const int incl = wave_incl_scan(mine);
+        int base = 0;
+        if (lane == 63) base = atomicAdd(&s_nc, incl);
+        int at = __builtin_amdgcn_readlane(base, 63) + incl - mine;
+#pragma unroll
+        for (int r = 0; r < KPT; ++r)
+          if ((key[r] & pmask) == prefix) cand[at++] = key[r];
+        __syncthreads();
+        n_cand = s_nc;
+      }
+    }
   }
   const uint32_t thr = prefix;       // key of the k-th largest score
   const int need_eq = remaining;     // keys equal to it to take, lowest index first
 
-  // counts above / equal to the threshold per (round, wave), scanned in index order
+  // counts above / equal to the threshold per (round, wave), then one wave
+  // turns them into exclusive prefixes in index order (round-major)
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
     const bool in = r * 1024 + tid < nv;
@@ -209,24 +279,26 @@ __global__ __launch_bounds__(1024) void topk_kernel(IndexParams p) {
     }
   }
   __syncthreads();
-  for (int e0 = 0; e0 < KPT * 16; e0 += 1024) {  // entries in index order (round-major)
-    const int e = e0 + tid;
-    const bool ok = e < KPT * 16;
-    int gt_tot, eq_tot;
-    const int g = ok ? s_gt[e] : 0, q = ok ? s_eq[e] : 0;
-    const int gp = block_exclusive_scan(g, scan_buf, &gt_tot);
-    const int qp = block_exclusive_scan(q, scan_buf, &eq_tot);
-    if (ok) {
-      s_gt[e] = gp + (e0 > 0 ? hist[0] : 0);
-      s_eq[e] = qp + (e0 > 0 ? hist[1] : 0);
+  if (wave == 0) {
+    constexpr int PER = KPT * 16 / 64;  // entries per lane
+    int lg = 0, lq = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      lg += s_gt[lane * PER + j];
+      lq += s_eq[lane * PER + j];
     }
-    __syncthreads();
-    if (tid == 0) {  // running totals for the next 1024 entries
-      hist[0] = (e0 > 0 ? hist[0] : 0) + gt_tot;
-      hist[1] = (e0 > 0 ? hist[1] : 0) + eq_tot;
+    const int xg = wave_incl_scan(lg), xq = wave_incl_scan(lq);
+    int cg = xg - lg, cq = xq - lq;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int g = s_gt[lane * PER + j], q = s_eq[lane * PER + j];
+      s_gt[lane * PER + j] = cg;
+      s_eq[lane * PER + j] = cq;
+      cg += g;
+      cq += q;
     }
-    __syncthreads();
   }
+  __syncthreads();
   const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
@@ -247,7 +319,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(IndexParams p) {
 }
 
 size_t index_workspace_bytes(const csa_index_args& a) {
-  return (size_t)a.batch * (size_t)a.entries * sizeof(float);
+  return (size_t)a.batch * (size_t)((a.entries + 3) & ~int64_t(3)) * sizeof(float);
 }
 
 hipError_t launch_index_topk(const csa_index_args& a, void* ws, hipStream_t stream) {
@@ -260,6 +332,7 @@ hipError_t launch_index_topk(const csa_index_args& a, void* ws, hipStream_t stre
   p.out_score = a.out_score;
   p.scores = static_cast<float*>(ws);
   p.heads = a.heads; p.entries = a.entries; p.k = a.k; p.m = a.block;
+  p.stride = (a.entries + 3) & ~int64_t(3);
   if (a.entries > 0) {
     const dim3 grid((unsigned)((a.entries + 255) / 256), (unsigned)a.batch);
     switch (a.dim) {
