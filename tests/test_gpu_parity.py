@@ -272,6 +272,27 @@ def test_decode_hca_treated(lib, rd, nb):
     check_bf16(host(lse), rl, "HCA lse")
 
 
+@pytest.mark.parametrize("Hq,B,nb", [(16, 3, 40), (32, 2, 40), (48, 1, 7), (32, 1, 300)])
+def test_decode_mqa_512_head_counts(lib, Hq, B, nb):
+    # 512-dim shared-series MQA with 16 or 48 query heads (16-head groups) and
+    # 32 (one 32-head block of the wide kernel), treated, with a sink
+    d, m, W = 512, 128, 128
+    T = 128 * nb + 33
+    H = _dev(synth.hca_layer(f"dec-mqa512-{Hq}-{B}-{nb}", B, Hq, T, d, m))
+    t_list = [T - 1, 128 * 3 + 5, 900][:B]
+    N = T // m
+    entries = torch.zeros((B, 1, N, d), dtype=torch.bfloat16, device=DEV)
+    treat = dict(rmsnorm_eps=1e-6, rope_dims=64)
+    lib.pool_blocks(H["c"], H["z"], H["bias"], m, 0, N, entries, **treat)
+    pos = torch.tensor(t_list, device=DEV)
+    o, lse = lib.attend_decode(H["q"], entries, H["c"], pos, m, W, O.OVERLAP, sink=H["sink"], **treat)
+    pooled = O.pool_single(host(H["c"]), host(H["z"]), host(H["bias"]), m, 0, N)
+    ro, rl = O.attend_decode(host(H["q"]), pooled, None, host(H["c"]), None, t_list, m, W, O.OVERLAP,
+                             1 / math.sqrt(d), sink=host(H["sink"]), **treat)
+    check_bf16(host(o), ro, f"MQA-512 decode Hq={Hq}")
+    check_bf16(host(lse), rl, "lse")
+
+
 def test_decode_selected_entries(lib):
     # CSA-style: dual-pooled treated entries, a selection with -1 padding and invisible
     # ids, plus the 128-token window; MQA 64 heads, d=512
