@@ -13,12 +13,16 @@ touches (pooled cache, the last 192 raw tokens, the due block's logits); the
 every step streams from HBM.  The 14 launches are captured once as a HIP graph
 and replayed; HIP events on the launch stream bracket the timed region.
 
-Also reported: the decode launch's HBM roofline fraction, the oracle on the
-host cores (cpu_baseline), batch 1 and 4, the step with the due block pooled
-first (a block leaves the window every 64 steps), pooling GB/s for the whole
-history, and chunked prefill (16K context in 2048-token chunks) TFLOP/s.
+Also reported: the decode launch's HBM roofline fraction (and its HBM traffic
+from stored counter passes), the oracle on the host cores (cpu_baseline), batch
+1 and 4, the step with the due block pooled first (a block leaves the window
+every 64 steps), pooling GB/s for the whole history, chunked prefill (16K
+context in 2048-token chunks) TFLOP/s, HCA decode at 1M context (batch 4, 64
+query heads x 512, pooling GB/s of the whole history) and CSA at 128K (batch 2:
+indexer scores + top-512, decode over the selection, dual pooling GB/s).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py --counters    # only what the FETCH_SIZE / WRITE_SIZE passes profile
 """
 from __future__ import annotations
 
@@ -55,6 +59,57 @@ T_POS = CTX - 1                        # query position
 N_POOLED = 510                         # visible pooled entries at T_POS
 RAW0 = 509 * M                         # first token kept raw: block 509 (due) + window
 RAW_ROWS = CTX - RAW0                  # 192
+
+
+# HBM traffic of the batch-16 decode launch, from two rocprofv3 --pmc passes over
+# `python bench.py --counters` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, median over the
+# decode dispatches).  Each counter is scaled by what it reads for the 256 MiB device-to-device
+# copy in the same run (FETCH_SIZE reports half the bytes a copy reads, WRITE_SIZE all it
+# writes).  The figure holds only for the decode source it was taken on: when the hash of
+# decode.hip + decode_common.h differs, bench reports traffic as null.
+COUNTERS = {"fetch_kib": 20553.5625, "write_kib": 197.0,
+            "copy_fetch_kib": 131083.5, "copy_write_kib": 262144.0, "copy_bytes": 256 << 20,
+            "source_sha256": "6939baec9d4c88dacafe7b006d703f0c814584bf88d2eafd3567b6c34f332aab"}
+COUNTER_SOURCES = ("decode.hip", "decode_common.h")
+
+
+def decode_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_compressed_kv_amd", "csrc")
+    for f in COUNTER_SOURCES:
+        with open(os.path.join(base, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic_bytes():
+    """HBM bytes per decode launch from the stored counter passes, or None if the source moved."""
+    c = COUNTERS
+    if c["source_sha256"] != decode_source_sha256():
+        return None
+    fetch = c["fetch_kib"] * c["copy_bytes"] / (c["copy_fetch_kib"] * 1024.0)
+    write = c["write_kib"] * c["copy_bytes"] / (c["copy_write_kib"] * 1024.0)
+    return (fetch + write) * 1024.0
+
+
+def counter_pass():
+    """What the --pmc passes profile: a 256 MiB copy (the counters' scale) and 3 decode steps."""
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    B = 16
+    pos = torch.full((B,), T_POS, dtype=torch.int64, device="cuda")
+    rpb = torch.full((B,), RAW0, dtype=torch.int64, device="cuda")
+    layers = [DecodeLayer(l, B, pos, rpb) for l in range(LAYERS)]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for L in layers:
+            L.decode()
+    torch.cuda.synchronize()
+    log(f"[bench] counter pass: 3 copies of {n} B, {3 * LAYERS} decode launches at batch {B}")
 
 
 def decode_bytes_per_seq_layer():
@@ -385,6 +440,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-small-batch", action="store_true")
     ap.add_argument("--no-mqa", action="store_true", help="skip the HCA 1M and CSA 128K lines")
+    ap.add_argument("--counters", action="store_true",
+                    help="only run what the FETCH_SIZE / WRITE_SIZE counter passes profile")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the decode/prefill hot path here has no multi-GPU "
@@ -394,6 +451,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     lbca.lib()  # fail loudly if the library is missing
+    if args.counters:
+        counter_pass()
+        return
 
     B = args.batch
     log(f"[bench] decode 32K: building {LAYERS} layers at batch {B}")
@@ -408,6 +468,7 @@ def main():
 
     per_launch_bytes = decode_bytes_per_seq_layer() * B
     achieved = per_launch_bytes / (us_launch * 1e-6) / 1e9
+    traffic = measured_traffic_bytes()
     value = LAYERS / (ms_step * 1e-3)
     us_pool = (ms_pool_step - ms_step) * 1e3 / LAYERS
     extra = {
@@ -418,6 +479,7 @@ def main():
         "amortised_layer_steps_per_s": 1e6 / (us_launch + us_pool / M),
         "history_pool_GBps": pool_bytes / (pool_ms * 1e-3) / 1e9,
         "history_pool_bytes": pool_bytes,
+        "decode_traffic_over_algorithmic": None if traffic is None else traffic / per_launch_bytes,
     }
 
     cpu = None
@@ -463,7 +525,7 @@ def main():
                    "q_heads": HQ, "kv_heads": HKV, "head_dim": D, "block": M, "window": W,
                    "layers": LAYERS, "step": "one lbca_attend_decode launch per layer"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "decode_kernel (lbca_attend_decode, one workgroup per unit at batch 16)"},
         "cpu_baseline": cpu,
         "extra": extra,
