@@ -40,6 +40,8 @@
 // decode_merge_kernel combines them in a fixed order (bitwise reproducible).
 // No device-scope fence is used anywhere: on this multi-XCD part a
 // device-scope release/acquire writes back and invalidates the XCD's L2.
+#include <type_traits>
+
 #include "decode_common.h"
 
 #ifndef LBCA_DECODE_TILES_PER_WAVE
@@ -213,6 +215,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
   __shared__ double s_freq[RD > 0 ? RD / 2 : 1];  // RoPE turns per position, pair k
   __shared__ int s_ids[SPEC ? 1 : kSelLds];        // selected ids of this workgroup's range
 
+  preload_params(p);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile choices stay scalar
   const int n = lane & 15, kq = lane >> 4;
@@ -237,6 +240,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
   const int64_t head0 = kvh * p.G + slot0;  // first query head of the unit
   const bool head_ok = n < nvalid;
 
+  // the position first (scalar loads: waiting for them does not wait for the rows)
+  const int64_t t_pos = load_uniform(p.pos + b);
+  const int64_t t_base = p.rpb ? load_uniform(p.rpb + b) : 0;
   // queries of this head group as B operands (zero for padded heads); their
   // addresses do not depend on the position, so they load alongside it
   uint4 qr[KS];
@@ -286,7 +292,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
       }
     }
   }
-  const SeqView sv = seq_view(p, b);
+  const SeqView sv = seq_view(p, b, t_pos, t_base);
   if (!sv.ok) {  // rows do not fit the buffers: NaN, written once per unit and slice
     if (split == 0) {
       for (int i = tid; i < nvalid * DV; i += blockDim.x)
@@ -591,11 +597,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
 // (NG = 256 / CK split groups; all loads independent); the groups are added
 // in LDS in a fixed order, and thread (slot, u < CK/8) finishes the pair of
 // float4s at c0 + 4u and c0 + 4u + CK/2 (a rotate-half pair in the last chunk).
+// NORM: each split's partial is its own normalised output in bf16 (the wide
+// path), weighted by exp2(m_s - M) * l_s instead of exp2(m_s - M).
 constexpr int kMergeGroups = 4;  // for 64-dim chunks
+template <bool NORM>
 __global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeParams p, int D, int CK) {
   __shared__ float s_w[64][16], s_l[64][16];  // split maxima (then weights) and sums
   __shared__ float s_inv[16], s_lse[16];
   __shared__ float4 s_part[kMergeGroups][16][32];  // [group][slot][float4 of the chunk], CK <= 128
+  using PT = typename std::conditional<NORM, uint2, float4>::type;  // one partial's 4 dims
+  constexpr int kPre = 8;  // partials per thread requested before the weights are known
   const int tid = threadIdx.x;
   const int64_t unit = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
   const int hg = (int)(blockIdx.x % (unsigned)p.head_groups);
@@ -604,16 +615,30 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeParams p, int 
   const int slot0 = hg * 16;
   const int nvalid = (int)(p.G - slot0 < 16 ? p.G - slot0 : 16);
   const int64_t head0 = kvh * p.G + slot0;
-  const SeqView sv = seq_view(p, b);
-  if (!sv.ok) return;  // the decode kernel already wrote NaN for this unit
   const int S = p.splits;
   const int64_t part0 = unit * S;
+  const int nf = CK / 4;   // float4s per slot in the chunk
+  const int NG = 256 / CK;  // split groups
+  const int c0 = (int)blockIdx.z * CK;
+  const int u0 = tid % nf, sl0 = (tid / nf) % 16, sg = tid / (nf * 16);
+  const bool mine = sg < NG && sl0 < nvalid;
+  const int64_t off = (part0 * 16 + sl0) * D + c0 + 4 * u0;
+  const PT* pa = reinterpret_cast<const PT*>(NORM ? static_cast<const void*>(p.ws_o + off)
+                                                  : static_cast<const void*>(p.ws_acc + off));
+  const int64_t pstride = (int64_t)16 * D / 4;  // one split on, in units of PT
+  // this thread's first partials (splits sg, sg + NG, ...) go out with the maxima
+  PT pre[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i)
+    if (mine && sg + i * NG < S) pre[i] = pa[(int64_t)(sg + i * NG) * pstride];
   // every split's (max, sum) of the 16 slots to LDS at once (one load per thread)
   for (int i = tid; i < S * 16; i += blockDim.x) {
     const float2 ml = *reinterpret_cast<const float2*>(&p.ws_ml[(part0 * 16 + i) * 2]);
     s_w[i >> 4][i & 15] = ml.x;
     s_l[i >> 4][i & 15] = ml.y;
   }
+  const SeqView sv = seq_view(p, b);
+  if (!sv.ok) return;  // the decode kernel already wrote NaN for this unit
   __syncthreads();
   if (tid < nvalid) {
     float M = kNegInf;
@@ -622,7 +647,7 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeParams p, int 
     for (int s = 0; s < S; ++s) {
       const float ms = s_w[s][tid];
       const float sw = ms == kNegInf ? 0.f : exp2f(ms - M);
-      s_w[s][tid] = sw;
+      s_w[s][tid] = NORM ? sw * s_l[s][tid] : sw;
       L = fmaf(s_l[s][tid], sw, L);
     }
     if (p.sink) L += exp2f(p.sink[head0 + tid] * kLog2e - M);
@@ -630,22 +655,21 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeParams p, int 
     s_lse[tid] = (M + log2f(L)) * 0.69314718055994531f;
   }
   __syncthreads();
-  const int nf = CK / 4;   // float4s per slot in the chunk
-  const int NG = 256 / CK;  // split groups
-  const int c0 = (int)blockIdx.z * CK;
-  {
-    const int u = tid % nf, sl = (tid / nf) % 16, sg = tid / (nf * 16);
-    if (sg < NG && sl < nvalid) {
-      const float* pa = p.ws_acc + (part0 * 16 + sl) * D + c0 + 4 * u;
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-      for (int s = sg; s < S; s += NG) {
-        const float w = s_w[s][sl];
-        const float4 a = *reinterpret_cast<const float4*>(pa + (int64_t)s * 16 * D);
+  if (mine) {
+    auto add = [&](float4& x, const PT& a, float w) {
+      if constexpr (NORM) {
+        x.x = fmaf(lo_bf16(a.x), w, x.x); x.y = fmaf(hi_bf16(a.x), w, x.y);
+        x.z = fmaf(lo_bf16(a.y), w, x.z); x.w = fmaf(hi_bf16(a.y), w, x.w);
+      } else {
         x.x = fmaf(a.x, w, x.x); x.y = fmaf(a.y, w, x.y); x.z = fmaf(a.z, w, x.z); x.w = fmaf(a.w, w, x.w);
       }
-      s_part[sg][sl][u] = x;
-    }
+    };
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < kPre; ++i)
+      if (sg + i * NG < S) add(x, pre[i], s_w[sg + i * NG][sl0]);
+    for (int s = sg + kPre * NG; s < S; s += NG) add(x, pa[(int64_t)s * pstride], s_w[s][sl0]);
+    s_part[sg][sl0][u0] = x;
   }
   __syncthreads();
   const int sl = tid / (nf / 2), u = tid % (nf / 2);
@@ -681,11 +705,12 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeParams p, int 
   if (p.lse && blockIdx.z == 0 && tid < nvalid) p.lse[b * p.hq + head0 + tid] = s_lse[tid];
 }
 
-void launch_decode_merge(const DecodeParams& p, int64_t batch, int64_t dim, hipStream_t stream) {
+void launch_decode_merge(const DecodeParams& p, int64_t batch, int64_t dim, bool norm, hipStream_t stream) {
   // chunks of the rotated width when dims rotate, else of min(dim, 64)
   const int ck = p.rope_dims > 0 ? p.rope_dims : (dim < 64 ? (int)dim : 64);
-  decode_merge_kernel<<<dim3((unsigned)(p.hkv * p.head_groups), (unsigned)batch, (unsigned)(dim / ck)),
-                        1024, 0, stream>>>(p, (int)dim, ck);
+  const dim3 grid((unsigned)(p.hkv * p.head_groups), (unsigned)batch, (unsigned)(dim / ck));
+  if (norm) decode_merge_kernel<true><<<grid, 1024, 0, stream>>>(p, (int)dim, ck);
+  else decode_merge_kernel<false><<<grid, 1024, 0, stream>>>(p, (int)dim, ck);
 }
 
 // ---------------------------------------------------------------------------
@@ -694,10 +719,15 @@ static int waves_per_wg(int64_t dim) { return dim <= 128 ? 8 : 4; }
 
 // Wide-row MQA path (512 dims, shared series, query heads in 32-head blocks):
 // workgroups per (sequence, KV head) along the row list.  Enough splits to
-// give about LBCA_WIDE_TARGET_WGS workgroups (one CU streams only about
-// 40 GB/s), but at least LBCA_WIDE_MIN_TILES 32-row tiles per workgroup (a
-// split's partial, 64 KB per head block, stays below the rows it reads), and
-// enough that each range's selected ids fit the LDS stage.
+// give about LBCA_WIDE_TARGET_WGS row ranges (one CU streams only about
+// 40 GB/s), but at least LBCA_WIDE_MIN_TILES 32-row tiles per range (a
+// split's bf16 partial, 32 KB per head block, stays below the rows it reads),
+// and enough that each range's selected ids fit the LDS stage.  With 64 query
+// heads each range is worked by two 4-wave "twin" workgroups, one per 32-head
+// block (LBCA_WIDE_TWINS), rather than one 8-wave workgroup for both.
+#ifndef LBCA_WIDE_TWINS
+#define LBCA_WIDE_TWINS 1
+#endif
 #ifndef LBCA_WIDE_TARGET_WGS
 #define LBCA_WIDE_TARGET_WGS 128
 #endif
@@ -716,7 +746,12 @@ static DecodePlan plan_decode_wide(const lbca_decode_args& a, int64_t G) {
   const int64_t raw_span = a.mode == LBCA_EXCLUSIVE ? a.window + a.block - 1 : a.window;
   const int64_t raw_max = raw_span < a.raw_rows ? raw_span : a.raw_rows;
   const int64_t tiles = (sel_max + 31) / 32 + (raw_max + 31) / 32;
-  const int64_t per_split = a.batch * a.kv_heads;  // workgroups per split
+  pl.wide_twins = 1;
+  if (LBCA_WIDE_TWINS && pl.wide_blocks == 2) {  // one 4-wave workgroup per 32-head block
+    pl.wide_twins = 2;
+    pl.wide_blocks = 1;
+  }
+  const int64_t per_split = a.batch * a.kv_heads;  // (sequence, KV head) ranges per split
   int64_t s = (LBCA_WIDE_TARGET_WGS + per_split - 1) / per_split;
   const int64_t by_rows = (tiles + LBCA_WIDE_MIN_TILES - 1) / LBCA_WIDE_MIN_TILES;
   if (s > by_rows) s = by_rows;
@@ -727,7 +762,7 @@ static DecodePlan plan_decode_wide(const lbca_decode_args& a, int64_t G) {
   pl.splits = (int)s;
   if (s == 1) return pl;
   const size_t u = (size_t)(a.batch * a.kv_heads * pl.head_groups);
-  pl.ws_bytes = u * s * 16 * 2 * sizeof(float) + u * s * 16 * (size_t)a.dim * sizeof(float);
+  pl.ws_bytes = u * s * 16 * 2 * sizeof(float) + u * s * 16 * (size_t)a.dim * sizeof(bf16_t);
   return pl;
 }
 
@@ -820,7 +855,9 @@ hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void
   if (plan.splits > 1) {
     p.ws_ml = static_cast<float*>(ws);
     p.ws_acc = p.ws_ml + units * plan.splits * 16 * 2;
+    p.ws_o = reinterpret_cast<bf16_t*>(p.ws_acc);
   }
+  p.wide_twins = plan.wide_twins;
   p.hq = a.q_heads; p.hkv = a.kv_heads; p.G = G;
   p.entries = a.entries; p.raw_rows = a.raw_rows; p.k_sel = a.sel_idx ? a.k_sel : 0;
   p.m = a.block; p.W = a.window; p.mode = a.mode;
@@ -835,7 +872,7 @@ hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void
   if (plan.wide_blocks > 0) {
     hipError_t e = launch_decode_wide(p, a.rope_dims, treat, plan.wide_blocks, stream);
     if (e != hipSuccess || plan.splits == 1) return e;
-    launch_decode_merge(p, a.batch, a.dim, stream);
+    launch_decode_merge(p, a.batch, a.dim, true, stream);
     return hipGetLastError();
   }
   const size_t pairs = units * plan.splits;  // (unit, split) pairs
@@ -852,7 +889,7 @@ hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || plan.splits == 1) return e;
-  launch_decode_merge(p, a.batch, a.dim, stream);
+  launch_decode_merge(p, a.batch, a.dim, false, stream);
   return hipGetLastError();
 }
 

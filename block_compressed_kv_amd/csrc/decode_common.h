@@ -18,15 +18,37 @@ struct DecodeParams {
   float* out;
   float* lse;
   float* ws_ml;    // [units * splits][16][2]
-  float* ws_acc;   // [units * splits][16][D]
+  float* ws_acc;   // [units * splits][16][D] unnormalised fp32 partials (decode_kernel)
+  bf16_t* ws_o;    // [units * splits][16][D] normalised bf16 partials (wide path)
   int64_t hq, hkv, G, entries, raw_rows, k_sel, m, W;
   int mode, splits, head_groups;
   int units;       // batch * kv_heads * head_groups
+  int wide_twins;  // wide path: workgroups per (sequence, KV head, split), one per head-block set
   float scale_log2;
   float eps;
   int rope_dims;
   double log2_base;
 };
+
+// Puts the argument fields a decode prologue needs into registers before its
+// first branch.  Left to itself the compiler loads kernel arguments one basic
+// block at a time, and at kernel start each of those dependent rounds is a
+// full memory round trip before the first row load can be issued; an empty
+// asm that takes every field as an input makes them one batch.
+__device__ __forceinline__ void preload_params(const DecodeParams& p) {
+  asm volatile("" ::"s"(p.q), "s"(p.pk), "s"(p.pv), "s"(p.rk), "s"(p.rv), "s"(p.pos), "s"(p.rpb), "s"(p.sel),
+               "s"(p.hq), "s"(p.hkv), "s"(p.G), "s"(p.entries), "s"(p.raw_rows), "s"(p.k_sel), "s"(p.m), "s"(p.W),
+               "s"(p.mode), "s"(p.splits), "s"(p.head_groups), "s"(p.units), "s"(p.wide_twins));
+}
+
+// A uniform value the kernel only reads (positions, raw bases), loaded through
+// the scalar cache straight into scalar registers.  A vector load of it would
+// be moved to scalar registers right after issue, which waits for every
+// vector load before it; this one is waited for on its own counter, so row
+// loads issued after it stay in flight.
+__device__ __forceinline__ int64_t load_uniform(const int64_t* ptr) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) int64_t*>(reinterpret_cast<uintptr_t>(ptr));
+}
 
 struct SeqView {
   int64_t t, raw_begin, raw_row0;
@@ -51,13 +73,14 @@ __device__ __forceinline__ SeqView seq_view(const DecodeParams& p, int64_t b, in
   return v;
 }
 __device__ __forceinline__ SeqView seq_view(const DecodeParams& p, int64_t b) {
-  return seq_view(p, b, p.pos[b], p.rpb ? p.rpb[b] : 0);
+  return seq_view(p, b, load_uniform(p.pos + b), p.rpb ? load_uniform(p.rpb + b) : 0);
 }
 
 // Wide-row MQA decode (512 dims, shared series, query heads in blocks of 32
 // per KV head): launched by launch_decode when the plan selects it.
 hipError_t launch_decode_wide(const DecodeParams& p, int rope_dims, bool treat, int head_blocks,
                               hipStream_t stream);
-void launch_decode_merge(const DecodeParams& p, int64_t batch, int64_t dim, hipStream_t stream);
+// norm: the partials are the wide path's normalised bf16 outputs (ws_o).
+void launch_decode_merge(const DecodeParams& p, int64_t batch, int64_t dim, bool norm, hipStream_t stream);
 
 }  // namespace lbca

@@ -9,12 +9,15 @@
 // t, the output rotated back by -t), an attention sink in the denominator, and
 // for CSA only the selected entries plus the sliding window.
 //
-// Work split: a workgroup owns (sequence, KV head, split), a contiguous range
-// of 32-row tiles of the visible-row list (pooled or selected entries, then
-// the raw span), for all query heads of the KV head (one or two blocks of 32):
-// each tile crosses from memory to a CU once.  A CU streams at most about
-// 40 GB/s, so the host picks enough splits to spread the rows over most CUs,
-// few enough that the split partials stay small.
+// Work split: a range is (sequence, KV head, split), a contiguous run of
+// 32-row tiles of the visible-row list (pooled or selected entries, then the
+// raw span).  One workgroup works a range for HB 32-head blocks; with 64
+// query heads the host either launches one 8-wave workgroup (HB = 2) or two
+// 4-wave "twin" workgroups (HB = 1, one per head block) whose linear ids are
+// 8 apart, so both land on the same XCD and the second read of a tile is an
+// L2 hit.  A CU streams at most about 40 GB/s, so the host picks enough splits
+// to spread the rows over most CUs, few enough that the split partials stay
+// small.
 //
 // 4 x HB waves: wave (hb, q) owns head block hb and the 128-dim quarter q of
 // the rows and of the output.  Tiles go straight from global memory to LDS
@@ -39,8 +42,9 @@
 //
 // The running max moves lazily (only when a score exceeds it by 2^8); with
 // one split the workgroup finishes the heads (sink, normalisation, LSE, -t
-// rotation), otherwise it writes its unnormalised partial for
-// decode_merge_kernel in the 16-head-unit layout of the other decode path.
+// rotation), otherwise it writes its own normalised output in bf16 plus its
+// (max, sum) in fp32 for decode_merge_kernel, in the 16-head-unit layout of
+// the other decode path (half the bytes of an fp32 partial).
 // No device-scope fence is used.
 #include <type_traits>
 
@@ -102,35 +106,43 @@ __device__ __forceinline__ void wide_k_reads(uint4 (&r)[WKST], const uint32_t (&
       : "memory");
 }
 
-// The A operands of O^T += V^T P^T for both 16-row blocks of a quarter tile
+// The P^T B operands of this lane for both 16-row blocks: the 8-byte words of
+// the waves that finished rows j = 0..3 (512 bytes apart), pr[j]; and the A
+// operands of O^T += V^T P^T for both 16-row blocks of a quarter tile
 // and the wave's 4 output blocks: lane (i, mq, g) reads rows 16kb + 4g + i/4
 // and 16kb + 8 + 4g + i/4 at dims 32*db + 16*mq + 4*(i%4); the transposing
 // reads give lane (m, g) dims 32*db + m of rows {4g.., 8+4g..} of block kb.
 // a[2*db + h]: address of (row r1 + 8h, block db) in block 0; block 1 is
-// 4096 bytes on (same swizzle).  r[kb][2*db + h].
-__device__ __forceinline__ void wide_tr_reads(s16x4 (&r)[2][8], const uint32_t (&a)[8]) {
+// 4096 bytes on (same swizzle).  r[kb][2*db + h].  All reads in one block
+// with one wait.
+__device__ __forceinline__ void wide_ptr_reads(uint2 (&pr)[4], uint32_t pa, s16x4 (&r)[2][8], const uint32_t (&a)[8]) {
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %16\n"
-      "ds_read_b64_tr_b16 %1, %17\n"
-      "ds_read_b64_tr_b16 %2, %18\n"
-      "ds_read_b64_tr_b16 %3, %19\n"
-      "ds_read_b64_tr_b16 %4, %20\n"
-      "ds_read_b64_tr_b16 %5, %21\n"
-      "ds_read_b64_tr_b16 %6, %22\n"
-      "ds_read_b64_tr_b16 %7, %23\n"
-      "ds_read_b64_tr_b16 %8, %16 offset:4096\n"
-      "ds_read_b64_tr_b16 %9, %17 offset:4096\n"
-      "ds_read_b64_tr_b16 %10, %18 offset:4096\n"
-      "ds_read_b64_tr_b16 %11, %19 offset:4096\n"
-      "ds_read_b64_tr_b16 %12, %20 offset:4096\n"
-      "ds_read_b64_tr_b16 %13, %21 offset:4096\n"
-      "ds_read_b64_tr_b16 %14, %22 offset:4096\n"
-      "ds_read_b64_tr_b16 %15, %23 offset:4096\n"
+      "ds_read_b64 %0, %20\n"
+      "ds_read_b64 %1, %20 offset:512\n"
+      "ds_read_b64 %2, %20 offset:1024\n"
+      "ds_read_b64 %3, %20 offset:1536\n"
+      "ds_read_b64_tr_b16 %4, %21\n"
+      "ds_read_b64_tr_b16 %5, %22\n"
+      "ds_read_b64_tr_b16 %6, %23\n"
+      "ds_read_b64_tr_b16 %7, %24\n"
+      "ds_read_b64_tr_b16 %8, %25\n"
+      "ds_read_b64_tr_b16 %9, %26\n"
+      "ds_read_b64_tr_b16 %10, %27\n"
+      "ds_read_b64_tr_b16 %11, %28\n"
+      "ds_read_b64_tr_b16 %12, %21 offset:4096\n"
+      "ds_read_b64_tr_b16 %13, %22 offset:4096\n"
+      "ds_read_b64_tr_b16 %14, %23 offset:4096\n"
+      "ds_read_b64_tr_b16 %15, %24 offset:4096\n"
+      "ds_read_b64_tr_b16 %16, %25 offset:4096\n"
+      "ds_read_b64_tr_b16 %17, %26 offset:4096\n"
+      "ds_read_b64_tr_b16 %18, %27 offset:4096\n"
+      "ds_read_b64_tr_b16 %19, %28 offset:4096\n"
       "s_waitcnt lgkmcnt(0)\n"
-      : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[0][2]), "=&v"(r[0][3]), "=&v"(r[0][4]), "=&v"(r[0][5]),
+      : "=&v"(pr[0]), "=&v"(pr[1]), "=&v"(pr[2]), "=&v"(pr[3]),
+        "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[0][2]), "=&v"(r[0][3]), "=&v"(r[0][4]), "=&v"(r[0][5]),
         "=&v"(r[0][6]), "=&v"(r[0][7]), "=&v"(r[1][0]), "=&v"(r[1][1]), "=&v"(r[1][2]), "=&v"(r[1][3]),
         "=&v"(r[1][4]), "=&v"(r[1][5]), "=&v"(r[1][6]), "=&v"(r[1][7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "v"(pa), "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
       : "memory");
 }
 
@@ -142,20 +154,6 @@ __device__ __forceinline__ void wide_x4_reads(float4 (&r)[4], uint32_t a) {
       "ds_read_b128 %1, %4 offset:4096\n"
       "ds_read_b128 %2, %4 offset:8192\n"
       "ds_read_b128 %3, %4 offset:12288\n"
-      "s_waitcnt lgkmcnt(0)\n"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-      : "v"(a)
-      : "memory");
-}
-
-// The P^T B operands of this lane for both 16-row blocks: the 8-byte words of
-// the waves that finished rows j = 0..3 (512 bytes apart).
-__device__ __forceinline__ void wide_p_reads(uint2 (&r)[4], uint32_t a) {
-  asm volatile(
-      "ds_read_b64 %0, %4\n"
-      "ds_read_b64 %1, %4 offset:512\n"
-      "ds_read_b64 %2, %4 offset:1024\n"
-      "ds_read_b64 %3, %4 offset:1536\n"
       "s_waitcnt lgkmcnt(0)\n"
       : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
       : "v"(a)
@@ -189,20 +187,30 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
   __shared__ int s_ids[SEL ? kWideSel : 1];
   __shared__ double s_freq[RD > 0 ? RD / 2 : 1];
 
+  preload_params(p);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = wave & 3, hb = wave >> 2;  // dim quarter, head block
   const int n = lane & 31, g = lane >> 5;
 
   const int S = p.splits;
-  const int split = (int)(blockIdx.x % (unsigned)S);
-  const unsigned bk = blockIdx.x / (unsigned)S;
+  // linear id -> (range, twin); twins of a range sit 8 ids apart (same XCD)
+  unsigned u = blockIdx.x, tw = 0;
+  if (p.wide_twins > 1) {
+    const unsigned rest = blockIdx.x >> 3;
+    tw = rest & 1u;
+    u = (rest >> 1) * 8 + (blockIdx.x & 7);
+  }
+  if (u >= (unsigned)(p.units / p.head_groups) * (unsigned)S) return;  // padding of the XCD mapping
+  const int split = (int)(u % (unsigned)S);
+  const unsigned bk = u / (unsigned)S;
   const int64_t kvh = bk % (unsigned)p.hkv;
   const int64_t b = bk / (unsigned)p.hkv;
-  const int64_t head0 = kvh * p.G + 32 * hb;  // first query head of this wave's block
+  const int hbg = (int)tw * HB + hb;            // head block of this wave within the KV head
+  const int64_t head0 = kvh * p.G + 32 * hbg;  // first query head of this wave's block
 
-  const int64_t t_pos = p.pos[b];                     // requested first, used after the first copies
-  const int64_t t_base = p.rpb ? p.rpb[b] : 0;
+  const int64_t t_pos = load_uniform(p.pos + b);  // requested first, used after the first copies
+  const int64_t t_base = p.rpb ? load_uniform(p.rpb + b) : 0;
   // query B operands (head n, dims 128q + 16ks + 8g ..); their addresses do
   // not depend on the position, so they load alongside it
   uint4 qb[WKST];
@@ -331,7 +339,7 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
   if (!sv.ok) {  // rows do not fit the buffers: NaN, written once
     vm_wait<0>();
     if (split == 0) {
-      const int64_t h0 = kvh * p.G;
+      const int64_t h0 = kvh * p.G + 32 * HB * (int)tw;
       for (int i = tid; i < 32 * HB * WD; i += 256 * HB) p.out[(b * p.hq + h0) * WD + i] = __builtin_nanf("");
       if (p.lse && tid < 32 * HB) p.lse[b * p.hq + h0 + tid] = __builtin_nanf("");
     }
@@ -418,29 +426,33 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[db][e] = 0.f;
 
-  // Per tile two barriers: A after the partial scores are written (it also
-  // ends every wave's reads of the previous tile, whose slot then receives the
-  // copy of tile + 2), and C after P and the row-slice maxima are written; each
-  // wave waits for its copies of the next tile before C, so C also publishes
-  // that tile.  P is computed against the running max; when a score exceeds it
-  // by more than 2^8 (the first tile, and rarely after), every wave takes the
-  // rescaling path, which recomputes P and adds one barrier.
+  // Software-pipelined tile loop.  Step `tile` reads from LDS and issues the
+  // score MFMAs of tile + 1, then the P.V MFMAs of tile, and writes tile + 1's
+  // partial scores; while the P.V MFMAs run: barrier A (the partials are
+  // visible, and every wave is past its reads of tile's ring slot, which then
+  // receives the copy of tile + 3), the softmax of tile + 1 (the four partials
+  // of its rows summed in a fixed order, P against the running max, P and the
+  // row-slice maxima to LDS), the wait for this wave's copies of tile + 2,
+  // barrier C (P visible, tile + 2 landed) and the rescale decision.  When a
+  // head's tile max exceeds its running max by more than 2^8 (the first tile,
+  // and rarely after), every wave rescales, recomputes P and adds a barrier.
+  // One buffer each for the partial scores, P and the maxima suffices: every
+  // write of them follows a barrier that follows every wave's last read of the
+  // previous contents.
   if (t0 < t1) {
     if (t0 + 1 < t1) vm_wait<NI>();
     else vm_wait<0>();
   }
   lds_barrier();  // the first tile landed
-  int slot = 0;
-#pragma unroll 1
-  for (int tile = t0; tile < t1; ++tile) {
-    const uint32_t sa = ring_a + (uint32_t)(slot * 4 * WQB);  // this wave's quarter tile (LDS address)
-    const bool raw = tile >= tiles_p;
-    const int v0 = raw ? (tile - tiles_p) * WTR : tile * WTR;
+
+  // Raw rows of `tile` (ring slot sl): RMSNorm over all 512 dims, RoPE on the
+  // last RD, in LDS, by head block 0's waves.  Every wave calls it (barriers).
+  auto treat_raw = [&](int tile, int sl) __attribute__((always_inline)) {
     if constexpr (TREAT) {
-      if (raw) {  // raw rows: RMSNorm over all 512 dims, RoPE on the last RD (head block 0's waves)
+      if (tile >= tiles_p) {
         // lane (n, g): row n, chunks c = g, g+2, ..., g+14 of quarter q (a
         // rotate-half partner chunk is RD/16 chunks on: same parity, same lane)
-        uint8_t* rowp = ring + slot * (4 * WQB) + q * WQB + n * (WQ * 2);
+        uint8_t* rowp = ring + sl * (4 * WQB) + q * WQB + n * (WQ * 2);
         if (hb == 0 && p.eps >= 0.f) {
           float ss = 0.f;
 #pragma unroll
@@ -457,7 +469,7 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
         if (hb == 0) {
           float inv = 1.f;
           if (p.eps >= 0.f) inv = 1.f / sqrtf((((ts[0][n] + ts[1][n]) + ts[2][n]) + ts[3][n]) / (float)WD + p.eps);
-          const double pos = (double)(sv.raw_begin + v0 + n);
+          const double pos = (double)(sv.raw_begin + (tile - tiles_p) * WTR + n);
           constexpr int RC0 = (WQ - RD) / 8;  // first rotated chunk of the last quarter
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
@@ -492,43 +504,64 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
         lds_barrier();  // treated rows visible to every wave
       }
     }
-    // valid rows of the tile (lane n: row n)
-    uint32_t mk = 0xffffffffu;
+  };
+  // Score MFMAs of the quarter tile at LDS address sa, two independent chains.
+  auto qk_issue = [&](uint32_t sa, f32x16& c0, f32x16& c1) __attribute__((always_inline)) {
+    uint4 ka[WKST];
+    uint32_t kad[WKST];
+#pragma unroll
+    for (int ks = 0; ks < WKST; ++ks) kad[ks] = sa + koff[ks];
+    wide_k_reads(ka, kad);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) c0[e] = c1[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < WKST; ks += 2) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[ks]),
+                                                   __builtin_bit_cast(bf16x8, qb[ks]), c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[ks + 1]),
+                                                   __builtin_bit_cast(bf16x8, qb[ks + 1]), c1, 0, 0, 0);
+    }
+  };
+  // O^T += V^T P^T for the quarter tile at sa, two 16-row blocks: P^T of block
+  // kb is this lane's P of rows j = 2kb, 2kb + 1 (from the waves that finished them).
+  auto pv = [&](uint32_t sa) __attribute__((always_inline)) {
+    uint2 pr[4];
+    s16x4 va[2][8];
+    uint32_t ta[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ta[k] = sa + toff[k];
+    wide_ptr_reads(pr, p_a, va, ta);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pr[2 * kb].x, pr[2 * kb].y, pr[2 * kb + 1].x, pr[2 * kb + 1].y));
+#pragma unroll
+      for (int db = 0; db < WDB; ++db) {
+        const s16x4 a0 = va[kb][2 * db], a1 = va[kb][2 * db + 1];
+        const bf16x8 a = __builtin_bit_cast(bf16x8, s16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
+      }
+    }
+  };
+  auto write_xs = [&](const f32x16& c0, const f32x16& c1) __attribute__((always_inline)) {
+    float* xw = xs[hb][q];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<float4*>(&xw[(j * 64 + lane) * 4]) =
+          make_float4(c0[4 * j] + c1[4 * j], c0[4 * j + 1] + c1[4 * j + 1], c0[4 * j + 2] + c1[4 * j + 2],
+                      c0[4 * j + 3] + c1[4 * j + 3]);
+  };
+  // Rows 8q + 4g + i (i < 4) of `tile`: the four partials summed in a fixed
+  // order, masked, scaled into the exponent's units; P against the running
+  // max to LDS, and this wave's row-slice max for the decision.
+  auto softmax = [&](int tile, float (&s4)[4], float (&pj)[4]) __attribute__((always_inline)) {
+    const bool raw = tile >= tiles_p;
+    const int v0 = raw ? (tile - tiles_p) * WTR : tile * WTR;
+    uint32_t mk = 0xffffffffu;  // valid rows of the tile (lane n: row n)
     if (!tile_full(raw, v0)) {
       int64_t row;
       const bool ok = locate(raw, v0 + n, row);
       mk = (uint32_t)(__ballot(ok) & 0xffffffffull);
     }
-    // partial scores over this wave's dims: S^T[row, head], rows 8j + 4g + i
-    f32x16 sc;
-    {
-      uint4 ka[WKST];
-      uint32_t kad[WKST];
-#pragma unroll
-      for (int ks = 0; ks < WKST; ++ks) kad[ks] = sa + koff[ks];
-      wide_k_reads(ka, kad);
-      f32x16 s2;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sc[e] = s2[e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < WKST; ks += 2) {  // two independent chains
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[ks]),
-                                                     __builtin_bit_cast(bf16x8, qb[ks]), sc, 0, 0, 0);
-        s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[ks + 1]),
-                                                     __builtin_bit_cast(bf16x8, qb[ks + 1]), s2, 0, 0, 0);
-      }
-      sc += s2;
-    }
-    float* xw = xs[hb][q];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<float4*>(&xw[(j * 64 + lane) * 4]) =
-          make_float4(sc[4 * j], sc[4 * j + 1], sc[4 * j + 2], sc[4 * j + 3]);
-    lds_barrier();  // A
-    if (tile + 2 < t1) issue(tile + 2, slot == 0 ? 2 : slot - 1);
-    // Rows 8q + 4g + i (i < 4) are finished here: the four partials summed in a
-    // fixed order, masked, scaled into the exponent's units.
-    float s4[4];
     {
       float4 xr[4];
       wide_x4_reads(xr, xs_a);
@@ -545,25 +578,16 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
       for (int e = 0; e < 4; ++e)
         if (!((mk >> (8 * q + 4 * g + e)) & 1u)) s4[e] = kNegInf;
     }
-    // P against the running max; this wave's row-slice max for the check
-    float pj[4];
-    {
-      const float mu = m_run == kNegInf ? 0.f : m_run;
+    const float mu = m_run == kNegInf ? 0.f : m_run;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pj[e] = fast_exp2(s4[e] - mu);
-    }
+    for (int e = 0; e < 4; ++e) pj[e] = fast_exp2(s4[e] - mu);
     s_p[hb][q][lane] = make_uint2(pack_bf16x2(pj[0], pj[1]), pack_bf16x2(pj[2], pj[3]));
-    {
-      const float lm = xor32_max(fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3])));
-      if (g == 0) s_mx[hb][q][n] = lm;
-    }
-    if (tile + 1 < t1) {  // this wave's copies of the next tile landed
-      if (tile + 2 < t1) vm_wait<NI>();
-      else vm_wait<0>();
-    }
-    lds_barrier();  // C
-    // tile max of head n in both head blocks; every wave tracks both running
-    // maxima, so the rescale decision is the same in all waves
+    const float lm = xor32_max(fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3])));
+    if (g == 0) s_mx[hb][q][n] = lm;
+  };
+  // After barrier C: the tile max of head n in both head blocks (every wave
+  // tracks both running maxima, so the decision is the same in all waves).
+  auto decide = [&](const float (&s4)[4], float (&pj)[4]) __attribute__((always_inline)) {
     const float tm = fmaxf(fmaxf(s_mx[hb][0][n], s_mx[hb][1][n]), fmaxf(s_mx[hb][2][n], s_mx[hb][3][n]));
     float tm_o = kNegInf;
     if constexpr (HB > 1)
@@ -583,33 +607,49 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
       lds_barrier();  // nobody has read the first P yet
     }
     l_run += (pj[0] + pj[1]) + (pj[2] + pj[3]);
-    uint2 pr[4];  // P of rows j = 0..3 (this lane's g half)
-    wide_p_reads(pr, p_a);
-    uint32_t pw[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      pw[2 * j] = pr[j].x;
-      pw[2 * j + 1] = pr[j].y;
+  };
+
+  const auto slot_addr = [&](int sl) { return ring_a + (uint32_t)(sl * 4 * WQB); };  // this wave's quarter
+  float s4[4], pj[4];
+  if (t0 < t1) {  // prologue: scores and P of the first tile
+    treat_raw(t0, 0);
+    f32x16 c0, c1;
+    qk_issue(slot_addr(0), c0, c1);
+    write_xs(c0, c1);
+    lds_barrier();  // A
+    if (t0 + 2 < t1) issue(t0 + 2, 2);
+    softmax(t0, s4, pj);
+    if (t0 + 1 < t1) {  // this wave's copies of t0 + 1 landed
+      if (t0 + 2 < t1) vm_wait<NI>();
+      else vm_wait<0>();
     }
-    // O^T += V^T P^T, two 16-row blocks: P^T of block kb is this lane's rows of j = 2kb, 2kb+1
-    {
-      s16x4 va[2][8];
-      uint32_t ta[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) ta[k] = sa + toff[k];
-      wide_tr_reads(va, ta);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pw[4 * kb], pw[4 * kb + 1], pw[4 * kb + 2], pw[4 * kb + 3]));
-#pragma unroll
-        for (int db = 0; db < WDB; ++db) {
-          const s16x4 a0 = va[kb][2 * db], a1 = va[kb][2 * db + 1];
-          const bf16x8 a = __builtin_bit_cast(bf16x8, s16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
-        }
+    lds_barrier();  // C
+    decide(s4, pj);
+  }
+  int slot = 0;  // ring slot of `tile`
+#pragma unroll 1
+  for (int tile = t0; tile < t1; ++tile) {
+    const int nslot = slot == WSLOTS - 1 ? 0 : slot + 1;
+    const bool more = tile + 1 < t1;
+    f32x16 c0, c1;
+    if (more) {
+      treat_raw(tile + 1, nslot);
+      qk_issue(slot_addr(nslot), c0, c1);
+    }
+    pv(slot_addr(slot));
+    if (more) {
+      write_xs(c0, c1);
+      lds_barrier();  // A
+      if (tile + 3 < t1) issue(tile + 3, slot);
+      softmax(tile + 1, s4, pj);
+      if (tile + 2 < t1) {  // this wave's copies of tile + 2 landed
+        if (tile + 3 < t1) vm_wait<NI>();
+        else vm_wait<0>();
       }
+      lds_barrier();  // C
+      decide(s4, pj);
     }
-    slot = slot == WSLOTS - 1 ? 0 : slot + 1;
+    slot = nslot;
   }
   const float M = m_run;
   float L;
@@ -653,16 +693,19 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
     if (p.lse && q == 0 && g == 0) p.lse[b * p.hq + head] = (M + log2f(L)) * 0.69314718055994531f;
     return;
   }
-  // split partial in the 16-head-unit layout: unit (b, kvh, 16-head group), part = unit * S + split
-  const int64_t unit = (b * p.hkv + kvh) * p.head_groups + 2 * hb + (n >> 4);
+  // split partial in the 16-head-unit layout: unit (b, kvh, 16-head group), part = unit * S + split;
+  // this split's own normalised output in bf16 (zero where no row of the range is visible)
+  const int64_t unit = (b * p.hkv + kvh) * p.head_groups + 2 * hbg + (n >> 4);
   const int64_t part = unit * S + split;
-  float* o = p.ws_acc + (part * 16 + (n & 15)) * WD + WQ * q + 4 * g;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  bf16_t* o = p.ws_o + (part * 16 + (n & 15)) * WD + WQ * q + 4 * g;
 #pragma unroll
   for (int db = 0; db < WDB; ++db)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<float4*>(o + 32 * db + 8 * j) =
-          make_float4(acc[db][4 * j], acc[db][4 * j + 1], acc[db][4 * j + 2], acc[db][4 * j + 3]);
+      *reinterpret_cast<uint2*>(o + 32 * db + 8 * j) =
+          make_uint2(pack_bf16x2(acc[db][4 * j] * inv, acc[db][4 * j + 1] * inv),
+                     pack_bf16x2(acc[db][4 * j + 2] * inv, acc[db][4 * j + 3] * inv));
   if (q == 0 && g == 0) {
     p.ws_ml[(part * 16 + (n & 15)) * 2] = M;
     p.ws_ml[(part * 16 + (n & 15)) * 2 + 1] = L;
@@ -671,8 +714,8 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
 
 hipError_t launch_decode_wide(const DecodeParams& p, int rope_dims, bool treat, int head_blocks,
                               hipStream_t stream) {
-  const unsigned seqs = (unsigned)(p.units / (2 * head_blocks));  // sequences x KV heads
-  const dim3 grid(seqs * (unsigned)p.splits);
+  const unsigned pairs = (unsigned)(p.units / p.head_groups) * (unsigned)p.splits;  // (sequence, KV head, split)
+  const dim3 grid(p.wide_twins > 1 ? (pairs + 7) / 8 * 8 * (unsigned)p.wide_twins : pairs);
   const bool sel = p.sel != nullptr;
   auto go = [&](auto kern, int hb) {
     kern<<<grid, 256 * hb, 0, stream>>>(p);

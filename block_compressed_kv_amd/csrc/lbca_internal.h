@@ -15,7 +15,8 @@ struct DecodePlan {
   int head_groups;   // ceil(G / 16): 16-head groups per KV head (MFMA path)
   int splits;        // workgroups along the row list of one (sequence, KV head, head group)
   int dim_splits;    // twin workgroups per (unit, split), each owning 1/dim_splits of the dims
-  int wide_blocks;   // > 0: wide-row MQA kernel with this many 32-head blocks per KV head
+  int wide_blocks;   // > 0: wide-row MQA kernel with this many 32-head blocks per workgroup
+  int wide_twins;    // wide-row workgroups per (sequence, KV head, split)
   size_t ws_bytes;   // split partials (acc, max, sum); 0 with one split
 };
 DecodePlan plan_decode(const lbca_decode_args& a);
