@@ -367,8 +367,9 @@ def run_csa(reps):
             sc=torch.empty((B, k), dtype=torch.float32, device=dev),
             out=torch.empty((B, X_HQ, X_D), device=dev), lse=torch.empty((B, X_HQ), device=dev)))
     kw = dict(raw_pos_base=rpb, sink=sink, **treat)
-    ws_i = torch.empty(B * N * 4, dtype=torch.uint8, device=dev)
     x = inst[0]
+    ws_i = torch.empty(lbca.index_workspace_bytes(x["qi"], x["w"], x["keys"], pos, m, k), dtype=torch.uint8,
+                       device=dev)
     nws = lbca.decode_workspace_bytes(x["q"], x["ent"], x["raw"], pos, m, W, OVER, sel_idx=x["idx"], **kw)
     ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
 

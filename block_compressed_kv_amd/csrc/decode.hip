@@ -240,17 +240,19 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
   const int64_t head0 = kvh * p.G + slot0;  // first query head of the unit
   const bool head_ok = n < nvalid;
 
-  // the position first (scalar loads: waiting for them does not wait for the rows)
-  const int64_t t_pos = load_uniform(p.pos + b);
-  const int64_t t_base = p.rpb ? load_uniform(p.rpb + b) : 0;
-  // queries of this head group as B operands (zero for padded heads); their
-  // addresses do not depend on the position, so they load alongside it
+  // the position first: it is waited for after the first rows are requested
+  const EarlyI64 e_pos = load_early(p.pos + b);
+  const EarlyI64 e_base = load_early(p.rpb ? p.rpb + b : p.pos + b);
+  // queries of this head group as B operands; their addresses do not depend
+  // on the position, so they load alongside it.  Padded head slots load head
+  // 0's row: a lane's scores, softmax state and output column belong to its
+  // own head, and padded heads are never written.  (Loads without a branch
+  // keep the count of loads after the position exact for the wait on it.)
   uint4 qr[KS];
   {
-    const bf16_t* qrow = p.q + (b * p.hq + head0 + n) * D + 8 * kq;
+    const bf16_t* qrow = p.q + (b * p.hq + head0 + (head_ok ? n : 0)) * D + 8 * kq;
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qr[s] = head_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s) : make_uint4(0, 0, 0, 0);
+    for (int s = 0; s < KS; ++s) qr[s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
   }
   // Addresses of this (sequence, KV head) slice (none depends on the position).
   Slices sl;
@@ -275,7 +277,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
   if constexpr (SPEC) {
 #pragma unroll
     for (int i = 0; i < TMAX; ++i) {
-      if ((wave + i * NW) * R >= p.entries) break;  // no buffer rows left
+      // no buffer rows left (the first tile is always requested, reading the
+      // stand-in row past the buffer, so every path has the same loads)
+      if (i > 0 && (wave + i * NW) * R >= p.entries) break;
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
         const int e = (wave + i * NW) * R + 16 * h + n;
@@ -292,7 +296,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
       }
     }
   }
-  const SeqView sv = seq_view(p, b, t_pos, t_base);
+  const SeqView sv = seq_view(p, b, uniform_value(e_pos), p.rpb ? uniform_value(e_base) : 0);
   if (!sv.ok) {  // rows do not fit the buffers: NaN, written once per unit and slice
     if (split == 0) {
       for (int i = tid; i < nvalid * DV; i += blockDim.x)

@@ -41,13 +41,26 @@ __device__ __forceinline__ void preload_params(const DecodeParams& p) {
                "s"(p.mode), "s"(p.splits), "s"(p.head_groups), "s"(p.units), "s"(p.wide_twins));
 }
 
-// A uniform value the kernel only reads (positions, raw bases), loaded through
-// the scalar cache straight into scalar registers.  A vector load of it would
-// be moved to scalar registers right after issue, which waits for every
-// vector load before it; this one is waited for on its own counter, so row
-// loads issued after it stay in flight.
-__device__ __forceinline__ int64_t load_uniform(const int64_t* ptr) {
-  return *reinterpret_cast<const __attribute__((address_space(4))) int64_t*>(reinterpret_cast<uintptr_t>(ptr));
+// A uniform value (a position, a raw base) requested before the row loads
+// and used after them.  A plain load of it is taken as uniform and moved to
+// scalar registers right after issue, which waits for it at once; a load
+// through the scalar cache queues behind the row traffic and arrives late.
+// Here the load goes out first as a vector load whose address the compiler
+// takes as per-lane (an opaque zero), so nothing waits for it until
+// uniform_value(), placed after the row loads, reads lane 0 (vector loads
+// return in order, so that wait covers this load only).
+struct EarlyI64 {
+  int64_t v;
+};
+__device__ __forceinline__ EarlyI64 load_early(const int64_t* ptr) {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return EarlyI64{ptr[z]};
+}
+__device__ __forceinline__ int64_t uniform_value(EarlyI64 e) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)e.v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)e.v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 struct SeqView {
@@ -73,7 +86,7 @@ __device__ __forceinline__ SeqView seq_view(const DecodeParams& p, int64_t b, in
   return v;
 }
 __device__ __forceinline__ SeqView seq_view(const DecodeParams& p, int64_t b) {
-  return seq_view(p, b, load_uniform(p.pos + b), p.rpb ? load_uniform(p.rpb + b) : 0);
+  return seq_view(p, b, p.pos[b], p.rpb ? p.rpb[b] : 0);
 }
 
 // Wide-row MQA decode (512 dims, shared series, query heads in blocks of 32

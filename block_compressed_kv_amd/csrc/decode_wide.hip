@@ -209,8 +209,8 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
   const int hbg = (int)tw * HB + hb;            // head block of this wave within the KV head
   const int64_t head0 = kvh * p.G + 32 * hbg;  // first query head of this wave's block
 
-  const int64_t t_pos = load_uniform(p.pos + b);  // requested first, used after the first copies
-  const int64_t t_base = p.rpb ? load_uniform(p.rpb + b) : 0;
+  const EarlyI64 e_pos = load_early(p.pos + b);  // requested first, used after the first copies
+  const EarlyI64 e_base = load_early(p.rpb ? p.rpb + b : p.pos + b);
   // query B operands (head n, dims 128q + 16ks + 8g ..); their addresses do
   // not depend on the position, so they load alongside it
   uint4 qb[WKST];
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
   if constexpr (RD > 0) {  // RoPE turns per position (published by the barrier below)
     if (tid < RD / 2) s_freq[tid] = rope_turns_per_pos(tid, RD, p.log2_base);
   }
-  sv = seq_view(p, b, t_pos, t_base);
+  sv = seq_view(p, b, uniform_value(e_pos), p.rpb ? uniform_value(e_base) : 0);
   if (!sv.ok) {  // rows do not fit the buffers: NaN, written once
     vm_wait<0>();
     if (split == 0) {

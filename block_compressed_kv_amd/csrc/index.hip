@@ -30,7 +30,11 @@ struct IndexParams {
   int32_t* out_idx;
   float* out_score;
   float* scores;  // [B][stride]
+  uint32_t* cand_key;  // two-stage selection: [B][slices * k] order keys of the slices' top-k
+  int32_t* cand_id;    // [B][slices * k] their entry ids (-1: padding)
   int64_t heads, entries, k, m, stride;  // stride: entries rounded up to 4 (16-byte rows)
+  int slices;                            // two-stage selection: slices of kSliceLen entries
+  int64_t cstride;                       // candidates per sequence, rounded up to 4
 };
 
 __device__ __forceinline__ int64_t n_visible(const IndexParams& p, int64_t b) {
@@ -115,7 +119,27 @@ __device__ __forceinline__ int wave_crossing(int v, int target, int before, int*
   return L;
 }
 
-// One workgroup per sequence; every thread keeps KPT scores (as order-preserving
+// Key back to the score it was made from (order_key is a bijection on floats
+// other than -0).
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Entries per slice of the two-stage selection (1024 threads x 4 keys).
+constexpr int kSliceLen = 4096;
+
+// MODE 0: one workgroup per sequence over all its visible scores.
+// MODE 1 (first stage of two): workgroup (slice, sequence) over the visible
+// scores of entries [slice * kSliceLen, +kSliceLen); it writes the slice's
+// top-k as (order key, entry id) candidates in index order, padded with
+// (0, -1) when the slice has at most k visible entries.  The top-k of the
+// whole sequence is among the slices' top-k (each of its members is in the
+// top-k of its own slice under the same order and tie rule).
+// MODE 2 (second stage): one workgroup per sequence over the slices *
+// k candidates; candidate order is index order, so the same tie rule (lower
+// index first) is the lower candidate position, and padding (key 0, below
+// every finite score's key) is never chosen.
+// Every thread keeps KPT scores (as order-preserving
 // 32-bit keys) of entries r * 1024 + tid in registers.  The k-th largest key is
 // found by a radix select over 12 + 10 + 10 bits: each pass counts the keys
 // that still match the digits chosen so far into an LDS histogram, and a
@@ -123,8 +147,9 @@ __device__ __forceinline__ int wave_crossing(int v, int target, int before, int*
 // The selection then takes every key above it and the lowest-index keys equal
 // to it: each element's output slot is the number of selected elements before
 // it in index order, from per-(round, wave) counts scanned across the block.
-template <int KPT>
+template <int KPT, int MODE>
 __global__ __launch_bounds__(1024) void topk_kernel(IndexParams p) {
+  static_assert(MODE != 1 || KPT * 1024 == kSliceLen, "a first-stage workgroup holds one slice");
   // LDS: first the scores (copied straight from global memory), then the
   // histograms (4 interleaved copies per bin, so lanes of one wave that hit
   // the same bin mostly hit different words)
@@ -137,18 +162,59 @@ __global__ __launch_bounds__(1024) void topk_kernel(IndexParams p) {
   __shared__ int s_nc;
   __shared__ int s_pick[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t b = blockIdx.x;
-  const int nv = (int)n_visible(p, b);
+  const int64_t b = MODE == 1 ? blockIdx.y : blockIdx.x;
+  const int nvis = (int)n_visible(p, b);
   const int K = (int)p.k;
-  const float* sc = p.scores + b * p.stride;
+  const int base = MODE == 1 ? (int)blockIdx.x * kSliceLen : 0;  // entry id of item 0
+  // items of this workgroup: visible scores (MODE 0), the slice's visible
+  // scores (MODE 1), or every candidate slot (MODE 2)
+  const int nv = MODE == 0 ? nvis
+               : MODE == 1 ? (nvis - base < 0 ? 0 : (nvis - base < kSliceLen ? nvis - base : kSliceLen))
+                           : p.slices * K;
+  const float* sc = p.scores + b * p.stride + base;
+  const uint32_t* ck = p.cand_key + b * p.cstride;
+  const int32_t* cid = p.cand_id + b * p.cstride;
   int32_t* oi = p.out_idx + b * K;
   float* os = p.out_score ? p.out_score + b * K : nullptr;
+  const int64_t wofs = b * p.cstride + (int64_t)(MODE == 1 ? (int)blockIdx.x : 0) * K;  // MODE 1 output
+  uint32_t* wk = p.cand_key + wofs;
+  int32_t* wi = p.cand_id + wofs;
 
-  if (nv <= K) {
+  if constexpr (MODE == 2) {
+    // real candidates: min(k, visible entries of the slice) at the head of each slice's block
+    int n_real = 0;
+    for (int q = 0; q < p.slices; ++q) {
+      const int c = nvis - q * kSliceLen;
+      n_real += c <= 0 ? 0 : (c < K ? c : K);
+    }
+    if (n_real <= K) {  // all of them, in order, then padding
+      for (int i = tid; i < K; i += blockDim.x) {
+        int q = 0, at = i, id = -1;
+        uint32_t key = 0;
+        for (; q < p.slices; ++q) {
+          const int c0 = nvis - q * kSliceLen, c = c0 <= 0 ? 0 : (c0 < K ? c0 : K);
+          if (at < c) {
+            id = cid[q * K + at];
+            key = ck[q * K + at];
+            break;
+          }
+          at -= c;
+        }
+        oi[i] = id;
+        if (os) os[i] = id >= 0 ? key_score(key) : __builtin_nanf("");
+      }
+      return;
+    }
+  } else if (nv <= K) {
     for (int i = tid; i < K; i += blockDim.x) {
       const bool in = i < nv;
-      oi[i] = in ? (int32_t)i : -1;
-      if (os) os[i] = in ? sc[i] : __builtin_nanf("");
+      if constexpr (MODE == 0) {
+        oi[i] = in ? (int32_t)i : -1;
+        if (os) os[i] = in ? sc[i] : __builtin_nanf("");
+      } else {
+        wk[i] = in ? order_key(sc[i]) : 0u;
+        wi[i] = in ? (int32_t)(base + i) : -1;
+      }
     }
     return;
   }
@@ -157,27 +223,29 @@ __global__ __launch_bounds__(1024) void topk_kernel(IndexParams p) {
   if constexpr (STAGE > 0) {
     // 16-byte copies of the visible scores to LDS (lane i of a wave writes
     // bytes 16 i of the wave's 1 KB), the last nv % 4 scores one by one
+    // (MODE 2: the candidates' keys, 4 bytes each as well)
     const int nc = nv >> 2;
-    float* stage = reinterpret_cast<float*>(lds_words);
+    uint32_t* stage = reinterpret_cast<uint32_t*>(lds_words);
+    const uint32_t* src = MODE == 2 ? ck : reinterpret_cast<const uint32_t*>(sc);
     for (int c0 = wave * 64; c0 < nc; c0 += 1024) {
       if (c0 + lane < nc)
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(reinterpret_cast<uintptr_t>(sc + 4 * (c0 + lane))),
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(reinterpret_cast<uintptr_t>(src + 4 * (c0 + lane))),
                                          (lds_void*)(stage + 4 * c0), 16, 0, 0);
     }
-    if (tid < nv - 4 * nc) stage[4 * nc + tid] = sc[4 * nc + tid];
+    if (tid < nv - 4 * nc) stage[4 * nc + tid] = src[4 * nc + tid];
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies landed
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int i = r * 1024 + tid;
-      key[r] = i < nv ? order_key(stage[i]) : 0u;
+      key[r] = i < nv ? (MODE == 2 ? stage[i] : order_key(__uint_as_float(stage[i]))) : 0u;
     }
     __syncthreads();  // the LDS becomes the histogram
   } else {
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int i = r * 1024 + tid;
-      key[r] = i < nv ? order_key(sc[i]) : 0u;
+      key[r] = i < nv ? (MODE == 2 ? ck[i] : order_key(sc[i])) : 0u;
     }
   }
 
@@ -312,14 +380,34 @@ __global__ __launch_bounds__(1024) void topk_kernel(IndexParams p) {
     if (gt) slot = gb + (eb < need_eq ? eb : need_eq);
     else if (eq && eb < need_eq) slot = gb + eb;
     if (slot >= 0) {
-      oi[slot] = (int32_t)i;
-      if (os) os[slot] = sc[i];
+      if constexpr (MODE == 0) {
+        oi[slot] = (int32_t)i;
+        if (os) os[slot] = sc[i];
+      } else if constexpr (MODE == 1) {
+        wk[slot] = key[r];
+        wi[slot] = (int32_t)(base + i);
+      } else {
+        oi[slot] = cid[i];
+        if (os) os[slot] = key_score(key[r]);
+      }
     }
   }
 }
 
+// Two-stage selection when the entries span at least 3 slices and each slice
+// keeps at most a quarter of its entries; the second stage holds every
+// candidate in registers (at most 16 per thread).
+static int select_slices(const csa_index_args& a) {
+  const int64_t P = (a.entries + kSliceLen - 1) / kSliceLen;
+  if (P < 3 || a.k * 4 > kSliceLen || P * a.k > 16 * 1024) return 0;
+  return (int)P;
+}
+
 size_t index_workspace_bytes(const csa_index_args& a) {
-  return (size_t)a.batch * (size_t)((a.entries + 3) & ~int64_t(3)) * sizeof(float);
+  size_t bytes = (size_t)a.batch * (size_t)((a.entries + 3) & ~int64_t(3)) * sizeof(float);
+  const int P = select_slices(a);
+  if (P > 0) bytes += (size_t)a.batch * (size_t)((P * a.k + 3) & ~int64_t(3)) * (sizeof(uint32_t) + sizeof(int32_t));
+  return bytes;
 }
 
 hipError_t launch_index_topk(const csa_index_args& a, void* ws, hipStream_t stream) {
@@ -333,6 +421,12 @@ hipError_t launch_index_topk(const csa_index_args& a, void* ws, hipStream_t stre
   p.scores = static_cast<float*>(ws);
   p.heads = a.heads; p.entries = a.entries; p.k = a.k; p.m = a.block;
   p.stride = (a.entries + 3) & ~int64_t(3);
+  p.slices = select_slices(a);
+  if (p.slices > 0) {
+    p.cstride = (p.slices * a.k + 3) & ~int64_t(3);
+    p.cand_key = reinterpret_cast<uint32_t*>(p.scores + a.batch * p.stride);
+    p.cand_id = reinterpret_cast<int32_t*>(p.cand_key + a.batch * p.cstride);
+  }
   if (a.entries > 0) {
     const dim3 grid((unsigned)((a.entries + 255) / 256), (unsigned)a.batch);
     switch (a.dim) {
@@ -345,10 +439,20 @@ hipError_t launch_index_topk(const csa_index_args& a, void* ws, hipStream_t stre
     if (e != hipSuccess) return e;
   }
   const dim3 g((unsigned)a.batch);
-  if (a.entries <= 4096) topk_kernel<4><<<g, 1024, 0, stream>>>(p);
-  else if (a.entries <= 16384) topk_kernel<16><<<g, 1024, 0, stream>>>(p);
-  else if (a.entries <= 32768) topk_kernel<32><<<g, 1024, 0, stream>>>(p);
-  else topk_kernel<64><<<g, 1024, 0, stream>>>(p);
+  if (p.slices > 0) {
+    topk_kernel<4, 1><<<dim3((unsigned)p.slices, (unsigned)a.batch), 1024, 0, stream>>>(p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nc = p.slices * a.k;
+    if (nc <= 4096) topk_kernel<4, 2><<<g, 1024, 0, stream>>>(p);
+    else if (nc <= 8192) topk_kernel<8, 2><<<g, 1024, 0, stream>>>(p);
+    else topk_kernel<16, 2><<<g, 1024, 0, stream>>>(p);
+    return hipGetLastError();
+  }
+  if (a.entries <= 4096) topk_kernel<4, 0><<<g, 1024, 0, stream>>>(p);
+  else if (a.entries <= 16384) topk_kernel<16, 0><<<g, 1024, 0, stream>>>(p);
+  else if (a.entries <= 32768) topk_kernel<32, 0><<<g, 1024, 0, stream>>>(p);
+  else topk_kernel<64, 0><<<g, 1024, 0, stream>>>(p);
   return hipGetLastError();
 }
 

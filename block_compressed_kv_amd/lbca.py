@@ -233,6 +233,17 @@ def attend_prefill(q, q_pos0, pooled_k, raw_k, raw_pos_base, block, window, mode
     return out, lse
 
 
+def index_workspace_bytes(q_idx, head_w, keys, pos, block, k):
+    """csa_index_topk_workspace: bytes of workspace csa_index_topk needs for these shapes
+    (the query's buffer stands in for the output, which the size does not depend on)."""
+    B, HI, dI = q_idx.shape
+    a = IndexArgs(_p(q_idx), _p(head_w), _p(keys), _p(pos), _p(q_idx), None,
+                  B, HI, dI, keys.shape[1], k, block, _dt(q_idx))
+    need = ctypes.c_size_t()
+    _check(lib().csa_index_topk_workspace(ctypes.byref(a), ctypes.byref(need)), "csa_index_topk_workspace")
+    return need.value
+
+
 def csa_index_topk(q_idx, head_w, keys, pos, block, k, out_idx=None, out_score=None,
                    workspace=None, stream=None):
     """csa_index_topk: q_idx [B,HI,dI], head_w [B,HI], keys [B,N,dI]; returns (idx, score)."""

@@ -255,7 +255,12 @@ LBCA_API int lbca_attend_prefill(const lbca_prefill_args* a, void* stream);
  *   keys  [batch, entries, dim] dtype;  pos [batch] int64 (device)
  *   out_idx [batch, k] int32;  out_score [batch, k] float32 or NULL
  * Supported: dtype BF16; dim in {32, 64, 128}; heads <= 16;
- * 1 <= k <= 2048; entries <= 65536.  Workspace: csa_index_topk_workspace.
+ * 1 <= k <= 2048; entries <= 65536.  Workspace (csa_index_topk_workspace,
+ * 16-byte aligned, caller-owned, contents need no initialisation): the fp32
+ * scores, batch x entries rounded up to 4; plus, when the selection runs in
+ * two stages (entries span P = ceil(entries / 4096) >= 3 slices of 4096,
+ * 4 k <= 4096 and P k <= 16384), batch x (P k rounded up to 4) candidate
+ * (key, id) pairs of 8 bytes.
  * Sequences with t < 0 get an all -1 row.
  */
 typedef struct csa_index_args {

@@ -201,9 +201,15 @@ def test_index_validation(kw, code):
 
 @fake_ptr
 def test_index_workspace_required():
+    # 32768 entries: 8 slices of 4096, k = 512 -> two stages: scores plus 8 x 512 (key, id) pairs
     st, st2, need = _index()
-    assert st == 0 and need == 2 * 32768 * 4
+    assert st == 0 and need == 2 * 32768 * 4 + 2 * 8 * 512 * 8
     assert st2 == lbca.ERR_WORKSPACE
+    # one stage: too few slices, or k above a quarter of a slice
+    assert _index(entries=8192)[2] == 2 * 8192 * 4
+    assert _index(entries=8193)[2] == 2 * 8196 * 4 + 2 * 3 * 512 * 8
+    assert _index(k=1025)[2] == 2 * 32768 * 4
+    assert _index(entries=32768, k=3)[2] == 2 * 32768 * 4 + 2 * 24 * 8
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

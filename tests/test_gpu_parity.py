@@ -379,8 +379,14 @@ def test_prefill_overlap_shared_sink(lib):
 # ---------------------------------------------------------------------------
 # indexer + top-k
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("N,k,t_list", [(2000, 64, [7999, 3001]), (700, 512, [2799, 100]),
-                                        (5000, 2048, [19999, 19999])])
+@pytest.mark.parametrize("N,k,t_list", [
+    (2000, 64, [7999, 3001]), (700, 512, [2799, 100]), (5000, 2048, [19999, 19999]),
+    # two-stage selection (slices of 4096): 5 slices with a ragged last one, 3 visible
+    # slices, one slice holding more than k, fewer visible than k
+    (20000, 300, [79999, 35999, 2399, 999]),
+    # k at a quarter of a slice; the 4th slice empty or holding a single entry
+    (12289, 1024, [49155, 49159]),
+])
 def test_index_topk(lib, N, k, t_list):
     B, HI, dI, m = len(t_list), 8, 64, 4
     g = lambda n, shape: synth.normal(shape, synth.seed_of("idx", N, n), dtype="bf16", device=DEV)
@@ -397,6 +403,28 @@ def test_index_topk(lib, N, k, t_list):
         sel = idx[b][idx[b] >= 0]
         np.testing.assert_allclose(score[b][:sel.size], s[sel], rtol=1e-5, atol=1e-5)
         assert np.isnan(score[b][sel.size:]).all()
+
+
+def test_topk_two_stage_ties_across_slices(lib):
+    # exact small-integer scores: 300 nines spread over every slice, eights every 20th
+    # entry from 3000 on (55 of them in slice 0), ones elsewhere; the top 500 are the
+    # nines plus the 200 lowest-index eights, which straddle the slice 0 / 1 boundary
+    B, HI, dI, N, m, k = 1, 1, 32, 16384, 1, 500
+    vals = np.ones(N)
+    vals[3000::20] = 8
+    rng = np.random.default_rng(synth.seed_of("ties-two-stage") % (1 << 32))
+    vals[rng.choice(N, 300, replace=False)] = 9
+    qi = torch.zeros((B, HI, dI), dtype=torch.bfloat16, device=DEV)
+    qi[0, 0, 0] = 1.0
+    keys = torch.zeros((B, N, dI), dtype=torch.bfloat16, device=DEV)
+    keys[0, :, 0] = torch.tensor(vals, dtype=torch.bfloat16)
+    w = torch.ones((B, HI), device=DEV)
+    idx, score = lib.csa_index_topk(qi, w, keys, torch.tensor([N - 1], device=DEV), m, k)
+    ref = O.topk_select(vals.astype(np.float64), k)
+    got = idx[0].cpu().numpy()
+    assert list(got) == list(ref)
+    assert (np.sort(vals)[::-1][:k] == np.sort(vals[got])[::-1]).all()
+    np.testing.assert_array_equal(score[0].cpu().numpy(), vals[got].astype(np.float32))
 
 
 def test_topk_ties_and_zero_scores(lib):
