@@ -19,7 +19,11 @@ from stored counter passes), the oracle on the host cores (cpu_baseline), batch
 every 64 steps), pooling GB/s for the whole history, chunked prefill (16K
 context in 2048-token chunks) TFLOP/s, HCA decode at 1M context (batch 4, 64
 query heads x 512, pooling GB/s of the whole history) and CSA at 128K (batch 2:
-indexer scores + top-512, decode over the selection, dual pooling GB/s).
+indexer scores + top-512, decode over the selection, dual pooling GB/s); the
+measured ceilings of the part (streaming read, one launch reading the decode's
+bytes, a bf16 MFMA loop, the empty-kernel launch floor) with each kernel's
+fraction of them; and the oracle timed beside prefill, HCA and CSA on bounded
+samples.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
     python bench.py --counters    # only what the FETCH_SIZE / WRITE_SIZE passes profile
@@ -401,6 +405,54 @@ def run_csa(reps):
 
 
 # ---------------------------------------------------------------------------
+# measured ceilings of this part (probe kernels in libceilings.so)
+# ---------------------------------------------------------------------------
+def run_ceilings():
+    """Streaming HBM read (1 GiB), one launch reading the batch-16 decode's bytes
+    (14 distinct buffers in a graph, like the decode step), a bf16 MFMA loop and
+    the empty-kernel launch floor."""
+    import ctypes
+
+    from block_compressed_kv_amd import build as B
+    if not os.path.exists(B.CEIL_LIB):
+        raise RuntimeError(f"{B.CEIL_LIB} is missing: build it with `python -m block_compressed_kv_amd.build`")
+    L = ctypes.CDLL(B.CEIL_LIB)
+    L.ceil_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.ceil_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.ceil_empty.argtypes = [ctypes.c_void_p]
+    stream = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def ok(r):
+        if r != 0:
+            raise RuntimeError(f"ceiling probe failed (hip error {r})")
+
+    res = {}
+    grid = 2048
+    out = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+    big = torch.zeros(1 << 30, dtype=torch.uint8, device="cuda")
+    g = capture(lambda: ok(L.ceil_read(big.data_ptr(), big.numel(), out.data_ptr(), grid, stream())))
+    res["hbm_read_GBps"] = big.numel() / (time_graph(g, 20) * 1e-3) / 1e9
+    del big, g
+    nb = decode_bytes_per_seq_layer() * 16
+    bufs = [torch.zeros(nb, dtype=torch.uint8, device="cuda") for _ in range(LAYERS)]
+    for grid_dec in (256, 1024):
+        g = capture(lambda: [ok(L.ceil_read(b.data_ptr(), nb, out.data_ptr(), grid_dec, stream())) for b in bufs])
+        res[f"read_decode_bytes_one_launch_us_grid{grid_dec}"] = time_graph(g, 50) * 1e3 / LAYERS
+    del bufs, g
+    mg, iters = 1024, 4096
+    mo = torch.empty(mg * 256, dtype=torch.float32, device="cuda")
+    g = capture(lambda: ok(L.ceil_mfma(mo.data_ptr(), mg, iters, stream())))
+    res["mfma_bf16_TFLOPs"] = mg * 4 * iters * 4 * 32768 / (time_graph(g, 5) * 1e-3) / 1e12
+    g = capture(lambda: [ok(L.ceil_empty(stream())) for _ in range(LAYERS)])
+    res["empty_launch_us"] = time_graph(g, 200) * 1e3 / LAYERS
+    res["note"] = ("hbm_read: 2048 workgroups streaming 1 GiB; read_decode_bytes_one_launch: one launch reading "
+                   f"{nb} B (the batch-16 decode's algorithmic bytes), 14 distinct buffers per graph replay; "
+                   "mfma: 1024 workgroups x 4 waves x 4 chains of v_mfma_f32_32x32x16_bf16; "
+                   "empty_launch: 14 empty kernels per graph replay")
+    return res
+
+
+# ---------------------------------------------------------------------------
 # oracle on the host
 # ---------------------------------------------------------------------------
 def cpu_baseline(layer, budget_s=12.0):
@@ -430,6 +482,80 @@ def cpu_baseline(layer, budget_s=12.0):
                       f"{len(os.sched_getaffinity(0))} cores available"}
 
 
+def _timed(fn, budget_s):
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            return el / n, n
+
+
+def oracle_samples(budget_s=3.0):
+    """The oracle beside the other timed ops, each on a bounded sample of its
+    workload (fp64 NumPy on the host cores; seeded synthetic inputs of the
+    workload's shapes): batch-1 32K decode per layer-step, queries of the last
+    16K prefill chunk (time per chunk extrapolated from the sample), one HCA
+    sequence's decode at 1M and one CSA sequence's indexer + top-512 + decode
+    at 128K (per step = per sequence x batch)."""
+    import numpy as np
+
+    from oracle import lbca_oracle as O
+
+    f64 = lambda t: t.to(torch.float64).numpy()
+    res = {}
+    # 32K decode at batch 1
+    tag = ("bench-oracle-32k",)
+    q = f64(synth.normal((1, HQ, D), synth.seed_of(*tag, "q"), dtype="bf16"))
+    pk, pv = (f64(synth.normal((1, HKV, N_POOLED, D), synth.seed_of(*tag, n), dtype="bf16")) for n in ("pk", "pv"))
+    rk, rv = (f64(synth.normal((1, HKV, RAW_ROWS, D), synth.seed_of(*tag, n), dtype="bf16")) for n in ("rk", "rv"))
+    sec, n = _timed(lambda: O.attend_decode(q, pk, pv, rk, rv, [T_POS], M, W, O.EXCLUSIVE, 1 / math.sqrt(D),
+                                            raw_pos_base=[RAW0]), budget_s)
+    res["decode_32k_b1"] = {"oracle_s": sec, "sample": f"{n} layer-steps"}
+    # prefill: the last 16 query positions of chunk 7 (positions 16368..16383)
+    tag = ("bench-oracle-prefill",)
+    nq, n_pool = 16, P_CTX // P_M
+    qp = f64(synth.normal((1, nq, HQ, D), synth.seed_of(*tag, "q"), dtype="bf16"))
+    ppk, ppv = (f64(synth.normal((1, HKV, n_pool, D), synth.seed_of(*tag, n), dtype="bf16")) for n in ("pk", "pv"))
+    prk, prv = (f64(synth.normal((1, HKV, P_CTX, D), synth.seed_of(*tag, n), dtype="bf16")) for n in ("rk", "rv"))
+    sec, n = _timed(lambda: O.attend_prefill(qp, P_CTX - nq, ppk, ppv, prk, prv, 0, P_M, W, O.EXCLUSIVE,
+                                             1 / math.sqrt(D)), budget_s)
+    res["prefill_16k_chunk7"] = {"oracle_s_per_chunk_est": sec * P_CHUNK / nq,
+                                 "sample": f"{n} runs of the last {nq} queries of chunk 7, scaled to {P_CHUNK}"}
+    # HCA decode, one sequence at t = 2^20 - 1
+    tag = ("bench-oracle-hca",)
+    treat = dict(rmsnorm_eps=X_EPS, rope_dims=X_RD, rope_base=X_BASE)
+    N = HCA_T // HCA_M
+    qh = f64(synth.normal((1, X_HQ, X_D), synth.seed_of(*tag, "q"), dtype="bf16"))
+    eh = f64(synth.normal((1, 1, N, X_D), synth.seed_of(*tag, "ent"), dtype="bf16"))
+    rh = f64(synth.normal((1, 1, W, X_D), synth.seed_of(*tag, "raw"), dtype="bf16"))
+    sk = f64(synth.normal((X_HQ,), synth.seed_of(*tag, "sink")))
+    sec, n = _timed(lambda: O.attend_decode(qh, eh, None, rh, None, [HCA_T - 1], HCA_M, W, O.OVERLAP,
+                                            1 / math.sqrt(X_D), raw_pos_base=[HCA_T - W], sink=sk, **treat),
+                    budget_s)
+    res["hca_1m_step"] = {"oracle_s": sec * HCA_B, "sample": f"{n} decodes of one sequence, x {HCA_B} sequences"}
+    # CSA: indexer scores + top-512 + decode over the selection, one sequence at t = 2^17 - 1
+    tag = ("bench-oracle-csa",)
+    N = CSA_T // CSA_M
+    qi = f64(synth.normal((CSA_HI, CSA_DI), synth.seed_of(*tag, "qi"), dtype="bf16"))
+    wi = f64(synth.uniform((CSA_HI,), synth.seed_of(*tag, "w")))
+    ki = f64(synth.normal((N, CSA_DI), synth.seed_of(*tag, "keys"), dtype="bf16"))
+    qc = f64(synth.normal((1, X_HQ, X_D), synth.seed_of(*tag, "q"), dtype="bf16"))
+    ec = f64(synth.normal((1, 1, N, X_D), synth.seed_of(*tag, "ent"), dtype="bf16"))
+    rc = f64(synth.normal((1, 1, W, X_D), synth.seed_of(*tag, "raw"), dtype="bf16"))
+
+    def csa_step():
+        sel = O.topk_select(O.index_scores(qi, wi, ki, N), CSA_K)
+        return O.attend_decode(qc, ec, None, rc, None, [CSA_T - 1], CSA_M, W, O.OVERLAP, 1 / math.sqrt(X_D),
+                               raw_pos_base=[CSA_T - W], sel_idx=sel[None], sink=sk, **treat)
+
+    sec, n = _timed(csa_step, budget_s)
+    res["csa_128k_step"] = {"oracle_s": sec * CSA_B, "sample": f"{n} steps of one sequence, x {CSA_B} sequences"}
+    del np
+    return res
+
+
 # ---------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser()
@@ -441,6 +567,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-small-batch", action="store_true")
     ap.add_argument("--no-mqa", action="store_true", help="skip the HCA 1M and CSA 128K lines")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured-ceiling probes")
     ap.add_argument("--counters", action="store_true",
                     help="only run what the FETCH_SIZE / WRITE_SIZE counter passes profile")
     args = ap.parse_args()
@@ -517,6 +644,33 @@ def main():
         log("[bench] CSA index top-512 + decode 128K (batch 2)")
         extra["csa_128k"] = run_csa(max(5, args.steps // 4))
         torch.cuda.empty_cache()
+
+    if not args.no_ceilings:
+        log("[bench] measured ceilings (streaming read, MFMA loop, launch floor)")
+        ce = run_ceilings()
+        ce["decode_launch_vs_one_launch_read"] = min(ce["read_decode_bytes_one_launch_us_grid256"],
+                                                     ce["read_decode_bytes_one_launch_us_grid1024"]) / us_launch
+        ce["decode_GBps_vs_stream_read"] = achieved / ce["hbm_read_GBps"]
+        if "prefill" in extra:
+            ce["prefill_vs_mfma_loop"] = extra["prefill"]["tflops"] / ce["mfma_bf16_TFLOPs"]
+        extra["ceilings"] = ce
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        log("[bench] oracle samples beside the other timed ops")
+        osm = oracle_samples()
+        osm["decode_32k_b1"]["gpu_s"] = extra["b1"]["decode_launch_us"] * 1e-6 if "b1" in extra else None
+        if "prefill" in extra:
+            osm["prefill_16k_chunk7"]["gpu_s_mean_chunk"] = extra["prefill"]["attention_ms"] * 1e-3 / 8
+        if "hca_1m" in extra:
+            osm["hca_1m_step"]["gpu_s"] = extra["hca_1m"]["decode_us"] * 1e-6
+        if "csa_128k" in extra:
+            osm["csa_128k_step"]["gpu_s"] = extra["csa_128k"]["step_us"] * 1e-6
+        for v in osm.values():
+            o = v.get("oracle_s", v.get("oracle_s_per_chunk_est"))
+            gs = v.get("gpu_s", v.get("gpu_s_mean_chunk"))
+            v["speedup"] = o / gs if o and gs else None
+        extra["oracle_vs_gpu"] = osm
 
     line = {
         "metric": METRIC, "value": value, "unit": "layer-steps/s", "n_gpus": 1, "steps": args.steps,

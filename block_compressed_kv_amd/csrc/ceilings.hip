@@ -1,0 +1,87 @@
+// Probes of this part's measured ceilings, reported beside the kernels'
+// roofline fractions: a streaming HBM read, a bf16 MFMA loop and an empty
+// kernel (the launch floor).  Built into libceilings.so, a library of its own
+// that only the benchmark loads; nothing here is part of the attention path.
+//
+// Each entry point checks its sizes and returns a hipError_t value (0 = success).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Grid-stride read of n16 16-byte vectors, eight loads in flight per thread;
+// each thread writes the xor of what it read (so no load can be dropped).
+__global__ __launch_bounds__(256) void read_kernel(const u32x4_t* __restrict__ src, int64_t n16,
+                                                   uint32_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = __builtin_nontemporal_load(src + i + j * stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4_t v = src[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+// Four independent chains of v_mfma_f32_32x32x16_bf16 per wave (32768 flops
+// each); every thread writes one sum of its accumulators.
+__global__ __launch_bounds__(256) void mfma_kernel(float* __restrict__ out, int iters) {
+  const float s = 1e-3f * (float)(threadIdx.x & 63);
+  bf16x8_t a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(s + 0.25f * e);
+    b[e] = (__bf16)(0.5f - s);
+  }
+  f32x16_t c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = c0[0] + c1[5] + c2[10] + c3[15];
+}
+
+__global__ void empty_kernel() {}
+
+}  // namespace
+
+extern "C" {
+
+// Reads `bytes` (a multiple of 16) from src with `grid` workgroups of 256
+// threads; out holds grid * 256 uint32.
+__attribute__((visibility("default"))) int ceil_read(const void* src, size_t bytes, void* out, int grid,
+                                                     void* stream) {
+  if (!src || !out || grid < 1 || bytes % 16 != 0) return (int)hipErrorInvalidValue;
+  read_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<const u32x4_t*>(src),
+                                                                  (int64_t)(bytes / 16),
+                                                                  static_cast<uint32_t*>(out));
+  return (int)hipGetLastError();
+}
+
+// grid workgroups of 4 waves, each wave 4 * iters MFMAs of 32768 flops; out
+// holds grid * 256 floats.
+__attribute__((visibility("default"))) int ceil_mfma(void* out, int grid, int iters, void* stream) {
+  if (!out || grid < 1 || iters < 1) return (int)hipErrorInvalidValue;
+  mfma_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<float*>(out), iters);
+  return (int)hipGetLastError();
+}
+
+__attribute__((visibility("default"))) int ceil_empty(void* stream) {
+  empty_kernel<<<1, 64, 0, static_cast<hipStream_t>(stream)>>>();
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"
