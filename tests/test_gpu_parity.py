@@ -293,6 +293,26 @@ def test_decode_mqa_512_head_counts(lib, Hq, B, nb):
     check_bf16(host(lse), rl, "lse")
 
 
+def test_decode_mqa_512_first_positions(lib):
+    # the wide path at the smallest positions: t = 0 (one raw row, no pooled entry),
+    # t = 1, t = 127 (one complete block, window 0..127) and t = 128
+    B, Hq, d, m, W = 4, 64, 512, 128, 128
+    T = 512
+    H = _dev(synth.hca_layer("dec-mqa512-first", B, Hq, T, d, m))
+    t_list = [0, 1, 127, 128]
+    N = T // m
+    entries = torch.zeros((B, 1, N, d), dtype=torch.bfloat16, device=DEV)
+    treat = dict(rmsnorm_eps=1e-6, rope_dims=64)
+    lib.pool_blocks(H["c"], H["z"], H["bias"], m, 0, N, entries, **treat)
+    pos = torch.tensor(t_list, device=DEV)
+    o, lse = lib.attend_decode(H["q"], entries, H["c"], pos, m, W, O.OVERLAP, sink=H["sink"], **treat)
+    pooled = O.pool_single(host(H["c"]), host(H["z"]), host(H["bias"]), m, 0, N)
+    ro, rl = O.attend_decode(host(H["q"]), pooled, None, host(H["c"]), None, t_list, m, W, O.OVERLAP,
+                             1 / math.sqrt(d), sink=host(H["sink"]), **treat)
+    check_bf16(host(o), ro, "MQA-512 first positions")
+    check_bf16(host(lse), rl, "lse")
+
+
 def test_decode_selected_entries(lib):
     # CSA-style: dual-pooled treated entries, a selection with -1 padding and invisible
     # ids, plus the 128-token window; MQA 64 heads, d=512
@@ -361,6 +381,27 @@ def test_prefill_chunked_bf16(lib, chunk):
     check_bf16(host(lse), rl, "prefill lse")
 
 
+@pytest.mark.parametrize("q0,q_len", [(0, 1), (777, 1), (500, 3)])
+def test_prefill_tiny_chunks(lib, q0, q_len):
+    # chunks of one to three queries (one 16-row group, mostly padding), GQA bf16, EXCLUSIVE
+    B, Hq, Hkv, d, m, W = 2, 24, 8, 128, 16, 128
+    T = 800
+    L = _dev(synth.lbca_layer("prefill-tiny", B, Hq, Hkv, T, d, m, "bf16", "f32", q_len=T))
+    need, _ = O.visible_range(q0 + q_len - 1, m, W, O.EXCLUSIVE)
+    pk = torch.zeros((B, Hkv, T // m, d), dtype=torch.bfloat16, device=DEV)
+    pv = torch.zeros_like(pk)
+    if need > 0:
+        lib.pool_blocks(L["k"], L["z"], L["bias"], m, 0, need, pk, v=L["v"], out_v=pv)
+    q = L["q"][:, q0:q0 + q_len].contiguous()
+    o, lse = lib.attend_prefill(q, q0, pk, L["k"], 0, m, W, O.EXCLUSIVE, pooled_v=pv, raw_v=L["v"],
+                                out_dtype=torch.float32)
+    rpk, rpv = O.pool_single(host(L["k"]), host(L["z"]), host(L["bias"]), m, 0, T // m, values=host(L["v"]))
+    ro, rl = O.attend_prefill(host(q), q0, rpk, rpv, host(L["k"]), host(L["v"]), 0, m, W, O.EXCLUSIVE,
+                              1 / math.sqrt(d))
+    check_bf16(host(o), ro, f"prefill q0={q0} len={q_len}")
+    check_bf16(host(lse), rl, "lse")
+
+
 def test_prefill_overlap_shared_sink(lib):
     # OVERLAP visibility, shared K=V series, sink, fp32 output, MQA-like 8 heads over 1 KV head, d=64
     B, Hq, d, m, W, T = 2, 8, 64, 8, 24, 333
@@ -403,6 +444,23 @@ def test_index_topk(lib, N, k, t_list):
         sel = idx[b][idx[b] >= 0]
         np.testing.assert_allclose(score[b][:sel.size], s[sel], rtol=1e-5, atol=1e-5)
         assert np.isnan(score[b][sel.size:]).all()
+
+
+@pytest.mark.parametrize("N,k,t_list", [(600, 50, [-1, -7]), (20000, 300, [1199, -1])])
+def test_index_topk_no_or_exactly_k_visible(lib, N, k, t_list):
+    # t < 0 sees nothing (an all -1 row); t = 1199 with m = 4 sees exactly k = 300 entries
+    B, HI, dI, m = len(t_list), 8, 64, 4
+    g = lambda n, shape: synth.normal(shape, synth.seed_of("idx-edge", N, n), dtype="bf16", device=DEV)
+    qi, keys = g("qi", (B, HI, dI)), g("k", (B, N, dI))
+    w = synth.uniform((B, HI), synth.seed_of("idx-edge", N, "w"), device=DEV)
+    idx, score = lib.csa_index_topk(qi, w, keys, torch.tensor(t_list, device=DEV), m, k)
+    idx, score = idx.cpu().numpy(), score.cpu().numpy()
+    for b, t in enumerate(t_list):
+        n_vis = 0 if t < 0 else min((t + 1) // m, N)
+        s = O.index_scores(host(qi[b]), host(w[b]), host(keys[b]), n_vis)
+        assert list(idx[b]) == list(O.topk_select(s, k)), f"seq {b} t={t}"
+        np.testing.assert_allclose(score[b][:n_vis], s, rtol=1e-5, atol=1e-5)
+        assert np.isnan(score[b][n_vis:]).all()
 
 
 def test_topk_two_stage_ties_across_slices(lib):
