@@ -230,6 +230,26 @@ def prefill_flops():
     return tot
 
 
+def prefill_executed_flops():
+    """FLOPs the kernels execute for the 16K chunked prefill: each workgroup (256
+    rows of the flattened (position, GQA head) space of one KV head) multiplies
+    its rows by every 32-key tile of the union of its rows' visible spans (the
+    pooled prefix of its last position, then the raw band from its first
+    position's window start to its last position), masked or not."""
+    G = HQ // HKV
+    tot = 0
+    for c0 in range(0, P_CTX, P_CHUNK):
+        rows = P_CHUNK * G
+        for r0 in range(0, rows, 256):
+            r1 = min(rows, r0 + 256) - 1
+            p_first, p_last = c0 + r0 // G, c0 + r1 // G
+            n_p, _ = lbca.visible_range(p_last, P_M, W, EXCL)
+            _, rb = lbca.visible_range(p_first, P_M, W, EXCL)
+            tiles = -(-n_p // 32) + -(-(p_last - rb + 1) // 32)
+            tot += HKV * 256 * tiles * 32 * D * 4
+    return tot
+
+
 def run_prefill(reps):
     dev = "cuda"
     L = synth.lbca_layer(("bench-prefill-16k",), 1, HQ, HKV, P_CTX, D, P_M, "bf16", "f32", device=dev,
@@ -633,9 +653,11 @@ def main():
         log("[bench] chunked prefill 16K (8 x 2048)")
         ms_full, ms_attn = run_prefill(max(5, args.steps // 10))
         fl = prefill_flops()
+        fx = prefill_executed_flops()
         extra["prefill"] = {"tflops": fl / (ms_attn * 1e-3) / 1e12, "attention_ms": ms_attn,
                             "with_pooling_ms": ms_full, "algorithmic_flops": fl,
-                            "frac_of_bf16_peak": fl / (ms_attn * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+                            "frac_of_bf16_peak": fl / (ms_attn * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                            "executed_tile_flops": fx, "executed_tflops": fx / (ms_attn * 1e-3) / 1e12}
 
     if not args.no_mqa:
         log("[bench] HCA decode 1M (batch 4)")
