@@ -44,6 +44,19 @@ __device__ __forceinline__ int64_t n_visible(const IndexParams& p, int64_t b) {
   return n < p.entries ? n : p.entries;
 }
 
+// Sum over each 16-lane row with DPP moves; the total lands in lane 15 of the row.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xF, 0xF, true));
+  return x;
+}
+
+// One wave scores 64 keys.  Every load is issued up front and carries no
+// branch (keys past the visible ones read the last visible key; padded heads
+// read head 0's query and have weight 0), so the loads overlap and each wait
+// covers only what it needs.
 template <int DI>
 __global__ __launch_bounds__(256) void index_score_kernel(IndexParams p) {
   constexpr int KS = DI / 32;
@@ -54,37 +67,42 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexParams p) {
   const int64_t key0 = ((int64_t)blockIdx.x * 4 + wave) * 64;
   if (key0 >= nv) return;  // whole wave beyond the visible keys
   const bool head_ok = n < p.heads;
-  const bf16_t* qrow = p.q + (b * p.heads + n) * DI + 8 * kq;
+  const bf16_t* qrow = p.q + (b * p.heads + (head_ok ? n : 0)) * DI + 8 * kq;
   uint4 qr[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s)
-    qr[s] = head_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s) : make_uint4(0, 0, 0, 0);
-  const float wh = head_ok ? p.w[b * p.heads + n] : 0.f;
+  for (int s = 0; s < KS; ++s) qr[s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
+  const float wv = p.w[b * p.heads + (head_ok ? n : 0)];
+  uint4 kv[4][KS];
 #pragma unroll
   for (int hh = 0; hh < 4; ++hh) {
-    const int64_t key = key0 + 16 * hh + n;
-    const bool ok = key < nv;
+    int64_t key = key0 + 16 * hh + n;
+    key = key < nv ? key : nv - 1;
     const bf16_t* krow = p.keys + (b * p.entries + key) * DI + 8 * kq;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kv[hh][s] = *reinterpret_cast<const uint4*>(krow + 32 * s);
+  }
+  const float wh = head_ok ? wv : 0.f;
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh) {
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const uint4 kv = ok ? *reinterpret_cast<const uint4*>(krow + 32 * s) : make_uint4(0, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv),
+    for (int s = 0; s < KS; ++s)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv[hh][s]),
                                                    __builtin_bit_cast(bf16x8, qr[s]), c, 0, 0, 0);
-    }
+    // lane (n, kq) holds head n's dot products with keys kbase .. kbase + 3
     float v[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = wh * fmaxf(c[j], 0.f);
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] += __shfl_xor(v[j], o, 64);
-    const int64_t kbase = key0 + 16 * hh + 4 * kq;  // keys of lane (., kq): kbase .. kbase+3
-    if (n == 0) {
+    for (int j = 0; j < 4; ++j) v[j] = row16_sum(wh * fmaxf(c[j], 0.f));
+    const int64_t kbase = key0 + 16 * hh + 4 * kq;
+    if (n == 15) {
       float* dst = p.scores + b * p.stride + kbase;
+      if (kbase + 3 < nv) {
+        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (kbase + j < nv) dst[j] = v[j];
+        for (int j = 0; j < 4; ++j)
+          if (kbase + j < nv) dst[j] = v[j];
+      }
     }
   }
 }
