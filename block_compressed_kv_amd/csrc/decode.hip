@@ -606,7 +606,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
 constexpr int kMergeGroups = 4;  // for 64-dim chunks
 template <bool NORM>
 __global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeParams p, int D, int CK) {
-  __shared__ float s_w[64][16], s_l[64][16];  // split maxima (then weights) and sums
+  __shared__ float s_w[64][16];                 // split weights
+  __shared__ float s_red[16][16], s_red2[16][16];  // per-wave max and sum of each slot
   __shared__ float s_inv[16], s_lse[16];
   __shared__ float4 s_part[kMergeGroups][16][32];  // [group][slot][float4 of the chunk], CK <= 128
   using PT = typename std::conditional<NORM, uint2, float4>::type;  // one partial's 4 dims
@@ -635,25 +636,33 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeParams p, int 
 #pragma unroll
   for (int i = 0; i < kPre; ++i)
     if (mine && sg + i * NG < S) pre[i] = pa[(int64_t)(sg + i * NG) * pstride];
-  // every split's (max, sum) of the 16 slots to LDS at once (one load per thread)
-  for (int i = tid; i < S * 16; i += blockDim.x) {
-    const float2 ml = *reinterpret_cast<const float2*>(&p.ws_ml[(part0 * 16 + i) * 2]);
-    s_w[i >> 4][i & 15] = ml.x;
-    s_l[i >> 4][i & 15] = ml.y;
-  }
+  // Split weights, one thread per (split s = tid / 16, slot tid % 16) (S <= 64):
+  // the slot's max and sum over splits go over the four splits of a wave by
+  // lane exchanges, then over the waves through LDS, both in a fixed order.
+  const int ws = tid >> 4, wsl = tid & 15, wave = tid >> 6;
+  const int nwv = (S + 3) >> 2;  // waves holding splits
+  float2 ml = make_float2(kNegInf, 0.f);
+  if (ws < S) ml = *reinterpret_cast<const float2*>(&p.ws_ml[(part0 * 16 + tid) * 2]);
   const SeqView sv = seq_view(p, b);
   if (!sv.ok) return;  // the decode kernel already wrote NaN for this unit
+  float M = fmaxf(ml.x, __shfl_xor(ml.x, 16, 64));
+  M = fmaxf(M, __shfl_xor(M, 32, 64));
+  if (wave < nwv && (tid & 63) < 16) s_red[wave][wsl] = M;
+  __syncthreads();
+  M = s_red[0][wsl];
+#pragma unroll
+  for (int w = 1; w < 16; ++w)
+    if (w < nwv) M = fmaxf(M, s_red[w][wsl]);
+  const float sw = ml.x == kNegInf ? 0.f : exp2f(ml.x - M);
+  if (ws < S) s_w[ws][wsl] = NORM ? sw * ml.y : sw;
+  float L = ml.y * sw;
+  L += __shfl_xor(L, 16, 64);
+  L += __shfl_xor(L, 32, 64);
+  if (wave < nwv && (tid & 63) < 16) s_red2[wave][wsl] = L;
   __syncthreads();
   if (tid < nvalid) {
-    float M = kNegInf;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, s_w[s][tid]);
-    float L = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float ms = s_w[s][tid];
-      const float sw = ms == kNegInf ? 0.f : exp2f(ms - M);
-      s_w[s][tid] = NORM ? sw * s_l[s][tid] : sw;
-      L = fmaf(s_l[s][tid], sw, L);
-    }
+    L = s_red2[0][tid];
+    for (int w = 1; w < nwv; ++w) L += s_red2[w][tid];
     if (p.sink) L += exp2f(p.sink[head0 + tid] * kLog2e - M);
     s_inv[tid] = 1.f / L;
     s_lse[tid] = (M + log2f(L)) * 0.69314718055994531f;

@@ -125,9 +125,37 @@ struct PoolAcc {
     mx[c] = nm;
   }
 
+  // Merge with the state of lane (lane ^ OFF), OFF = 16 or 32, through the
+  // gfx950 lane swaps (VALU, no LDS round trip).  A swap of a register with
+  // itself leaves the same two values in the same two result slots on both
+  // lanes of a pair (the lower row's or half's value in the first, the other
+  // in the second), so both lanes combine the same states in the same order.
+  template <int OFF>
+  __device__ __forceinline__ void merge_swap() {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    auto sw = [](float x) -> f2 {
+      const uint32_t u = __float_as_uint(x);
+      if constexpr (OFF == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return f2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+      } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return f2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+      }
+    };
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const f2 m2 = sw(mx[c]), l2 = sw(l[c]), x2 = sw(ax[c]);
+      const f2 v2 = HAS_V ? sw(av[c]) : f2{0.f, 0.f};
+      combine1(c, m2[0], l2[0], x2[0], v2[0], m2[1], l2[1], x2[1], v2[1]);
+    }
+  }
+
   // Merge with the state of lane (lane ^ off); `lower`: this lane holds the
   // lower phase.  Both lanes of a pair evaluate the same expression.
   __device__ __forceinline__ void merge_xor(int off, bool lower) {
+    if (off == 16) return merge_swap<16>();
+    if (off == 32) return merge_swap<32>();
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const float omx = __shfl_xor(mx[c], off, 64), ol = __shfl_xor(l[c], off, 64);

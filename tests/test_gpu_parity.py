@@ -313,6 +313,51 @@ def test_decode_mqa_512_first_positions(lib):
     check_bf16(host(lse), rl, "lse")
 
 
+@pytest.mark.parametrize("path", ["gqa128", "mqa512"])
+def test_decode_merge_64_splits(lib, path):
+    # one sequence whose rows are cut into the most splits (64), so the merge
+    # combines 64 partials per head: split maxima and sums reduced over the
+    # splits of 16 waves.  gqa128: unnormalised fp32 partials of the GQA path;
+    # mqa512: normalised bf16 partials of the wide path (entries pooled and
+    # treated from a raw series with 4-token blocks, sink).
+    say(f"64-split decode {path}")
+    if path == "gqa128":
+        Hq, Hkv, d, m, W, N = 24, 8, 128, 64, 128, 65000
+        t = N * m + 127
+        n_p, rb = O.visible_range(t, m, W, O.EXCLUSIVE)
+        assert n_p == N
+        g = lambda n, shape: synth.normal(shape, synth.seed_of("dec-64splits", n), dtype="bf16", device=DEV)
+        q = g("q", (1, Hq, d))
+        pk, pv = g("pk", (1, Hkv, N, d)), g("pv", (1, Hkv, N, d))
+        rk, rv = g("rk", (1, Hkv, 256, d)), g("rv", (1, Hkv, 256, d))
+        pos, rpb = torch.tensor([t], device=DEV), torch.tensor([rb], device=DEV)
+        kw = dict(pooled_v=pv, raw_v=rv, raw_pos_base=rpb)
+        need = lib.decode_workspace_bytes(q, pk, rk, pos, m, W, O.EXCLUSIVE, **kw)
+        assert need == Hkv * 64 * 16 * (2 * 4 + d * 4), need      # 64 fp32 partials per unit
+        o, lse = lib.attend_decode(q, pk, rk, pos, m, W, O.EXCLUSIVE, **kw)
+        ro, rl = O.attend_decode(host(q), host(pk), host(pv), host(rk), host(rv), [t], m, W, O.EXCLUSIVE,
+                                 1 / math.sqrt(d), raw_pos_base=[rb])
+    else:
+        Hq, d, m, W = 64, 512, 4, 128
+        T = 4 * 4200 + 3
+        N = T // m
+        H = _dev(synth.hca_layer("dec-64splits-mqa", 1, Hq, T, d, m))
+        entries = torch.zeros((1, 1, N, d), dtype=torch.bfloat16, device=DEV)
+        treat = dict(rmsnorm_eps=1e-6, rope_dims=64)
+        lib.pool_blocks(H["c"], H["z"], H["bias"], m, 0, N, entries, **treat)
+        t = T - 1
+        pos = torch.tensor([t], device=DEV)
+        kw = dict(sink=H["sink"], **treat)
+        need = lib.decode_workspace_bytes(H["q"], entries, H["c"], pos, m, W, O.OVERLAP, **kw)
+        assert need == (Hq // 16) * 64 * 16 * (2 * 4 + d * 2), need  # 64 bf16 partials per unit
+        o, lse = lib.attend_decode(H["q"], entries, H["c"], pos, m, W, O.OVERLAP, **kw)
+        pooled = O.pool_single(host(H["c"]), host(H["z"]), host(H["bias"]), m, 0, N)
+        ro, rl = O.attend_decode(host(H["q"]), pooled, None, host(H["c"]), None, [t], m, W, O.OVERLAP,
+                                 1 / math.sqrt(d), sink=host(H["sink"]), **treat)
+    check_bf16(host(o), ro, f"64-split decode {path}")
+    check_bf16(host(lse), rl, "lse")
+
+
 def test_decode_selected_entries(lib):
     # CSA-style: dual-pooled treated entries, a selection with -1 padding and invisible
     # ids, plus the 128-token window; MQA 64 heads, d=512
