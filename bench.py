@@ -16,7 +16,9 @@ and replayed; HIP events on the launch stream bracket the timed region.
 Also reported: the decode launch's HBM roofline fraction (and its HBM traffic
 from stored counter passes), the oracle on the host cores (cpu_baseline), batch
 1 and 4, the step with the due block pooled first (a block leaves the window
-every 64 steps), pooling GB/s for the whole history, chunked prefill (16K
+every 64 steps), an incremental decode loop (64 steps of lbca_cache_append into a
+mirrored raw ring, the due block pooled on its step, then decode from the ring),
+pooling GB/s for the whole history, chunked prefill (16K
 context in 2048-token chunks) TFLOP/s, HCA decode at 1M context (batch 4, 64
 query heads x 512, pooling GB/s of the whole history) and CSA at 128K (batch 2:
 indexer scores + top-512, decode over the selection, dual pooling GB/s); the
@@ -36,6 +38,7 @@ import math
 import os
 import sys
 import time
+import types
 
 import torch
 
@@ -214,6 +217,81 @@ def run_decode(B, steps, warmup, pool_timer=None):
     ms_step = time_graph(g_step, steps)          # 14 decode launches
     ms_pool_step = time_graph(g_pool, steps)     # 14 x (pool due block + decode)
     return layers, ms_step, ms_pool_step
+
+
+# ---------------------------------------------------------------------------
+# incremental decode loop: the cache step (token into the raw ring, due block
+# pooled on its step) followed by decode, as a decode loop runs it
+# ---------------------------------------------------------------------------
+RING = W + M          # ring slots (the raw buffers hold 2 * RING mirrored rows)
+INC_STEPS = M         # one block period: each layer pools exactly one due block
+
+
+def run_incremental(B, reps):
+    """Decode steps at positions T_POS-63 .. T_POS of 14 layers at batch 16 (the last
+    step makes block 509 visible).  Per layer and step, lbca_cache_append writes the
+    token to the mirrored raw ring (pooling the due block on its step), then
+    lbca_attend_decode reads the pooled entries and the ring.  A second graph runs the
+    same decodes alone (raw bases precomputed), so the cache step's share is the
+    difference."""
+    dev = "cuda"
+    t0 = T_POS - INC_STEPS + 1
+    poss = [torch.full((B,), t0 + s, dtype=torch.int64, device=dev) for s in range(INC_STEPS)]
+    bases = []
+    for pos in poss:
+        _, rb = lbca.visible_range(int(pos[0]), M, W, EXCL)
+        bases.append(torch.full((B,), rb - rb % RING, dtype=torch.int64, device=dev))
+    layers = []
+    for l in range(LAYERS):
+        g = lambda n, shape, dt="bf16": synth.normal(shape, synth.seed_of("bench-inc", l, B, n), dtype=dt,
+                                                     device=dev)
+        L = types.SimpleNamespace()
+        L.pk, L.pv = g("pk", (B, HKV, N_POOLED + 2, D)), g("pv", (B, HKV, N_POOLED + 2, D))
+        L.rk, L.rv, L.rz = g("rk", (B, HKV, 2 * RING, D)), g("rv", (B, HKV, 2 * RING, D)), \
+            g("rz", (B, HKV, 2 * RING, D), "f32")
+        L.xk, L.xv, L.xz = g("xk", (B, HKV, D)), g("xv", (B, HKV, D)), g("xz", (B, HKV, D), "f32")
+        L.bias = synth.normal((HKV, M, D), synth.seed_of("bench-inc", l, "bias"), std=0.1, device=dev)
+        L.q = g("q", (B, HQ, D))
+        L.rpb = torch.zeros((B,), dtype=torch.int64, device=dev)
+        L.out = torch.empty((B, HQ, D), dtype=torch.float32, device=dev)
+        L.lse = torch.empty((B, HQ), dtype=torch.float32, device=dev)
+        nb = lbca.decode_workspace_bytes(L.q, L.pk, L.rk, poss[0], M, W, EXCL, pooled_v=L.pv, raw_v=L.rv,
+                                         raw_pos_base=L.rpb)
+        L.ws = torch.zeros(max(nb, 16), dtype=torch.uint8, device=dev)
+        layers.append(L)
+
+    def decode(L, pos, rpb):
+        lbca.attend_decode(L.q, L.pk, L.rk, pos, M, W, EXCL, out=L.out, lse=L.lse, pooled_v=L.pv, raw_v=L.rv,
+                           raw_pos_base=rpb, workspace=L.ws)
+
+    def loop():
+        for pos in poss:
+            for L in layers:
+                lbca.cache_append(L.xk, L.xz, L.rk, L.rz, L.bias, pos, L.rpb, M, W, EXCL, L.pk, v_new=L.xv,
+                                  raw_v=L.rv, out_v=L.pv)
+                decode(L, pos, L.rpb)
+
+    def decode_only():
+        for pos, rpb in zip(poss, bases):
+            for L in layers:
+                decode(L, pos, rpb)
+
+    loop()  # eager pass; the graphs then revisit the same 64 positions with the same tokens
+    torch.cuda.synchronize()
+    ref = [L.out.clone() for L in layers]
+    if not all(torch.equal(L.rpb, bases[-1]) for L in layers):
+        raise RuntimeError("cache step left an unexpected raw base")
+    g_loop, g_dec = capture(loop), capture(decode_only)
+    g_loop.replay()
+    torch.cuda.synchronize()
+    if not all(torch.equal(L.out, r) for L, r in zip(layers, ref)):
+        raise RuntimeError("graph replay of the decode loop differs from the eager pass")
+    ms_loop, ms_dec = time_graph(g_loop, reps), time_graph(g_dec, reps)
+    n = INC_STEPS * LAYERS
+    return {"layer_steps_per_s": n / (ms_loop * 1e-3), "layer_step_us": ms_loop * 1e3 / n,
+            "decode_us": ms_dec * 1e3 / n, "cache_append_us": (ms_loop - ms_dec) * 1e3 / n,
+            "workload": f"batch {B}, 14 layers, positions {t0}..{T_POS} (one due block per layer), "
+                        f"mirrored raw ring of {RING} slots"}
 
 
 # ---------------------------------------------------------------------------
@@ -585,6 +663,7 @@ def main():
     ap.add_argument("--batch", type=int, default=16)
     ap.add_argument("--no-cpu", action="store_true", help="skip the host oracle timing")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-incremental", action="store_true", help="skip the cache-step decode loop")
     ap.add_argument("--no-small-batch", action="store_true")
     ap.add_argument("--no-mqa", action="store_true", help="skip the HCA 1M and CSA 128K lines")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured-ceiling probes")
@@ -648,6 +727,11 @@ def main():
                               "note": "14 layers fit in the 256 MB Infinity Cache at this batch"}
             del ls
             torch.cuda.empty_cache()
+
+    if not args.no_incremental:
+        log("[bench] incremental decode loop 32K (cache step + decode, 64 steps)")
+        extra["incremental_32k"] = run_incremental(B, max(5, args.steps // 10))
+        torch.cuda.empty_cache()
 
     if not args.no_prefill:
         log("[bench] chunked prefill 16K (8 x 2048)")

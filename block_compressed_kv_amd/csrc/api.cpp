@@ -1,6 +1,7 @@
 // C-ABI entry points of liblbca: host-side validation, then one launcher call.
 // Validation never touches the GPU, so every argument error is reported
 // (and testable) on a machine without one.
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -101,6 +102,39 @@ int lbca_pool_blocks(const lbca_pool_args* a, void* stream) {
   }
   if (a->batch == 0 || a->block_end == a->block_begin) return LBCA_OK;
   return hip_status(lbca::launch_pool(*a, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+int lbca_cache_append(const lbca_cache_args* a, void* stream) {
+  if (!a || !a->x_new || !a->z_new || !a->raw_x || !a->raw_z || !a->bias || !a->out_x || !a->pos ||
+      !a->raw_pos_base)
+    return LBCA_ERR_INVALID_ARG;
+  const bool has_v = a->v_new != nullptr;
+  if ((a->raw_v != nullptr) != has_v || (a->out_v != nullptr) != has_v) return LBCA_ERR_INVALID_ARG;
+  if (!is_dtype(a->x_dtype) || !is_dtype(a->z_dtype)) return LBCA_ERR_INVALID_ARG;
+  if (a->mode != LBCA_EXCLUSIVE && a->mode != LBCA_OVERLAP) return LBCA_ERR_INVALID_ARG;
+  if (a->batch < 0 || a->heads < 1 || a->block < 1 || a->window < 1 || a->entries < 0 || a->ring < 1)
+    return LBCA_ERR_INVALID_ARG;
+  if (!pow2(a->dim) || a->dim < 8) return a->dim > 0 ? LBCA_ERR_UNSUPPORTED : LBCA_ERR_INVALID_ARG;
+  if (a->dim > 512) return LBCA_ERR_UNSUPPORTED;
+  // every token a step reads must still be in the ring
+  const int64_t need = a->mode == LBCA_EXCLUSIVE ? a->window + a->block
+                                                  : (a->window > a->block ? a->window : a->block);
+  if (a->window > kMaxElems || a->block > kMaxElems || a->ring < need) return LBCA_ERR_INVALID_ARG;
+  if (a->batch > INT32_MAX / a->heads) return LBCA_ERR_UNSUPPORTED;  // one workgroup per (sequence, head)
+  if (!sane_product({a->batch, a->heads, 2 * a->ring, a->dim}) ||
+      !sane_product({a->batch, a->heads, a->entries, a->dim}) || !sane_product({a->heads, a->block, a->dim}))
+    return LBCA_ERR_INVALID_ARG;
+  const bool treat = a->rmsnorm_eps >= 0.f || a->rope_dims != 0;
+  int st = check_treatment(a->rmsnorm_eps, a->rope_dims, a->rope_base, a->dim);
+  if (st != LBCA_OK) return st;
+  if (treat && has_v) return LBCA_ERR_UNSUPPORTED;
+  if (!aligned16(a->x_new) || !aligned16(a->v_new) || !aligned16(a->z_new) || !aligned16(a->raw_x) ||
+      !aligned16(a->raw_v) || !aligned16(a->raw_z) || !aligned16(a->bias) || !aligned16(a->out_x) ||
+      !aligned16(a->out_v))
+    return LBCA_ERR_INVALID_ARG;
+  if (a->batch == 0) return LBCA_OK;
+  return hip_status(lbca::launch_cache_append(*a, static_cast<hipStream_t>(stream)));
 }
 
 // ---------------------------------------------------------------------------

@@ -1,0 +1,172 @@
+// Decode-time cache step: append each sequence's newest token to a mirrored
+// raw ring and pool the block that becomes visible at that token.
+//
+// Method: "mSeek: learned KV-cache compression in a 3B model", section "How LBCA
+// works" (steps 1-3: new tokens join the raw cache; a block that is complete
+// and has left the W-token window becomes one pooled entry); "HCA: Heavily
+// Compressed Attention (toy implementation)", "What is implemented" (every
+// complete block is an entry, with RMSNorm and partial RoPE at its start).
+//
+// Design: one 256-thread workgroup per (sequence, head) row.  The first L =
+// dim/8 lanes copy the new token's key, value and logit rows (16-byte
+// vectors) into both rows of its ring slot.  On the step that makes a block
+// visible, the whole workgroup pools it: its m tokens sit in m consecutive
+// ring rows (the mirror keeps any run of at most `ring` positions
+// contiguous), the 256 / L lane groups take token phases, and the phases are
+// merged and the entry finished exactly as in the pooling kernels (shared
+// code), so an entry written here is bitwise the one lbca_pool_blocks writes.
+// Under the OVERLAP rule the due block ends with the new token, which the
+// workgroup's barrier after the copy makes visible to every lane.
+#include "lbca_internal.h"
+#include "pool_common.h"
+
+namespace lbca {
+
+struct CacheParams {
+  const void* x_new;
+  const void* v_new;
+  const void* z_new;
+  void* raw_x;
+  void* raw_v;
+  void* raw_z;
+  const float* bias;
+  void* out_x;
+  void* out_v;
+  const int64_t* pos;
+  int64_t* raw_pos_base;
+  int64_t heads, dim, m, W, ring, entries;
+  int mode;
+  int lanes_per_row;  // L = dim / 8
+  int log2_lanes;
+  float eps;
+  int rope_dims;
+  double log2_base;
+};
+
+// 16-byte vector i of row r (8 elements are one vector in bf16, two in fp32).
+template <typename T>
+__device__ __forceinline__ uint4 ld16(const T* r, int i) { return reinterpret_cast<const uint4*>(r)[i]; }
+template <typename T>
+__device__ __forceinline__ void st16(T* r, int i, uint4 v) { reinterpret_cast<uint4*>(r)[i] = v; }
+
+template <typename TX, typename TZ, bool HAS_V, bool TREAT>
+__global__ __launch_bounds__(256) void cache_append_kernel(CacheParams p) {
+  __shared__ float part[32][256];  // cross-wave phase merge
+  // every argument field in one batch of scalar loads (otherwise they come in
+  // dependent rounds, one per basic block)
+  asm volatile("" ::"s"(p.x_new), "s"(p.v_new), "s"(p.z_new), "s"(p.raw_x), "s"(p.raw_v), "s"(p.raw_z),
+               "s"(p.pos), "s"(p.raw_pos_base), "s"(p.heads), "s"(p.dim), "s"(p.m), "s"(p.W), "s"(p.ring),
+               "s"(p.entries), "s"(p.mode), "s"(p.lanes_per_row), "s"(p.log2_lanes));
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int L = p.lanes_per_row;
+  const int li = lane & (L - 1);
+  const int phase = tid >> p.log2_lanes;  // every lane group is a token phase of this row
+  const int P = 256 >> p.log2_lanes;
+  const unsigned row = blockIdx.x;  // sequence * heads + head (the host keeps it below 2^31)
+  const unsigned b = row / (unsigned)p.heads, h = row % (unsigned)p.heads;
+  const int64_t dim = p.dim, ring = p.ring;
+  const int64_t c0 = (int64_t)li * 8;
+  // the new token's rows first: their addresses do not depend on the position
+  constexpr bool X2 = sizeof(TX) == 4, Z2 = sizeof(TZ) == 4;  // two vectors per 8 fp32 elements
+  const int64_t src = (int64_t)row * dim + c0;
+  const TX* xs = static_cast<const TX*>(p.x_new) + src;
+  const TX* vs = static_cast<const TX*>(p.v_new) + src;
+  const TZ* zs = static_cast<const TZ*>(p.z_new) + src;
+  uint4 x0 = {}, x1 = {}, v0 = {}, v1 = {}, z0 = {}, z1 = {};
+  if (phase == 0) {
+    x0 = ld16(xs, 0);
+    if constexpr (X2) x1 = ld16(xs, 1);
+    if constexpr (HAS_V) {
+      v0 = ld16(vs, 0);
+      if constexpr (X2) v1 = ld16(vs, 1);
+    }
+    z0 = ld16(zs, 0);
+    if constexpr (Z2) z1 = ld16(zs, 1);
+  }
+  const int64_t t = p.pos[b];
+  if (t < 0) return;
+  const int64_t series = (int64_t)row * 2 * ring * dim + c0;  // ring rows of this (sequence, head)
+
+  // 1. the new token into both rows of its slot
+  const int64_t slot = t % ring;
+  if (phase == 0) {
+    const int64_t d0 = series + slot * dim, d1 = d0 + ring * dim;
+    TX* rx = static_cast<TX*>(p.raw_x);
+    TZ* rz = static_cast<TZ*>(p.raw_z);
+    st16(rx + d0, 0, x0);
+    st16(rx + d1, 0, x0);
+    if constexpr (X2) {
+      st16(rx + d0, 1, x1);
+      st16(rx + d1, 1, x1);
+    }
+    if constexpr (HAS_V) {
+      TX* rv = static_cast<TX*>(p.raw_v);
+      st16(rv + d0, 0, v0);
+      st16(rv + d1, 0, v0);
+      if constexpr (X2) {
+        st16(rv + d0, 1, v1);
+        st16(rv + d1, 1, v1);
+      }
+    }
+    st16(rz + d0, 0, z0);
+    st16(rz + d1, 0, z0);
+    if constexpr (Z2) {
+      st16(rz + d0, 1, z1);
+      st16(rz + d1, 1, z1);
+    }
+  }
+  // 2. the raw base that maps t's raw span onto ring rows
+  int64_t n_pooled, raw_begin;
+  visible_range(t, p.m, p.W, p.mode, &n_pooled, &raw_begin);
+  if (h == 0 && tid == 0) p.raw_pos_base[b] = raw_begin - raw_begin % ring;
+  // 3. the block that becomes visible at t, if any
+  const int64_t x = p.mode == LBCA_EXCLUSIVE ? t + 1 - p.W : t + 1;
+  if (x <= 0 || x % p.m != 0) return;
+  const int64_t j = x / p.m - 1;
+  if (j >= p.entries) return;
+  __syncthreads();  // the copied token (the last one of an OVERLAP block) is visible to every lane
+  const int64_t r0 = (j * p.m) % ring;  // first ring row of the block
+  PoolAcc<TX, TZ, HAS_V> acc;
+  acc.init();
+  acc.run(static_cast<const TX*>(p.raw_x) + series + r0 * dim,
+          HAS_V ? static_cast<const TX*>(p.raw_v) + series + r0 * dim : nullptr,
+          static_cast<const TZ*>(p.raw_z) + series + r0 * dim, p.bias + h * p.m * dim + c0, phase, P, p.m, dim);
+  const int64_t o = ((int64_t)row * p.entries + j) * dim + c0;
+  finish_entry<TX, TZ, HAS_V, TREAT>(acc, part, L, P, phase, true, dim, c0, j * p.m,
+                                     EntryTreat{p.eps, p.rope_dims, p.log2_base}, static_cast<TX*>(p.out_x) + o,
+                                     HAS_V ? static_cast<TX*>(p.out_v) + o : nullptr);
+}
+
+template <typename TX, typename TZ>
+static hipError_t launch_cache_typed(const CacheParams& p, bool has_v, bool treat, dim3 grid, hipStream_t s) {
+  if (has_v) cache_append_kernel<TX, TZ, true, false><<<grid, 256, 0, s>>>(p);
+  else if (treat) cache_append_kernel<TX, TZ, false, true><<<grid, 256, 0, s>>>(p);
+  else cache_append_kernel<TX, TZ, false, false><<<grid, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_append(const lbca_cache_args& a, hipStream_t stream) {
+  CacheParams p;
+  p.x_new = a.x_new; p.v_new = a.v_new; p.z_new = a.z_new;
+  p.raw_x = a.raw_x; p.raw_v = a.raw_v; p.raw_z = a.raw_z;
+  p.bias = a.bias; p.out_x = a.out_x; p.out_v = a.out_v;
+  p.pos = a.pos; p.raw_pos_base = a.raw_pos_base;
+  p.heads = a.heads; p.dim = a.dim; p.m = a.block; p.W = a.window; p.ring = a.ring; p.entries = a.entries;
+  p.mode = a.mode;
+  p.lanes_per_row = (int)(a.dim / 8);
+  p.log2_lanes = __builtin_ctz((unsigned)p.lanes_per_row);
+  p.eps = a.rmsnorm_eps;
+  p.rope_dims = a.rope_dims;
+  p.log2_base = a.rope_dims > 0 ? log2((double)a.rope_base) : 0.0;
+  const dim3 grid((unsigned)(a.batch * a.heads));
+  const bool has_v = a.v_new != nullptr;
+  const bool treat = a.rmsnorm_eps >= 0.f || a.rope_dims > 0;
+  if (a.x_dtype == LBCA_BF16) {
+    if (a.z_dtype == LBCA_BF16) return launch_cache_typed<bf16_t, bf16_t>(p, has_v, treat, grid, stream);
+    return launch_cache_typed<bf16_t, float>(p, has_v, treat, grid, stream);
+  }
+  if (a.z_dtype == LBCA_BF16) return launch_cache_typed<float, bf16_t>(p, has_v, treat, grid, stream);
+  return launch_cache_typed<float, float>(p, has_v, treat, grid, stream);
+}
+
+}  // namespace lbca

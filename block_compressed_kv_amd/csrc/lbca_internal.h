@@ -9,6 +9,7 @@ namespace lbca {
 // Host validation has already run when these are called; they only pick the
 // kernel instance and launch it on `stream`.
 hipError_t launch_pool(const lbca_pool_args& a, hipStream_t stream);
+hipError_t launch_cache_append(const lbca_cache_args& a, hipStream_t stream);
 
 struct DecodePlan {
   int tile_rows;     // rows per wave tile

@@ -34,6 +34,15 @@ class PoolArgs(ctypes.Structure):
                 ("rope_base", _f32)]
 
 
+class CacheArgs(ctypes.Structure):
+    _fields_ = [("x_new", _vp), ("v_new", _vp), ("z_new", _vp), ("raw_x", _vp), ("raw_v", _vp),
+                ("raw_z", _vp), ("bias", _vp), ("out_x", _vp), ("out_v", _vp), ("pos", _vp),
+                ("raw_pos_base", _vp),
+                ("batch", _i64), ("heads", _i64), ("dim", _i64), ("block", _i64), ("window", _i64),
+                ("ring", _i64), ("entries", _i64), ("mode", _i32), ("x_dtype", _i32), ("z_dtype", _i32),
+                ("rmsnorm_eps", _f32), ("rope_dims", _i32), ("rope_base", _f32)]
+
+
 class DecodeArgs(ctypes.Structure):
     _fields_ = [("q", _vp), ("pooled_k", _vp), ("pooled_v", _vp), ("raw_k", _vp), ("raw_v", _vp),
                 ("pos", _vp), ("raw_pos_base", _vp), ("sel_idx", _vp), ("sink", _vp), ("out", _vp),
@@ -83,6 +92,7 @@ def lib():
         L.lbca_status_string.argtypes = [ctypes.c_int]
         L.lbca_visible_range.argtypes = [_i64, _i64, _i64, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
         L.lbca_pool_blocks.argtypes = [ctypes.POINTER(PoolArgs), _vp]
+        L.lbca_cache_append.argtypes = [ctypes.POINTER(CacheArgs), _vp]
         L.lbca_attend_decode_workspace.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_size_t)]
         L.lbca_attend_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp, ctypes.c_size_t, _vp]
         L.lbca_attend_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
@@ -157,6 +167,25 @@ def pool_blocks(x, z, bias, block, block_begin, block_end, out_x, v=None, out_v=
                  float(rope_base))
     _check(lib().lbca_pool_blocks(ctypes.byref(a), _stream(stream)), "lbca_pool_blocks")
     return out_x if out_v is None else (out_x, out_v)
+
+
+def cache_append(x_new, z_new, raw_x, raw_z, bias, pos, raw_pos_base, block, window, mode, out_x,
+                 v_new=None, raw_v=None, out_v=None, rmsnorm_eps=None, rope_dims=0, rope_base=10000.0,
+                 stream=None):
+    """lbca_cache_append: x_new, v_new, z_new [B,H,d]; raw_* [B,H,2*ring,d] (mirrored ring);
+    bias [H,m,d]; out [B,H,N,d]; pos, raw_pos_base [B] int64 (raw_pos_base is written)."""
+    for t, n, nd in ((x_new, "x_new", 3), (v_new, "v_new", 3), (z_new, "z_new", 3), (raw_x, "raw_x", 4),
+                     (raw_v, "raw_v", 4), (raw_z, "raw_z", 4), (bias, "bias", 3), (out_x, "out_x", 4),
+                     (out_v, "out_v", 4), (pos, "pos", 1), (raw_pos_base, "raw_pos_base", 1)):
+        _need(t, n, nd)
+    B, H, d = x_new.shape
+    if raw_x.shape[2] % 2:
+        raise ValueError("raw buffers hold 2 * ring rows")
+    a = CacheArgs(_p(x_new), _p(v_new), _p(z_new), _p(raw_x), _p(raw_v), _p(raw_z), _p(bias), _p(out_x),
+                  _p(out_v), _p(pos), _p(raw_pos_base), B, H, d, block, window, raw_x.shape[2] // 2,
+                  out_x.shape[2], mode, _dt(x_new), _dt(z_new),
+                  -1.0 if rmsnorm_eps is None else float(rmsnorm_eps), int(rope_dims), float(rope_base))
+    _check(lib().lbca_cache_append(ctypes.byref(a), _stream(stream)), "lbca_cache_append")
 
 
 def _decode_args(q, pooled_k, raw_k, pos, block, window, mode, out, lse, pooled_v, raw_v,

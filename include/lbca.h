@@ -143,6 +143,65 @@ typedef struct lbca_pool_args {
 LBCA_API int lbca_pool_blocks(const lbca_pool_args* a, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Decode-time cache step (mSeek "How LBCA works" steps 1-3: the newest token
+ * joins the raw cache; a block that is complete and, under the EXCLUSIVE rule,
+ * wholly older than the window is pooled into one entry; HCA "What is
+ * implemented" item 1 for the OVERLAP rule, where every complete block is an
+ * entry).
+ *
+ * Raw cache: a mirrored ring of `ring` slots.  Position s is stored in rows
+ * (s mod ring) and (s mod ring) + ring of the raw buffers, so every run of at
+ * most `ring` consecutive positions is one contiguous range of rows.  For
+ * sequence b whose new token sits at t = pos[b] (positions before t appended
+ * by earlier calls, in order) one call:
+ *   1. writes x_new[b], v_new[b], z_new[b] to both rows of position t;
+ *   2. pools block j into entry row j when it becomes visible at t:
+ *      EXCLUSIVE: t+1-W > 0 and (t+1-W) % m == 0, j = (t+1-W)/m - 1;
+ *      OVERLAP:   (t+1) % m == 0,                 j = (t+1)/m - 1;
+ *      exactly as lbca_pool_blocks (bias, treatment), reading the block's
+ *      tokens from the ring; skipped when j >= entries;
+ *   3. writes raw_pos_base[b] = rb - (rb mod ring), rb = raw_begin(t), so that
+ *      lbca_attend_decode with raw rows = 2 * ring and this raw_pos_base reads
+ *      the raw span of t from the ring.
+ * The ring must hold every token a step reads: ring >= W + m (EXCLUSIVE: the
+ * oldest token of the due block is t+1-W-m) or ring >= max(W, m) (OVERLAP).
+ * Sequences with t < 0 are skipped.  Dual (CSA) pooling is not covered.
+ *
+ *   x_new, v_new   [batch, heads, dim]          x_dtype
+ *   z_new          [batch, heads, dim]          z_dtype
+ *   raw_x, raw_v   [batch, heads, 2*ring, dim]  x_dtype
+ *   raw_z          [batch, heads, 2*ring, dim]  z_dtype
+ *   bias           [heads, block, dim] float32
+ *   out_x, out_v   [batch, heads, entries, dim] x_dtype
+ *   pos            [batch] int64 (device);  raw_pos_base [batch] int64 (device, written)
+ * v_new, raw_v and out_v are all NULL for a shared series (x is key and value).
+ * Treatment flags as lbca_pool_blocks (shared series only).
+ * Constraints: dim a power of two in [8, 512].
+ * Errors: INVALID_ARG for a NULL required pointer, a ring below the bound,
+ * bad sizes or mode; UNSUPPORTED for treatment with v.
+ */
+typedef struct lbca_cache_args {
+  const void* x_new;
+  const void* v_new;
+  const void* z_new;
+  void* raw_x;
+  void* raw_v;
+  void* raw_z;
+  const float* bias;
+  void* out_x;
+  void* out_v;
+  const int64_t* pos;
+  int64_t* raw_pos_base;
+  int64_t batch, heads, dim, block, window, ring, entries;
+  int32_t mode, x_dtype, z_dtype;
+  float rmsnorm_eps; /* < 0: off */
+  int32_t rope_dims; /* 0: off */
+  float rope_base;
+} lbca_cache_args;
+
+LBCA_API int lbca_cache_append(const lbca_cache_args* a, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Decode attention: one query per sequence (mSeek "How LBCA works" step 4;
  * HCA "What is implemented" item 2; CSA "What is implemented" item 3).
  *

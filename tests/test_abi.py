@@ -98,6 +98,42 @@ def test_pool_empty_range_is_ok_without_gpu():
     assert _pool(batch=0) == 0
 
 
+def _cache(**kw):
+    a = dict(x_new=FAKE, v_new=FAKE, z_new=FAKE, raw_x=FAKE, raw_v=FAKE, raw_z=FAKE, bias=FAKE, out_x=FAKE,
+             out_v=FAKE, pos=FAKE, raw_pos_base=FAKE, batch=2, heads=8, dim=128, block=64, window=128,
+             ring=192, entries=512, mode=0, x_dtype=1, z_dtype=0, rmsnorm_eps=-1.0, rope_dims=0,
+             rope_base=10000.0)
+    a.update(kw)
+    s = lbca.CacheArgs(**a)
+    return lbca.lib().lbca_cache_append(ctypes.byref(s), None)
+
+
+@fake_ptr
+@pytest.mark.parametrize("kw,code", [
+    (dict(x_new=None), -1), (dict(z_new=None), -1), (dict(raw_x=None), -1), (dict(raw_z=None), -1),
+    (dict(bias=None), -1), (dict(out_x=None), -1), (dict(pos=None), -1), (dict(raw_pos_base=None), -1),
+    (dict(v_new=None), -1), (dict(raw_v=None), -1), (dict(out_v=None), -1),  # values all or none
+    (dict(mode=2), -1), (dict(x_dtype=3), -1), (dict(heads=0), -1), (dict(block=0), -1),
+    (dict(window=0), -1), (dict(entries=-1), -1), (dict(ring=0), -1),
+    (dict(dim=96), -2), (dict(dim=1024), -2), (dict(dim=0), -1),
+    (dict(ring=191), -1),                                   # EXCLUSIVE needs ring >= W + m
+    (dict(mode=1, ring=127), -1),                           # OVERLAP needs ring >= max(W, m)
+    (dict(mode=1, window=16, ring=63), -1),
+    (dict(rmsnorm_eps=1e-6), -2),                           # treatment needs a shared series
+    (dict(v_new=None, raw_v=None, out_v=None, rope_dims=24), -2),
+    (dict(v_new=None, raw_v=None, out_v=None, rope_dims=64, rope_base=0.5), -1),
+    (dict(raw_z=FAKE + 4), -1),                             # misaligned
+])
+def test_cache_validation(kw, code):
+    assert _cache(**kw) == code
+
+
+@fake_ptr
+def test_cache_empty_batch_is_ok_without_gpu():
+    assert _cache(batch=0) == 0
+    assert _cache(batch=0, mode=1, ring=128) == 0
+
+
 def _decode(ws=None, ws_bytes=0, **kw):
     a = dict(q=FAKE, pooled_k=FAKE, pooled_v=FAKE, raw_k=FAKE, raw_v=FAKE, pos=FAKE, raw_pos_base=None,
              sel_idx=None, sink=None, out=FAKE, lse=None, batch=2, q_heads=24, kv_heads=8, dim=128,

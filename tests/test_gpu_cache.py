@@ -1,0 +1,171 @@
+"""GPU parity of the decode-time cache step (lbca_cache_append) through the C ABI.
+
+Each case replays a decode loop token by token over a seeded history, with
+sequences that start at different steps (position < 0 = not started yet), on
+a mirrored raw ring whose size is not a multiple of the block, so blocks
+straddle the mirror.  Checked against what the method fixes for the state after
+tokens 0..t ("mSeek: learned KV-cache compression in a 3B model", "How LBCA
+works" steps 1-5):
+- the ring rows of every position of the raw span of t hold that token, bit
+  for bit, at row (position - raw_pos_base), and raw_pos_base follows the
+  header's rule;
+- every entry that became visible equals, bit for bit, what lbca_pool_blocks
+  writes from the linear history (same pooling code), and the oracle's pooled
+  entry within the bf16 / fp32 tolerance;
+- decode through the ring equals the oracle's attention over the linear
+  history.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_compressed_kv_amd import synth
+from oracle import lbca_oracle as O
+
+from parity_util import check, check_bf16, host, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _dev(d):
+    return {k: v.to(DEV) for k, v in d.items()}
+
+
+def _loop(lib, series, z, bias, m, W, mode, ring, entries, offsets, steps, check_at, v=None, treat=None,
+          on_check=None):
+    """Append tokens 0.. of each sequence (sequence b starts at step offsets[b]); call
+    on_check(step, t_list, raw_x, raw_v, raw_z, rpb, out_x, out_v) at the listed steps."""
+    treat = treat or {}
+    B, H, T, d = series.shape
+    raw_x = torch.full((B, H, 2 * ring, d), float("nan"), dtype=series.dtype, device=DEV)
+    raw_z = torch.full((B, H, 2 * ring, d), float("nan"), dtype=z.dtype, device=DEV)
+    raw_v = None if v is None else torch.full_like(raw_x, float("nan"))
+    out_x = torch.full((B, H, entries, d), 7.0, dtype=series.dtype, device=DEV)
+    out_v = None if v is None else torch.full_like(out_x, 7.0)
+    rpb = torch.full((B,), -123, dtype=torch.int64, device=DEV)
+    bidx = torch.arange(B, device=DEV)
+    for step in range(steps):
+        t_list = [step - o for o in offsets]
+        assert max(t_list) < T, "the history covers every appended position"
+        pos = torch.tensor(t_list, dtype=torch.int64, device=DEV)
+        ti = pos.clamp(min=0)
+        x_new = series[bidx, :, ti].contiguous()
+        z_new = z[bidx, :, ti].contiguous()
+        v_new = None if v is None else v[bidx, :, ti].contiguous()
+        lib.cache_append(x_new, z_new, raw_x, raw_z, bias, pos, rpb, m, W, mode, out_x, v_new=v_new,
+                         raw_v=raw_v, out_v=out_v, **treat)
+        if step in check_at:
+            torch.cuda.synchronize()
+            on_check(step, t_list, raw_x, raw_v, raw_z, rpb, out_x, out_v)
+    return raw_x, raw_v, raw_z, rpb, out_x, out_v
+
+
+def _check_ring(t_list, m, W, mode, ring, raw_x, raw_z, rpb, series, z, raw_v=None, v=None):
+    base = host(rpb).astype(np.int64)
+    for b, t in enumerate(t_list):
+        if t < 0:
+            assert base[b] == -123, "a sequence that has not started keeps its raw base"
+            continue
+        _, rb = O.visible_range(t, m, W, mode)
+        assert base[b] == rb - rb % ring, (b, t, base[b], rb)
+        rows = torch.arange(rb, t + 1, device=DEV) - int(base[b])
+        assert int(rows.min()) >= 0 and int(rows.max()) < 2 * ring
+        assert torch.equal(raw_x[b][:, rows], series[b][:, rb:t + 1]), f"ring x, sequence {b}"
+        assert torch.equal(raw_z[b][:, rows], z[b][:, rb:t + 1]), f"ring z, sequence {b}"
+        if v is not None:
+            assert torch.equal(raw_v[b][:, rows], v[b][:, rb:t + 1]), f"ring v, sequence {b}"
+        # the mirror: both rows of each of the last `ring` positions hold the token
+        lo = max(0, t - ring + 1)
+        slots = torch.arange(lo, t + 1, device=DEV) % ring
+        assert torch.equal(raw_x[b][:, slots], raw_x[b][:, slots + ring])
+
+
+@pytest.mark.parametrize("xdt,zdt,d", [("bf16", "f32", 128), ("f32", "f32", 64)])
+def test_cache_exclusive_gqa(lib, xdt, zdt, d):
+    # LBCA rule, separate K and V, 2 KV heads x 3 query heads each, ragged starts
+    H, Hq, m, W, ring, T = 2, 6, 16, 32, 56, 420
+    offsets = [0, 37, 101]
+    B = len(offsets)
+    L = _dev(synth.lbca_layer(f"cache-excl-{xdt}-{d}", B, Hq, H, T, d, m, xdt, zdt))
+    k, v, z, bias = L["k"], L["v"], L["z"], L["bias"]
+    entries = T // m + 2
+    steps = 400                       # sequence 0 ends at t = 399, within its history
+    q = synth.normal((B, Hq, d), synth.seed_of("cache-excl-q", xdt, d), dtype=xdt, device=DEV)
+    checked = []
+
+    def on_check(step, t_list, raw_x, raw_v, raw_z, rpb, out_x, out_v):
+        _check_ring(t_list, m, W, O.EXCLUSIVE, ring, raw_x, raw_z, rpb, k, z, raw_v, v)
+        pos = torch.tensor(t_list, dtype=torch.int64, device=DEV)
+        o, lse = lib.attend_decode(q, out_x, raw_x, pos, m, W, O.EXCLUSIVE, pooled_v=out_v, raw_v=raw_v,
+                                   raw_pos_base=rpb)
+        live = [b for b, t in enumerate(t_list) if t >= 0]
+        n_max = max(O.visible_range(t_list[b], m, W, O.EXCLUSIVE)[0] for b in live)
+        rk, rv = O.pool_single(host(k), host(z), host(bias), m, 0, max(n_max, 1), values=host(v))
+        ro, rl = O.attend_decode(host(q)[live], rk[live], rv[live], host(k)[live], host(v)[live],
+                                 [t_list[b] for b in live], m, W, O.EXCLUSIVE, 1 / math.sqrt(d))
+        check(xdt, host(o)[live], ro, f"decode through the ring at step {step}")
+        check(xdt, host(lse)[live][..., None], rl[..., None], "lse")
+        checked.append(step)
+
+    check_at = {0, 1, 47, 48, 63, 64, 65, 130, 200, 311, 312, steps - 1}
+    say(f"cache EXCLUSIVE {xdt}/{zdt} d={d}: {steps} steps")
+    raw_x, raw_v, raw_z, rpb, out_x, out_v = _loop(lib, k, z, bias, m, W, O.EXCLUSIVE, ring, entries, offsets,
+                                                   steps, check_at, v=v, on_check=on_check)
+    assert len(checked) == len(check_at)
+    # every entry that became visible: bitwise the linear-history pooling, and the oracle's
+    t_end = [steps - 1 - o for o in offsets]
+    ref_x = torch.full_like(out_x, 7.0)
+    ref_v = torch.full_like(out_v, 7.0)
+    lib.pool_blocks(k, z, bias, m, 0, T // m, ref_x, v=v, out_v=ref_v)
+    rk, rv = O.pool_single(host(k), host(z), host(bias), m, 0, T // m, values=host(v))
+    for b, t in enumerate(t_end):
+        n_p, _ = O.visible_range(t, m, W, O.EXCLUSIVE)
+        assert torch.equal(out_x[b, :, :n_p], ref_x[b, :, :n_p]) and torch.equal(out_v[b, :, :n_p], ref_v[b, :, :n_p])
+        assert (out_x[b, :, n_p:] == 7.0).all(), "entries not yet visible are untouched"
+        check(xdt, host(out_x[b, :, :n_p]), rk[b, :, :n_p], f"entries of sequence {b}")
+        check(xdt, host(out_v[b, :, :n_p]), rv[b, :, :n_p], f"value entries of sequence {b}")
+
+
+@pytest.mark.parametrize("Hq", [16, 32])
+def test_cache_overlap_hca_treated(lib, Hq):
+    # HCA rule: shared 512-dim series, RMSNorm + RoPE on entries, sink; the due block ends
+    # with the token appended in the same call; 32 heads take the wide decode path
+    B, d, m, W, ring, T = 2, 512, 8, 16, 20, 170
+    offsets = [0, 13]
+    H = _dev(synth.hca_layer(f"cache-hca-{Hq}", B, Hq, T, d, m))
+    c, z, bias, q, sink = H["c"], H["z"], H["bias"], H["q"], H["sink"]
+    treat = dict(rmsnorm_eps=1e-6, rope_dims=64)
+    entries = T // m + 1
+    steps = 160
+    checked = []
+
+    def on_check(step, t_list, raw_x, raw_v, raw_z, rpb, out_x, out_v):
+        _check_ring(t_list, m, W, O.OVERLAP, ring, raw_x, raw_z, rpb, c, z)
+        pos = torch.tensor(t_list, dtype=torch.int64, device=DEV)
+        o, lse = lib.attend_decode(q, out_x, raw_x, pos, m, W, O.OVERLAP, raw_pos_base=rpb, sink=sink, **treat)
+        live = [b for b, t in enumerate(t_list) if t >= 0]
+        n_max = max(O.visible_range(t_list[b], m, W, O.OVERLAP)[0] for b in live)
+        pooled = O.pool_single(host(c), host(z), host(bias), m, 0, max(n_max, 1))
+        ro, rl = O.attend_decode(host(q)[live], pooled[live], None, host(c)[live], None,
+                                 [t_list[b] for b in live], m, W, O.OVERLAP, 1 / math.sqrt(d),
+                                 sink=host(sink), **treat)
+        check_bf16(host(o)[live], ro, f"treated decode through the ring at step {step}")
+        check_bf16(host(lse)[live], rl, "lse")
+        checked.append(step)
+
+    check_at = {0, 7, 8, 19, 20, 21, 40, 99, steps - 1}
+    say(f"cache OVERLAP HCA Hq={Hq}: {steps} steps")
+    raw_x, _, raw_z, rpb, out_x, _ = _loop(lib, c, z, bias, m, W, O.OVERLAP, ring, entries, offsets, steps,
+                                           check_at, treat=treat, on_check=on_check)
+    assert len(checked) == len(check_at)
+    ref = torch.full_like(out_x, 7.0)
+    lib.pool_blocks(c, z, bias, m, 0, T // m, ref, **treat)
+    pooled = O.pool_single(host(c), host(z), host(bias), m, 0, T // m)
+    treated = O.rope(O.rmsnorm(pooled, 1e-6), (np.arange(T // m) * m)[None, None], 64, 10000.0)
+    for b, o in enumerate(offsets):
+        n_p, _ = O.visible_range(steps - 1 - o, m, W, O.OVERLAP)
+        assert torch.equal(out_x[b, :, :n_p], ref[b, :, :n_p]), f"entries of sequence {b}"
+        check_bf16(host(out_x[b, :, :n_p]), treated[b, :, :n_p], f"treated entries of sequence {b}")
