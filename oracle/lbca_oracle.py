@@ -150,6 +150,51 @@ def pool_single(series, logits, bias, m, block_begin, block_end, values=None):
     return pk, (w * vb).sum(axis=-2)
 
 
+def pool_single_backward(series, logits, bias, m, block_begin, block_end, grad_out, values=None,
+                         grad_values=None):
+    """Gradients of single-series pooling (``pool_single``) of blocks
+    [block_begin, block_end) for upstream gradients ``grad_out`` (and
+    ``grad_values``) of the pooled rows, [..., n, d].
+
+    The chain rule through the definition ([mSeek] "How LBCA works", steps 2-3:
+    a = z + bias, w = softmax over the block's tokens per channel, out = sum w x):
+      d series[s] = w[s] * g                              (s in block j, g = grad_out[j])
+      d values[s] = w[s] * gv
+      d logits[s] = w[s] * (g * (x[s] - out[j]) + gv * (v[s] - vout[j]))
+      d bias[i]   = d logits of token j*m + i, summed over blocks and over the
+                    leading axes the bias broadcasts along.
+    Token rows outside the blocks get zero gradient.  Returns (d_series,
+    d_values or None, d_logits, d_bias) in float64, shaped like the inputs.
+    """
+    x, z, b = _f64(series), _f64(logits), _f64(bias)
+    g = _f64(grad_out)
+    n = block_end - block_begin
+    lead, d = x.shape[:-2], x.shape[-1]
+    dx, dz = np.zeros_like(x), np.zeros_like(z)
+    v = None if values is None else _f64(values)
+    dv = None if values is None else np.zeros_like(v)
+    if n <= 0:
+        return dx, dv, dz, np.zeros_like(b)
+    lo, hi = block_begin * m, block_end * m
+    xb = x[..., lo:hi, :].reshape(lead + (n, m, d))
+    w = pool_weights(z[..., lo:hi, :].reshape(lead + (n, m, d)), b[..., None, :, :])
+    out = (w * xb).sum(axis=-2)                          # [..., n, d]
+    gb = g[..., None, :]                                 # one upstream row per block
+    dx[..., lo:hi, :] = (w * gb).reshape(lead + (n * m, d))
+    da = w * gb * (xb - out[..., None, :])
+    if v is not None:
+        vb = v[..., lo:hi, :].reshape(lead + (n, m, d))
+        vout = (w * vb).sum(axis=-2)
+        gvb = _f64(grad_values)[..., None, :]
+        dv[..., lo:hi, :] = (w * gvb).reshape(lead + (n * m, d))
+        da = da + w * gvb * (vb - vout[..., None, :])
+    dz[..., lo:hi, :] = da.reshape(lead + (n * m, d))
+    db = da.sum(axis=-3)                                 # over blocks: [..., m, d]
+    while db.ndim > b.ndim:                              # over axes the bias broadcasts along
+        db = db.sum(axis=0)
+    return dx, dv, dz, db
+
+
 def pool_dual(ca, za, bias_a, cb, zb, bias_b, m, entry_begin, entry_end):
     """CSA dual overlapped pooling ([CSA] "What is implemented", first item).
 
