@@ -18,6 +18,7 @@ from stored counter passes), the oracle on the host cores (cpu_baseline), batch
 1 and 4, the step with the due block pooled first (a block leaves the window
 every 64 steps), an incremental decode loop (64 steps of lbca_cache_append into a
 mirrored raw ring, the due block pooled on its step, then decode from the ring),
+the pooling gradients of one layer's history (GB/s),
 pooling GB/s for the whole history, chunked prefill (16K
 context in 2048-token chunks) TFLOP/s, HCA decode at 1M context (batch 4, 64
 query heads x 512, pooling GB/s of the whole history) and CSA at 128K (batch 2:
@@ -294,6 +295,39 @@ def run_incremental(B, reps):
                         f"mirrored raw ring of {RING} slots"}
 
 
+def run_pool_backward(B, reps):
+    """Gradients of the pooling of one layer's 509-block history at batch 16 (K, V bf16,
+    logits fp32): reads x, v, z and writes dx, dv, dz once per token channel (16 B) plus
+    the upstream rows; the bias gradient is reduced in a second small launch."""
+    dev = "cuda"
+    tag = ("bench-pool-grad", B)
+    L = synth.lbca_layer(tag, B, HQ, HKV, RAW0, D, M, "bf16", "f32", device=dev)
+    n = N_POOLED - 1
+    gx = synth.normal((B, HKV, n, D), synth.seed_of(*tag, "gx"), dtype="bf16", device=dev)
+    gv = synth.normal((B, HKV, n, D), synth.seed_of(*tag, "gv"), dtype="bf16", device=dev)
+    dx, dv, dz = torch.empty_like(L["k"]), torch.empty_like(L["v"]), torch.empty_like(L["z"])
+    dbias = torch.empty_like(L["bias"])
+    nb = lbca.pool_blocks_backward_workspace_bytes(L["k"], L["z"], L["bias"], M, 0, n, gx, v=L["v"], grad_v=gv)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    call = lambda: lbca.pool_blocks_backward(L["k"], L["z"], L["bias"], M, 0, n, gx, v=L["v"], grad_v=gv,
+                                             dx=dx, dv=dv, dz=dz, dbias=dbias, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    ref = dbias.clone()
+    g = capture(call)
+    g.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(dbias, ref):
+        raise RuntimeError("graph replay of the pooling backward differs from the eager call")
+    ms = time_graph(g, reps)
+    tok = B * HKV * n * M * D
+    nbytes = tok * (2 + 2 + 4) * 2 + 2 * B * HKV * n * D * 2 + HKV * M * D * 4
+    del L, dx, dv, dz
+    return {"ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes, "workspace_bytes": nb,
+            "workload": f"batch {B}, 8 KV heads, {n} blocks of {M} tokens, d={D}: gradients of K, V "
+                        f"(bf16), logits (fp32) and bias"}
+
+
 # ---------------------------------------------------------------------------
 # chunked prefill, 16K context
 # ---------------------------------------------------------------------------
@@ -516,6 +550,7 @@ def run_ceilings():
         raise RuntimeError(f"{B.CEIL_LIB} is missing: build it with `python -m block_compressed_kv_amd.build`")
     L = ctypes.CDLL(B.CEIL_LIB)
     L.ceil_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.ceil_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
     L.ceil_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     L.ceil_empty.argtypes = [ctypes.c_void_p]
     stream = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -530,7 +565,10 @@ def run_ceilings():
     big = torch.zeros(1 << 30, dtype=torch.uint8, device="cuda")
     g = capture(lambda: ok(L.ceil_read(big.data_ptr(), big.numel(), out.data_ptr(), grid, stream())))
     res["hbm_read_GBps"] = big.numel() / (time_graph(g, 20) * 1e-3) / 1e9
-    del big, g
+    dst = torch.empty_like(big)
+    g = capture(lambda: ok(L.ceil_copy(big.data_ptr(), dst.data_ptr(), big.numel(), grid, stream())))
+    res["hbm_copy_GBps"] = 2 * big.numel() / (time_graph(g, 20) * 1e-3) / 1e9  # bytes read + written
+    del big, dst, g
     nb = decode_bytes_per_seq_layer() * 16
     bufs = [torch.zeros(nb, dtype=torch.uint8, device="cuda") for _ in range(LAYERS)]
     for grid_dec in (256, 1024):
@@ -543,7 +581,8 @@ def run_ceilings():
     res["mfma_bf16_TFLOPs"] = mg * 4 * iters * 4 * 32768 / (time_graph(g, 5) * 1e-3) / 1e12
     g = capture(lambda: [ok(L.ceil_empty(stream())) for _ in range(LAYERS)])
     res["empty_launch_us"] = time_graph(g, 200) * 1e3 / LAYERS
-    res["note"] = ("hbm_read: 2048 workgroups streaming 1 GiB; read_decode_bytes_one_launch: one launch reading "
+    res["note"] = ("hbm_read: 2048 workgroups streaming 1 GiB; hbm_copy: the same workgroups copying 1 GiB "
+                   "(bytes read + written); read_decode_bytes_one_launch: one launch reading "
                    f"{nb} B (the batch-16 decode's algorithmic bytes), 14 distinct buffers per graph replay; "
                    "mfma: 1024 workgroups x 4 waves x 4 chains of v_mfma_f32_32x32x16_bf16; "
                    "empty_launch: 14 empty kernels per graph replay")
@@ -664,6 +703,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the host oracle timing")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-incremental", action="store_true", help="skip the cache-step decode loop")
+    ap.add_argument("--no-backward", action="store_true", help="skip the pooling-gradient line")
     ap.add_argument("--no-small-batch", action="store_true")
     ap.add_argument("--no-mqa", action="store_true", help="skip the HCA 1M and CSA 128K lines")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured-ceiling probes")
@@ -728,6 +768,11 @@ def main():
             del ls
             torch.cuda.empty_cache()
 
+    if not args.no_backward:
+        log("[bench] pooling gradients of a 32K history (batch 16)")
+        extra["pool_backward_32k"] = run_pool_backward(B, max(3, args.steps // 40))
+        torch.cuda.empty_cache()
+
     if not args.no_incremental:
         log("[bench] incremental decode loop 32K (cache step + decode, 64 steps)")
         extra["incremental_32k"] = run_incremental(B, max(5, args.steps // 10))
@@ -759,6 +804,8 @@ def main():
         ce["decode_GBps_vs_stream_read"] = achieved / ce["hbm_read_GBps"]
         if "prefill" in extra:
             ce["prefill_vs_mfma_loop"] = extra["prefill"]["tflops"] / ce["mfma_bf16_TFLOPs"]
+        if "pool_backward_32k" in extra:
+            ce["pool_backward_vs_copy"] = extra["pool_backward_32k"]["GBps"] / ce["hbm_copy_GBps"]
         extra["ceilings"] = ce
         torch.cuda.empty_cache()
 

@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblbca.so")
-SOURCES = ["api.cpp", "pool.hip", "cache.hip", "decode.hip", "decode_wide.hip", "attend_f32.hip", "prefill.hip", "index.hip"]
+SOURCES = ["api.cpp", "pool.hip", "pool_grad.hip", "cache.hip", "decode.hip", "decode_wide.hip", "attend_f32.hip", "prefill.hip", "index.hip"]
 # measured-ceiling probes for the benchmark report (a library of their own, not the attention path)
 CEIL_LIB = os.path.join(PKG, "libceilings.so")
 CEIL_SOURCES = ["ceilings.hip"]

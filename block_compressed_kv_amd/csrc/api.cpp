@@ -105,6 +105,53 @@ int lbca_pool_blocks(const lbca_pool_args* a, void* stream) {
 }
 
 // ---------------------------------------------------------------------------
+static int validate_pool_grad(const lbca_pool_grad_args* a) {
+  if (!a || !a->x || !a->z || !a->bias || !a->grad_x || !a->dx || !a->dz || !a->dbias)
+    return LBCA_ERR_INVALID_ARG;
+  const bool has_v = a->v != nullptr;
+  if ((a->grad_v != nullptr) != has_v || (a->dv != nullptr) != has_v) return LBCA_ERR_INVALID_ARG;
+  if (!is_dtype(a->x_dtype) || !is_dtype(a->z_dtype)) return LBCA_ERR_INVALID_ARG;
+  if (a->batch < 0 || a->heads < 1 || a->tokens < 0 || a->block < 1 || a->entries < 0)
+    return LBCA_ERR_INVALID_ARG;
+  if (!pow2(a->dim) || a->dim < 8) return a->dim > 0 ? LBCA_ERR_UNSUPPORTED : LBCA_ERR_INVALID_ARG;
+  if (a->dim > 512) return LBCA_ERR_UNSUPPORTED;
+  if (a->block_begin < 0 || a->block_end < a->block_begin || a->block_end > a->entries)
+    return LBCA_ERR_INVALID_ARG;
+  if (!sane_product({a->batch, a->heads, a->tokens, a->dim}) ||
+      !sane_product({a->batch, a->heads, a->entries, a->dim}) ||
+      !sane_product({a->heads, a->block, a->dim}) || a->block_end > kMaxElems / a->block)
+    return LBCA_ERR_INVALID_ARG;
+  if (a->block * a->dim > 8192 || a->heads > 65535) return LBCA_ERR_UNSUPPORTED;  // four tokens per lane
+  if (!aligned16(a->x) || !aligned16(a->v) || !aligned16(a->z) || !aligned16(a->bias) ||
+      !aligned16(a->grad_x) || !aligned16(a->grad_v) || !aligned16(a->dx) || !aligned16(a->dv) ||
+      !aligned16(a->dz) || !aligned16(a->dbias))
+    return LBCA_ERR_INVALID_ARG;
+  if (a->block_end > a->block_begin) {
+    const int64_t lo = a->block_begin * a->block - a->pos_base;
+    const int64_t hi = a->block_end * a->block - a->pos_base;
+    if (lo < 0 || hi > a->tokens) return LBCA_ERR_INVALID_ARG;
+  }
+  return LBCA_OK;
+}
+
+int lbca_pool_blocks_backward_workspace(const lbca_pool_grad_args* a, size_t* bytes) {
+  if (!bytes) return LBCA_ERR_INVALID_ARG;
+  const int st = validate_pool_grad(a);
+  if (st != LBCA_OK) return st;
+  *bytes = lbca::pool_grad_workspace_bytes(*a);
+  return LBCA_OK;
+}
+
+int lbca_pool_blocks_backward(const lbca_pool_grad_args* a, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  const int st = validate_pool_grad(a);
+  if (st != LBCA_OK) return st;
+  const size_t need = lbca::pool_grad_workspace_bytes(*a);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return LBCA_ERR_WORKSPACE;
+  return hip_status(lbca::launch_pool_grad(*a, workspace, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
 int lbca_cache_append(const lbca_cache_args* a, void* stream) {
   if (!a || !a->x_new || !a->z_new || !a->raw_x || !a->raw_z || !a->bias || !a->out_x || !a->pos ||
       !a->raw_pos_base)

@@ -1,6 +1,6 @@
 // Probes of this part's measured ceilings, reported beside the kernels'
-// roofline fractions: a streaming HBM read, a bf16 MFMA loop and an empty
-// kernel (the launch floor).  Built into libceilings.so, a library of its own
+// roofline fractions: a streaming HBM read, a streaming copy (read and
+// write), a bf16 MFMA loop and an empty kernel (the launch floor).  Built into libceilings.so, a library of its own
 // that only the benchmark loads; nothing here is part of the attention path.
 //
 // Each entry point checks its sizes and returns a hipError_t value (0 = success).
@@ -32,6 +32,22 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4_t* __restrict__ s
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+// Grid-stride copy of n16 16-byte vectors, eight loads in flight per thread
+// before their stores.
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst,
+                                                   int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = __builtin_nontemporal_load(src + i + j * stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) __builtin_nontemporal_store(v[j], dst + i + j * stride);
+  }
+  for (; i < n16; i += stride) dst[i] = src[i];
 }
 
 // Four independent chains of v_mfma_f32_32x32x16_bf16 per wave (32768 flops
@@ -68,6 +84,15 @@ __attribute__((visibility("default"))) int ceil_read(const void* src, size_t byt
   read_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<const u32x4_t*>(src),
                                                                   (int64_t)(bytes / 16),
                                                                   static_cast<uint32_t*>(out));
+  return (int)hipGetLastError();
+}
+
+// Copies `bytes` (a multiple of 16) from src to dst with `grid` workgroups of 256 threads.
+__attribute__((visibility("default"))) int ceil_copy(const void* src, void* dst, size_t bytes, int grid,
+                                                     void* stream) {
+  if (!src || !dst || grid < 1 || bytes % 16 != 0) return (int)hipErrorInvalidValue;
+  copy_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<const u32x4_t*>(src),
+                                                                  static_cast<u32x4_t*>(dst), (int64_t)(bytes / 16));
   return (int)hipGetLastError();
 }
 

@@ -10,6 +10,8 @@ namespace lbca {
 // kernel instance and launch it on `stream`.
 hipError_t launch_pool(const lbca_pool_args& a, hipStream_t stream);
 hipError_t launch_cache_append(const lbca_cache_args& a, hipStream_t stream);
+size_t pool_grad_workspace_bytes(const lbca_pool_grad_args& a);
+hipError_t launch_pool_grad(const lbca_pool_grad_args& a, void* ws, hipStream_t stream);
 
 struct DecodePlan {
   int tile_rows;     // rows per wave tile

@@ -1,0 +1,385 @@
+// Gradients of single-series block pooling (key, value, logit and bias rows).
+//
+// Method: "mSeek: learned KV-cache compression in a 3B model", section "How LBCA
+// works" (steps 2-3: per channel, w = softmax over the block's tokens of
+// z + bias, entry = sum w x).  The chain rule through that definition gives,
+// for token s of block j with upstream gradient rows g (key) and gv (value):
+//   dx[s] = w[s] g,   dv[s] = w[s] gv,
+//   dz[s] = w[s] (g (x[s] - entry_x) + gv (v[s] - entry_v)),
+//   dbias[h, s - j m] = dz[s] summed over sequences and blocks.
+//
+// Design: one 256-thread workgroup per (head, chunk of consecutive blocks of
+// that head's (sequence, block) list), so every block of a workgroup shares
+// the bias rows, staged once in LDS.  L = dim/8 lanes cover a token row (8
+// channels per lane, 16-byte vectors); the 256/L lane groups take token
+// phases, at most four tokens per lane, held in registers as loaded, and the
+// next block's rows are requested while the current one is worked.  Per block
+// each lane's online-softmax state (channel max, weight sum, weighted key and
+// value sums) is merged over the phases in a fixed order (lane exchanges
+// inside a wave, the four waves' states through LDS), so the entry is
+// recomputed in fp32 (not read back rounded), and each lane writes its
+// tokens' gradients and adds their logit gradients to its bias partial.  Workgroup partials of the bias gradient go
+// to the workspace; a second kernel sums them per (head, offset, channel) in
+// chunk order, so every output is bitwise reproducible.  HBM-bound: per token
+// channel it reads x, v, z and writes dx, dv, dz once.
+#include "lbca_internal.h"
+#include "device_util.h"
+
+namespace lbca {
+
+struct PoolGradParams {
+  const void* x;
+  const void* v;
+  const void* z;
+  const float* bias;
+  const void* gx;
+  const void* gv;
+  void* dx;
+  void* dv;
+  void* dz;
+  float* dbias;
+  float* part;  // [heads][chunks][m][dim] bias-gradient partials
+  int64_t batch, heads, tokens, dim, m, entries, block_begin, n_blocks, pos_base;
+  int chunks, per_chunk;  // workgroups per head, blocks per workgroup
+  int log2_lanes;
+};
+
+constexpr int kGradNT = 256;  // threads per workgroup (4 waves)
+constexpr int kGradNW = kGradNT / 64;
+constexpr int kGradTPL = 4;    // tokens per lane at most: m * dim <= kGradNT * 8 * kGradTPL = 8192
+
+// Raw rows of one block for this lane: up to kGradTPL tokens of 8 channels,
+// kept packed as loaded (16-byte vectors) so that the next block's loads can
+// be in flight while the current block is worked.
+template <typename TX, typename TZ, bool HAS_V>
+struct BlockRows {
+  static constexpr int NX = (int)(sizeof(TX) * 8 / 16), NZ = (int)(sizeof(TZ) * 8 / 16);
+  uint4 x[kGradTPL][NX], v[kGradTPL][HAS_V ? NX : 1], z[kGradTPL][NZ];
+  __device__ __forceinline__ void load(const TX* xb, const TX* vb, const TZ* zb, int64_t stride, const bool* has) {
+#pragma unroll
+    for (int k = 0; k < kGradTPL; ++k) {
+      if (!has[k]) continue;
+#pragma unroll
+      for (int i = 0; i < NX; ++i) {
+        x[k][i] = reinterpret_cast<const uint4*>(xb + k * stride)[i];
+        if constexpr (HAS_V) v[k][i] = reinterpret_cast<const uint4*>(vb + k * stride)[i];
+      }
+#pragma unroll
+      for (int i = 0; i < NZ; ++i) z[k][i] = reinterpret_cast<const uint4*>(zb + k * stride)[i];
+    }
+  }
+};
+
+template <typename T, int N>
+__device__ __forceinline__ void unpack_row(const uint4 (&u)[N], float* f) {
+  if constexpr (sizeof(T) == 2) {
+    f[0] = lo_bf16(u[0].x); f[1] = hi_bf16(u[0].x); f[2] = lo_bf16(u[0].y); f[3] = hi_bf16(u[0].y);
+    f[4] = lo_bf16(u[0].z); f[5] = hi_bf16(u[0].z); f[6] = lo_bf16(u[0].w); f[7] = hi_bf16(u[0].w);
+  } else {
+    f[0] = __uint_as_float(u[0].x); f[1] = __uint_as_float(u[0].y);
+    f[2] = __uint_as_float(u[0].z); f[3] = __uint_as_float(u[0].w);
+    f[4] = __uint_as_float(u[1].x); f[5] = __uint_as_float(u[1].y);
+    f[6] = __uint_as_float(u[1].z); f[7] = __uint_as_float(u[1].w);
+  }
+}
+
+// Per channel online-softmax state of a set of tokens: max mx, sum l of
+// 2^(a - mx), and the 2^(a - mx)-weighted sums of keys and values.
+struct GradState {
+  float mx[8], l[8], sx[8], sv[8];
+};
+
+// Combines `lo` (the lower phases) and `hi` into `lo` (two empty states stay empty).
+__device__ __forceinline__ void combine_state(GradState& lo, const GradState& hi) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float nm = fmaxf(lo.mx[c], hi.mx[c]);
+    const bool none = nm == kNegInf;
+    const float a = none ? 0.f : exp2f(lo.mx[c] - nm), b = none ? 0.f : exp2f(hi.mx[c] - nm);
+    lo.l[c] = lo.l[c] * a + hi.l[c] * b;
+    lo.sx[c] = lo.sx[c] * a + hi.sx[c] * b;
+    lo.sv[c] = lo.sv[c] * a + hi.sv[c] * b;
+    lo.mx[c] = nm;
+  }
+}
+
+// Merges the states of every phase of the block into every lane, in a fixed
+// order: lane exchanges inside a wave (lanes lane ^ L, ^2L, ..), then the
+// waves' states through LDS, read and combined in wave order by every lane
+// (a workgroup of eight waves, two tokens per lane, measured slower: 4.0
+// against 3.0 ms for a 32K history at batch 16).
+// Called by every thread of the workgroup.
+__device__ __forceinline__ void merge_phases(GradState& st, float (*red)[64][32], int L, int li) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int off = L; off < 64; off <<= 1) {
+    GradState lo, hi;
+    if (off == 16 || off == 32) {
+      // a swap of a register with itself: lower row's (half's) value first on both lanes
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float* src[4] = {&st.mx[c], &st.l[c], &st.sx[c], &st.sv[c]};
+        float* dl[4] = {&lo.mx[c], &lo.l[c], &lo.sx[c], &lo.sv[c]};
+        float* dh[4] = {&hi.mx[c], &hi.l[c], &hi.sx[c], &hi.sv[c]};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t u = __float_as_uint(*src[q]);
+          const auto r = off == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                                   : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+          *dl[q] = __uint_as_float(r[0]);
+          *dh[q] = __uint_as_float(r[1]);
+        }
+      }
+    } else {
+      const bool lower = (lane & off) == 0;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float om = __shfl_xor(st.mx[c], off, 64), ol = __shfl_xor(st.l[c], off, 64);
+        const float ox = __shfl_xor(st.sx[c], off, 64), ov = __shfl_xor(st.sv[c], off, 64);
+        lo.mx[c] = lower ? st.mx[c] : om; hi.mx[c] = lower ? om : st.mx[c];
+        lo.l[c] = lower ? st.l[c] : ol;   hi.l[c] = lower ? ol : st.l[c];
+        lo.sx[c] = lower ? st.sx[c] : ox; hi.sx[c] = lower ? ox : st.sx[c];
+        lo.sv[c] = lower ? st.sv[c] : ov; hi.sv[c] = lower ? ov : st.sv[c];
+      }
+    }
+    combine_state(lo, hi);
+    st = lo;
+  }
+  if (lane < L) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      red[wave][li][c] = st.mx[c];
+      red[wave][li][8 + c] = st.l[c];
+      red[wave][li][16 + c] = st.sx[c];
+      red[wave][li][24 + c] = st.sv[c];
+    }
+  }
+  __syncthreads();
+  GradState acc;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    acc.mx[c] = red[0][li][c];
+    acc.l[c] = red[0][li][8 + c];
+    acc.sx[c] = red[0][li][16 + c];
+    acc.sv[c] = red[0][li][24 + c];
+  }
+#pragma unroll
+  for (int w = 1; w < kGradNW; ++w) {
+    GradState t;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      t.mx[c] = red[w][li][c];
+      t.l[c] = red[w][li][8 + c];
+      t.sx[c] = red[w][li][16 + c];
+      t.sv[c] = red[w][li][24 + c];
+    }
+    combine_state(acc, t);
+  }
+  __syncthreads();  // `red` free for the next block
+  st = acc;
+}
+
+template <typename TX, typename TZ, bool HAS_V>
+__global__ __launch_bounds__(kGradNT) void pool_grad_kernel(PoolGradParams p) {
+  __shared__ float red[kGradNW][64][32];
+  __shared__ __attribute__((aligned(16))) float s_bias[8192];  // this head's bias rows, m * dim <= 8192
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int L = 1 << p.log2_lanes;
+  const int li = lane & (L - 1);
+  const int phase = tid >> p.log2_lanes;
+  const int P = kGradNT >> p.log2_lanes;
+  const int h = (int)blockIdx.y, chunk = (int)blockIdx.x;
+  const int64_t dim = p.dim, m = p.m;
+  const int64_t c0 = (int64_t)li * 8;
+  const int64_t list_n = p.batch * p.n_blocks;  // (sequence, block) pairs of this head
+  const int64_t k0 = (int64_t)chunk * p.per_chunk;
+  const int64_t k1 = k0 + p.per_chunk < list_n ? k0 + p.per_chunk : list_n;
+
+  bool has[kGradTPL];  // this lane's tokens of a block: offsets phase + P k, present when < m
+#pragma unroll
+  for (int k = 0; k < kGradTPL; ++k) has[k] = phase + (int64_t)P * k < m;
+  const int64_t tstride = (int64_t)P * dim;  // elements between this lane's tokens
+  auto rows_of = [&](int64_t kk, const TX*& xb, const TX*& vb, const TZ*& zb, int64_t& bh, int64_t& j) {
+    const int64_t b = kk / p.n_blocks;
+    j = p.block_begin + kk % p.n_blocks;
+    bh = b * p.heads + h;
+    const int64_t o = (bh * p.tokens + j * m - p.pos_base + phase) * dim + c0;
+    xb = static_cast<const TX*>(p.x) + o;
+    vb = static_cast<const TX*>(p.v) + o;
+    zb = static_cast<const TZ*>(p.z) + o;
+  };
+  BlockRows<TX, TZ, HAS_V> cur;
+  {
+    const TX *xb, *vb;
+    const TZ* zb;
+    int64_t bh, j;
+    rows_of(k0, xb, vb, zb, bh, j);
+    cur.load(xb, vb, zb, tstride, has);
+  }
+  for (int64_t e = tid * 4; e < m * dim; e += kGradNT * 4)
+    *reinterpret_cast<float4*>(&s_bias[e]) = *reinterpret_cast<const float4*>(p.bias + h * m * dim + e);
+  __syncthreads();
+
+  float db[kGradTPL][8];
+#pragma unroll
+  for (int k = 0; k < kGradTPL; ++k)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) db[k][c] = 0.f;
+
+  for (int64_t kk = k0; kk < k1; ++kk) {
+    const TX *xb, *vb;
+    const TZ* zb;
+    int64_t bh, j;
+    rows_of(kk, xb, vb, zb, bh, j);
+    const int64_t eo = (bh * p.entries + j) * dim + c0;
+    float g[8], gvv[8];
+    load8(static_cast<const TX*>(p.gx) + eo, g);
+    if constexpr (HAS_V) load8(static_cast<const TX*>(p.gv) + eo, gvv);
+    // logits (log2 units) of this lane's tokens, then the next block's rows go out
+    float a[kGradTPL][8];
+#pragma unroll
+    for (int k = 0; k < kGradTPL; ++k) {
+      if (!has[k]) continue;
+      float zz[8];
+      unpack_row<TZ>(cur.z[k], zz);
+      const float* br = &s_bias[(phase + P * k) * dim + c0];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) a[k][c] = (zz[c] + br[c]) * kLog2e;
+    }
+    BlockRows<TX, TZ, HAS_V> nxt;
+    if (kk + 1 < k1) {
+      const TX *xn, *vn;
+      const TZ* zn;
+      int64_t bhn, jn;
+      rows_of(kk + 1, xn, vn, zn, bhn, jn);
+      nxt.load(xn, vn, zn, tstride, has);
+    }
+    // this lane's state, then the block's
+    GradState st;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int k = 0; k < kGradTPL; ++k)
+        if (has[k]) mx = fmaxf(mx, a[k][c]);
+      st.mx[c] = mx;
+      st.l[c] = st.sx[c] = st.sv[c] = 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kGradTPL; ++k) {
+      if (!has[k]) continue;
+      float xs[8], vs[8];
+      unpack_row<TX>(cur.x[k], xs);
+      if constexpr (HAS_V) unpack_row<TX>(cur.v[k], vs);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float w = exp2f(a[k][c] - st.mx[c]);
+        st.l[c] += w;
+        st.sx[c] = fmaf(w, xs[c], st.sx[c]);
+        if constexpr (HAS_V) st.sv[c] = fmaf(w, vs[c], st.sv[c]);
+      }
+    }
+    merge_phases(st, red, L, li);
+    float inv[8], ex[8], ev[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      inv[c] = 1.f / st.l[c];
+      ex[c] = st.sx[c] * inv[c];
+      ev[c] = st.sv[c] * inv[c];
+    }
+    // gradients of this lane's tokens
+#pragma unroll
+    for (int k = 0; k < kGradTPL; ++k) {
+      if (!has[k]) continue;
+      float xs[8], vs[8];
+      unpack_row<TX>(cur.x[k], xs);
+      if constexpr (HAS_V) unpack_row<TX>(cur.v[k], vs);
+      float ox[8], ov[8], oz[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float w = exp2f(a[k][c] - st.mx[c]) * inv[c];
+        ox[c] = w * g[c];
+        float da = g[c] * (xs[c] - ex[c]);
+        if constexpr (HAS_V) {
+          ov[c] = w * gvv[c];
+          da = fmaf(gvv[c], vs[c] - ev[c], da);
+        }
+        oz[c] = w * da;
+        db[k][c] += oz[c];
+      }
+      const int64_t o = (xb - static_cast<const TX*>(p.x)) + k * tstride;
+      store8(static_cast<TX*>(p.dx) + o, ox);
+      if constexpr (HAS_V) store8(static_cast<TX*>(p.dv) + o, ov);
+      store8(static_cast<TZ*>(p.dz) + o, oz);
+    }
+    cur = nxt;
+  }
+  // this workgroup's bias-gradient partial
+  float* part = p.part + (((int64_t)h * p.chunks + chunk) * m) * dim + c0;
+#pragma unroll
+  for (int k = 0; k < kGradTPL; ++k)
+    if (has[k]) store8(part + (phase + (int64_t)P * k) * dim, db[k]);
+}
+
+// dbias[h, i, c] = sum over chunks (in order) of the partials.
+__global__ __launch_bounds__(256) void pool_grad_bias_kernel(PoolGradParams p) {
+  const int64_t n = p.heads * p.m * p.dim;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  const int64_t md = p.m * p.dim;
+  const int64_t h = e / md, r = e % md;
+  const float* src = p.part + h * p.chunks * md + r;
+  float s = 0.f;
+  for (int c = 0; c < p.chunks; ++c) s += src[(int64_t)c * md];
+  p.dbias[e] = s;
+}
+
+// Workgroups per head: about 1024 in all, each over consecutive blocks.
+static void grad_plan(const lbca_pool_grad_args& a, int* chunks, int* per_chunk) {
+  const int64_t list_n = a.batch * (a.block_end - a.block_begin);
+  int64_t per = (list_n * a.heads + 1023) / 1024;
+  if (per < 1) per = 1;
+  const int64_t ch = list_n > 0 ? (list_n + per - 1) / per : 0;
+  *chunks = (int)ch;
+  *per_chunk = (int)per;
+}
+
+size_t pool_grad_workspace_bytes(const lbca_pool_grad_args& a) {
+  int chunks, per;
+  grad_plan(a, &chunks, &per);
+  return (size_t)a.heads * (size_t)chunks * (size_t)(a.block * a.dim) * sizeof(float);
+}
+
+template <typename TX, typename TZ>
+static void launch_grad_typed(const PoolGradParams& p, bool has_v, dim3 grid, hipStream_t s) {
+  if (has_v) pool_grad_kernel<TX, TZ, true><<<grid, kGradNT, 0, s>>>(p);
+  else pool_grad_kernel<TX, TZ, false><<<grid, kGradNT, 0, s>>>(p);
+}
+
+hipError_t launch_pool_grad(const lbca_pool_grad_args& a, void* ws, hipStream_t stream) {
+  PoolGradParams p;
+  p.x = a.x; p.v = a.v; p.z = a.z; p.bias = a.bias; p.gx = a.grad_x; p.gv = a.grad_v;
+  p.dx = a.dx; p.dv = a.dv; p.dz = a.dz; p.dbias = a.dbias; p.part = static_cast<float*>(ws);
+  p.batch = a.batch; p.heads = a.heads; p.tokens = a.tokens; p.dim = a.dim; p.m = a.block;
+  p.entries = a.entries; p.block_begin = a.block_begin; p.n_blocks = a.block_end - a.block_begin;
+  p.pos_base = a.pos_base;
+  grad_plan(a, &p.chunks, &p.per_chunk);
+  p.log2_lanes = __builtin_ctz((unsigned)(a.dim / 8));
+  if (p.chunks > 0) {
+    const dim3 grid((unsigned)p.chunks, (unsigned)a.heads);
+    const bool has_v = a.v != nullptr;
+    if (a.x_dtype == LBCA_BF16) {
+      if (a.z_dtype == LBCA_BF16) launch_grad_typed<bf16_t, bf16_t>(p, has_v, grid, stream);
+      else launch_grad_typed<bf16_t, float>(p, has_v, grid, stream);
+    } else {
+      if (a.z_dtype == LBCA_BF16) launch_grad_typed<float, bf16_t>(p, has_v, grid, stream);
+      else launch_grad_typed<float, float>(p, has_v, grid, stream);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t n = a.heads * a.block * a.dim;
+  pool_grad_bias_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace lbca

@@ -34,6 +34,14 @@ class PoolArgs(ctypes.Structure):
                 ("rope_base", _f32)]
 
 
+class PoolGradArgs(ctypes.Structure):
+    _fields_ = [("x", _vp), ("v", _vp), ("z", _vp), ("bias", _vp), ("grad_x", _vp), ("grad_v", _vp),
+                ("dx", _vp), ("dv", _vp), ("dz", _vp), ("dbias", _vp),
+                ("batch", _i64), ("heads", _i64), ("tokens", _i64), ("dim", _i64), ("block", _i64),
+                ("entries", _i64), ("block_begin", _i64), ("block_end", _i64), ("pos_base", _i64),
+                ("x_dtype", _i32), ("z_dtype", _i32)]
+
+
 class CacheArgs(ctypes.Structure):
     _fields_ = [("x_new", _vp), ("v_new", _vp), ("z_new", _vp), ("raw_x", _vp), ("raw_v", _vp),
                 ("raw_z", _vp), ("bias", _vp), ("out_x", _vp), ("out_v", _vp), ("pos", _vp),
@@ -93,6 +101,9 @@ def lib():
         L.lbca_visible_range.argtypes = [_i64, _i64, _i64, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
         L.lbca_pool_blocks.argtypes = [ctypes.POINTER(PoolArgs), _vp]
         L.lbca_cache_append.argtypes = [ctypes.POINTER(CacheArgs), _vp]
+        L.lbca_pool_blocks_backward_workspace.argtypes = [ctypes.POINTER(PoolGradArgs),
+                                                          ctypes.POINTER(ctypes.c_size_t)]
+        L.lbca_pool_blocks_backward.argtypes = [ctypes.POINTER(PoolGradArgs), _vp, ctypes.c_size_t, _vp]
         L.lbca_attend_decode_workspace.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_size_t)]
         L.lbca_attend_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp, ctypes.c_size_t, _vp]
         L.lbca_attend_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
@@ -167,6 +178,51 @@ def pool_blocks(x, z, bias, block, block_begin, block_end, out_x, v=None, out_v=
                  float(rope_base))
     _check(lib().lbca_pool_blocks(ctypes.byref(a), _stream(stream)), "lbca_pool_blocks")
     return out_x if out_v is None else (out_x, out_v)
+
+
+def _pool_grad_args(x, z, bias, block, block_begin, block_end, grad_x, dx, dz, dbias, v, grad_v, dv,
+                    pos_base):
+    for t, n in ((x, "x"), (v, "v"), (z, "z"), (grad_x, "grad_x"), (grad_v, "grad_v"), (dx, "dx"),
+                 (dv, "dv"), (dz, "dz")):
+        _need(t, n, 4)
+    _need(bias, "bias", 3)
+    _need(dbias, "dbias", 3)
+    B, H, T, d = x.shape
+    return PoolGradArgs(_p(x), _p(v), _p(z), _p(bias), _p(grad_x), _p(grad_v), _p(dx), _p(dv), _p(dz),
+                        _p(dbias), B, H, T, d, block, grad_x.shape[2], block_begin, block_end, pos_base,
+                        _dt(x), _dt(z))
+
+
+def pool_blocks_backward(x, z, bias, block, block_begin, block_end, grad_x, v=None, grad_v=None, dx=None,
+                         dv=None, dz=None, dbias=None, pos_base=0, workspace=None, stream=None):
+    """lbca_pool_blocks_backward: gradients of pool_blocks (single series, optional values).
+    Returns (dx, dv or None, dz, dbias); missing outputs are allocated (rows outside the
+    pooled blocks of new outputs are zeros)."""
+    dx = torch.zeros_like(x) if dx is None else dx
+    dz = torch.zeros_like(z) if dz is None else dz
+    if v is not None and dv is None:
+        dv = torch.zeros_like(v)
+    if dbias is None:
+        dbias = torch.empty_like(bias)
+    a = _pool_grad_args(x, z, bias, block, block_begin, block_end, grad_x, dx, dz, dbias, v, grad_v, dv,
+                        pos_base)
+    if workspace is None:
+        n = ctypes.c_size_t()
+        _check(lib().lbca_pool_blocks_backward_workspace(ctypes.byref(a), ctypes.byref(n)),
+               "lbca_pool_blocks_backward_workspace")
+        workspace = torch.empty(max(n.value, 16), dtype=torch.uint8, device=x.device)
+    _check(lib().lbca_pool_blocks_backward(ctypes.byref(a), _p(workspace), workspace.numel(), _stream(stream)),
+           "lbca_pool_blocks_backward")
+    return dx, dv, dz, dbias
+
+
+def pool_blocks_backward_workspace_bytes(x, z, bias, block, block_begin, block_end, grad_x, v=None,
+                                         grad_v=None, pos_base=0):
+    a = _pool_grad_args(x, z, bias, block, block_begin, block_end, grad_x, x, z, bias, v, grad_v, v, pos_base)
+    n = ctypes.c_size_t()
+    _check(lib().lbca_pool_blocks_backward_workspace(ctypes.byref(a), ctypes.byref(n)),
+           "lbca_pool_blocks_backward_workspace")
+    return n.value
 
 
 def cache_append(x_new, z_new, raw_x, raw_z, bias, pos, raw_pos_base, block, window, mode, out_x,

@@ -143,6 +143,50 @@ typedef struct lbca_pool_args {
 LBCA_API int lbca_pool_blocks(const lbca_pool_args* a, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Gradients of single-series pooling (mSeek "How LBCA works" steps 2-3: with
+ * a = z + bias[h, s - j*m] and w = softmax over block j's tokens per channel,
+ * out_x[j] = sum w x, out_v[j] = sum w v).  For upstream gradients grad_x[j]
+ * (and grad_v[j]) of the pooled rows of blocks [block_begin, block_end):
+ *   dx[s] = w[s] * grad_x[j]          dv[s] = w[s] * grad_v[j]
+ *   dz[s] = w[s] * (grad_x[j] * (x[s] - out_x[j]) + grad_v[j] * (v[s] - out_v[j]))
+ *   dbias[h, i] = sum over sequences b and blocks j of dz[b, h, j*m + i]
+ * with the entries recomputed in fp32.  Token rows of those blocks are
+ * written in dx, dv, dz; every other row is left as is.  dbias is overwritten
+ * (zeros for an empty range).  Results are bitwise reproducible.
+ *
+ *   x, v, z            [batch, heads, tokens, dim]; row r holds position pos_base+r
+ *   bias               [heads, block, dim] float32
+ *   grad_x, grad_v     [batch, heads, entries, dim]   (x_dtype)
+ *   dx, dv / dz        [batch, heads, tokens, dim]    (x_dtype / z_dtype)
+ *   dbias              [heads, block, dim] float32
+ * v, grad_v and dv are all NULL without values.  No treatment, no dual mode.
+ * Constraints: dim a power of two in [8, 512], block * dim <= 8192,
+ * heads <= 65535.  Workspace (lbca_pool_blocks_backward_workspace bytes,
+ * 16-byte aligned, caller-owned, no initialisation needed): the bias-gradient
+ * partials.  Errors as lbca_pool_blocks, plus WORKSPACE.
+ */
+typedef struct lbca_pool_grad_args {
+  const void* x;
+  const void* v;
+  const void* z;
+  const float* bias;
+  const void* grad_x;
+  const void* grad_v;
+  void* dx;
+  void* dv;
+  void* dz;
+  float* dbias;
+  int64_t batch, heads, tokens, dim, block, entries;
+  int64_t block_begin, block_end;
+  int64_t pos_base;
+  int32_t x_dtype, z_dtype;
+} lbca_pool_grad_args;
+
+LBCA_API int lbca_pool_blocks_backward_workspace(const lbca_pool_grad_args* a, size_t* bytes);
+LBCA_API int lbca_pool_blocks_backward(const lbca_pool_grad_args* a, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Decode-time cache step (mSeek "How LBCA works" steps 1-3: the newest token
  * joins the raw cache; a block that is complete and, under the EXCLUSIVE rule,
  * wholly older than the window is pooled into one entry; HCA "What is

@@ -98,6 +98,47 @@ def test_pool_empty_range_is_ok_without_gpu():
     assert _pool(batch=0) == 0
 
 
+def _pgrad(ws=None, ws_bytes=0, **kw):
+    a = dict(x=FAKE, v=FAKE, z=FAKE, bias=FAKE, grad_x=FAKE, grad_v=FAKE, dx=FAKE, dv=FAKE, dz=FAKE,
+             dbias=FAKE, batch=2, heads=8, tokens=4096, dim=128, block=64, entries=64, block_begin=0,
+             block_end=64, pos_base=0, x_dtype=1, z_dtype=0)
+    a.update(kw)
+    s = lbca.PoolGradArgs(**a)
+    n = ctypes.c_size_t()
+    st_ws = lbca.lib().lbca_pool_blocks_backward_workspace(ctypes.byref(s), ctypes.byref(n))
+    st = lbca.lib().lbca_pool_blocks_backward(ctypes.byref(s), ws, ws_bytes, None)
+    return st_ws, st, n.value
+
+
+@fake_ptr
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), -1), (dict(z=None), -1), (dict(bias=None), -1), (dict(grad_x=None), -1),
+    (dict(dx=None), -1), (dict(dz=None), -1), (dict(dbias=None), -1),
+    (dict(v=None), -1), (dict(grad_v=None), -1), (dict(dv=None), -1),    # values all or none
+    (dict(x_dtype=2), -1), (dict(heads=0), -1), (dict(block=0), -1), (dict(tokens=-1), -1),
+    (dict(dim=96), -2), (dict(dim=1024), -2), (dict(dim=0), -1),
+    (dict(block=128), -2),                                                # block * dim > 8192
+    (dict(heads=70000, batch=1), -2),
+    (dict(block_end=65), -1), (dict(block_begin=3, block_end=2), -1),
+    (dict(tokens=4095), -1), (dict(pos_base=64), -1),                     # rows outside the buffer
+    (dict(dz=FAKE + 4), -1),                                              # misaligned
+])
+def test_pool_grad_validation(kw, code):
+    st_ws, st, _ = _pgrad(**kw)
+    assert st_ws == code and st == code
+
+
+@fake_ptr
+def test_pool_grad_workspace_required():
+    st_ws, st, need = _pgrad()
+    assert st_ws == 0 and need > 0
+    assert st == -3                                                       # no workspace
+    assert _pgrad(ws=FAKE, ws_bytes=need - 1)[1] == -3
+    assert _pgrad(ws=FAKE + 8, ws_bytes=need)[1] == -3                    # misaligned
+    st_ws, _, need0 = _pgrad(block_begin=5, block_end=5)
+    assert st_ws == 0 and need0 == 0                                      # empty range: no partials
+
+
 def _cache(**kw):
     a = dict(x_new=FAKE, v_new=FAKE, z_new=FAKE, raw_x=FAKE, raw_v=FAKE, raw_z=FAKE, bias=FAKE, out_x=FAKE,
              out_v=FAKE, pos=FAKE, raw_pos_base=FAKE, batch=2, heads=8, dim=128, block=64, window=128,

@@ -97,6 +97,46 @@ def test_pool_dual_csa(lib, d, treat):
     assert torch.equal(out2[:, :, 17:90], out[:, :, 17:90])
 
 
+@pytest.mark.parametrize("xdt,zdt,B,H,T,d,m,b0,b1,pb,with_v", [
+    ("bf16", "f32", 2, 3, 300, 128, 16, 2, 17, 0, True),     # LBCA-shaped, ragged block range
+    ("f32", "f32", 1, 2, 700, 64, 64, 3, 10, 64, False),     # raw rows start at position 64
+    ("bf16", "bf16", 2, 1, 520, 512, 16, 0, 32, 0, True),    # 512 dims (m * d = 8192)
+    ("bf16", "f32", 3, 2, 130, 128, 64, 0, 2, 0, True),      # four tokens per lane, few blocks
+])
+def test_pool_backward(lib, xdt, zdt, B, H, T, d, m, b0, b1, pb, with_v):
+    say(f"pool backward {xdt}/{zdt} B={B} H={H} d={d} m={m} blocks [{b0},{b1}) pos_base={pb}")
+    L = _dev(synth.lbca_layer(f"pool-grad-{xdt}-{d}-{m}", B, H, H, T, d, m, xdt, zdt))
+    N = T // m
+    g = lambda n: synth.normal((B, H, N, d), synth.seed_of("pool-grad", xdt, d, m, n), dtype=xdt, device=DEV)
+    gx, gv = g("gx"), (g("gv") if with_v else None)
+    sub = lambda t: t[:, :, pb:].contiguous()
+    x, z = sub(L["k"]), sub(L["z"])
+    v = sub(L["v"]) if with_v else None
+    dx, dz = torch.full_like(x, 7.0), torch.full_like(z, 7.0)
+    dv = torch.full_like(v, 7.0) if with_v else None
+    lib.pool_blocks_backward(x, z, L["bias"], m, b0, b1, gx, v=v, grad_v=gv, dx=dx, dv=dv, dz=dz, pos_base=pb)
+    _, _, _, dbias = lib.pool_blocks_backward(x, z, L["bias"], m, b0, b1, gx, v=v, grad_v=gv, pos_base=pb)
+    rx, rv, rz, rb = O.pool_single_backward(host(L["k"]), host(L["z"]), host(L["bias"]), m, b0, b1,
+                                            host(gx)[:, :, b0:b1], values=host(L["v"]) if with_v else None,
+                                            grad_values=host(gv)[:, :, b0:b1] if with_v else None)
+    lo, hi = b0 * m, b1 * m
+    check(xdt, host(dx[:, :, lo - pb:hi - pb]), rx[:, :, lo:hi], "d series")
+    check(zdt, host(dz[:, :, lo - pb:hi - pb]), rz[:, :, lo:hi], "d logits")
+    if with_v:
+        check(xdt, host(dv[:, :, lo - pb:hi - pb]), rv[:, :, lo:hi], "d values")
+    check("f32", host(dbias), rb, "d bias")
+    # rows outside the pooled blocks are untouched
+    assert (dx[:, :, :lo - pb] == 7.0).all() and (dx[:, :, hi - pb:] == 7.0).all()
+    assert (dz[:, :, :lo - pb] == 7.0).all() and (dz[:, :, hi - pb:] == 7.0).all()
+    # bitwise reproducible
+    dx2, dv2, dz2, db2 = lib.pool_blocks_backward(x, z, L["bias"], m, b0, b1, gx, v=v, grad_v=gv, pos_base=pb)
+    assert torch.equal(dx2[:, :, lo - pb:hi - pb], dx[:, :, lo - pb:hi - pb]) and torch.equal(db2, dbias)
+    assert torch.equal(dz2[:, :, lo - pb:hi - pb], dz[:, :, lo - pb:hi - pb])
+    # an empty range writes a zero bias gradient and nothing else
+    _, _, dz3, db3 = lib.pool_blocks_backward(x, z, L["bias"], m, b1, b1, gx, v=v, grad_v=gv, pos_base=pb)
+    assert (db3 == 0).all() and (dz3 == 0).all()
+
+
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
