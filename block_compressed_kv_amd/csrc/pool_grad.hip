@@ -95,7 +95,7 @@ __device__ __forceinline__ void combine_state(GradState& lo, const GradState& hi
   for (int c = 0; c < 8; ++c) {
     const float nm = fmaxf(lo.mx[c], hi.mx[c]);
     const bool none = nm == kNegInf;
-    const float a = none ? 0.f : exp2f(lo.mx[c] - nm), b = none ? 0.f : exp2f(hi.mx[c] - nm);
+    const float a = none ? 0.f : fast_exp2(lo.mx[c] - nm), b = none ? 0.f : fast_exp2(hi.mx[c] - nm);
     lo.l[c] = lo.l[c] * a + hi.l[c] * b;
     lo.sx[c] = lo.sx[c] * a + hi.sx[c] * b;
     lo.sv[c] = lo.sv[c] * a + hi.sv[c] * b;
@@ -264,6 +264,7 @@ __global__ __launch_bounds__(kGradNT) void pool_grad_kernel(PoolGradParams p) {
       st.mx[c] = mx;
       st.l[c] = st.sx[c] = st.sv[c] = 0.f;
     }
+    // a[k][c] becomes the token's weight relative to this lane's maximum
 #pragma unroll
     for (int k = 0; k < kGradTPL; ++k) {
       if (!has[k]) continue;
@@ -272,19 +273,24 @@ __global__ __launch_bounds__(kGradNT) void pool_grad_kernel(PoolGradParams p) {
       if constexpr (HAS_V) unpack_row<TX>(cur.v[k], vs);
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const float w = exp2f(a[k][c] - st.mx[c]);
-        st.l[c] += w;
-        st.sx[c] = fmaf(w, xs[c], st.sx[c]);
-        if constexpr (HAS_V) st.sv[c] = fmaf(w, vs[c], st.sv[c]);
+        a[k][c] = fast_exp2(a[k][c] - st.mx[c]);
+        st.l[c] += a[k][c];
+        st.sx[c] = fmaf(a[k][c], xs[c], st.sx[c]);
+        if constexpr (HAS_V) st.sv[c] = fmaf(a[k][c], vs[c], st.sv[c]);
       }
     }
+    float lmx[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) lmx[c] = st.mx[c];
     merge_phases(st, red, L, li);
-    float inv[8], ex[8], ev[8];
+    // the block's entry, and the factor that turns a lane weight into the softmax weight
+    float scale[8], ex[8], ev[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      inv[c] = 1.f / st.l[c];
-      ex[c] = st.sx[c] * inv[c];
-      ev[c] = st.sv[c] * inv[c];
+      const float inv = 1.f / st.l[c];
+      ex[c] = st.sx[c] * inv;
+      ev[c] = st.sv[c] * inv;
+      scale[c] = lmx[c] == kNegInf ? 0.f : fast_exp2(lmx[c] - st.mx[c]) * inv;
     }
     // gradients of this lane's tokens
 #pragma unroll
@@ -296,7 +302,7 @@ __global__ __launch_bounds__(kGradNT) void pool_grad_kernel(PoolGradParams p) {
       float ox[8], ov[8], oz[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const float w = exp2f(a[k][c] - st.mx[c]) * inv[c];
+        const float w = a[k][c] * scale[c];
         ox[c] = w * g[c];
         float da = g[c] * (xs[c] - ex[c]);
         if constexpr (HAS_V) {
