@@ -148,9 +148,6 @@ __device__ __forceinline__ void finish_entry(PoolAcc<TX, TZ, HAS_V>& acc, float 
                                              int phase, bool active, int64_t dim, int64_t c0, int64_t block_pos,
                                              const EntryTreat& tr, TX* out_x, TX* out_v) {
   const int tid = threadIdx.x, lane = tid & 63;
-  // Merge the P phases of a row in a fixed order: inside a wave by lane
-  // exchanges (phases of a row sit in consecutive groups), then across the
-  // row's waves through LDS, read by the row's first wave.
   if (P > 1) {
     const int span = L * P;  // lanes of one row
     for (int off = L; off < 64 && off < span; off <<= 1) acc.merge_xor(off, (lane & off) == 0);
