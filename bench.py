@@ -552,6 +552,7 @@ def run_ceilings():
     L.ceil_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     L.ceil_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
     L.ceil_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.ceil_lds.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     L.ceil_empty.argtypes = [ctypes.c_void_p]
     stream = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -575,6 +576,13 @@ def run_ceilings():
         g = capture(lambda: [ok(L.ceil_read(b.data_ptr(), nb, out.data_ptr(), grid_dec, stream())) for b in bufs])
         res[f"read_decode_bytes_one_launch_us_grid{grid_dec}"] = time_graph(g, 50) * 1e3 / LAYERS
     del bufs, g
+    lg, lit = 1024, 2048
+    lsrc = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
+    lo_ = torch.empty(lg * 256, dtype=torch.int32, device="cuda")
+    g = capture(lambda: ok(L.ceil_lds(lsrc.data_ptr(), lo_.data_ptr(), lg, lit, stream())))
+    lds_s = time_graph(g, 10) * 1e-3
+    res["lds_read_TBps"] = lg * 256 * 8 * lit * 16 / lds_s / 1e12
+    res["lds_read_bytes_per_clock_per_cu_at_2p4GHz"] = res["lds_read_TBps"] * 1e12 / 256 / 2.4e9
     mg, iters = 1024, 4096
     mo = torch.empty(mg * 256, dtype=torch.float32, device="cuda")
     g = capture(lambda: ok(L.ceil_mfma(mo.data_ptr(), mg, iters, stream())))
@@ -582,7 +590,8 @@ def run_ceilings():
     g = capture(lambda: [ok(L.ceil_empty(stream())) for _ in range(LAYERS)])
     res["empty_launch_us"] = time_graph(g, 200) * 1e3 / LAYERS
     res["note"] = ("hbm_read: 2048 workgroups streaming 1 GiB; hbm_copy: the same workgroups copying 1 GiB "
-                   "(bytes read + written); read_decode_bytes_one_launch: one launch reading "
+                   "(bytes read + written); lds_read: 1024 workgroups x 256 threads each reading 16 B per step "
+                   "from LDS, eight reads in flight; read_decode_bytes_one_launch: one launch reading "
                    f"{nb} B (the batch-16 decode's algorithmic bytes), 14 distinct buffers per graph replay; "
                    "mfma: 1024 workgroups x 4 waves x 4 chains of v_mfma_f32_32x32x16_bf16; "
                    "empty_launch: 14 empty kernels per graph replay")

@@ -1,6 +1,7 @@
 // Probes of this part's measured ceilings, reported beside the kernels'
 // roofline fractions: a streaming HBM read, a streaming copy (read and
-// write), a bf16 MFMA loop and an empty kernel (the launch floor).  Built into libceilings.so, a library of its own
+// write), LDS read bandwidth, a bf16 MFMA loop and an empty kernel (the
+// launch floor).  Built into libceilings.so, a library of its own
 // that only the benchmark loads; nothing here is part of the attention path.
 //
 // Each entry point checks its sizes and returns a hipError_t value (0 = success).
@@ -50,6 +51,28 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4_t* __restrict__ s
   for (; i < n16; i += stride) dst[i] = src[i];
 }
 
+// LDS read bandwidth: 256 threads fill 64 KB of LDS from src, then each
+// thread reads 16 bytes per step at a lane-contiguous address (the 64 lanes of
+// a wave cover 1 KB, free of bank conflicts), eight reads in flight, for
+// `iters` steps; every thread writes the xor of what it read.
+__global__ __launch_bounds__(256) void lds_kernel(const u32x4_t* __restrict__ src, uint32_t* __restrict__ out,
+                                                  int iters) {
+  __shared__ u32x4_t buf[4096];  // 64 KB
+  for (int i = threadIdx.x; i < 4096; i += 256) buf[i] = src[i];
+  __syncthreads();
+  uint32_t acc = 0;
+  int idx = threadIdx.x;
+  for (int it = 0; it < iters; ++it) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = buf[(idx + j * 512) & 4095];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    idx = (idx + 256 + (int)(acc & 1u) * 64) & 4095;  // the next addresses depend on the data read
+  }
+  out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
 // Four independent chains of v_mfma_f32_32x32x16_bf16 per wave (32768 flops
 // each); every thread writes one sum of its accumulators.
 __global__ __launch_bounds__(256) void mfma_kernel(float* __restrict__ out, int iters) {
@@ -93,6 +116,15 @@ __attribute__((visibility("default"))) int ceil_copy(const void* src, void* dst,
   if (!src || !dst || grid < 1 || bytes % 16 != 0) return (int)hipErrorInvalidValue;
   copy_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<const u32x4_t*>(src),
                                                                   static_cast<u32x4_t*>(dst), (int64_t)(bytes / 16));
+  return (int)hipGetLastError();
+}
+
+// grid workgroups of 256 threads, each thread 8 * iters LDS reads of 16 bytes
+// after copying 64 KB of src (at least 64 KB) into LDS; out holds grid * 256 uint32.
+__attribute__((visibility("default"))) int ceil_lds(const void* src, void* out, int grid, int iters, void* stream) {
+  if (!src || !out || grid < 1 || iters < 1) return (int)hipErrorInvalidValue;
+  lds_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<const u32x4_t*>(src),
+                                                                 static_cast<uint32_t*>(out), iters);
   return (int)hipGetLastError();
 }
 
