@@ -169,3 +169,34 @@ def test_cache_overlap_hca_treated(lib, Hq):
         n_p, _ = O.visible_range(steps - 1 - o, m, W, O.OVERLAP)
         assert torch.equal(out_x[b, :, :n_p], ref[b, :, :n_p]), f"entries of sequence {b}"
         check_bf16(host(out_x[b, :, :n_p]), treated[b, :, :n_p], f"treated entries of sequence {b}")
+
+
+def test_cache_due_entry_past_capacity(lib):
+    # entries beyond the pooled buffer are not written (pooling skipped) while the ring
+    # and the raw base still advance; decode then reports such a sequence as not fitting
+    H, d, m, W, ring, T = 1, 64, 8, 16, 24, 120
+    offsets = [0, 60]
+    B = len(offsets)
+    L = _dev(synth.lbca_layer("cache-cap", B, 2, H, T, d, m, "bf16", "f32"))
+    k, v, z, bias = L["k"], L["v"], L["z"], L["bias"]
+    entries = 6                       # blocks 0..5 fit; sequence 0 makes blocks up to 11 visible
+    steps = 119
+    raw_x, raw_v, raw_z, rpb, out_x, out_v = _loop(lib, k, z, bias, m, W, O.EXCLUSIVE, ring, entries, offsets,
+                                                   steps, set(), v=v)
+    torch.cuda.synchronize()
+    t_end = [steps - 1 - o for o in offsets]
+    _check_ring(t_end, m, W, O.EXCLUSIVE, ring, raw_x, raw_z, rpb, k, z, raw_v, v)
+    ref_x = torch.full_like(out_x, 7.0)
+    ref_v = torch.full_like(out_v, 7.0)
+    lib.pool_blocks(k, z, bias, m, 0, entries, ref_x, v=v, out_v=ref_v)
+    for b, t in enumerate(t_end):
+        n = min(O.visible_range(t, m, W, O.EXCLUSIVE)[0], entries)
+        assert torch.equal(out_x[b, :, :n], ref_x[b, :, :n]) and torch.equal(out_v[b, :, :n], ref_v[b, :, :n])
+        assert (out_x[b, :, n:] == 7.0).all()
+    q = synth.normal((B, 2, d), 5, dtype="bf16", device=DEV)
+    pos = torch.tensor(t_end, dtype=torch.int64, device=DEV)
+    o, lse = lib.attend_decode(q, out_x, raw_x, pos, m, W, O.EXCLUSIVE, pooled_v=out_v, raw_v=raw_v,
+                               raw_pos_base=rpb)
+    n_p = [O.visible_range(t, m, W, O.EXCLUSIVE)[0] for t in t_end]
+    assert n_p[0] > entries and n_p[1] <= entries
+    assert torch.isnan(o[0]).all() and torch.isfinite(o[1]).all()

@@ -102,6 +102,7 @@ def test_pool_dual_csa(lib, d, treat):
     ("f32", "f32", 1, 2, 700, 64, 64, 3, 10, 64, False),     # raw rows start at position 64
     ("bf16", "bf16", 2, 1, 520, 512, 16, 0, 32, 0, True),    # 512 dims (m * d = 8192)
     ("bf16", "f32", 3, 2, 130, 128, 64, 0, 2, 0, True),      # four tokens per lane, few blocks
+    ("bf16", "f32", 1, 2, 64, 128, 1, 5, 60, 0, True),       # m = 1: most lane phases empty
 ])
 def test_pool_backward(lib, xdt, zdt, B, H, T, d, m, b0, b1, pb, with_v):
     say(f"pool backward {xdt}/{zdt} B={B} H={H} d={d} m={m} blocks [{b0},{b1}) pos_base={pb}")
