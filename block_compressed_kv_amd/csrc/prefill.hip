@@ -130,11 +130,16 @@ __device__ __forceinline__ void read_v_tiles(s16x4 (&r)[16], const bf16_t* vt, i
   }
 }
 
+#ifndef LBCA_PREFILL_THREADS
+#define LBCA_PREFILL_THREADS 512  // 8 waves (two per SIMD) x 32 query rows
+#endif
+constexpr int kPrefillThreads = LBCA_PREFILL_THREADS;
+
 template <int D, bool SHARED>
-__global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
-  constexpr int NWV = 8;                 // waves per workgroup: two per SIMD
-  constexpr int NT = NWV * 64;
-  constexpr int QG = 2;                  // 16-row query groups per wave
+__global__ __launch_bounds__(kPrefillThreads, 1) void prefill_kernel(PrefillParams p) {
+  constexpr int NWV = kPrefillThreads / 64;  // waves per workgroup
+  constexpr int NT = kPrefillThreads;
+  constexpr int QG = 256 / (NWV * 16);       // 16-row query groups per wave
   constexpr int KT = D <= 64 ? 64 : 32;  // keys per tile (registers bound it at 128 dims)
   constexpr int KB = KT / 16;            // 16-key blocks per tile
   constexpr int KS = D / 32;             // 32-wide head-dim chunks (Q.K contraction)
@@ -430,12 +435,12 @@ hipError_t launch_prefill(const lbca_prefill_args& a, hipStream_t stream) {
   const bool shared = a.pooled_v == nullptr;
   switch (a.dim) {
     case 64:
-      if (shared) prefill_kernel<64, true><<<grid, 512, 0, stream>>>(p);
-      else prefill_kernel<64, false><<<grid, 512, 0, stream>>>(p);
+      if (shared) prefill_kernel<64, true><<<grid, kPrefillThreads, 0, stream>>>(p);
+      else prefill_kernel<64, false><<<grid, kPrefillThreads, 0, stream>>>(p);
       break;
     case 128:
-      if (shared) prefill_kernel<128, true><<<grid, 512, 0, stream>>>(p);
-      else prefill_kernel<128, false><<<grid, 512, 0, stream>>>(p);
+      if (shared) prefill_kernel<128, true><<<grid, kPrefillThreads, 0, stream>>>(p);
+      else prefill_kernel<128, false><<<grid, kPrefillThreads, 0, stream>>>(p);
       break;
     default: return hipErrorInvalidValue;
   }
