@@ -158,6 +158,9 @@ int lbca_cache_append(const lbca_cache_args* a, void* stream) {
     return LBCA_ERR_INVALID_ARG;
   const bool has_v = a->v_new != nullptr;
   if ((a->raw_v != nullptr) != has_v || (a->out_v != nullptr) != has_v) return LBCA_ERR_INVALID_ARG;
+  const bool dual = a->xb_new || a->zb_new || a->raw_xb || a->raw_zb || a->bias_b;
+  if (dual && !(a->xb_new && a->zb_new && a->raw_xb && a->raw_zb && a->bias_b)) return LBCA_ERR_INVALID_ARG;
+  if (dual && has_v) return LBCA_ERR_UNSUPPORTED;
   if (!is_dtype(a->x_dtype) || !is_dtype(a->z_dtype)) return LBCA_ERR_INVALID_ARG;
   if (a->mode != LBCA_EXCLUSIVE && a->mode != LBCA_OVERLAP) return LBCA_ERR_INVALID_ARG;
   if (a->batch < 0 || a->heads < 1 || a->block < 1 || a->window < 1 || a->entries < 0 || a->ring < 1)
@@ -168,6 +171,8 @@ int lbca_cache_append(const lbca_cache_args* a, void* stream) {
   const int64_t need = a->mode == LBCA_EXCLUSIVE ? a->window + a->block
                                                   : (a->window > a->block ? a->window : a->block);
   if (a->window > kMaxElems || a->block > kMaxElems || a->ring < need) return LBCA_ERR_INVALID_ARG;
+  if (dual && a->ring < (a->mode == LBCA_EXCLUSIVE ? a->window + 2 * a->block : 2 * a->block))
+    return LBCA_ERR_INVALID_ARG;  // block j-1 of the b-series is read too
   if (a->batch > INT32_MAX / a->heads) return LBCA_ERR_UNSUPPORTED;  // one workgroup per (sequence, head)
   if (!sane_product({a->batch, a->heads, 2 * a->ring, a->dim}) ||
       !sane_product({a->batch, a->heads, a->entries, a->dim}) || !sane_product({a->heads, a->block, a->dim}))
@@ -178,7 +183,8 @@ int lbca_cache_append(const lbca_cache_args* a, void* stream) {
   if (treat && has_v) return LBCA_ERR_UNSUPPORTED;
   if (!aligned16(a->x_new) || !aligned16(a->v_new) || !aligned16(a->z_new) || !aligned16(a->raw_x) ||
       !aligned16(a->raw_v) || !aligned16(a->raw_z) || !aligned16(a->bias) || !aligned16(a->out_x) ||
-      !aligned16(a->out_v))
+      !aligned16(a->out_v) || !aligned16(a->xb_new) || !aligned16(a->zb_new) || !aligned16(a->raw_xb) ||
+      !aligned16(a->raw_zb) || !aligned16(a->bias_b))
     return LBCA_ERR_INVALID_ARG;
   if (a->batch == 0) return LBCA_OK;
   return hip_status(lbca::launch_cache_append(*a, static_cast<hipStream_t>(stream)));

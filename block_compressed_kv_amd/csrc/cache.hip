@@ -16,7 +16,10 @@
 // merged and the entry finished exactly as in the pooling kernels (shared
 // code), so an entry written here is bitwise the one lbca_pool_blocks writes.
 // Under the OVERLAP rule the due block ends with the new token, which the
-// workgroup's barrier after the copy makes visible to every lane.
+// workgroup's barrier after the copy makes visible to every lane.  In dual
+// (CSA) mode a second ring holds the b-series and the entry's softmax also
+// folds block j-1 of it ("CSA: Compressed Sparse Attention (toy
+// implementation)", "What is implemented", dual overlapped pooling).
 #include "lbca_internal.h"
 #include "pool_common.h"
 
@@ -34,6 +37,11 @@ struct CacheParams {
   void* out_v;
   const int64_t* pos;
   int64_t* raw_pos_base;
+  const void* xb_new;  // dual (CSA) mode: the b-series
+  const void* zb_new;
+  void* raw_xb;
+  void* raw_zb;
+  const float* bias_b;
   int64_t heads, dim, m, W, ring, entries;
   int mode;
   int lanes_per_row;  // L = dim / 8
@@ -49,12 +57,13 @@ __device__ __forceinline__ uint4 ld16(const T* r, int i) { return reinterpret_ca
 template <typename T>
 __device__ __forceinline__ void st16(T* r, int i, uint4 v) { reinterpret_cast<uint4*>(r)[i] = v; }
 
-template <typename TX, typename TZ, bool HAS_V, bool TREAT>
+template <typename TX, typename TZ, bool HAS_V, bool TREAT, bool DUAL>
 __global__ __launch_bounds__(256) void cache_append_kernel(CacheParams p) {
   __shared__ float part[32][256];  // cross-wave phase merge
   // every argument field in one batch of scalar loads (otherwise they come in
   // dependent rounds, one per basic block)
-  asm volatile("" ::"s"(p.x_new), "s"(p.v_new), "s"(p.z_new), "s"(p.raw_x), "s"(p.raw_v), "s"(p.raw_z),
+  asm volatile("" ::"s"(p.x_new), "s"(p.v_new), "s"(p.z_new), "s"(p.raw_x), "s"(p.raw_v), "s"(p.raw_z), "s"(p.xb_new),
+               "s"(p.zb_new), "s"(p.raw_xb), "s"(p.raw_zb),
                "s"(p.pos), "s"(p.raw_pos_base), "s"(p.heads), "s"(p.dim), "s"(p.m), "s"(p.W), "s"(p.ring),
                "s"(p.entries), "s"(p.mode), "s"(p.lanes_per_row), "s"(p.log2_lanes));
   const int tid = threadIdx.x, lane = tid & 63;
@@ -72,7 +81,9 @@ __global__ __launch_bounds__(256) void cache_append_kernel(CacheParams p) {
   const TX* xs = static_cast<const TX*>(p.x_new) + src;
   const TX* vs = static_cast<const TX*>(p.v_new) + src;
   const TZ* zs = static_cast<const TZ*>(p.z_new) + src;
-  uint4 x0 = {}, x1 = {}, v0 = {}, v1 = {}, z0 = {}, z1 = {};
+  const TX* xbs = static_cast<const TX*>(p.xb_new) + src;
+  const TZ* zbs = static_cast<const TZ*>(p.zb_new) + src;
+  uint4 x0 = {}, x1 = {}, v0 = {}, v1 = {}, z0 = {}, z1 = {}, xb0 = {}, xb1 = {}, zb0 = {}, zb1 = {};
   if (phase == 0) {
     x0 = ld16(xs, 0);
     if constexpr (X2) x1 = ld16(xs, 1);
@@ -82,6 +93,12 @@ __global__ __launch_bounds__(256) void cache_append_kernel(CacheParams p) {
     }
     z0 = ld16(zs, 0);
     if constexpr (Z2) z1 = ld16(zs, 1);
+    if constexpr (DUAL) {
+      xb0 = ld16(xbs, 0);
+      if constexpr (X2) xb1 = ld16(xbs, 1);
+      zb0 = ld16(zbs, 0);
+      if constexpr (Z2) zb1 = ld16(zbs, 1);
+    }
   }
   const int64_t t = p.pos[b];
   if (t < 0) return;
@@ -114,6 +131,22 @@ __global__ __launch_bounds__(256) void cache_append_kernel(CacheParams p) {
       st16(rz + d0, 1, z1);
       st16(rz + d1, 1, z1);
     }
+    if constexpr (DUAL) {
+      TX* rxb = static_cast<TX*>(p.raw_xb);
+      TZ* rzb = static_cast<TZ*>(p.raw_zb);
+      st16(rxb + d0, 0, xb0);
+      st16(rxb + d1, 0, xb0);
+      st16(rzb + d0, 0, zb0);
+      st16(rzb + d1, 0, zb0);
+      if constexpr (X2) {
+        st16(rxb + d0, 1, xb1);
+        st16(rxb + d1, 1, xb1);
+      }
+      if constexpr (Z2) {
+        st16(rzb + d0, 1, zb1);
+        st16(rzb + d1, 1, zb1);
+      }
+    }
   }
   // 2. the raw base that maps t's raw span onto ring rows
   int64_t n_pooled, raw_begin;
@@ -131,6 +164,11 @@ __global__ __launch_bounds__(256) void cache_append_kernel(CacheParams p) {
   acc.run(static_cast<const TX*>(p.raw_x) + series + r0 * dim,
           HAS_V ? static_cast<const TX*>(p.raw_v) + series + r0 * dim : nullptr,
           static_cast<const TZ*>(p.raw_z) + series + r0 * dim, p.bias + h * p.m * dim + c0, phase, P, p.m, dim);
+  if (DUAL && j > 0) {  // block j-1 of the b-series, under the same softmax
+    const int64_t rb0 = ((j - 1) * p.m) % ring;
+    acc.run(static_cast<const TX*>(p.raw_xb) + series + rb0 * dim, nullptr,
+            static_cast<const TZ*>(p.raw_zb) + series + rb0 * dim, p.bias_b + h * p.m * dim + c0, phase, P, p.m, dim);
+  }
   const int64_t o = ((int64_t)row * p.entries + j) * dim + c0;
   finish_entry<TX, TZ, HAS_V, TREAT>(acc, part, L, P, phase, true, dim, c0, j * p.m,
                                      EntryTreat{p.eps, p.rope_dims, p.log2_base}, static_cast<TX*>(p.out_x) + o,
@@ -138,10 +176,13 @@ __global__ __launch_bounds__(256) void cache_append_kernel(CacheParams p) {
 }
 
 template <typename TX, typename TZ>
-static hipError_t launch_cache_typed(const CacheParams& p, bool has_v, bool treat, dim3 grid, hipStream_t s) {
-  if (has_v) cache_append_kernel<TX, TZ, true, false><<<grid, 256, 0, s>>>(p);
-  else if (treat) cache_append_kernel<TX, TZ, false, true><<<grid, 256, 0, s>>>(p);
-  else cache_append_kernel<TX, TZ, false, false><<<grid, 256, 0, s>>>(p);
+static hipError_t launch_cache_typed(const CacheParams& p, bool has_v, bool treat, bool dual, dim3 grid,
+                                     hipStream_t s) {
+  if (has_v) cache_append_kernel<TX, TZ, true, false, false><<<grid, 256, 0, s>>>(p);
+  else if (dual && treat) cache_append_kernel<TX, TZ, false, true, true><<<grid, 256, 0, s>>>(p);
+  else if (dual) cache_append_kernel<TX, TZ, false, false, true><<<grid, 256, 0, s>>>(p);
+  else if (treat) cache_append_kernel<TX, TZ, false, true, false><<<grid, 256, 0, s>>>(p);
+  else cache_append_kernel<TX, TZ, false, false, false><<<grid, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -151,6 +192,7 @@ hipError_t launch_cache_append(const lbca_cache_args& a, hipStream_t stream) {
   p.raw_x = a.raw_x; p.raw_v = a.raw_v; p.raw_z = a.raw_z;
   p.bias = a.bias; p.out_x = a.out_x; p.out_v = a.out_v;
   p.pos = a.pos; p.raw_pos_base = a.raw_pos_base;
+  p.xb_new = a.xb_new; p.zb_new = a.zb_new; p.raw_xb = a.raw_xb; p.raw_zb = a.raw_zb; p.bias_b = a.bias_b;
   p.heads = a.heads; p.dim = a.dim; p.m = a.block; p.W = a.window; p.ring = a.ring; p.entries = a.entries;
   p.mode = a.mode;
   p.lanes_per_row = (int)(a.dim / 8);
@@ -161,12 +203,13 @@ hipError_t launch_cache_append(const lbca_cache_args& a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.batch * a.heads));
   const bool has_v = a.v_new != nullptr;
   const bool treat = a.rmsnorm_eps >= 0.f || a.rope_dims > 0;
+  const bool dual = a.xb_new != nullptr;
   if (a.x_dtype == LBCA_BF16) {
-    if (a.z_dtype == LBCA_BF16) return launch_cache_typed<bf16_t, bf16_t>(p, has_v, treat, grid, stream);
-    return launch_cache_typed<bf16_t, float>(p, has_v, treat, grid, stream);
+    if (a.z_dtype == LBCA_BF16) return launch_cache_typed<bf16_t, bf16_t>(p, has_v, treat, dual, grid, stream);
+    return launch_cache_typed<bf16_t, float>(p, has_v, treat, dual, grid, stream);
   }
-  if (a.z_dtype == LBCA_BF16) return launch_cache_typed<float, bf16_t>(p, has_v, treat, grid, stream);
-  return launch_cache_typed<float, float>(p, has_v, treat, grid, stream);
+  if (a.z_dtype == LBCA_BF16) return launch_cache_typed<float, bf16_t>(p, has_v, treat, dual, grid, stream);
+  return launch_cache_typed<float, float>(p, has_v, treat, dual, grid, stream);
 }
 
 }  // namespace lbca

@@ -48,7 +48,8 @@ class CacheArgs(ctypes.Structure):
                 ("raw_pos_base", _vp),
                 ("batch", _i64), ("heads", _i64), ("dim", _i64), ("block", _i64), ("window", _i64),
                 ("ring", _i64), ("entries", _i64), ("mode", _i32), ("x_dtype", _i32), ("z_dtype", _i32),
-                ("rmsnorm_eps", _f32), ("rope_dims", _i32), ("rope_base", _f32)]
+                ("rmsnorm_eps", _f32), ("rope_dims", _i32), ("rope_base", _f32),
+                ("xb_new", _vp), ("zb_new", _vp), ("raw_xb", _vp), ("raw_zb", _vp), ("bias_b", _vp)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -227,12 +228,15 @@ def pool_blocks_backward_workspace_bytes(x, z, bias, block, block_begin, block_e
 
 def cache_append(x_new, z_new, raw_x, raw_z, bias, pos, raw_pos_base, block, window, mode, out_x,
                  v_new=None, raw_v=None, out_v=None, rmsnorm_eps=None, rope_dims=0, rope_base=10000.0,
-                 stream=None):
+                 xb_new=None, zb_new=None, raw_xb=None, raw_zb=None, bias_b=None, stream=None):
     """lbca_cache_append: x_new, v_new, z_new [B,H,d]; raw_* [B,H,2*ring,d] (mirrored ring);
-    bias [H,m,d]; out [B,H,N,d]; pos, raw_pos_base [B] int64 (raw_pos_base is written)."""
+    bias [H,m,d]; out [B,H,N,d]; pos, raw_pos_base [B] int64 (raw_pos_base is written).
+    Dual (CSA) mode: xb_new, zb_new, raw_xb, raw_zb, bias_b for the b-series."""
     for t, n, nd in ((x_new, "x_new", 3), (v_new, "v_new", 3), (z_new, "z_new", 3), (raw_x, "raw_x", 4),
                      (raw_v, "raw_v", 4), (raw_z, "raw_z", 4), (bias, "bias", 3), (out_x, "out_x", 4),
-                     (out_v, "out_v", 4), (pos, "pos", 1), (raw_pos_base, "raw_pos_base", 1)):
+                     (out_v, "out_v", 4), (pos, "pos", 1), (raw_pos_base, "raw_pos_base", 1),
+                     (xb_new, "xb_new", 3), (zb_new, "zb_new", 3), (raw_xb, "raw_xb", 4), (raw_zb, "raw_zb", 4),
+                     (bias_b, "bias_b", 3)):
         _need(t, n, nd)
     B, H, d = x_new.shape
     if raw_x.shape[2] % 2:
@@ -240,7 +244,8 @@ def cache_append(x_new, z_new, raw_x, raw_z, bias, pos, raw_pos_base, block, win
     a = CacheArgs(_p(x_new), _p(v_new), _p(z_new), _p(raw_x), _p(raw_v), _p(raw_z), _p(bias), _p(out_x),
                   _p(out_v), _p(pos), _p(raw_pos_base), B, H, d, block, window, raw_x.shape[2] // 2,
                   out_x.shape[2], mode, _dt(x_new), _dt(z_new),
-                  -1.0 if rmsnorm_eps is None else float(rmsnorm_eps), int(rope_dims), float(rope_base))
+                  -1.0 if rmsnorm_eps is None else float(rmsnorm_eps), int(rope_dims), float(rope_base),
+                  _p(xb_new), _p(zb_new), _p(raw_xb), _p(raw_zb), _p(bias_b))
     _check(lib().lbca_cache_append(ctypes.byref(a), _stream(stream)), "lbca_cache_append")
 
 

@@ -207,9 +207,14 @@ LBCA_API int lbca_pool_blocks_backward(const lbca_pool_grad_args* a, void* works
  *   3. writes raw_pos_base[b] = rb - (rb mod ring), rb = raw_begin(t), so that
  *      lbca_attend_decode with raw rows = 2 * ring and this raw_pos_base reads
  *      the raw span of t from the ring.
+ * Dual mode (xb_new != NULL, CSA "What is implemented" item 1): the b-series
+ * token (xb_new, zb_new) goes to its own ring (raw_xb, raw_zb) and entry j
+ * pools block j of the a-series with block j-1 of the b-series under one
+ * softmax per channel (bias_b for the b part), as lbca_pool_blocks in dual mode.
  * The ring must hold every token a step reads: ring >= W + m (EXCLUSIVE: the
- * oldest token of the due block is t+1-W-m) or ring >= max(W, m) (OVERLAP).
- * Sequences with t < 0 are skipped.  Dual (CSA) pooling is not covered.
+ * oldest token of the due block is t+1-W-m) or ring >= max(W, m) (OVERLAP),
+ * and in dual mode, which also reads block j-1, ring >= W + 2 m (EXCLUSIVE) or
+ * ring >= max(W, 2 m) (OVERLAP).  Sequences with t < 0 are skipped.
  *
  *   x_new, v_new   [batch, heads, dim]          x_dtype
  *   z_new          [batch, heads, dim]          z_dtype
@@ -218,8 +223,10 @@ LBCA_API int lbca_pool_blocks_backward(const lbca_pool_grad_args* a, void* works
  *   bias           [heads, block, dim] float32
  *   out_x, out_v   [batch, heads, entries, dim] x_dtype
  *   pos            [batch] int64 (device);  raw_pos_base [batch] int64 (device, written)
+ *   xb_new, zb_new, raw_xb, raw_zb, bias_b: the b-series, as x_new, z_new,
+ *   raw_x, raw_z, bias (all NULL outside dual mode)
  * v_new, raw_v and out_v are all NULL for a shared series (x is key and value).
- * Treatment flags as lbca_pool_blocks (shared series only).
+ * Treatment flags as lbca_pool_blocks (shared series only; dual mode has no values).
  * Constraints: dim a power of two in [8, 512].
  * Errors: INVALID_ARG for a NULL required pointer, a ring below the bound,
  * bad sizes or mode; UNSUPPORTED for treatment with v.
@@ -241,6 +248,11 @@ typedef struct lbca_cache_args {
   float rmsnorm_eps; /* < 0: off */
   int32_t rope_dims; /* 0: off */
   float rope_base;
+  const void* xb_new; /* dual mode: the b-series */
+  const void* zb_new;
+  void* raw_xb;
+  void* raw_zb;
+  const float* bias_b;
 } lbca_cache_args;
 
 LBCA_API int lbca_cache_append(const lbca_cache_args* a, void* stream);

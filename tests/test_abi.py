@@ -164,6 +164,12 @@ def _cache(**kw):
     (dict(v_new=None, raw_v=None, out_v=None, rope_dims=24), -2),
     (dict(v_new=None, raw_v=None, out_v=None, rope_dims=64, rope_base=0.5), -1),
     (dict(raw_z=FAKE + 4), -1),                             # misaligned
+    (dict(v_new=None, raw_v=None, out_v=None, xb_new=FAKE), -1),   # partial dual arguments
+    (dict(xb_new=FAKE, zb_new=FAKE, raw_xb=FAKE, raw_zb=FAKE, bias_b=FAKE), -2),  # dual with values
+    (dict(v_new=None, raw_v=None, out_v=None, xb_new=FAKE, zb_new=FAKE, raw_xb=FAKE, raw_zb=FAKE,
+          bias_b=FAKE, ring=255), -1),                      # dual EXCLUSIVE needs ring >= W + 2m
+    (dict(v_new=None, raw_v=None, out_v=None, xb_new=FAKE, zb_new=FAKE, raw_xb=FAKE, raw_zb=FAKE,
+          bias_b=FAKE, mode=1, window=16, ring=127), -1),   # dual OVERLAP needs ring >= 2m
 ])
 def test_cache_validation(kw, code):
     assert _cache(**kw) == code

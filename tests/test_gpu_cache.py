@@ -35,7 +35,7 @@ def _dev(d):
 
 
 def _loop(lib, series, z, bias, m, W, mode, ring, entries, offsets, steps, check_at, v=None, treat=None,
-          on_check=None):
+          on_check=None, dual=None):
     """Append tokens 0.. of each sequence (sequence b starts at step offsets[b]); call
     on_check(step, t_list, raw_x, raw_v, raw_z, rpb, out_x, out_v) at the listed steps."""
     treat = treat or {}
@@ -47,6 +47,11 @@ def _loop(lib, series, z, bias, m, W, mode, ring, entries, offsets, steps, check
     out_v = None if v is None else torch.full_like(out_x, 7.0)
     rpb = torch.full((B,), -123, dtype=torch.int64, device=DEV)
     bidx = torch.arange(B, device=DEV)
+    if dual is not None:  # (xb, zb, bias_b): the b-series of dual (CSA) pooling
+        xb, zb, bias_b = dual
+        raw_xb, raw_zb = torch.full_like(raw_x, float("nan")), torch.full_like(raw_z, float("nan"))
+        dual_kw = lambda ti: dict(xb_new=xb[bidx, :, ti].contiguous(), zb_new=zb[bidx, :, ti].contiguous(),
+                                  raw_xb=raw_xb, raw_zb=raw_zb, bias_b=bias_b)
     for step in range(steps):
         t_list = [step - o for o in offsets]
         assert max(t_list) < T, "the history covers every appended position"
@@ -56,10 +61,13 @@ def _loop(lib, series, z, bias, m, W, mode, ring, entries, offsets, steps, check
         z_new = z[bidx, :, ti].contiguous()
         v_new = None if v is None else v[bidx, :, ti].contiguous()
         lib.cache_append(x_new, z_new, raw_x, raw_z, bias, pos, rpb, m, W, mode, out_x, v_new=v_new,
-                         raw_v=raw_v, out_v=out_v, **treat)
+                         raw_v=raw_v, out_v=out_v, **treat, **(dual_kw(ti) if dual is not None else {}))
         if step in check_at:
             torch.cuda.synchronize()
             on_check(step, t_list, raw_x, raw_v, raw_z, rpb, out_x, out_v)
+    if dual is not None:
+        torch.cuda.synchronize()
+        _check_ring([steps - 1 - o for o in offsets], m, W, mode, ring, raw_xb, raw_zb, rpb, xb, zb)
     return raw_x, raw_v, raw_z, rpb, out_x, out_v
 
 
@@ -200,3 +208,38 @@ def test_cache_due_entry_past_capacity(lib):
     n_p = [O.visible_range(t, m, W, O.EXCLUSIVE)[0] for t in t_end]
     assert n_p[0] > entries and n_p[1] <= entries
     assert torch.isnan(o[0]).all() and torch.isfinite(o[1]).all()
+
+
+def test_cache_overlap_csa_dual(lib):
+    # CSA: dual overlapped pooling (block j of the a-series with block j-1 of the b-series
+    # under one softmax), treated 512-dim entries, 4-token blocks, ring of 2m..W slots;
+    # 64 heads take the wide decode path
+    B, Hq, d, m, W, ring, T = 2, 64, 512, 4, 16, 20, 120
+    offsets = [0, 9]
+    C = _dev(synth.csa_layer("cache-csa", B, Hq, T, d, m, 8, 64))
+    treat = dict(rmsnorm_eps=1e-6, rope_dims=64)
+    entries = T // m
+    steps = 110
+    say(f"cache OVERLAP CSA dual: {steps} steps")
+    raw_x, _, raw_z, rpb, out_x, _ = _loop(lib, C["ca"], C["za"], C["bias_a"], m, W, O.OVERLAP, ring, entries,
+                                           offsets, steps, set(), treat=treat,
+                                           dual=(C["cb"], C["zb"], C["bias_b"]))
+    t_end = [steps - 1 - o for o in offsets]
+    _check_ring(t_end, m, W, O.OVERLAP, ring, raw_x, raw_z, rpb, C["ca"], C["za"])
+    ref = torch.full_like(out_x, 7.0)
+    lib.pool_blocks(C["ca"], C["za"], C["bias_a"], m, 0, entries, ref, xb=C["cb"], zb=C["zb"], bias_b=C["bias_b"],
+                    **treat)
+    pooled = O.pool_dual(host(C["ca"]), host(C["za"]), host(C["bias_a"][0]), host(C["cb"]), host(C["zb"]),
+                         host(C["bias_b"][0]), m, 0, entries)
+    treated = O.rope(O.rmsnorm(pooled, 1e-6), (np.arange(entries) * m)[None, None], 64, 10000.0)
+    for b, t in enumerate(t_end):
+        n_p, _ = O.visible_range(t, m, W, O.OVERLAP)
+        assert torch.equal(out_x[b, :, :n_p], ref[b, :, :n_p]), f"entries of sequence {b}"
+        assert (out_x[b, :, n_p:] == 7.0).all()
+        check_bf16(host(out_x[b, :, :n_p]), treated[b, :, :n_p], f"treated dual entries of sequence {b}")
+    pos = torch.tensor(t_end, dtype=torch.int64, device=DEV)
+    o, lse = lib.attend_decode(C["q"], out_x, raw_x, pos, m, W, O.OVERLAP, raw_pos_base=rpb, sink=C["sink"], **treat)
+    ro, rl = O.attend_decode(host(C["q"]), pooled, None, host(C["ca"]), None, t_end, m, W, O.OVERLAP,
+                             1 / math.sqrt(d), sink=host(C["sink"]), **treat)
+    check_bf16(host(o), ro, "decode over dual entries through the ring")
+    check_bf16(host(lse), rl, "lse")
