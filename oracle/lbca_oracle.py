@@ -257,6 +257,64 @@ def rope(x, pos, rope_dims, base):
     return x
 
 
+def treat_backward(x, grad_y, eps, rope_dims, base, pos):
+    """Gradient with respect to x of y = rope(rmsnorm(x, eps), pos, rope_dims,
+    base) for an upstream gradient ``grad_y`` (the chain rule through the
+    treatment of ``rmsnorm`` and ``rope`` above; eps < 0 means no RMSNorm,
+    rope_dims 0 no RoPE).
+
+    RoPE is a rotation, so its gradient turns grad_y back by the same angle; for
+    u = x / r, r = sqrt(mean(x^2) + eps), the gradient is
+    (g_u - u * mean(g_u * u)) / r.
+    """
+    x, g = _f64(x), _f64(grad_y)
+    if rope_dims:
+        g = rope(g, -np.asarray(pos, dtype=np.float64), rope_dims, base)
+    if eps is None or eps < 0:
+        return g
+    r = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    u = x / r
+    return (g - u * np.mean(g * u, axis=-1, keepdims=True)) / r
+
+
+def pool_dual_backward(ca, za, bias_a, cb, zb, bias_b, m, entry_begin, entry_end, grad_out):
+    """Gradients of ``pool_dual`` for upstream gradients ``grad_out`` [..., n, d]
+    of entries [entry_begin, entry_end): the single-series formulas of
+    ``pool_single_backward`` over the joint 2m-token softmax of each entry
+    (block i of the a-series, block i-1 of the b-series; block i alone for
+    i = 0).  Returns (d ca, d za, d bias_a, d cb, d zb, d bias_b); the biases
+    are [m, d] and sum over blocks and leading axes.
+    """
+    ca, za, cb, zb = _f64(ca), _f64(za), _f64(cb), _f64(zb)
+    ba, bb = _f64(bias_a), _f64(bias_b)
+    g = _f64(grad_out)
+    dca, dza, dcb, dzb = (np.zeros_like(a) for a in (ca, za, cb, zb))
+    dba, dbb = np.zeros(ca.shape[:-2] + ba.shape), np.zeros(ca.shape[:-2] + bb.shape)
+    for i in range(entry_begin, entry_end):
+        gi = g[..., i - entry_begin, None, :]                  # [..., 1, d]
+        la = za[..., i * m:(i + 1) * m, :] + ba
+        xa = ca[..., i * m:(i + 1) * m, :]
+        if i == 0:
+            logits, rows = la, xa
+        else:
+            logits = np.concatenate([la, zb[..., (i - 1) * m:i * m, :] + bb], axis=-2)
+            rows = np.concatenate([xa, cb[..., (i - 1) * m:i * m, :]], axis=-2)
+        w = _softmax_over_axis(logits, axis=-2)
+        out = (w * rows).sum(axis=-2, keepdims=True)
+        dx = w * gi
+        da = w * gi * (rows - out)
+        dca[..., i * m:(i + 1) * m, :] += dx[..., :m, :]
+        dza[..., i * m:(i + 1) * m, :] += da[..., :m, :]
+        dba += da[..., :m, :]
+        if i > 0:
+            dcb[..., (i - 1) * m:i * m, :] += dx[..., m:, :]
+            dzb[..., (i - 1) * m:i * m, :] += da[..., m:, :]
+            dbb += da[..., m:, :]
+    while dba.ndim > ba.ndim:
+        dba, dbb = dba.sum(axis=0), dbb.sum(axis=0)
+    return dca, dza, dba, dcb, dzb, dbb
+
+
 # ----------------------------------------------------------------------------
 # a5-a7, a10. Attention
 # ----------------------------------------------------------------------------

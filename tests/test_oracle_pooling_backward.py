@@ -1,4 +1,5 @@
-"""Pins for the oracle's pooling gradients (pool_single_backward) on the CPU.
+"""Pins for the oracle's pooling gradients (pool_single_backward,
+pool_dual_backward, treat_backward) on the CPU.
 
 The gradients are pinned against numbers the oracle's formula does not
 produce: central finite differences of the forward pooling (a plausible slip in
@@ -6,7 +7,10 @@ the backward, a dropped term, a wrong sign or index, a bias summed over the
 wrong axis, fails them), plus invariants of a per-channel softmax: the logit
 gradients of a block sum to zero per channel, the series gradients of a block
 sum to the upstream gradient, uniform logits spread it evenly, and a block
-size of one passes it straight through with zero logit gradient.
+size of one passes it straight through with zero logit gradient.  The entry
+treatment's gradient (RMSNorm, then partial RoPE) and the dual gradients are
+pinned by finite differences too; the RMSNorm gradient is orthogonal to its
+input row, and dual pooling with an absent b-part reduces to the single form.
 """
 import numpy as np
 import pytest
@@ -109,3 +113,49 @@ def test_empty_range():
     x = _rand(1, 1, 8, 2)
     dx, dv, dz, db = O.pool_single_backward(x, x, _rand(1, 4, 2), 4, 1, 1, np.zeros((1, 1, 0, 2)))
     assert dv is None and not dx.any() and not dz.any() and not db.any()
+
+
+@pytest.mark.parametrize("eps,r", [(1e-6, 0), (-1.0, 8), (1e-3, 8)])
+def test_treatment_gradient_matches_finite_differences(eps, r):
+    d, pos = 16, np.array([[3.0], [17.0]])
+    x = _rand(2, 2, d)
+    g = _rand(2, 2, d)
+    treat = lambda: O.rope(O.rmsnorm(x, eps) if eps >= 0 else x, pos, r, 10000.0)
+    dx = O.treat_backward(x, g, eps, r, 10000.0, pos)
+    np.testing.assert_allclose(dx, _numeric(lambda: float((treat() * g).sum()), x), rtol=1e-6, atol=1e-8)
+
+
+def test_treatment_gradient_is_orthogonal_to_the_row():
+    # RMSNorm output is invariant to scaling its input row, so the gradient has no
+    # component along x (after undoing the rotation, which keeps x fixed here: r = 0)
+    x, g = _rand(3, 32), _rand(3, 32)
+    dx = O.treat_backward(x, g, 0.0, 0, 10000.0, np.zeros((3, 1)))
+    np.testing.assert_allclose((dx * x).sum(axis=-1), 0.0, atol=1e-12)
+
+
+def test_dual_gradients_match_finite_differences():
+    B, H, m, d, n = 1, 2, 3, 2, 4
+    T = n * m
+    ca, za, cb, zb = _rand(B, H, T, d), _rand(B, H, T, d), _rand(B, H, T, d), _rand(B, H, T, d)
+    ba, bb = _rand(m, d, std=0.3), _rand(m, d, std=0.3)
+    e0, e1 = 0, n
+    g = _rand(B, H, e1 - e0, d)
+    f = lambda: float((O.pool_dual(ca, za, ba, cb, zb, bb, m, e0, e1) * g).sum())
+    dca, dza, dba, dcb, dzb, dbb = O.pool_dual_backward(ca, za, ba, cb, zb, bb, m, e0, e1, g)
+    for got, arr in ((dca, ca), (dza, za), (dba, ba), (dcb, cb), (dzb, zb), (dbb, bb)):
+        np.testing.assert_allclose(got, _numeric(f, arr), rtol=1e-6, atol=1e-8)
+    # the b-series block after the last entry's is unused
+    assert not dcb[..., (n - 1) * m:, :].any()
+
+
+def test_dual_with_absent_b_part_equals_single():
+    B, H, m, d, n = 1, 1, 4, 3, 3
+    x, z = _rand(B, H, n * m, d), _rand(B, H, n * m, d)
+    bias = _rand(m, d)
+    g = _rand(B, H, n, d)
+    dca, dza, dba, dcb, _, _ = O.pool_dual_backward(x, z, bias, x, np.full_like(z, -1e300), bias, m, 0, n, g)
+    sx, _, sz, sb = O.pool_single_backward(x, z, bias, m, 0, n, g)
+    np.testing.assert_allclose(dca, sx, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dza, sz, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dba, sb, rtol=1e-12, atol=1e-14)
+    assert np.abs(dcb).max() < 1e-300
