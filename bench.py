@@ -481,6 +481,20 @@ def run_csa(reps):
     g_pool = capture(pool)
     ms_pool = time_graph(g_pool, 3)
     pool_bytes = B * T * X_D * 2 * 4 + B * N * X_D * 2
+    # gradients of that pooling (dual series, treated entries) for one upstream gradient per entry
+    gd = synth.normal((B, 1, N, X_D), synth.seed_of("bench-csa-128k", "grad"), dtype="bf16", device=dev)
+    outs = dict(dx=torch.empty_like(C["ca"]), dz=torch.empty_like(C["za"]), dbias=torch.empty_like(C["bias_a"]),
+                dxb=torch.empty_like(C["cb"]), dzb=torch.empty_like(C["zb"]), dbias_b=torch.empty_like(C["bias_b"]))
+    dual = dict(xb=C["cb"], zb=C["zb"], bias_b=C["bias_b"])
+    nbw = lbca.pool_blocks_backward_workspace_bytes(C["ca"], C["za"], C["bias_a"], m, 0, N, gd, **dual, **treat)
+    wsb = torch.empty(max(nbw, 16), dtype=torch.uint8, device=dev)
+    back = lambda: lbca.pool_blocks_backward(C["ca"], C["za"], C["bias_a"], m, 0, N, gd, workspace=wsb, **dual,
+                                             **treat, **outs)
+    back()
+    g_back = capture(back)
+    ms_back = time_graph(g_back, 3)
+    back_bytes = B * T * X_D * 2 * 4 * 2 + B * N * X_D * 2  # a- and b-series rows and logits read and written
+    del gd, outs, dual, wsb, g_back
     raw = C["ca"][:, :, T - W:].contiguous()
     sink = C["sink"]
     del C, g_pool
@@ -532,6 +546,7 @@ def run_csa(reps):
             "decode_us": us_dec, "decode_GBps": by_dec / (us_dec * 1e-6) / 1e9,
             "decode_workspace_bytes": nws, "instances": n_inst,
             "pool_ms": ms_pool, "pool_GBps": pool_bytes / (ms_pool * 1e-3) / 1e9, "pool_bytes": pool_bytes,
+            "pool_backward_ms": ms_back, "pool_backward_GBps": back_bytes / (ms_back * 1e-3) / 1e9,
             "workload": f"CSA batch {B}, t = 2^17 - 1: top-{k} of {N} entries (8 x 64 indexer) + {W} raw, "
                         f"64 query heads x 512"}
 

@@ -110,6 +110,8 @@ static int validate_pool_grad(const lbca_pool_grad_args* a) {
     return LBCA_ERR_INVALID_ARG;
   const bool has_v = a->v != nullptr;
   if ((a->grad_v != nullptr) != has_v || (a->dv != nullptr) != has_v) return LBCA_ERR_INVALID_ARG;
+  const bool dual = a->xb || a->zb || a->bias_b || a->dxb || a->dzb || a->dbias_b;
+  if (dual && !(a->xb && a->zb && a->bias_b && a->dxb && a->dzb && a->dbias_b)) return LBCA_ERR_INVALID_ARG;
   if (!is_dtype(a->x_dtype) || !is_dtype(a->z_dtype)) return LBCA_ERR_INVALID_ARG;
   if (a->batch < 0 || a->heads < 1 || a->tokens < 0 || a->block < 1 || a->entries < 0)
     return LBCA_ERR_INVALID_ARG;
@@ -121,13 +123,19 @@ static int validate_pool_grad(const lbca_pool_grad_args* a) {
       !sane_product({a->batch, a->heads, a->entries, a->dim}) ||
       !sane_product({a->heads, a->block, a->dim}) || a->block_end > kMaxElems / a->block)
     return LBCA_ERR_INVALID_ARG;
-  if (a->block * a->dim > 8192 || a->heads > 65535) return LBCA_ERR_UNSUPPORTED;  // four tokens per lane
+  const bool treat = a->rmsnorm_eps >= 0.f || a->rope_dims != 0;
+  const int st = check_treatment(a->rmsnorm_eps, a->rope_dims, a->rope_base, a->dim);
+  if (st != LBCA_OK) return st;
+  if ((treat || dual) && has_v) return LBCA_ERR_UNSUPPORTED;
+  if ((dual ? 2 : 1) * a->block * a->dim > 8192 || a->heads > 65535) return LBCA_ERR_UNSUPPORTED;  // 4 tokens per lane
   if (!aligned16(a->x) || !aligned16(a->v) || !aligned16(a->z) || !aligned16(a->bias) ||
       !aligned16(a->grad_x) || !aligned16(a->grad_v) || !aligned16(a->dx) || !aligned16(a->dv) ||
-      !aligned16(a->dz) || !aligned16(a->dbias))
+      !aligned16(a->dz) || !aligned16(a->dbias) || !aligned16(a->xb) || !aligned16(a->zb) ||
+      !aligned16(a->bias_b) || !aligned16(a->dxb) || !aligned16(a->dzb) || !aligned16(a->dbias_b))
     return LBCA_ERR_INVALID_ARG;
   if (a->block_end > a->block_begin) {
-    const int64_t lo = a->block_begin * a->block - a->pos_base;
+    const int64_t first_block = (dual && a->block_begin > 0) ? a->block_begin - 1 : a->block_begin;
+    const int64_t lo = first_block * a->block - a->pos_base;
     const int64_t hi = a->block_end * a->block - a->pos_base;
     if (lo < 0 || hi > a->tokens) return LBCA_ERR_INVALID_ARG;
   }

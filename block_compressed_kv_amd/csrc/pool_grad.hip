@@ -38,7 +38,16 @@ struct PoolGradParams {
   void* dv;
   void* dz;
   float* dbias;
-  float* part;  // [heads][chunks][m][dim] bias-gradient partials
+  const void* xb;  // dual (CSA) mode: the b-series and its outputs
+  const void* zb;
+  const float* bias_b;
+  void* dxb;
+  void* dzb;
+  float* dbias_b;
+  float* part;  // [heads][chunks][M2][dim] bias-gradient partials (M2 = m, or 2m in dual mode)
+  float eps;    // treatment of the entry (shared series): < 0 no RMSNorm
+  int rope_dims;
+  double log2_base;
   int64_t batch, heads, tokens, dim, m, entries, block_begin, n_blocks, pos_base;
   int chunks, per_chunk;  // workgroups per head, blocks per workgroup
   int log2_lanes;
@@ -55,17 +64,19 @@ template <typename TX, typename TZ, bool HAS_V>
 struct BlockRows {
   static constexpr int NX = (int)(sizeof(TX) * 8 / 16), NZ = (int)(sizeof(TZ) * 8 / 16);
   uint4 x[kGradTPL][NX], v[kGradTPL][HAS_V ? NX : 1], z[kGradTPL][NZ];
-  __device__ __forceinline__ void load(const TX* xb, const TX* vb, const TZ* zb, int64_t stride, const bool* has) {
+  // token slot k's rows at element offset off[k] of its series (a or b per slot)
+  __device__ __forceinline__ void load(const TX* const* xs, const TX* vs, const TZ* const* zs, const int64_t* off,
+                                       const bool* present) {
 #pragma unroll
     for (int k = 0; k < kGradTPL; ++k) {
-      if (!has[k]) continue;
+      if (!present[k]) continue;
 #pragma unroll
       for (int i = 0; i < NX; ++i) {
-        x[k][i] = reinterpret_cast<const uint4*>(xb + k * stride)[i];
-        if constexpr (HAS_V) v[k][i] = reinterpret_cast<const uint4*>(vb + k * stride)[i];
+        x[k][i] = reinterpret_cast<const uint4*>(xs[k] + off[k])[i];
+        if constexpr (HAS_V) v[k][i] = reinterpret_cast<const uint4*>(vs + off[k])[i];
       }
 #pragma unroll
-      for (int i = 0; i < NZ; ++i) z[k][i] = reinterpret_cast<const uint4*>(zb + k * stride)[i];
+      for (int i = 0; i < NZ; ++i) z[k][i] = reinterpret_cast<const uint4*>(zs[k] + off[k])[i];
     }
   }
 };
@@ -178,10 +189,55 @@ __device__ __forceinline__ void merge_phases(GradState& st, float (*red)[64][32]
   st = acc;
 }
 
-template <typename TX, typename TZ, bool HAS_V>
+// The gradient of the treated entry y = rope(rmsnorm(e)) with respect to e,
+// for this lane's channels c0.. of a row held by the L lanes of a group
+// (every group holds the same row): the rotation back by the entry's angle
+// (partner dims k + r/2 sit r/16 lanes away; freq[k]: turns per position of
+// pair k, an LDS table), then the RMSNorm gradient
+// (g - u mean(g u)) / r with row sums over the group.  Every lane calls it.
+__device__ __forceinline__ void treat_grad(float (&g)[8], const float (&e)[8], int L, int64_t c0, int64_t dim,
+                                           double block_pos, float eps, int rope_dims, const double* freq) {
+  const int lane = threadIdx.x & 63;
+  if (rope_dims > 0) {
+    const int r = rope_dims, half = r >> 1;
+    const int64_t first = dim - r;
+    const bool lo_half = c0 >= first && c0 < first + half;
+    const bool hi_half = c0 >= first + half;
+    const int src = lo_half ? lane + (half >> 3) : (hi_half ? lane - (half >> 3) : lane);
+    float prt[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) prt[c] = __shfl(g[c], src, 64);
+    if (lo_half || hi_half) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int k = (int)(c0 + c - first) - (hi_half ? half : 0);
+        float cs, sn;
+        rope_cos_sin_turns(block_pos * freq[k], &cs, &sn);
+        g[c] = lo_half ? g[c] * cs + prt[c] * sn : g[c] * cs - prt[c] * sn;
+      }
+    }
+  }
+  if (eps >= 0.f) {
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) ss = fmaf(e[c], e[c], ss);
+    for (int o = L >> 1; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const float inv_r = 1.f / sqrtf(ss / (float)dim + eps);
+    float gu = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) gu = fmaf(g[c], e[c] * inv_r, gu);
+    for (int o = L >> 1; o > 0; o >>= 1) gu += __shfl_xor(gu, o, 64);
+    const float mean_gu = gu / (float)dim;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) g[c] = (g[c] - e[c] * inv_r * mean_gu) * inv_r;
+  }
+}
+
+template <typename TX, typename TZ, bool HAS_V, bool TREAT, bool DUAL>
 __global__ __launch_bounds__(kGradNT) void pool_grad_kernel(PoolGradParams p) {
   __shared__ float red[kGradNW][64][32];
-  __shared__ __attribute__((aligned(16))) float s_bias[8192];  // this head's bias rows, m * dim <= 8192
+  __shared__ __attribute__((aligned(16))) float s_bias[8192];  // bias rows of the token set, M2 * dim <= 8192
+  __shared__ double s_freq[TREAT ? 256 : 1];                     // RoPE turns per position, pair k
   const int tid = threadIdx.x, lane = tid & 63;
   const int L = 1 << p.log2_lanes;
   const int li = lane & (L - 1);
@@ -189,34 +245,53 @@ __global__ __launch_bounds__(kGradNT) void pool_grad_kernel(PoolGradParams p) {
   const int P = kGradNT >> p.log2_lanes;
   const int h = (int)blockIdx.y, chunk = (int)blockIdx.x;
   const int64_t dim = p.dim, m = p.m;
+  const int64_t M2 = DUAL ? 2 * m : m;  // tokens of an entry's softmax: block j (and block j-1 of the b-series)
   const int64_t c0 = (int64_t)li * 8;
   const int64_t list_n = p.batch * p.n_blocks;  // (sequence, block) pairs of this head
   const int64_t k0 = (int64_t)chunk * p.per_chunk;
   const int64_t k1 = k0 + p.per_chunk < list_n ? k0 + p.per_chunk : list_n;
 
-  bool has[kGradTPL];  // this lane's tokens of a block: offsets phase + P k, present when < m
+  // this lane's token slots: offset u = phase + P k of the token set, present when < M2;
+  // slots u >= m (dual mode) are block j-1 of the b-series
+  bool has[kGradTPL], is_b[kGradTPL];
+  int64_t uoff[kGradTPL];  // row offset from the entry's own block start
+  const TX* xser[kGradTPL];
+  const TZ* zser[kGradTPL];
 #pragma unroll
-  for (int k = 0; k < kGradTPL; ++k) has[k] = phase + (int64_t)P * k < m;
-  const int64_t tstride = (int64_t)P * dim;  // elements between this lane's tokens
-  auto rows_of = [&](int64_t kk, const TX*& xb, const TX*& vb, const TZ*& zb, int64_t& bh, int64_t& j) {
+  for (int k = 0; k < kGradTPL; ++k) {
+    const int64_t u = phase + (int64_t)P * k;
+    has[k] = u < M2;
+    is_b[k] = DUAL && u >= m;
+    uoff[k] = is_b[k] ? u - 2 * m : u;
+    xser[k] = static_cast<const TX*>(is_b[k] ? p.xb : p.x);
+    zser[k] = static_cast<const TZ*>(is_b[k] ? p.zb : p.z);
+  }
+  auto block_of = [&](int64_t kk, int64_t& bh, int64_t& j, int64_t (&off)[kGradTPL], bool (&present)[kGradTPL]) {
     const int64_t b = kk / p.n_blocks;
     j = p.block_begin + kk % p.n_blocks;
     bh = b * p.heads + h;
-    const int64_t o = (bh * p.tokens + j * m - p.pos_base + phase) * dim + c0;
-    xb = static_cast<const TX*>(p.x) + o;
-    vb = static_cast<const TX*>(p.v) + o;
-    zb = static_cast<const TZ*>(p.z) + o;
+    const int64_t row0 = bh * p.tokens + j * m - p.pos_base;
+#pragma unroll
+    for (int k = 0; k < kGradTPL; ++k) {
+      off[k] = (row0 + uoff[k]) * dim + c0;
+      present[k] = has[k] && !(is_b[k] && j == 0);  // entry 0 has no b-part
+    }
   };
   BlockRows<TX, TZ, HAS_V> cur;
   {
-    const TX *xb, *vb;
-    const TZ* zb;
-    int64_t bh, j;
-    rows_of(k0, xb, vb, zb, bh, j);
-    cur.load(xb, vb, zb, tstride, has);
+    int64_t bh, j, off[kGradTPL];
+    bool present[kGradTPL];
+    block_of(k0, bh, j, off, present);
+    cur.load(xser, static_cast<const TX*>(p.v), zser, off, present);
   }
-  for (int64_t e = tid * 4; e < m * dim; e += kGradNT * 4)
+  if constexpr (TREAT) {
+    if (tid < p.rope_dims / 2) s_freq[tid] = rope_turns_per_pos(tid, p.rope_dims, p.log2_base);
+  }
+  for (int64_t e = tid * 4; e < m * dim; e += kGradNT * 4) {
     *reinterpret_cast<float4*>(&s_bias[e]) = *reinterpret_cast<const float4*>(p.bias + h * m * dim + e);
+    if constexpr (DUAL)
+      *reinterpret_cast<float4*>(&s_bias[m * dim + e]) = *reinterpret_cast<const float4*>(p.bias_b + h * m * dim + e);
+  }
   __syncthreads();
 
   float db[kGradTPL][8];
@@ -226,10 +301,9 @@ __global__ __launch_bounds__(kGradNT) void pool_grad_kernel(PoolGradParams p) {
     for (int c = 0; c < 8; ++c) db[k][c] = 0.f;
 
   for (int64_t kk = k0; kk < k1; ++kk) {
-    const TX *xb, *vb;
-    const TZ* zb;
-    int64_t bh, j;
-    rows_of(kk, xb, vb, zb, bh, j);
+    int64_t bh, j, off[kGradTPL];
+    bool present[kGradTPL];
+    block_of(kk, bh, j, off, present);
     const int64_t eo = (bh * p.entries + j) * dim + c0;
     float g[8], gvv[8];
     load8(static_cast<const TX*>(p.gx) + eo, g);
@@ -238,7 +312,7 @@ __global__ __launch_bounds__(kGradNT) void pool_grad_kernel(PoolGradParams p) {
     float a[kGradTPL][8];
 #pragma unroll
     for (int k = 0; k < kGradTPL; ++k) {
-      if (!has[k]) continue;
+      if (!present[k]) continue;
       float zz[8];
       unpack_row<TZ>(cur.z[k], zz);
       const float* br = &s_bias[(phase + P * k) * dim + c0];
@@ -247,11 +321,10 @@ __global__ __launch_bounds__(kGradNT) void pool_grad_kernel(PoolGradParams p) {
     }
     BlockRows<TX, TZ, HAS_V> nxt;
     if (kk + 1 < k1) {
-      const TX *xn, *vn;
-      const TZ* zn;
-      int64_t bhn, jn;
-      rows_of(kk + 1, xn, vn, zn, bhn, jn);
-      nxt.load(xn, vn, zn, tstride, has);
+      int64_t bhn, jn, offn[kGradTPL];
+      bool presn[kGradTPL];
+      block_of(kk + 1, bhn, jn, offn, presn);
+      nxt.load(xser, static_cast<const TX*>(p.v), zser, offn, presn);
     }
     // this lane's state, then the block's
     GradState st;
@@ -260,14 +333,14 @@ __global__ __launch_bounds__(kGradNT) void pool_grad_kernel(PoolGradParams p) {
       float mx = kNegInf;
 #pragma unroll
       for (int k = 0; k < kGradTPL; ++k)
-        if (has[k]) mx = fmaxf(mx, a[k][c]);
+        if (present[k]) mx = fmaxf(mx, a[k][c]);
       st.mx[c] = mx;
       st.l[c] = st.sx[c] = st.sv[c] = 0.f;
     }
     // a[k][c] becomes the token's weight relative to this lane's maximum
 #pragma unroll
     for (int k = 0; k < kGradTPL; ++k) {
-      if (!has[k]) continue;
+      if (!present[k]) continue;
       float xs[8], vs[8];
       unpack_row<TX>(cur.x[k], xs);
       if constexpr (HAS_V) unpack_row<TX>(cur.v[k], vs);
@@ -292,10 +365,12 @@ __global__ __launch_bounds__(kGradNT) void pool_grad_kernel(PoolGradParams p) {
       ev[c] = st.sv[c] * inv;
       scale[c] = lmx[c] == kNegInf ? 0.f : fast_exp2(lmx[c] - st.mx[c]) * inv;
     }
+    // the upstream gradient of a treated entry, taken back to the pooled row
+    if constexpr (TREAT) treat_grad(g, ex, L, c0, dim, (double)(j * m), p.eps, p.rope_dims, s_freq);
     // gradients of this lane's tokens
 #pragma unroll
     for (int k = 0; k < kGradTPL; ++k) {
-      if (!has[k]) continue;
+      if (!present[k]) continue;
       float xs[8], vs[8];
       unpack_row<TX>(cur.x[k], xs);
       if constexpr (HAS_V) unpack_row<TX>(cur.v[k], vs);
@@ -312,31 +387,34 @@ __global__ __launch_bounds__(kGradNT) void pool_grad_kernel(PoolGradParams p) {
         oz[c] = w * da;
         db[k][c] += oz[c];
       }
-      const int64_t o = (xb - static_cast<const TX*>(p.x)) + k * tstride;
-      store8(static_cast<TX*>(p.dx) + o, ox);
-      if constexpr (HAS_V) store8(static_cast<TX*>(p.dv) + o, ov);
-      store8(static_cast<TZ*>(p.dz) + o, oz);
+      store8(static_cast<TX*>(is_b[k] ? p.dxb : p.dx) + off[k], ox);
+      if constexpr (HAS_V) store8(static_cast<TX*>(p.dv) + off[k], ov);
+      store8(static_cast<TZ*>(is_b[k] ? p.dzb : p.dz) + off[k], oz);
     }
     cur = nxt;
   }
-  // this workgroup's bias-gradient partial
-  float* part = p.part + (((int64_t)h * p.chunks + chunk) * m) * dim + c0;
+  // this workgroup's bias-gradient partial (rows u of the token set)
+  float* part = p.part + (((int64_t)h * p.chunks + chunk) * M2) * dim + c0;
 #pragma unroll
   for (int k = 0; k < kGradTPL; ++k)
     if (has[k]) store8(part + (phase + (int64_t)P * k) * dim, db[k]);
 }
 
-// dbias[h, i, c] = sum over chunks (in order) of the partials.
-__global__ __launch_bounds__(256) void pool_grad_bias_kernel(PoolGradParams p) {
-  const int64_t n = p.heads * p.m * p.dim;
+// dbias[h, i, c] (and, in dual mode, dbias_b[h, i, c] from rows m + i) = sum
+// over chunks (in order) of the partials.
+__global__ __launch_bounds__(256) void pool_grad_bias_kernel(PoolGradParams p, int dual) {
+  const int64_t M2 = dual ? 2 * p.m : p.m;
+  const int64_t n = p.heads * M2 * p.dim;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= n) return;
-  const int64_t md = p.m * p.dim;
+  const int64_t md = M2 * p.dim;
   const int64_t h = e / md, r = e % md;
   const float* src = p.part + h * p.chunks * md + r;
   float s = 0.f;
   for (int c = 0; c < p.chunks; ++c) s += src[(int64_t)c * md];
-  p.dbias[e] = s;
+  const int64_t u = r / p.dim, ch = r % p.dim;
+  if (u < p.m) p.dbias[(h * p.m + u) * p.dim + ch] = s;
+  else p.dbias_b[(h * p.m + u - p.m) * p.dim + ch] = s;
 }
 
 // Workgroups per head: about 1024 in all, each over consecutive blocks.
@@ -352,39 +430,48 @@ static void grad_plan(const lbca_pool_grad_args& a, int* chunks, int* per_chunk)
 size_t pool_grad_workspace_bytes(const lbca_pool_grad_args& a) {
   int chunks, per;
   grad_plan(a, &chunks, &per);
-  return (size_t)a.heads * (size_t)chunks * (size_t)(a.block * a.dim) * sizeof(float);
+  const int64_t m2 = a.xb ? 2 * a.block : a.block;
+  return (size_t)a.heads * (size_t)chunks * (size_t)(m2 * a.dim) * sizeof(float);
 }
 
 template <typename TX, typename TZ>
-static void launch_grad_typed(const PoolGradParams& p, bool has_v, dim3 grid, hipStream_t s) {
-  if (has_v) pool_grad_kernel<TX, TZ, true><<<grid, kGradNT, 0, s>>>(p);
-  else pool_grad_kernel<TX, TZ, false><<<grid, kGradNT, 0, s>>>(p);
+static void launch_grad_typed(const PoolGradParams& p, bool has_v, bool treat, bool dual, dim3 grid, hipStream_t s) {
+  if (has_v) pool_grad_kernel<TX, TZ, true, false, false><<<grid, kGradNT, 0, s>>>(p);
+  else if (dual && treat) pool_grad_kernel<TX, TZ, false, true, true><<<grid, kGradNT, 0, s>>>(p);
+  else if (dual) pool_grad_kernel<TX, TZ, false, false, true><<<grid, kGradNT, 0, s>>>(p);
+  else if (treat) pool_grad_kernel<TX, TZ, false, true, false><<<grid, kGradNT, 0, s>>>(p);
+  else pool_grad_kernel<TX, TZ, false, false, false><<<grid, kGradNT, 0, s>>>(p);
 }
 
 hipError_t launch_pool_grad(const lbca_pool_grad_args& a, void* ws, hipStream_t stream) {
   PoolGradParams p;
   p.x = a.x; p.v = a.v; p.z = a.z; p.bias = a.bias; p.gx = a.grad_x; p.gv = a.grad_v;
   p.dx = a.dx; p.dv = a.dv; p.dz = a.dz; p.dbias = a.dbias; p.part = static_cast<float*>(ws);
+  p.xb = a.xb; p.zb = a.zb; p.bias_b = a.bias_b; p.dxb = a.dxb; p.dzb = a.dzb; p.dbias_b = a.dbias_b;
+  p.eps = a.rmsnorm_eps; p.rope_dims = a.rope_dims;
+  p.log2_base = a.rope_dims > 0 ? log2((double)a.rope_base) : 0.0;
   p.batch = a.batch; p.heads = a.heads; p.tokens = a.tokens; p.dim = a.dim; p.m = a.block;
   p.entries = a.entries; p.block_begin = a.block_begin; p.n_blocks = a.block_end - a.block_begin;
   p.pos_base = a.pos_base;
   grad_plan(a, &p.chunks, &p.per_chunk);
   p.log2_lanes = __builtin_ctz((unsigned)(a.dim / 8));
+  const bool dual = a.xb != nullptr;
+  const bool treat = a.rmsnorm_eps >= 0.f || a.rope_dims > 0;
   if (p.chunks > 0) {
     const dim3 grid((unsigned)p.chunks, (unsigned)a.heads);
     const bool has_v = a.v != nullptr;
     if (a.x_dtype == LBCA_BF16) {
-      if (a.z_dtype == LBCA_BF16) launch_grad_typed<bf16_t, bf16_t>(p, has_v, grid, stream);
-      else launch_grad_typed<bf16_t, float>(p, has_v, grid, stream);
+      if (a.z_dtype == LBCA_BF16) launch_grad_typed<bf16_t, bf16_t>(p, has_v, treat, dual, grid, stream);
+      else launch_grad_typed<bf16_t, float>(p, has_v, treat, dual, grid, stream);
     } else {
-      if (a.z_dtype == LBCA_BF16) launch_grad_typed<float, bf16_t>(p, has_v, grid, stream);
-      else launch_grad_typed<float, float>(p, has_v, grid, stream);
+      if (a.z_dtype == LBCA_BF16) launch_grad_typed<float, bf16_t>(p, has_v, treat, dual, grid, stream);
+      else launch_grad_typed<float, float>(p, has_v, treat, dual, grid, stream);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t n = a.heads * a.block * a.dim;
-  pool_grad_bias_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(p);
+  const int64_t n = a.heads * (dual ? 2 : 1) * a.block * a.dim;
+  pool_grad_bias_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(p, dual ? 1 : 0);
   return hipGetLastError();
 }
 

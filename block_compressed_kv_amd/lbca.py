@@ -39,7 +39,9 @@ class PoolGradArgs(ctypes.Structure):
                 ("dx", _vp), ("dv", _vp), ("dz", _vp), ("dbias", _vp),
                 ("batch", _i64), ("heads", _i64), ("tokens", _i64), ("dim", _i64), ("block", _i64),
                 ("entries", _i64), ("block_begin", _i64), ("block_end", _i64), ("pos_base", _i64),
-                ("x_dtype", _i32), ("z_dtype", _i32)]
+                ("x_dtype", _i32), ("z_dtype", _i32), ("rmsnorm_eps", _f32), ("rope_dims", _i32),
+                ("rope_base", _f32), ("xb", _vp), ("zb", _vp), ("bias_b", _vp), ("dxb", _vp), ("dzb", _vp),
+                ("dbias_b", _vp)]
 
 
 class CacheArgs(ctypes.Structure):
@@ -182,31 +184,41 @@ def pool_blocks(x, z, bias, block, block_begin, block_end, out_x, v=None, out_v=
 
 
 def _pool_grad_args(x, z, bias, block, block_begin, block_end, grad_x, dx, dz, dbias, v, grad_v, dv,
-                    pos_base):
+                    pos_base, rmsnorm_eps=None, rope_dims=0, rope_base=10000.0, xb=None, zb=None, bias_b=None,
+                    dxb=None, dzb=None, dbias_b=None):
     for t, n in ((x, "x"), (v, "v"), (z, "z"), (grad_x, "grad_x"), (grad_v, "grad_v"), (dx, "dx"),
-                 (dv, "dv"), (dz, "dz")):
+                 (dv, "dv"), (dz, "dz"), (xb, "xb"), (zb, "zb"), (dxb, "dxb"), (dzb, "dzb")):
         _need(t, n, 4)
-    _need(bias, "bias", 3)
-    _need(dbias, "dbias", 3)
+    for t, n in ((bias, "bias"), (dbias, "dbias"), (bias_b, "bias_b"), (dbias_b, "dbias_b")):
+        _need(t, n, 3)
     B, H, T, d = x.shape
     return PoolGradArgs(_p(x), _p(v), _p(z), _p(bias), _p(grad_x), _p(grad_v), _p(dx), _p(dv), _p(dz),
                         _p(dbias), B, H, T, d, block, grad_x.shape[2], block_begin, block_end, pos_base,
-                        _dt(x), _dt(z))
+                        _dt(x), _dt(z), -1.0 if rmsnorm_eps is None else float(rmsnorm_eps), int(rope_dims),
+                        float(rope_base), _p(xb), _p(zb), _p(bias_b), _p(dxb), _p(dzb), _p(dbias_b))
 
 
 def pool_blocks_backward(x, z, bias, block, block_begin, block_end, grad_x, v=None, grad_v=None, dx=None,
-                         dv=None, dz=None, dbias=None, pos_base=0, workspace=None, stream=None):
-    """lbca_pool_blocks_backward: gradients of pool_blocks (single series, optional values).
-    Returns (dx, dv or None, dz, dbias); missing outputs are allocated (rows outside the
-    pooled blocks of new outputs are zeros)."""
+                         dv=None, dz=None, dbias=None, pos_base=0, workspace=None, rmsnorm_eps=None, rope_dims=0,
+                         rope_base=10000.0, xb=None, zb=None, bias_b=None, dxb=None, dzb=None, dbias_b=None,
+                         stream=None):
+    """lbca_pool_blocks_backward: gradients of pool_blocks (single series with optional values,
+    the shared series with its entry treatment, or dual mode with xb, zb, bias_b).
+    Returns (dx, dv or None, dz, dbias), plus (dxb, dzb, dbias_b) in dual mode; missing outputs
+    are allocated (rows outside the pooled blocks of new outputs are zeros)."""
     dx = torch.zeros_like(x) if dx is None else dx
     dz = torch.zeros_like(z) if dz is None else dz
     if v is not None and dv is None:
         dv = torch.zeros_like(v)
     if dbias is None:
         dbias = torch.empty_like(bias)
+    dual = xb is not None
+    if dual:
+        dxb = torch.zeros_like(xb) if dxb is None else dxb
+        dzb = torch.zeros_like(zb) if dzb is None else dzb
+        dbias_b = torch.empty_like(bias_b) if dbias_b is None else dbias_b
     a = _pool_grad_args(x, z, bias, block, block_begin, block_end, grad_x, dx, dz, dbias, v, grad_v, dv,
-                        pos_base)
+                        pos_base, rmsnorm_eps, rope_dims, rope_base, xb, zb, bias_b, dxb, dzb, dbias_b)
     if workspace is None:
         n = ctypes.c_size_t()
         _check(lib().lbca_pool_blocks_backward_workspace(ctypes.byref(a), ctypes.byref(n)),
@@ -214,12 +226,14 @@ def pool_blocks_backward(x, z, bias, block, block_begin, block_end, grad_x, v=No
         workspace = torch.empty(max(n.value, 16), dtype=torch.uint8, device=x.device)
     _check(lib().lbca_pool_blocks_backward(ctypes.byref(a), _p(workspace), workspace.numel(), _stream(stream)),
            "lbca_pool_blocks_backward")
-    return dx, dv, dz, dbias
+    return (dx, dv, dz, dbias, dxb, dzb, dbias_b) if dual else (dx, dv, dz, dbias)
 
 
 def pool_blocks_backward_workspace_bytes(x, z, bias, block, block_begin, block_end, grad_x, v=None,
-                                         grad_v=None, pos_base=0):
-    a = _pool_grad_args(x, z, bias, block, block_begin, block_end, grad_x, x, z, bias, v, grad_v, v, pos_base)
+                                         grad_v=None, pos_base=0, xb=None, zb=None, bias_b=None, **treat):
+    a = _pool_grad_args(x, z, bias, block, block_begin, block_end, grad_x, x, z, bias, v, grad_v, v, pos_base,
+                        treat.get("rmsnorm_eps"), treat.get("rope_dims", 0), treat.get("rope_base", 10000.0),
+                        xb, zb, bias_b, xb, zb, bias_b)
     n = ctypes.c_size_t()
     _check(lib().lbca_pool_blocks_backward_workspace(ctypes.byref(a), ctypes.byref(n)),
            "lbca_pool_blocks_backward_workspace")

@@ -153,15 +153,28 @@ LBCA_API int lbca_pool_blocks(const lbca_pool_args* a, void* stream);
  * with the entries recomputed in fp32.  Token rows of those blocks are
  * written in dx, dv, dz; every other row is left as is.  dbias is overwritten
  * (zeros for an empty range).  Results are bitwise reproducible.
+ * Treatment (shared series only; HCA/CSA "What is implemented"): with
+ * rmsnorm_eps >= 0 and/or rope_dims > 0 the stored entries were
+ * rope(rmsnorm(out_x[j])) at position j*m (as lbca_pool_blocks writes them)
+ * and grad_x is the gradient of those; it is taken back through the rotation
+ * and the RMSNorm before the formulas above.
+ * Dual mode (xb != NULL, CSA "What is implemented" item 1): entry j's softmax
+ * also covers block j-1 of the b-series (xb, zb, bias_b); its rows get dxb,
+ * dzb and its bias offsets dbias_b by the same formulas (entry 0 has no
+ * b-part); b-series rows of blocks [max(block_begin,1)-1, block_end-1) are
+ * written.
  *
  *   x, v, z            [batch, heads, tokens, dim]; row r holds position pos_base+r
  *   bias               [heads, block, dim] float32
  *   grad_x, grad_v     [batch, heads, entries, dim]   (x_dtype)
  *   dx, dv / dz        [batch, heads, tokens, dim]    (x_dtype / z_dtype)
  *   dbias              [heads, block, dim] float32
- * v, grad_v and dv are all NULL without values.  No treatment, no dual mode.
- * Constraints: dim a power of two in [8, 512], block * dim <= 8192,
- * heads <= 65535.  Workspace (lbca_pool_blocks_backward_workspace bytes,
+ *   xb, zb, dxb, dzb   [batch, heads, tokens, dim]; bias_b, dbias_b [heads, block, dim]
+ * v, grad_v and dv are all NULL without values; xb, zb, bias_b, dxb, dzb,
+ * dbias_b all NULL outside dual mode.  Treatment and dual mode need a shared
+ * series (no values).
+ * Constraints: dim a power of two in [8, 512], block * dim <= 8192 (dual:
+ * 2 * block * dim <= 8192), heads <= 65535.  Workspace (lbca_pool_blocks_backward_workspace bytes,
  * 16-byte aligned, caller-owned, no initialisation needed): the bias-gradient
  * partials.  Errors as lbca_pool_blocks, plus WORKSPACE.
  */
@@ -180,6 +193,15 @@ typedef struct lbca_pool_grad_args {
   int64_t block_begin, block_end;
   int64_t pos_base;
   int32_t x_dtype, z_dtype;
+  float rmsnorm_eps; /* treatment of the stored entries: < 0 off */
+  int32_t rope_dims; /* 0: off */
+  float rope_base;
+  const void* xb;    /* dual mode: the b-series, its bias and outputs */
+  const void* zb;
+  const float* bias_b;
+  void* dxb;
+  void* dzb;
+  float* dbias_b;
 } lbca_pool_grad_args;
 
 LBCA_API int lbca_pool_blocks_backward_workspace(const lbca_pool_grad_args* a, size_t* bytes);

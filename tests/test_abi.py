@@ -101,7 +101,7 @@ def test_pool_empty_range_is_ok_without_gpu():
 def _pgrad(ws=None, ws_bytes=0, **kw):
     a = dict(x=FAKE, v=FAKE, z=FAKE, bias=FAKE, grad_x=FAKE, grad_v=FAKE, dx=FAKE, dv=FAKE, dz=FAKE,
              dbias=FAKE, batch=2, heads=8, tokens=4096, dim=128, block=64, entries=64, block_begin=0,
-             block_end=64, pos_base=0, x_dtype=1, z_dtype=0)
+             block_end=64, pos_base=0, x_dtype=1, z_dtype=0, rmsnorm_eps=-1.0, rope_dims=0, rope_base=10000.0)
     a.update(kw)
     s = lbca.PoolGradArgs(**a)
     n = ctypes.c_size_t()
@@ -122,6 +122,14 @@ def _pgrad(ws=None, ws_bytes=0, **kw):
     (dict(block_end=65), -1), (dict(block_begin=3, block_end=2), -1),
     (dict(tokens=4095), -1), (dict(pos_base=64), -1),                     # rows outside the buffer
     (dict(dz=FAKE + 4), -1),                                              # misaligned
+    (dict(rmsnorm_eps=1e-6), -2),                                         # treatment needs a shared series
+    (dict(v=None, grad_v=None, dv=None, rope_dims=24), -2),
+    (dict(v=None, grad_v=None, dv=None, xb=FAKE), -1),                    # partial dual arguments
+    (dict(xb=FAKE, zb=FAKE, bias_b=FAKE, dxb=FAKE, dzb=FAKE, dbias_b=FAKE), -2),   # dual with values
+    (dict(v=None, grad_v=None, dv=None, xb=FAKE, zb=FAKE, bias_b=FAKE, dxb=FAKE, dzb=FAKE, dbias_b=FAKE),
+     -2),                                                                 # dual: 2 * block * dim > 8192
+    (dict(v=None, grad_v=None, dv=None, xb=FAKE, zb=FAKE, bias_b=FAKE, dxb=FAKE, dzb=FAKE, dbias_b=FAKE,
+          block=32, block_begin=1, block_end=64, pos_base=32), -1),       # dual reads block begin-1
 ])
 def test_pool_grad_validation(kw, code):
     st_ws, st, _ = _pgrad(**kw)

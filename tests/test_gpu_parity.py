@@ -138,6 +138,48 @@ def test_pool_backward(lib, xdt, zdt, B, H, T, d, m, b0, b1, pb, with_v):
     assert (db3 == 0).all() and (dz3 == 0).all()
 
 
+@pytest.mark.parametrize("form,d,m,b0,b1", [
+    ("hca", 512, 16, 2, 30),      # shared series, RMSNorm + RoPE on the stored entries
+    ("csa", 512, 4, 3, 40),       # dual series (block j with b-block j-1), treated
+    ("csa-plain", 64, 4, 0, 45),  # dual series without treatment, entry 0 without a b-part
+])
+def test_pool_backward_treated_and_dual(lib, form, d, m, b0, b1):
+    say(f"pool backward {form} d={d} m={m} blocks [{b0},{b1})")
+    B, T = 2, 4 * 128
+    N = T // m
+    treat = {} if form == "csa-plain" else dict(rmsnorm_eps=1e-6, rope_dims=64, rope_base=10000.0)
+    g = synth.normal((B, 1, N, d), synth.seed_of("pool-grad-treat", form), dtype="bf16", device=DEV)
+    gi = host(g)[:, :, b0:b1]
+    pos = (np.arange(b0, b1) * m)[None, None, :]          # each entry's block start
+    if form == "hca":
+        H = _dev(synth.hca_layer(f"pool-grad-{form}", B, 4, T, d, m))
+        x, z, bias = H["c"], H["z"], H["bias"]
+        dx, _, dz, dbias = lib.pool_blocks_backward(x, z, bias, m, b0, b1, g, **treat)
+        pooled = O.pool_single(host(x), host(z), host(bias), m, b0, b1)
+        ge = O.treat_backward(pooled, gi, 1e-6, 64, 10000.0, pos)
+        rx, _, rz, rb = O.pool_single_backward(host(x), host(z), host(bias), m, b0, b1, ge)
+    else:
+        C = _dev(synth.csa_layer(f"pool-grad-{form}", B, 4, T, d, m, 8, 64))
+        x, z, bias = C["ca"], C["za"], C["bias_a"]
+        dx, _, dz, dbias, dxb, dzb, dbias_b = lib.pool_blocks_backward(
+            x, z, bias, m, b0, b1, g, xb=C["cb"], zb=C["zb"], bias_b=C["bias_b"], **treat)
+        pooled = O.pool_dual(host(x), host(z), host(bias[0]), host(C["cb"]), host(C["zb"]), host(C["bias_b"][0]),
+                             m, b0, b1)
+        ge = O.treat_backward(pooled, gi, 1e-6, 64, 10000.0, pos) if treat else gi
+        rx, rz, rb, rxb, rzb, rbb = O.pool_dual_backward(host(x), host(z), host(bias[0]), host(C["cb"]),
+                                                         host(C["zb"]), host(C["bias_b"][0]), m, b0, b1, ge)
+        lo_b, hi_b = (max(b0, 1) - 1) * m, (b1 - 1) * m
+        check_bf16(host(dxb[:, :, lo_b:hi_b]), rxb[:, :, lo_b:hi_b], "d b-series")
+        check_bf16(host(dzb[:, :, lo_b:hi_b]), rzb[:, :, lo_b:hi_b], "d b-logits")
+        check("f32", host(dbias_b[0]), rbb, "d bias_b")
+        assert (dxb[:, :, :lo_b] == 0).all() and (dxb[:, :, hi_b:] == 0).all()
+    lo, hi = b0 * m, b1 * m
+    check_bf16(host(dx[:, :, lo:hi]), rx[:, :, lo:hi], "d series")
+    check_bf16(host(dz[:, :, lo:hi]), rz[:, :, lo:hi], "d logits")
+    check("f32", host(dbias if form == "hca" else dbias[0]), rb, "d bias")
+    assert (dx[:, :, :lo] == 0).all() and (dx[:, :, hi:] == 0).all()
+
+
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
