@@ -74,10 +74,12 @@ def hca_layer(tag, B, Hq, T, d, m, dtype="bf16", device="cpu", bias_std=0.1):
     }
 
 
-def csa_layer(tag, B, Hq, T, d, m, HI, dI, dtype="bf16", device="cpu", bias_std=0.1):
+def csa_layer(tag, B, Hq, T, d, m, HI, dI, dtype="bf16", device="cpu", bias_std=0.1, q_len=None):
     """CSA: a- and b-series with logits and biases for the core entries (dim d)
     and for the indexer keys (dim dI), decode queries, indexer queries and head
-    weights U(0,1), sink logits."""
+    weights U(0,1), sink logits.  With q_len, a chunk of q_len queries per
+    sequence: q [B, q_len, Hq, d], qi [B, q_len, HI, dI], w [B, q_len, HI]."""
+    lead = (B,) if q_len is None else (B, q_len)
     out = {}
     for s in ("a", "b"):
         out["c" + s] = normal((B, 1, T, d), seed_of(tag, "c" + s), dtype=dtype, device=device)
@@ -86,8 +88,8 @@ def csa_layer(tag, B, Hq, T, d, m, HI, dI, dtype="bf16", device="cpu", bias_std=
         out["ic" + s] = normal((B, 1, T, dI), seed_of(tag, "ic" + s), dtype=dtype, device=device)
         out["iz" + s] = normal((B, 1, T, dI), seed_of(tag, "iz" + s), dtype=dtype, device=device)
         out["ibias_" + s] = normal((1, m, dI), seed_of(tag, "ibias_" + s), std=bias_std, device=device)
-    out["q"] = normal((B, Hq, d), seed_of(tag, "q"), dtype=dtype, device=device)
-    out["qi"] = normal((B, HI, dI), seed_of(tag, "qi"), dtype=dtype, device=device)
-    out["w"] = uniform((B, HI), seed_of(tag, "w"), device=device)
+    out["q"] = normal(lead + (Hq, d), seed_of(tag, "q"), dtype=dtype, device=device)
+    out["qi"] = normal(lead + (HI, dI), seed_of(tag, "qi"), dtype=dtype, device=device)
+    out["w"] = uniform(lead + (HI,), seed_of(tag, "w"), device=device)
     out["sink"] = normal((Hq,), seed_of(tag, "sink"), device=device)
     return out

@@ -543,3 +543,33 @@ def csa_index_topk(qi, w, ki, t, m, k):
         ok = sel >= 0
         sc[b, ok] = s[sel[ok]]
     return idx, sc
+
+
+def csa_sparse_prefill(qi, w, ki, q, entries, raw, raw_pos_base, q_pos0, m, W, k, scale,
+                       sink=None, rmsnorm_eps=None, rope_dims=0, rope_base=10000.0):
+    """CSA prefill of a chunk of consecutive queries ([CSA] "What is implemented",
+    second and third items, taken for every query of a chunk): query i sits at
+    t = q_pos0 + i, scores the indexer keys visible at t (OVERLAP rule), keeps
+    its own top-k, and attends to those entries plus its W-token raw window
+    under one softmax (MQA, shared K = V series), exactly the decode rule at t.
+
+    qi [B, Tq, HI, dI], w [B, Tq, HI], ki [B, N, dI]; q [B, Tq, Hq, d];
+    entries [B, N, d] (pooled, before the treatment); raw [B, R, d] with row r
+    at position raw_pos_base + r.  Returns idx [B, Tq, k] (ascending, -1
+    padded), o [B, Tq, Hq, d], lse [B, Tq, Hq].
+    """
+    B, Tq = q.shape[0], q.shape[1]
+    idx = np.full((B, Tq, k), -1, dtype=np.int64)
+    o = np.zeros(q.shape)
+    lse = np.zeros(q.shape[:3])
+    for b in range(B):
+        for i in range(Tq):
+            t = q_pos0 + i
+            sel, _ = csa_index_topk(qi[b, i][None], w[b, i][None], ki[b][None], [t], m, k)
+            idx[b, i] = sel[0]
+            ob, lb = attend_decode(q[b, i][None], entries[b][None, None], None, raw[b][None, None], None,
+                                   [t], m, W, OVERLAP, scale, raw_pos_base=[raw_pos_base], sel_idx=sel,
+                                   sink=sink, rmsnorm_eps=rmsnorm_eps, rope_dims=rope_dims,
+                                   rope_base=rope_base)
+            o[b, i], lse[b, i] = ob[0], lb[0]
+    return idx, o, lse
