@@ -323,6 +323,113 @@ int csa_index_topk_workspace(const csa_index_args* a, size_t* bytes) {
   return LBCA_OK;
 }
 
+// ---------------------------------------------------------------------------
+namespace {
+
+int validate_csa_prefill(const csa_prefill_args* a) {
+  if (!a || !a->q_idx || !a->head_w || !a->idx_keys || !a->q || !a->entries || !a->raw || !a->out)
+    return LBCA_ERR_INVALID_ARG;
+  if (!is_dtype(a->dtype)) return LBCA_ERR_INVALID_ARG;
+  if (a->dtype != LBCA_BF16) return LBCA_ERR_UNSUPPORTED;
+  if (a->batch < 0 || a->q_len < 0 || a->idx_heads < 1 || a->idx_dim < 1 || a->q_heads < 1 || a->dim < 1 ||
+      a->n_entries < 0 || a->raw_rows < 1 || a->k < 1 || a->q_pos0 < 0 || a->block < 1 || a->window < 1)
+    return LBCA_ERR_INVALID_ARG;
+  if (!isfinite(a->scale)) return LBCA_ERR_INVALID_ARG;
+  if (!sane_product({a->batch, a->q_len, a->q_heads, a->dim}) ||
+      !sane_product({a->batch, a->q_len, a->idx_heads, a->idx_dim}) ||
+      !sane_product({a->batch, a->n_entries, a->dim}) || !sane_product({a->batch, a->raw_rows, a->dim}) ||
+      !sane_product({a->batch, a->q_len, a->n_entries}) || !sane_product({a->batch, a->q_len, a->k}) ||
+      a->q_pos0 > kMaxElems || a->raw_pos_base < -kMaxElems || a->raw_pos_base > kMaxElems)
+    return LBCA_ERR_INVALID_ARG;
+  const int st = check_treatment(a->rmsnorm_eps, a->rope_dims, a->rope_base, a->dim);
+  if (st != LBCA_OK) return st;
+  if (!(a->idx_dim == 32 || a->idx_dim == 64 || a->idx_dim == 128) || a->idx_heads > 16 || a->k > 2048 ||
+      a->n_entries > 65536)
+    return LBCA_ERR_UNSUPPORTED;
+  if (a->dim != 512 || a->q_heads % 32 != 0 || a->q_heads > 64 || a->batch * a->q_len > 65535 ||
+      a->n_entries * a->dim >= (int64_t(1) << 30) || a->raw_rows * a->dim >= (int64_t(1) << 30))
+    return LBCA_ERR_UNSUPPORTED;
+  if (!aligned16(a->q_idx) || !aligned16(a->head_w) || !aligned16(a->idx_keys) || !aligned16(a->q) ||
+      !aligned16(a->entries) || !aligned16(a->raw) || !aligned16(a->out) || !aligned16(a->out_idx))
+    return LBCA_ERR_INVALID_ARG;
+  if (a->q_len > 0) {
+    const int64_t t_last = a->q_pos0 + a->q_len - 1;
+    if ((t_last + 1) / a->block > a->n_entries) return LBCA_ERR_INVALID_ARG;
+    const int64_t lo = a->q_pos0 - a->window + 1 > 0 ? a->q_pos0 - a->window + 1 : 0;
+    if (lo < a->raw_pos_base || t_last - a->raw_pos_base >= a->raw_rows) return LBCA_ERR_INVALID_ARG;
+  }
+  return LBCA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// The two calls a chunk runs (selection over rows = batch * q_len queries, then
+// the selected-entry attention over the same rows) and their workspace layout:
+// positions, raw bases, selections, index workspace, decode workspace.
+struct CsaPrefillPlan {
+  csa_index_args ia;
+  lbca_decode_args da;
+  lbca::DecodePlan dp;
+  size_t off_rpb, off_idx, off_index, off_decode, total;
+};
+
+CsaPrefillPlan plan_csa_prefill(const csa_prefill_args* a) {
+  CsaPrefillPlan pl{};
+  const int64_t rows = a->batch * a->q_len;
+  pl.ia.q_idx = a->q_idx; pl.ia.head_w = a->head_w; pl.ia.keys = a->idx_keys;
+  pl.ia.out_idx = a->out_idx; pl.ia.out_score = nullptr;
+  pl.ia.batch = rows; pl.ia.heads = a->idx_heads; pl.ia.dim = a->idx_dim; pl.ia.entries = a->n_entries;
+  pl.ia.k = a->k; pl.ia.block = a->block; pl.ia.dtype = a->dtype;
+  pl.da.q = a->q; pl.da.pooled_k = a->entries; pl.da.raw_k = a->raw; pl.da.sink = a->sink;
+  pl.da.out = a->out; pl.da.lse = a->lse;
+  pl.da.batch = rows; pl.da.q_heads = a->q_heads; pl.da.kv_heads = 1; pl.da.dim = a->dim;
+  pl.da.entries = a->n_entries; pl.da.raw_rows = a->raw_rows; pl.da.k_sel = a->k;
+  pl.da.block = a->block; pl.da.window = a->window; pl.da.mode = LBCA_OVERLAP; pl.da.dtype = a->dtype;
+  pl.da.scale = a->scale; pl.da.rmsnorm_eps = a->rmsnorm_eps; pl.da.rope_dims = a->rope_dims;
+  pl.da.rope_base = a->rope_base;
+  pl.da.sel_idx = reinterpret_cast<const int32_t*>(1);  // planned as a selection; set at launch
+  if (rows > 0) pl.dp = lbca::plan_decode(pl.da);  // (its split sizing divides by the rows)
+  const size_t r = (size_t)rows;
+  pl.off_rpb = align256(r * sizeof(int64_t));
+  pl.off_idx = pl.off_rpb + align256(r * sizeof(int64_t));
+  pl.off_index = pl.off_idx + (a->out_idx ? 0 : align256(r * (size_t)a->k * sizeof(int32_t)));
+  pl.off_decode = pl.off_index + align256(lbca::index_workspace_bytes(pl.ia));
+  pl.total = pl.off_decode + pl.dp.ws_bytes;
+  return pl;
+}
+
+}  // namespace
+
+int csa_sparse_prefill_workspace(const csa_prefill_args* a, size_t* bytes) {
+  if (!bytes) return LBCA_ERR_INVALID_ARG;
+  const int st = validate_csa_prefill(a);
+  if (st != LBCA_OK) return st;
+  *bytes = plan_csa_prefill(a).total;
+  return LBCA_OK;
+}
+
+int csa_sparse_prefill(const csa_prefill_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = validate_csa_prefill(a);
+  if (st != LBCA_OK) return st;
+  CsaPrefillPlan pl = plan_csa_prefill(a);
+  if (workspace == nullptr || workspace_bytes < pl.total || !aligned16(workspace)) return LBCA_ERR_WORKSPACE;
+  if (a->batch * a->q_len == 0) return LBCA_OK;
+  char* ws = static_cast<char*>(workspace);
+  int64_t* pos = reinterpret_cast<int64_t*>(ws);
+  int64_t* rpb = reinterpret_cast<int64_t*>(ws + pl.off_rpb);
+  int32_t* idx = a->out_idx ? a->out_idx : reinterpret_cast<int32_t*>(ws + pl.off_idx);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  pl.ia.pos = pos;
+  pl.ia.out_idx = idx;
+  hipError_t e = lbca::launch_index_topk_chunk(pl.ia, a->q_len, a->q_pos0, a->raw_pos_base, pos, rpb,
+                                               ws + pl.off_index, s);
+  if (e != hipSuccess) return LBCA_ERR_HIP;
+  pl.da.pos = pos;
+  pl.da.raw_pos_base = rpb;
+  pl.da.sel_idx = idx;
+  return hip_status(lbca::launch_decode(pl.da, pl.dp, ws + pl.off_decode, s, (int)a->q_len));
+}
+
 int csa_index_topk(const csa_index_args* a, void* workspace, size_t workspace_bytes, void* stream) {
   int st = validate_index(a);
   if (st != LBCA_OK) return st;

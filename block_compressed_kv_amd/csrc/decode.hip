@@ -853,10 +853,12 @@ static hipError_t launch_d(const DecodeParams& p, bool shared, int rd, bool trea
 }
 
 hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void* ws,
-                         hipStream_t stream) {
+                         hipStream_t stream, int qrows) {
   if (a.dtype != LBCA_BF16) return launch_decode_f32(a, stream);
   const int64_t G = a.q_heads / a.kv_heads;
   DecodeParams p{};
+  p.qrows = qrows;
+  if (qrows > 1 && plan.wide_blocks == 0) return hipErrorInvalidValue;  // shared cache rows: wide path only
   p.q = static_cast<const bf16_t*>(a.q);
   p.pk = static_cast<const bf16_t*>(a.pooled_k);
   p.pv = static_cast<const bf16_t*>(a.pooled_v);

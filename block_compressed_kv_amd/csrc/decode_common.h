@@ -28,6 +28,7 @@ struct DecodeParams {
   float eps;
   int rope_dims;
   double log2_base;
+  int qrows;  // > 1: consecutive rows b share cache sequence b / qrows (a query chunk)
 };
 
 // Puts the argument fields a decode prologue needs into registers before its

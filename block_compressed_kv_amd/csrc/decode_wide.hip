@@ -244,8 +244,9 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
   SeqView sv;  // filled once the position arrives (after the first copies)
 
   // ---- tile copies: the waves of quarter q copy its 32 rows between them ----
-  const uintptr_t pk_slice = reinterpret_cast<uintptr_t>(p.pk) + (uint64_t)((b * p.hkv + kvh) * p.entries) * (WD * 2);
-  const uintptr_t rk_slice = reinterpret_cast<uintptr_t>(p.rk) + (uint64_t)((b * p.hkv + kvh) * p.raw_rows) * (WD * 2);
+  const int64_t cb = p.qrows > 1 ? (int64_t)((unsigned)b / (unsigned)p.qrows) : b;  // cache sequence
+  const uintptr_t pk_slice = reinterpret_cast<uintptr_t>(p.pk) + (uint64_t)((cb * p.hkv + kvh) * p.entries) * (WD * 2);
+  const uintptr_t rk_slice = reinterpret_cast<uintptr_t>(p.rk) + (uint64_t)((cb * p.hkv + kvh) * p.raw_rows) * (WD * 2);
   const uintptr_t dummy = reinterpret_cast<uintptr_t>(p.q + (b * p.hq + kvh * p.G) * WD);  // 1 KB, cached
   const int rq = lane >> 4, c_lane = lane & 15;  // row within 4 and LDS chunk this lane writes
   // Row v of the tile's part of the list -> (valid, buffer row).

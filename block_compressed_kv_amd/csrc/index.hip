@@ -35,6 +35,7 @@ struct IndexParams {
   int64_t heads, entries, k, m, stride;  // stride: entries rounded up to 4 (16-byte rows)
   int slices;                            // two-stage selection: slices of kSliceLen entries
   int64_t cstride;                       // candidates per sequence, rounded up to 4
+  int64_t qrows;                         // chunk scoring: query rows per key sequence
 };
 
 __device__ __forceinline__ int64_t n_visible(const IndexParams& p, int64_t b) {
@@ -105,6 +106,108 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexParams p) {
       }
     }
   }
+}
+
+// Sum over aligned groups of HP lanes (8 or 16) inside each 16-lane row; every
+// lane of a group gets the total (quad swaps, then the half-row and row mirrors).
+template <int HP>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+  if constexpr (HP == 16)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+
+constexpr int kChunkQ = 64;  // queries per workgroup of the chunk scorer
+
+// Chunk scoring: one wave holds 64 keys in registers and runs every query of
+// its workgroup's group of kChunkQ over them; the MFMA's 16 B columns carry QP
+// queries' heads at once (HP = 16 / QP head slots each, padded heads weigh 0),
+// so a key tile read once serves the whole query group.  The next query's
+// rows are requested before the current one is scored.
+template <int DI, int QP>
+__global__ __launch_bounds__(256) void index_score_chunk_kernel(IndexParams p) {
+  constexpr int KS = DI / 32, HP = 16 / QP;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, kq = lane >> 4;
+  const int qo = n / HP, hd = n % HP;
+  const int64_t seq = blockIdx.z;
+  const int64_t q0 = (int64_t)blockIdx.y * kChunkQ;
+  const int64_t qn = p.qrows - q0 < kChunkQ ? p.qrows - q0 : kChunkQ;
+  const int64_t r0 = seq * p.qrows + q0;
+  const int64_t nv_last = n_visible(p, r0 + qn - 1);  // positions grow along the chunk
+  const int64_t key0 = ((int64_t)blockIdx.x * 4 + wave) * 64;
+  if (key0 >= nv_last) return;  // no query of the group sees these keys
+  uint4 kv[4][KS];
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh) {
+    int64_t key = key0 + 16 * hh + n;
+    key = key < nv_last ? key : nv_last - 1;
+    const bf16_t* krow = p.keys + (seq * p.entries + key) * DI + 8 * kq;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kv[hh][s] = *reinterpret_cast<const uint4*>(krow + 32 * s);
+  }
+  const bool head_ok = hd < p.heads;
+  const int hsafe = head_ok ? hd : 0;
+  // query slot i + qo of the group: its row (clamped into the group), rows and weight
+  auto row_of = [&](int64_t i) { return r0 + (i + qo < qn ? i + qo : i); };
+  uint4 qr[KS];
+  int64_t r = row_of(0);
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qr[s] = *reinterpret_cast<const uint4*>(p.q + (r * p.heads + hsafe) * DI + 8 * kq + 32 * s);
+  float wv = p.w[r * p.heads + hsafe];
+  int64_t tpos = p.pos[r];
+  for (int64_t i = 0; i < qn; i += QP) {
+    // request the next slot's rows first
+    const int64_t rn = row_of(i + QP < qn ? i + QP : i);
+    uint4 qn_r[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qn_r[s] = *reinterpret_cast<const uint4*>(p.q + (rn * p.heads + hsafe) * DI + 8 * kq + 32 * s);
+    const float wn = p.w[rn * p.heads + hsafe];
+    const int64_t tn = p.pos[rn];
+    const bool q_ok = i + qo < qn;
+    const float wh = head_ok && q_ok ? wv : 0.f;
+    int64_t nv = tpos < 0 ? 0 : (tpos + 1) / p.m;
+    nv = nv < p.entries ? nv : p.entries;
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv[hh][s]),
+                                                     __builtin_bit_cast(bf16x8, qr[s]), c, 0, 0, 0);
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = lane_group_sum<HP>(wh * fmaxf(c[j], 0.f));
+      const int64_t kbase = key0 + 16 * hh + 4 * kq;
+      if (hd == 0 && q_ok) {
+        float* dst = p.scores + r * p.stride + kbase;
+        if (kbase + 3 < nv) {
+          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (kbase + j < nv) dst[j] = v[j];
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qr[s] = qn_r[s];
+    r = rn;
+    wv = wn;
+    tpos = tn;
+  }
+}
+
+__global__ void fill_rows_kernel(int64_t* pos, int64_t* rpb, int64_t rows, int64_t q_len, int64_t q_pos0,
+                                 int64_t raw_pos_base) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  pos[r] = q_pos0 + r % q_len;
+  rpb[r] = raw_pos_base;
 }
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -428,7 +531,9 @@ size_t index_workspace_bytes(const csa_index_args& a) {
   return bytes;
 }
 
-hipError_t launch_index_topk(const csa_index_args& a, void* ws, hipStream_t stream) {
+static hipError_t launch_topk(const IndexParams& p, const csa_index_args& a, hipStream_t stream);
+
+static IndexParams index_params(const csa_index_args& a, void* ws) {
   IndexParams p{};
   p.q = static_cast<const bf16_t*>(a.q_idx);
   p.w = a.head_w;
@@ -445,6 +550,12 @@ hipError_t launch_index_topk(const csa_index_args& a, void* ws, hipStream_t stre
     p.cand_key = reinterpret_cast<uint32_t*>(p.scores + a.batch * p.stride);
     p.cand_id = reinterpret_cast<int32_t*>(p.cand_key + a.batch * p.cstride);
   }
+  p.qrows = 1;
+  return p;
+}
+
+hipError_t launch_index_topk(const csa_index_args& a, void* ws, hipStream_t stream) {
+  const IndexParams p = index_params(a, ws);
   if (a.entries > 0) {
     const dim3 grid((unsigned)((a.entries + 255) / 256), (unsigned)a.batch);
     switch (a.dim) {
@@ -456,6 +567,38 @@ hipError_t launch_index_topk(const csa_index_args& a, void* ws, hipStream_t stre
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  return launch_topk(p, a, stream);
+}
+
+hipError_t launch_index_topk_chunk(const csa_index_args& a, int64_t q_len, int64_t q_pos0, int64_t raw_pos_base,
+                                   int64_t* pos_ws, int64_t* rpb_ws, void* ws, hipStream_t stream) {
+  fill_rows_kernel<<<(unsigned)((a.batch + 255) / 256), 256, 0, stream>>>(pos_ws, rpb_ws, a.batch, q_len, q_pos0,
+                                                                          raw_pos_base);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  IndexParams p = index_params(a, ws);
+  p.pos = pos_ws;
+  p.qrows = q_len;
+  if (a.entries > 0) {
+    const dim3 grid((unsigned)((a.entries + 255) / 256), (unsigned)((q_len + kChunkQ - 1) / kChunkQ),
+                    (unsigned)(a.batch / q_len));
+    const bool two = a.heads <= 8;
+    switch (a.dim * 2 + (two ? 1 : 0)) {
+      case 32 * 2 + 1: index_score_chunk_kernel<32, 2><<<grid, 256, 0, stream>>>(p); break;
+      case 32 * 2: index_score_chunk_kernel<32, 1><<<grid, 256, 0, stream>>>(p); break;
+      case 64 * 2 + 1: index_score_chunk_kernel<64, 2><<<grid, 256, 0, stream>>>(p); break;
+      case 64 * 2: index_score_chunk_kernel<64, 1><<<grid, 256, 0, stream>>>(p); break;
+      case 128 * 2 + 1: index_score_chunk_kernel<128, 2><<<grid, 256, 0, stream>>>(p); break;
+      case 128 * 2: index_score_chunk_kernel<128, 1><<<grid, 256, 0, stream>>>(p); break;
+      default: return hipErrorInvalidValue;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_topk(p, a, stream);
+}
+
+static hipError_t launch_topk(const IndexParams& p, const csa_index_args& a, hipStream_t stream) {
   const dim3 g((unsigned)a.batch);
   if (p.slices > 0) {
     topk_kernel<4, 1><<<dim3((unsigned)p.slices, (unsigned)a.batch), 1024, 0, stream>>>(p);

@@ -23,8 +23,10 @@ struct DecodePlan {
   size_t ws_bytes;   // split partials (acc, max, sum); 0 with one split
 };
 DecodePlan plan_decode(const lbca_decode_args& a);
+// qrows > 1 (wide-row path only): rows b of the call are queries of a chunk,
+// and consecutive groups of qrows rows read cache sequence b / qrows
 hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void* ws,
-                         hipStream_t stream);
+                         hipStream_t stream, int qrows = 1);
 
 hipError_t launch_prefill(const lbca_prefill_args& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const lbca_prefill_args& a, hipStream_t stream);
@@ -32,5 +34,11 @@ hipError_t launch_decode_f32(const lbca_decode_args& a, hipStream_t stream);
 
 size_t index_workspace_bytes(const csa_index_args& a);
 hipError_t launch_index_topk(const csa_index_args& a, void* ws, hipStream_t stream);
+// Query chunk: a.batch = sequences * q_len rows (q_idx [rows, heads, dim],
+// head_w [rows, heads], out_idx [rows, k]); keys [sequences, entries, dim];
+// row r sits at q_pos0 + r % q_len.  Writes the rows' positions to pos_ws and
+// raw_pos_base to rpb_ws (rows int64 each), then scores and selects.
+hipError_t launch_index_topk_chunk(const csa_index_args& a, int64_t q_len, int64_t q_pos0, int64_t raw_pos_base,
+                                   int64_t* pos_ws, int64_t* rpb_ws, void* ws, hipStream_t stream);
 
 }  // namespace lbca

@@ -80,6 +80,16 @@ class IndexArgs(ctypes.Structure):
                 ("block", _i64), ("dtype", _i32)]
 
 
+class CsaPrefillArgs(ctypes.Structure):
+    _fields_ = [("q_idx", _vp), ("head_w", _vp), ("idx_keys", _vp), ("q", _vp), ("entries", _vp),
+                ("raw", _vp), ("sink", _vp), ("out", _vp), ("lse", _vp), ("out_idx", _vp),
+                ("batch", _i64), ("q_len", _i64), ("idx_heads", _i64), ("idx_dim", _i64),
+                ("q_heads", _i64), ("dim", _i64), ("n_entries", _i64), ("raw_rows", _i64), ("k", _i64),
+                ("q_pos0", _i64), ("raw_pos_base", _i64), ("block", _i64), ("window", _i64),
+                ("dtype", _i32), ("scale", ctypes.c_float), ("rmsnorm_eps", ctypes.c_float),
+                ("rope_dims", _i32), ("rope_base", ctypes.c_float)]
+
+
 class LbcaError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
@@ -112,6 +122,8 @@ def lib():
         L.lbca_attend_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
         L.csa_index_topk_workspace.argtypes = [ctypes.POINTER(IndexArgs), ctypes.POINTER(ctypes.c_size_t)]
         L.csa_index_topk.argtypes = [ctypes.POINTER(IndexArgs), _vp, ctypes.c_size_t, _vp]
+        L.csa_sparse_prefill_workspace.argtypes = [ctypes.POINTER(CsaPrefillArgs), ctypes.POINTER(ctypes.c_size_t)]
+        L.csa_sparse_prefill.argtypes = [ctypes.POINTER(CsaPrefillArgs), _vp, ctypes.c_size_t, _vp]
         for name in exported_names():
             getattr(L, name).restype = ctypes.c_int if name != "lbca_status_string" else ctypes.c_char_p
         if L.lbca_abi_version() != 1:
@@ -368,3 +380,42 @@ def csa_index_topk(q_idx, head_w, keys, pos, block, k, out_idx=None, out_score=N
     _check(lib().csa_index_topk(ctypes.byref(a), _p(workspace), ws_bytes, _stream(stream)),
            "csa_index_topk")
     return out_idx, out_score
+
+
+def _csa_prefill_args(q_idx, head_w, idx_keys, q, entries, raw, q_pos0, raw_pos_base, block, window, k,
+                      out, lse, out_idx, sink, scale, rmsnorm_eps, rope_dims, rope_base):
+    for t, n, nd in ((q_idx, "q_idx", 4), (head_w, "head_w", 3), (idx_keys, "idx_keys", 3), (q, "q", 4),
+                     (entries, "entries", 3), (raw, "raw", 3), (out, "out", 4), (out_idx, "out_idx", 3)):
+        _need(t, n, nd)
+    B, Tq, Hq, d = q.shape
+    HI, dI = q_idx.shape[2], q_idx.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return CsaPrefillArgs(_p(q_idx), _p(head_w), _p(idx_keys), _p(q), _p(entries), _p(raw), _p(sink), _p(out),
+                          _p(lse), _p(out_idx), B, Tq, HI, dI, Hq, d, entries.shape[1], raw.shape[1], k,
+                          q_pos0, raw_pos_base, block, window, _dt(q), float(scale),
+                          -1.0 if rmsnorm_eps is None else float(rmsnorm_eps), int(rope_dims), float(rope_base))
+
+
+def csa_sparse_prefill(q_idx, head_w, idx_keys, q, entries, raw, q_pos0, raw_pos_base, block, window, k,
+                       out=None, lse=None, out_idx=None, sink=None, scale=None, rmsnorm_eps=None, rope_dims=0,
+                       rope_base=10000.0, workspace=None, stream=None):
+    """csa_sparse_prefill: q_idx [B,Tq,HI,dI], head_w [B,Tq,HI], idx_keys [B,N,dI], q [B,Tq,Hq,d],
+    entries [B,N,d], raw [B,R,d]; returns (out [B,Tq,Hq,d] fp32, lse [B,Tq,Hq], idx [B,Tq,k] int32)."""
+    B, Tq, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, Tq, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
+    if out_idx is None:
+        out_idx = torch.empty((B, Tq, k), dtype=torch.int32, device=q.device)
+    a = _csa_prefill_args(q_idx, head_w, idx_keys, q, entries, raw, q_pos0, raw_pos_base, block, window, k,
+                          out, lse, out_idx, sink, scale, rmsnorm_eps, rope_dims, rope_base)
+    need = ctypes.c_size_t()
+    _check(lib().csa_sparse_prefill_workspace(ctypes.byref(a), ctypes.byref(need)), "csa_sparse_prefill_workspace")
+    if workspace is None:  # positions, selections, scores; contents on entry do not matter
+        workspace = torch.empty(max(need.value, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().csa_sparse_prefill(ctypes.byref(a), _p(workspace), ws_bytes, _stream(stream)),
+           "csa_sparse_prefill")
+    return out, lse, out_idx

@@ -415,6 +415,59 @@ LBCA_API int csa_index_topk_workspace(const csa_index_args* a, size_t* bytes);
 LBCA_API int csa_index_topk(const csa_index_args* a, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* CSA sparse prefill of a chunk of q_len consecutive queries (CSA "What is
+ * implemented", second and third items, applied to every query of a chunk).
+ * Query i of sequence b sits at t = q_pos0 + i.  It scores the indexer keys
+ * visible at t (OVERLAP rule, j < floor((t+1)/block)), keeps its own top-k
+ * exactly as csa_index_topk would, and attends to those entries plus its raw
+ * window [max(0, t-window+1), t] under one softmax, exactly as
+ * lbca_attend_decode with sel_idx would at t (MQA: one shared K = V series;
+ * RMSNorm / partial RoPE of q and the raw rows, the output's last rope_dims
+ * turned back by -t; entries are used as stored, already treated).
+ *
+ *   q_idx    [batch, q_len, idx_heads, idx_dim] dtype;  head_w [batch, q_len, idx_heads] float32
+ *   idx_keys [batch, entries, idx_dim] dtype
+ *   q        [batch, q_len, q_heads, dim] dtype
+ *   entries  [batch, entries, dim] dtype  (pooled, treated)
+ *   raw      [batch, raw_rows, dim] dtype  row r = position raw_pos_base + r (host scalar)
+ *   sink     [q_heads] float32 or NULL
+ *   out      [batch, q_len, q_heads, dim] float32;  lse [batch, q_len, q_heads] float32 or NULL
+ *   out_idx  [batch, q_len, k] int32 or NULL: each query's selection (ascending, -1 padded)
+ * Supported: dtype BF16; idx_dim in {32, 64, 128}, idx_heads <= 16,
+ * 1 <= k <= 2048, entries <= 65536; dim 512 with q_heads a multiple of 32 up
+ * to 64; batch * q_len <= 65535; entries * dim and raw_rows * dim < 2^30.
+ * Errors: INVALID_ARG if the last query's visible entries exceed `entries`
+ * or some query's raw window leaves the raw buffer (checked on the host).
+ * Workspace (csa_sparse_prefill_workspace; 16-byte aligned, caller-owned,
+ * contents on entry do not matter): per-query positions and selections, the
+ * fp32 scores (batch * q_len rows of entries), and split partials when a
+ * query's rows are split.  Calls sharing one workspace must not overlap.
+ */
+typedef struct csa_prefill_args {
+  const void* q_idx;
+  const float* head_w;
+  const void* idx_keys;
+  const void* q;
+  const void* entries;
+  const void* raw;
+  const float* sink;
+  float* out;
+  float* lse;
+  int32_t* out_idx;
+  int64_t batch, q_len, idx_heads, idx_dim, q_heads, dim, n_entries, raw_rows, k;
+  int64_t q_pos0, raw_pos_base, block, window;
+  int32_t dtype;
+  float scale;
+  float rmsnorm_eps; /* < 0: off */
+  int32_t rope_dims; /* 0: off */
+  float rope_base;
+} csa_prefill_args;
+
+LBCA_API int csa_sparse_prefill_workspace(const csa_prefill_args* a, size_t* bytes);
+LBCA_API int csa_sparse_prefill(const csa_prefill_args* a, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -308,3 +308,54 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(lbca, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         lbca.lib()
+
+
+def _csap(ws_query=True, **kw):
+    a = dict(q_idx=FAKE, head_w=FAKE, idx_keys=FAKE, q=FAKE, entries=FAKE, raw=FAKE, sink=None, out=FAKE,
+             lse=None, out_idx=FAKE, batch=2, q_len=100, idx_heads=8, idx_dim=64, q_heads=64, dim=512,
+             n_entries=1000, raw_rows=500, k=64, q_pos0=3000, raw_pos_base=2800, block=4, window=128, dtype=1,
+             scale=0.05, rmsnorm_eps=1e-6, rope_dims=64, rope_base=10000.0)
+    a.update(kw)
+    s = lbca.CsaPrefillArgs(**a)
+    if ws_query:
+        n = ctypes.c_size_t()
+        return lbca.lib().csa_sparse_prefill_workspace(ctypes.byref(s), ctypes.byref(n)), n.value
+    return lbca.lib().csa_sparse_prefill(ctypes.byref(s), ctypes.c_void_p(FAKE), 16, None), 0
+
+
+@fake_ptr
+@pytest.mark.parametrize("kw,code", [
+    (dict(), 0),
+    (dict(q_idx=None), -1), (dict(head_w=None), -1), (dict(idx_keys=None), -1), (dict(q=None), -1),
+    (dict(entries=None), -1), (dict(raw=None), -1), (dict(out=None), -1),
+    (dict(dtype=3), -1), (dict(dtype=0), -2), (dict(k=0), -1), (dict(k=4096), -2),
+    (dict(idx_dim=48), -2), (dict(idx_heads=17), -2), (dict(idx_heads=0), -1), (dict(n_entries=70000), -2),
+    (dict(dim=128), -2), (dict(q_heads=48), -2), (dict(q_heads=128), -2),
+    (dict(batch=700), -2),                                   # batch * q_len rows above 65535
+    (dict(q_len=600), -1),                                   # last query (t = 3599) past the raw buffer
+    (dict(q_pos0=3950), -1),                                 # last query sees 1012 entries > 1000
+    (dict(raw_pos_base=2900), -1),                           # first query's window starts below the base
+    (dict(raw_rows=299), -1),                                # last query's row (t = 3099) past the buffer
+    (dict(rope_dims=24), -2), (dict(rope_base=1.0), -1), (dict(scale=float("nan")), -1),
+    (dict(out=FAKE + 4), -1), (dict(q_pos0=-1), -1), (dict(window=0), -1), (dict(block=0), -1),
+])
+def test_csa_sparse_prefill_validation(kw, code):
+    st, n = _csap(**kw)
+    assert st == code, kw
+    if code == 0:
+        assert n > 0
+
+
+@fake_ptr
+def test_csa_sparse_prefill_workspace_layout():
+    st, with_idx = _csap()
+    st2, without = _csap(out_idx=None)
+    assert st == st2 == 0
+    rows = 2 * 100
+    assert without - with_idx == (rows * 64 * 4 + 255) // 256 * 256   # the internal selection rows
+    st, big = _csap(n_entries=2000)
+    assert st == 0 and big - with_idx >= rows * 1000 * 4               # fp32 scores per row and entry
+    # a short workspace fails before any launch
+    assert _csap(ws_query=False)[0] == -3
+    st, empty = _csap(q_len=0)
+    assert st == 0

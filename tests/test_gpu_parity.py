@@ -626,3 +626,72 @@ def test_topk_ties_and_zero_scores(lib):
     s = np.maximum(np.array(vals, dtype=np.float64), 0)
     ref = O.topk_select(s, k)
     assert list(idx[0].cpu().numpy()) == list(ref)
+
+
+# ---------------------------------------------------------------------------
+# CSA sparse prefill (a query chunk: indexer, per-query top-k, selected attention)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,Tq,p0,HI,dI,k,treated", [
+    (2, 70, 2330, 8, 64, 64, True),     # two query groups (64 + ragged 6), k well below the visible count
+    (1, 40, 0, 16, 128, 16, True),      # 16 indexer heads, early queries see fewer than k (or no) entries
+    (1, 33, 1000, 5, 32, 100, False),   # padded indexer heads, odd query tail, untreated
+])
+def test_csa_sparse_prefill(lib, B, Tq, p0, HI, dI, k, treated):
+    Hq, d, m, W = 64, 512, 4, 128
+    T = p0 + Tq
+    N = T // m
+    C = _dev(synth.csa_layer(f"csa-pf-{p0}", B, Hq, T, d, m, HI, dI, q_len=Tq))
+    treat = dict(rmsnorm_eps=1e-6, rope_dims=64, rope_base=10000.0) if treated else {}
+    entries = torch.zeros((B, 1, N, d), dtype=torch.bfloat16, device=DEV)
+    lib.pool_blocks(C["ca"], C["za"], C["bias_a"], m, 0, N, entries, xb=C["cb"], zb=C["zb"],
+                    bias_b=C["bias_b"], **treat)
+    ikeys = torch.zeros((B, 1, N, dI), dtype=torch.bfloat16, device=DEV)
+    lib.pool_blocks(C["ica"], C["iza"], C["ibias_a"], m, 0, N, ikeys, xb=C["icb"], zb=C["izb"],
+                    bias_b=C["ibias_b"])
+    say(f"csa sparse prefill B={B} Tq={Tq} p0={p0} HI={HI} dI={dI} k={k}")
+    o, lse, idx = lib.csa_sparse_prefill(C["qi"], C["w"], ikeys[:, 0], C["q"], entries[:, 0], C["ca"][:, 0],
+                                         p0, 0, m, W, k, sink=C["sink"], **treat)
+    o, lse, idx = host(o), host(lse), idx.cpu().numpy()
+    pooled = O.pool_dual(host(C["ca"]), host(C["za"]), host(C["bias_a"][0]), host(C["cb"]),
+                         host(C["zb"]), host(C["bias_b"][0]), m, 0, N)
+    qi, w, ki, q, raw = host(C["qi"]), host(C["w"]), host(ikeys[:, 0]), host(C["q"]), host(C["ca"])
+    sink = host(C["sink"])
+    for b in range(B):
+        ro = np.zeros((Tq, Hq, d))
+        rl = np.zeros((Tq, Hq))
+        for i in range(Tq):
+            t = p0 + i
+            n_vis = min((t + 1) // m, N)
+            topk_matches(idx[b, i], O.index_scores(qi[b, i], w[b, i], ki[b], n_vis), k, f"seq {b} query {i}")
+            # the attention over the GPU's (valid) selection
+            oo, ll = O.attend_decode(q[b, i][None], pooled[b][None], None, raw[b][None], None, [t], m, W,
+                                     O.OVERLAP, 1 / math.sqrt(d), raw_pos_base=[0], sel_idx=idx[b, i][None],
+                                     sink=sink, **treat)
+            ro[i], rl[i] = oo[0], ll[0]
+        check_bf16(o[b], ro, f"sparse prefill out seq {b}")
+        check_bf16(lse[b], rl, f"sparse prefill lse seq {b}")
+
+
+def test_csa_sparse_prefill_two_stage_selection(lib):
+    # 12500 entries: the per-query selection runs in two stages (4 slices of 4096)
+    B, Tq, Hq, d, m, W, HI, dI, k = 1, 20, 32, 512, 4, 128, 8, 64, 512
+    N = 12500
+    p0 = N * m - Tq
+    g = lambda n, shape: synth.normal(shape, synth.seed_of("csa-pf-2s", n), dtype="bf16", device=DEV)
+    qi, ki, q, ent, raw = g("qi", (B, Tq, HI, dI)), g("ki", (B, N, dI)), g("q", (B, Tq, Hq, d)), \
+        g("e", (B, N, d)), g("raw", (B, 256, d))
+    w = synth.uniform((B, Tq, HI), synth.seed_of("csa-pf-2s", "w"), device=DEV)
+    base = p0 - W + 1
+    o, lse, idx = lib.csa_sparse_prefill(qi, w, ki, q, ent, raw, p0, base, m, W, k)
+    o, lse, idx = host(o), host(lse), idx.cpu().numpy()
+    qh, wh, kh, eh, rh = host(qi), host(w), host(ki), host(ent), host(raw)
+    ro, rl = np.zeros((Tq, Hq, d)), np.zeros((Tq, Hq))
+    for i in range(Tq):
+        t = p0 + i
+        n_vis = min((t + 1) // m, N)
+        topk_matches(idx[0, i], O.index_scores(qh[0, i], wh[0, i], kh[0], n_vis), k, f"query {i}")
+        oo, ll = O.attend_decode(host(q)[0, i][None], eh[0][None, None], None, rh[0][None, None], None, [t], m, W,
+                                 O.OVERLAP, 1 / math.sqrt(d), raw_pos_base=[base], sel_idx=idx[0, i][None])
+        ro[i], rl[i] = oo[0], ll[0]
+    check_bf16(o[0], ro, "two-stage sparse prefill out")
+    check_bf16(lse[0], rl, "two-stage sparse prefill lse")
