@@ -405,6 +405,7 @@ def run_prefill(reps):
 X_HQ, X_D, X_RD, X_EPS, X_BASE = 64, 512, 64, 1e-6, 10000.0
 HCA_T, HCA_M, HCA_B = 1 << 20, 128, 4
 CSA_T, CSA_M, CSA_B, CSA_HI, CSA_DI, CSA_K = 1 << 17, 4, 2, 8, 64, 512
+CSA_CHUNK = 2048  # sparse prefill: queries per sequence in the timed chunk
 ROTATE_BYTES = 600 << 20   # distinct bytes a timing loop cycles through (> 2 x Infinity Cache)
 
 
@@ -495,6 +496,31 @@ def run_csa(reps):
     ms_back = time_graph(g_back, 3)
     back_bytes = B * T * X_D * 2 * 4 * 2 + B * N * X_D * 2  # a- and b-series rows and logits read and written
     del gd, outs, dual, wsb, g_back
+    # sparse prefill of the context's last chunk of CSA_CHUNK queries per sequence: chunk indexer,
+    # per-query top-k and the selected-entry attention (treated entries as above)
+    CH, tg = CSA_CHUNK, "bench-csa-128k-chunk"
+    t0 = T - CH
+    pf = dict(qi=synth.normal((B, CH, CSA_HI, CSA_DI), synth.seed_of(tg, "qi"), dtype="bf16", device=dev),
+              w=synth.uniform((B, CH, CSA_HI), synth.seed_of(tg, "w"), device=dev),
+              keys=synth.normal((B, N, CSA_DI), synth.seed_of(tg, "keys"), dtype="bf16", device=dev),
+              q=synth.normal((B, CH, X_HQ, X_D), synth.seed_of(tg, "q"), dtype="bf16", device=dev))
+    rbase = t0 - W + 1
+    rawc = C["ca"][:, 0, rbase:].contiguous()
+    pf_out = torch.empty((B, CH, X_HQ, X_D), device=dev)
+    pf_lse = torch.empty((B, CH, X_HQ), device=dev)
+    pf_idx = torch.empty((B, CH, k), dtype=torch.int32, device=dev)
+    pf_args = (pf["qi"], pf["w"], pf["keys"], pf["q"], ent[:, 0], rawc, t0, rbase, m, W, k)
+    pf_kw = dict(sink=C["sink"], out=pf_out, lse=pf_lse, out_idx=pf_idx, **treat)
+    ws_pf = torch.empty(max(lbca.csa_sparse_prefill_workspace_bytes(*pf_args, **pf_kw), 16), dtype=torch.uint8,
+                        device=dev)
+    sparse = lambda: lbca.csa_sparse_prefill(*pf_args, workspace=ws_pf, **pf_kw)
+    sparse()
+    g_sp = capture(sparse)
+    ms_sp = time_graph(g_sp, 3)
+    n_vis_sum = sum((t + 1) // m for t in range(t0, T))
+    sp_index_flop = B * n_vis_sum * CSA_HI * CSA_DI * 2
+    sp_attn_flop = B * CH * X_HQ * (k + W) * X_D * 4
+    del pf, rawc, pf_out, pf_lse, pf_idx, ws_pf, g_sp, pf_args, pf_kw
     raw = C["ca"][:, :, T - W:].contiguous()
     sink = C["sink"]
     del C, g_pool
@@ -541,7 +567,12 @@ def run_csa(reps):
     by_idx = B * (N * CSA_DI * 2 + CSA_HI * CSA_DI * 2 + CSA_HI * 4 + k * 8)
     by_dec = mqa_step_bytes(B, k + W)
     by = by_idx + by_dec
-    return {"step_us": us_both, "step_GBps": by / (us_both * 1e-6) / 1e9, "step_algorithmic_bytes": by,
+    return {"sparse_prefill_chunk": {"workload": f"batch {B}, last {CSA_CHUNK} queries of a {T}-token context, "
+                                              f"top-{k} of {N} entries plus the {W}-token window, {X_HQ} heads x {X_D}",
+                                  "ms": ms_sp, "queries_per_s": B * CSA_CHUNK / (ms_sp * 1e-3),
+                                  "index_GFLOP": sp_index_flop / 1e9, "attention_GFLOP": sp_attn_flop / 1e9,
+                                  "TFLOPs": (sp_index_flop + sp_attn_flop) / (ms_sp * 1e-3) / 1e12},
+            "step_us": us_both, "step_GBps": by / (us_both * 1e-6) / 1e9, "step_algorithmic_bytes": by,
             "index_topk_us": us_idx, "index_GBps": by_idx / (us_idx * 1e-6) / 1e9,
             "decode_us": us_dec, "decode_GBps": by_dec / (us_dec * 1e-6) / 1e9,
             "decode_workspace_bytes": nws, "instances": n_inst,

@@ -397,6 +397,18 @@ def _csa_prefill_args(q_idx, head_w, idx_keys, q, entries, raw, q_pos0, raw_pos_
                           -1.0 if rmsnorm_eps is None else float(rmsnorm_eps), int(rope_dims), float(rope_base))
 
 
+def csa_sparse_prefill_workspace_bytes(q_idx, head_w, idx_keys, q, entries, raw, q_pos0, raw_pos_base, block,
+                                      window, k, out=None, lse=None, out_idx=None, sink=None, scale=None,
+                                      rmsnorm_eps=None, rope_dims=0, rope_base=10000.0):
+    """csa_sparse_prefill_workspace: bytes of workspace csa_sparse_prefill needs for these shapes
+    (the query's buffer stands in for an absent output, which the size does not depend on)."""
+    a = _csa_prefill_args(q_idx, head_w, idx_keys, q, entries, raw, q_pos0, raw_pos_base, block, window, k,
+                          q if out is None else out, lse, out_idx, sink, scale, rmsnorm_eps, rope_dims, rope_base)
+    need = ctypes.c_size_t()
+    _check(lib().csa_sparse_prefill_workspace(ctypes.byref(a), ctypes.byref(need)), "csa_sparse_prefill_workspace")
+    return need.value
+
+
 def csa_sparse_prefill(q_idx, head_w, idx_keys, q, entries, raw, q_pos0, raw_pos_base, block, window, k,
                        out=None, lse=None, out_idx=None, sink=None, scale=None, rmsnorm_eps=None, rope_dims=0,
                        rope_base=10000.0, workspace=None, stream=None):
