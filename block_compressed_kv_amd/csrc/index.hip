@@ -598,9 +598,13 @@ hipError_t launch_index_topk_chunk(const csa_index_args& a, int64_t q_len, int64
   return launch_topk(p, a, stream);
 }
 
+// From this many rows on, one selection workgroup per row already fills the
+// chip, and the slice stage would only add a pass over the candidates.
+constexpr int64_t kOneStageRows = 256;
+
 static hipError_t launch_topk(const IndexParams& p, const csa_index_args& a, hipStream_t stream) {
   const dim3 g((unsigned)a.batch);
-  if (p.slices > 0) {
+  if (p.slices > 0 && a.batch < kOneStageRows) {
     topk_kernel<4, 1><<<dim3((unsigned)p.slices, (unsigned)a.batch), 1024, 0, stream>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

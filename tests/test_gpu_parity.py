@@ -672,15 +672,17 @@ def test_csa_sparse_prefill(lib, B, Tq, p0, HI, dI, k, treated):
         check_bf16(lse[b], rl, f"sparse prefill lse seq {b}")
 
 
-def test_csa_sparse_prefill_two_stage_selection(lib):
-    # 12500 entries: the per-query selection runs in two stages (4 slices of 4096)
-    B, Tq, Hq, d, m, W, HI, dI, k = 1, 20, 32, 512, 4, 128, 8, 64, 512
-    N = 12500
+@pytest.mark.parametrize("Tq,N", [
+    (20, 12500),    # 20 rows: the per-query selection runs in two stages (4 slices of 4096)
+    (300, 20000),   # 300 rows: one selection workgroup per row over up to 20000 entries
+])
+def test_csa_sparse_prefill_two_stage_selection(lib, Tq, N):
+    B, Hq, d, m, W, HI, dI, k = 1, 32, 512, 4, 128, 8, 64, 512
     p0 = N * m - Tq
-    g = lambda n, shape: synth.normal(shape, synth.seed_of("csa-pf-2s", n), dtype="bf16", device=DEV)
+    g = lambda n, shape: synth.normal(shape, synth.seed_of("csa-pf-2s", N, n), dtype="bf16", device=DEV)
     qi, ki, q, ent, raw = g("qi", (B, Tq, HI, dI)), g("ki", (B, N, dI)), g("q", (B, Tq, Hq, d)), \
-        g("e", (B, N, d)), g("raw", (B, 256, d))
-    w = synth.uniform((B, Tq, HI), synth.seed_of("csa-pf-2s", "w"), device=DEV)
+        g("e", (B, N, d)), g("raw", (B, Tq + W, d))
+    w = synth.uniform((B, Tq, HI), synth.seed_of("csa-pf-2s", N, "w"), device=DEV)
     base = p0 - W + 1
     o, lse, idx = lib.csa_sparse_prefill(qi, w, ki, q, ent, raw, p0, base, m, W, k)
     o, lse, idx = host(o), host(lse), idx.cpu().numpy()
