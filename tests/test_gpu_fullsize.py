@@ -175,3 +175,46 @@ def test_csa_decode_128k_batch2(lib):
                              sink=_cpu(C["sink"]), **treat)
     check_bf16(host(o), ro, "CSA decode out")
     check_bf16(host(lse), rl, "CSA decode lse")
+
+
+def test_csa_sparse_prefill_128k_chunk_batch2(lib):
+    # the bench's sparse prefill: the last 2048 queries of each 128K sequence, sampled queries
+    B, Hq, d, m, W, T, HI, dI, k, CH = 2, 64, 512, 4, 128, 1 << 17, 8, 64, 512, 2048
+    N, t0 = T // m, T - CH
+    say(f"full-size CSA sparse prefill B={B} T={T} chunk={CH}: generating")
+    C = synth.csa_layer(("full-csa-128k-chunk",), B, Hq, T, d, m, HI, dI, device=DEV, q_len=CH)
+    keys = synth.normal((B, N, dI), synth.seed_of("full-csa-128k-chunk", "index-keys"), dtype="bf16", device=DEV)
+    ent = torch.empty((B, 1, N, d), dtype=torch.bfloat16, device=DEV)
+    treat = dict(rmsnorm_eps=EPS, rope_dims=RD, rope_base=BASE)
+    lib.pool_blocks(C["ca"], C["za"], C["bias_a"], m, 0, N, ent, xb=C["cb"], zb=C["zb"],
+                    bias_b=C["bias_b"], **treat)
+    rbase = t0 - W + 1
+    raw = C["ca"][:, 0, rbase:].contiguous()
+    say("sparse prefill of the chunk")
+    o, lse, idx = lib.csa_sparse_prefill(C["qi"], C["w"], keys, C["q"], ent[:, 0], raw, t0, rbase, m, W, k,
+                                         sink=C["sink"], **treat)
+    torch.cuda.synchronize()
+    gidx = _cpu(idx).numpy()
+    kh, rawh = _cpu(keys), _cpu(raw)
+    ba, bb = _cpu(C["bias_a"][0]), _cpu(C["bias_b"][0])
+    for b in range(B):
+        for i in (0, 1, 1023, CH - 2, CH - 1):
+            t = t0 + i
+            n_vis = (t + 1) // m
+            say(f"oracle: sequence {b} query {i} (t = {t})")
+            s = O.index_scores(_cpu(C["qi"][b, i]), _cpu(C["w"][b, i]), kh[b], n_vis)
+            topk_matches(gidx[b, i], s, k, f"sparse prefill top-k b={b} i={i}")
+            sel = gidx[b, i]
+            pooled = np.zeros((1, 1, N, d))
+            for j in sel[sel >= 0]:
+                lo = max(0, j - 1) * m
+                sl = slice(lo, (j + 1) * m)
+                e = O.pool_dual(_cpu(C["ca"][b:b + 1, :, sl]), _cpu(C["za"][b:b + 1, :, sl]), ba,
+                                _cpu(C["cb"][b:b + 1, :, sl]), _cpu(C["zb"][b:b + 1, :, sl]), bb, m,
+                                j - lo // m, j - lo // m + 1)
+                pooled[0, 0, j] = e[0, 0, 0]
+            ro, rl = O.attend_decode(_cpu(C["q"][b, i])[None], pooled, None, rawh[b][None, None], None, [t], m, W,
+                                     O.OVERLAP, 1 / math.sqrt(d), raw_pos_base=[rbase], sel_idx=sel[None],
+                                     sink=_cpu(C["sink"]), **treat)
+            check_bf16(host(o[b, i]), ro[0], f"sparse prefill out b={b} i={i}")
+            check_bf16(host(lse[b, i]), rl[0], f"sparse prefill lse b={b} i={i}")
