@@ -749,6 +749,8 @@ static int waves_per_wg(int64_t dim) { return dim <= 128 ? 8 : 4; }
 #endif
 constexpr int kWideSelLds = 1024;  // matches the wide kernel's id stage
 
+constexpr int64_t kWideOneGroupRows = 512;
+
 static DecodePlan plan_decode_wide(const lbca_decode_args& a, int64_t G) {
   DecodePlan pl{};
   pl.tile_rows = 32;
@@ -760,7 +762,10 @@ static DecodePlan plan_decode_wide(const lbca_decode_args& a, int64_t G) {
   const int64_t raw_max = raw_span < a.raw_rows ? raw_span : a.raw_rows;
   const int64_t tiles = (sel_max + 31) / 32 + (raw_max + 31) / 32;
   pl.wide_twins = 1;
-  if (LBCA_WIDE_TWINS && pl.wide_blocks == 2) {  // one 4-wave workgroup per 32-head block
+  // one 4-wave workgroup per 32-head block, unless there are so many rows (a
+  // query chunk) that one 8-wave workgroup per row already fills the chip and
+  // gathers the row's entries once for both blocks
+  if (LBCA_WIDE_TWINS && pl.wide_blocks == 2 && a.batch * a.kv_heads < kWideOneGroupRows) {
     pl.wide_twins = 2;
     pl.wide_blocks = 1;
   }

@@ -635,6 +635,7 @@ def test_topk_ties_and_zero_scores(lib):
     (2, 70, 2330, 8, 64, 64, True),     # two query groups (64 + ragged 6), k well below the visible count
     (1, 40, 0, 16, 128, 16, True),      # 16 indexer heads, early queries see fewer than k (or no) entries
     (1, 33, 1000, 5, 32, 100, False),   # padded indexer heads, odd query tail, untreated
+    (1, 520, 2000, 8, 64, 64, True),    # 520 rows: one 8-wave attention workgroup per query
 ])
 def test_csa_sparse_prefill(lib, B, Tq, p0, HI, dI, k, treated):
     Hq, d, m, W = 64, 512, 4, 128
