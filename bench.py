@@ -77,7 +77,7 @@ RAW_ROWS = CTX - RAW0                  # 192
 # decode.hip + decode_common.h differs, bench reports traffic as null.
 COUNTERS = {"fetch_kib": 20556.9, "write_kib": 197.0,
             "copy_fetch_kib": 131085.5, "copy_write_kib": 262144.0, "copy_bytes": 256 << 20,
-            "source_sha256": "a083b39e4287a63651ca305e16430a2c439268d5af6b07f00c396047f108872e"}
+            "source_sha256": "3b29c7c2d23621abff42bb76eb4e163b582278ed961e77ffbe7e4a5f39acf54c"}
 COUNTER_SOURCES = ("decode.hip", "decode_common.h")
 
 

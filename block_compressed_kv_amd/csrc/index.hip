@@ -120,7 +120,10 @@ __device__ __forceinline__ float lane_group_sum(float x) {
   return x;
 }
 
-constexpr int kChunkQ = 64;  // queries per workgroup of the chunk scorer
+#ifndef LBCA_CHUNK_Q
+#define LBCA_CHUNK_Q 64
+#endif
+constexpr int kChunkQ = LBCA_CHUNK_Q;  // queries per workgroup of the chunk scorer
 
 // Chunk scoring: one wave holds 64 keys in registers and runs every query of
 // its workgroup's group of kChunkQ over them; the MFMA's 16 B columns carry QP
