@@ -22,7 +22,9 @@ the pooling gradients of one layer's history (GB/s),
 pooling GB/s for the whole history, chunked prefill (16K
 context in 2048-token chunks) TFLOP/s, HCA decode at 1M context (batch 4, 64
 query heads x 512, pooling GB/s of the whole history) and CSA at 128K (batch 2:
-indexer scores + top-512, decode over the selection, dual pooling GB/s); the
+indexer scores + top-512, decode over the selection, dual pooling GB/s, its
+treated dual pooling gradients, and the sparse prefill of a 2048-query chunk per
+sequence: chunk indexer, per-query top-512 and selected attention); the
 measured ceilings of the part (streaming read, one launch reading the decode's
 bytes, a bf16 MFMA loop, the empty-kernel launch floor) with each kernel's
 fraction of them; and the oracle timed beside prefill, HCA and CSA on bounded
