@@ -235,6 +235,9 @@ static int validate_decode(const lbca_decode_args* a) {
   if (!aligned16(a->q) || !aligned16(a->pooled_k) || !aligned16(a->pooled_v) ||
       !aligned16(a->raw_k) || !aligned16(a->raw_v) || !aligned16(a->out))
     return LBCA_ERR_INVALID_ARG;
+  // the selected ids of one workgroup's row range are staged in LDS; the
+  // planner reports sizes that no split count (at most 64) can cover
+  if (lbca::plan_decode(*a).unsupported) return LBCA_ERR_UNSUPPORTED;
   return LBCA_OK;
 }
 
@@ -404,7 +407,9 @@ int csa_sparse_prefill_workspace(const csa_prefill_args* a, size_t* bytes) {
   if (!bytes) return LBCA_ERR_INVALID_ARG;
   const int st = validate_csa_prefill(a);
   if (st != LBCA_OK) return st;
-  *bytes = plan_csa_prefill(a).total;
+  const CsaPrefillPlan pl = plan_csa_prefill(a);
+  if (pl.dp.unsupported) return LBCA_ERR_UNSUPPORTED;  // selected ids beyond what the splits can stage
+  *bytes = pl.total;
   return LBCA_OK;
 }
 
@@ -412,6 +417,7 @@ int csa_sparse_prefill(const csa_prefill_args* a, void* workspace, size_t worksp
   const int st = validate_csa_prefill(a);
   if (st != LBCA_OK) return st;
   CsaPrefillPlan pl = plan_csa_prefill(a);
+  if (pl.dp.unsupported) return LBCA_ERR_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < pl.total || !aligned16(workspace)) return LBCA_ERR_WORKSPACE;
   if (a->batch * a->q_len == 0) return LBCA_OK;
   char* ws = static_cast<char*>(workspace);

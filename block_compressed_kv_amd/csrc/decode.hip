@@ -773,10 +773,18 @@ static DecodePlan plan_decode_wide(const lbca_decode_args& a, int64_t G) {
   int64_t s = (LBCA_WIDE_TARGET_WGS + per_split - 1) / per_split;
   const int64_t by_rows = (tiles + LBCA_WIDE_MIN_TILES - 1) / LBCA_WIDE_MIN_TILES;
   if (s > by_rows) s = by_rows;
-  if (a.sel_idx && s < (tiles + kWideSelLds / 32 - 1) / (kWideSelLds / 32))
-    s = (tiles + kWideSelLds / 32 - 1) / (kWideSelLds / 32);
+  if (s > 64) s = 64;  // the merge combines at most 64 splits
+  if (a.sel_idx) {
+    // every range's selected ids must fit the LDS stage; with more ids than
+    // 64 ranges can stage there is no valid plan (unsupported)
+    const int64_t need = (tiles + kWideSelLds / 32 - 1) / (kWideSelLds / 32);
+    if (need > 64) {
+      pl.unsupported = 1;
+      return pl;
+    }
+    if (s < need) s = need;
+  }
   if (s < 1) s = 1;
-  if (s > 64) s = 64;  // k_sel <= 32768 keeps the id constraint within this
   pl.splits = (int)s;
   if (s == 1) return pl;
   const size_t u = (size_t)(a.batch * a.kv_heads * pl.head_groups);
@@ -810,11 +818,19 @@ DecodePlan plan_decode(const lbca_decode_args& a) {
   const int64_t part_bytes = (int64_t)pl.head_groups * 16 * (a.dim + 2) * 4;
   const int64_t by_traffic = kv_bytes / (4 * part_bytes) > 0 ? kv_bytes / (4 * part_bytes) : 1;
   if (s > by_traffic) s = by_traffic;
-  if (s > 64) s = 64;
+  if (s > 64) s = 64;  // the merge combines at most 64 splits
   if (s < 1) s = 1;
-  // a workgroup's range of selected ids must fit its LDS stage
-  const int64_t tiles_per_ids = kSelLds / pl.tile_rows;
-  if (a.sel_idx && s < (tiles + tiles_per_ids - 1) / tiles_per_ids) s = (tiles + tiles_per_ids - 1) / tiles_per_ids;
+  // a workgroup's range of selected ids must fit its LDS stage; with more ids
+  // than 64 ranges can stage there is no valid plan (unsupported)
+  if (a.sel_idx) {
+    const int64_t tiles_per_ids = kSelLds / pl.tile_rows;
+    const int64_t need = (tiles + tiles_per_ids - 1) / tiles_per_ids;
+    if (need > 64) {
+      pl.unsupported = 1;
+      return pl;
+    }
+    if (s < need) s = need;
+  }
   pl.splits = (int)s;
   // dim-split twins when the workgroups would not cover the 256 CUs, and
   // always for 512 dims (a full-width accumulator does not fit beside a tile)

@@ -21,6 +21,7 @@ struct DecodePlan {
   int wide_blocks;   // > 0: wide-row MQA kernel with this many 32-head blocks per workgroup
   int wide_twins;    // wide-row workgroups per (sequence, KV head, split)
   size_t ws_bytes;   // split partials (acc, max, sum); 0 with one split
+  int unsupported;   // 1: no launch shape covers these sizes (too many selected ids)
 };
 DecodePlan plan_decode(const lbca_decode_args& a);
 // qrows > 1 (wide-row path only): rows b of the call are queries of a chunk,

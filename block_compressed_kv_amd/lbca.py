@@ -164,6 +164,25 @@ def _need(t, name, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
 
 
+_FLOAT = (torch.float32, torch.bfloat16)
+
+
+def _expect(t, name, shape, dtypes=_FLOAT, device=None):
+    """The library sees raw pointers only, so every buffer's full shape, dtype and
+    device are checked here: a short buffer would otherwise be read or written
+    past its end."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be one of {dtypes}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
 def _stream(stream):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
@@ -182,11 +201,19 @@ def pool_blocks(x, z, bias, block, block_begin, block_end, out_x, v=None, out_v=
                 zb=None, bias_b=None, pos_base=0, rmsnorm_eps=None, rope_dims=0,
                 rope_base=10000.0, stream=None):
     """lbca_pool_blocks: x, v, z, xb, zb [B,H,T,d]; bias [H,m,d]; out [B,H,N,d]."""
-    for t, n in ((x, "x"), (v, "v"), (z, "z"), (xb, "xb"), (zb, "zb"), (out_x, "out_x"), (out_v, "out_v")):
-        _need(t, n, 4)
-    _need(bias, "bias", 3)
-    _need(bias_b, "bias_b", 3)
+    _need(x, "x", 4)
+    _need(out_x, "out_x", 4)
     B, H, T, d = x.shape
+    N, dev, xt = out_x.shape[2], x.device, (x.dtype,)
+    _expect(x, "x", (B, H, T, d))
+    _expect(z, "z", (B, H, T, d), device=dev)
+    for t, n in ((v, "v"), (xb, "xb")):
+        _expect(t, n, (B, H, T, d), xt, dev)
+    _expect(zb, "zb", (B, H, T, d), (z.dtype,), dev)
+    for t, n in ((out_x, "out_x"), (out_v, "out_v")):
+        _expect(t, n, (B, H, N, d), xt, dev)
+    for t, n in ((bias, "bias"), (bias_b, "bias_b")):
+        _expect(t, n, (H, block, d), (torch.float32,), dev)
     a = PoolArgs(_p(x), _p(v), _p(z), _p(bias), _p(xb), _p(zb), _p(bias_b), _p(out_x), _p(out_v),
                  B, H, T, d, block, out_x.shape[2], block_begin, block_end, pos_base,
                  _dt(x), _dt(z), -1.0 if rmsnorm_eps is None else float(rmsnorm_eps), int(rope_dims),
@@ -198,12 +225,20 @@ def pool_blocks(x, z, bias, block, block_begin, block_end, out_x, v=None, out_v=
 def _pool_grad_args(x, z, bias, block, block_begin, block_end, grad_x, dx, dz, dbias, v, grad_v, dv,
                     pos_base, rmsnorm_eps=None, rope_dims=0, rope_base=10000.0, xb=None, zb=None, bias_b=None,
                     dxb=None, dzb=None, dbias_b=None):
-    for t, n in ((x, "x"), (v, "v"), (z, "z"), (grad_x, "grad_x"), (grad_v, "grad_v"), (dx, "dx"),
-                 (dv, "dv"), (dz, "dz"), (xb, "xb"), (zb, "zb"), (dxb, "dxb"), (dzb, "dzb")):
-        _need(t, n, 4)
-    for t, n in ((bias, "bias"), (dbias, "dbias"), (bias_b, "bias_b"), (dbias_b, "dbias_b")):
-        _need(t, n, 3)
+    _need(x, "x", 4)
+    _need(grad_x, "grad_x", 4)
     B, H, T, d = x.shape
+    N, dev, xt, zt = grad_x.shape[2], x.device, (x.dtype,), (z.dtype,)
+    _expect(x, "x", (B, H, T, d))
+    _expect(z, "z", (B, H, T, d), device=dev)
+    for t, n in ((v, "v"), (dx, "dx"), (dv, "dv"), (xb, "xb"), (dxb, "dxb")):
+        _expect(t, n, (B, H, T, d), xt, dev)
+    for t, n in ((dz, "dz"), (zb, "zb"), (dzb, "dzb")):
+        _expect(t, n, (B, H, T, d), zt, dev)
+    for t, n in ((grad_x, "grad_x"), (grad_v, "grad_v")):
+        _expect(t, n, (B, H, N, d), xt, dev)
+    for t, n in ((bias, "bias"), (dbias, "dbias"), (bias_b, "bias_b"), (dbias_b, "dbias_b")):
+        _expect(t, n, (H, block, d), (torch.float32,), dev)
     return PoolGradArgs(_p(x), _p(v), _p(z), _p(bias), _p(grad_x), _p(grad_v), _p(dx), _p(dv), _p(dz),
                         _p(dbias), B, H, T, d, block, grad_x.shape[2], block_begin, block_end, pos_base,
                         _dt(x), _dt(z), -1.0 if rmsnorm_eps is None else float(rmsnorm_eps), int(rope_dims),
@@ -258,15 +293,27 @@ def cache_append(x_new, z_new, raw_x, raw_z, bias, pos, raw_pos_base, block, win
     """lbca_cache_append: x_new, v_new, z_new [B,H,d]; raw_* [B,H,2*ring,d] (mirrored ring);
     bias [H,m,d]; out [B,H,N,d]; pos, raw_pos_base [B] int64 (raw_pos_base is written).
     Dual (CSA) mode: xb_new, zb_new, raw_xb, raw_zb, bias_b for the b-series."""
-    for t, n, nd in ((x_new, "x_new", 3), (v_new, "v_new", 3), (z_new, "z_new", 3), (raw_x, "raw_x", 4),
-                     (raw_v, "raw_v", 4), (raw_z, "raw_z", 4), (bias, "bias", 3), (out_x, "out_x", 4),
-                     (out_v, "out_v", 4), (pos, "pos", 1), (raw_pos_base, "raw_pos_base", 1),
-                     (xb_new, "xb_new", 3), (zb_new, "zb_new", 3), (raw_xb, "raw_xb", 4), (raw_zb, "raw_zb", 4),
-                     (bias_b, "bias_b", 3)):
+    for t, n, nd in ((x_new, "x_new", 3), (raw_x, "raw_x", 4), (out_x, "out_x", 4)):
         _need(t, n, nd)
     B, H, d = x_new.shape
     if raw_x.shape[2] % 2:
         raise ValueError("raw buffers hold 2 * ring rows")
+    R2, N, dev, xt, zt = raw_x.shape[2], out_x.shape[2], x_new.device, (x_new.dtype,), (z_new.dtype,)
+    _expect(x_new, "x_new", (B, H, d))
+    for t, n in ((v_new, "v_new"), (xb_new, "xb_new")):
+        _expect(t, n, (B, H, d), xt, dev)
+    for t, n in ((z_new, "z_new"), (zb_new, "zb_new")):
+        _expect(t, n, (B, H, d), zt, dev)
+    for t, n in ((raw_x, "raw_x"), (raw_v, "raw_v"), (raw_xb, "raw_xb")):
+        _expect(t, n, (B, H, R2, d), xt, dev)
+    for t, n in ((raw_z, "raw_z"), (raw_zb, "raw_zb")):
+        _expect(t, n, (B, H, R2, d), zt, dev)
+    for t, n in ((out_x, "out_x"), (out_v, "out_v")):
+        _expect(t, n, (B, H, N, d), xt, dev)
+    for t, n in ((bias, "bias"), (bias_b, "bias_b")):
+        _expect(t, n, (H, block, d), (torch.float32,), dev)
+    for t, n in ((pos, "pos"), (raw_pos_base, "raw_pos_base")):
+        _expect(t, n, (B,), (torch.int64,), dev)
     a = CacheArgs(_p(x_new), _p(v_new), _p(z_new), _p(raw_x), _p(raw_v), _p(raw_z), _p(bias), _p(out_x),
                   _p(out_v), _p(pos), _p(raw_pos_base), B, H, d, block, window, raw_x.shape[2] // 2,
                   out_x.shape[2], mode, _dt(x_new), _dt(z_new),
@@ -276,13 +323,24 @@ def cache_append(x_new, z_new, raw_x, raw_z, bias, pos, raw_pos_base, block, win
 
 
 def _decode_args(q, pooled_k, raw_k, pos, block, window, mode, out, lse, pooled_v, raw_v,
-                 raw_pos_base, sel_idx, sink, scale, rmsnorm_eps, rope_dims, rope_base):
-    for t, n, nd in ((q, "q", 3), (pooled_k, "pooled_k", 4), (pooled_v, "pooled_v", 4),
-                     (raw_k, "raw_k", 4), (raw_v, "raw_v", 4), (sel_idx, "sel_idx", 2),
-                     (out, "out", 3)):
+                 raw_pos_base, sel_idx, sink, scale, rmsnorm_eps, rope_dims, rope_base, check_out=True):
+    for t, n, nd in ((q, "q", 3), (pooled_k, "pooled_k", 4), (raw_k, "raw_k", 4), (sel_idx, "sel_idx", 2)):
         _need(t, n, nd)
     B, Hq, d = q.shape
-    Hkv, N = pooled_k.shape[1], pooled_k.shape[2]
+    Hkv, N, R, dev, qt = pooled_k.shape[1], pooled_k.shape[2], raw_k.shape[2], q.device, (q.dtype,)
+    _expect(q, "q", (B, Hq, d))
+    for t, n in ((pooled_k, "pooled_k"), (pooled_v, "pooled_v")):
+        _expect(t, n, (B, Hkv, N, d), qt, dev)
+    for t, n in ((raw_k, "raw_k"), (raw_v, "raw_v")):
+        _expect(t, n, (B, Hkv, R, d), qt, dev)
+    for t, n in ((pos, "pos"), (raw_pos_base, "raw_pos_base")):
+        _expect(t, n, (B,), (torch.int64,), dev)
+    if sel_idx is not None:
+        _expect(sel_idx, "sel_idx", (B, sel_idx.shape[1]), (torch.int32,), dev)
+    _expect(sink, "sink", (Hq,), (torch.float32,), dev)
+    if check_out:
+        _expect(out, "out", (B, Hq, d), (torch.float32,), dev)
+        _expect(lse, "lse", (B, Hq), (torch.float32,), dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     return DecodeArgs(_p(q), _p(pooled_k), _p(pooled_v), _p(raw_k), _p(raw_v), _p(pos),
@@ -298,7 +356,7 @@ def decode_workspace_bytes(q, pooled_k, raw_k, pos, block, window, mode, **kw):
     a = _decode_args(q, pooled_k, raw_k, pos, block, window, mode, out if out is not None else q,
                      kw.get("lse"), kw.get("pooled_v"), kw.get("raw_v"), kw.get("raw_pos_base"),
                      kw.get("sel_idx"), kw.get("sink"), kw.get("scale"), kw.get("rmsnorm_eps"),
-                     kw.get("rope_dims", 0), kw.get("rope_base", 10000.0))
+                     kw.get("rope_dims", 0), kw.get("rope_base", 10000.0), check_out=out is not None)
     n = ctypes.c_size_t()
     _check(lib().lbca_attend_decode_workspace(ctypes.byref(a), ctypes.byref(n)),
            "lbca_attend_decode_workspace")
@@ -331,15 +389,22 @@ def attend_prefill(q, q_pos0, pooled_k, raw_k, raw_pos_base, block, window, mode
                    lse=None, pooled_v=None, raw_v=None, sink=None, scale=None, out_dtype=None,
                    stream=None):
     """lbca_attend_prefill: q [B,Tq,Hq,d]; returns (out [B,Tq,Hq,d], lse [B,Tq,Hq])."""
-    for t, n, nd in ((q, "q", 4), (pooled_k, "pooled_k", 4), (pooled_v, "pooled_v", 4),
-                     (raw_k, "raw_k", 4), (raw_v, "raw_v", 4)):
+    for t, n, nd in ((q, "q", 4), (pooled_k, "pooled_k", 4), (raw_k, "raw_k", 4)):
         _need(t, n, nd)
     B, Tq, Hq, d = q.shape
+    Hkv, N, R, dev, qt = pooled_k.shape[1], pooled_k.shape[2], raw_k.shape[2], q.device, (q.dtype,)
     if out is None:
         out = torch.empty((B, Tq, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
-    _need(out, "out", 4)
     if lse is None:
         lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
+    _expect(q, "q", (B, Tq, Hq, d))
+    for t, n in ((pooled_k, "pooled_k"), (pooled_v, "pooled_v")):
+        _expect(t, n, (B, Hkv, N, d), qt, dev)
+    for t, n in ((raw_k, "raw_k"), (raw_v, "raw_v")):
+        _expect(t, n, (B, Hkv, R, d), qt, dev)
+    _expect(sink, "sink", (Hq,), (torch.float32,), dev)
+    _expect(out, "out", (B, Tq, Hq, d), device=dev)
+    _expect(lse, "lse", (B, Tq, Hq), (torch.float32,), dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     a = PrefillArgs(_p(q), _p(pooled_k), _p(pooled_v), _p(raw_k), _p(raw_v), _p(sink), _p(out), _p(lse),
@@ -349,9 +414,20 @@ def attend_prefill(q, q_pos0, pooled_k, raw_k, raw_pos_base, block, window, mode
     return out, lse
 
 
+def _check_index(q_idx, head_w, keys, pos):
+    B, HI, dI = q_idx.shape
+    dev = q_idx.device
+    _expect(q_idx, "q_idx", (B, HI, dI))
+    _expect(head_w, "head_w", (B, HI), (torch.float32,), dev)
+    _expect(keys, "keys", (B, keys.shape[1], dI), (q_idx.dtype,), dev)
+    _expect(pos, "pos", (B,), (torch.int64,), dev)
+
+
 def index_workspace_bytes(q_idx, head_w, keys, pos, block, k):
     """csa_index_topk_workspace: bytes of workspace csa_index_topk needs for these shapes
     (the query's buffer stands in for the output, which the size does not depend on)."""
+    _need(keys, "keys", 3)
+    _check_index(q_idx, head_w, keys, pos)
     B, HI, dI = q_idx.shape
     a = IndexArgs(_p(q_idx), _p(head_w), _p(keys), _p(pos), _p(q_idx), None,
                   B, HI, dI, keys.shape[1], k, block, _dt(q_idx))
@@ -363,13 +439,16 @@ def index_workspace_bytes(q_idx, head_w, keys, pos, block, k):
 def csa_index_topk(q_idx, head_w, keys, pos, block, k, out_idx=None, out_score=None,
                    workspace=None, stream=None):
     """csa_index_topk: q_idx [B,HI,dI], head_w [B,HI], keys [B,N,dI]; returns (idx, score)."""
-    for t, n, nd in ((q_idx, "q_idx", 3), (head_w, "head_w", 2), (keys, "keys", 3)):
+    for t, n, nd in ((q_idx, "q_idx", 3), (keys, "keys", 3)):
         _need(t, n, nd)
     B, HI, dI = q_idx.shape
     if out_idx is None:
         out_idx = torch.empty((B, k), dtype=torch.int32, device=q_idx.device)
     if out_score is None:
         out_score = torch.empty((B, k), dtype=torch.float32, device=q_idx.device)
+    _check_index(q_idx, head_w, keys, pos)
+    _expect(out_idx, "out_idx", (B, k), (torch.int32,), q_idx.device)
+    _expect(out_score, "out_score", (B, k), (torch.float32,), q_idx.device)
     a = IndexArgs(_p(q_idx), _p(head_w), _p(keys), _p(pos), _p(out_idx), _p(out_score),
                   B, HI, dI, keys.shape[1], k, block, _dt(q_idx))
     need = ctypes.c_size_t()
@@ -384,11 +463,22 @@ def csa_index_topk(q_idx, head_w, keys, pos, block, k, out_idx=None, out_score=N
 
 def _csa_prefill_args(q_idx, head_w, idx_keys, q, entries, raw, q_pos0, raw_pos_base, block, window, k,
                       out, lse, out_idx, sink, scale, rmsnorm_eps, rope_dims, rope_base):
-    for t, n, nd in ((q_idx, "q_idx", 4), (head_w, "head_w", 3), (idx_keys, "idx_keys", 3), (q, "q", 4),
-                     (entries, "entries", 3), (raw, "raw", 3), (out, "out", 4), (out_idx, "out_idx", 3)):
+    for t, n, nd in ((q_idx, "q_idx", 4), (q, "q", 4), (entries, "entries", 3), (raw, "raw", 3)):
         _need(t, n, nd)
     B, Tq, Hq, d = q.shape
     HI, dI = q_idx.shape[2], q_idx.shape[3]
+    N, R, dev, qt = entries.shape[1], raw.shape[1], q.device, (q.dtype,)
+    _expect(q, "q", (B, Tq, Hq, d))
+    _expect(q_idx, "q_idx", (B, Tq, HI, dI), qt, dev)
+    _expect(head_w, "head_w", (B, Tq, HI), (torch.float32,), dev)
+    _expect(idx_keys, "idx_keys", (B, N, dI), qt, dev)
+    _expect(entries, "entries", (B, N, d), qt, dev)
+    _expect(raw, "raw", (B, R, d), qt, dev)
+    _expect(sink, "sink", (Hq,), (torch.float32,), dev)
+    if out is not q:  # the workspace query passes q in place of an absent output
+        _expect(out, "out", (B, Tq, Hq, d), (torch.float32,), dev)
+    _expect(lse, "lse", (B, Tq, Hq), (torch.float32,), dev)
+    _expect(out_idx, "out_idx", (B, Tq, k), (torch.int32,), dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     return CsaPrefillArgs(_p(q_idx), _p(head_w), _p(idx_keys), _p(q), _p(entries), _p(raw), _p(sink), _p(out),

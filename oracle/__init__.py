@@ -17,6 +17,7 @@ Modules
                  used only to check ``lbca_oracle``.
 
 Pins: every function is checked in ``tests/test_oracle_*.py`` against values the
-pages print (``tests/golden/``), closed forms, invariants and brute force.  The
-one function with no such pin is listed as "parity unpinned" in its docstring.
+pages print (``tests/golden/``), closed forms, invariants and brute force; no
+function is without a pin.  The pages print no output values at the workload
+sizes, so beyond those pins the fp64 oracle itself is the reference there.
 """

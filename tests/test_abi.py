@@ -225,6 +225,24 @@ def test_decode_validation(kw, code):
 
 
 @fake_ptr
+def test_decode_selection_split_limit():
+    # The selected ids of one workgroup's row range are staged in LDS (1024 ids)
+    # and at most 64 splits are merged, so a selection plus raw span beyond
+    # 64 x 1024 rows has no launch shape: rejected, not silently truncated.
+    sel = dict(sel_idx=FAKE, k_sel=2048, mode=1, raw_rows=70000)
+    wide = dict(q_heads=64, kv_heads=1, dim=512, pooled_v=None, raw_v=None, entries=4096)
+    for kw in (dict(sel), dict(sel, **wide)):
+        st, st2, _ = _decode(window=64000, **kw)          # 64 + 2000 tiles of 32 rows: 65 ranges
+        assert st == st2 == lbca.ERR_UNSUPPORTED, kw
+        st, _, need = _decode(window=63488, **kw)         # 64 + 1984 tiles: exactly 64 ranges
+        assert st == 0 and need > 0, kw
+    assert _csap(k=2048, window=64000, raw_rows=70000, q_pos0=69000, raw_pos_base=0,
+                 n_entries=20000)[0] == lbca.ERR_UNSUPPORTED
+    assert _csap(k=2048, window=63488, raw_rows=70000, q_pos0=69000, raw_pos_base=0,
+                 n_entries=20000)[0] == 0
+
+
+@fake_ptr
 def test_decode_workspace_required():
     big = dict(entries=8192)                            # long row lists are split over workgroups
     st, st2, need = _decode(**big)

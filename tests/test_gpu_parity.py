@@ -14,7 +14,7 @@ import torch
 from block_compressed_kv_amd import synth
 from oracle import lbca_oracle as O
 
-from parity_util import check, check_bf16, check_f32_rows, host, say, topk_matches
+from parity_util import check, check_bf16, check_f32_rows, host, index_score_bound, say, topk_matches
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -567,8 +567,9 @@ def test_index_topk(lib, N, k, t_list):
     for b, t in enumerate(t_list):
         n_vis = min((t + 1) // m, N)
         s = O.index_scores(host(qi[b]), host(w[b]), host(keys[b]), n_vis)
-        margin = topk_matches(idx[b], s, k, f"top-k seq {b}")
-        say(f"top-k seq {b}: n_vis={n_vis} k={k} margin={margin:.3e}")
+        margin, band = topk_matches(idx[b], s, k, f"top-k seq {b}",
+                                    index_score_bound(host(qi[b]), host(w[b]), host(keys[b]), n_vis))
+        say(f"top-k seq {b}: n_vis={n_vis} k={k} margin={margin:.3e}" + (" in the fp32 tie band" if band else ""))
         sel = idx[b][idx[b] >= 0]
         np.testing.assert_allclose(score[b][:sel.size], s[sel], rtol=1e-5, atol=1e-5)
         assert np.isnan(score[b][sel.size:]).all()
@@ -657,13 +658,15 @@ def test_csa_sparse_prefill(lib, B, Tq, p0, HI, dI, k, treated):
                          host(C["zb"]), host(C["bias_b"][0]), m, 0, N)
     qi, w, ki, q, raw = host(C["qi"]), host(C["w"]), host(ikeys[:, 0]), host(C["q"]), host(C["ca"])
     sink = host(C["sink"])
+    band_rows = 0
     for b in range(B):
         ro = np.zeros((Tq, Hq, d))
         rl = np.zeros((Tq, Hq))
         for i in range(Tq):
             t = p0 + i
             n_vis = min((t + 1) // m, N)
-            topk_matches(idx[b, i], O.index_scores(qi[b, i], w[b, i], ki[b], n_vis), k, f"seq {b} query {i}")
+            band_rows += topk_matches(idx[b, i], O.index_scores(qi[b, i], w[b, i], ki[b], n_vis), k,
+                                      f"seq {b} query {i}", index_score_bound(qi[b, i], w[b, i], ki[b], n_vis))[1]
             # the attention over the GPU's (valid) selection
             oo, ll = O.attend_decode(q[b, i][None], pooled[b][None], None, raw[b][None], None, [t], m, W,
                                      O.OVERLAP, 1 / math.sqrt(d), raw_pos_base=[0], sel_idx=idx[b, i][None],
@@ -671,6 +674,7 @@ def test_csa_sparse_prefill(lib, B, Tq, p0, HI, dI, k, treated):
             ro[i], rl[i] = oo[0], ll[0]
         check_bf16(o[b], ro, f"sparse prefill out seq {b}")
         check_bf16(lse[b], rl, f"sparse prefill lse seq {b}")
+    say(f"sparse prefill: {band_rows} of {B * Tq} selections in the fp32 tie band (validity checked)")
 
 
 @pytest.mark.parametrize("Tq,N", [
@@ -692,7 +696,8 @@ def test_csa_sparse_prefill_two_stage_selection(lib, Tq, N):
     for i in range(Tq):
         t = p0 + i
         n_vis = min((t + 1) // m, N)
-        topk_matches(idx[0, i], O.index_scores(qh[0, i], wh[0, i], kh[0], n_vis), k, f"query {i}")
+        topk_matches(idx[0, i], O.index_scores(qh[0, i], wh[0, i], kh[0], n_vis), k, f"query {i}",
+                     index_score_bound(qh[0, i], wh[0, i], kh[0], n_vis))
         oo, ll = O.attend_decode(host(q)[0, i][None], eh[0][None, None], None, rh[0][None, None], None, [t], m, W,
                                  O.OVERLAP, 1 / math.sqrt(d), raw_pos_base=[base], sel_idx=idx[0, i][None])
         ro[i], rl[i] = oo[0], ll[0]
