@@ -48,6 +48,7 @@ const char* lbca_status_string(int status) {
     case LBCA_ERR_UNSUPPORTED: return "unsupported dtype, dimension or flag combination";
     case LBCA_ERR_WORKSPACE: return "workspace missing or too small";
     case LBCA_ERR_HIP: return "HIP runtime error";
+    case LBCA_ERR_TOO_LARGE: return "sizes need more than the static scratch of the no-allocation entry point";
     default: return "unknown status";
   }
 }
@@ -258,6 +259,17 @@ int lbca_attend_decode(const lbca_decode_args* a, void* workspace, size_t worksp
     return LBCA_ERR_WORKSPACE;
   if (a->batch == 0) return LBCA_OK;
   return hip_status(lbca::launch_decode(*a, plan, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int lbca_attend_decode_noalloc(const lbca_decode_args* a, void* stream) {
+  int st = validate_decode(a);
+  if (st != LBCA_OK) return st;
+  const lbca::DecodePlan plan = lbca::plan_decode(*a);
+  if (plan.ws_bytes > LBCA_NOALLOC_SCRATCH_BYTES) return LBCA_ERR_TOO_LARGE;
+  if (a->batch == 0) return LBCA_OK;
+  void* ws = nullptr;
+  if (plan.ws_bytes > 0 && lbca::static_scratch(&ws) != hipSuccess) return LBCA_ERR_HIP;
+  return hip_status(lbca::launch_decode(*a, plan, ws, static_cast<hipStream_t>(stream)));
 }
 
 // ---------------------------------------------------------------------------

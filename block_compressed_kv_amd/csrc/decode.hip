@@ -40,6 +40,7 @@
 // decode_merge_kernel combines them in a fixed order (bitwise reproducible).
 // No device-scope fence is used anywhere: on this multi-XCD part a
 // device-scope release/acquire writes back and invalidates the XCD's L2.
+#include <mutex>
 #include <type_traits>
 
 #include "decode_common.h"
@@ -927,6 +928,33 @@ hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void
   if (e != hipSuccess || plan.splits == 1) return e;
   launch_decode_merge(p, a.batch, a.dim, false, stream);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of lbca_attend_decode_noalloc: the split partials of the
+// decode kernels live in this file-scope device array instead of a caller
+// workspace.  Each GPU holds its own copy at its own address; host code must
+// use the address hipGetSymbolAddress reports for the current device (the
+// array's name is only a host-side stand-in), looked up once per device.
+static __device__ __align__(256) unsigned char scratch[LBCA_NOALLOC_SCRATCH_BYTES];
+
+hipError_t static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 }  // namespace lbca

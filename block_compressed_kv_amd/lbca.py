@@ -18,7 +18,8 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblbca.so")
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "lbca.h")
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_TOO_LARGE = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 16 << 20
 F32, BF16 = 0, 1
 EXCLUSIVE, OVERLAP = 0, 1
 
@@ -119,6 +120,7 @@ def lib():
         L.lbca_pool_blocks_backward.argtypes = [ctypes.POINTER(PoolGradArgs), _vp, ctypes.c_size_t, _vp]
         L.lbca_attend_decode_workspace.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_size_t)]
         L.lbca_attend_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp, ctypes.c_size_t, _vp]
+        L.lbca_attend_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
         L.lbca_attend_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
         L.csa_index_topk_workspace.argtypes = [ctypes.POINTER(IndexArgs), ctypes.POINTER(ctypes.c_size_t)]
         L.csa_index_topk.argtypes = [ctypes.POINTER(IndexArgs), _vp, ctypes.c_size_t, _vp]
@@ -382,6 +384,17 @@ def attend_decode(q, pooled_k, raw_k, pos, block, window, mode, out=None, lse=No
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().lbca_attend_decode(ctypes.byref(a), _p(workspace), ws_bytes, _stream(stream)),
            "lbca_attend_decode")
+    return out, lse
+
+
+def attend_decode_noalloc(q, pooled_k, raw_k, pos, block, window, mode, out, lse, pooled_v=None, raw_v=None,
+                          raw_pos_base=None, sel_idx=None, sink=None, scale=None, rmsnorm_eps=None, rope_dims=0,
+                          rope_base=10000.0, stream=None):
+    """lbca_attend_decode_noalloc: lbca_attend_decode with the split partials in the
+    library's static scratch; the caller passes the outputs (nothing is allocated)."""
+    a = _decode_args(q, pooled_k, raw_k, pos, block, window, mode, out, lse, pooled_v, raw_v,
+                     raw_pos_base, sel_idx, sink, scale, rmsnorm_eps, rope_dims, rope_base)
+    _check(lib().lbca_attend_decode_noalloc(ctypes.byref(a), _stream(stream)), "lbca_attend_decode_noalloc")
     return out, lse
 
 

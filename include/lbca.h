@@ -3,9 +3,11 @@
  *
  * C ABI.  Plain pointers and sizes only.  Device pointers are HIP device
  * memory owned by the caller; the library allocates nothing, keeps no state
- * between calls, never frees a caller buffer, and only enqueues work on the
- * stream the caller passes (a hipStream_t, 0 = the null stream).  Every call is
- * asynchronous with respect to the host unless stated otherwise.
+ * between calls (except the static scratch array of
+ * lbca_attend_decode_noalloc, part of the loaded code object), never frees a
+ * caller buffer, and only enqueues work on the stream the caller passes (a
+ * hipStream_t, 0 = the null stream).  Every call is asynchronous with respect
+ * to the host unless stated otherwise.
  *
  * Errors: every entry point returns an int status.  Argument validation runs on
  * the host BEFORE any device work is enqueued; an argument error returns
@@ -62,6 +64,7 @@ extern "C" {
 #define LBCA_ERR_UNSUPPORTED (-2)  /* valid but not implemented (dtype, dim, flag mix) */
 #define LBCA_ERR_WORKSPACE (-3)    /* workspace missing or too small */
 #define LBCA_ERR_HIP (-4)          /* a HIP runtime call failed */
+#define LBCA_ERR_TOO_LARGE (-5)    /* beyond the static scratch of lbca_attend_decode_noalloc */
 
 /* element types */
 #define LBCA_F32 0
@@ -341,6 +344,23 @@ typedef struct lbca_decode_args {
 LBCA_API int lbca_attend_decode_workspace(const lbca_decode_args* a, size_t* bytes);
 LBCA_API int lbca_attend_decode(const lbca_decode_args* a, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* Decode attention that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, validation, kernels and results as
+ * lbca_attend_decode; the split partials go to a static scratch array that the
+ * library holds in every GPU's memory until the process ends instead of a
+ * caller workspace.  The scratch is at most LBCA_NOALLOC_SCRATCH_BYTES; a call
+ * whose lbca_attend_decode_workspace size exceeds it returns
+ * LBCA_ERR_TOO_LARGE before any device work.  The stream must belong to the
+ * calling thread's current device.  Every call on one GPU shares that GPU's
+ * scratch: calls that overlap on one GPU (other streams, other threads) race.
+ * The scratch needs no initialisation (the kernels overwrite every partial
+ * they read).  No hipMalloc, hipFree or allocating library call is made; the
+ * first call on a device looks the scratch address up once.
+ */
+#define LBCA_NOALLOC_SCRATCH_BYTES (16u << 20)
+LBCA_API int lbca_attend_decode_noalloc(const lbca_decode_args* a, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Prefill attention over a chunk of q_len consecutive queries (mSeek "How LBCA
