@@ -12,6 +12,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // Grid-stride read of n16 16-byte vectors, eight loads in flight per thread;
@@ -93,6 +94,27 @@ __global__ __launch_bounds__(256) void mfma_kernel(float* __restrict__ out, int 
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = c0[0] + c1[5] + c2[10] + c3[15];
 }
 
+// Eight independent chains of v_mfma_f32_16x16x32_bf16 per wave (16384 flops
+// each), the instruction the attention kernels use.
+__global__ __launch_bounds__(256) void mfma16_kernel(float* __restrict__ out, int iters) {
+  const float s = 1e-3f * (float)(threadIdx.x & 63);
+  bf16x8_t a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(s + 0.25f * e);
+    b[e] = (__bf16)(0.5f - s);
+  }
+  f32x4_t c[8] = {};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[k], 0, 0, 0);
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r += c[k][k & 3];
+  out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = r;
+}
+
 __global__ void empty_kernel() {}
 
 }  // namespace
@@ -133,6 +155,14 @@ __attribute__((visibility("default"))) int ceil_lds(const void* src, void* out, 
 __attribute__((visibility("default"))) int ceil_mfma(void* out, int grid, int iters, void* stream) {
   if (!out || grid < 1 || iters < 1) return (int)hipErrorInvalidValue;
   mfma_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<float*>(out), iters);
+  return (int)hipGetLastError();
+}
+
+// grid workgroups of 4 waves, each wave 8 * iters MFMAs of 16384 flops; out
+// holds grid * 256 floats.
+__attribute__((visibility("default"))) int ceil_mfma16(void* out, int grid, int iters, void* stream) {
+  if (!out || grid < 1 || iters < 1) return (int)hipErrorInvalidValue;
+  mfma16_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<float*>(out), iters);
   return (int)hipGetLastError();
 }
 

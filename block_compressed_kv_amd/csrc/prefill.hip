@@ -453,34 +453,49 @@ __global__ __launch_bounds__(NWV * 64, 1) void prefill_kernel(PrefillParams p) {
   }
 }
 
+// Raw buffer resource over [base, base + bytes) (bytes below 2^31) and a
+// 16-byte load from it at vector offset + scalar offset; offsets at or past
+// the limit read zeros without a memory access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(uintptr_t base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 ldb16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0));
+}
+
 // ---------------------------------------------------------------------------
-// 128-dim prefill with a register-staged, four-buffer tile pipeline.
+// 128-dim prefill on 32x32 MFMA tiles with a register-staged, four-buffer tile
+// pipeline.
 //
-// Same work split, operand layouts and softmax as prefill_kernel (8 waves, 256
-// rows of the flattened (position, GQA head) space per workgroup, 32-key tiles,
-// S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16), but the loop is
-// arranged so that every phase pairs matrix work with independent vector work
-// and the LDS reads of a phase are issued one phase ahead:
-//   tile u: global rows -> registers at step u-4, registers -> LDS buffer
-//   u % 4 at step u-2 (one barrier per step makes it visible);
-//   step t: the reads of V(t) and K(t+1) go out first, then
-//     block A: exponentials of tile t beside the Q.K MFMAs of tile t+1,
-//     block B: the P.V MFMAs of tile t beside the mask and max of tile t+1,
-//   and the (rare) accumulator rescale for tile t+1 closes the step.
-// Plain LDS stores and the transposing-read builtin let the compiler count
-// LDS operations exactly (no LDS DMA whose waits it cannot place).
+// Same work split as prefill_kernel (8 waves, 256 rows of the flattened
+// (position, GQA head) space per workgroup, 32-key tiles, a per-query visible
+// span), but each wave holds its 32 query rows as one 32-column block and uses
+// v_mfma_f32_32x32x16_bf16, which moves twice the flops per cycle of the
+// 16x16x32 form on this part:
+//   S^T (32 keys x 32 rows) = K (32 x 16 dims) Q^T, eight MFMAs per tile; lane
+//   (n, h) then holds 16 scores of query row n: keys 8j + 4h + r (j, r < 4), so
+//   a row's max and sum need one 32-lane swap;
+//   O^T (4 x 32 dims x 32 rows) += V^T P^T, two MFMAs of 16 keys per 32-dim
+//   block: P^T is the score layout itself (key k-slot order 4h..4h+3,
+//   8+4h..8+4h+3, then +16), V^T comes from transposing LDS reads in the same
+//   key order.
+// The loop: tile u goes global -> registers at step u-4 and registers -> LDS
+// buffer u % 4 at step u-2 (plain stores, so the compiler counts every LDS
+// operation; one barrier per step makes a tile visible).  Step t issues the
+// reads of V(t) and K(t+1), then the exponentials of tile t beside the Q.K
+// MFMAs of tile t+1, then P.V of tile t and the mask and max of tile t+1; the
+// (rare) accumulator rescale closes the step.
 template <bool SHARED>
 __global__ __launch_bounds__(512, 1) void prefill128_kernel(PrefillParams p) {
-  constexpr int D = 128, NWV = 8, NT = 512, QG = 2, KT = 32, KB = 2, KS = 4, DT = 8, CH = 16;
-  constexpr int ROWS = NWV * QG * 16;  // 256
-  constexpr int TILE = KT * D;         // bf16 elements of one K (or V) tile
+  constexpr int D = 128, NWV = 8, NT = 512, KT = 32, DC = D / 16, DB = D / 32, CH = 16;
+  constexpr int ROWS = NWV * 32;  // 256
+  constexpr int TILE = KT * D;    // bf16 elements of one K (or V) tile
   static_assert(KT * CH == NT, "one 16-byte chunk per thread per tile and series");
   __shared__ __attribute__((aligned(16))) bf16_t lds[4 * (SHARED ? 1 : 2) * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15, kq = lane >> 4;
-  const int swz_n = swz<D>(n), swz_tr = swz<D>(4 * kq + (n >> 2));
+  const int n = lane & 31, h = lane >> 5;
   const int bid = blockIdx.x;
   const int rblk = bid % p.row_blocks;
   const int bh = bid / p.row_blocks;
@@ -492,27 +507,26 @@ __global__ __launch_bounds__(512, 1) void prefill128_kernel(PrefillParams p) {
   const int q0 = (int)p.q_pos0;
   const int p_first = q0 + row0 / G, p_last = q0 + row_last / G;
 
-  uint4 qr[QG][KS];
-  int my_np[QG], my_rb[QG], my_pos[QG];
-  int64_t my_out[QG];
-  bool my_ok[QG];
-#pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    const int r = row0 + wave * (QG * 16) + g * 16 + n;
-    const bool ok = r < rows_total;
-    const int rr = ok ? r : rows_total - 1;
+  // this lane's query row (B operand: dims 16c + 8h .. +8) and its visibility
+  uint4 qr[DC];
+  int my_np, my_rb, my_pos;
+  int64_t my_out;
+  bool my_ok;
+  {
+    const int r = row0 + wave * 32 + n;
+    my_ok = r < rows_total;
+    const int rr = my_ok ? r : rows_total - 1;
     const int pl = rr / G, hg = rr - pl * G;
     int64_t np, rb;
     visible_range(q0 + pl, p.m, p.W, p.mode, &np, &rb);
-    my_np[g] = (int)np;
-    my_rb[g] = (int)rb;
-    my_pos[g] = q0 + pl;
-    my_ok[g] = ok;
-    my_out[g] = (((int64_t)b * p.q_len + pl) * p.hq + (int64_t)kvh * G + hg) * D;
-    const bf16_t* qrow = p.q + my_out[g] + 8 * kq;
+    my_np = (int)np;
+    my_rb = (int)rb;
+    my_pos = q0 + pl;
+    my_out = (((int64_t)b * p.q_len + pl) * p.hq + (int64_t)kvh * G + hg) * D;
+    const bf16_t* qrow = p.q + my_out + 8 * h;
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qr[g][s] = ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s) : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < DC; ++c)
+      qr[c] = my_ok ? *reinterpret_cast<const uint4*>(qrow + 16 * c) : make_uint4(0, 0, 0, 0);
   }
 
   int64_t t64a, t64b;
@@ -527,8 +541,9 @@ __global__ __launch_bounds__(512, 1) void prefill128_kernel(PrefillParams p) {
   const uintptr_t rk_base = reinterpret_cast<uintptr_t>(p.rk) + ((int64_t)bh * p.raw_rows - p.raw_pos_base) * (D * 2);
   const uintptr_t rv_base = reinterpret_cast<uintptr_t>(SHARED ? p.rk : p.rv) + ((int64_t)bh * p.raw_rows - p.raw_pos_base) * (D * 2);
 
-  // this thread's chunk of every tile: LDS slot (r, c) = element 8 * tid holds
-  // global chunk c ^ swz(r) of tile row r (the swizzled layout of prefill_kernel)
+  // LDS tile layout: row r holds its 16-byte chunks in swizzled order, chunk
+  // x at position x ^ swz(r); this thread's chunk of every tile is LDS slot
+  // 8 * tid = (row tid / 16, position tid % 16), global chunk position ^ swz.
   const int st_r = tid / CH, st_c = tid % CH;
   const uint32_t st_goff = 16u * (uint32_t)(st_c ^ swz<D>(st_r));
   // tile u lives in buffer u % 4 (compile-time below, so buffer bases fold into
@@ -538,26 +553,31 @@ __global__ __launch_bounds__(512, 1) void prefill128_kernel(PrefillParams p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
   // two tiles' chunks in flight between global memory and LDS: tile u goes to
   // staging slot u % 2 at step u - 4 and into LDS at step u - 2
   uint4 stg_k[2], stg_v[2];
   // (captures by value: a select between references to the bases would become
   // a private-memory table lookup)
+  // Tile rows come through buffer resources (scalar base and byte limit) with
+  // a wave-uniform tile offset and this thread's fixed vector offset: no
+  // vector address register that later instructions could overwrite while a
+  // load is in flight (which would make the compiler wait for it), and rows
+  // past the span's end (the last tile's tail) read as zeros without touching
+  // memory.  Each span's limit is its last visible row.
+  const uint32_t st_voff = (uint32_t)(st_r * D * 2) + st_goff;
+  const int64_t raw_lim = ((int64_t)p_last + 1 - p.raw_pos_base) * (D * 2);
+  const __amdgpu_buffer_rsrc_t rs_pk = make_rsrc(pk_base, (int64_t)NP * (D * 2));
+  const __amdgpu_buffer_rsrc_t rs_pv = make_rsrc(pv_base, (int64_t)NP * (D * 2));
+  const __amdgpu_buffer_rsrc_t rs_rk = make_rsrc(rk_base + (uintptr_t)(p.raw_pos_base * (D * 2)), raw_lim);
+  const __amdgpu_buffer_rsrc_t rs_rv = make_rsrc(rv_base + (uintptr_t)(p.raw_pos_base * (D * 2)), raw_lim);
   auto fetch = [=, &stg_k, &stg_v](int u, auto slot) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot)::value;
     (void)stg_v;
     const bool pooled = u < T1;
-    const int x0 = pooled ? u * KT : RB + (u - T1) * KT;
-    const int lim = pooled ? NP : p_last + 1;
-    const int x = x0 + st_r < lim ? x0 + st_r : lim - 1;  // rows past the list re-read its last row
-    const uint64_t off = (uint64_t)(int64_t)x * (D * 2) + st_goff;
-    const uintptr_t kb = pooled ? pk_base : rk_base, vb = pooled ? pv_base : rv_base;
-    // global (not flat) loads: a flat load also counts against the LDS counter,
-    // so every wait for an LDS read would wait for these rows too
-    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
-    stg_k[SL] = __builtin_bit_cast(uint4, *reinterpret_cast<g_u32x4*>(kb + off));
-    if constexpr (!SHARED) stg_v[SL] = __builtin_bit_cast(uint4, *reinterpret_cast<g_u32x4*>(vb + off));
+    const int soff = (pooled ? u * KT : RB - (int)p.raw_pos_base + (u - T1) * KT) * (D * 2);
+    stg_k[SL] = ldb16(pooled ? rs_pk : rs_rk, st_voff, soff);
+    if constexpr (!SHARED) stg_v[SL] = ldb16(pooled ? rs_pv : rs_rv, st_voff, soff);
   };
   auto stash = [&](auto c, auto slot) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot)::value;
@@ -565,125 +585,108 @@ __global__ __launch_bounds__(512, 1) void prefill128_kernel(PrefillParams p) {
     if constexpr (!SHARED) *reinterpret_cast<uint4*>(vbuf(c) + 8 * tid) = stg_v[SL];
   };
 
-  // row sums come from the MFMA: an all-ones A operand against P^T gives every
-  // lane its row's sum of the bf16 weights (the same weights P.V uses)
-  float m_run[QG], mu[QG];
-  f32x4 acc[QG][DT], lsum[QG];
-  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+  float m_run = kNegInf, mu = 0.f, l_run = 0.f;
+  f32x16 acc[DB];
 #pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    m_run[g] = kNegInf;
-    mu[g] = 0.f;
-    lsum[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < DT; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
   auto is_full = [&](int u) -> bool {
     const bool pooled = u < T1;
     const int x0 = pooled ? u * KT : RB + (u - T1) * KT;
     return pooled ? (u + 1) * KT <= NPmin : (x0 >= RBmax && x0 + KT - 1 <= p_first);
   };
-  auto read_k = [&](auto c, int kb, uint4 (&ka)[KS]) __attribute__((always_inline)) {
-    const bf16_t* kt = kbuf(c);
+  // K A operands of dim chunks [c0, c0 + 4): lane (key n, h), dims 16c + 8h .. +8
+  auto read_k = [&](auto c, int c0, uint4 (&ka)[4]) __attribute__((always_inline)) {
+    const bf16_t* kt = kbuf(c) + n * D;
+    const int sw = swz<D>(n);
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      ka[s] = *reinterpret_cast<const uint4*>(&kt[(16 * kb + n) * D + 8 * ((4 * s + kq) ^ swz_n)]);
+    for (int i = 0; i < 4; ++i) ka[i] = *reinterpret_cast<const uint4*>(kt + 8 * ((2 * (c0 + i) + h) ^ sw));
   };
-  // V^T operand: lane (n, kq) at row 4kq + n/4 (+16 for the second key block),
-  // column 16t + 4(n%4) (+ 8 ^ swizzle), two transposing reads per 16-dim block
-  auto read_v = [&](auto c, s16x4 (&va)[2 * DT]) __attribute__((always_inline)) {
+  // V^T A operands: lane (dim 16 (q % 2) + i, h = q / 2) of 16-lane group q, for
+  // 32-dim block db and key half kh: keys 16kh + 4h.. and 16kh + 8 + 4h.., two
+  // transposing reads (lane j of the group points at row base + j / 4,
+  // dims 4 (j % 4) ..+4 of its 16-dim half)
+  const int vq = lane >> 4, vj = lane & 15;
+  const int v_row = 4 * (vq >> 1) + (vj >> 2), v_col = 16 * (vq & 1) + 4 * (vj & 3);
+  auto read_v = [&](auto c, s16x4 (&va)[DB][2][2]) __attribute__((always_inline)) {
     const bf16_t* vt = vbuf(c);
 #pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      const bf16_t* a = vt + (4 * kq + (n >> 2)) * D + 4 * (n & 1) + 8 * ((2 * t + ((n & 3) >> 1)) ^ swz_tr);
-      va[2 * t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a));
-      va[2 * t + 1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a + 16 * D));
-    }
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = 16 * kh + 8 * u + v_row;
+          const int col = 32 * db + v_col;
+          const bf16_t* a = vt + r * D + 8 * ((col >> 3) ^ swz<D>(r)) + (col & 7);
+          va[db][kh][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a));
+        }
   };
-  // S^T of one 16-key block: 16 keys x 16 rows per MFMA, each K operand feeding QG MFMAs
-  auto qk = [&](const uint4 (&ka)[KS], f32x4 (&sc)[QG]) __attribute__((always_inline)) {
+  auto qk = [&](const uint4 (&ka)[4], int c0, f32x16& sc) __attribute__((always_inline)) {
 #pragma unroll
-    for (int g = 0; g < QG; ++g) sc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-      for (int g = 0; g < QG; ++g)
-        sc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[s]),
-                                                        __builtin_bit_cast(bf16x8, qr[g][s]), sc[g], 0, 0, 0);
+    for (int i = 0; i < 4; ++i)
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[i]),
+                                                   __builtin_bit_cast(bf16x8, qr[c0 + i]), sc, 0, 0, 0);
   };
   // mask (tiles some row does not fully see) and this lane's max of the tile in
-  // scaled log2 units (the row max over the row's four lanes is taken only when
+  // scaled log2 units (the row max over the row's two lanes is taken only when
   // some lane's max passes the reference)
-  auto mask_max = [&](int u, bool full, f32x4 (&sc)[KB][QG], float (&tmax)[QG]) __attribute__((always_inline)) {
-    const bool pooled = u < T1;
-    const int x0 = pooled ? u * KT : RB + (u - T1) * KT;
+  auto mask_max = [&](int u, bool full, f32x16& sc) __attribute__((always_inline)) -> float {
+    if (!full) {
+      const bool pooled = u < T1;
+      const int x0 = pooled ? u * KT : RB + (u - T1) * KT;
+      const int lo = pooled ? 0 : my_rb, hi = pooled ? my_np - 1 : my_pos;
 #pragma unroll
-    for (int g = 0; g < QG; ++g) {
-      if (!full) {
-        const int lo = pooled ? 0 : my_rb[g], hi = pooled ? my_np[g] - 1 : my_pos[g];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int x = x0 + 16 * kb + 4 * kq + j;
-            sc[kb][g][j] = (x >= lo && x <= hi) ? sc[kb][g][j] : kNegInf;
-          }
+      for (int e = 0; e < 16; ++e) {
+        const int x = x0 + 8 * (e >> 2) + 4 * h + (e & 3);
+        sc[e] = (x >= lo && x <= hi) ? sc[e] : kNegInf;
       }
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sc[kb][g][j]);
-      tmax[g] = mx * p.scale_log2;
     }
+    float mx = sc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+    return mx * p.scale_log2;
   };
   // lazy reference max: moves only when a score passes it by 2^8; the
   // accumulators (which hold every tile before this one) are rescaled then
-  auto rescale = [&](const float (&tmax)[QG]) __attribute__((always_inline)) {
+  auto rescale = [&](float tmax) __attribute__((always_inline)) {
+    if (__ballot(tmax > m_run + 8.f)) {
+      const float nm = fmaxf(m_run, xor32_max(tmax));  // the row's max over its two lanes
+      const float corr = nm == kNegInf ? 1.f : fast_exp2(m_run - nm);
+      l_run *= corr;
 #pragma unroll
-    for (int g = 0; g < QG; ++g) {
-      if (__ballot(tmax[g] > m_run[g] + 8.f)) {
-        const float nm = fmaxf(m_run[g], xor32_max(xor16_max(tmax[g])));  // the row's max
-        const float corr = nm == kNegInf ? 1.f : fast_exp2(m_run[g] - nm);
-        lsum[g] *= corr;
-#pragma unroll
-        for (int t = 0; t < DT; ++t) acc[g][t] *= corr;
-        m_run[g] = nm;
-      }
-      mu[g] = m_run[g] == kNegInf ? 0.f : m_run[g];
+      for (int db = 0; db < DB; ++db) acc[db] *= corr;
+      m_run = nm;
     }
+    mu = m_run == kNegInf ? 0.f : m_run;
   };
-  auto exps = [&](const f32x4 (&sc)[KB][QG], uint4 (&pb)[QG]) __attribute__((always_inline)) {
+  // P^T B operands (16 keys each): the score layout itself, rounded to bf16
+  auto exps = [&](const f32x16& sc, uint4 (&pb)[2]) __attribute__((always_inline)) {
+    float pj[16];
 #pragma unroll
-    for (int g = 0; g < QG; ++g) {
-      uint32_t w[KB][2];
+    for (int e = 0; e < 16; ++e) pj[e] = fast_exp2(fmaf(sc[e], p.scale_log2, -mu));
+    float ps = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        float pj[4];
+    for (int e = 0; e < 16; ++e) ps += pj[e];
+    l_run += ps;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pj[j] = fast_exp2(fmaf(sc[kb][g][j], p.scale_log2, -mu[g]));
-        w[kb][0] = pack_bf16x2(pj[0], pj[1]);
-        w[kb][1] = pack_bf16x2(pj[2], pj[3]);
-      }
-      pb[g] = make_uint4(w[0][0], w[0][1], w[1][0], w[1][1]);
-    }
+    for (int kh = 0; kh < 2; ++kh)
+      pb[kh] = make_uint4(pack_bf16x2(pj[8 * kh + 0], pj[8 * kh + 1]), pack_bf16x2(pj[8 * kh + 2], pj[8 * kh + 3]),
+                          pack_bf16x2(pj[8 * kh + 4], pj[8 * kh + 5]), pack_bf16x2(pj[8 * kh + 6], pj[8 * kh + 7]));
   };
-  auto pv = [&](const s16x4 (&va)[2 * DT], const uint4 (&pb)[QG]) __attribute__((always_inline)) {
+  auto pv = [&](const s16x4 (&va)[DB][2][2], const uint4 (&pb)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int g = 0; g < QG; ++g) lsum[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8, pb[g]), lsum[g], 0, 0, 0);
+    for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      const s16x4 a0 = va[2 * t], a1 = va[2 * t + 1];
-      const bf16x8 a = __builtin_bit_cast(bf16x8, s16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
-#pragma unroll
-      for (int g = 0; g < QG; ++g)
-        acc[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pb[g]), acc[g][t], 0, 0, 0);
-    }
+      for (int db = 0; db < DB; ++db) {
+        const s16x4 a0 = va[db][kh][0], a1 = va[db][kh][1];
+        const bf16x8 a = __builtin_bit_cast(bf16x8, s16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pb[kh]), acc[db], 0, 0, 0);
+      }
   };
 
-  // prologue: tiles 0 and 1 into LDS, tile 2 in flight; scores of tile 0
-  f32x4 s_a[KB][QG], s_b[KB][QG];
+  // prologue: tiles 0 and 1 into LDS, tiles 2 and 3 in flight; scores of tile 0
+  f32x16 s_a = f32x16{}, s_b = f32x16{};
   if (T > 0) {
     fetch(0, I0{});
     stash(I0{}, I0{});
@@ -695,17 +698,15 @@ __global__ __launch_bounds__(512, 1) void prefill128_kernel(PrefillParams p) {
     if (T > 3) fetch(3, I1{});
     __syncthreads();
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      uint4 ka[KS];
-      read_k(I0{}, kb, ka);
-      qk(ka, s_a[kb]);
+    for (int c0 = 0; c0 < DC; c0 += 4) {
+      uint4 ka[4];
+      read_k(I0{}, c0, ka);
+      qk(ka, c0, s_a);
     }
-    float tm[QG];
-    mask_max(0, is_full(0), s_a, tm);
-    rescale(tm);
+    rescale(mask_max(0, is_full(0), s_a));
   }
-  // step t (buffer of tile t: C): S(t) in s_cur (masked, mu set for it); S(t+1) into s_next
-  auto step = [&](int t, auto c, f32x4 (&s_cur)[KB][QG], f32x4 (&s_next)[KB][QG]) __attribute__((always_inline)) {
+  // step t (tile t in buffer C): S(t) in s_cur (masked, mu set for it); S(t+1) into s_next
+  auto step = [&](int t, auto c, f32x16& s_cur, f32x16& s_next) __attribute__((always_inline)) {
     constexpr int C = decltype(c)::value;
     using CN = std::integral_constant<int, (C + 1) % 4>;
     using CS = std::integral_constant<int, (C + 2) % 4>;
@@ -715,23 +716,19 @@ __global__ __launch_bounds__(512, 1) void prefill128_kernel(PrefillParams p) {
       stash(CS{}, SL{});  // waits for its rows (fetched two steps ago)
       if (t + 4 < T) fetch(t + 4, SL{});
     }
-    uint4 ka0[KS], ka1[KS];
+    uint4 ka0[4], ka1[4];
     read_k(CN{}, 0, ka0);
-    read_k(CN{}, 1, ka1);
-    uint4 pb[QG];
-    // block A: exponentials of tile t beside the Q.K MFMAs of tile t+1
-    exps(s_cur, pb);
-    qk(ka0, s_next[0]);
-    qk(ka1, s_next[1]);
-    s16x4 va[2 * DT];
+    read_k(CN{}, 4, ka1);
+    uint4 pb[2];
+    exps(s_cur, pb);  // the exponentials of tile t beside the Q.K MFMAs of tile t+1
+    s_next = f32x16{};
+    qk(ka0, 0, s_next);
+    qk(ka1, 4, s_next);
+    s16x4 va[DB][2][2];
     read_v(c, va);
-    // block B: P.V MFMAs of tile t, then the mask and max of tile t+1
-    pv(va, pb);
-    float tm[QG];
-    mask_max(t + 1, is_full(t + 1), s_next, tm);
-    rescale(tm);
+    pv(va, pb);       // P.V of tile t, then the mask and max of tile t+1
+    rescale(mask_max(t + 1, is_full(t + 1), s_next));
   };
-  using I3 = std::integral_constant<int, 3>;
   for (int t = 0;; t += 4) {  // every tile but the last: one step per buffer
     if (t + 1 >= T) break;
     step(t, I0{}, s_a, s_b);
@@ -744,50 +741,54 @@ __global__ __launch_bounds__(512, 1) void prefill128_kernel(PrefillParams p) {
   }
   if (T > 0) {  // the last tile: scores in s_a (even) or s_b (odd), buffer (T-1) % 4
     const int tl = T - 1;
-    if (tl & 1) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int g = 0; g < QG; ++g) s_a[kb][g] = s_b[kb][g];
-    }
+    if (tl & 1) s_a = s_b;
     __syncthreads();
-    uint4 pb[QG];
+    uint4 pb[2];
     exps(s_a, pb);
-    s16x4 va[2 * DT];
+    s16x4 va[DB][2][2];
     const bf16_t* vt = lds + (tl & 3) * (SHARED ? 1 : 2) * TILE + (SHARED ? 0 : TILE);
 #pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      const bf16_t* a = vt + (4 * kq + (n >> 2)) * D + 4 * (n & 1) + 8 * ((2 * t + ((n & 3) >> 1)) ^ swz_tr);
-      va[2 * t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a));
-      va[2 * t + 1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a + 16 * D));
-    }
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = 16 * kh + 8 * u + v_row;
+          const int col = 32 * db + v_col;
+          const bf16_t* a = vt + r * D + 8 * ((col >> 3) ^ swz<D>(r)) + (col & 7);
+          va[db][kh][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a));
+        }
     pv(va, pb);
   }
+
+  // finish: the row's sum over its two lanes, sink, normalisation, LSE; lane
+  // (n, h) writes dims 32 db + 8 j + 4 h .. +4 of its row
+  float l = xor32_sum(l_run);
+  if (!my_ok) return;
+  if (p.sink) l += fast_exp2(p.sink[(my_out / D) % p.hq] * kLog2e - m_run);
+  const float inv = 1.f / l;
+  if (p.out_bf16) {
+    bf16_t* o = static_cast<bf16_t*>(p.out) + my_out + 4 * h;
 #pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    float l = lsum[g][0];
-    if (!my_ok[g]) continue;
-    const int64_t h = (my_out[g] / D) % p.hq;
-    if (p.sink) l += fast_exp2(p.sink[h] * kLog2e - m_run[g]);
-    const float inv = 1.f / l;
-    if (p.out_bf16) {
-      bf16_t* o = static_cast<bf16_t*>(p.out) + my_out[g] + 4 * kq;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int tt = 0; tt < DT; ++tt) {
+      for (int j = 0; j < 4; ++j) {
         uint2 w;
-        w.x = pack_bf16x2(acc[g][tt][0] * inv, acc[g][tt][1] * inv);
-        w.y = pack_bf16x2(acc[g][tt][2] * inv, acc[g][tt][3] * inv);
-        *reinterpret_cast<uint2*>(o + 16 * tt) = w;
+        w.x = pack_bf16x2(acc[db][4 * j + 0] * inv, acc[db][4 * j + 1] * inv);
+        w.y = pack_bf16x2(acc[db][4 * j + 2] * inv, acc[db][4 * j + 3] * inv);
+        *reinterpret_cast<uint2*>(o + 32 * db + 8 * j) = w;
       }
-    } else {
-      float* o = static_cast<float*>(p.out) + my_out[g] + 4 * kq;
+  } else {
+    float* o = static_cast<float*>(p.out) + my_out + 4 * h;
 #pragma unroll
-      for (int tt = 0; tt < DT; ++tt)
-        *reinterpret_cast<float4*>(o + 16 * tt) =
-            make_float4(acc[g][tt][0] * inv, acc[g][tt][1] * inv, acc[g][tt][2] * inv, acc[g][tt][3] * inv);
-    }
-    if (p.lse && kq == 0) p.lse[my_out[g] / D] = (m_run[g] + log2f(l)) * 0.69314718055994531f;
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(o + 32 * db + 8 * j) =
+            make_float4(acc[db][4 * j + 0] * inv, acc[db][4 * j + 1] * inv, acc[db][4 * j + 2] * inv,
+                        acc[db][4 * j + 3] * inv);
   }
+  if (p.lse && h == 0) p.lse[my_out / D] = (m_run + log2f(l)) * 0.69314718055994531f;
 }
 
 hipError_t launch_prefill(const lbca_prefill_args& a, hipStream_t stream) {
