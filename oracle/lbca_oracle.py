@@ -573,3 +573,48 @@ def csa_sparse_prefill(qi, w, ki, q, entries, raw, raw_pos_base, q_pos0, m, W, k
                                    rope_base=rope_base)
             o[b, i], lse[b, i] = ob[0], lb[0]
     return idx, o, lse
+
+
+# ----------------------------------------------------------------------------
+# Projections around the path ([CSA] "What is implemented", second item: low-rank
+# indexer queries; third item and [HCA] "What is implemented": grouped output
+# projection).  The pages name both without formulas; the readings:
+#   * low-rank indexer queries: q^I_t = W^IUQ c^Q_t, where c^Q_t is the query's
+#     low-rank latent (d_c dims) and W^IUQ maps it to all indexer heads at once
+#     ([heads * head_dim, d_c]); the result is split into heads;
+#   * grouped output projection: the attention output of a token (all query
+#     heads concatenated) is cut into g groups of consecutive heads; group i is
+#     projected by its own matrix W_i to an intermediate width, the g results are
+#     concatenated and projected by W_O to the model width.
+# Weights are stored [out_features, in_features] (each output feature is a
+# dot product with one weight row).
+# ----------------------------------------------------------------------------
+def grouped_projection(x, w):
+    """Block-diagonal projection.  x [..., g * K]; w [g, N, K].  The input's last
+    axis is cut into g consecutive slices of K; slice i is multiplied by w[i]^T.
+    Returns [..., g * N] (group i in columns i*N .. (i+1)*N - 1)."""
+    x, w = _f64(x), _f64(w)
+    g, N, K = w.shape
+    if x.shape[-1] != g * K:
+        raise ValueError("input width must be groups x in_features")
+    xs = x.reshape(x.shape[:-1] + (g, K))
+    out = np.empty(x.shape[:-1] + (g, N))
+    for i in range(g):
+        out[..., i, :] = xs[..., i, :] @ w[i].T
+    return out.reshape(x.shape[:-1] + (g * N,))
+
+
+def indexer_queries(c_q, w_uq, heads):
+    """Low-rank indexer queries: c_q [..., d_c], w_uq [heads * d_I, d_c] ->
+    [..., heads, d_I]."""
+    q = _f64(c_q) @ _f64(w_uq).T
+    return q.reshape(q.shape[:-1] + (heads, q.shape[-1] // heads))
+
+
+def output_projection(o, w_groups, w_out):
+    """Grouped output projection of attention outputs o [..., H, c] (heads
+    consecutive): w_groups [g, d_g, (H/g) * c], w_out [d_model, g * d_g]."""
+    o = _f64(o)
+    flat = o.reshape(o.shape[:-2] + (o.shape[-2] * o.shape[-1],))
+    mid = grouped_projection(flat, w_groups)
+    return mid @ _f64(w_out).T
