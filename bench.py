@@ -585,6 +585,50 @@ def run_csa(reps):
 
 
 # ---------------------------------------------------------------------------
+# projections around the path, at the CSA sparse prefill chunk (batch 2 x 2048 tokens)
+# ---------------------------------------------------------------------------
+PJ_T, PJ_H, PJ_C, PJ_DC, PJ_HI, PJ_DI, PJ_G, PJ_DG, PJ_DM = 4096, 64, 512, 1024, 8, 64, 8, 1024, 4096
+
+
+def run_projections(reps):
+    """Low-rank indexer queries (d_c = 1024 -> 8 x 64) and the grouped output
+    projection (64 heads x 512 in 8 groups to 1024 each, then to 4096) of 4096
+    tokens, as three lbca_grouped_gemm launches captured in one graph."""
+    dev = "cuda"
+    sd = lambda n: synth.seed_of("bench-proj", n)
+    cq = synth.normal((PJ_T, PJ_DC), sd("cq"), dtype="bf16", device=dev)
+    wuq = synth.normal((PJ_HI * PJ_DI, PJ_DC), sd("wuq"), std=PJ_DC ** -0.5, dtype="bf16", device=dev)
+    o = synth.normal((PJ_T, PJ_H, PJ_C), sd("o"), device=dev)
+    wg = synth.normal((PJ_G, PJ_DG, PJ_H // PJ_G * PJ_C), sd("wg"), std=(PJ_H // PJ_G * PJ_C) ** -0.5,
+                      dtype="bf16", device=dev)
+    wo = synth.normal((PJ_DM, PJ_G * PJ_DG), sd("wo"), std=(PJ_G * PJ_DG) ** -0.5, dtype="bf16", device=dev)
+    qi = torch.empty((PJ_T, PJ_HI * PJ_DI), dtype=torch.bfloat16, device=dev)
+    mid = torch.empty((PJ_T, PJ_G * PJ_DG), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((PJ_T, PJ_DM), dtype=torch.float32, device=dev)
+    flat = o.reshape(PJ_T, -1)
+    parts = {
+        "indexer_queries": (lambda: lbca.grouped_gemm(cq, wuq, out=qi), 2 * PJ_T * PJ_DC * PJ_HI * PJ_DI),
+        "output_groups": (lambda: lbca.grouped_gemm(flat, wg, out=mid, groups=PJ_G),
+                          2 * PJ_T * PJ_H * PJ_C * PJ_DG),
+        "output_model": (lambda: lbca.grouped_gemm(mid, wo, out=y), 2 * PJ_T * PJ_G * PJ_DG * PJ_DM),
+    }
+    res = {"workload": f"{PJ_T} tokens: indexer queries {PJ_DC} -> {PJ_HI} x {PJ_DI}; output projection "
+                       f"{PJ_H} heads x {PJ_C} in {PJ_G} groups -> {PJ_G} x {PJ_DG} -> {PJ_DM} "
+                       f"(fp32 attention output rounded to bf16 on load)"}
+    tot_ms, tot_fl = 0.0, 0
+    for name, (fn, fl) in parts.items():
+        g = capture(fn)
+        ms = time_graph(g, reps)
+        res[name] = {"ms": ms, "tflops": fl / (ms * 1e-3) / 1e12, "flops": fl}
+        tot_ms += ms
+        tot_fl += fl
+    res["total_ms"] = tot_ms
+    res["tflops"] = tot_fl / (tot_ms * 1e-3) / 1e12
+    res["frac_of_bf16_peak"] = res["tflops"] / BF16_PEAK_TFLOPS
+    return res
+
+
+# ---------------------------------------------------------------------------
 # measured ceilings of this part (probe kernels in libceilings.so)
 # ---------------------------------------------------------------------------
 def run_ceilings():
@@ -635,6 +679,11 @@ def run_ceilings():
     mo = torch.empty(mg * 256, dtype=torch.float32, device="cuda")
     g = capture(lambda: ok(L.ceil_mfma(mo.data_ptr(), mg, iters, stream())))
     res["mfma_bf16_TFLOPs"] = mg * 4 * iters * 4 * 32768 / (time_graph(g, 5) * 1e-3) / 1e12
+    L.ceil_mfma16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    mg16 = 2048
+    mo16 = torch.empty(mg16 * 256, dtype=torch.float32, device="cuda")
+    g = capture(lambda: ok(L.ceil_mfma16(mo16.data_ptr(), mg16, iters, stream())))
+    res["mfma16_bf16_TFLOPs"] = mg16 * 4 * iters * 8 * 16384 / (time_graph(g, 5) * 1e-3) / 1e12
     g = capture(lambda: [ok(L.ceil_empty(stream())) for _ in range(LAYERS)])
     res["empty_launch_us"] = time_graph(g, 200) * 1e3 / LAYERS
     res["note"] = ("hbm_read: 2048 workgroups streaming 1 GiB; hbm_copy: the same workgroups copying 1 GiB "
@@ -642,6 +691,7 @@ def run_ceilings():
                    "from LDS, eight reads in flight; read_decode_bytes_one_launch: one launch reading "
                    f"{nb} B (the batch-16 decode's algorithmic bytes), 14 distinct buffers per graph replay; "
                    "mfma: 1024 workgroups x 4 waves x 4 chains of v_mfma_f32_32x32x16_bf16; "
+                   "mfma16: 2048 workgroups x 4 waves x 8 chains of v_mfma_f32_16x16x32_bf16; "
                    "empty_launch: 14 empty kernels per graph replay")
     return res
 
@@ -764,6 +814,7 @@ def main():
     ap.add_argument("--no-small-batch", action="store_true")
     ap.add_argument("--no-mqa", action="store_true", help="skip the HCA 1M and CSA 128K lines")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured-ceiling probes")
+    ap.add_argument("--no-proj", action="store_true", help="skip the projection GEMM line")
     ap.add_argument("--counters", action="store_true",
                     help="only run what the FETCH_SIZE / WRITE_SIZE counter passes profile")
     args = ap.parse_args()
@@ -845,6 +896,11 @@ def main():
                             "frac_of_bf16_peak": fl / (ms_attn * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                             "executed_tile_flops": fx, "executed_tflops": fx / (ms_attn * 1e-3) / 1e12}
 
+    if not args.no_proj:
+        log("[bench] projections around the path (grouped GEMM, 4096 tokens)")
+        extra["projections"] = run_projections(max(5, args.steps // 20))
+        torch.cuda.empty_cache()
+
     if not args.no_mqa:
         log("[bench] HCA decode 1M (batch 4)")
         extra["hca_1m"] = run_hca(max(5, args.steps // 4))
@@ -861,6 +917,8 @@ def main():
         ce["decode_GBps_vs_stream_read"] = achieved / ce["hbm_read_GBps"]
         if "prefill" in extra:
             ce["prefill_vs_mfma_loop"] = extra["prefill"]["tflops"] / ce["mfma_bf16_TFLOPs"]
+        if "projections" in extra:
+            ce["projections_vs_mfma_loop"] = extra["projections"]["tflops"] / ce["mfma_bf16_TFLOPs"]
         if "pool_backward_32k" in extra:
             ce["pool_backward_vs_copy"] = extra["pool_backward_32k"]["GBps"] / ce["hbm_copy_GBps"]
         extra["ceilings"] = ce

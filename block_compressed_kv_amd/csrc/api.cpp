@@ -448,6 +448,30 @@ int csa_sparse_prefill(const csa_prefill_args* a, void* workspace, size_t worksp
   return hip_status(lbca::launch_decode(pl.da, pl.dp, ws + pl.off_decode, s, (int)a->q_len));
 }
 
+int lbca_grouped_gemm(const lbca_gemm_args* a, void* stream) {
+  if (!a || !a->a || !a->w || !a->c) return LBCA_ERR_INVALID_ARG;
+  if (!is_dtype(a->a_dtype) || !is_dtype(a->c_dtype)) return LBCA_ERR_INVALID_ARG;
+  if (a->groups < 0 || a->m < 0 || a->n < 0 || a->k < 1) return LBCA_ERR_INVALID_ARG;
+  if (a->lda < a->k || a->ldw < a->k || a->ldc < a->n || a->a_group_stride < 0 || a->w_group_stride < 0 ||
+      a->c_group_stride < 0)
+    return LBCA_ERR_INVALID_ARG;
+  if (!aligned16(a->a) || !aligned16(a->w) || !aligned16(a->c)) return LBCA_ERR_INVALID_ARG;
+  if (!sane_product({a->groups, a->m, a->lda}) || !sane_product({a->groups, a->n, a->ldw}) ||
+      !sane_product({a->groups, a->m, a->ldc}) || a->a_group_stride > kMaxElems || a->w_group_stride > kMaxElems ||
+      a->c_group_stride > kMaxElems)
+    return LBCA_ERR_INVALID_ARG;
+  if (a->k % 8 || a->lda % 8 || a->ldw % 8 || a->a_group_stride % 8 || a->w_group_stride % 8)
+    return LBCA_ERR_UNSUPPORTED;
+  const int64_t ka = a->a_dtype == LBCA_F32 ? 4 : 2;
+  // 128-row bands are addressed with 32-bit byte offsets; the grid's y and z
+  // carry row tiles and groups
+  if ((127 * a->lda + a->k) * ka >= (int64_t(1) << 31) || (127 * a->ldw + a->k) * 2 >= (int64_t(1) << 31) ||
+      a->groups > 65535 || (a->m + 127) / 128 > 65535 || (a->n + 127) / 128 > INT32_MAX)
+    return LBCA_ERR_UNSUPPORTED;
+  if (a->groups == 0 || a->m == 0 || a->n == 0) return LBCA_OK;
+  return hip_status(lbca::launch_gemm(*a, static_cast<hipStream_t>(stream)));
+}
+
 int csa_index_topk(const csa_index_args* a, void* workspace, size_t workspace_bytes, void* stream) {
   int st = validate_index(a);
   if (st != LBCA_OK) return st;

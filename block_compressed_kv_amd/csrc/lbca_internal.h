@@ -37,6 +37,8 @@ hipError_t launch_prefill(const lbca_prefill_args& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const lbca_prefill_args& a, hipStream_t stream);
 hipError_t launch_decode_f32(const lbca_decode_args& a, hipStream_t stream);
 
+hipError_t launch_gemm(const lbca_gemm_args& a, hipStream_t stream);
+
 size_t index_workspace_bytes(const csa_index_args& a);
 hipError_t launch_index_topk(const csa_index_args& a, void* ws, hipStream_t stream);
 // Query chunk: a.batch = sequences * q_len rows (q_idx [rows, heads, dim],

@@ -91,6 +91,12 @@ class CsaPrefillArgs(ctypes.Structure):
                 ("rope_dims", _i32), ("rope_base", ctypes.c_float)]
 
 
+class GemmArgs(ctypes.Structure):
+    _fields_ = [("a", _vp), ("w", _vp), ("c", _vp), ("groups", _i64), ("m", _i64), ("n", _i64), ("k", _i64),
+                ("lda", _i64), ("ldw", _i64), ("ldc", _i64), ("a_group_stride", _i64), ("w_group_stride", _i64),
+                ("c_group_stride", _i64), ("a_dtype", _i32), ("c_dtype", _i32)]
+
+
 class LbcaError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
@@ -126,6 +132,7 @@ def lib():
         L.csa_index_topk.argtypes = [ctypes.POINTER(IndexArgs), _vp, ctypes.c_size_t, _vp]
         L.csa_sparse_prefill_workspace.argtypes = [ctypes.POINTER(CsaPrefillArgs), ctypes.POINTER(ctypes.c_size_t)]
         L.csa_sparse_prefill.argtypes = [ctypes.POINTER(CsaPrefillArgs), _vp, ctypes.c_size_t, _vp]
+        L.lbca_grouped_gemm.argtypes = [ctypes.POINTER(GemmArgs), _vp]
         for name in exported_names():
             getattr(L, name).restype = ctypes.c_int if name != "lbca_status_string" else ctypes.c_char_p
         if L.lbca_abi_version() != 1:
@@ -534,3 +541,45 @@ def csa_sparse_prefill(q_idx, head_w, idx_keys, q, entries, raw, q_pos0, raw_pos
     _check(lib().csa_sparse_prefill(ctypes.byref(a), _p(workspace), ws_bytes, _stream(stream)),
            "csa_sparse_prefill")
     return out, lse, out_idx
+
+
+# ---------------------------------------------------------------------------
+def grouped_gemm(a, w, out=None, out_dtype=None, groups=1, stream=None):
+    """lbca_grouped_gemm on dense tensors: a [M, groups * K] (or [M, K] with groups = 1),
+    w [groups, N, K] bf16 ([out, in] per group); returns out [M, groups * N] with group g's
+    projection in columns g*N .. (g+1)*N - 1 (fp32 accumulation)."""
+    if w.dim() == 2:
+        w = w.unsqueeze(0)
+    G, N, K = w.shape
+    if G != groups:
+        raise ValueError(f"w holds {G} groups, {groups} requested")
+    _need(a, "a", 2)
+    M = a.shape[0]
+    _expect(a, "a", (M, G * K))
+    _expect(w, "w", (G, N, K), (torch.bfloat16,), a.device)
+    if out is None:
+        out = torch.empty((M, G * N), dtype=out_dtype or torch.bfloat16, device=a.device)
+    _expect(out, "out", (M, G * N), device=a.device)
+    args = GemmArgs(_p(a), _p(w), _p(out), G, M, N, K, G * K, K, G * N, K, N * K, N, _dt(a), _dt(out))
+    _check(lib().lbca_grouped_gemm(ctypes.byref(args), _stream(stream)), "lbca_grouped_gemm")
+    return out
+
+
+def indexer_queries(c_q, w_uq, heads, out=None, stream=None):
+    """Low-rank indexer queries: c_q [..., d_c], w_uq [heads * d_I, d_c] bf16 ->
+    [..., heads, d_I] bf16 (one grouped_gemm call with one group)."""
+    lead = c_q.shape[:-1]
+    flat = c_q.reshape(-1, c_q.shape[-1])
+    res = grouped_gemm(flat, w_uq, out=out, stream=stream)
+    return res.reshape(*lead, heads, w_uq.shape[0] // heads)
+
+
+def output_projection(o, w_groups, w_out, mid=None, out=None, out_dtype=torch.float32, stream=None):
+    """Grouped output projection: o [T, H, c] (fp32 or bf16, heads consecutive),
+    w_groups [g, d_g, (H/g) * c] bf16, w_out [d_model, g * d_g] bf16 -> [T, d_model]
+    (two grouped_gemm calls: the g group maps, then the model-width map)."""
+    T = o.shape[0]
+    g = w_groups.shape[0]
+    flat = o.reshape(T, -1)
+    mid = grouped_gemm(flat, w_groups, out=mid, groups=g, stream=stream)
+    return grouped_gemm(mid, w_out, out=out, out_dtype=out_dtype, stream=stream)

@@ -488,6 +488,39 @@ LBCA_API int csa_sparse_prefill_workspace(const csa_prefill_args* a, size_t* byt
 LBCA_API int csa_sparse_prefill(const csa_prefill_args* a, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Grouped projection GEMM: the projections around the path (CSA "What is
+ * implemented" items 2 and 3: low-rank indexer queries and the grouped output
+ * projection; HCA "What is implemented": the grouped output projection).
+ *   C[g][i][j] = sum_l A[g][i][l] * W[g][j][l]     (fp32 accumulation)
+ * for g < groups, i < m, j < n, l < k.  Weights are stored [out, in]:
+ *   A  at a + g * a_group_stride + i * lda + l     a_dtype (F32 rounded to bf16, or BF16)
+ *   W  at w + g * w_group_stride + j * ldw + l     BF16
+ *   C  at c + g * c_group_stride + i * ldc + j     c_dtype (F32 or BF16), overwritten
+ * (strides in elements).  Low-rank indexer queries: groups = 1, A = the query
+ * latents [tokens, d_c], W = [heads * d_I, d_c], C = [tokens, heads * d_I].
+ * Grouped output projection, stage 1: groups = g, A = the attention output
+ * [tokens, H * c] with a_group_stride (H/g) * c and lda = H * c, W = [g, d_g,
+ * (H/g) * c], C = [tokens, g * d_g] with c_group_stride d_g; stage 2: groups =
+ * 1, A = that C, W = [d_model, g * d_g].
+ * Constraints: k a multiple of 8; lda, ldw >= k and multiples of 8; ldc >= n;
+ * A and W group strides multiples of 8; every 128-row band of A
+ * or W below 2 GiB; groups and ceil(m / 128) at most 65535.  C must not
+ * overlap A or W.  Errors: INVALID_ARG for NULL or misaligned pointers and bad
+ * sizes, UNSUPPORTED for dtypes, k or strides outside the constraints.
+ */
+typedef struct lbca_gemm_args {
+  const void* a;
+  const void* w;
+  void* c;
+  int64_t groups, m, n, k;
+  int64_t lda, ldw, ldc;
+  int64_t a_group_stride, w_group_stride, c_group_stride;
+  int32_t a_dtype, c_dtype;
+} lbca_gemm_args;
+
+LBCA_API int lbca_grouped_gemm(const lbca_gemm_args* a, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

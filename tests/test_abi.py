@@ -377,3 +377,28 @@ def test_csa_sparse_prefill_workspace_layout():
     assert _csap(ws_query=False)[0] == -3
     st, empty = _csap(q_len=0)
     assert st == 0
+
+
+def _gemm(**kw):
+    a = dict(a=FAKE, w=FAKE, c=FAKE, groups=2, m=300, n=200, k=512, lda=1024, ldw=512, ldc=400,
+             a_group_stride=512, w_group_stride=200 * 512, c_group_stride=200, a_dtype=1, c_dtype=0)
+    a.update(kw)
+    return lbca.lib().lbca_grouped_gemm(ctypes.byref(lbca.GemmArgs(**a)), None)
+
+
+@fake_ptr
+@pytest.mark.parametrize("kw,code", [
+    (dict(a=None), -1), (dict(w=None), -1), (dict(c=None), -1), (dict(c=FAKE + 8), -1),
+    (dict(a_dtype=5), -1), (dict(k=0), -1), (dict(m=-1), -1), (dict(lda=500), -1), (dict(ldc=199), -1),
+    (dict(ldw=511), -1),
+    (dict(k=500, lda=1000, ldw=500, a_group_stride=500, w_group_stride=100000), -2),   # k not a multiple of 8
+    (dict(a_group_stride=516), -2), (dict(w_group_stride=100004), -2), (dict(groups=70000), -2),
+    (dict(lda=1 << 24), -2),                                                            # 128-row band of 2 GiB
+])
+def test_gemm_validation(kw, code):
+    assert _gemm(**kw) == code
+
+
+@fake_ptr
+def test_gemm_empty_is_ok_without_gpu():
+    assert _gemm(groups=0) == 0 and _gemm(m=0) == 0 and _gemm(n=0) == 0
