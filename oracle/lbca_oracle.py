@@ -35,6 +35,11 @@ Readings where the pages are silent or garbled:
   * Indexer score: I_j = sum_h w_h * relu(q_h . k_j), no scale.
   * Top-k: ties go to the lower index; fewer than k visible -> all visible,
     padded with -1; indices returned in ascending order.
+  * Attention backward: the pages train the layer end to end ([mSeek]
+    "Experiment at a glance") without writing its gradients out; the oracle
+    differentiates the forward above exactly (softmax-attention backward with
+    per-query visibility and the sink), pinned by finite differences
+    (tests/test_oracle_attention_backward.py).
 """
 from __future__ import annotations
 
@@ -618,3 +623,63 @@ def output_projection(o, w_groups, w_out):
     flat = o.reshape(o.shape[:-2] + (o.shape[-2] * o.shape[-1],))
     mid = grouped_projection(flat, w_groups)
     return mid @ _f64(w_out).T
+
+
+# ----------------------------------------------------------------------------
+# Attention backward (training the compressed layer: [mSeek] "Experiment at a
+# glance", continued pretraining; the gradients of the attention over pooled
+# entries plus the window, per query with its own visibility).  Forward per
+# query t and query head h: logits l_j = scale * q . k_j over the visible rows
+# (pooled entries j < n_p(t), then the raw span), p = softmax(l) with exp(sigma_h)
+# added to the denominator when a sink is given, o = sum_j p_j v_j.  For an
+# upstream gradient g = dL/do:
+#   D = g . o,  dp_j = g . v_j,  ds_j = p_j (dp_j - D)
+#   dq = scale * sum_j ds_j k_j,  dk_j += scale * ds_j q,  dv_j += p_j g
+#   dsigma_h = -sum over queries of p_sink * D,  p_sink = exp(sigma_h - lse).
+# ----------------------------------------------------------------------------
+def attend_prefill_backward(q, q_pos0, pooled_k, pooled_v, raw_k, raw_v, raw_pos_base, m, W, mode, scale,
+                            grad_out, sink=None):
+    """Gradients of attend_prefill (separate K and V series).  Shapes as
+    attend_prefill; grad_out [B, Tq, Hq, d].  Returns dq [B, Tq, Hq, d],
+    dpooled_k, dpooled_v [B, Hkv, N, d], draw_k, draw_v [B, Hkv, R, d] and dsink
+    [Hq] (None without a sink)."""
+    q, gout = _f64(q), _f64(grad_out)
+    pk, pv, rk, rv = _f64(pooled_k), _f64(pooled_v), _f64(raw_k), _f64(raw_v)
+    B, Tq, Hq, d = q.shape
+    Hkv = pk.shape[1]
+    G = Hq // Hkv
+    sk = None if sink is None else _f64(sink)
+    dq = np.zeros_like(q)
+    dpk, dpv, drk, drv = np.zeros_like(pk), np.zeros_like(pv), np.zeros_like(rk), np.zeros_like(rv)
+    dsink = None if sk is None else np.zeros(Hq)
+    for i in range(Tq):
+        t = q_pos0 + i
+        n_p, rb = visible_range(t, m, W, mode)
+        rows = np.arange(rb, t + 1) - raw_pos_base
+        for b in range(B):
+            for kh in range(Hkv):
+                keys = np.concatenate([pk[b, kh, :n_p], rk[b, kh, rows]], axis=0)
+                vals = np.concatenate([pv[b, kh, :n_p], rv[b, kh, rows]], axis=0)
+                for g in range(G):
+                    h = kh * G + g
+                    lg = scale * (keys @ q[b, i, h])
+                    mx = lg.max()
+                    if sk is not None:
+                        mx = max(mx, sk[h])
+                    e = np.exp(lg - mx)
+                    den = e.sum() + (0.0 if sk is None else np.exp(sk[h] - mx))
+                    p = e / den
+                    o = p @ vals
+                    go = gout[b, i, h]
+                    D = go @ o
+                    ds = p * (vals @ go - D)
+                    dq[b, i, h] = scale * (ds @ keys)
+                    dk = scale * np.outer(ds, q[b, i, h])
+                    dv = np.outer(p, go)
+                    dpk[b, kh, :n_p] += dk[:n_p]
+                    dpv[b, kh, :n_p] += dv[:n_p]
+                    drk[b, kh, rows] += dk[n_p:]
+                    drv[b, kh, rows] += dv[n_p:]
+                    if sk is not None:
+                        dsink[h] -= np.exp(sk[h] - mx) / den * D
+    return dq, dpk, dpv, drk, drv, dsink
