@@ -402,6 +402,40 @@ def run_prefill(reps):
 
 
 # ---------------------------------------------------------------------------
+# attention backward over one 16K sequence (same layer shape, one call)
+# ---------------------------------------------------------------------------
+def run_attention_backward(reps):
+    """Gradients of attention over all 16384 queries of one sequence (pooled
+    entries 0..1015 plus the window; random bf16 inputs and upstream gradient):
+    the D / dq-zeroing pass and the key-major gradient kernel, timed as one graph."""
+    dev = "cuda"
+    N = lbca.visible_range(P_CTX - 1, P_M, W, EXCL)[0]
+    g = lambda n, shape: synth.normal(shape, synth.seed_of("bench-attn-grad-16k", n), dtype="bf16", device=dev)
+    q, do = g("q", (1, P_CTX, HQ, D)), g("do", (1, P_CTX, HQ, D))
+    pk, pv = g("pk", (1, HKV, N, D)), g("pv", (1, HKV, N, D))
+    rk, rv = g("rk", (1, HKV, P_CTX, D)), g("rv", (1, HKV, P_CTX, D))
+    o, lse = lbca.attend_prefill(q, 0, pk, rk, 0, P_M, W, EXCL, pooled_v=pv, raw_v=rv, out_dtype=torch.bfloat16)
+    f32 = dict(dtype=torch.float32, device=dev)
+    bufs = dict(grad_q=torch.empty((1, P_CTX, HQ, D), **f32), grad_pooled_k=torch.empty((1, HKV, N, D), **f32),
+                grad_pooled_v=torch.empty((1, HKV, N, D), **f32), grad_raw_k=torch.empty((1, HKV, P_CTX, D), **f32),
+                grad_raw_v=torch.empty((1, HKV, P_CTX, D), **f32))
+    ws = torch.empty(P_CTX * HQ * 4, dtype=torch.uint8, device=dev)
+
+    def step():
+        lbca.attend_prefill_backward(q, 0, pk, rk, 0, P_M, W, EXCL, o, lse, do, pooled_v=pv, raw_v=rv,
+                                     workspace=ws, **bufs)
+
+    gr = capture(step)
+    ms = time_graph(gr, reps)
+    fl = 5 * prefill_flops() // 2    # S, dP, dV, dK, dQ: 10 d flops per visible (row, key) pair
+    del q, do, pk, pv, rk, rv, o, lse, bufs, ws
+    return {"ms": ms, "tflops": fl / (ms * 1e-3) / 1e12, "algorithmic_flops": fl,
+            "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "workload": f"one sequence of {P_CTX} queries, 24 query / 8 KV heads, d=128, m={P_M}, W={W}, "
+                        f"{N} pooled entries; gradients of q, pooled and raw K and V (fp32)"}
+
+
+# ---------------------------------------------------------------------------
 # HCA decode at 1M context and CSA decode at 128K (MQA, 64 query heads, dim 512)
 # ---------------------------------------------------------------------------
 X_HQ, X_D, X_RD, X_EPS, X_BASE = 64, 512, 64, 1e-6, 10000.0
@@ -815,6 +849,7 @@ def main():
     ap.add_argument("--no-mqa", action="store_true", help="skip the HCA 1M and CSA 128K lines")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured-ceiling probes")
     ap.add_argument("--no-proj", action="store_true", help="skip the projection GEMM line")
+    ap.add_argument("--no-attn-grad", action="store_true", help="skip the attention-backward line")
     ap.add_argument("--counters", action="store_true",
                     help="only run what the FETCH_SIZE / WRITE_SIZE counter passes profile")
     args = ap.parse_args()
@@ -896,6 +931,11 @@ def main():
                             "frac_of_bf16_peak": fl / (ms_attn * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                             "executed_tile_flops": fx, "executed_tflops": fx / (ms_attn * 1e-3) / 1e12}
 
+    if not args.no_attn_grad:
+        log("[bench] attention backward 16K (one call)")
+        extra["attention_backward_16k"] = run_attention_backward(max(3, args.steps // 20))
+        torch.cuda.empty_cache()
+
     if not args.no_proj:
         log("[bench] projections around the path (grouped GEMM, 4096 tokens)")
         extra["projections"] = run_projections(max(5, args.steps // 20))
@@ -917,6 +957,9 @@ def main():
         ce["decode_GBps_vs_stream_read"] = achieved / ce["hbm_read_GBps"]
         if "prefill" in extra:
             ce["prefill_vs_mfma_loop"] = extra["prefill"]["tflops"] / ce["mfma_bf16_TFLOPs"]
+        if "attention_backward_16k" in extra:
+            ce["attention_backward_vs_mfma_loop"] = (extra["attention_backward_16k"]["tflops"]
+                                                     / ce["mfma_bf16_TFLOPs"])
         if "projections" in extra:
             ce["projections_vs_mfma_loop"] = extra["projections"]["tflops"] / ce["mfma_bf16_TFLOPs"]
         if "pool_backward_32k" in extra:

@@ -315,6 +315,70 @@ int lbca_attend_prefill(const lbca_prefill_args* a, void* stream) {
 }
 
 // ---------------------------------------------------------------------------
+static int validate_prefill_grad(const lbca_prefill_grad_args* a) {
+  if (!a || !a->q || !a->pooled_k || !a->raw_k || !a->out || !a->lse || !a->grad_out || !a->grad_q ||
+      !a->grad_pooled_k || !a->grad_raw_k)
+    return LBCA_ERR_INVALID_ARG;
+  const bool shared = a->pooled_v == nullptr;
+  if ((a->raw_v == nullptr) != shared || (a->grad_pooled_v == nullptr) != shared ||
+      (a->grad_raw_v == nullptr) != shared)
+    return LBCA_ERR_INVALID_ARG;
+  if (a->grad_sink && !a->sink) return LBCA_ERR_INVALID_ARG;
+  if (!is_dtype(a->dtype) || !is_dtype(a->out_dtype)) return LBCA_ERR_INVALID_ARG;
+  if (a->accumulate != 0 && a->accumulate != 1) return LBCA_ERR_INVALID_ARG;
+  if (a->batch < 0 || a->q_len < 0 || a->q_heads < 1 || a->kv_heads < 1 || a->q_heads % a->kv_heads != 0)
+    return LBCA_ERR_INVALID_ARG;
+  if (a->dim < 1 || a->entries < 0 || a->raw_rows < 1 || a->block < 1 || a->window < 1 || a->q_pos0 < 0 ||
+      a->raw_pos_base < 0)
+    return LBCA_ERR_INVALID_ARG;
+  if (a->mode != LBCA_EXCLUSIVE && a->mode != LBCA_OVERLAP) return LBCA_ERR_INVALID_ARG;
+  if (!isfinite(a->scale)) return LBCA_ERR_INVALID_ARG;
+  if (!sane_product({a->batch, a->q_len, a->q_heads, a->dim}) ||
+      !sane_product({a->batch, a->kv_heads, a->entries, a->dim}) ||
+      !sane_product({a->batch, a->kv_heads, a->raw_rows, a->dim}) || a->q_pos0 > kMaxElems ||
+      a->raw_pos_base > kMaxElems)
+    return LBCA_ERR_INVALID_ARG;
+  if (a->dtype != LBCA_BF16 || !(a->dim == 64 || a->dim == 128) || !(a->scale > 0.f)) return LBCA_ERR_UNSUPPORTED;
+  const int64_t lim = int64_t(1) << 31;
+  if (a->batch * a->q_len * a->q_heads >= lim || a->q_pos0 + a->q_len >= lim ||
+      a->raw_pos_base + a->raw_rows >= lim || a->batch * a->kv_heads > 65535)
+    return LBCA_ERR_UNSUPPORTED;
+  if (!aligned16(a->q) || !aligned16(a->pooled_k) || !aligned16(a->pooled_v) || !aligned16(a->raw_k) ||
+      !aligned16(a->raw_v) || !aligned16(a->out) || !aligned16(a->grad_out) || !aligned16(a->grad_q) ||
+      !aligned16(a->grad_pooled_k) || !aligned16(a->grad_pooled_v) || !aligned16(a->grad_raw_k) ||
+      !aligned16(a->grad_raw_v))
+    return LBCA_ERR_INVALID_ARG;
+  if (a->q_len > 0) {
+    int64_t np_last, rb_first, np0, rb_last;
+    lbca_visible_range(a->q_pos0 + a->q_len - 1, a->block, a->window, a->mode, &np_last, &rb_last);
+    lbca_visible_range(a->q_pos0, a->block, a->window, a->mode, &np0, &rb_first);
+    if (np_last > a->entries) return LBCA_ERR_INVALID_ARG;
+    if (rb_first - a->raw_pos_base < 0) return LBCA_ERR_INVALID_ARG;
+    if (a->q_pos0 + a->q_len - 1 - a->raw_pos_base >= a->raw_rows) return LBCA_ERR_INVALID_ARG;
+  }
+  return LBCA_OK;
+}
+
+int lbca_attend_prefill_backward_workspace(const lbca_prefill_grad_args* a, size_t* bytes) {
+  if (!bytes) return LBCA_ERR_INVALID_ARG;
+  const int st = validate_prefill_grad(a);
+  if (st != LBCA_OK) return st;
+  *bytes = lbca::prefill_grad_workspace_bytes(*a);
+  return LBCA_OK;
+}
+
+int lbca_attend_prefill_backward(const lbca_prefill_grad_args* a, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  const int st = validate_prefill_grad(a);
+  if (st != LBCA_OK) return st;
+  const size_t need = lbca::prefill_grad_workspace_bytes(*a);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return LBCA_ERR_WORKSPACE;
+  // q_len == 0 without accumulate still zeroes the key, value and sink gradients
+  if (a->batch == 0 || (a->q_len == 0 && a->accumulate)) return LBCA_OK;
+  return hip_status(lbca::launch_prefill_grad(*a, workspace, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
 static int validate_index(const csa_index_args* a) {
   if (!a || !a->q_idx || !a->head_w || !a->keys || !a->pos || !a->out_idx) return LBCA_ERR_INVALID_ARG;
   if (!is_dtype(a->dtype)) return LBCA_ERR_INVALID_ARG;

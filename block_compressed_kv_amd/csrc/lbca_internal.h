@@ -35,6 +35,8 @@ hipError_t static_scratch(void** ptr);
 
 hipError_t launch_prefill(const lbca_prefill_args& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const lbca_prefill_args& a, hipStream_t stream);
+size_t prefill_grad_workspace_bytes(const lbca_prefill_grad_args& a);
+hipError_t launch_prefill_grad(const lbca_prefill_grad_args& a, void* workspace, hipStream_t stream);
 hipError_t launch_decode_f32(const lbca_decode_args& a, hipStream_t stream);
 
 hipError_t launch_gemm(const lbca_gemm_args& a, hipStream_t stream);

@@ -74,6 +74,17 @@ class PrefillArgs(ctypes.Structure):
                 ("scale", _f32)]
 
 
+class PrefillGradArgs(ctypes.Structure):
+    _fields_ = [("q", _vp), ("pooled_k", _vp), ("pooled_v", _vp), ("raw_k", _vp), ("raw_v", _vp),
+                ("sink", _vp), ("out", _vp), ("lse", _vp), ("grad_out", _vp), ("grad_q", _vp),
+                ("grad_pooled_k", _vp), ("grad_pooled_v", _vp), ("grad_raw_k", _vp), ("grad_raw_v", _vp),
+                ("grad_sink", _vp),
+                ("batch", _i64), ("q_len", _i64), ("q_heads", _i64), ("kv_heads", _i64), ("dim", _i64),
+                ("entries", _i64), ("raw_rows", _i64), ("q_pos0", _i64), ("raw_pos_base", _i64),
+                ("block", _i64), ("window", _i64), ("mode", _i32), ("dtype", _i32), ("out_dtype", _i32),
+                ("accumulate", _i32), ("scale", _f32)]
+
+
 class IndexArgs(ctypes.Structure):
     _fields_ = [("q_idx", _vp), ("head_w", _vp), ("keys", _vp), ("pos", _vp), ("out_idx", _vp),
                 ("out_score", _vp),
@@ -128,6 +139,9 @@ def lib():
         L.lbca_attend_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp, ctypes.c_size_t, _vp]
         L.lbca_attend_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
         L.lbca_attend_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
+        L.lbca_attend_prefill_backward_workspace.argtypes = [ctypes.POINTER(PrefillGradArgs),
+                                                             ctypes.POINTER(ctypes.c_size_t)]
+        L.lbca_attend_prefill_backward.argtypes = [ctypes.POINTER(PrefillGradArgs), _vp, ctypes.c_size_t, _vp]
         L.csa_index_topk_workspace.argtypes = [ctypes.POINTER(IndexArgs), ctypes.POINTER(ctypes.c_size_t)]
         L.csa_index_topk.argtypes = [ctypes.POINTER(IndexArgs), _vp, ctypes.c_size_t, _vp]
         L.csa_sparse_prefill_workspace.argtypes = [ctypes.POINTER(CsaPrefillArgs), ctypes.POINTER(ctypes.c_size_t)]
@@ -152,8 +166,17 @@ def _check(status, where):
         raise LbcaError(status, where)
 
 
+_EMPTY = 256  # non-null, aligned address passed for a buffer with no elements (never dereferenced)
+
+
 def _p(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device pointer of t for the C ABI; None stays NULL (an absent optional buffer).
+    A tensor with no elements may have a null data pointer, which the ABI would read
+    as an absent buffer, so it is passed as a placeholder address: the library never
+    reads or writes a buffer of size 0."""
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr() if t.numel() > 0 else _EMPTY)
 
 
 def _dt(t):
@@ -432,6 +455,71 @@ def attend_prefill(q, q_pos0, pooled_k, raw_k, raw_pos_base, block, window, mode
                     raw_pos_base, block, window, mode, _dt(q), _dt(out), float(scale))
     _check(lib().lbca_attend_prefill(ctypes.byref(a), _stream(stream)), "lbca_attend_prefill")
     return out, lse
+
+
+def attend_prefill_backward(q, q_pos0, pooled_k, raw_k, raw_pos_base, block, window, mode, out, lse,
+                            grad_out, pooled_v=None, raw_v=None, sink=None, scale=None, grad_q=None,
+                            grad_pooled_k=None, grad_pooled_v=None, grad_raw_k=None, grad_raw_v=None,
+                            grad_sink=None, accumulate=False, workspace=None, stream=None):
+    """lbca_attend_prefill_backward: gradients of attend_prefill given its out and lse and
+    the upstream gradient grad_out [B,Tq,Hq,d].  Returns (grad_q, grad_pooled_k,
+    grad_pooled_v, grad_raw_k, grad_raw_v, grad_sink), all float32; with pooled_v/raw_v
+    None (one series as K and V) the value gradients are None and the key gradients
+    hold both roles; grad_sink is None without a sink.  accumulate=True adds the key,
+    value and sink gradients into the given buffers (chunked backward)."""
+    for t, n, nd in ((q, "q", 4), (pooled_k, "pooled_k", 4), (raw_k, "raw_k", 4)):
+        _need(t, n, nd)
+    B, Tq, Hq, d = q.shape
+    Hkv, N, R, dev, qt = pooled_k.shape[1], pooled_k.shape[2], raw_k.shape[2], q.device, (q.dtype,)
+    shared = pooled_v is None
+    f32 = torch.float32
+
+    def new(shape):
+        return torch.empty(shape, dtype=f32, device=dev)
+
+    if accumulate and (grad_pooled_k is None or grad_raw_k is None or (not shared and (
+            grad_pooled_v is None or grad_raw_v is None)) or (sink is not None and grad_sink is None)):
+        raise ValueError("accumulate=True needs the gradient buffers to add into")
+    grad_q = new((B, Tq, Hq, d)) if grad_q is None else grad_q
+    grad_pooled_k = new((B, Hkv, N, d)) if grad_pooled_k is None else grad_pooled_k
+    grad_raw_k = new((B, Hkv, R, d)) if grad_raw_k is None else grad_raw_k
+    if not shared:
+        grad_pooled_v = new((B, Hkv, N, d)) if grad_pooled_v is None else grad_pooled_v
+        grad_raw_v = new((B, Hkv, R, d)) if grad_raw_v is None else grad_raw_v
+    elif grad_pooled_v is not None or grad_raw_v is not None:
+        raise ValueError("one shared K/V series has no separate value gradients")
+    if sink is not None and grad_sink is None:
+        grad_sink = new((Hq,))
+    _expect(q, "q", (B, Tq, Hq, d))
+    _expect(grad_out, "grad_out", (B, Tq, Hq, d), qt, dev)
+    for t, n in ((pooled_k, "pooled_k"), (pooled_v, "pooled_v")):
+        _expect(t, n, (B, Hkv, N, d), qt, dev)
+    for t, n in ((raw_k, "raw_k"), (raw_v, "raw_v")):
+        _expect(t, n, (B, Hkv, R, d), qt, dev)
+    _expect(sink, "sink", (Hq,), (f32,), dev)
+    _expect(out, "out", (B, Tq, Hq, d), device=dev)
+    _expect(lse, "lse", (B, Tq, Hq), (f32,), dev)
+    _expect(grad_q, "grad_q", (B, Tq, Hq, d), (f32,), dev)
+    for t, n in ((grad_pooled_k, "grad_pooled_k"), (grad_pooled_v, "grad_pooled_v")):
+        _expect(t, n, (B, Hkv, N, d), (f32,), dev)
+    for t, n in ((grad_raw_k, "grad_raw_k"), (grad_raw_v, "grad_raw_v")):
+        _expect(t, n, (B, Hkv, R, d), (f32,), dev)
+    _expect(grad_sink, "grad_sink", (Hq,), (f32,), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    a = PrefillGradArgs(_p(q), _p(pooled_k), _p(pooled_v), _p(raw_k), _p(raw_v), _p(sink), _p(out), _p(lse),
+                        _p(grad_out), _p(grad_q), _p(grad_pooled_k), _p(grad_pooled_v), _p(grad_raw_k),
+                        _p(grad_raw_v), _p(grad_sink), B, Tq, Hq, Hkv, d, N, R, q_pos0, raw_pos_base, block,
+                        window, mode, _dt(q), _dt(out), int(bool(accumulate)), float(scale))
+    need = ctypes.c_size_t()
+    _check(lib().lbca_attend_prefill_backward_workspace(ctypes.byref(a), ctypes.byref(need)),
+           "lbca_attend_prefill_backward_workspace")
+    if workspace is None and need.value > 0:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().lbca_attend_prefill_backward(ctypes.byref(a), _p(workspace), ws_bytes, _stream(stream)),
+           "lbca_attend_prefill_backward")
+    return grad_q, grad_pooled_k, grad_pooled_v, grad_raw_k, grad_raw_v, grad_sink
 
 
 def _check_index(q_idx, head_w, keys, pos):

@@ -399,6 +399,66 @@ typedef struct lbca_prefill_args {
 LBCA_API int lbca_attend_prefill(const lbca_prefill_args* a, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Gradients of lbca_attend_prefill.  The forward is mSeek "How LBCA works"
+ * steps 4-5; the layer is trained end to end (mSeek "Experiment at a glance"),
+ * which needs these.  For each query row with forward output O and
+ * log-sum-exp lse (sink included), over the rows it sees (same visibility as
+ * the forward): P = exp(scale q.k - lse), D = dO . O, dS = P (dO . v - D), and
+ *   grad_q = scale sum_k dS k,  grad_k += scale dS q,  grad_v += P dO,
+ *   grad_sink[h] += -sum_rows exp(sink[h] - lse) D.
+ *
+ *   q, grad_out      [batch, q_len, q_heads, dim]          dtype
+ *   pooled_k/v       [batch, kv_heads, entries, dim]       dtype
+ *   raw_k/v          [batch, kv_heads, raw_rows, dim]      row r = position raw_pos_base + r
+ *                    (v NULL: one series is both K and V; its gradient, the
+ *                    sum of both roles, goes to grad_pooled_k / grad_raw_k and
+ *                    grad_pooled_v / grad_raw_v must be NULL)
+ *   out              [batch, q_len, q_heads, dim]          out_dtype (F32 or BF16): the forward's output
+ *   lse              [batch, q_len, q_heads] float32       the forward's lse
+ *   sink             [q_heads] float32 or NULL             the forward's sink
+ *   grad_q           [batch, q_len, q_heads, dim] float32  overwritten
+ *   grad_pooled_k/v  [batch, kv_heads, entries, dim] float32
+ *   grad_raw_k/v     [batch, kv_heads, raw_rows, dim] float32
+ *   grad_sink        [q_heads] float32 or NULL (needs sink)
+ * accumulate = 0: the key, value and sink gradients are overwritten (rows that
+ * no query of the call sees get 0); 1: added to them, so a chunked backward
+ * calls this once per chunk of queries.
+ * Supported: dtype BF16, dim 64 or 128, scale > 0, batch * q_len * q_heads
+ * and raw positions below 2^31, batch * kv_heads <= 65535.  The visibility
+ * checks of lbca_attend_prefill apply (INVALID_ARG).
+ * Workspace (lbca_attend_prefill_backward_workspace): 4 bytes per query row
+ * (batch * q_len * q_heads, rounded up to 16), 16-byte aligned, contents on
+ * entry do not matter; calls sharing one must not overlap.  grad_q, the
+ * pooled-entry gradients and grad_sink are summed with floating-point atomics,
+ * so their last bits can differ from run to run.
+ */
+typedef struct lbca_prefill_grad_args {
+  const void* q;
+  const void* pooled_k;
+  const void* pooled_v;
+  const void* raw_k;
+  const void* raw_v;
+  const float* sink;
+  const void* out;
+  const float* lse;
+  const void* grad_out;
+  float* grad_q;
+  float* grad_pooled_k;
+  float* grad_pooled_v;
+  float* grad_raw_k;
+  float* grad_raw_v;
+  float* grad_sink;
+  int64_t batch, q_len, q_heads, kv_heads, dim, entries, raw_rows;
+  int64_t q_pos0, raw_pos_base, block, window;
+  int32_t mode, dtype, out_dtype, accumulate;
+  float scale;
+} lbca_prefill_grad_args;
+
+LBCA_API int lbca_attend_prefill_backward_workspace(const lbca_prefill_grad_args* a, size_t* bytes);
+LBCA_API int lbca_attend_prefill_backward(const lbca_prefill_grad_args* a, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* CSA lightning indexer + top-k (CSA "What is implemented" item 2).
  * For sequence b at position t = pos[b], the visible compressed keys are
  * j < n_vis = min(floor((t+1)/block), entries) (OVERLAP rule).  Score

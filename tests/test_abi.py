@@ -285,6 +285,51 @@ def test_prefill_empty_is_ok_without_gpu():
     assert _prefill(batch=0) == 0
 
 
+def _prefill_grad(ws_query=False, **kw):
+    a = dict(q=FAKE, pooled_k=FAKE, pooled_v=FAKE, raw_k=FAKE, raw_v=FAKE, sink=None, out=FAKE, lse=FAKE,
+             grad_out=FAKE, grad_q=FAKE, grad_pooled_k=FAKE, grad_pooled_v=FAKE, grad_raw_k=FAKE,
+             grad_raw_v=FAKE, grad_sink=None, batch=1, q_len=2048, q_heads=24, kv_heads=8, dim=128,
+             entries=1016, raw_rows=16384, q_pos0=14336, raw_pos_base=0, block=16, window=128, mode=0,
+             dtype=1, out_dtype=0, accumulate=0, scale=0.08)
+    a.update(kw)
+    s = lbca.PrefillGradArgs(**a)
+    n = ctypes.c_size_t()
+    L = lbca.lib()
+    if ws_query:
+        return L.lbca_attend_prefill_backward_workspace(ctypes.byref(s), ctypes.byref(n)), n.value
+    return L.lbca_attend_prefill_backward(ctypes.byref(s), None, 0, None), 0
+
+
+@fake_ptr
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(out=None), -1), (dict(lse=None), -1), (dict(grad_out=None), -1),
+    (dict(grad_q=None), -1), (dict(grad_pooled_k=None), -1), (dict(grad_raw_k=None), -1),
+    (dict(pooled_v=None), -1),                # V shared on one series only
+    (dict(grad_raw_v=None), -1),              # separate V needs its gradient buffer
+    (dict(pooled_v=None, raw_v=None), -1),    # shared series takes no value-gradient buffers
+    (dict(grad_sink=FAKE), -1),               # a sink gradient needs the sink
+    (dict(accumulate=2), -1), (dict(q_heads=23), -1), (dict(mode=2), -1), (dict(out_dtype=5), -1),
+    (dict(entries=1015), -1), (dict(raw_rows=16383), -1), (dict(raw_pos_base=14300), -1),
+    (dict(grad_q=FAKE + 4), -1),              # fp32 buffers 16-byte aligned
+    (dict(dim=256), -2), (dict(dtype=0), -2), (dict(scale=0.0), -2),
+    (dict(batch=9000), -2),                   # batch * kv_heads above 65535
+])
+def test_prefill_backward_validation(kw, code):
+    assert _prefill_grad(ws_query=True, **kw)[0] == code
+    assert _prefill_grad(**kw)[0] == code
+
+
+@fake_ptr
+def test_prefill_backward_workspace_and_empty_calls():
+    st, n = _prefill_grad(ws_query=True)
+    assert st == 0 and n == 2048 * 24 * 4
+    assert _prefill_grad()[0] == -3                                  # no workspace given
+    assert _prefill_grad(batch=0)[0] == 0
+    assert _prefill_grad(q_len=0, accumulate=1)[0] == 0               # nothing to add
+    ok = _prefill_grad(pooled_v=None, raw_v=None, grad_pooled_v=None, grad_raw_v=None, ws_query=True)
+    assert ok[0] == 0
+
+
 def _index(ws=None, ws_bytes=0, **kw):
     a = dict(q_idx=FAKE, head_w=FAKE, keys=FAKE, pos=FAKE, out_idx=FAKE, out_score=None, batch=2,
              heads=8, dim=64, entries=32768, k=512, block=4, dtype=1)

@@ -10,6 +10,11 @@ seeded inputs copied exactly to the host.  Tolerances: tests/parity_util.py.
   * Chunked prefill at 16K in 2048-token chunks: every chunk pools its new
     blocks then attends; all pooled entries and 16 query positions (chunk
     edges, window edges, random) checked for all 24 heads.
+  * Attention backward at 16K, one call over all 16384 queries (the
+    Llama-shaped layer, 1016 pooled entries, random bf16 inputs and upstream
+    gradient): 12 query positions' dq, 6 raw positions' and 4 pooled entries'
+    dK/dV recomputed from exactly the queries that see them (the entries seen
+    by more than 1024 rows span two query runs).
   * HCA at 1M context, batch 4: 8192 treated entries pooled, decode with
     RMSNorm, partial RoPE and a sink; one sequence recomputed by the oracle,
     which streams its 2^20 tokens block range by block range.
@@ -95,6 +100,41 @@ def test_llama_chunked_prefill_16k(lib):
                                   1 / math.sqrt(d))
         check_bf16(host(out[:, t:t + 1]), ro, f"prefill out t={t}")
         check_bf16(host(lse[:, t:t + 1]), rl, f"prefill lse t={t}")
+
+
+def test_llama_attention_backward_16k(lib):
+    B, Hq, Hkv, d, m, W, T = 1, 24, 8, 128, 16, 128, 16384
+    EX = O.EXCLUSIVE
+    N = O.visible_range(T - 1, m, W, EX)[0]
+    say(f"full-size attention backward T={T} N={N}: generating")
+    g = lambda n, shape: synth.normal(shape, synth.seed_of("full-attn-grad-16k", n), dtype="bf16", device=DEV)
+    q, do = g("q", (B, T, Hq, d)), g("do", (B, T, Hq, d))
+    pk, pv, rk, rv = g("pk", (B, Hkv, N, d)), g("pv", (B, Hkv, N, d)), g("rk", (B, Hkv, T, d)), g("rv", (B, Hkv, T, d))
+    o, lse = lib.attend_prefill(q, 0, pk, rk, 0, m, W, EX, pooled_v=pv, raw_v=rv, out_dtype=torch.bfloat16)
+    dq, dpk, dpv, drk, drv, _ = lib.attend_prefill_backward(q, 0, pk, rk, 0, m, W, EX, o, lse, do,
+                                                           pooled_v=pv, raw_v=rv)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(d)
+    qh, doh = _cpu(q), _cpu(do)
+    keys = tuple(_cpu(t) for t in (pk, pv, rk, rv))
+
+    def oracle(t0, t1):
+        return O.attend_prefill_backward(qh[:, t0:t1], t0, *keys, 0, m, W, EX, scale, doh[:, t0:t1])
+
+    rng = np.random.default_rng(1601)
+    for t in sorted({0, 1, 127, 128, 143, 144, 8191, 16383, *rng.integers(0, T, 4).tolist()}):
+        check_bf16(host(dq[:, t:t + 1]), oracle(t, t + 1)[0], f"dq t={t}")
+    for p in (0, 100, 129, 8000, 16300, 16383):
+        t_last = min(T - 1, (p // m + 1) * m + W - 2)    # last query whose window holds p
+        r = oracle(p, t_last + 1)
+        check_bf16(host(drk[:, :, p]), r[3][:, :, p], f"raw dK p={p}")
+        check_bf16(host(drv[:, :, p]), r[4][:, :, p], f"raw dV p={p}")
+    for j in (990, 1000, 1014, 1015):
+        t_first = (j + 1) * m + W - 1                    # first query that sees entry j
+        say(f"pooled entry {j}: queries from {t_first}")
+        r = oracle(t_first, T)
+        check_bf16(host(dpk[:, :, j]), r[1][:, :, j], f"pooled dK j={j}")
+        check_bf16(host(dpv[:, :, j]), r[2][:, :, j], f"pooled dV j={j}")
 
 
 def test_hca_decode_1m_batch4(lib):
