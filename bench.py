@@ -419,7 +419,8 @@ def run_attention_backward(reps):
     bufs = dict(grad_q=torch.empty((1, P_CTX, HQ, D), **f32), grad_pooled_k=torch.empty((1, HKV, N, D), **f32),
                 grad_pooled_v=torch.empty((1, HKV, N, D), **f32), grad_raw_k=torch.empty((1, HKV, P_CTX, D), **f32),
                 grad_raw_v=torch.empty((1, HKV, P_CTX, D), **f32))
-    ws = torch.empty(P_CTX * HQ * 4, dtype=torch.uint8, device=dev)
+    ws = torch.empty(lbca.attend_prefill_backward_workspace_bytes(tuple(q.shape), 0, HKV, N, P_CTX, 0, P_M, W, EXCL),
+                     dtype=torch.uint8, device=dev)
 
     def step():
         lbca.attend_prefill_backward(q, 0, pk, rk, 0, P_M, W, EXCL, o, lse, do, pooled_v=pv, raw_v=rv,

@@ -341,7 +341,7 @@ static int validate_prefill_grad(const lbca_prefill_grad_args* a) {
   if (a->dtype != LBCA_BF16 || !(a->dim == 64 || a->dim == 128) || !(a->scale > 0.f)) return LBCA_ERR_UNSUPPORTED;
   const int64_t lim = int64_t(1) << 31;
   if (a->batch * a->q_len * a->q_heads >= lim || a->q_pos0 + a->q_len >= lim ||
-      a->raw_pos_base + a->raw_rows >= lim || a->batch * a->kv_heads > 65535)
+      a->raw_pos_base + a->raw_rows + a->block + a->window >= lim || a->batch * a->kv_heads > 65535)
     return LBCA_ERR_UNSUPPORTED;
   if (!aligned16(a->q) || !aligned16(a->pooled_k) || !aligned16(a->pooled_v) || !aligned16(a->raw_k) ||
       !aligned16(a->raw_v) || !aligned16(a->out) || !aligned16(a->grad_out) || !aligned16(a->grad_q) ||

@@ -13,21 +13,25 @@
 // consecutive keys of one series (pooled entries, or raw positions) of one
 // (sequence, KV head); wave w owns keys 32w..32w+31 and keeps their K and V
 // rows in registers as MFMA operands, with dK and dV accumulating in
-// registers.  It walks the query rows that can see its keys (the flattened
-// (position, GQA head) rows of that KV head: every row from the first that
-// sees its first key for pooled entries, split across workgroups in runs of
-// 1024 rows; the window band for raw positions) in tiles of 32 rows staged
-// through LDS (next tile prefetched into registers while the current one
-// computes).  Per tile and wave, on v_mfma_f32_32x32x16_bf16:
-//   S = Q K^T and dP = dO V^T       (rows x the wave's keys, contraction dims)
-//   dV^T += dO^T P, dK^T += Q^T dS  (contraction over the 32 rows; P and dS
-//                                    feed straight from the accumulator layout,
-//                                    dO^T and Q^T come from transposing LDS reads)
+// registers.  Each lane works out once which query positions see its key (an
+// interval: from the first position whose pooled prefix holds the entry on,
+// or the positions whose window holds the raw position), so a score's mask is
+// two integer compares.  The workgroup walks the positions that can see any of
+// its keys (for pooled entries split across workgroups in runs of 512
+// positions) in tiles of 32 positions of one query head, the heads of the GQA
+// group innermost, staged through LDS with the next tile prefetched into
+// registers.  Per tile and wave, on v_mfma_f32_32x32x16_bf16:
+//   S = Q K^T and dP = dO V^T       (positions x the wave's keys, over dims)
+//   dV^T += dO^T P, dK^T += Q^T dS  (over the 32 positions; P and dS feed
+//                                    straight from the accumulator layout, dO^T
+//                                    and Q^T come from transposing LDS reads)
 //   dQ  = dS K                      (dS goes through LDS transposed; each wave
 //                                    covers 32 dims, then adds its partial to
 //                                    the fp32 dQ with atomics)
-// Pooled-entry gradients are added with atomics (several query runs touch one
-// entry); raw-position gradients have one owner and are stored.
+// Raw-position gradients have one owner and are stored; a pooled entry's
+// gradient is the sum over the runs that touch it, so each run stores its
+// partial in the workspace and a reduction kernel adds them up (many runs
+// adding into the same entries with atomics at the same time serialise).
 #include "device_util.h"
 #include "lbca_internal.h"
 
@@ -36,8 +40,8 @@ namespace lbca {
 namespace {
 
 constexpr int GK = 128;      // keys per workgroup
-constexpr int GQ = 32;       // query rows per tile
-constexpr int QSPLIT = 1024; // query rows per workgroup on the pooled series
+constexpr int GQ = 32;       // query positions per tile
+constexpr int PSPLIT = 512;  // query positions per workgroup on the pooled series
 
 struct GradParams {
   const bf16_t* q;
@@ -49,11 +53,11 @@ struct GradParams {
   const bf16_t* rk;
   const bf16_t* rv;
   float* dq;
-  float* dpk;
-  float* dpv;
+  float* part;  // pooled-entry partials: [batch * kv_heads][pool tile][split][128 keys][K, V][dim]
   float* drk;
   float* drv;
-  int64_t q_len, hq, hkv, G, entries, raw_rows, q_pos0, raw_pos_base, m, W;
+  int64_t entries, raw_rows;
+  int q_len, hq, hkv, G, q_pos0, raw_pos_base, m, W;
   int mode, accumulate, shared;
   int n_pool, pool_tiles, pool_splits, raw_tiles;
   float scale, scale_log2;
@@ -66,10 +70,6 @@ template <int D>
 __device__ __forceinline__ int qswz(int r) {
   if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
   else return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1);
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
 }
 
 // 8 bf16 of one column from two transposing LDS reads (rows r..r+3 at a, then
@@ -87,166 +87,143 @@ __device__ __forceinline__ bf16x8 pack8(const float* f) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_grad_kernel(GradParams p) {
+__global__ __launch_bounds__(512, 1) void attn_grad_kernel(GradParams p) {
   constexpr int DS = D / 16;                  // 16-dim slices of the S / dP contraction
   constexpr int DB = D / 32;                  // 32-dim blocks of dV^T / dK^T
+  constexpr int DBH = DB / 2;                 // blocks of one wave's half of the dims
   constexpr int CH = D / 8;                   // 16-byte chunks per row
-  constexpr int NCH = GQ * CH / 256;          // chunks per thread per tile and tensor
-  static_assert(NCH == 1 || NCH == 2, "staging holds one or two chunks per tensor");
-  constexpr int KSL = D == 128 ? 8 : 4;       // 16-key slices of the wave's dQ contraction
+  constexpr int KSL = D == 128 ? 8 : 4;       // 16-key slices of a wave's dQ contraction
+  constexpr int TCH = GQ * CH;                // chunks of one tile of one tensor
+  static_assert(2 * TCH == 512 || TCH == 512, "staging: one chunk per thread and tensor, or one in all");
+  __shared__ __attribute__((aligned(16))) bf16_t sk[GK * D];     // the workgroup's K rows
+  __shared__ __attribute__((aligned(16))) bf16_t sv[GK * D];     // and V rows
   __shared__ __attribute__((aligned(16))) bf16_t sq[2][GQ * D];
   __shared__ __attribute__((aligned(16))) bf16_t sdo[2][GQ * D];
   __shared__ __attribute__((aligned(16))) bf16_t sdst[GK * GQ];  // dS^T: row = key, 32 query columns
   __shared__ __attribute__((aligned(16))) float s_l2[2][GQ];
   __shared__ __attribute__((aligned(16))) float s_dv[2][GQ];
-  __shared__ __attribute__((aligned(16))) int s_a[2][GQ];       // pooled: n_pooled(t); raw: raw_begin(t)
-  __shared__ __attribute__((aligned(16))) int s_b[2][GQ];       // raw: t
-  __shared__ __attribute__((aligned(16))) int s_row[2][GQ];     // flat query-row index, -1 if not this tile's
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave & 3, dh = wave >> 2;  // this wave's 32 keys and half of the dims
   const int n = lane & 31, h = lane >> 5, j16 = lane & 15, g4 = lane >> 4;
   const int bh = blockIdx.y;
-  const int b = bh / (int)p.hkv, kvh = bh % (int)p.hkv;
-  const int G = (int)p.G;
-  const int rows_total = (int)p.q_len * G;
+  const int b = bh / p.hkv, kvh = bh % p.hkv;
+  const int G = p.G;
+  const int q_end = p.q_pos0 + p.q_len;  // one past the last query position
   const int wi = blockIdx.x;
   const bool pooled = wi < p.pool_tiles * p.pool_splits;
 
-  int k0, nkeys, row_begin, row_end;
+  // keys [k0, k0 + nkeys) of one series; query positions [t_begin, t_end)
+  int k0, nkeys, t_begin, t_end;
   if (pooled) {
     const int tile = wi / p.pool_splits, split = wi % p.pool_splits;
     k0 = tile * GK;
     nkeys = min(GK, p.n_pool - k0);
     // first position whose pooled prefix includes entry k0
-    const int64_t t_first = p.mode == LBCA_EXCLUSIVE ? (int64_t)(k0 + 1) * p.m + p.W - 1 : (int64_t)(k0 + 1) * p.m - 1;
-    const int64_t i_first = t_first - p.q_pos0 > 0 ? t_first - p.q_pos0 : 0;
-    row_begin = (int)(i_first * G) + split * QSPLIT;
-    row_end = min(row_begin + QSPLIT, rows_total);
-    if (row_begin >= rows_total) return;  // nothing in this run: the entries' gradients were set beforehand
+    const int t_first = p.mode == LBCA_EXCLUSIVE ? (k0 + 1) * p.m + p.W - 1 : (k0 + 1) * p.m - 1;
+    t_begin = max(t_first, p.q_pos0) + split * PSPLIT;
+    t_end = min(t_begin + PSPLIT, q_end);
+    if (t_begin >= q_end) return;  // nothing in this run: the entries' gradients were set beforehand
   } else {
     k0 = (wi - p.pool_tiles * p.pool_splits) * GK;
     nkeys = (int)min((int64_t)GK, p.raw_rows - k0);
-    // queries t seeing some position in [p0, p1]: t >= p0 and raw_begin(t) <= p1
-    const int64_t p0 = p.raw_pos_base + k0, p1 = p0 + nkeys - 1;
-    const int64_t t_last = p.mode == LBCA_EXCLUSIVE ? (p1 / p.m + 1) * p.m + p.W - 2 : p1 + p.W - 1;
-    const int64_t lo = p0 > p.q_pos0 ? p0 : p.q_pos0;
-    const int64_t hi = t_last < p.q_pos0 + p.q_len - 1 ? t_last : p.q_pos0 + p.q_len - 1;
-    row_begin = (int)((lo - p.q_pos0) * G);
-    row_end = hi >= lo ? (int)((hi - p.q_pos0 + 1) * G) : row_begin;
+    // queries seeing some position in [p0, p1]: t >= p0 and raw_begin(t) <= p1
+    const int p0 = p.raw_pos_base + k0, p1 = p0 + nkeys - 1;
+    const int t_last = p.mode == LBCA_EXCLUSIVE ? (p1 / p.m + 1) * p.m + p.W - 2 : p1 + p.W - 1;
+    t_begin = max(p0, p.q_pos0);
+    t_end = max(t_begin, min(t_last + 1, q_end));
   }
 
   const int64_t key_base = pooled ? (int64_t)bh * p.entries + k0 : (int64_t)bh * p.raw_rows + k0;
   const bf16_t* kser = pooled ? p.pk : p.rk;
   const bf16_t* vser = pooled ? (p.shared ? p.pk : p.pv) : (p.shared ? p.rk : p.rv);
 
-  // this wave's K and V rows as B operands (N = key, K = dims 16 s + 8 h ..)
-  const int key_rel = 32 * wave + n;
+  // the workgroup's K and V rows into LDS (rows past the series read as
+  // zeros), chunk c of row r at position c ^ qswz(r)
+  for (int idx = tid; idx < GK * CH; idx += 512) {
+    const int r = idx / CH, c = idx % CH;
+    const bool ok = r < nkeys;
+    const uint4 vk = ok ? *reinterpret_cast<const uint4*>(kser + (key_base + r) * D + 8 * c) : make_uint4(0, 0, 0, 0);
+    const uint4 vv = ok ? *reinterpret_cast<const uint4*>(vser + (key_base + r) * D + 8 * c) : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&sk[r * D + 8 * (c ^ qswz<D>(r))]) = vk;
+    *reinterpret_cast<uint4*>(&sv[r * D + 8 * (c ^ qswz<D>(r))]) = vv;
+  }
+  const int key_rel = 32 * kw + n;
   const bool key_ok = key_rel < nkeys;
-  uint4 kb[DS], vb[DS];
-  {
-    const bf16_t* kr = kser + (key_base + (key_ok ? key_rel : 0)) * D + 8 * h;
-    const bf16_t* vr = vser + (key_base + (key_ok ? key_rel : 0)) * D + 8 * h;
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      kb[s] = key_ok ? *reinterpret_cast<const uint4*>(kr + 16 * s) : make_uint4(0, 0, 0, 0);
-      vb[s] = key_ok ? *reinterpret_cast<const uint4*>(vr + 16 * s) : make_uint4(0, 0, 0, 0);
-    }
+  // the query positions that see this lane's key: [vis_lo, vis_hi]
+  int vis_lo, vis_hi;
+  if (!key_ok) {
+    vis_lo = 0x7fffffff;
+    vis_hi = -1;
+  } else if (pooled) {
+    const int j = k0 + key_rel;
+    vis_lo = p.mode == LBCA_EXCLUSIVE ? (j + 1) * p.m + p.W - 1 : (j + 1) * p.m - 1;
+    vis_hi = 0x7fffffff;
+  } else {
+    const int pos = p.raw_pos_base + k0 + key_rel;
+    vis_lo = pos;
+    vis_hi = p.mode == LBCA_EXCLUSIVE ? (pos / p.m + 1) * p.m + p.W - 2 : pos + p.W - 1;
   }
-  // K as the B operand of dQ (N = dim, K = keys): this wave's 32 dims over its
-  // key range (all 128 keys at 128 dims; at 64 dims the waves split dims x key halves)
-  const int dq_db = D == 128 ? wave : (wave & 1);
-  const int dq_kb = D == 128 ? 0 : 64 * (wave >> 1);
-  bf16x8 kt[KSL];
-#pragma unroll
-  for (int s = 0; s < KSL; ++s) {
-    uint16_t e[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int kk = dq_kb + 16 * s + 8 * h + j;
-      e[j] = kk < nkeys ? reinterpret_cast<const uint16_t*>(kser)[(key_base + kk) * D + 32 * dq_db + n] : (uint16_t)0;
-    }
-    const uint4 u = make_uint4(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
-                               e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16));
-    kt[s] = __builtin_bit_cast(bf16x8, u);
-  }
+  // dQ is the first half's job: wave kw covers 32 dims (all 128 keys at 128
+  // dims; at 64 dims the four waves split dims x key halves)
+  const bool do_dq = dh == 0;
+  const int dq_db = D == 128 ? kw : (kw & 1);
+  const int dq_kb = D == 128 ? 0 : 64 * (kw >> 1);
 
-  f32x16 dva[DB], dka[DB];
+  f32x16 dva[DBH], dka[DBH];
 #pragma unroll
-  for (int i = 0; i < DB; ++i) dva[i] = dka[i] = f32x16{};
+  for (int i = 0; i < DBH; ++i) dva[i] = dka[i] = f32x16{};
 
-  // staging of one query tile (held in named registers: NCH chunks of Q and of
-  // dO per thread, plus one row's bookkeeping for threads 0..31)
-  uint4 stq0 = make_uint4(0, 0, 0, 0), stq1 = stq0, sto0 = stq0, sto1 = stq0;
-  float st_l2 = 0.f, st_dv = 0.f;
-  int st_a = 0, st_b = 0, st_row = -1;
-  auto fetch = [&](int rt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int idx = tid + 256 * c, row = idx / CH, ch = idx % CH;
-      const int gr = rt + row;
-      uint4 vq = make_uint4(0, 0, 0, 0), vo = vq;
-      if (gr < row_end) {
-        const int i = gr / G, hg = gr - i * G;
-        const int64_t off = (((int64_t)b * p.q_len + i) * p.hq + (int64_t)kvh * G + hg) * D + 8 * ch;
-        vq = *reinterpret_cast<const uint4*>(p.q + off);
-        vo = *reinterpret_cast<const uint4*>(p.dout + off);
-      }
-      if (c == 0) { stq0 = vq; sto0 = vo; }
-      else { stq1 = vq; sto1 = vo; }
-    }
+  // tiles: 32 positions (from t_begin) x each query head of the group, heads inner
+  const int n_tiles = ((t_end - t_begin + GQ - 1) / GQ) * G;
+  const int qh0 = kvh * G;
+
+  // staging of one tile: one 16-byte chunk of Q and of dO per thread at 128
+  // dims (Q by threads 0..255 and dO by 256..511 at 64 dims); threads 0..31
+  // also one row's lse and D
+  constexpr bool BOTH = TCH == 512;
+  const int st_idx = BOTH ? tid : (tid & (TCH - 1));
+  const int st_row = st_idx / CH, st_ch = st_idx % CH;
+  const int st_pos = st_row * D + 8 * (st_ch ^ qswz<D>(st_row));
+  uint4 stq, sto;
+  float st_l2, st_dv;
+  auto fetch = [&](int it) __attribute__((always_inline)) {
+    const int tp = t_begin + GQ * (it / G), hq = qh0 + it % G;
+    const int t = min(tp + st_row, t_end - 1);  // rows past the run repeat its last row (masked)
+    const int64_t off = (((int64_t)b * p.q_len + (t - p.q_pos0)) * p.hq + hq) * D + 8 * st_ch;
+    if (BOTH || tid < TCH) stq = *reinterpret_cast<const uint4*>(p.q + off);
+    if (BOTH || tid >= TCH) sto = *reinterpret_cast<const uint4*>(p.dout + off);
+    const int tr = min(tp + (tid & 31), t_end - 1);
+    const int64_t rid = ((int64_t)b * p.q_len + (tr - p.q_pos0)) * p.hq + hq;
     if (tid < GQ) {
-      const int gr = rt + tid;
-      if (gr < row_end) {
-        const int i = gr / G, hg = gr - i * G;
-        const int64_t rid = ((int64_t)b * p.q_len + i) * p.hq + (int64_t)kvh * G + hg;
-        st_row = (int)rid;
-        st_l2 = p.lse[rid] * kLog2e;
-        st_dv = p.dvec[rid];
-        int64_t np, rb;
-        visible_range(p.q_pos0 + i, p.m, p.W, p.mode, &np, &rb);
-        st_a = pooled ? (int)np : (int)rb;
-        st_b = (int)(p.q_pos0 + i);
-      } else {
-        st_row = -1;
-        st_l2 = __builtin_inff();
-        st_dv = 0.f;
-        st_a = pooled ? 0 : 0x7fffffff;
-        st_b = -1;
-      }
+      st_l2 = p.lse[rid];
+      st_dv = p.dvec[rid];
     }
   };
-  auto stash = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int idx = tid + 256 * c, row = idx / CH, ch = idx % CH;
-      const int pos = row * D + 8 * (ch ^ qswz<D>(row));
-      *reinterpret_cast<uint4*>(&sq[buf][pos]) = c == 0 ? stq0 : stq1;
-      *reinterpret_cast<uint4*>(&sdo[buf][pos]) = c == 0 ? sto0 : sto1;
-    }
+  auto stash = [&](int it, int buf) __attribute__((always_inline)) {
+    if (BOTH || tid < TCH) *reinterpret_cast<uint4*>(&sq[buf][st_pos]) = stq;
+    if (BOTH || tid >= TCH) *reinterpret_cast<uint4*>(&sdo[buf][st_pos]) = sto;
     if (tid < GQ) {
-      s_l2[buf][tid] = st_l2;
-      s_dv[buf][tid] = st_dv;
-      s_a[buf][tid] = st_a;
-      s_b[buf][tid] = st_b;
-      s_row[buf][tid] = st_row;
+      const int tp = t_begin + GQ * (it / G);
+      const bool ok = tp + tid < t_end;
+      s_l2[buf][tid] = ok ? st_l2 * kLog2e : __builtin_inff();
+      s_dv[buf][tid] = ok ? st_dv : 0.f;
     }
   };
 
-  // this lane's key as a pooled entry id or a raw position
-  const int my_key = pooled ? k0 + key_rel : (int)(p.raw_pos_base + k0 + key_rel);
-
-  if (row_begin < row_end) {
-    fetch(row_begin);
-    stash(0);
+  if (n_tiles > 0) {
+    fetch(0);
+    stash(0, 0);
   }
   __syncthreads();
-  int buf = 0;
-  for (int rt = row_begin; rt < row_end; rt += GQ) {
-    const bool more = rt + GQ < row_end;
-    if (more) fetch(rt + GQ);
+  for (int it = 0; it < n_tiles; ++it) {
+    const int buf = it & 1;
+    const bool more = it + 1 < n_tiles;
+    if (more) fetch(it + 1);
     const bf16_t* tq = sq[buf];
     const bf16_t* tdo = sdo[buf];
+    const int tp = t_begin + GQ * (it / G), hq = qh0 + it % G;
 
     // S = Q K^T, dP = dO V^T: lane (key n, h) gets rows 8 (e / 4) + 4 h + e % 4
     f32x16 sacc = {}, dpacc = {};
@@ -255,106 +232,121 @@ __global__ __launch_bounds__(256, 1) void attn_grad_kernel(GradParams p) {
       const int pos = n * D + 8 * ((2 * s + h) ^ qswz<D>(n));
       const bf16x8 aq = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&tq[pos]));
       const bf16x8 ao = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&tdo[pos]));
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, __builtin_bit_cast(bf16x8, kb[s]), sacc, 0, 0, 0);
-      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, __builtin_bit_cast(bf16x8, vb[s]), dpacc, 0, 0, 0);
+      const int kpos = key_rel * D + 8 * ((2 * s + h) ^ qswz<D>(key_rel));
+      const bf16x8 bk = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sk[kpos]));
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sv[kpos]));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, sacc, 0, 0, 0);
+      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bv, dpacc, 0, 0, 0);
     }
 
-    // probabilities and scaled dS, masked by each row's visibility
-    float pe[16], dse[16];
+    // probabilities and scaled dS; row r sees this lane's key iff its position is
+    // in [vis_lo, vis_hi] (rows past the run have lse +inf, so P = 0)
+    // (computed in place: sacc becomes P, dpacc becomes dS)
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const int r0 = 8 * qq + 4 * h;
       const float4 l2 = *reinterpret_cast<const float4*>(&s_l2[buf][r0]);
       const float4 dv = *reinterpret_cast<const float4*>(&s_dv[buf][r0]);
-      const int4 va = *reinterpret_cast<const int4*>(&s_a[buf][r0]);
-      const int4 vbv = *reinterpret_cast<const int4*>(&s_b[buf][r0]);
       const float l2a[4] = {l2.x, l2.y, l2.z, l2.w}, dva4[4] = {dv.x, dv.y, dv.z, dv.w};
-      const int aa[4] = {va.x, va.y, va.z, va.w}, bb[4] = {vbv.x, vbv.y, vbv.z, vbv.w};
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int e = 4 * qq + rr;
-        const bool vis = key_ok && (pooled ? my_key < aa[rr] : (aa[rr] <= my_key && my_key <= bb[rr]));
-        const float pr = vis ? fast_exp2(sacc[e] * p.scale_log2 - l2a[rr]) : 0.f;
-        pe[e] = pr;
-        dse[e] = pr * (dpacc[e] - dva4[rr]) * p.scale;
+        const int e = 4 * qq + rr, t = tp + r0 + rr;
+        const bool vis = t >= vis_lo && t <= vis_hi;
+        const float x = vis ? sacc[e] * p.scale_log2 - l2a[rr] : kNegInf;
+        const float pr = fast_exp2(x);
+        sacc[e] = pr;
+        dpacc[e] = pr * (dpacc[e] - dva4[rr]) * p.scale;
       }
     }
-    const bf16x8 pb0 = pack8(pe), pb1 = pack8(pe + 8);
-    const bf16x8 db0 = pack8(dse), db1 = pack8(dse + 8);
-
-    // dS^T into LDS: row key_rel, query columns 8 qq + 4 h .. +3
+    uint32_t pw[8], dw[8];
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const uint2 w2 = make_uint2(pack_bf16x2(dse[4 * qq], dse[4 * qq + 1]), pack_bf16x2(dse[4 * qq + 2], dse[4 * qq + 3]));
-      *reinterpret_cast<uint2*>(&sdst[key_rel * GQ + 8 * (qq ^ ((key_rel >> 2) & 3)) + 4 * h]) = w2;
+    for (int i = 0; i < 8; ++i) {
+      pw[i] = pack_bf16x2(sacc[2 * i], sacc[2 * i + 1]);
+      dw[i] = pack_bf16x2(dpacc[2 * i], dpacc[2 * i + 1]);
+    }
+    const bf16x8 pb0 = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    const bf16x8 pb1 = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
+    const bf16x8 db0 = __builtin_bit_cast(bf16x8, make_uint4(dw[0], dw[1], dw[2], dw[3]));
+    const bf16x8 db1 = __builtin_bit_cast(bf16x8, make_uint4(dw[4], dw[5], dw[6], dw[7]));
+
+    // dS^T into LDS (one wave of each pair): row key_rel, query columns 8 qq + 4 h .. +3
+    if (do_dq) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        *reinterpret_cast<uint2*>(&sdst[key_rel * GQ + 8 * (qq ^ ((key_rel >> 2) & 3)) + 4 * h]) =
+            make_uint2(dw[2 * qq], dw[2 * qq + 1]);
     }
 
-    // dV^T += dO^T P, dK^T += Q^T dS over the tile's rows: k slice ks holds
-    // rows 16 ks + 4 h .. +3 and 16 ks + 8 + 4 h .. +3 (the accumulator order)
+    // dV^T += dO^T P, dK^T += Q^T dS over the tile's rows, on this wave's half
+    // of the dims: k slice ks holds rows 16 ks + 4 h .. +3 and 16 ks + 8 + 4 h
+    // .. +3 (the accumulator order)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int ra = 16 * ks + 4 * (g4 >> 1) + (j16 >> 2), rb2 = ra + 8;
 #pragma unroll
-      for (int dbk = 0; dbk < DB; ++dbk) {
-        const int c = 4 * dbk + 2 * (g4 & 1) + ((j16 & 3) >> 1);
+      for (int i = 0; i < DBH; ++i) {
+        const int c = 4 * (DBH * dh + i) + 2 * (g4 & 1) + ((j16 & 3) >> 1);
         const int pa = ra * D + 8 * (c ^ qswz<D>(ra)) + 4 * (j16 & 1);
         const int pbb = rb2 * D + 8 * (c ^ qswz<D>(rb2)) + 4 * (j16 & 1);
         const bf16x8 aot = tr_pair(&tdo[pa], &tdo[pbb]);
         const bf16x8 aqt = tr_pair(&tq[pa], &tq[pbb]);
-        dva[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aot, ks ? pb1 : pb0, dva[dbk], 0, 0, 0);
-        dka[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, ks ? db1 : db0, dka[dbk], 0, 0, 0);
+        dva[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aot, ks ? pb1 : pb0, dva[i], 0, 0, 0);
+        dka[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, ks ? db1 : db0, dka[i], 0, 0, 0);
       }
     }
     __syncthreads();
 
-    // dQ (rows x this wave's 32 dims) = dS K over the wave's key range
-    f32x16 dqa = {};
+    // dQ (rows x this wave's 32 dims) = dS K over its key range; K^T from LDS
+    if (do_dq) {
+      f32x16 dqa = {};
 #pragma unroll
-    for (int s = 0; s < KSL; ++s) {
-      const int ka = dq_kb + 16 * s + 8 * (g4 >> 1) + (j16 >> 2), kb2 = ka + 4;
-      const int c = 2 * (g4 & 1) + ((j16 & 3) >> 1);
-      const bf16x8 ad = tr_pair(&sdst[ka * GQ + 8 * (c ^ ((ka >> 2) & 3)) + 4 * (j16 & 1)],
-                                &sdst[kb2 * GQ + 8 * (c ^ ((kb2 >> 2) & 3)) + 4 * (j16 & 1)]);
-      dqa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, kt[s], dqa, 0, 0, 0);
+      for (int s = 0; s < KSL; ++s) {
+        const int ka = dq_kb + 16 * s + 8 * (g4 >> 1) + (j16 >> 2), kb2 = ka + 4;
+        const int c = 2 * (g4 & 1) + ((j16 & 3) >> 1);
+        const bf16x8 ad = tr_pair(&sdst[ka * GQ + 8 * (c ^ ((ka >> 2) & 3)) + 4 * (j16 & 1)],
+                                  &sdst[kb2 * GQ + 8 * (c ^ ((kb2 >> 2) & 3)) + 4 * (j16 & 1)]);
+        const int ck = 4 * dq_db + 2 * (g4 & 1) + ((j16 & 3) >> 1);
+        const bf16x8 bk = tr_pair(&sk[ka * D + 8 * (ck ^ qswz<D>(ka)) + 4 * (j16 & 1)],
+                                  &sk[kb2 * D + 8 * (ck ^ qswz<D>(kb2)) + 4 * (j16 & 1)]);
+        dqa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bk, dqa, 0, 0, 0);
+      }
+      float* dqrow = p.dq + (((int64_t)b * p.q_len + (tp - p.q_pos0)) * p.hq + hq) * D + 32 * dq_db + n;
+      const int64_t rstride = (int64_t)p.hq * D;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = 8 * (e >> 2) + 4 * h + (e & 3);
+        if (tp + r < t_end) unsafeAtomicAdd(dqrow + r * rstride, dqa[e]);
+      }
     }
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const int4 rid = *reinterpret_cast<const int4*>(&s_row[buf][8 * qq + 4 * h]);
-      const int ra[4] = {rid.x, rid.y, rid.z, rid.w};
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        if (ra[rr] >= 0) unsafeAtomicAdd(p.dq + (int64_t)ra[rr] * D + 32 * dq_db + n, dqa[4 * qq + rr]);
-    }
-
-    if (more) stash(buf ^ 1);
+    if (more) stash(it + 1, buf ^ 1);
     __syncthreads();
-    buf ^= 1;
   }
 
-  // dK, dV of this wave's keys: lane (key n, h) holds dims 32 db + 8 qq + 4 h .. +3
+  // dK, dV of this wave's keys and dims: lane (key n, h) holds dims
+  // 32 (DBH dh + i) + 8 qq + 4 h .. +3
   if (!key_ok) return;
   const int64_t krow = (key_base + key_rel) * D;
-  float* gk = pooled ? p.dpk : p.drk;
-  float* gv = pooled ? p.dpv : p.drv;
+  // a run's partial: row (bh, tile, split, key) of K then (separate series) V
+  const int nser = p.shared ? 1 : 2;
+  const int64_t prow = pooled ? ((((int64_t)bh * p.pool_tiles + wi / p.pool_splits) * p.pool_splits + wi % p.pool_splits) *
+                                     GK + key_rel) * nser * D
+                              : 0;
 #pragma unroll
-  for (int dbk = 0; dbk < DB; ++dbk)
+  for (int i = 0; i < DBH; ++i)
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
-      const int d = 32 * dbk + 8 * qq + 4 * h;
+      const int d = 32 * (DBH * dh + i) + 8 * qq + 4 * h;
       float kv[4], vv[4];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        vv[rr] = dva[dbk][4 * qq + rr];
-        kv[rr] = dka[dbk][4 * qq + rr] + (p.shared ? vv[rr] : 0.f);
+        vv[rr] = dva[i][4 * qq + rr];
+        kv[rr] = dka[i][4 * qq + rr] + (p.shared ? vv[rr] : 0.f);
       }
       if (pooled) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          unsafeAtomicAdd(gk + krow + d + rr, kv[rr]);
-          if (!p.shared) unsafeAtomicAdd(gv + krow + d + rr, vv[rr]);
-        }
+        *reinterpret_cast<float4*>(p.part + prow + d) = make_float4(kv[0], kv[1], kv[2], kv[3]);
+        if (!p.shared) *reinterpret_cast<float4*>(p.part + prow + D + d) = make_float4(vv[0], vv[1], vv[2], vv[3]);
       } else {
-        float4* pk4 = reinterpret_cast<float4*>(gk + krow + d);
+        float4* pk4 = reinterpret_cast<float4*>(p.drk + krow + d);
         float4 k4 = make_float4(kv[0], kv[1], kv[2], kv[3]);
         if (p.accumulate) {
           const float4 o = *pk4;
@@ -362,7 +354,7 @@ __global__ __launch_bounds__(256, 1) void attn_grad_kernel(GradParams p) {
         }
         *pk4 = k4;
         if (!p.shared) {
-          float4* pv4 = reinterpret_cast<float4*>(gv + krow + d);
+          float4* pv4 = reinterpret_cast<float4*>(p.drv + krow + d);
           float4 v4 = make_float4(vv[0], vv[1], vv[2], vv[3]);
           if (p.accumulate) {
             const float4 o = *pv4;
@@ -426,6 +418,61 @@ __global__ __launch_bounds__(256) void attn_grad_prep_kernel(PrepParams p) {
   if (tid == 0) unsafeAtomicAdd(p.dsink + hh, red[0] + red[1] + red[2] + red[3]);
 }
 
+// Pooled-entry gradients: the sum of the partials of the runs that touched the
+// entry's 128-key tile (entries no query sees get 0), stored or added.  One
+// thread per 4 dims of one entry.
+struct ReduceParams {
+  const float* part;
+  float* gk;
+  float* gv;
+  int64_t entries;
+  int64_t total;  // batch * kv_heads * entries * dim / 4
+  int dim, n_pool, pool_tiles, pool_splits, shared, accumulate;
+  int q_pos0, q_end, block, window, mode;
+};
+
+__global__ __launch_bounds__(256) void attn_grad_reduce_kernel(ReduceParams p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= p.total) return;
+  const int q4 = p.dim / 4;
+  const int d = (int)(i % q4) * 4;
+  const int64_t row = i / q4;  // (bh, entry)
+  const int j = (int)(row % p.entries);
+  const int64_t bh = row / p.entries;
+  float4 k4 = make_float4(0.f, 0.f, 0.f, 0.f), v4 = k4;
+  if (j < p.n_pool) {
+    const int tile = j / GK, k0 = tile * GK;
+    const int t_first = p.mode == LBCA_EXCLUSIVE ? (k0 + 1) * p.block + p.window - 1 : (k0 + 1) * p.block - 1;
+    const int start = t_first > p.q_pos0 ? t_first : p.q_pos0;
+    const int runs = (p.q_end - start + PSPLIT - 1) / PSPLIT;
+    const int nser = p.shared ? 1 : 2;
+    const float* src = p.part + (((bh * p.pool_tiles + tile) * p.pool_splits) * GK + (j - k0)) * nser * p.dim + d;
+    const int64_t step = (int64_t)GK * nser * p.dim;
+    for (int r = 0; r < runs; ++r) {
+      const float4 a = *reinterpret_cast<const float4*>(src + r * step);
+      k4.x += a.x; k4.y += a.y; k4.z += a.z; k4.w += a.w;
+      if (!p.shared) {
+        const float4 c = *reinterpret_cast<const float4*>(src + r * step + p.dim);
+        v4.x += c.x; v4.y += c.y; v4.z += c.z; v4.w += c.w;
+      }
+    }
+  }
+  float4* gk4 = reinterpret_cast<float4*>(p.gk + row * p.dim + d);
+  if (p.accumulate) {
+    const float4 o = *gk4;
+    k4.x += o.x; k4.y += o.y; k4.z += o.z; k4.w += o.w;
+  }
+  *gk4 = k4;
+  if (!p.shared) {
+    float4* gv4 = reinterpret_cast<float4*>(p.gv + row * p.dim + d);
+    if (p.accumulate) {
+      const float4 o = *gv4;
+      v4.x += o.x; v4.y += o.y; v4.z += o.z; v4.w += o.w;
+    }
+    *gv4 = v4;
+  }
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ x, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) x[i] = 0.f;
 }
@@ -437,24 +484,52 @@ hipError_t zero_f32(float* x, int64_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// pooled-entry tiles of 128 keys, and query runs of 512 positions the first
+// tile's entries are seen by (every later tile is seen by no more)
+struct GradPlan {
+  int n_pool = 0, pool_tiles = 0, pool_splits = 0;
+  size_t dvec_bytes = 0, part_bytes = 0;
+};
+
+GradPlan grad_plan(const lbca_prefill_grad_args& a) {
+  GradPlan g;
+  g.dvec_bytes = (size_t)((a.batch * a.q_len * a.q_heads * 4 + 255) / 256 * 256);
+  if (a.q_len == 0) return g;
+  int64_t np_last, rb_last;
+  lbca_visible_range(a.q_pos0 + a.q_len - 1, a.block, a.window, a.mode, &np_last, &rb_last);
+  g.n_pool = (int)np_last;
+  g.pool_tiles = (int)((np_last + GK - 1) / GK);
+  if (g.pool_tiles > 0) {
+    const int64_t t_first = a.mode == LBCA_EXCLUSIVE ? a.block + a.window - 1 : a.block - 1;
+    const int64_t t0 = t_first > a.q_pos0 ? t_first : a.q_pos0;
+    g.pool_splits = (int)((a.q_pos0 + a.q_len - t0 + PSPLIT - 1) / PSPLIT);
+  }
+  const int nser = a.pooled_v == nullptr ? 1 : 2;
+  g.part_bytes = (size_t)(a.batch * a.kv_heads) * g.pool_tiles * g.pool_splits * GK * nser * a.dim * 4;
+  return g;
+}
+
 }  // namespace
 
 size_t prefill_grad_workspace_bytes(const lbca_prefill_grad_args& a) {
-  return (size_t)((a.batch * a.q_len * a.q_heads * 4 + 15) / 16 * 16);
+  const GradPlan g = grad_plan(a);
+  return g.dvec_bytes + g.part_bytes;
 }
 
 hipError_t launch_prefill_grad(const lbca_prefill_grad_args& a, void* workspace, hipStream_t stream) {
   const bool shared = a.pooled_v == nullptr;
   const int64_t G = a.q_heads / a.kv_heads;
+  const GradPlan g = grad_plan(a);
   float* dvec = static_cast<float*>(workspace);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + g.dvec_bytes);
   hipError_t e;
   if (!a.accumulate) {
-    const int64_t pooled_elems = a.batch * a.kv_heads * a.entries * a.dim;
-    if ((e = zero_f32(a.grad_pooled_k, pooled_elems, stream)) != hipSuccess) return e;
-    if (!shared && (e = zero_f32(a.grad_pooled_v, pooled_elems, stream)) != hipSuccess) return e;
     if ((e = zero_f32(a.grad_sink, a.q_heads, stream)) != hipSuccess) return e;
-    if (a.q_len == 0) {  // no queries: every raw row's gradient is zero too
+    if (a.q_len == 0) {  // no queries: every key and value gradient is zero
+      const int64_t pooled_elems = a.batch * a.kv_heads * a.entries * a.dim;
       const int64_t raw_elems = a.batch * a.kv_heads * a.raw_rows * a.dim;
+      if ((e = zero_f32(a.grad_pooled_k, pooled_elems, stream)) != hipSuccess) return e;
+      if (!shared && (e = zero_f32(a.grad_pooled_v, pooled_elems, stream)) != hipSuccess) return e;
       if ((e = zero_f32(a.grad_raw_k, raw_elems, stream)) != hipSuccess) return e;
       if (!shared && (e = zero_f32(a.grad_raw_v, raw_elems, stream)) != hipSuccess) return e;
     }
@@ -485,32 +560,47 @@ hipError_t launch_prefill_grad(const lbca_prefill_grad_args& a, void* workspace,
   p.rk = static_cast<const bf16_t*>(a.raw_k);
   p.rv = static_cast<const bf16_t*>(a.raw_v);
   p.dq = a.grad_q;
-  p.dpk = a.grad_pooled_k;
-  p.dpv = a.grad_pooled_v;
+  p.part = part;
   p.drk = a.grad_raw_k;
   p.drv = a.grad_raw_v;
-  p.q_len = a.q_len; p.hq = a.q_heads; p.hkv = a.kv_heads; p.G = G;
-  p.entries = a.entries; p.raw_rows = a.raw_rows; p.q_pos0 = a.q_pos0; p.raw_pos_base = a.raw_pos_base;
-  p.m = a.block; p.W = a.window;
+  p.entries = a.entries;
+  p.raw_rows = a.raw_rows;
+  p.q_len = (int)a.q_len; p.hq = (int)a.q_heads; p.hkv = (int)a.kv_heads; p.G = (int)G;
+  p.q_pos0 = (int)a.q_pos0; p.raw_pos_base = (int)a.raw_pos_base;
+  p.m = (int)a.block; p.W = (int)a.window;
   p.mode = a.mode;
   p.accumulate = a.accumulate;
   p.shared = shared;
-  int64_t np_last, rb_last;
-  lbca_visible_range(a.q_pos0 + a.q_len - 1, a.block, a.window, a.mode, &np_last, &rb_last);
-  p.n_pool = (int)np_last;
-  p.pool_tiles = (int)((np_last + GK - 1) / GK);
-  if (p.pool_tiles > 0) {
-    const int64_t t_first = a.mode == LBCA_EXCLUSIVE ? a.block + a.window - 1 : a.block - 1;
-    const int64_t i_first = t_first - a.q_pos0 > 0 ? t_first - a.q_pos0 : 0;
-    const int64_t rows = (a.q_len - i_first) * G;
-    p.pool_splits = (int)((rows + QSPLIT - 1) / QSPLIT);
-  }
+  p.n_pool = g.n_pool;
+  p.pool_tiles = g.pool_tiles;
+  p.pool_splits = g.pool_splits;
   p.raw_tiles = (int)((a.raw_rows + GK - 1) / GK);
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
   const dim3 grid((unsigned)(p.pool_tiles * p.pool_splits + p.raw_tiles), (unsigned)(a.batch * a.kv_heads));
-  if (a.dim == 128) attn_grad_kernel<128><<<grid, 256, 0, stream>>>(p);
-  else attn_grad_kernel<64><<<grid, 256, 0, stream>>>(p);
+  if (a.dim == 128) attn_grad_kernel<128><<<grid, 512, 0, stream>>>(p);
+  else attn_grad_kernel<64><<<grid, 512, 0, stream>>>(p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  ReduceParams rp{};
+  rp.part = part;
+  rp.gk = a.grad_pooled_k;
+  rp.gv = a.grad_pooled_v;
+  rp.entries = a.entries;
+  rp.total = a.batch * a.kv_heads * a.entries * a.dim / 4;
+  rp.dim = (int)a.dim;
+  rp.n_pool = g.n_pool;
+  rp.pool_tiles = g.pool_tiles;
+  rp.pool_splits = g.pool_splits;
+  rp.shared = shared;
+  rp.accumulate = a.accumulate;
+  rp.q_pos0 = (int)a.q_pos0;
+  rp.q_end = (int)(a.q_pos0 + a.q_len);
+  rp.block = (int)a.block;
+  rp.window = (int)a.window;
+  rp.mode = a.mode;
+  if (rp.total > 0)
+    attn_grad_reduce_kernel<<<(unsigned)((rp.total + 255) / 256), 256, 0, stream>>>(rp);
   return hipGetLastError();
 }
 

@@ -514,12 +514,30 @@ def attend_prefill_backward(q, q_pos0, pooled_k, raw_k, raw_pos_base, block, win
     need = ctypes.c_size_t()
     _check(lib().lbca_attend_prefill_backward_workspace(ctypes.byref(a), ctypes.byref(need)),
            "lbca_attend_prefill_backward_workspace")
+    if workspace is not None and workspace.numel() * workspace.element_size() < need.value:
+        raise ValueError(f"workspace needs {need.value} bytes")
     if workspace is None and need.value > 0:
         workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().lbca_attend_prefill_backward(ctypes.byref(a), _p(workspace), ws_bytes, _stream(stream)),
            "lbca_attend_prefill_backward")
     return grad_q, grad_pooled_k, grad_pooled_v, grad_raw_k, grad_raw_v, grad_sink
+
+
+def attend_prefill_backward_workspace_bytes(q_shape, q_pos0, kv_heads, entries, raw_rows, raw_pos_base, block,
+                                            window, mode, shared=False, dtype=torch.bfloat16):
+    """lbca_attend_prefill_backward_workspace for these sizes (B, Tq, Hq, d = q_shape); no
+    buffer is touched, so placeholder addresses stand in for them."""
+    B, Tq, Hq, d = q_shape
+    ph = ctypes.c_void_p(_EMPTY)
+    a = PrefillGradArgs(ph, ph, None if shared else ph, ph, None if shared else ph, None, ph, ph, ph, ph, ph,
+                        None if shared else ph, ph, None if shared else ph, None, B, Tq, Hq, kv_heads, d, entries,
+                        raw_rows, q_pos0, raw_pos_base, block, window, mode,
+                        F32 if dtype == torch.float32 else BF16, F32, 0, 1.0)
+    need = ctypes.c_size_t()
+    _check(lib().lbca_attend_prefill_backward_workspace(ctypes.byref(a), ctypes.byref(need)),
+           "lbca_attend_prefill_backward_workspace")
+    return need.value
 
 
 def _check_index(q_idx, head_w, keys, pos):

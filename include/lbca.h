@@ -424,13 +424,19 @@ LBCA_API int lbca_attend_prefill(const lbca_prefill_args* a, void* stream);
  * no query of the call sees get 0); 1: added to them, so a chunked backward
  * calls this once per chunk of queries.
  * Supported: dtype BF16, dim 64 or 128, scale > 0, batch * q_len * q_heads
- * and raw positions below 2^31, batch * kv_heads <= 65535.  The visibility
+ * and raw_pos_base + raw_rows + block + window below 2^31,
+ * batch * kv_heads <= 65535.  The visibility
  * checks of lbca_attend_prefill apply (INVALID_ARG).
- * Workspace (lbca_attend_prefill_backward_workspace): 4 bytes per query row
- * (batch * q_len * q_heads, rounded up to 16), 16-byte aligned, contents on
- * entry do not matter; calls sharing one must not overlap.  grad_q, the
- * pooled-entry gradients and grad_sink are summed with floating-point atomics,
- * so their last bits can differ from run to run.
+ * Workspace (lbca_attend_prefill_backward_workspace; 16-byte aligned,
+ * contents on entry do not matter, calls sharing one must not overlap): D per
+ * query row (4 * batch * q_len * q_heads bytes, rounded up to 256), then one
+ * fp32 partial gradient per pooled entry, K and V (K only when shared), and
+ * run of 512 query positions: 4 * batch * kv_heads * T * S * 128 * nser * dim
+ * bytes with T = ceil(n / 128) for the n entries the last query sees, S =
+ * ceil((q_pos0 + q_len - max(f, q_pos0)) / 512), f = block + window - 1
+ * (EXCLUSIVE) or block - 1 (OVERLAP) the first position that sees entry 0,
+ * nser = 2 (1 shared).  grad_q and grad_sink are summed with floating-point
+ * atomics, so their last bits can differ from run to run.
  */
 typedef struct lbca_prefill_grad_args {
   const void* q;

@@ -322,7 +322,13 @@ def test_prefill_backward_validation(kw, code):
 @fake_ptr
 def test_prefill_backward_workspace_and_empty_calls():
     st, n = _prefill_grad(ws_query=True)
-    assert st == 0 and n == 2048 * 24 * 4
+    # D per query row, then the pooled partials: 8 KV heads x 8 tiles of 128 entries
+    # (1016 seen by the last query) x 4 runs of 512 positions x 128 x (K, V) x 128 dims
+    assert st == 0 and n == 2048 * 24 * 4 + 8 * 8 * 4 * 128 * 2 * 128 * 4
+    st, n = _prefill_grad(ws_query=True, pooled_v=None, raw_v=None, grad_pooled_v=None, grad_raw_v=None)
+    assert st == 0 and n == 2048 * 24 * 4 + 8 * 8 * 4 * 128 * 1 * 128 * 4
+    assert lbca.attend_prefill_backward_workspace_bytes((1, 2048, 24, 128), 14336, 8, 1016, 16384, 0, 16, 128,
+                                                        0) == 2048 * 24 * 4 + 8 * 8 * 4 * 128 * 2 * 128 * 4
     assert _prefill_grad()[0] == -3                                  # no workspace given
     assert _prefill_grad(batch=0)[0] == 0
     assert _prefill_grad(q_len=0, accumulate=1)[0] == 0               # nothing to add
