@@ -279,22 +279,34 @@ def run_incremental(B, reps):
             for L in layers:
                 decode(L, pos, rpb)
 
+    def fused():  # lbca_decode_step: append, pool on completion and decode in one launch
+        for pos in poss:
+            for L in layers:
+                lbca.decode_step(L.q, L.xk, L.xv, L.xz, L.rk, L.rv, L.rz, L.bias, L.pk, L.pv, pos, L.rpb, M, W,
+                                 out=L.out, lse=L.lse, workspace=L.ws)
+
     loop()  # eager pass; the graphs then revisit the same 64 positions with the same tokens
     torch.cuda.synchronize()
     ref = [L.out.clone() for L in layers]
     if not all(torch.equal(L.rpb, bases[-1]) for L in layers):
         raise RuntimeError("cache step left an unexpected raw base")
-    g_loop, g_dec = capture(loop), capture(decode_only)
+    fused()  # the same positions through the fused step (entries the loop pooled are read back)
+    torch.cuda.synchronize()
+    if not all(torch.equal(L.out, r) for L, r in zip(layers, ref)):
+        raise RuntimeError("the fused decode step differs from cache step + decode")
+    g_loop, g_dec, g_fused = capture(loop), capture(decode_only), capture(fused)
     g_loop.replay()
     torch.cuda.synchronize()
     if not all(torch.equal(L.out, r) for L, r in zip(layers, ref)):
         raise RuntimeError("graph replay of the decode loop differs from the eager pass")
-    ms_loop, ms_dec = time_graph(g_loop, reps), time_graph(g_dec, reps)
+    ms_loop, ms_dec, ms_fused = time_graph(g_loop, reps), time_graph(g_dec, reps), time_graph(g_fused, reps)
     n = INC_STEPS * LAYERS
     return {"layer_steps_per_s": n / (ms_loop * 1e-3), "layer_step_us": ms_loop * 1e3 / n,
             "decode_us": ms_dec * 1e3 / n, "cache_append_us": (ms_loop - ms_dec) * 1e3 / n,
+            "fused_layer_step_us": ms_fused * 1e3 / n, "fused_layer_steps_per_s": n / (ms_fused * 1e-3),
+            "fused_over_decode_us": (ms_fused - ms_dec) * 1e3 / n,
             "workload": f"batch {B}, 14 layers, positions {t0}..{T_POS} (one due block per layer), "
-                        f"mirrored raw ring of {RING} slots"}
+                        f"mirrored raw ring of {RING} slots; fused: lbca_decode_step, one launch per layer-step"}
 
 
 def run_pool_backward(B, reps):

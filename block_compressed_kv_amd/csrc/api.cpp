@@ -161,7 +161,7 @@ int lbca_pool_blocks_backward(const lbca_pool_grad_args* a, void* workspace, siz
 }
 
 // ---------------------------------------------------------------------------
-int lbca_cache_append(const lbca_cache_args* a, void* stream) {
+static int validate_cache(const lbca_cache_args* a) {
   if (!a || !a->x_new || !a->z_new || !a->raw_x || !a->raw_z || !a->bias || !a->out_x || !a->pos ||
       !a->raw_pos_base)
     return LBCA_ERR_INVALID_ARG;
@@ -195,6 +195,12 @@ int lbca_cache_append(const lbca_cache_args* a, void* stream) {
       !aligned16(a->out_v) || !aligned16(a->xb_new) || !aligned16(a->zb_new) || !aligned16(a->raw_xb) ||
       !aligned16(a->raw_zb) || !aligned16(a->bias_b))
     return LBCA_ERR_INVALID_ARG;
+  return LBCA_OK;
+}
+
+int lbca_cache_append(const lbca_cache_args* a, void* stream) {
+  const int st = validate_cache(a);
+  if (st != LBCA_OK) return st;
   if (a->batch == 0) return LBCA_OK;
   return hip_status(lbca::launch_cache_append(*a, static_cast<hipStream_t>(stream)));
 }
@@ -270,6 +276,60 @@ int lbca_attend_decode_noalloc(const lbca_decode_args* a, void* stream) {
   void* ws = nullptr;
   if (plan.ws_bytes > 0 && lbca::static_scratch(&ws) != hipSuccess) return LBCA_ERR_HIP;
   return hip_status(lbca::launch_decode(*a, plan, ws, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// lbca_decode_step: the decode and cache-step arguments it stands for
+static void step_parts(const lbca_step_args* a, lbca_decode_args* d, lbca_cache_args* c) {
+  *d = lbca_decode_args{};
+  d->q = a->q; d->pooled_k = a->pooled_k; d->pooled_v = a->pooled_v;
+  d->raw_k = a->raw_k; d->raw_v = a->raw_v; d->pos = a->pos; d->raw_pos_base = a->raw_pos_base;
+  d->sel_idx = nullptr; d->sink = a->sink; d->out = a->out; d->lse = a->lse;
+  d->batch = a->batch; d->q_heads = a->q_heads; d->kv_heads = a->kv_heads; d->dim = a->dim;
+  d->entries = a->entries; d->raw_rows = 2 * a->ring; d->k_sel = 0;
+  d->block = a->block; d->window = a->window; d->mode = LBCA_EXCLUSIVE; d->dtype = a->dtype;
+  d->scale = a->scale; d->rmsnorm_eps = -1.f; d->rope_dims = 0; d->rope_base = 0.f;
+  *c = lbca_cache_args{};
+  c->x_new = a->k_new; c->v_new = a->v_new; c->z_new = a->z_new;
+  c->raw_x = a->raw_k; c->raw_v = a->raw_v; c->raw_z = a->raw_z; c->bias = a->bias;
+  c->out_x = a->pooled_k; c->out_v = a->pooled_v; c->pos = a->pos; c->raw_pos_base = a->raw_pos_base;
+  c->batch = a->batch; c->heads = a->kv_heads; c->dim = a->dim; c->block = a->block; c->window = a->window;
+  c->ring = a->ring; c->entries = a->entries; c->mode = LBCA_EXCLUSIVE; c->x_dtype = a->dtype;
+  c->z_dtype = a->z_dtype; c->rmsnorm_eps = -1.f; c->rope_dims = 0; c->rope_base = 0.f;
+}
+
+static int validate_step(const lbca_step_args* a, lbca_decode_args* d, lbca_cache_args* c) {
+  if (!a || !a->k_new || !a->v_new || !a->pooled_v || !a->raw_v || !a->raw_pos_base) return LBCA_ERR_INVALID_ARG;
+  if (a->ring < 1 || a->ring > kMaxElems) return LBCA_ERR_INVALID_ARG;
+  step_parts(a, d, c);
+  int st = validate_decode(d);
+  if (st != LBCA_OK) return st;
+  st = validate_cache(c);
+  if (st != LBCA_OK) return st;
+  if (a->dtype != LBCA_BF16 || !(a->dim == 64 || a->dim == 128)) return LBCA_ERR_UNSUPPORTED;
+  return LBCA_OK;
+}
+
+int lbca_decode_step_workspace(const lbca_step_args* a, size_t* bytes) {
+  if (!bytes) return LBCA_ERR_INVALID_ARG;
+  lbca_decode_args d;
+  lbca_cache_args c;
+  const int st = validate_step(a, &d, &c);
+  if (st != LBCA_OK) return st;
+  *bytes = lbca::plan_decode(d).ws_bytes;
+  return LBCA_OK;
+}
+
+int lbca_decode_step(const lbca_step_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  lbca_decode_args d;
+  lbca_cache_args c;
+  const int st = validate_step(a, &d, &c);
+  if (st != LBCA_OK) return st;
+  const lbca::DecodePlan plan = lbca::plan_decode(d);
+  if (plan.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.ws_bytes || !aligned16(workspace)))
+    return LBCA_ERR_WORKSPACE;
+  if (a->batch == 0) return LBCA_OK;
+  return hip_status(lbca::launch_decode_step(d, c, plan, workspace, static_cast<hipStream_t>(stream)));
 }
 
 // ---------------------------------------------------------------------------

@@ -43,6 +43,7 @@
 #include <mutex>
 #include <type_traits>
 
+#include "cache_common.h"
 #include "decode_common.h"
 
 #ifndef LBCA_DECODE_TILES_PER_WAVE
@@ -140,6 +141,7 @@ struct Tile {
 // valid memory and already in cache, so such loads cost no HBM traffic).
 struct Slices {
   uintptr_t pk, pv, rk, rv, dummy;
+  uintptr_t tk, tv;  // fused cache step: the new token's rows
 };
 
 // Selected ids of one workgroup's range are staged in LDS (a global load of
@@ -163,7 +165,7 @@ __device__ __forceinline__ void clear_valid(Tile<D, R, DS, SHARED>& T) {
 // not loaded at all: each load instruction costs address-unit time even when
 // its data is cached, and a wave cannot end before its loads return.
 // ids: the selected ids of list positions r0, r0+1, ... (LDS).
-template <int D, int R, int DS, bool SHARED>
+template <int D, int R, int DS, bool SHARED, bool FUSED = false>
 __device__ __forceinline__ void load_tile(Tile<D, R, DS, SHARED>& T, const int* ids, int r0,
                                           bool sel, const Slices& sl, const SeqView& sv,
                                           int tiles_p, int pad_p, int tile, bool live, int n,
@@ -188,11 +190,13 @@ __device__ __forceinline__ void load_tile(Tile<D, R, DS, SHARED>& T, const int* 
       ok = ok && row >= 0 && row < sv.n_pooled;
     }
     const uint64_t off = (uint64_t)(uint32_t)row * (D * 2) + 16u * kq;
-    const uintptr_t kp = ok ? kb + off : sl.dummy + 16u * kq;
+    // fused cache step: the raw row at the position is the new token's input row
+    const bool tok = FUSED && is_raw && v == sv.n_raw - 1;
+    const uintptr_t kp = ok ? (tok ? sl.tk + 16u * kq : kb + off) : sl.dummy + 16u * kq;
 #pragma unroll
     for (int s = 0; s < KS; ++s) T.k[h][s] = ldg16(kp + 64u * s);
     if constexpr (!SHARED) {
-      const uintptr_t vp = (ok ? vb + off : sl.dummy + 16u * kq) + 2u * dv0;
+      const uintptr_t vp = (ok ? (tok ? sl.tv + 16u * kq : vb + off) : sl.dummy + 16u * kq) + 2u * dv0;
 #pragma unroll
       for (int s = 0; s < KV; ++s) T.v[h][s] = ldg16(vp + 64u * s);
     }
@@ -200,8 +204,11 @@ __device__ __forceinline__ void load_tile(Tile<D, R, DS, SHARED>& T, const int* 
   }
 }
 
-template <int D, int R, int NW, int DS, bool SHARED, int RD, bool TREAT, bool SPEC>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
+// One decode workgroup's work (workgroup id bid); FUSED: the launch also runs
+// the cache step (lbca_decode_step), so the raw row at the position is read
+// from the new token's input and the raw base follows from the position.
+template <int D, int R, int NW, int DS, bool SHARED, int RD, bool TREAT, bool SPEC, bool FUSED>
+__device__ __forceinline__ void decode_body(const DecodeParams& p, unsigned bid) {
   constexpr int KS = D / 32, NH = R / 16;
   constexpr int DV = D / DS;                         // output dims of this workgroup
   constexpr int KV = DV / 32, DT = DV / 16, PITCH = DV + 16;
@@ -221,11 +228,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile choices stay scalar
   const int n = lane & 15, kq = lane >> 4;
   // linear id -> (unit, split, dim slice); twins of a unit sit 8 ids apart (same XCD)
-  unsigned u = blockIdx.x, dh = 0;
+  unsigned u = bid, dh = 0;
   if constexpr (DS > 1) {
-    const unsigned rest = blockIdx.x >> 3;
+    const unsigned rest = bid >> 3;
     dh = rest % DS;
-    u = (rest / DS) * 8 + (blockIdx.x & 7);
+    u = (rest / DS) * 8 + (bid & 7);
   }
   if (u >= (unsigned)p.units * (unsigned)p.splits) return;  // padding of the XCD mapping
   const int split = (int)(u % (unsigned)p.splits);
@@ -265,6 +272,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     sl.pv = SHARED ? sl.pk : reinterpret_cast<uintptr_t>(p.pv) + sp;
     sl.rv = SHARED ? sl.rk : reinterpret_cast<uintptr_t>(p.rv) + sr;
     sl.dummy = reinterpret_cast<uintptr_t>(p.q + (b * p.hq + head0) * D);
+    if constexpr (FUSED) {
+      sl.tk = reinterpret_cast<uintptr_t>(p.tk + (b * p.hkv + kvh) * D);
+      sl.tv = reinterpret_cast<uintptr_t>(p.tv + (b * p.hkv + kvh) * D);
+    } else {
+      sl.tk = sl.tv = 0;
+    }
   }
   // Each wave keeps TMAX tiles in flight.  SPEC instances (one split, no
   // selection, launched as such by the host) request their first TMAX tiles,
@@ -297,7 +310,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
       }
     }
   }
-  const SeqView sv = seq_view(p, b, uniform_value(e_pos), p.rpb ? uniform_value(e_base) : 0);
+  int64_t base = 0;
+  if constexpr (FUSED) {  // the raw base the cache step writes for this position
+    const int64_t t = uniform_value(e_pos);
+    int64_t np = 0, rb = 0;
+    if (t >= 0) visible_range(t, p.m, p.W, p.mode, &np, &rb);
+    base = rb - rb % p.ring;
+    (void)e_base;
+  } else {
+    base = p.rpb ? uniform_value(e_base) : 0;
+  }
+  const SeqView sv = seq_view(p, b, uniform_value(e_pos), base);
   if (!sv.ok) {  // rows do not fit the buffers: NaN, written once per unit and slice
     if (split == 0) {
       for (int i = tid; i < nvalid * DV; i += blockDim.x)
@@ -448,7 +471,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     // computation would need a second buffer and spill)
 #pragma unroll 1
     for (int ti = t0 + wave; ti < t1; ti += NW) {
-      load_tile<D, R, DS, SHARED>(T[0], s_ids, r0, sel, sl, sv, tiles_p, pad_p, ti, true, n, kq, dv0);
+      load_tile<D, R, DS, SHARED, FUSED>(T[0], s_ids, r0, sel, sl, sv, tiles_p, pad_p, ti, true, n, kq, dv0);
       unsigned any = 0;
 #pragma unroll
       for (int h = 0; h < NH; ++h) any |= T[0].valid[h];
@@ -466,7 +489,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < TMAX; ++i) {
         const int ti = t0 + wave + i * NW;
-        if (ti < t1) load_tile<D, R, DS, SHARED>(T[i], s_ids, r0, sel, sl, sv, tiles_p, pad_p, ti, true, n, kq, dv0);
+        if (ti < t1) load_tile<D, R, DS, SHARED, FUSED>(T[i], s_ids, r0, sel, sl, sv, tiles_p, pad_p, ti, true, n, kq, dv0);
         else clear_valid(T[i]);
       }
     }
@@ -480,7 +503,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
         for (int h = 0; h < NH; ++h) any |= T[i].valid[h];
         if (any) process(T[i], ti);
         const int nt = ti + step;
-        if (nt < t1) load_tile<D, R, DS, SHARED>(T[i], s_ids, r0, sel, sl, sv, tiles_p, pad_p, nt, true, n, kq, dv0);
+        if (nt < t1) load_tile<D, R, DS, SHARED, FUSED>(T[i], s_ids, r0, sel, sl, sv, tiles_p, pad_p, nt, true, n, kq, dv0);
         else clear_valid(T[i]);
       }
     }
@@ -605,6 +628,35 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
 // NORM: each split's partial is its own normalised output in bf16 (the wide
 // path), weighted by exp2(m_s - M) * l_s instead of exp2(m_s - M).
 constexpr int kMergeGroups = 4;  // for 64-dim chunks
+template <int D, int R, int NW, int DS, bool SHARED, int RD, bool TREAT, bool SPEC>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
+  decode_body<D, R, NW, DS, SHARED, RD, TREAT, SPEC, false>(p, blockIdx.x);
+}
+
+// Fused decode step (lbca_decode_step, EXCLUSIVE rule, K and V series):
+// workgroups [0, n_dec) decode exactly as decode_kernel, except that each
+// reads its position's raw row from the new token's input; the others run the
+// cache step of one (sequence, KV head) row each with their first 256 threads
+// (append to the ring; pool the block the token completes, which no query of
+// this step can see yet: under EXCLUSIVE a block is visible only once it is
+// wholly older than the window).  Nothing one role writes is read by the other.
+struct StepParams {
+  DecodeParams d;
+  CacheParams c;
+  unsigned n_dec;
+};
+
+template <int D, int R, int NW, int DS, bool SPEC, typename TZ>
+__global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepParams sp) {
+  static_assert(NW * 64 >= 256, "the cache step needs 256 threads");
+  __shared__ float part[32][256];  // the cache step's cross-wave phase merge
+  if (blockIdx.x >= sp.n_dec) {
+    cache_row<bf16_t, TZ, true, false, false, true>(sp.c, blockIdx.x - sp.n_dec, part, threadIdx.x < 256);
+    return;
+  }
+  decode_body<D, R, NW, DS, false, 0, false, SPEC, true>(sp.d, blockIdx.x);
+}
+
 template <bool NORM>
 __global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeParams p, int D, int CK) {
   __shared__ float s_w[64][16];                 // split weights
@@ -927,6 +979,76 @@ hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void
   }
   if (e != hipSuccess || plan.splits == 1) return e;
   launch_decode_merge(p, a.batch, a.dim, false, stream);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fused decode step: the decode launch of launch_decode with the cache rows'
+// workgroups appended (plus the merge when the rows are split).
+template <int D, int DS, typename TZ>
+static void launch_step_d(const StepParams& sp, bool spec, unsigned grid, hipStream_t s) {
+  if (spec) decode_step_kernel<D, 32, 8, DS, true, TZ><<<grid, 512, 0, s>>>(sp);
+  else decode_step_kernel<D, 32, 8, DS, false, TZ><<<grid, 512, 0, s>>>(sp);
+}
+
+hipError_t launch_decode_step(const lbca_decode_args& da, const lbca_cache_args& ca, const DecodePlan& plan,
+                              void* ws, hipStream_t stream) {
+  StepParams sp{};
+  DecodeParams& p = sp.d;
+  p.qrows = 1;
+  p.q = static_cast<const bf16_t*>(da.q);
+  p.pk = static_cast<const bf16_t*>(da.pooled_k);
+  p.pv = static_cast<const bf16_t*>(da.pooled_v);
+  p.rk = static_cast<const bf16_t*>(da.raw_k);
+  p.rv = static_cast<const bf16_t*>(da.raw_v);
+  p.pos = da.pos; p.rpb = nullptr; p.sel = nullptr; p.sink = da.sink;
+  p.out = da.out; p.lse = da.lse;
+  p.tk = static_cast<const bf16_t*>(ca.x_new);
+  p.tv = static_cast<const bf16_t*>(ca.v_new);
+  p.ring = ca.ring;
+  const size_t units = (size_t)da.batch * da.kv_heads * plan.head_groups;
+  if (plan.splits > 1) {
+    p.ws_ml = static_cast<float*>(ws);
+    p.ws_acc = p.ws_ml + units * plan.splits * 16 * 2;
+  }
+  p.hq = da.q_heads; p.hkv = da.kv_heads; p.G = da.q_heads / da.kv_heads;
+  p.entries = da.entries; p.raw_rows = da.raw_rows; p.k_sel = 0;
+  p.m = da.block; p.W = da.window; p.mode = da.mode;
+  p.splits = plan.splits; p.head_groups = plan.head_groups;
+  p.units = (int)units;
+  p.scale_log2 = da.scale * kLog2e;
+  p.eps = -1.f;
+  CacheParams& c = sp.c;
+  c.x_new = ca.x_new; c.v_new = ca.v_new; c.z_new = ca.z_new;
+  c.raw_x = ca.raw_x; c.raw_v = ca.raw_v; c.raw_z = ca.raw_z;
+  c.bias = ca.bias; c.out_x = ca.out_x; c.out_v = ca.out_v;
+  c.pos = ca.pos; c.raw_pos_base = ca.raw_pos_base;
+  c.heads = ca.heads; c.dim = ca.dim; c.m = ca.block; c.W = ca.window; c.ring = ca.ring; c.entries = ca.entries;
+  c.mode = ca.mode;
+  c.lanes_per_row = (int)(ca.dim / 8);
+  c.log2_lanes = __builtin_ctz((unsigned)c.lanes_per_row);
+  c.eps = -1.f;
+  const size_t pairs = units * plan.splits;
+  const int ds = plan.dim_splits;
+  sp.n_dec = (unsigned)(ds == 1 ? pairs : (pairs + 7) / 8 * 8 * ds);
+  const unsigned grid = sp.n_dec + (unsigned)(ca.batch * ca.heads);
+  const bool spec = plan.splits == 1;
+  const bool zf = ca.z_dtype == LBCA_F32;
+  switch (da.dim * 4 + ds) {
+    case 64 * 4 + 1:
+      zf ? launch_step_d<64, 1, float>(sp, spec, grid, stream) : launch_step_d<64, 1, bf16_t>(sp, spec, grid, stream);
+      break;
+    case 128 * 4 + 1:
+      zf ? launch_step_d<128, 1, float>(sp, spec, grid, stream) : launch_step_d<128, 1, bf16_t>(sp, spec, grid, stream);
+      break;
+    case 128 * 4 + 2:
+      zf ? launch_step_d<128, 2, float>(sp, spec, grid, stream) : launch_step_d<128, 2, bf16_t>(sp, spec, grid, stream);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.splits == 1) return e;
+  launch_decode_merge(p, da.batch, da.dim, false, stream);
   return hipGetLastError();
 }
 

@@ -29,6 +29,12 @@ struct DecodeParams {
   int rope_dims;
   double log2_base;
   int qrows;  // > 1: consecutive rows b share cache sequence b / qrows (a query chunk)
+  // fused cache step (lbca_decode_step): the new token's K and V rows
+  // [batch, kv_heads, dim], read in place of the raw row at the position; the
+  // raw base is worked out from the position and the ring size
+  const bf16_t* tk;
+  const bf16_t* tv;
+  int64_t ring;  // > 0 only in the fused step
 };
 
 // Puts the argument fields a decode prologue needs into registers before its
@@ -87,7 +93,14 @@ __device__ __forceinline__ SeqView seq_view(const DecodeParams& p, int64_t b, in
   return v;
 }
 __device__ __forceinline__ SeqView seq_view(const DecodeParams& p, int64_t b) {
-  return seq_view(p, b, p.pos[b], p.rpb ? p.rpb[b] : 0);
+  const int64_t t = p.pos[b];
+  int64_t base = p.rpb ? p.rpb[b] : 0;
+  if (p.ring > 0 && t >= 0) {  // fused cache step: the base it writes for t
+    int64_t np, rb;
+    visible_range(t, p.m, p.W, p.mode, &np, &rb);
+    base = rb - rb % p.ring;
+  }
+  return seq_view(p, b, t, base);
 }
 
 // Wide-row MQA decode (512 dims, shared series, query heads in blocks of 32

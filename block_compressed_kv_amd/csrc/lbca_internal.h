@@ -32,6 +32,8 @@ hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void
 // Address of the calling thread's current device's copy of the static decode
 // scratch (LBCA_NOALLOC_SCRATCH_BYTES), looked up once per device.
 hipError_t static_scratch(void** ptr);
+hipError_t launch_decode_step(const lbca_decode_args& da, const lbca_cache_args& ca, const DecodePlan& plan,
+                              void* ws, hipStream_t stream);
 
 hipError_t launch_prefill(const lbca_prefill_args& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const lbca_prefill_args& a, hipStream_t stream);

@@ -142,18 +142,20 @@ struct EntryTreat {
 // in a fixed order (inside a wave by lane exchanges, across the row's waves
 // through `part`, read by the row's first wave), normalises, applies the
 // treatment and stores channels c0.. of the entry (phase-0 lanes of active
-// rows).  Every thread of the workgroup calls it (lane exchanges, barrier).
+// rows).  Every thread of the workgroup calls it (lane exchanges, barrier);
+// in a workgroup wider than the pooling threads (the first 256), the others
+// pass member = false and only take part in the barrier.
 template <typename TX, typename TZ, bool HAS_V, bool TREAT>
 __device__ __forceinline__ void finish_entry(PoolAcc<TX, TZ, HAS_V>& acc, float (*part)[256], int L, int P,
                                              int phase, bool active, int64_t dim, int64_t c0, int64_t block_pos,
-                                             const EntryTreat& tr, TX* out_x, TX* out_v) {
+                                             const EntryTreat& tr, TX* out_x, TX* out_v, bool member = true) {
   const int tid = threadIdx.x, lane = tid & 63;
   if (P > 1) {
     const int span = L * P;  // lanes of one row
     for (int off = L; off < 64 && off < span; off <<= 1) acc.merge_xor(off, (lane & off) == 0);
     if (span > 64) {
       const int wave = tid >> 6, waves_per_row = span >> 6;
-      if (lane < L) {  // the wave's lowest phase group holds its merge
+      if (member && lane < L) {  // the wave's lowest phase group holds its merge
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           part[c][tid] = acc.mx[c];
@@ -163,7 +165,7 @@ __device__ __forceinline__ void finish_entry(PoolAcc<TX, TZ, HAS_V>& acc, float 
         }
       }
       __syncthreads();
-      if ((wave & (waves_per_row - 1)) == 0) {
+      if (member && (wave & (waves_per_row - 1)) == 0) {
         for (int w = 1; w < waves_per_row; ++w) {
           const int src = tid + 64 * w;
 #pragma unroll
@@ -215,7 +217,7 @@ __device__ __forceinline__ void finish_entry(PoolAcc<TX, TZ, HAS_V>& acc, float 
     }
   }
 
-  if (active && phase == 0) {
+  if (member && active && phase == 0) {
     store8(out_x, ox);
     if constexpr (HAS_V) store8(out_v, ov);
   }

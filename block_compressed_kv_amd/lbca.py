@@ -85,6 +85,15 @@ class PrefillGradArgs(ctypes.Structure):
                 ("accumulate", _i32), ("scale", _f32)]
 
 
+class StepArgs(ctypes.Structure):
+    _fields_ = [("q", _vp), ("k_new", _vp), ("v_new", _vp), ("z_new", _vp), ("raw_k", _vp), ("raw_v", _vp),
+                ("raw_z", _vp), ("bias", _vp), ("pooled_k", _vp), ("pooled_v", _vp), ("pos", _vp),
+                ("raw_pos_base", _vp), ("sink", _vp), ("out", _vp), ("lse", _vp),
+                ("batch", _i64), ("q_heads", _i64), ("kv_heads", _i64), ("dim", _i64), ("block", _i64),
+                ("window", _i64), ("ring", _i64), ("entries", _i64), ("dtype", _i32), ("z_dtype", _i32),
+                ("scale", _f32)]
+
+
 class IndexArgs(ctypes.Structure):
     _fields_ = [("q_idx", _vp), ("head_w", _vp), ("keys", _vp), ("pos", _vp), ("out_idx", _vp),
                 ("out_score", _vp),
@@ -139,6 +148,8 @@ def lib():
         L.lbca_attend_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp, ctypes.c_size_t, _vp]
         L.lbca_attend_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
         L.lbca_attend_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
+        L.lbca_decode_step_workspace.argtypes = [ctypes.POINTER(StepArgs), ctypes.POINTER(ctypes.c_size_t)]
+        L.lbca_decode_step.argtypes = [ctypes.POINTER(StepArgs), _vp, ctypes.c_size_t, _vp]
         L.lbca_attend_prefill_backward_workspace.argtypes = [ctypes.POINTER(PrefillGradArgs),
                                                              ctypes.POINTER(ctypes.c_size_t)]
         L.lbca_attend_prefill_backward.argtypes = [ctypes.POINTER(PrefillGradArgs), _vp, ctypes.c_size_t, _vp]
@@ -352,6 +363,50 @@ def cache_append(x_new, z_new, raw_x, raw_z, bias, pos, raw_pos_base, block, win
                   -1.0 if rmsnorm_eps is None else float(rmsnorm_eps), int(rope_dims), float(rope_base),
                   _p(xb_new), _p(zb_new), _p(raw_xb), _p(raw_zb), _p(bias_b))
     _check(lib().lbca_cache_append(ctypes.byref(a), _stream(stream)), "lbca_cache_append")
+
+
+def decode_step(q, k_new, v_new, z_new, raw_k, raw_v, raw_z, bias, pooled_k, pooled_v, pos, raw_pos_base,
+                block, window, out=None, lse=None, sink=None, scale=None, workspace=None, stream=None):
+    """lbca_decode_step (EXCLUSIVE rule): append k/v/z_new [B,Hkv,d] to the mirrored ring
+    raw_* [B,Hkv,2*ring,d], pool the block the token completes into pooled_* [B,Hkv,N,d],
+    write raw_pos_base [B], and decode q [B,Hq,d] at pos [B]; returns (out, lse)."""
+    for t, n, nd in ((q, "q", 3), (k_new, "k_new", 3), (raw_k, "raw_k", 4), (pooled_k, "pooled_k", 4)):
+        _need(t, n, nd)
+    B, Hq, d = q.shape
+    Hkv, R2, N, dev, qt, zt = k_new.shape[1], raw_k.shape[2], pooled_k.shape[2], q.device, (q.dtype,), (z_new.dtype,)
+    if R2 % 2:
+        raise ValueError("raw buffers hold 2 * ring rows")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    _expect(q, "q", (B, Hq, d))
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _expect(t, n, (B, Hkv, d), qt, dev)
+    _expect(z_new, "z_new", (B, Hkv, d), device=dev)
+    for t, n in ((raw_k, "raw_k"), (raw_v, "raw_v")):
+        _expect(t, n, (B, Hkv, R2, d), qt, dev)
+    _expect(raw_z, "raw_z", (B, Hkv, R2, d), zt, dev)
+    _expect(bias, "bias", (Hkv, block, d), (torch.float32,), dev)
+    for t, n in ((pooled_k, "pooled_k"), (pooled_v, "pooled_v")):
+        _expect(t, n, (B, Hkv, N, d), qt, dev)
+    for t, n in ((pos, "pos"), (raw_pos_base, "raw_pos_base")):
+        _expect(t, n, (B,), (torch.int64,), dev)
+    _expect(sink, "sink", (Hq,), (torch.float32,), dev)
+    _expect(out, "out", (B, Hq, d), (torch.float32,), dev)
+    _expect(lse, "lse", (B, Hq), (torch.float32,), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    a = StepArgs(_p(q), _p(k_new), _p(v_new), _p(z_new), _p(raw_k), _p(raw_v), _p(raw_z), _p(bias), _p(pooled_k),
+                 _p(pooled_v), _p(pos), _p(raw_pos_base), _p(sink), _p(out), _p(lse), B, Hq, Hkv, d, block,
+                 window, R2 // 2, N, _dt(q), _dt(z_new), float(scale))
+    need = ctypes.c_size_t()
+    _check(lib().lbca_decode_step_workspace(ctypes.byref(a), ctypes.byref(need)), "lbca_decode_step_workspace")
+    if workspace is None and need.value > 0:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().lbca_decode_step(ctypes.byref(a), _p(workspace), ws_bytes, _stream(stream)), "lbca_decode_step")
+    return out, lse
 
 
 def _decode_args(q, pooled_k, raw_k, pos, block, window, mode, out, lse, pooled_v, raw_v,

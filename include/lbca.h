@@ -283,6 +283,68 @@ typedef struct lbca_cache_args {
 LBCA_API int lbca_cache_append(const lbca_cache_args* a, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* One decode step of an LBCA layer in one launch (mSeek "How LBCA works"
+ * steps 1-4 and "Repository layout", generation through the LBCA cache):
+ * the cache step and the attention of lbca_cache_append + lbca_attend_decode,
+ * fused, for the EXCLUSIVE rule with separate K and V series.  For sequence b
+ * at t = pos[b] (positions before t appended by earlier calls, in order):
+ *   1. k_new[b], v_new[b], z_new[b] go to both ring rows of position t, as
+ *      lbca_cache_append;
+ *   2. when t completes a block ((t+1) % block == 0) it is pooled into entry
+ *      j = (t+1)/block - 1 (skipped when j >= entries), bitwise as
+ *      lbca_pool_blocks.  Unlike lbca_cache_append, which pools a block on
+ *      the step that makes it visible, this pools it on its last token: under
+ *      EXCLUSIVE a block is visible only once it is wholly older than the
+ *      window, so no query of the same step reads it, and the one launch
+ *      needs no ordering between its cache and attention work.  A caller that
+ *      starts decoding after a prefill has pooled every block completed by
+ *      then (not only the visible ones);
+ *   3. raw_pos_base[b] is written as lbca_cache_append writes it;
+ *   4. out[b], lse[b] are lbca_attend_decode's for q[b] at t over the pooled
+ *      entries and the ring (raw rows 2 * ring), the row at t being k_new[b]
+ *      and v_new[b] themselves.
+ *
+ *   q                [batch, q_heads, dim]          dtype
+ *   k_new, v_new     [batch, kv_heads, dim]         dtype
+ *   z_new            [batch, kv_heads, dim]         z_dtype (pooling logits)
+ *   raw_k, raw_v     [batch, kv_heads, 2*ring, dim] dtype
+ *   raw_z            [batch, kv_heads, 2*ring, dim] z_dtype
+ *   bias             [kv_heads, block, dim] float32
+ *   pooled_k/v       [batch, kv_heads, entries, dim] dtype
+ *   pos              [batch] int64 (device);  raw_pos_base [batch] int64 (device, written)
+ *   sink             [q_heads] float32 or NULL
+ *   out              [batch, q_heads, dim] float32;  lse [batch, q_heads] float32 or NULL
+ * Supported: dtype BF16 with dim 64 or 128, z_dtype F32 or BF16, ring >=
+ * window + block, and the constraints of lbca_attend_decode and
+ * lbca_cache_append.  One launch when the decode rows are not split across
+ * workgroups (lbca_decode_step_workspace reports 0), else a second (merge).
+ * Workspace as lbca_attend_decode (the same split partials).
+ */
+typedef struct lbca_step_args {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  const void* z_new;
+  void* raw_k;
+  void* raw_v;
+  void* raw_z;
+  const float* bias;
+  void* pooled_k;
+  void* pooled_v;
+  const int64_t* pos;
+  int64_t* raw_pos_base;
+  const float* sink;
+  float* out;
+  float* lse;
+  int64_t batch, q_heads, kv_heads, dim, block, window, ring, entries;
+  int32_t dtype, z_dtype;
+  float scale;
+} lbca_step_args;
+
+LBCA_API int lbca_decode_step_workspace(const lbca_step_args* a, size_t* bytes);
+LBCA_API int lbca_decode_step(const lbca_step_args* a, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Decode attention: one query per sequence (mSeek "How LBCA works" step 4;
  * HCA "What is implemented" item 2; CSA "What is implemented" item 3).
  *

@@ -336,6 +336,44 @@ def test_prefill_backward_workspace_and_empty_calls():
     assert ok[0] == 0
 
 
+def _step(ws_query=False, **kw):
+    a = dict(q=FAKE, k_new=FAKE, v_new=FAKE, z_new=FAKE, raw_k=FAKE, raw_v=FAKE, raw_z=FAKE, bias=FAKE,
+             pooled_k=FAKE, pooled_v=FAKE, pos=FAKE, raw_pos_base=FAKE, sink=None, out=FAKE, lse=FAKE, batch=16,
+             q_heads=24, kv_heads=8, dim=128, block=64, window=128, ring=192, entries=520, dtype=1, z_dtype=0,
+             scale=0.088)
+    a.update(kw)
+    s = lbca.StepArgs(**a)
+    n = ctypes.c_size_t()
+    L = lbca.lib()
+    if ws_query:
+        return L.lbca_decode_step_workspace(ctypes.byref(s), ctypes.byref(n)), n.value
+    return L.lbca_decode_step(ctypes.byref(s), None, 0, None), 0
+
+
+@fake_ptr
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k_new=None), -1), (dict(z_new=None), -1), (dict(raw_z=None), -1),
+    (dict(bias=None), -1), (dict(raw_pos_base=None), -1), (dict(out=None), -1),
+    (dict(v_new=None), -1), (dict(pooled_v=None, raw_v=None), -1),   # the fused step has K and V series
+    (dict(ring=191), -1),                     # ring below window + block
+    (dict(ring=0), -1), (dict(q_heads=23), -1), (dict(z_dtype=3), -1),
+    (dict(dim=256), -2), (dict(dim=48), -2), (dict(dtype=0), -2),
+])
+def test_decode_step_validation(kw, code):
+    assert _step(ws_query=True, **kw)[0] == code
+    assert _step(**kw)[0] == code
+
+
+@fake_ptr
+def test_decode_step_workspace():
+    # batch 16 at the 32K layer shape: one workgroup pair per (sequence, KV head), no split partials
+    assert _step(ws_query=True) == (0, 0)
+    assert _step(batch=0)[0] == 0
+    # one sequence with room for 1300 entries: the rows are split (merge partials in the workspace)
+    st, n = _step(ws_query=True, batch=1, entries=1300)
+    assert st == 0 and n > 0
+
+
 def _index(ws=None, ws_bytes=0, **kw):
     a = dict(q_idx=FAKE, head_w=FAKE, keys=FAKE, pos=FAKE, out_idx=FAKE, out_score=None, batch=2,
              heads=8, dim=64, entries=32768, k=512, block=4, dtype=1)

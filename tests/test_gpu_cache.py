@@ -1,4 +1,5 @@
-"""GPU parity of the decode-time cache step (lbca_cache_append) through the C ABI.
+"""GPU parity of the decode-time cache step (lbca_cache_append) and of the
+fused decode step (lbca_decode_step) through the C ABI.
 
 Each case replays a decode loop token by token over a seeded history, with
 sequences that start at different steps (position < 0 = not started yet), on
@@ -243,3 +244,112 @@ def test_cache_overlap_csa_dual(lib):
                              1 / math.sqrt(d), sink=host(C["sink"]), **treat)
     check_bf16(host(o), ro, "decode over dual entries through the ring")
     check_bf16(host(lse), rl, "lse")
+
+
+# ---------------------------------------------------------------------------
+# the fused step: append, pool on completion and decode in one launch
+# ---------------------------------------------------------------------------
+def _step_state(B, H, ring, entries, d, xdt, zdt):
+    nanx = lambda: torch.full((B, H, 2 * ring, d), float("nan"), dtype=xdt, device=DEV)
+    st = dict(rk=nanx(), rv=nanx(), rz=torch.full((B, H, 2 * ring, d), float("nan"), dtype=zdt, device=DEV),
+              pk=torch.full((B, H, entries, d), 7.0, dtype=xdt, device=DEV),
+              rpb=torch.full((B,), -123, dtype=torch.int64, device=DEV))
+    st["pv"] = torch.full_like(st["pk"], 7.0)
+    return st
+
+
+def _run_steps(lib, L, qs, offsets, m, W, first_step, steps, fused, plain, check_at=(), on_check=None):
+    """Advance both states over the given steps: fused by lbca_decode_step, plain by
+    lbca_cache_append + lbca_attend_decode; the live sequences' outputs must be bitwise equal."""
+    k, v, z, bias = L["k"], L["v"], L["z"], L["bias"]
+    B = k.shape[0]
+    bidx = torch.arange(B, device=DEV)
+    for step in range(first_step, first_step + steps):
+        t_list = [step - o for o in offsets]
+        pos = torch.tensor(t_list, dtype=torch.int64, device=DEV)
+        ti = pos.clamp(min=0)
+        k_new, v_new, z_new = (x[bidx, :, ti].contiguous() for x in (k, v, z))
+        q = qs[step % qs.shape[0]]
+        of, lf = lib.decode_step(q, k_new, v_new, z_new, fused["rk"], fused["rv"], fused["rz"], bias, fused["pk"],
+                                 fused["pv"], pos, fused["rpb"], m, W)
+        lib.cache_append(k_new, z_new, plain["rk"], plain["rz"], bias, pos, plain["rpb"], m, W, O.EXCLUSIVE,
+                         plain["pk"], v_new=v_new, raw_v=plain["rv"], out_v=plain["pv"])
+        ou, lu = lib.attend_decode(q, plain["pk"], plain["rk"], pos, m, W, O.EXCLUSIVE, pooled_v=plain["pv"],
+                                   raw_v=plain["rv"], raw_pos_base=plain["rpb"])
+        live = [b for b, t in enumerate(t_list) if t >= 0]
+        assert torch.equal(of[live], ou[live]) and torch.equal(lf[live], lu[live]), f"fused step {step} differs"
+        assert torch.equal(fused["rpb"][live], plain["rpb"][live]), "raw base"
+        if step in check_at:
+            torch.cuda.synchronize()
+            on_check(step, t_list, q, of, lf)
+    return [first_step + steps - 1 - o for o in offsets]
+
+
+def _decode_vs_oracle(L, m, W, d, xdt):
+    k, v, z, bias = (host(L[n]) for n in ("k", "v", "z", "bias"))
+
+    def on_check(step, t_list, q, o, lse):
+        live = [b for b, t in enumerate(t_list) if t >= 0]
+        n_max = max(O.visible_range(t_list[b], m, W, O.EXCLUSIVE)[0] for b in live)
+        rk, rv = O.pool_single(k, z, bias, m, 0, max(n_max, 1), values=v)
+        ro, rl = O.attend_decode(host(q)[live], rk[live], rv[live], k[live], v[live], [t_list[b] for b in live], m,
+                                 W, O.EXCLUSIVE, 1 / math.sqrt(d))
+        check(xdt, host(o)[live], ro, f"fused decode step {step}")
+        check(xdt, host(lse)[live][..., None], rl[..., None], "lse")
+    return on_check
+
+
+@pytest.mark.parametrize("zdt,d,Hq", [("f32", 128, 6), ("bf16", 64, 4)])
+def test_decode_step_fused(lib, zdt, d, Hq):
+    # lbca_decode_step token by token from the start, ragged starts, ring not a
+    # multiple of the block: every step bitwise equal to the separate cache step +
+    # decode, decode against the oracle at the listed steps, the ring rows as the
+    # rule places them, and every block completed so far pooled bitwise as
+    # lbca_pool_blocks writes it from the linear history (later entries untouched)
+    H, m, W, ring, T = 2, 16, 32, 56, 420
+    offsets = [0, 37, 101]
+    B = len(offsets)
+    L = _dev(synth.lbca_layer(f"step-{zdt}-{d}", B, Hq, H, T, d, m, "bf16", zdt))
+    entries = T // m + 2
+    steps = 400
+    qs = synth.normal((steps, B, Hq, d), synth.seed_of("step-q", zdt, d), dtype="bf16", device=DEV)
+    xdt, zt = torch.bfloat16, L["z"].dtype
+    fused, plain = _step_state(B, H, ring, entries, d, xdt, zt), _step_state(B, H, ring, entries, d, xdt, zt)
+    check_at = {0, 1, 15, 16, 47, 48, 63, 64, 65, 130, 311, 312, steps - 1}
+    say(f"fused decode step bf16/{zdt} d={d}: {steps} steps")
+    t_end = _run_steps(lib, L, qs, offsets, m, W, 0, steps, fused, plain, check_at, _decode_vs_oracle(L, m, W, d, "bf16"))
+    torch.cuda.synchronize()
+    _check_ring(t_end, m, W, O.EXCLUSIVE, ring, fused["rk"], fused["rz"], fused["rpb"], L["k"], L["z"], fused["rv"],
+                L["v"])
+    ref_k = torch.full_like(fused["pk"], 7.0)
+    ref_v = torch.full_like(fused["pv"], 7.0)
+    lib.pool_blocks(L["k"], L["z"], L["bias"], m, 0, T // m, ref_k, v=L["v"], out_v=ref_v)
+    for b, t in enumerate(t_end):
+        done = (t + 1) // m                    # blocks completed by t
+        assert torch.equal(fused["pk"][b, :, :done], ref_k[b, :, :done])
+        assert torch.equal(fused["pv"][b, :, :done], ref_v[b, :, :done])
+        assert (fused["pk"][b, :, done:] == 7.0).all(), "blocks not completed yet are untouched"
+
+
+def test_decode_step_split_rows(lib):
+    # decode at t ~ 20000 (1250 pooled blocks): the rows are split across
+    # workgroups, so the step is the fused launch plus the merge; state set up as
+    # a prefill would leave it (every completed block pooled, the ring filled)
+    B, Hq, H, d, m, W, ring, t0, steps = 1, 6, 2, 128, 16, 128, 160, 20000, 40
+    T = t0 + steps
+    L = _dev(synth.lbca_layer("step-split", B, Hq, H, T, d, m, "bf16", "f32"))
+    entries = T // m + 1
+    qs = synth.normal((4, B, Hq, d), synth.seed_of("step-split-q"), dtype="bf16", device=DEV)
+    xdt, zt = torch.bfloat16, torch.float32
+    states = []
+    for _ in range(2):
+        st = _step_state(B, H, ring, entries, d, xdt, zt)
+        lib.pool_blocks(L["k"], L["z"], L["bias"], m, 0, t0 // m, st["pk"], v=L["v"], out_v=st["pv"])
+        s = torch.arange(t0 - ring + 1, t0, device=DEV)
+        for key, src in (("rk", "k"), ("rv", "v"), ("rz", "z")):
+            st[key][:, :, s % ring] = L[src][:, :, s]
+            st[key][:, :, s % ring + ring] = L[src][:, :, s]
+        states.append(st)
+    say(f"fused decode step with split rows: t from {t0}, {steps} steps")
+    _run_steps(lib, L, qs, [0], m, W, t0, steps, states[0], states[1], {t0, t0 + 1, t0 + 15, t0 + steps - 1},
+               _decode_vs_oracle(L, m, W, d, "bf16"))
