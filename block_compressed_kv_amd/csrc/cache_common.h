@@ -48,8 +48,11 @@ __device__ __forceinline__ void st16(T* r, int i, uint4 v) { reinterpret_cast<ui
 // the workgroup (member); wider workgroups' other threads pass member = false
 // and only take part in the barriers.  AT_COMPLETION pools a block on the step
 // of its last token (lbca_decode_step) instead of the step that makes it
-// visible (lbca_cache_append).
-template <typename TX, typename TZ, bool HAS_V, bool TREAT, bool DUAL, bool AT_COMPLETION>
+// visible (lbca_cache_append).  COPY: the token append and the raw base (no
+// barrier: the first L threads' work); POOL: the due block (every thread of the
+// workgroup calls it when it pools, for the barriers).
+template <typename TX, typename TZ, bool HAS_V, bool TREAT, bool DUAL, bool AT_COMPLETION, bool COPY = true,
+          bool POOL = true>
 __device__ __forceinline__ void cache_row(const CacheParams& p, unsigned row, float (*part)[256], bool member) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int L = p.lanes_per_row;
@@ -68,7 +71,7 @@ __device__ __forceinline__ void cache_row(const CacheParams& p, unsigned row, fl
   const TX* xbs = static_cast<const TX*>(p.xb_new) + src;
   const TZ* zbs = static_cast<const TZ*>(p.zb_new) + src;
   uint4 x0 = {}, x1 = {}, v0 = {}, v1 = {}, z0 = {}, z1 = {}, xb0 = {}, xb1 = {}, zb0 = {}, zb1 = {};
-  if (member && phase == 0) {
+  if (COPY && member && phase == 0) {
     x0 = ld16(xs, 0);
     if constexpr (X2) x1 = ld16(xs, 1);
     if constexpr (HAS_V) {
@@ -90,7 +93,7 @@ __device__ __forceinline__ void cache_row(const CacheParams& p, unsigned row, fl
 
   // 1. the new token into both rows of its slot
   const int64_t slot = t % ring;
-  if (member && phase == 0) {
+  if (COPY && member && phase == 0) {
     const int64_t d0 = series + slot * dim, d1 = d0 + ring * dim;
     TX* rx = static_cast<TX*>(p.raw_x);
     TZ* rz = static_cast<TZ*>(p.raw_z);
@@ -135,7 +138,8 @@ __device__ __forceinline__ void cache_row(const CacheParams& p, unsigned row, fl
   // 2. the raw base that maps t's raw span onto ring rows
   int64_t n_pooled, raw_begin;
   visible_range(t, p.m, p.W, p.mode, &n_pooled, &raw_begin);
-  if (h == 0 && tid == 0) p.raw_pos_base[b] = raw_begin - raw_begin % ring;
+  if (COPY && h == 0 && tid == 0) p.raw_pos_base[b] = raw_begin - raw_begin % ring;
+  if constexpr (!POOL) return;
   // 3. the block that becomes visible at t (or, AT_COMPLETION, whose last token is t), if any
   const int64_t x = (p.mode == LBCA_EXCLUSIVE && !AT_COMPLETION) ? t + 1 - p.W : t + 1;
   if (x <= 0 || x % p.m != 0) return;

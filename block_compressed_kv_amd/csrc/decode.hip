@@ -204,11 +204,16 @@ __device__ __forceinline__ void load_tile(Tile<D, R, DS, SHARED>& T, const int* 
   }
 }
 
-// One decode workgroup's work (workgroup id bid); FUSED: the launch also runs
-// the cache step (lbca_decode_step), so the raw row at the position is read
-// from the new token's input and the raw base follows from the position.
-template <int D, int R, int NW, int DS, bool SHARED, int RD, bool TREAT, bool SPEC, bool FUSED>
-__device__ __forceinline__ void decode_body(const DecodeParams& p, unsigned bid) {
+// One decode workgroup's work (workgroup id bid).  FUSED (lbca_decode_step):
+// the raw row at the position is read from the new token's input and the raw
+// base follows from the position; the workgroup that owns split 0 of a
+// (sequence, KV head) also appends the token to the ring (cp): its rows are
+// requested first and stored once the position is known; it returns that
+// cache row (else -1) so the caller can pool a completed block after the
+// decode.
+template <int D, int R, int NW, int DS, bool SHARED, int RD, bool TREAT, bool SPEC, bool FUSED,
+          typename TZ = float>
+__device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, const CacheParams* cp = nullptr) {
   constexpr int KS = D / 32, NH = R / 16;
   constexpr int DV = D / DS;                         // output dims of this workgroup
   constexpr int KV = DV / 32, DT = DV / 16, PITCH = DV + 16;
@@ -224,6 +229,9 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, unsigned bid)
   __shared__ int s_ids[SPEC ? 1 : kSelLds];        // selected ids of this workgroup's range
 
   preload_params(p);
+  if constexpr (FUSED)  // the cache-step fields too, in the same batch of scalar loads
+    asm volatile("" ::"s"(cp->x_new), "s"(cp->v_new), "s"(cp->z_new), "s"(cp->raw_x), "s"(cp->raw_v),
+                 "s"(cp->raw_z), "s"(cp->raw_pos_base), "s"(cp->ring), "s"(p.ring));
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile choices stay scalar
   const int n = lane & 15, kq = lane >> 4;
@@ -234,7 +242,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, unsigned bid)
     dh = rest % DS;
     u = (rest / DS) * 8 + (bid & 7);
   }
-  if (u >= (unsigned)p.units * (unsigned)p.splits) return;  // padding of the XCD mapping
+  if (u >= (unsigned)p.units * (unsigned)p.splits) return -1;  // padding of the XCD mapping
   const int split = (int)(u % (unsigned)p.splits);
   const unsigned unit = u / (unsigned)p.splits;
   const unsigned uy = (unsigned)(p.hkv * p.head_groups);
@@ -247,6 +255,22 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, unsigned bid)
   const int nvalid = (int)(p.G - slot0 < 16 ? p.G - slot0 : 16);
   const int64_t head0 = kvh * p.G + slot0;  // first query head of the unit
   const bool head_ok = n < nvalid;
+  const int own_row = (FUSED && split == 0 && dh == 0 && hg == 0) ? (int)(b * p.hkv + kvh) : -1;
+  // fused step: the owner's first dim/8 lanes request the new token's rows
+  // before anything else, so the wait for them is covered by the wait for the
+  // position (vector loads return in order)
+  uint4 tok_k = {}, tok_v = {}, tok_z0 = {}, tok_z1 = {};
+  const bool tok_lane = FUSED && own_row >= 0 && tid < D / 8;
+  if constexpr (FUSED) {
+    if (tok_lane) {
+      const int64_t src = (int64_t)own_row * D + 8 * tid;
+      tok_k = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(cp->x_new) + src);
+      tok_v = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(cp->v_new) + src);
+      const TZ* zs = static_cast<const TZ*>(cp->z_new) + src;
+      tok_z0 = reinterpret_cast<const uint4*>(zs)[0];
+      if constexpr (sizeof(TZ) == 4) tok_z1 = reinterpret_cast<const uint4*>(zs)[1];
+    }
+  }
 
   // the position first: it is waited for after the first rows are requested
   const EarlyI64 e_pos = load_early(p.pos + b);
@@ -321,13 +345,33 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, unsigned bid)
     base = p.rpb ? uniform_value(e_base) : 0;
   }
   const SeqView sv = seq_view(p, b, uniform_value(e_pos), base);
+  if constexpr (FUSED) {  // the token into both ring rows of its slot, and the raw base (lbca_cache_append's rule)
+    if (tok_lane && sv.t >= 0) {
+      const int64_t ring = cp->ring, slot = sv.t % ring;
+      const int64_t d0 = ((int64_t)own_row * 2 * ring + slot) * D + 8 * tid, d1 = d0 + ring * D;
+      bf16_t* rk = static_cast<bf16_t*>(cp->raw_x);
+      bf16_t* rv = static_cast<bf16_t*>(cp->raw_v);
+      TZ* rz = static_cast<TZ*>(cp->raw_z);
+      *reinterpret_cast<uint4*>(rk + d0) = tok_k;
+      *reinterpret_cast<uint4*>(rk + d1) = tok_k;
+      *reinterpret_cast<uint4*>(rv + d0) = tok_v;
+      *reinterpret_cast<uint4*>(rv + d1) = tok_v;
+      reinterpret_cast<uint4*>(rz + d0)[0] = tok_z0;
+      reinterpret_cast<uint4*>(rz + d1)[0] = tok_z0;
+      if constexpr (sizeof(TZ) == 4) {
+        reinterpret_cast<uint4*>(rz + d0)[1] = tok_z1;
+        reinterpret_cast<uint4*>(rz + d1)[1] = tok_z1;
+      }
+      if (kvh == 0 && tid == 0) cp->raw_pos_base[b] = sv.raw_begin - sv.raw_begin % ring;
+    }
+  }
   if (!sv.ok) {  // rows do not fit the buffers: NaN, written once per unit and slice
     if (split == 0) {
       for (int i = tid; i < nvalid * DV; i += blockDim.x)
         p.out[(b * p.hq + head0 + i / DV) * D + dv0 + i % DV] = __builtin_nanf("");
       if (p.lse && dh == 0 && tid < nvalid) p.lse[b * p.hq + head0 + tid] = __builtin_nanf("");
     }
-    return;
+    return own_row;
   }
   if constexpr (TREAT) {
     if constexpr (RD > 0) {
@@ -605,7 +649,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, unsigned bid)
       }
     }
     if (p.lse && dh == 0 && tid < nvalid) p.lse[b * p.hq + head0 + tid] = s_lse[tid];
-    return;
+    return own_row;
   }
   // ---- split partial to the workspace; decode_merge_kernel combines the splits ----
   const int64_t part = (int64_t)unit * p.splits + split;
@@ -615,6 +659,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, unsigned bid)
     p.ws_ml[(part * 16 + tid) * 2] = s_M[tid];
     p.ws_ml[(part * 16 + tid) * 2 + 1] = s_L[tid];
   }
+  return own_row;
 }
 
 // Combine the splits of one unit (16 query-head slots) over one chunk of CK
@@ -633,28 +678,28 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
   decode_body<D, R, NW, DS, SHARED, RD, TREAT, SPEC, false>(p, blockIdx.x);
 }
 
-// Fused decode step (lbca_decode_step, EXCLUSIVE rule, K and V series):
-// workgroups [0, n_dec) decode exactly as decode_kernel, except that each
-// reads its position's raw row from the new token's input; the others run the
-// cache step of one (sequence, KV head) row each with their first 256 threads
-// (append to the ring; pool the block the token completes, which no query of
-// this step can see yet: under EXCLUSIVE a block is visible only once it is
-// wholly older than the window).  Nothing one role writes is read by the other.
+// Fused decode step (lbca_decode_step, EXCLUSIVE rule, K and V series): the
+// decode launch of decode_kernel, each workgroup reading its position's raw
+// row from the new token's input.  The workgroup that owns split 0 of a
+// (sequence, KV head) also runs that row's cache step: the token append, and,
+// on the step whose token completes a block, the pooling of that block after
+// its decode work, with its first 256
+// threads (bitwise as lbca_pool_blocks).  No query of the step reads what the
+// cache step writes: the row at the position comes from the input, and under
+// EXCLUSIVE a block is visible only once it is wholly older than the window.
+// (Separate cache workgroups would be given the decode's registers and could
+// not share a CU with a decode workgroup.)
 struct StepParams {
   DecodeParams d;
   CacheParams c;
-  unsigned n_dec;
 };
 
 template <int D, int R, int NW, int DS, bool SPEC, typename TZ>
 __global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepParams sp) {
   static_assert(NW * 64 >= 256, "the cache step needs 256 threads");
   __shared__ float part[32][256];  // the cache step's cross-wave phase merge
-  if (blockIdx.x >= sp.n_dec) {
-    cache_row<bf16_t, TZ, true, false, false, true>(sp.c, blockIdx.x - sp.n_dec, part, threadIdx.x < 256);
-    return;
-  }
-  decode_body<D, R, NW, DS, false, 0, false, SPEC, true>(sp.d, blockIdx.x);
+  const int row = decode_body<D, R, NW, DS, false, 0, false, SPEC, true, TZ>(sp.d, blockIdx.x, &sp.c);
+  if (row >= 0) cache_row<bf16_t, TZ, true, false, false, true, false, true>(sp.c, row, part, threadIdx.x < 256);
 }
 
 template <bool NORM>
@@ -1030,8 +1075,7 @@ hipError_t launch_decode_step(const lbca_decode_args& da, const lbca_cache_args&
   c.eps = -1.f;
   const size_t pairs = units * plan.splits;
   const int ds = plan.dim_splits;
-  sp.n_dec = (unsigned)(ds == 1 ? pairs : (pairs + 7) / 8 * 8 * ds);
-  const unsigned grid = sp.n_dec + (unsigned)(ca.batch * ca.heads);
+  const unsigned grid = (unsigned)(ds == 1 ? pairs : (pairs + 7) / 8 * 8 * ds);
   const bool spec = plan.splits == 1;
   const bool zf = ca.z_dtype == LBCA_F32;
   switch (da.dim * 4 + ds) {
