@@ -6,7 +6,9 @@
 // clear reference): a query sees every completed summary older than its
 // window plus its exact raw window, never a summary holding a later token.
 //
-// bf16 path (MFMA, a dense contraction).  A workgroup of 8 waves (two per
+// bf16 path (MFMA, a dense contraction).  At 128 dims prefill128_kernel
+// (below, on 32x32x16 MFMAs) runs; prefill_kernel, described here, serves 64
+// dims.  A workgroup of 8 waves (two per
 // SIMD, so one wave's softmax arithmetic runs beside the other's MFMAs) owns
 // one (sequence, KV head) and 256 consecutive rows of the flattened (position,
 // query head in the GQA group) space; each wave holds 32 of those rows (two
