@@ -144,6 +144,9 @@ class DecodeLayer:
         e1.record()
         if pool_timer is not None:
             pool_timer.append((e0, e1, B * HKV * (N_POOLED - 1) * M * D * (2 + 2 + 4)))
+        # the raw window in buffers of its own, as a serving cache holds it (the
+        # ring of lbca_cache_append): views into the 32K history would scatter
+        # each (sequence, head)'s rows 8 MB apart
         self.rk = full["k"][:, :, RAW0:].contiguous()
         self.rv = full["v"][:, :, RAW0:].contiguous()
         self.z = full["z"][:, :, RAW0:].contiguous()
@@ -384,7 +387,7 @@ def run_prefill(reps):
     pv = torch.zeros_like(pk)
     out = torch.empty((1, P_CTX, HQ, D), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((1, P_CTX, HQ), dtype=torch.float32, device=dev)
-    qs = [L["q"][:, c:c + P_CHUNK].contiguous() for c in range(0, P_CTX, P_CHUNK)]
+    qs = [L["q"][:, c:c + P_CHUNK] for c in range(0, P_CTX, P_CHUNK)]
     plan = []
     done = 0
     for i, c0 in enumerate(range(0, P_CTX, P_CHUNK)):
@@ -478,7 +481,7 @@ def run_hca(reps):
     g_pool = capture(pool)
     ms_pool = time_graph(g_pool, 3)
     pool_bytes = B * T * X_D * 2 * 2 + B * N * X_D * 2
-    raw = H["c"][:, :, T - W:].contiguous()
+    raw = H["c"][:, :, T - W:].contiguous()  # the window in its own buffer, as a serving cache holds it
     pos = torch.full((B,), T - 1, dtype=torch.int64, device=dev)
     rpb = torch.full((B,), T - W, dtype=torch.int64, device=dev)
     sink = H["sink"]
@@ -554,7 +557,7 @@ def run_csa(reps):
               keys=synth.normal((B, N, CSA_DI), synth.seed_of(tg, "keys"), dtype="bf16", device=dev),
               q=synth.normal((B, CH, X_HQ, X_D), synth.seed_of(tg, "q"), dtype="bf16", device=dev))
     rbase = t0 - W + 1
-    rawc = C["ca"][:, 0, rbase:].contiguous()
+    rawc = C["ca"][:, 0, rbase:].contiguous()  # the chunk's raw rows in their own buffer
     pf_out = torch.empty((B, CH, X_HQ, X_D), device=dev)
     pf_lse = torch.empty((B, CH, X_HQ), device=dev)
     pf_idx = torch.empty((B, CH, k), dtype=torch.int32, device=dev)
@@ -570,7 +573,7 @@ def run_csa(reps):
     sp_index_flop = B * n_vis_sum * CSA_HI * CSA_DI * 2
     sp_attn_flop = B * CH * X_HQ * (k + W) * X_D * 4
     del pf, rawc, pf_out, pf_lse, pf_idx, ws_pf, g_sp, pf_args, pf_kw
-    raw = C["ca"][:, :, T - W:].contiguous()
+    raw = C["ca"][:, :, T - W:].contiguous()  # the window in its own buffer, as a serving cache holds it
     sink = C["sink"]
     del C, g_pool
     torch.cuda.empty_cache()

@@ -35,6 +35,69 @@ int check_treatment(float eps, int32_t rope_dims, float rope_base, int64_t dim) 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LBCA_OK : LBCA_ERR_HIP; }
 
+int64_t esize(int32_t dtype) { return dtype == LBCA_F32 ? 4 : 2; }
+
+// One tensor argument's strides: with all used strides zero, fills in the
+// dense row-major ones for outer extents ext (outermost first) and feature dim
+// d; then checks the rules of lbca_strides (non-negative, rows 16-byte
+// aligned, every element within kMaxElems of the base and, for an output, no
+// two elements at one address).  An absent tensor (ptr NULL) is not checked.
+int fix_strides(lbca_strides& st, const void* ptr, std::initializer_list<int64_t> ext, int64_t d, int32_t dtype,
+                bool output) {
+  const int n = (int)ext.size();
+  const int64_t* e = ext.begin();
+  bool zero = true;
+  for (int i = 0; i < n; ++i) zero = zero && st.s[i] == 0;
+  if (zero) {
+    int64_t s = d;
+    for (int i = n - 1; i >= 0; --i) {
+      st.s[i] = s;
+      if (e[i] > 1) s = s <= kMaxElems / e[i] ? s * e[i] : kMaxElems + 1;
+    }
+  }
+  for (int i = n; i < 3; ++i) st.s[i] = 0;
+  if (!ptr) return LBCA_OK;
+  for (int i = 1; i < n; ++i)
+    if (st.s[i] >= (int64_t(1) << 31)) return LBCA_ERR_UNSUPPORTED;  // the kernels hold inner strides in 32 bits
+  bool empty = d == 0;
+  for (int i = 0; i < n; ++i) {
+    if (st.s[i] < 0 || st.s[i] > kMaxElems || (st.s[i] * esize(dtype)) % 16 != 0) return LBCA_ERR_INVALID_ARG;
+    empty = empty || e[i] == 0;
+  }
+  if (empty) return LBCA_OK;
+  int64_t far = d;  // one past the furthest element
+  for (int i = 0; i < n; ++i) {
+    if (e[i] > 1 && st.s[i] > (kMaxElems - far) / (e[i] - 1)) return LBCA_ERR_INVALID_ARG;
+    far += (e[i] - 1) * st.s[i];
+  }
+  if (output) {  // dimensions of extent > 1 in stride order, each past everything inside it
+    int idx[3], k = 0;
+    for (int i = 0; i < n; ++i)
+      if (e[i] > 1) idx[k++] = i;
+    for (int i = 1; i < k; ++i)
+      for (int j = i; j > 0 && st.s[idx[j]] < st.s[idx[j - 1]]; --j) {
+        const int t = idx[j];
+        idx[j] = idx[j - 1];
+        idx[j - 1] = t;
+      }
+    int64_t cover = d;
+    for (int j = 0; j < k; ++j) {
+      if (st.s[idx[j]] < cover) return LBCA_ERR_INVALID_ARG;
+      cover += (e[idx[j]] - 1) * st.s[idx[j]];
+    }
+  }
+  return LBCA_OK;
+}
+
+// Elements spanned by `rows` rows of row stride sr (one sequence and head's slice).
+int64_t slice_span(int64_t rows, int64_t sr, int64_t d) { return rows > 0 ? (rows - 1) * sr + d : 0; }
+
+#define LBCA_TRY(x)                 \
+  do {                              \
+    const int st_ = (x);            \
+    if (st_ != LBCA_OK) return st_; \
+  } while (0)
+
 }  // namespace
 
 extern "C" {
@@ -70,8 +133,23 @@ int lbca_visible_range(int64_t t, int64_t m, int64_t W, int32_t mode, int64_t* n
 }
 
 // ---------------------------------------------------------------------------
-int lbca_pool_blocks(const lbca_pool_args* a, void* stream) {
-  if (!a || !a->x || !a->z || !a->bias || !a->out_x) return LBCA_ERR_INVALID_ARG;
+static int strides_pool(lbca_pool_args* a) {
+  const int64_t B = a->batch, H = a->heads, T = a->tokens, N = a->entries, d = a->dim;
+  LBCA_TRY(fix_strides(a->x_st, a->x, {B, H, T}, d, a->x_dtype, false));
+  LBCA_TRY(fix_strides(a->v_st, a->v, {B, H, T}, d, a->x_dtype, false));
+  LBCA_TRY(fix_strides(a->z_st, a->z, {B, H, T}, d, a->z_dtype, false));
+  LBCA_TRY(fix_strides(a->xb_st, a->xb, {B, H, T}, d, a->x_dtype, false));
+  LBCA_TRY(fix_strides(a->zb_st, a->zb, {B, H, T}, d, a->z_dtype, false));
+  LBCA_TRY(fix_strides(a->out_x_st, a->out_x, {B, H, N}, d, a->x_dtype, true));
+  LBCA_TRY(fix_strides(a->out_v_st, a->out_v, {B, H, N}, d, a->x_dtype, true));
+  return LBCA_OK;
+}
+
+int lbca_pool_blocks(const lbca_pool_args* ap, void* stream) {
+  if (!ap) return LBCA_ERR_INVALID_ARG;
+  lbca_pool_args args = *ap;
+  lbca_pool_args* a = &args;
+  if (!a->x || !a->z || !a->bias || !a->out_x) return LBCA_ERR_INVALID_ARG;
   if ((a->v == nullptr) != (a->out_v == nullptr)) return LBCA_ERR_INVALID_ARG;
   const bool dual = a->xb != nullptr || a->zb != nullptr || a->bias_b != nullptr;
   if (dual && !(a->xb && a->zb && a->bias_b)) return LBCA_ERR_INVALID_ARG;
@@ -101,13 +179,32 @@ int lbca_pool_blocks(const lbca_pool_args* a, void* stream) {
     const int64_t hi = a->block_end * a->block - a->pos_base;
     if (lo < 0 || hi > a->tokens) return LBCA_ERR_INVALID_ARG;
   }
+  LBCA_TRY(strides_pool(a));
   if (a->batch == 0 || a->block_end == a->block_begin) return LBCA_OK;
   return hip_status(lbca::launch_pool(*a, static_cast<hipStream_t>(stream)));
 }
 
 // ---------------------------------------------------------------------------
-static int validate_pool_grad(const lbca_pool_grad_args* a) {
-  if (!a || !a->x || !a->z || !a->bias || !a->grad_x || !a->dx || !a->dz || !a->dbias)
+static int strides_pool_grad(lbca_pool_grad_args* a) {
+  const int64_t B = a->batch, H = a->heads, T = a->tokens, N = a->entries, d = a->dim;
+  const int32_t xt = a->x_dtype, zt = a->z_dtype;
+  LBCA_TRY(fix_strides(a->x_st, a->x, {B, H, T}, d, xt, false));
+  LBCA_TRY(fix_strides(a->v_st, a->v, {B, H, T}, d, xt, false));
+  LBCA_TRY(fix_strides(a->z_st, a->z, {B, H, T}, d, zt, false));
+  LBCA_TRY(fix_strides(a->xb_st, a->xb, {B, H, T}, d, xt, false));
+  LBCA_TRY(fix_strides(a->zb_st, a->zb, {B, H, T}, d, zt, false));
+  LBCA_TRY(fix_strides(a->grad_x_st, a->grad_x, {B, H, N}, d, xt, false));
+  LBCA_TRY(fix_strides(a->grad_v_st, a->grad_v, {B, H, N}, d, xt, false));
+  LBCA_TRY(fix_strides(a->dx_st, a->dx, {B, H, T}, d, xt, true));
+  LBCA_TRY(fix_strides(a->dv_st, a->dv, {B, H, T}, d, xt, true));
+  LBCA_TRY(fix_strides(a->dz_st, a->dz, {B, H, T}, d, zt, true));
+  LBCA_TRY(fix_strides(a->dxb_st, a->dxb, {B, H, T}, d, xt, true));
+  LBCA_TRY(fix_strides(a->dzb_st, a->dzb, {B, H, T}, d, zt, true));
+  return LBCA_OK;
+}
+
+static int validate_pool_grad(lbca_pool_grad_args* a) {
+  if (!a->x || !a->z || !a->bias || !a->grad_x || !a->dx || !a->dz || !a->dbias)
     return LBCA_ERR_INVALID_ARG;
   const bool has_v = a->v != nullptr;
   if ((a->grad_v != nullptr) != has_v || (a->dv != nullptr) != has_v) return LBCA_ERR_INVALID_ARG;
@@ -140,19 +237,24 @@ static int validate_pool_grad(const lbca_pool_grad_args* a) {
     const int64_t hi = a->block_end * a->block - a->pos_base;
     if (lo < 0 || hi > a->tokens) return LBCA_ERR_INVALID_ARG;
   }
-  return LBCA_OK;
+  return strides_pool_grad(a);
 }
 
-int lbca_pool_blocks_backward_workspace(const lbca_pool_grad_args* a, size_t* bytes) {
-  if (!bytes) return LBCA_ERR_INVALID_ARG;
+int lbca_pool_blocks_backward_workspace(const lbca_pool_grad_args* ap, size_t* bytes) {
+  if (!bytes || !ap) return LBCA_ERR_INVALID_ARG;
+  lbca_pool_grad_args args = *ap;
+  lbca_pool_grad_args* a = &args;
   const int st = validate_pool_grad(a);
   if (st != LBCA_OK) return st;
   *bytes = lbca::pool_grad_workspace_bytes(*a);
   return LBCA_OK;
 }
 
-int lbca_pool_blocks_backward(const lbca_pool_grad_args* a, void* workspace, size_t workspace_bytes,
+int lbca_pool_blocks_backward(const lbca_pool_grad_args* ap, void* workspace, size_t workspace_bytes,
                               void* stream) {
+  if (!ap) return LBCA_ERR_INVALID_ARG;
+  lbca_pool_grad_args args = *ap;
+  lbca_pool_grad_args* a = &args;
   const int st = validate_pool_grad(a);
   if (st != LBCA_OK) return st;
   const size_t need = lbca::pool_grad_workspace_bytes(*a);
@@ -161,8 +263,26 @@ int lbca_pool_blocks_backward(const lbca_pool_grad_args* a, void* workspace, siz
 }
 
 // ---------------------------------------------------------------------------
-static int validate_cache(const lbca_cache_args* a) {
-  if (!a || !a->x_new || !a->z_new || !a->raw_x || !a->raw_z || !a->bias || !a->out_x || !a->pos ||
+static int strides_cache(lbca_cache_args* a) {
+  const int64_t B = a->batch, H = a->heads, R = 2 * a->ring, N = a->entries, d = a->dim;
+  const int32_t xt = a->x_dtype, zt = a->z_dtype;
+  LBCA_TRY(fix_strides(a->x_new_st, a->x_new, {B, H}, d, xt, false));
+  LBCA_TRY(fix_strides(a->v_new_st, a->v_new, {B, H}, d, xt, false));
+  LBCA_TRY(fix_strides(a->z_new_st, a->z_new, {B, H}, d, zt, false));
+  LBCA_TRY(fix_strides(a->xb_new_st, a->xb_new, {B, H}, d, xt, false));
+  LBCA_TRY(fix_strides(a->zb_new_st, a->zb_new, {B, H}, d, zt, false));
+  LBCA_TRY(fix_strides(a->raw_x_st, a->raw_x, {B, H, R}, d, xt, true));
+  LBCA_TRY(fix_strides(a->raw_v_st, a->raw_v, {B, H, R}, d, xt, true));
+  LBCA_TRY(fix_strides(a->raw_z_st, a->raw_z, {B, H, R}, d, zt, true));
+  LBCA_TRY(fix_strides(a->raw_xb_st, a->raw_xb, {B, H, R}, d, xt, true));
+  LBCA_TRY(fix_strides(a->raw_zb_st, a->raw_zb, {B, H, R}, d, zt, true));
+  LBCA_TRY(fix_strides(a->out_x_st, a->out_x, {B, H, N}, d, xt, true));
+  LBCA_TRY(fix_strides(a->out_v_st, a->out_v, {B, H, N}, d, xt, true));
+  return LBCA_OK;
+}
+
+static int validate_cache(lbca_cache_args* a) {
+  if (!a->x_new || !a->z_new || !a->raw_x || !a->raw_z || !a->bias || !a->out_x || !a->pos ||
       !a->raw_pos_base)
     return LBCA_ERR_INVALID_ARG;
   const bool has_v = a->v_new != nullptr;
@@ -195,10 +315,13 @@ static int validate_cache(const lbca_cache_args* a) {
       !aligned16(a->out_v) || !aligned16(a->xb_new) || !aligned16(a->zb_new) || !aligned16(a->raw_xb) ||
       !aligned16(a->raw_zb) || !aligned16(a->bias_b))
     return LBCA_ERR_INVALID_ARG;
-  return LBCA_OK;
+  return strides_cache(a);
 }
 
-int lbca_cache_append(const lbca_cache_args* a, void* stream) {
+int lbca_cache_append(const lbca_cache_args* ap, void* stream) {
+  if (!ap) return LBCA_ERR_INVALID_ARG;
+  lbca_cache_args args = *ap;
+  lbca_cache_args* a = &args;
   const int st = validate_cache(a);
   if (st != LBCA_OK) return st;
   if (a->batch == 0) return LBCA_OK;
@@ -206,8 +329,28 @@ int lbca_cache_append(const lbca_cache_args* a, void* stream) {
 }
 
 // ---------------------------------------------------------------------------
-static int validate_decode(const lbca_decode_args* a) {
-  if (!a || !a->q || !a->pooled_k || !a->raw_k || !a->pos || !a->out) return LBCA_ERR_INVALID_ARG;
+static int strides_decode(lbca_decode_args* a) {
+  const int64_t B = a->batch, Hq = a->q_heads, Hk = a->kv_heads, d = a->dim;
+  const int32_t dt = a->dtype;
+  LBCA_TRY(fix_strides(a->q_st, a->q, {B, Hq}, d, dt, false));
+  LBCA_TRY(fix_strides(a->pooled_k_st, a->pooled_k, {B, Hk, a->entries}, d, dt, false));
+  LBCA_TRY(fix_strides(a->pooled_v_st, a->pooled_v, {B, Hk, a->entries}, d, dt, false));
+  LBCA_TRY(fix_strides(a->raw_k_st, a->raw_k, {B, Hk, a->raw_rows}, d, dt, false));
+  LBCA_TRY(fix_strides(a->raw_v_st, a->raw_v, {B, Hk, a->raw_rows}, d, dt, false));
+  LBCA_TRY(fix_strides(a->out_st, a->out, {B, Hq}, d, LBCA_F32, true));
+  if (dt == LBCA_BF16) {
+    // rows are addressed by 32-bit byte offsets within one (sequence, KV head) slice
+    const int64_t lim = int64_t(1) << 30;
+    if (slice_span(a->entries, a->pooled_k_st.s[2], d) >= lim ||
+        slice_span(a->entries, a->pooled_v_st.s[2], d) >= lim ||
+        slice_span(a->raw_rows, a->raw_k_st.s[2], d) >= lim || slice_span(a->raw_rows, a->raw_v_st.s[2], d) >= lim)
+      return LBCA_ERR_UNSUPPORTED;
+  }
+  return LBCA_OK;
+}
+
+static int validate_decode(lbca_decode_args* a) {
+  if (!a->q || !a->pooled_k || !a->raw_k || !a->pos || !a->out) return LBCA_ERR_INVALID_ARG;
   if ((a->pooled_v == nullptr) != (a->raw_v == nullptr)) return LBCA_ERR_INVALID_ARG;
   if (!is_dtype(a->dtype)) return LBCA_ERR_INVALID_ARG;
   if (a->batch < 0 || a->q_heads < 1 || a->kv_heads < 1 || a->q_heads % a->kv_heads != 0)
@@ -232,8 +375,7 @@ static int validate_decode(const lbca_decode_args* a) {
     if (!(a->rope_dims == 0 || a->rope_dims == 64 || a->rope_dims == 128)) return LBCA_ERR_UNSUPPORTED;
     // rows are addressed by 32-bit byte offsets within one (sequence, KV head)
     // slice; the merge grid's y/x carry batch and (KV head, head group)
-    if (a->entries * a->dim * 2 >= (int64_t(1) << 31) || a->raw_rows * a->dim * 2 >= (int64_t(1) << 31) ||
-        a->k_sel > 32768 || a->batch > 65535 || a->kv_heads * ((G + 15) / 16) > 65535)
+    if (a->k_sel > 32768 || a->batch > 65535 || a->kv_heads * ((G + 15) / 16) > 65535)
       return LBCA_ERR_UNSUPPORTED;
   } else {
     if (a->dim % 64 != 0 || a->dim > 512) return LBCA_ERR_UNSUPPORTED;
@@ -245,19 +387,24 @@ static int validate_decode(const lbca_decode_args* a) {
   // the selected ids of one workgroup's row range are staged in LDS; the
   // planner reports sizes that no split count (at most 64) can cover
   if (lbca::plan_decode(*a).unsupported) return LBCA_ERR_UNSUPPORTED;
-  return LBCA_OK;
+  return strides_decode(a);
 }
 
-int lbca_attend_decode_workspace(const lbca_decode_args* a, size_t* bytes) {
-  if (!bytes) return LBCA_ERR_INVALID_ARG;
+int lbca_attend_decode_workspace(const lbca_decode_args* ap, size_t* bytes) {
+  if (!bytes || !ap) return LBCA_ERR_INVALID_ARG;
+  lbca_decode_args args = *ap;
+  lbca_decode_args* a = &args;
   int st = validate_decode(a);
   if (st != LBCA_OK) return st;
   *bytes = lbca::plan_decode(*a).ws_bytes;
   return LBCA_OK;
 }
 
-int lbca_attend_decode(const lbca_decode_args* a, void* workspace, size_t workspace_bytes,
+int lbca_attend_decode(const lbca_decode_args* ap, void* workspace, size_t workspace_bytes,
                        void* stream) {
+  if (!ap) return LBCA_ERR_INVALID_ARG;
+  lbca_decode_args args = *ap;
+  lbca_decode_args* a = &args;
   int st = validate_decode(a);
   if (st != LBCA_OK) return st;
   const lbca::DecodePlan plan = lbca::plan_decode(*a);
@@ -267,7 +414,10 @@ int lbca_attend_decode(const lbca_decode_args* a, void* workspace, size_t worksp
   return hip_status(lbca::launch_decode(*a, plan, workspace, static_cast<hipStream_t>(stream)));
 }
 
-int lbca_attend_decode_noalloc(const lbca_decode_args* a, void* stream) {
+int lbca_attend_decode_noalloc(const lbca_decode_args* ap, void* stream) {
+  if (!ap) return LBCA_ERR_INVALID_ARG;
+  lbca_decode_args args = *ap;
+  lbca_decode_args* a = &args;
   int st = validate_decode(a);
   if (st != LBCA_OK) return st;
   const lbca::DecodePlan plan = lbca::plan_decode(*a);
@@ -289,6 +439,8 @@ static void step_parts(const lbca_step_args* a, lbca_decode_args* d, lbca_cache_
   d->entries = a->entries; d->raw_rows = 2 * a->ring; d->k_sel = 0;
   d->block = a->block; d->window = a->window; d->mode = LBCA_EXCLUSIVE; d->dtype = a->dtype;
   d->scale = a->scale; d->rmsnorm_eps = -1.f; d->rope_dims = 0; d->rope_base = 0.f;
+  d->q_st = a->q_st; d->pooled_k_st = a->pooled_k_st; d->pooled_v_st = a->pooled_v_st;
+  d->raw_k_st = a->raw_k_st; d->raw_v_st = a->raw_v_st; d->out_st = a->out_st;
   *c = lbca_cache_args{};
   c->x_new = a->k_new; c->v_new = a->v_new; c->z_new = a->z_new;
   c->raw_x = a->raw_k; c->raw_v = a->raw_v; c->raw_z = a->raw_z; c->bias = a->bias;
@@ -296,6 +448,9 @@ static void step_parts(const lbca_step_args* a, lbca_decode_args* d, lbca_cache_
   c->batch = a->batch; c->heads = a->kv_heads; c->dim = a->dim; c->block = a->block; c->window = a->window;
   c->ring = a->ring; c->entries = a->entries; c->mode = LBCA_EXCLUSIVE; c->x_dtype = a->dtype;
   c->z_dtype = a->z_dtype; c->rmsnorm_eps = -1.f; c->rope_dims = 0; c->rope_base = 0.f;
+  c->x_new_st = a->k_new_st; c->v_new_st = a->v_new_st; c->z_new_st = a->z_new_st;
+  c->raw_x_st = a->raw_k_st; c->raw_v_st = a->raw_v_st; c->raw_z_st = a->raw_z_st;
+  c->out_x_st = a->pooled_k_st; c->out_v_st = a->pooled_v_st;
 }
 
 static int validate_step(const lbca_step_args* a, lbca_decode_args* d, lbca_cache_args* c) {
@@ -333,8 +488,32 @@ int lbca_decode_step(const lbca_step_args* a, void* workspace, size_t workspace_
 }
 
 // ---------------------------------------------------------------------------
-int lbca_attend_prefill(const lbca_prefill_args* a, void* stream) {
-  if (!a || !a->q || !a->pooled_k || !a->raw_k || !a->out) return LBCA_ERR_INVALID_ARG;
+static int strides_prefill(lbca_prefill_args* a) {
+  const int64_t B = a->batch, Tq = a->q_len, Hq = a->q_heads, Hk = a->kv_heads, d = a->dim;
+  const int32_t dt = a->dtype;
+  LBCA_TRY(fix_strides(a->q_st, a->q, {B, Tq, Hq}, d, dt, false));
+  LBCA_TRY(fix_strides(a->pooled_k_st, a->pooled_k, {B, Hk, a->entries}, d, dt, false));
+  LBCA_TRY(fix_strides(a->pooled_v_st, a->pooled_v, {B, Hk, a->entries}, d, dt, false));
+  LBCA_TRY(fix_strides(a->raw_k_st, a->raw_k, {B, Hk, a->raw_rows}, d, dt, false));
+  LBCA_TRY(fix_strides(a->raw_v_st, a->raw_v, {B, Hk, a->raw_rows}, d, dt, false));
+  LBCA_TRY(fix_strides(a->out_st, a->out, {B, Tq, Hq}, d, a->out_dtype, true));
+  if (dt == LBCA_BF16) {
+    // cache rows are read through buffer resources with 31-bit byte offsets
+    auto big = [&](int64_t rows, const lbca_strides& st) {
+      return rows * (st.s[2] > d ? st.s[2] : d) * 2 >= (int64_t(1) << 31);
+    };
+    if (big(a->entries, a->pooled_k_st) || big(a->entries, a->pooled_v_st) || big(a->raw_rows, a->raw_k_st) ||
+        big(a->raw_rows, a->raw_v_st))
+      return LBCA_ERR_UNSUPPORTED;
+  }
+  return LBCA_OK;
+}
+
+int lbca_attend_prefill(const lbca_prefill_args* ap, void* stream) {
+  if (!ap) return LBCA_ERR_INVALID_ARG;
+  lbca_prefill_args args = *ap;
+  lbca_prefill_args* a = &args;
+  if (!a->q || !a->pooled_k || !a->raw_k || !a->out) return LBCA_ERR_INVALID_ARG;
   if ((a->pooled_v == nullptr) != (a->raw_v == nullptr)) return LBCA_ERR_INVALID_ARG;
   if (!is_dtype(a->dtype) || !is_dtype(a->out_dtype)) return LBCA_ERR_INVALID_ARG;
   if (a->batch < 0 || a->q_len < 0 || a->q_heads < 1 || a->kv_heads < 1 ||
@@ -370,13 +549,33 @@ int lbca_attend_prefill(const lbca_prefill_args* a, void* stream) {
     if (rb_first - a->raw_pos_base < 0) return LBCA_ERR_INVALID_ARG;
     if (a->q_pos0 + a->q_len - 1 - a->raw_pos_base >= a->raw_rows) return LBCA_ERR_INVALID_ARG;
   }
+  LBCA_TRY(strides_prefill(a));
   if (a->batch == 0 || a->q_len == 0) return LBCA_OK;
   return hip_status(lbca::launch_prefill(*a, static_cast<hipStream_t>(stream)));
 }
 
 // ---------------------------------------------------------------------------
-static int validate_prefill_grad(const lbca_prefill_grad_args* a) {
-  if (!a || !a->q || !a->pooled_k || !a->raw_k || !a->out || !a->lse || !a->grad_out || !a->grad_q ||
+static int strides_prefill_grad(lbca_prefill_grad_args* a) {
+  const int64_t B = a->batch, Tq = a->q_len, Hq = a->q_heads, Hk = a->kv_heads, d = a->dim;
+  const int64_t N = a->entries, R = a->raw_rows;
+  const int32_t dt = a->dtype, f = LBCA_F32;
+  LBCA_TRY(fix_strides(a->q_st, a->q, {B, Tq, Hq}, d, dt, false));
+  LBCA_TRY(fix_strides(a->grad_out_st, a->grad_out, {B, Tq, Hq}, d, dt, false));
+  LBCA_TRY(fix_strides(a->out_st, a->out, {B, Tq, Hq}, d, a->out_dtype, false));
+  LBCA_TRY(fix_strides(a->pooled_k_st, a->pooled_k, {B, Hk, N}, d, dt, false));
+  LBCA_TRY(fix_strides(a->pooled_v_st, a->pooled_v, {B, Hk, N}, d, dt, false));
+  LBCA_TRY(fix_strides(a->raw_k_st, a->raw_k, {B, Hk, R}, d, dt, false));
+  LBCA_TRY(fix_strides(a->raw_v_st, a->raw_v, {B, Hk, R}, d, dt, false));
+  LBCA_TRY(fix_strides(a->grad_q_st, a->grad_q, {B, Tq, Hq}, d, f, true));
+  LBCA_TRY(fix_strides(a->grad_pooled_k_st, a->grad_pooled_k, {B, Hk, N}, d, f, true));
+  LBCA_TRY(fix_strides(a->grad_pooled_v_st, a->grad_pooled_v, {B, Hk, N}, d, f, true));
+  LBCA_TRY(fix_strides(a->grad_raw_k_st, a->grad_raw_k, {B, Hk, R}, d, f, true));
+  LBCA_TRY(fix_strides(a->grad_raw_v_st, a->grad_raw_v, {B, Hk, R}, d, f, true));
+  return LBCA_OK;
+}
+
+static int validate_prefill_grad(lbca_prefill_grad_args* a) {
+  if (!a->q || !a->pooled_k || !a->raw_k || !a->out || !a->lse || !a->grad_out || !a->grad_q ||
       !a->grad_pooled_k || !a->grad_raw_k)
     return LBCA_ERR_INVALID_ARG;
   const bool shared = a->pooled_v == nullptr;
@@ -416,19 +615,24 @@ static int validate_prefill_grad(const lbca_prefill_grad_args* a) {
     if (rb_first - a->raw_pos_base < 0) return LBCA_ERR_INVALID_ARG;
     if (a->q_pos0 + a->q_len - 1 - a->raw_pos_base >= a->raw_rows) return LBCA_ERR_INVALID_ARG;
   }
-  return LBCA_OK;
+  return strides_prefill_grad(a);
 }
 
-int lbca_attend_prefill_backward_workspace(const lbca_prefill_grad_args* a, size_t* bytes) {
-  if (!bytes) return LBCA_ERR_INVALID_ARG;
+int lbca_attend_prefill_backward_workspace(const lbca_prefill_grad_args* ap, size_t* bytes) {
+  if (!bytes || !ap) return LBCA_ERR_INVALID_ARG;
+  lbca_prefill_grad_args args = *ap;
+  lbca_prefill_grad_args* a = &args;
   const int st = validate_prefill_grad(a);
   if (st != LBCA_OK) return st;
   *bytes = lbca::prefill_grad_workspace_bytes(*a);
   return LBCA_OK;
 }
 
-int lbca_attend_prefill_backward(const lbca_prefill_grad_args* a, void* workspace, size_t workspace_bytes,
+int lbca_attend_prefill_backward(const lbca_prefill_grad_args* ap, void* workspace, size_t workspace_bytes,
                                  void* stream) {
+  if (!ap) return LBCA_ERR_INVALID_ARG;
+  lbca_prefill_grad_args args = *ap;
+  lbca_prefill_grad_args* a = &args;
   const int st = validate_prefill_grad(a);
   if (st != LBCA_OK) return st;
   const size_t need = lbca::prefill_grad_workspace_bytes(*a);
@@ -439,8 +643,8 @@ int lbca_attend_prefill_backward(const lbca_prefill_grad_args* a, void* workspac
 }
 
 // ---------------------------------------------------------------------------
-static int validate_index(const csa_index_args* a) {
-  if (!a || !a->q_idx || !a->head_w || !a->keys || !a->pos || !a->out_idx) return LBCA_ERR_INVALID_ARG;
+static int validate_index(csa_index_args* a) {
+  if (!a->q_idx || !a->head_w || !a->keys || !a->pos || !a->out_idx) return LBCA_ERR_INVALID_ARG;
   if (!is_dtype(a->dtype)) return LBCA_ERR_INVALID_ARG;
   if (a->dtype != LBCA_BF16) return LBCA_ERR_UNSUPPORTED;
   if (a->batch < 0 || a->heads < 1 || a->entries < 0 || a->block < 1 || a->k < 1)
@@ -451,11 +655,15 @@ static int validate_index(const csa_index_args* a) {
   if (!aligned16(a->q_idx) || !aligned16(a->keys) || !aligned16(a->head_w) ||
       !aligned16(a->out_idx) || !aligned16(a->out_score))
     return LBCA_ERR_INVALID_ARG;
+  LBCA_TRY(fix_strides(a->q_idx_st, a->q_idx, {a->batch, a->heads}, a->dim, a->dtype, false));
+  LBCA_TRY(fix_strides(a->keys_st, a->keys, {a->batch, a->entries}, a->dim, a->dtype, false));
   return LBCA_OK;
 }
 
-int csa_index_topk_workspace(const csa_index_args* a, size_t* bytes) {
-  if (!bytes) return LBCA_ERR_INVALID_ARG;
+int csa_index_topk_workspace(const csa_index_args* ap, size_t* bytes) {
+  if (!bytes || !ap) return LBCA_ERR_INVALID_ARG;
+  csa_index_args args = *ap;
+  csa_index_args* a = &args;
   int st = validate_index(a);
   if (st != LBCA_OK) return st;
   *bytes = lbca::index_workspace_bytes(*a);
@@ -465,8 +673,8 @@ int csa_index_topk_workspace(const csa_index_args* a, size_t* bytes) {
 // ---------------------------------------------------------------------------
 namespace {
 
-int validate_csa_prefill(const csa_prefill_args* a) {
-  if (!a || !a->q_idx || !a->head_w || !a->idx_keys || !a->q || !a->entries || !a->raw || !a->out)
+int validate_csa_prefill(csa_prefill_args* a) {
+  if (!a->q_idx || !a->head_w || !a->idx_keys || !a->q || !a->entries || !a->raw || !a->out)
     return LBCA_ERR_INVALID_ARG;
   if (!is_dtype(a->dtype)) return LBCA_ERR_INVALID_ARG;
   if (a->dtype != LBCA_BF16) return LBCA_ERR_UNSUPPORTED;
@@ -485,8 +693,7 @@ int validate_csa_prefill(const csa_prefill_args* a) {
   if (!(a->idx_dim == 32 || a->idx_dim == 64 || a->idx_dim == 128) || a->idx_heads > 16 || a->k > 2048 ||
       a->n_entries > 65536)
     return LBCA_ERR_UNSUPPORTED;
-  if (a->dim != 512 || a->q_heads % 32 != 0 || a->q_heads > 64 || a->batch * a->q_len > 65535 ||
-      a->n_entries * a->dim >= (int64_t(1) << 30) || a->raw_rows * a->dim >= (int64_t(1) << 30))
+  if (a->dim != 512 || a->q_heads % 32 != 0 || a->q_heads > 64 || a->batch * a->q_len > 65535)
     return LBCA_ERR_UNSUPPORTED;
   if (!aligned16(a->q_idx) || !aligned16(a->head_w) || !aligned16(a->idx_keys) || !aligned16(a->q) ||
       !aligned16(a->entries) || !aligned16(a->raw) || !aligned16(a->out) || !aligned16(a->out_idx))
@@ -497,6 +704,17 @@ int validate_csa_prefill(const csa_prefill_args* a) {
     const int64_t lo = a->q_pos0 - a->window + 1 > 0 ? a->q_pos0 - a->window + 1 : 0;
     if (lo < a->raw_pos_base || t_last - a->raw_pos_base >= a->raw_rows) return LBCA_ERR_INVALID_ARG;
   }
+  const int64_t B = a->batch, Tq = a->q_len, N = a->n_entries;
+  LBCA_TRY(fix_strides(a->q_idx_st, a->q_idx, {B, Tq, a->idx_heads}, a->idx_dim, a->dtype, false));
+  LBCA_TRY(fix_strides(a->idx_keys_st, a->idx_keys, {B, N}, a->idx_dim, a->dtype, false));
+  LBCA_TRY(fix_strides(a->q_st, a->q, {B, Tq, a->q_heads}, a->dim, a->dtype, false));
+  LBCA_TRY(fix_strides(a->entries_st, a->entries, {B, N}, a->dim, a->dtype, false));
+  LBCA_TRY(fix_strides(a->raw_st, a->raw, {B, a->raw_rows}, a->dim, a->dtype, false));
+  LBCA_TRY(fix_strides(a->out_st, a->out, {B, Tq, a->q_heads}, a->dim, LBCA_F32, true));
+  // rows are addressed by 32-bit byte offsets within one sequence's cache
+  const int64_t lim = int64_t(1) << 30;
+  if (slice_span(N, a->entries_st.s[1], a->dim) >= lim || slice_span(a->raw_rows, a->raw_st.s[1], a->dim) >= lim)
+    return LBCA_ERR_UNSUPPORTED;
   return LBCA_OK;
 }
 
@@ -519,6 +737,9 @@ CsaPrefillPlan plan_csa_prefill(const csa_prefill_args* a) {
   pl.ia.out_idx = a->out_idx; pl.ia.out_score = nullptr;
   pl.ia.batch = rows; pl.ia.heads = a->idx_heads; pl.ia.dim = a->idx_dim; pl.ia.entries = a->n_entries;
   pl.ia.k = a->k; pl.ia.block = a->block; pl.ia.dtype = a->dtype;
+  // a query chunk's rows: [sequence, query, head] strides (launch_index_topk_chunk)
+  pl.ia.q_idx_st = a->q_idx_st;
+  pl.ia.keys_st = a->idx_keys_st;
   pl.da.q = a->q; pl.da.pooled_k = a->entries; pl.da.raw_k = a->raw; pl.da.sink = a->sink;
   pl.da.out = a->out; pl.da.lse = a->lse;
   pl.da.batch = rows; pl.da.q_heads = a->q_heads; pl.da.kv_heads = 1; pl.da.dim = a->dim;
@@ -526,6 +747,12 @@ CsaPrefillPlan plan_csa_prefill(const csa_prefill_args* a) {
   pl.da.block = a->block; pl.da.window = a->window; pl.da.mode = LBCA_OVERLAP; pl.da.dtype = a->dtype;
   pl.da.scale = a->scale; pl.da.rmsnorm_eps = a->rmsnorm_eps; pl.da.rope_dims = a->rope_dims;
   pl.da.rope_base = a->rope_base;
+  // rows of a query chunk: q and out as [sequence, query, head]; the caches as
+  // one KV head per sequence
+  pl.da.q_st = a->q_st;
+  pl.da.out_st = a->out_st;
+  pl.da.pooled_k_st = lbca_strides{{a->entries_st.s[0], 0, a->entries_st.s[1]}};
+  pl.da.raw_k_st = lbca_strides{{a->raw_st.s[0], 0, a->raw_st.s[1]}};
   pl.da.sel_idx = reinterpret_cast<const int32_t*>(1);  // planned as a selection; set at launch
   if (rows > 0) pl.dp = lbca::plan_decode(pl.da);  // (its split sizing divides by the rows)
   const size_t r = (size_t)rows;
@@ -539,8 +766,10 @@ CsaPrefillPlan plan_csa_prefill(const csa_prefill_args* a) {
 
 }  // namespace
 
-int csa_sparse_prefill_workspace(const csa_prefill_args* a, size_t* bytes) {
-  if (!bytes) return LBCA_ERR_INVALID_ARG;
+int csa_sparse_prefill_workspace(const csa_prefill_args* ap, size_t* bytes) {
+  if (!bytes || !ap) return LBCA_ERR_INVALID_ARG;
+  csa_prefill_args args = *ap;
+  csa_prefill_args* a = &args;
   const int st = validate_csa_prefill(a);
   if (st != LBCA_OK) return st;
   const CsaPrefillPlan pl = plan_csa_prefill(a);
@@ -549,7 +778,10 @@ int csa_sparse_prefill_workspace(const csa_prefill_args* a, size_t* bytes) {
   return LBCA_OK;
 }
 
-int csa_sparse_prefill(const csa_prefill_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+int csa_sparse_prefill(const csa_prefill_args* ap, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!ap) return LBCA_ERR_INVALID_ARG;
+  csa_prefill_args args = *ap;
+  csa_prefill_args* a = &args;
   const int st = validate_csa_prefill(a);
   if (st != LBCA_OK) return st;
   CsaPrefillPlan pl = plan_csa_prefill(a);
@@ -596,7 +828,10 @@ int lbca_grouped_gemm(const lbca_gemm_args* a, void* stream) {
   return hip_status(lbca::launch_gemm(*a, static_cast<hipStream_t>(stream)));
 }
 
-int csa_index_topk(const csa_index_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+int csa_index_topk(const csa_index_args* ap, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!ap) return LBCA_ERR_INVALID_ARG;
+  csa_index_args args = *ap;
+  csa_index_args* a = &args;
   int st = validate_index(a);
   if (st != LBCA_OK) return st;
   const size_t need = lbca::index_workspace_bytes(*a);

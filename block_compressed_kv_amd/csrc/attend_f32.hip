@@ -33,6 +33,8 @@ struct RowsParams {
   int64_t q_len, hq, hkv, G, entries, raw_rows, k_sel, m, W;
   int mode;
   float scale;
+  // element strides: q and out {sequence, query, head}; caches {sequence, KV head, row}
+  Str q_st, o_st, pk_st, pv_st, rk_st, rv_st;
 };
 
 template <int D>
@@ -53,20 +55,21 @@ __global__ __launch_bounds__(64) void rows_f32_kernel(RowsParams p) {
   if (ok) visible_range(t, p.m, p.W, p.mode, &np, &rb);
   ok = ok && np <= p.entries && rb - base >= 0 && t - base < p.raw_rows;
   float o[DPL];
-  const int64_t orow = id * D + lane * DPL;
+  const int64_t orow = b * p.o_st.s0 + i * p.o_st.s1 + h * p.o_st.s2 + lane * DPL;
   if (!ok) {
     for (int c = 0; c < DPL; ++c) o[c] = __builtin_nanf("");
   } else {
-    const float* qrow = p.q + id * D;
+    const float* qrow = p.q + b * p.q_st.s0 + i * p.q_st.s1 + h * p.q_st.s2;
     for (int d = lane; d < D; d += 64) qs[d] = qrow[d];
     __syncthreads();
     const int64_t n_sel = p.sel ? p.k_sel : np;
     const int64_t n_raw = t - rb + 1;
     const int64_t n_tot = n_sel + n_raw;
-    const int64_t kv_pool = (b * p.hkv + kvh) * p.entries;
-    const int64_t kv_raw = (b * p.hkv + kvh) * p.raw_rows + (rb - base);
-    const float* vpool = p.pv ? p.pv : p.pk;
-    const float* vraw = p.rv ? p.rv : p.rk;
+    const float* kpool = p.pk + b * p.pk_st.s0 + kvh * p.pk_st.s1;
+    const float* kraw = p.rk + b * p.rk_st.s0 + kvh * p.rk_st.s1 + (rb - base) * p.rk_st.s2;
+    const float* vpool = p.pv ? p.pv + b * p.pv_st.s0 + kvh * p.pv_st.s1 : kpool;
+    const float* vraw = p.rv ? p.rv + b * p.rv_st.s0 + kvh * p.rv_st.s1 + (rb - base) * p.rv_st.s2 : kraw;
+    const int64_t vps = p.pv ? p.pv_st.s2 : p.pk_st.s2, vrs = p.rv ? p.rv_st.s2 : p.rk_st.s2;
     float m_run = kNegInf, l_run = 0.f;
     for (int c = 0; c < DPL; ++c) o[c] = 0.f;
     for (int64_t g0 = 0; g0 < n_tot; g0 += 64) {
@@ -78,9 +81,9 @@ __global__ __launch_bounds__(64) void rows_f32_kernel(RowsParams p) {
         if (v < n_sel) {
           const int64_t e = p.sel ? (int64_t)p.sel[b * p.k_sel + v] : v;
           rok = e >= 0 && e < np;
-          krow = p.pk + (kv_pool + e) * D;
+          krow = kpool + e * p.pk_st.s2;
         } else {
-          krow = p.rk + (kv_raw + (v - n_sel)) * D;
+          krow = kraw + (v - n_sel) * p.rk_st.s2;
         }
       }
       float s = kNegInf;
@@ -111,9 +114,9 @@ __global__ __launch_bounds__(64) void rows_f32_kernel(RowsParams p) {
         const float* vrow;
         if (vv < n_sel) {
           const int64_t e = p.sel ? (int64_t)p.sel[b * p.k_sel + vv] : vv;
-          vrow = vpool + (kv_pool + e) * D;
+          vrow = vpool + e * vps;
         } else {
-          vrow = vraw + (kv_raw + (vv - n_sel)) * D;
+          vrow = vraw + (vv - n_sel) * vrs;
         }
         for (int c = 0; c < DPL; ++c) o[c] = fmaf(pw, vrow[lane * DPL + c], o[c]);
       }
@@ -170,6 +173,8 @@ hipError_t launch_prefill_f32(const lbca_prefill_args& a, hipStream_t stream) {
   rp.hq = a.q_heads; rp.hkv = a.kv_heads; rp.G = a.q_heads / a.kv_heads;
   rp.entries = a.entries; rp.raw_rows = a.raw_rows; rp.k_sel = 0;
   rp.m = a.block; rp.W = a.window; rp.mode = a.mode; rp.scale = a.scale;
+  rp.q_st = a.q_st; rp.o_st = a.out_st;
+  rp.pk_st = a.pooled_k_st; rp.pv_st = a.pooled_v_st; rp.rk_st = a.raw_k_st; rp.rv_st = a.raw_v_st;
   return launch_rows_f32(rp, a.dim, a.batch, stream);
 }
 
@@ -193,6 +198,10 @@ hipError_t launch_decode_f32(const lbca_decode_args& a, hipStream_t stream) {
   rp.hq = a.q_heads; rp.hkv = a.kv_heads; rp.G = a.q_heads / a.kv_heads;
   rp.entries = a.entries; rp.raw_rows = a.raw_rows; rp.k_sel = a.sel_idx ? a.k_sel : 0;
   rp.m = a.block; rp.W = a.window; rp.mode = a.mode; rp.scale = a.scale;
+  // q and out [batch, heads, dim] as {sequence, query (one), head}
+  rp.q_st = lbca_strides{{a.q_st.s[0], 0, a.q_st.s[1]}};
+  rp.o_st = lbca_strides{{a.out_st.s[0], 0, a.out_st.s[1]}};
+  rp.pk_st = a.pooled_k_st; rp.pv_st = a.pooled_v_st; rp.rk_st = a.raw_k_st; rp.rv_st = a.raw_v_st;
   return launch_rows_f32(rp, a.dim, a.batch, stream);
 }
 

@@ -63,6 +63,14 @@ struct GradParams {
   float scale, scale_log2;
 };
 
+// Element strides of the gradient kernel's tensors: q, dout, dq {sequence,
+// query, head}; K, V and the raw gradients {sequence, KV head, row}.  A kernel
+// argument of its own: held in GradParams they made the register allocation
+// of the 128-dim kernel spill.
+struct GradStrides {
+  Str q, dout, dq, pk, pv, rk, rv, drk, drv;
+};
+
 // Position of 16-byte chunk c of row r in an LDS tile of 32 query rows: 8
 // consecutive rows read at one chunk, and 4 consecutive rows read at 4 aligned
 // chunks (two transposing 16-lane groups), land in distinct banks.
@@ -86,8 +94,10 @@ __device__ __forceinline__ bf16x8 pack8(const float* f) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-template <int D>
-__global__ __launch_bounds__(512, 1) void attn_grad_kernel(GradParams p) {
+// DN: every tensor of the call dense; the kernel then works its offsets out
+// from the sizes and leaves the strides unread.
+template <int D, bool DN>
+__global__ __launch_bounds__(512, 1) void attn_grad_kernel(GradParams p, GradStrides ST) {
   constexpr int DS = D / 16;                  // 16-dim slices of the S / dP contraction
   constexpr int DB = D / 32;                  // 32-dim blocks of dV^T / dK^T
   constexpr int DBH = DB / 2;                 // blocks of one wave's half of the dims
@@ -135,17 +145,33 @@ __global__ __launch_bounds__(512, 1) void attn_grad_kernel(GradParams p) {
     t_end = max(t_begin, min(t_last + 1, q_end));
   }
 
-  const int64_t key_base = pooled ? (int64_t)bh * p.entries + k0 : (int64_t)bh * p.raw_rows + k0;
+  // first K and V rows of the workgroup and their row strides (a shared series
+  // reads values with the key strides; strides as values: a select between
+  // argument fields by reference would become a private-memory lookup)
   const bf16_t* kser = pooled ? p.pk : p.rk;
   const bf16_t* vser = pooled ? (p.shared ? p.pk : p.pv) : (p.shared ? p.rk : p.rv);
+  int64_t ksr = D, vsr = D;
+  if constexpr (DN) {
+    const int64_t key_base = pooled ? (int64_t)bh * p.entries + k0 : (int64_t)bh * p.raw_rows + k0;
+    kser += key_base * D;
+    vser += key_base * D;
+  } else {
+    const int64_t ks0 = pooled ? ST.pk.s0 : ST.rk.s0, ks1 = pooled ? ST.pk.s1 : ST.rk.s1;
+    const int64_t vs0 = p.shared ? ks0 : pooled ? ST.pv.s0 : ST.rv.s0;
+    const int64_t vs1 = p.shared ? ks1 : pooled ? ST.pv.s1 : ST.rv.s1;
+    ksr = pooled ? ST.pk.s2 : ST.rk.s2;
+    vsr = p.shared ? ksr : pooled ? ST.pv.s2 : ST.rv.s2;
+    kser += b * ks0 + kvh * ks1 + k0 * ksr;
+    vser += b * vs0 + kvh * vs1 + k0 * vsr;
+  }
 
   // the workgroup's K and V rows into LDS (rows past the series read as
   // zeros), chunk c of row r at position c ^ qswz(r)
   for (int idx = tid; idx < GK * CH; idx += 512) {
     const int r = idx / CH, c = idx % CH;
     const bool ok = r < nkeys;
-    const uint4 vk = ok ? *reinterpret_cast<const uint4*>(kser + (key_base + r) * D + 8 * c) : make_uint4(0, 0, 0, 0);
-    const uint4 vv = ok ? *reinterpret_cast<const uint4*>(vser + (key_base + r) * D + 8 * c) : make_uint4(0, 0, 0, 0);
+    const uint4 vk = ok ? *reinterpret_cast<const uint4*>(kser + r * ksr + 8 * c) : make_uint4(0, 0, 0, 0);
+    const uint4 vv = ok ? *reinterpret_cast<const uint4*>(vser + r * vsr + 8 * c) : make_uint4(0, 0, 0, 0);
     *reinterpret_cast<uint4*>(&sk[r * D + 8 * (c ^ qswz<D>(r))]) = vk;
     *reinterpret_cast<uint4*>(&sv[r * D + 8 * (c ^ qswz<D>(r))]) = vv;
   }
@@ -191,9 +217,19 @@ __global__ __launch_bounds__(512, 1) void attn_grad_kernel(GradParams p) {
   auto fetch = [&](int it) __attribute__((always_inline)) {
     const int tp = t_begin + GQ * (it / G), hq = qh0 + it % G;
     const int t = min(tp + st_row, t_end - 1);  // rows past the run repeat its last row (masked)
-    const int64_t off = (((int64_t)b * p.q_len + (t - p.q_pos0)) * p.hq + hq) * D + 8 * st_ch;
-    if (BOTH || tid < TCH) stq = *reinterpret_cast<const uint4*>(p.q + off);
-    if (BOTH || tid >= TCH) sto = *reinterpret_cast<const uint4*>(p.dout + off);
+    const int64_t i = t - p.q_pos0;
+    if constexpr (DN) {  // one row offset serves q and dout
+      const int64_t off = (((int64_t)b * p.q_len + i) * p.hq + hq) * D + 8 * st_ch;
+      if (BOTH || tid < TCH) stq = *reinterpret_cast<const uint4*>(p.q + off);
+      if (BOTH || tid >= TCH) sto = *reinterpret_cast<const uint4*>(p.dout + off);
+    } else {
+      if (BOTH || tid < TCH)
+        stq = *reinterpret_cast<const uint4*>(p.q + (int64_t)b * ST.q.s0 + i * ST.q.s1 + (int64_t)hq * ST.q.s2 +
+                                              8 * st_ch);
+      if (BOTH || tid >= TCH)
+        sto = *reinterpret_cast<const uint4*>(p.dout + (int64_t)b * ST.dout.s0 + i * ST.dout.s1 +
+                                              (int64_t)hq * ST.dout.s2 + 8 * st_ch);
+    }
     const int tr = min(tp + (tid & 31), t_end - 1);
     const int64_t rid = ((int64_t)b * p.q_len + (tr - p.q_pos0)) * p.hq + hq;
     if (tid < GQ) {
@@ -310,8 +346,10 @@ __global__ __launch_bounds__(512, 1) void attn_grad_kernel(GradParams p) {
                                   &sk[kb2 * D + 8 * (ck ^ qswz<D>(kb2)) + 4 * (j16 & 1)]);
         dqa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bk, dqa, 0, 0, 0);
       }
-      float* dqrow = p.dq + (((int64_t)b * p.q_len + (tp - p.q_pos0)) * p.hq + hq) * D + 32 * dq_db + n;
-      const int64_t rstride = (int64_t)p.hq * D;
+      float* dqrow = DN ? p.dq + (((int64_t)b * p.q_len + (tp - p.q_pos0)) * p.hq + hq) * D + 32 * dq_db + n
+                        : p.dq + (int64_t)b * ST.dq.s0 + (int64_t)(tp - p.q_pos0) * ST.dq.s1 +
+                              (int64_t)hq * ST.dq.s2 + 32 * dq_db + n;
+      const int64_t rstride = DN ? (int64_t)p.hq * D : (int64_t)ST.dq.s1;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = 8 * (e >> 2) + 4 * h + (e & 3);
@@ -325,7 +363,12 @@ __global__ __launch_bounds__(512, 1) void attn_grad_kernel(GradParams p) {
   // dK, dV of this wave's keys and dims: lane (key n, h) holds dims
   // 32 (DBH dh + i) + 8 qq + 4 h .. +3
   if (!key_ok) return;
-  const int64_t krow = (key_base + key_rel) * D;
+  const int64_t krel = k0 + key_rel;
+  const int64_t krow = DN ? ((int64_t)bh * p.raw_rows + krel) * D : 0;  // dense: one offset for K and V
+  float* const gk_row = DN ? p.drk + krow : p.drk + (int64_t)b * ST.drk.s0 + (int64_t)kvh * ST.drk.s1 + krel * ST.drk.s2;
+  float* const gv_row = p.shared ? nullptr
+                        : DN     ? p.drv + krow
+                                 : p.drv + (int64_t)b * ST.drv.s0 + (int64_t)kvh * ST.drv.s1 + krel * ST.drv.s2;
   // a run's partial: row (bh, tile, split, key) of K then (separate series) V
   const int nser = p.shared ? 1 : 2;
   const int64_t prow = pooled ? ((((int64_t)bh * p.pool_tiles + wi / p.pool_splits) * p.pool_splits + wi % p.pool_splits) *
@@ -346,7 +389,7 @@ __global__ __launch_bounds__(512, 1) void attn_grad_kernel(GradParams p) {
         *reinterpret_cast<float4*>(p.part + prow + d) = make_float4(kv[0], kv[1], kv[2], kv[3]);
         if (!p.shared) *reinterpret_cast<float4*>(p.part + prow + D + d) = make_float4(vv[0], vv[1], vv[2], vv[3]);
       } else {
-        float4* pk4 = reinterpret_cast<float4*>(p.drk + krow + d);
+        float4* pk4 = reinterpret_cast<float4*>(gk_row + d);
         float4 k4 = make_float4(kv[0], kv[1], kv[2], kv[3]);
         if (p.accumulate) {
           const float4 o = *pk4;
@@ -354,7 +397,7 @@ __global__ __launch_bounds__(512, 1) void attn_grad_kernel(GradParams p) {
         }
         *pk4 = k4;
         if (!p.shared) {
-          float4* pv4 = reinterpret_cast<float4*>(p.drv + krow + d);
+          float4* pv4 = reinterpret_cast<float4*>(gv_row + d);
           float4 v4 = make_float4(vv[0], vv[1], vv[2], vv[3]);
           if (p.accumulate) {
             const float4 o = *pv4;
@@ -378,8 +421,9 @@ struct PrepParams {
   float* dq;
   float* dsink;
   int64_t rows;  // batch * q_len
-  int64_t hq, dim;
+  int64_t hq, dim, q_len;
   int out_f32;
+  Str do_st, o_st, dq_st;  // {sequence, query, head}
 };
 
 __global__ __launch_bounds__(256) void attn_grad_prep_kernel(PrepParams p) {
@@ -395,17 +439,18 @@ __global__ __launch_bounds__(256) void attn_grad_prep_kernel(PrepParams p) {
     const int64_t row = r0 + r;
     if (row >= p.rows) break;
     const int64_t rid = row * p.hq + hh;
-    const int64_t off = rid * p.dim + 8 * sub;
+    const int64_t sb = row / p.q_len, si = row % p.q_len;
+    auto at = [&](Str st) { return sb * st.s0 + si * st.s1 + (int64_t)hh * st.s2 + 8 * sub; };
     float go[8], o[8];
-    load8(p.dout + off, go);
-    if (p.out_f32) load8(static_cast<const float*>(p.out) + off, o);
-    else load8(static_cast<const bf16_t*>(p.out) + off, o);
+    load8(p.dout + at(p.do_st), go);
+    if (p.out_f32) load8(static_cast<const float*>(p.out) + at(p.o_st), o);
+    else load8(static_cast<const bf16_t*>(p.out) + at(p.o_st), o);
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc = fmaf(go[i], o[i], acc);
     for (int w = tpr / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w);
     const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    store8(p.dq + off, z);
+    store8(p.dq + at(p.dq_st), z);
     if (sub == 0) {
       p.dvec[rid] = acc;
       if (p.sink) sink_acc -= __expf(sk - p.lse[rid]) * acc;
@@ -428,7 +473,8 @@ struct ReduceParams {
   int64_t entries;
   int64_t total;  // batch * kv_heads * entries * dim / 4
   int dim, n_pool, pool_tiles, pool_splits, shared, accumulate;
-  int q_pos0, q_end, block, window, mode;
+  int q_pos0, q_end, block, window, mode, hkv;
+  Str gk_st, gv_st;  // {sequence, KV head, entry}
 };
 
 __global__ __launch_bounds__(256) void attn_grad_reduce_kernel(ReduceParams p) {
@@ -457,14 +503,15 @@ __global__ __launch_bounds__(256) void attn_grad_reduce_kernel(ReduceParams p) {
       }
     }
   }
-  float4* gk4 = reinterpret_cast<float4*>(p.gk + row * p.dim + d);
+  const int64_t b = bh / p.hkv, kvh = bh % p.hkv;
+  float4* gk4 = reinterpret_cast<float4*>(p.gk + b * p.gk_st.s0 + kvh * p.gk_st.s1 + (int64_t)j * p.gk_st.s2 + d);
   if (p.accumulate) {
     const float4 o = *gk4;
     k4.x += o.x; k4.y += o.y; k4.z += o.z; k4.w += o.w;
   }
   *gk4 = k4;
   if (!p.shared) {
-    float4* gv4 = reinterpret_cast<float4*>(p.gv + row * p.dim + d);
+    float4* gv4 = reinterpret_cast<float4*>(p.gv + b * p.gv_st.s0 + kvh * p.gv_st.s1 + (int64_t)j * p.gv_st.s2 + d);
     if (p.accumulate) {
       const float4 o = *gv4;
       v4.x += o.x; v4.y += o.y; v4.z += o.z; v4.w += o.w;
@@ -475,6 +522,26 @@ __global__ __launch_bounds__(256) void attn_grad_reduce_kernel(ReduceParams p) {
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ x, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) x[i] = 0.f;
+}
+
+// Zeroes rows [n0][n1][n2] of dim floats at element strides st.
+__global__ __launch_bounds__(256) void zero_rows_kernel(float* x, Str st, int64_t n1, int64_t n2, int64_t rows,
+                                                        int dim) {
+  const int per = dim / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows * per; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / per, c = (i % per) * 4;
+    const int64_t r2 = r % n2, r1 = (r / n2) % n1, r0 = r / (n1 * n2);
+    *reinterpret_cast<float4*>(x + r0 * st.s0 + r1 * st.s1 + r2 * st.s2 + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+hipError_t zero_rows(float* x, const lbca_strides& st, int64_t n0, int64_t n1, int64_t n2, int64_t dim,
+                     hipStream_t stream) {
+  const int64_t rows = n0 * n1 * n2;
+  if (!x || rows <= 0) return hipSuccess;
+  const int64_t blocks = (rows * (dim / 4) + 255) / 256;
+  zero_rows_kernel<<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, stream>>>(x, st, n1, n2, rows, (int)dim);
+  return hipGetLastError();
 }
 
 hipError_t zero_f32(float* x, int64_t n, hipStream_t stream) {
@@ -526,12 +593,12 @@ hipError_t launch_prefill_grad(const lbca_prefill_grad_args& a, void* workspace,
   if (!a.accumulate) {
     if ((e = zero_f32(a.grad_sink, a.q_heads, stream)) != hipSuccess) return e;
     if (a.q_len == 0) {  // no queries: every key and value gradient is zero
-      const int64_t pooled_elems = a.batch * a.kv_heads * a.entries * a.dim;
-      const int64_t raw_elems = a.batch * a.kv_heads * a.raw_rows * a.dim;
-      if ((e = zero_f32(a.grad_pooled_k, pooled_elems, stream)) != hipSuccess) return e;
-      if (!shared && (e = zero_f32(a.grad_pooled_v, pooled_elems, stream)) != hipSuccess) return e;
-      if ((e = zero_f32(a.grad_raw_k, raw_elems, stream)) != hipSuccess) return e;
-      if (!shared && (e = zero_f32(a.grad_raw_v, raw_elems, stream)) != hipSuccess) return e;
+      const int64_t B = a.batch, H = a.kv_heads, N = a.entries, R = a.raw_rows, d = a.dim;
+      if ((e = zero_rows(a.grad_pooled_k, a.grad_pooled_k_st, B, H, N, d, stream)) != hipSuccess) return e;
+      if (!shared && (e = zero_rows(a.grad_pooled_v, a.grad_pooled_v_st, B, H, N, d, stream)) != hipSuccess)
+        return e;
+      if ((e = zero_rows(a.grad_raw_k, a.grad_raw_k_st, B, H, R, d, stream)) != hipSuccess) return e;
+      if (!shared && (e = zero_rows(a.grad_raw_v, a.grad_raw_v_st, B, H, R, d, stream)) != hipSuccess) return e;
     }
   }
   if (a.q_len == 0) return hipSuccess;
@@ -547,6 +614,8 @@ hipError_t launch_prefill_grad(const lbca_prefill_grad_args& a, void* workspace,
   pp.hq = a.q_heads;
   pp.dim = a.dim;
   pp.out_f32 = a.out_dtype == LBCA_F32;
+  pp.q_len = a.q_len;
+  pp.do_st = a.grad_out_st; pp.o_st = a.out_st; pp.dq_st = a.grad_q_st;
   attn_grad_prep_kernel<<<dim3((unsigned)((pp.rows + 63) / 64), (unsigned)a.q_heads), 256, 0, stream>>>(pp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
@@ -577,9 +646,24 @@ hipError_t launch_prefill_grad(const lbca_prefill_grad_args& a, void* workspace,
   p.raw_tiles = (int)((a.raw_rows + GK - 1) / GK);
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
+  GradStrides gs;
+  gs.q = a.q_st; gs.dout = a.grad_out_st; gs.dq = a.grad_q_st;
+  gs.pk = a.pooled_k_st; gs.pv = a.pooled_v_st; gs.rk = a.raw_k_st; gs.rv = a.raw_v_st;
+  gs.drk = a.grad_raw_k_st; gs.drv = a.grad_raw_v_st;
   const dim3 grid((unsigned)(p.pool_tiles * p.pool_splits + p.raw_tiles), (unsigned)(a.batch * a.kv_heads));
-  if (a.dim == 128) attn_grad_kernel<128><<<grid, 512, 0, stream>>>(p);
-  else attn_grad_kernel<64><<<grid, 512, 0, stream>>>(p);
+  const int64_t B = a.batch, Tq = a.q_len, Hq = a.q_heads, Hk = a.kv_heads, d = a.dim;
+  const bool dn = dense_strides(a.q, a.q_st, {B, Tq, Hq}, d) && dense_strides(a.grad_out, a.grad_out_st, {B, Tq, Hq}, d) &&
+                  dense_strides(a.grad_q, a.grad_q_st, {B, Tq, Hq}, d) &&
+                  dense_strides(a.pooled_k, a.pooled_k_st, {B, Hk, a.entries}, d) &&
+                  dense_strides(a.pooled_v, a.pooled_v_st, {B, Hk, a.entries}, d) &&
+                  dense_strides(a.raw_k, a.raw_k_st, {B, Hk, a.raw_rows}, d) &&
+                  dense_strides(a.raw_v, a.raw_v_st, {B, Hk, a.raw_rows}, d) &&
+                  dense_strides(a.grad_raw_k, a.grad_raw_k_st, {B, Hk, a.raw_rows}, d) &&
+                  dense_strides(a.grad_raw_v, a.grad_raw_v_st, {B, Hk, a.raw_rows}, d);
+  if (a.dim == 128) dn ? attn_grad_kernel<128, true><<<grid, 512, 0, stream>>>(p, gs)
+                       : attn_grad_kernel<128, false><<<grid, 512, 0, stream>>>(p, gs);
+  else dn ? attn_grad_kernel<64, true><<<grid, 512, 0, stream>>>(p, gs)
+          : attn_grad_kernel<64, false><<<grid, 512, 0, stream>>>(p, gs);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   ReduceParams rp{};
@@ -599,6 +683,8 @@ hipError_t launch_prefill_grad(const lbca_prefill_grad_args& a, void* workspace,
   rp.block = (int)a.block;
   rp.window = (int)a.window;
   rp.mode = a.mode;
+  rp.hkv = (int)a.kv_heads;
+  rp.gk_st = a.grad_pooled_k_st; rp.gv_st = a.grad_pooled_v_st;
   if (rp.total > 0)
     attn_grad_reduce_kernel<<<(unsigned)((rp.total + 255) / 256), 256, 0, stream>>>(rp);
   return hipGetLastError();

@@ -24,7 +24,7 @@
 
 namespace lbca {
 
-template <typename TX, typename TZ, bool HAS_V, bool TREAT, bool DUAL>
+template <typename TX, typename TZ, bool HAS_V, bool TREAT, bool DUAL, bool DN>
 __global__ __launch_bounds__(256) void cache_append_kernel(CacheParams p) {
   __shared__ float part[32][256];  // cross-wave phase merge
   // every argument field in one batch of scalar loads (otherwise they come in
@@ -34,18 +34,24 @@ __global__ __launch_bounds__(256) void cache_append_kernel(CacheParams p) {
                "s"(p.pos), "s"(p.raw_pos_base), "s"(p.heads), "s"(p.dim), "s"(p.m), "s"(p.W), "s"(p.ring),
                "s"(p.entries), "s"(p.mode), "s"(p.lanes_per_row), "s"(p.log2_lanes));
   // row = sequence * heads + head (the host keeps it below 2^31)
-  cache_row<TX, TZ, HAS_V, TREAT, DUAL, false>(p, blockIdx.x, part, true);
+  cache_row<TX, TZ, HAS_V, TREAT, DUAL, false, true, true, DN>(p, blockIdx.x, part, true);
+}
+
+template <typename TX, typename TZ, bool DN>
+static hipError_t launch_cache_d(const CacheParams& p, bool has_v, bool treat, bool dual, dim3 grid, hipStream_t s) {
+  if (has_v) cache_append_kernel<TX, TZ, true, false, false, DN><<<grid, 256, 0, s>>>(p);
+  else if (dual && treat) cache_append_kernel<TX, TZ, false, true, true, DN><<<grid, 256, 0, s>>>(p);
+  else if (dual) cache_append_kernel<TX, TZ, false, false, true, DN><<<grid, 256, 0, s>>>(p);
+  else if (treat) cache_append_kernel<TX, TZ, false, true, false, DN><<<grid, 256, 0, s>>>(p);
+  else cache_append_kernel<TX, TZ, false, false, false, DN><<<grid, 256, 0, s>>>(p);
+  return hipGetLastError();
 }
 
 template <typename TX, typename TZ>
-static hipError_t launch_cache_typed(const CacheParams& p, bool has_v, bool treat, bool dual, dim3 grid,
+static hipError_t launch_cache_typed(const CacheParams& p, bool has_v, bool treat, bool dual, dim3 grid, bool dn,
                                      hipStream_t s) {
-  if (has_v) cache_append_kernel<TX, TZ, true, false, false><<<grid, 256, 0, s>>>(p);
-  else if (dual && treat) cache_append_kernel<TX, TZ, false, true, true><<<grid, 256, 0, s>>>(p);
-  else if (dual) cache_append_kernel<TX, TZ, false, false, true><<<grid, 256, 0, s>>>(p);
-  else if (treat) cache_append_kernel<TX, TZ, false, true, false><<<grid, 256, 0, s>>>(p);
-  else cache_append_kernel<TX, TZ, false, false, false><<<grid, 256, 0, s>>>(p);
-  return hipGetLastError();
+  return dn ? launch_cache_d<TX, TZ, true>(p, has_v, treat, dual, grid, s)
+            : launch_cache_d<TX, TZ, false>(p, has_v, treat, dual, grid, s);
 }
 
 hipError_t launch_cache_append(const lbca_cache_args& a, hipStream_t stream) {
@@ -62,16 +68,25 @@ hipError_t launch_cache_append(const lbca_cache_args& a, hipStream_t stream) {
   p.eps = a.rmsnorm_eps;
   p.rope_dims = a.rope_dims;
   p.log2_base = a.rope_dims > 0 ? log2((double)a.rope_base) : 0.0;
+  set_cache_strides(p, a);
   const dim3 grid((unsigned)(a.batch * a.heads));
   const bool has_v = a.v_new != nullptr;
   const bool treat = a.rmsnorm_eps >= 0.f || a.rope_dims > 0;
   const bool dual = a.xb_new != nullptr;
+  const int64_t B = a.batch, H = a.heads, R = 2 * a.ring, N = a.entries, d = a.dim;
+  const bool dn =
+      dense_strides(a.x_new, a.x_new_st, {B, H}, d) && dense_strides(a.v_new, a.v_new_st, {B, H}, d) &&
+      dense_strides(a.z_new, a.z_new_st, {B, H}, d) && dense_strides(a.xb_new, a.xb_new_st, {B, H}, d) &&
+      dense_strides(a.zb_new, a.zb_new_st, {B, H}, d) && dense_strides(a.raw_x, a.raw_x_st, {B, H, R}, d) &&
+      dense_strides(a.raw_v, a.raw_v_st, {B, H, R}, d) && dense_strides(a.raw_z, a.raw_z_st, {B, H, R}, d) &&
+      dense_strides(a.raw_xb, a.raw_xb_st, {B, H, R}, d) && dense_strides(a.raw_zb, a.raw_zb_st, {B, H, R}, d) &&
+      dense_strides(a.out_x, a.out_x_st, {B, H, N}, d) && dense_strides(a.out_v, a.out_v_st, {B, H, N}, d);
   if (a.x_dtype == LBCA_BF16) {
-    if (a.z_dtype == LBCA_BF16) return launch_cache_typed<bf16_t, bf16_t>(p, has_v, treat, dual, grid, stream);
-    return launch_cache_typed<bf16_t, float>(p, has_v, treat, dual, grid, stream);
+    if (a.z_dtype == LBCA_BF16) return launch_cache_typed<bf16_t, bf16_t>(p, has_v, treat, dual, grid, dn, stream);
+    return launch_cache_typed<bf16_t, float>(p, has_v, treat, dual, grid, dn, stream);
   }
-  if (a.z_dtype == LBCA_BF16) return launch_cache_typed<float, bf16_t>(p, has_v, treat, dual, grid, stream);
-  return launch_cache_typed<float, float>(p, has_v, treat, dual, grid, stream);
+  if (a.z_dtype == LBCA_BF16) return launch_cache_typed<float, bf16_t>(p, has_v, treat, dual, grid, dn, stream);
+  return launch_cache_typed<float, float>(p, has_v, treat, dual, grid, dn, stream);
 }
 
 }  // namespace lbca

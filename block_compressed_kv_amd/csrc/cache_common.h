@@ -36,7 +36,33 @@ struct CacheParams {
   float eps;
   int rope_dims;
   double log2_base;
+  // element strides: token inputs {sequence, head}; rings and pooled outputs
+  // {sequence, head, row}
+  Str xn, vn, zn, xbn, zbn, rx, rv, rz, rxb, rzb, ox, ov;
 };
+
+// The strides of a cache step: the arguments', or, when every tensor of the
+// call is dense (DN), the row-major ones worked out from the sizes.
+struct CacheStr {
+  Str xn, vn, zn, xbn, zbn, rx, rv, rz, rxb, rzb, ox, ov;
+};
+template <bool DN>
+__device__ __forceinline__ CacheStr cache_strides(const CacheParams& p) {
+  if constexpr (DN) {
+    const Str tok{p.heads * p.dim, p.dim, 0};
+    const Str ring{p.heads * 2 * p.ring * p.dim, 2 * p.ring * p.dim, p.dim};
+    const Str ent{p.heads * p.entries * p.dim, p.entries * p.dim, p.dim};
+    return CacheStr{tok, tok, tok, tok, tok, ring, ring, ring, ring, ring, ent, ent};
+  } else {
+    return CacheStr{p.xn, p.vn, p.zn, p.xbn, p.zbn, p.rx, p.rv, p.rz, p.rxb, p.rzb, p.ox, p.ov};
+  }
+}
+
+inline void set_cache_strides(CacheParams& c, const lbca_cache_args& a) {
+  c.xn = a.x_new_st; c.vn = a.v_new_st; c.zn = a.z_new_st; c.xbn = a.xb_new_st; c.zbn = a.zb_new_st;
+  c.rx = a.raw_x_st; c.rv = a.raw_v_st; c.rz = a.raw_z_st; c.rxb = a.raw_xb_st; c.rzb = a.raw_zb_st;
+  c.ox = a.out_x_st; c.ov = a.out_v_st;
+}
 
 // 16-byte vector i of row r (8 elements are one vector in bf16, two in fp32).
 template <typename T>
@@ -52,8 +78,9 @@ __device__ __forceinline__ void st16(T* r, int i, uint4 v) { reinterpret_cast<ui
 // barrier: the first L threads' work); POOL: the due block (every thread of the
 // workgroup calls it when it pools, for the barriers).
 template <typename TX, typename TZ, bool HAS_V, bool TREAT, bool DUAL, bool AT_COMPLETION, bool COPY = true,
-          bool POOL = true>
+          bool POOL = true, bool DN = false>
 __device__ __forceinline__ void cache_row(const CacheParams& p, unsigned row, float (*part)[256], bool member) {
+  const CacheStr S = cache_strides<DN>(p);
   const int tid = threadIdx.x, lane = tid & 63;
   const int L = p.lanes_per_row;
   const int li = lane & (L - 1);
@@ -62,14 +89,15 @@ __device__ __forceinline__ void cache_row(const CacheParams& p, unsigned row, fl
   const unsigned b = row / (unsigned)p.heads, h = row % (unsigned)p.heads;
   const int64_t dim = p.dim, ring = p.ring;
   const int64_t c0 = (int64_t)li * 8;
+  auto tok = [&](Str st) { return (int64_t)b * st.s0 + (int64_t)h * st.s1 + c0; };
+  auto at = [&](Str st, int64_t r) { return tok(st) + r * st.s2; };
   // the new token's rows first: their addresses do not depend on the position
   constexpr bool X2 = sizeof(TX) == 4, Z2 = sizeof(TZ) == 4;  // two vectors per 8 fp32 elements
-  const int64_t src = (int64_t)row * dim + c0;
-  const TX* xs = static_cast<const TX*>(p.x_new) + src;
-  const TX* vs = static_cast<const TX*>(p.v_new) + src;
-  const TZ* zs = static_cast<const TZ*>(p.z_new) + src;
-  const TX* xbs = static_cast<const TX*>(p.xb_new) + src;
-  const TZ* zbs = static_cast<const TZ*>(p.zb_new) + src;
+  const TX* xs = static_cast<const TX*>(p.x_new) + tok(S.xn);
+  const TX* vs = static_cast<const TX*>(p.v_new) + tok(S.vn);
+  const TZ* zs = static_cast<const TZ*>(p.z_new) + tok(S.zn);
+  const TX* xbs = static_cast<const TX*>(p.xb_new) + tok(S.xbn);
+  const TZ* zbs = static_cast<const TZ*>(p.zb_new) + tok(S.zbn);
   uint4 x0 = {}, x1 = {}, v0 = {}, v1 = {}, z0 = {}, z1 = {}, xb0 = {}, xb1 = {}, zb0 = {}, zb1 = {};
   if (COPY && member && phase == 0) {
     x0 = ld16(xs, 0);
@@ -89,50 +117,27 @@ __device__ __forceinline__ void cache_row(const CacheParams& p, unsigned row, fl
   }
   const int64_t t = p.pos[b];
   if (t < 0) return;
-  const int64_t series = (int64_t)row * 2 * ring * dim + c0;  // ring rows of this (sequence, head)
 
   // 1. the new token into both rows of its slot
   const int64_t slot = t % ring;
   if (COPY && member && phase == 0) {
-    const int64_t d0 = series + slot * dim, d1 = d0 + ring * dim;
-    TX* rx = static_cast<TX*>(p.raw_x);
-    TZ* rz = static_cast<TZ*>(p.raw_z);
-    st16(rx + d0, 0, x0);
-    st16(rx + d1, 0, x0);
-    if constexpr (X2) {
-      st16(rx + d0, 1, x1);
-      st16(rx + d1, 1, x1);
-    }
-    if constexpr (HAS_V) {
-      TX* rv = static_cast<TX*>(p.raw_v);
-      st16(rv + d0, 0, v0);
-      st16(rv + d1, 0, v0);
-      if constexpr (X2) {
-        st16(rv + d0, 1, v1);
-        st16(rv + d1, 1, v1);
+    // both ring rows of the slot in one series: its first 16-byte vectors, then (X2/Z2) the second
+    auto put = [&](auto* base, Str st, uint4 a0, uint4 a1, bool two) {
+      auto* r0 = base + at(st, slot);
+      auto* r1 = r0 + ring * st.s2;
+      st16(r0, 0, a0);
+      st16(r1, 0, a0);
+      if (two) {
+        st16(r0, 1, a1);
+        st16(r1, 1, a1);
       }
-    }
-    st16(rz + d0, 0, z0);
-    st16(rz + d1, 0, z0);
-    if constexpr (Z2) {
-      st16(rz + d0, 1, z1);
-      st16(rz + d1, 1, z1);
-    }
+    };
+    put(static_cast<TX*>(p.raw_x), S.rx, x0, x1, X2);
+    if constexpr (HAS_V) put(static_cast<TX*>(p.raw_v), S.rv, v0, v1, X2);
+    put(static_cast<TZ*>(p.raw_z), S.rz, z0, z1, Z2);
     if constexpr (DUAL) {
-      TX* rxb = static_cast<TX*>(p.raw_xb);
-      TZ* rzb = static_cast<TZ*>(p.raw_zb);
-      st16(rxb + d0, 0, xb0);
-      st16(rxb + d1, 0, xb0);
-      st16(rzb + d0, 0, zb0);
-      st16(rzb + d1, 0, zb0);
-      if constexpr (X2) {
-        st16(rxb + d0, 1, xb1);
-        st16(rxb + d1, 1, xb1);
-      }
-      if constexpr (Z2) {
-        st16(rzb + d0, 1, zb1);
-        st16(rzb + d1, 1, zb1);
-      }
+      put(static_cast<TX*>(p.raw_xb), S.rxb, xb0, xb1, X2);
+      put(static_cast<TZ*>(p.raw_zb), S.rzb, zb0, zb1, Z2);
     }
   }
   // 2. the raw base that maps t's raw span onto ring rows
@@ -150,18 +155,20 @@ __device__ __forceinline__ void cache_row(const CacheParams& p, unsigned row, fl
   PoolAcc<TX, TZ, HAS_V> acc;
   acc.init();
   if (member)
-    acc.run(static_cast<const TX*>(p.raw_x) + series + r0 * dim,
-            HAS_V ? static_cast<const TX*>(p.raw_v) + series + r0 * dim : nullptr,
-            static_cast<const TZ*>(p.raw_z) + series + r0 * dim, p.bias + h * p.m * dim + c0, phase, P, p.m, dim);
+    acc.run(static_cast<const TX*>(p.raw_x) + at(S.rx, r0),
+            HAS_V ? static_cast<const TX*>(p.raw_v) + at(S.rv, r0) : nullptr,
+            static_cast<const TZ*>(p.raw_z) + at(S.rz, r0), p.bias + h * p.m * dim + c0, phase, P, p.m, dim,
+            RowPitch{S.rx.s2, S.rv.s2, S.rz.s2});
   if (member && DUAL && j > 0) {  // block j-1 of the b-series, under the same softmax
     const int64_t rb0 = ((j - 1) * p.m) % ring;
-    acc.run(static_cast<const TX*>(p.raw_xb) + series + rb0 * dim, nullptr,
-            static_cast<const TZ*>(p.raw_zb) + series + rb0 * dim, p.bias_b + h * p.m * dim + c0, phase, P, p.m, dim);
+    acc.run(static_cast<const TX*>(p.raw_xb) + at(S.rxb, rb0), nullptr,
+            static_cast<const TZ*>(p.raw_zb) + at(S.rzb, rb0), p.bias_b + h * p.m * dim + c0, phase, P, p.m, dim,
+            RowPitch{S.rxb.s2, 0, S.rzb.s2});
   }
-  const int64_t o = ((int64_t)row * p.entries + j) * dim + c0;
   finish_entry<TX, TZ, HAS_V, TREAT>(acc, part, L, P, phase, true, dim, c0, j * p.m,
-                                     EntryTreat{p.eps, p.rope_dims, p.log2_base}, static_cast<TX*>(p.out_x) + o,
-                                     HAS_V ? static_cast<TX*>(p.out_v) + o : nullptr, member);
+                                     EntryTreat{p.eps, p.rope_dims, p.log2_base},
+                                     static_cast<TX*>(p.out_x) + at(S.ox, j),
+                                     HAS_V ? static_cast<TX*>(p.out_v) + at(S.ov, j) : nullptr, member);
 }
 
 

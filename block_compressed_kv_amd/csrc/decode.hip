@@ -142,6 +142,7 @@ struct Tile {
 struct Slices {
   uintptr_t pk, pv, rk, rv, dummy;
   uintptr_t tk, tv;  // fused cache step: the new token's rows
+  uint32_t pks, pvs, rks, rvs;  // row strides in bytes
 };
 
 // Selected ids of one workgroup's range are staged in LDS (a global load of
@@ -189,14 +190,15 @@ __device__ __forceinline__ void load_tile(Tile<D, R, DS, SHARED>& T, const int* 
       if (sel) row = ids[ok ? min(v - r0, kSelLds - 1) : 0];
       ok = ok && row >= 0 && row < sv.n_pooled;
     }
-    const uint64_t off = (uint64_t)(uint32_t)row * (D * 2) + 16u * kq;
+    const uint64_t off = (uint64_t)(uint32_t)row * (is_raw ? sl.rks : sl.pks) + 16u * kq;
     // fused cache step: the raw row at the position is the new token's input row
     const bool tok = FUSED && is_raw && v == sv.n_raw - 1;
     const uintptr_t kp = ok ? (tok ? sl.tk + 16u * kq : kb + off) : sl.dummy + 16u * kq;
 #pragma unroll
     for (int s = 0; s < KS; ++s) T.k[h][s] = ldg16(kp + 64u * s);
     if constexpr (!SHARED) {
-      const uintptr_t vp = (ok ? (tok ? sl.tv + 16u * kq : vb + off) : sl.dummy + 16u * kq) + 2u * dv0;
+      const uint64_t offv = (uint64_t)(uint32_t)row * (is_raw ? sl.rvs : sl.pvs) + 16u * kq;
+      const uintptr_t vp = (ok ? (tok ? sl.tv + 16u * kq : vb + offv) : sl.dummy + 16u * kq) + 2u * dv0;
 #pragma unroll
       for (int s = 0; s < KV; ++s) T.v[h][s] = ldg16(vp + 64u * s);
     }
@@ -211,7 +213,7 @@ __device__ __forceinline__ void load_tile(Tile<D, R, DS, SHARED>& T, const int* 
 // requested first and stored once the position is known; it returns that
 // cache row (else -1) so the caller can pool a completed block after the
 // decode.
-template <int D, int R, int NW, int DS, bool SHARED, int RD, bool TREAT, bool SPEC, bool FUSED,
+template <int D, int R, int NW, int DS, bool SHARED, int RD, bool TREAT, bool SPEC, bool FUSED, bool DN,
           typename TZ = float>
 __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, const CacheParams* cp = nullptr) {
   constexpr int KS = D / 32, NH = R / 16;
@@ -229,9 +231,21 @@ __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, 
   __shared__ int s_ids[SPEC ? 1 : kSelLds];        // selected ids of this workgroup's range
 
   preload_params(p);
+  if constexpr (!DN) preload_strides(p);
+  const DecStr ST = dec_strides<DN, D>(p, 1);  // one query row per sequence here
   if constexpr (FUSED)  // the cache-step fields too, in the same batch of scalar loads
     asm volatile("" ::"s"(cp->x_new), "s"(cp->v_new), "s"(cp->z_new), "s"(cp->raw_x), "s"(cp->raw_v),
                  "s"(cp->raw_z), "s"(cp->raw_pos_base), "s"(cp->ring), "s"(p.ring));
+  CacheStr CS{};  // the cache step's strides (fused step; dense: from the decode's sizes)
+  if constexpr (FUSED) {
+    if constexpr (DN) {
+      const Str tok{p.hkv * D, D, 0}, ring{p.hkv * p.raw_rows * D, p.raw_rows * D, D};
+      CS.xn = CS.vn = CS.zn = tok;
+      CS.rx = CS.rv = CS.rz = ring;
+    } else {
+      CS = cache_strides<false>(*cp);
+    }
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile choices stay scalar
   const int n = lane & 15, kq = lane >> 4;
@@ -263,10 +277,11 @@ __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, 
   const bool tok_lane = FUSED && own_row >= 0 && tid < D / 8;
   if constexpr (FUSED) {
     if (tok_lane) {
-      const int64_t src = (int64_t)own_row * D + 8 * tid;
-      tok_k = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(cp->x_new) + src);
-      tok_v = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(cp->v_new) + src);
-      const TZ* zs = static_cast<const TZ*>(cp->z_new) + src;
+      tok_k = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(cp->x_new) + b * CS.xn.s0 +
+                                              kvh * CS.xn.s1 + 8 * tid);
+      tok_v = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(cp->v_new) + b * CS.vn.s0 +
+                                              kvh * CS.vn.s1 + 8 * tid);
+      const TZ* zs = static_cast<const TZ*>(cp->z_new) + b * CS.zn.s0 + kvh * CS.zn.s1 + 8 * tid;
       tok_z0 = reinterpret_cast<const uint4*>(zs)[0];
       if constexpr (sizeof(TZ) == 4) tok_z1 = reinterpret_cast<const uint4*>(zs)[1];
     }
@@ -282,23 +297,35 @@ __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, 
   // keep the count of loads after the position exact for the wait on it.)
   uint4 qr[KS];
   {
-    const bf16_t* qrow = p.q + (b * p.hq + head0 + (head_ok ? n : 0)) * D + 8 * kq;
+    const bf16_t* qrow = p.q + (DN ? (b * p.hq + head0 + (head_ok ? n : 0)) * D
+                                   : b * ST.q.s0 + (head0 + (head_ok ? n : 0)) * ST.q.s2) + 8 * kq;
 #pragma unroll
     for (int s = 0; s < KS; ++s) qr[s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
   }
   // Addresses of this (sequence, KV head) slice (none depends on the position).
   Slices sl;
   {
-    const uint64_t sp = (uint64_t)((b * p.hkv + kvh) * p.entries) * (D * 2);
-    const uint64_t sr = (uint64_t)((b * p.hkv + kvh) * p.raw_rows) * (D * 2);
-    sl.pk = reinterpret_cast<uintptr_t>(p.pk) + sp;
-    sl.rk = reinterpret_cast<uintptr_t>(p.rk) + sr;
-    sl.pv = SHARED ? sl.pk : reinterpret_cast<uintptr_t>(p.pv) + sp;
-    sl.rv = SHARED ? sl.rk : reinterpret_cast<uintptr_t>(p.rv) + sr;
-    sl.dummy = reinterpret_cast<uintptr_t>(p.q + (b * p.hq + head0) * D);
+    if constexpr (DN) {  // dense: one slice offset per series (pooled, raw)
+      const uint64_t sp = (uint64_t)((b * p.hkv + kvh) * p.entries) * (D * 2);
+      const uint64_t sr = (uint64_t)((b * p.hkv + kvh) * p.raw_rows) * (D * 2);
+      sl.pk = reinterpret_cast<uintptr_t>(p.pk) + sp;
+      sl.rk = reinterpret_cast<uintptr_t>(p.rk) + sr;
+      sl.pv = SHARED ? sl.pk : reinterpret_cast<uintptr_t>(p.pv) + sp;
+      sl.rv = SHARED ? sl.rk : reinterpret_cast<uintptr_t>(p.rv) + sr;
+    } else {
+      sl.pk = reinterpret_cast<uintptr_t>(p.pk + b * ST.pk.s0 + kvh * ST.pk.s1);
+      sl.rk = reinterpret_cast<uintptr_t>(p.rk + b * ST.rk.s0 + kvh * ST.rk.s1);
+      sl.pv = SHARED ? sl.pk : reinterpret_cast<uintptr_t>(p.pv + b * ST.pv.s0 + kvh * ST.pv.s1);
+      sl.rv = SHARED ? sl.rk : reinterpret_cast<uintptr_t>(p.rv + b * ST.rv.s0 + kvh * ST.rv.s1);
+    }
+    sl.pks = 2u * (uint32_t)ST.pk.s2;
+    sl.rks = 2u * (uint32_t)ST.rk.s2;
+    sl.pvs = SHARED ? sl.pks : 2u * (uint32_t)ST.pv.s2;
+    sl.rvs = SHARED ? sl.rks : 2u * (uint32_t)ST.rv.s2;
+    sl.dummy = reinterpret_cast<uintptr_t>(p.q + (DN ? (b * p.hq + head0) * D : b * ST.q.s0 + head0 * ST.q.s2));
     if constexpr (FUSED) {
-      sl.tk = reinterpret_cast<uintptr_t>(p.tk + (b * p.hkv + kvh) * D);
-      sl.tv = reinterpret_cast<uintptr_t>(p.tv + (b * p.hkv + kvh) * D);
+      sl.tk = reinterpret_cast<uintptr_t>(p.tk + b * ST.tk.s0 + kvh * ST.tk.s1);
+      sl.tv = reinterpret_cast<uintptr_t>(p.tv + b * ST.tv.s0 + kvh * ST.tv.s1);
     } else {
       sl.tk = sl.tv = 0;
     }
@@ -321,13 +348,14 @@ __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, 
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
         const int e = (wave + i * NW) * R + 16 * h + n;
-        const uint64_t off = (uint64_t)e * (D * 2) + 16u * kq;
+        const uint64_t off = (uint64_t)e * sl.pks + 16u * kq;
         const bool in = e < p.entries;  // rows past the buffer read the stand-in row
         const uintptr_t kp = in ? sl.pk + off : sl.dummy + 16u * kq;
 #pragma unroll
         for (int s = 0; s < KS; ++s) T[i].k[h][s] = ldg16(kp + 64u * s);
         if constexpr (!SHARED) {
-          const uintptr_t vp = (in ? sl.pv + off : sl.dummy + 16u * kq) + 2u * dv0;
+          const uint64_t offv = (uint64_t)e * sl.pvs + 16u * kq;
+          const uintptr_t vp = (in ? sl.pv + offv : sl.dummy + 16u * kq) + 2u * dv0;
 #pragma unroll
           for (int s = 0; s < KV; ++s) T[i].v[h][s] = ldg16(vp + 64u * s);
         }
@@ -348,19 +376,19 @@ __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, 
   if constexpr (FUSED) {  // the token into both ring rows of its slot, and the raw base (lbca_cache_append's rule)
     if (tok_lane && sv.t >= 0) {
       const int64_t ring = cp->ring, slot = sv.t % ring;
-      const int64_t d0 = ((int64_t)own_row * 2 * ring + slot) * D + 8 * tid, d1 = d0 + ring * D;
-      bf16_t* rk = static_cast<bf16_t*>(cp->raw_x);
-      bf16_t* rv = static_cast<bf16_t*>(cp->raw_v);
-      TZ* rz = static_cast<TZ*>(cp->raw_z);
+      bf16_t* rk = static_cast<bf16_t*>(cp->raw_x) + b * CS.rx.s0 + kvh * CS.rx.s1 + slot * CS.rx.s2 + 8 * tid;
+      bf16_t* rv = static_cast<bf16_t*>(cp->raw_v) + b * CS.rv.s0 + kvh * CS.rv.s1 + slot * CS.rv.s2 + 8 * tid;
+      TZ* rz = static_cast<TZ*>(cp->raw_z) + b * CS.rz.s0 + kvh * CS.rz.s1 + slot * CS.rz.s2 + 8 * tid;
+      const int64_t d0 = 0, d1 = ring * CS.rx.s2, v1 = ring * CS.rv.s2, z1 = ring * CS.rz.s2;
       *reinterpret_cast<uint4*>(rk + d0) = tok_k;
       *reinterpret_cast<uint4*>(rk + d1) = tok_k;
       *reinterpret_cast<uint4*>(rv + d0) = tok_v;
-      *reinterpret_cast<uint4*>(rv + d1) = tok_v;
+      *reinterpret_cast<uint4*>(rv + v1) = tok_v;
       reinterpret_cast<uint4*>(rz + d0)[0] = tok_z0;
-      reinterpret_cast<uint4*>(rz + d1)[0] = tok_z0;
+      reinterpret_cast<uint4*>(rz + z1)[0] = tok_z0;
       if constexpr (sizeof(TZ) == 4) {
         reinterpret_cast<uint4*>(rz + d0)[1] = tok_z1;
-        reinterpret_cast<uint4*>(rz + d1)[1] = tok_z1;
+        reinterpret_cast<uint4*>(rz + z1)[1] = tok_z1;
       }
       if (kvh == 0 && tid == 0) cp->raw_pos_base[b] = sv.raw_begin - sv.raw_begin % ring;
     }
@@ -368,7 +396,7 @@ __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, 
   if (!sv.ok) {  // rows do not fit the buffers: NaN, written once per unit and slice
     if (split == 0) {
       for (int i = tid; i < nvalid * DV; i += blockDim.x)
-        p.out[(b * p.hq + head0 + i / DV) * D + dv0 + i % DV] = __builtin_nanf("");
+        p.out[b * ST.o.s0 + (head0 + i / DV) * ST.o.s2 + dv0 + i % DV] = __builtin_nanf("");
       if (p.lse && dh == 0 && tid < nvalid) p.lse[b * p.hq + head0 + tid] = __builtin_nanf("");
     }
     return own_row;
@@ -635,7 +663,7 @@ __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, 
     for (int i = tid; i < items; i += blockDim.x) {
       const int sl = i / per_slot, dl = i % per_slot;
       const int d = dv0 + dl;
-      float* o = p.out + (b * p.hq + head0 + sl) * D;
+      float* o = p.out + b * ST.o.s0 + (head0 + sl) * ST.o.s2;
       const float inv = s_inv[sl];
       if (!rot || d < D - r) {
         o[d] = merged(sl, dl) * inv;
@@ -673,9 +701,9 @@ __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, 
 // NORM: each split's partial is its own normalised output in bf16 (the wide
 // path), weighted by exp2(m_s - M) * l_s instead of exp2(m_s - M).
 constexpr int kMergeGroups = 4;  // for 64-dim chunks
-template <int D, int R, int NW, int DS, bool SHARED, int RD, bool TREAT, bool SPEC>
+template <int D, int R, int NW, int DS, bool SHARED, int RD, bool TREAT, bool SPEC, bool DN = true>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
-  decode_body<D, R, NW, DS, SHARED, RD, TREAT, SPEC, false>(p, blockIdx.x);
+  decode_body<D, R, NW, DS, SHARED, RD, TREAT, SPEC, false, DN>(p, blockIdx.x);
 }
 
 // Fused decode step (lbca_decode_step, EXCLUSIVE rule, K and V series): the
@@ -694,12 +722,13 @@ struct StepParams {
   CacheParams c;
 };
 
-template <int D, int R, int NW, int DS, bool SPEC, typename TZ>
+template <int D, int R, int NW, int DS, bool SPEC, typename TZ, bool DN>
 __global__ __launch_bounds__(NW * 64) void decode_step_kernel(StepParams sp) {
   static_assert(NW * 64 >= 256, "the cache step needs 256 threads");
   __shared__ float part[32][256];  // the cache step's cross-wave phase merge
-  const int row = decode_body<D, R, NW, DS, false, 0, false, SPEC, true, TZ>(sp.d, blockIdx.x, &sp.c);
-  if (row >= 0) cache_row<bf16_t, TZ, true, false, false, true, false, true>(sp.c, row, part, threadIdx.x < 256);
+  const int row = decode_body<D, R, NW, DS, false, 0, false, SPEC, true, DN, TZ>(sp.d, blockIdx.x, &sp.c);
+  if (row >= 0)
+    cache_row<bf16_t, TZ, true, false, false, true, false, true, DN>(sp.c, row, part, threadIdx.x < 256);
 }
 
 template <bool NORM>
@@ -809,7 +838,7 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeParams p, int 
         o2[e] = x2 * cs + x1 * sn;
       }
     }
-    float* o = p.out + (b * p.hq + head0 + sl) * D;
+    float* o = p.out + qrow_off(p.o_st, p.qrows, b, head0 + sl);
     *reinterpret_cast<float4*>(o + d1) = make_float4(o1[0], o1[1], o1[2], o1[3]);
     *reinterpret_cast<float4*>(o + d2) = make_float4(o2[0], o2[1], o2[2], o2[3]);
   }
@@ -939,36 +968,74 @@ DecodePlan plan_decode(const lbca_decode_args& a) {
   return pl;
 }
 
-template <int D, int R, int NW, int DS>
-static hipError_t launch_d(const DecodeParams& p, bool shared, int rd, bool treat, dim3 g,
-                           hipStream_t s) {
+// DN: every tensor of the call dense (instances that work the strides out
+// from the sizes).  Strided calls run the same instance family, so their
+// results equal the dense ones bit for bit.
+template <int D, int R, int NW, int DS, bool DN>
+static hipError_t launch_dd(const DecodeParams& p, bool shared, int rd, bool treat, dim3 g, hipStream_t s) {
   const dim3 blk(NW * 64);
   if (!treat) {
     if constexpr (D <= 128) {  // early-request instances for one split without selection
       if (p.splits == 1 && p.sel == nullptr) {
-        if (shared) decode_kernel<D, R, NW, DS, true, 0, false, true><<<g, blk, 0, s>>>(p);
-        else decode_kernel<D, R, NW, DS, false, 0, false, true><<<g, blk, 0, s>>>(p);
+        if (shared) decode_kernel<D, R, NW, DS, true, 0, false, true, DN><<<g, blk, 0, s>>>(p);
+        else decode_kernel<D, R, NW, DS, false, 0, false, true, DN><<<g, blk, 0, s>>>(p);
         return hipGetLastError();
       }
     }
-    if (shared) decode_kernel<D, R, NW, DS, true, 0, false, false><<<g, blk, 0, s>>>(p);
-    else decode_kernel<D, R, NW, DS, false, 0, false, false><<<g, blk, 0, s>>>(p);
+    if (shared) decode_kernel<D, R, NW, DS, true, 0, false, false, DN><<<g, blk, 0, s>>>(p);
+    else decode_kernel<D, R, NW, DS, false, 0, false, false, DN><<<g, blk, 0, s>>>(p);
     return hipGetLastError();
   }
   if (!shared) return hipErrorInvalidValue;
   switch (rd) {
-    case 0: decode_kernel<D, R, NW, DS, true, 0, true, false><<<g, blk, 0, s>>>(p); break;
+    case 0: decode_kernel<D, R, NW, DS, true, 0, true, false, DN><<<g, blk, 0, s>>>(p); break;
     case 64:
-      if constexpr (D / DS >= 64) decode_kernel<D, R, NW, DS, true, 64, true, false><<<g, blk, 0, s>>>(p);
+      if constexpr (D / DS >= 64) decode_kernel<D, R, NW, DS, true, 64, true, false, DN><<<g, blk, 0, s>>>(p);
       else return hipErrorInvalidValue;
       break;
     case 128:
-      if constexpr (D / DS >= 128) decode_kernel<D, R, NW, DS, true, 128, true, false><<<g, blk, 0, s>>>(p);
+      if constexpr (D / DS >= 128) decode_kernel<D, R, NW, DS, true, 128, true, false, DN><<<g, blk, 0, s>>>(p);
       else return hipErrorInvalidValue;
       break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int D, int R, int NW, int DS>
+static hipError_t launch_d(const DecodeParams& p, bool shared, int rd, bool treat, dim3 g, bool dn,
+                           hipStream_t s) {
+  return dn ? launch_dd<D, R, NW, DS, true>(p, shared, rd, treat, g, s)
+            : launch_dd<D, R, NW, DS, false>(p, shared, rd, treat, g, s);
+}
+
+// Whether every tensor of a decode call has dense row-major strides.
+static bool decode_dense(const lbca_decode_args& a, int qrows) {
+  const int64_t B = a.batch / qrows, Hk = a.kv_heads, d = a.dim;
+  auto q_like = [&](const void* ptr, const lbca_strides& st) {
+    return qrows > 1 ? dense_strides(ptr, st, {B, (int64_t)qrows, a.q_heads}, d)
+                     : dense_strides(ptr, st, {a.batch, a.q_heads}, d);
+  };
+  return q_like(a.q, a.q_st) && q_like(a.out, a.out_st) &&
+         dense_strides(a.pooled_k, a.pooled_k_st, {B, Hk, a.entries}, d) &&
+         dense_strides(a.pooled_v, a.pooled_v_st, {B, Hk, a.entries}, d) &&
+         dense_strides(a.raw_k, a.raw_k_st, {B, Hk, a.raw_rows}, d) &&
+         dense_strides(a.raw_v, a.raw_v_st, {B, Hk, a.raw_rows}, d);
+}
+
+// Query and output strides as {sequence, query, head}: a decode call's q and
+// out are [batch, heads, dim]; a query chunk's (qrows > 1) [batch, qrows,
+// heads, dim].  A shared series reads its values with the key strides.
+static void set_strides(DecodeParams& p, const lbca_decode_args& a, int qrows) {
+  auto qform = [&](const lbca_strides& s) {
+    return qrows > 1 ? s : lbca_strides{{s.s[0], 0, s.s[1]}};
+  };
+  p.q_st = qform(a.q_st);
+  p.o_st = qform(a.out_st);
+  p.pk_st = a.pooled_k_st;
+  p.rk_st = a.raw_k_st;
+  p.pv_st = a.pooled_v ? a.pooled_v_st : a.pooled_k_st;
+  p.rv_st = a.raw_v ? a.raw_v_st : a.raw_k_st;
 }
 
 hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void* ws,
@@ -985,6 +1052,8 @@ hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void
   p.rv = static_cast<const bf16_t*>(a.raw_v);
   p.pos = a.pos; p.rpb = a.raw_pos_base; p.sel = a.sel_idx; p.sink = a.sink;
   p.out = a.out; p.lse = a.lse;
+  set_strides(p, a, qrows);
+  const bool dn = decode_dense(a, qrows);
   const size_t units = (size_t)a.batch * a.kv_heads * plan.head_groups;
   if (plan.splits > 1) {
     p.ws_ml = static_cast<float*>(ws);
@@ -1004,7 +1073,7 @@ hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void
   const bool shared = a.pooled_v == nullptr;
   const bool treat = a.rmsnorm_eps >= 0.f || a.rope_dims > 0;
   if (plan.wide_blocks > 0) {
-    hipError_t e = launch_decode_wide(p, a.rope_dims, treat, plan.wide_blocks, stream);
+    hipError_t e = launch_decode_wide(p, a.rope_dims, treat, plan.wide_blocks, dn, stream);
     if (e != hipSuccess || plan.splits == 1) return e;
     launch_decode_merge(p, a.batch, a.dim, true, stream);
     return hipGetLastError();
@@ -1014,12 +1083,12 @@ hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void
   const dim3 g((unsigned)(ds == 1 ? pairs : (pairs + 7) / 8 * 8 * ds));
   hipError_t e;
   switch (a.dim * 4 + ds) {
-    case 64 * 4 + 1: e = launch_d<64, 32, 8, 1>(p, shared, a.rope_dims, treat, g, stream); break;
-    case 128 * 4 + 1: e = launch_d<128, 32, 8, 1>(p, shared, a.rope_dims, treat, g, stream); break;
-    case 128 * 4 + 2: e = launch_d<128, 32, 8, 2>(p, shared, a.rope_dims, treat, g, stream); break;
-    case 256 * 4 + 1: e = launch_d<256, 32, 4, 1>(p, shared, a.rope_dims, treat, g, stream); break;
-    case 256 * 4 + 2: e = launch_d<256, 32, 4, 2>(p, shared, a.rope_dims, treat, g, stream); break;
-    case 512 * 4 + 2: e = launch_d<512, 16, 4, 2>(p, shared, a.rope_dims, treat, g, stream); break;
+    case 64 * 4 + 1: e = launch_d<64, 32, 8, 1>(p, shared, a.rope_dims, treat, g, dn, stream); break;
+    case 128 * 4 + 1: e = launch_d<128, 32, 8, 1>(p, shared, a.rope_dims, treat, g, dn, stream); break;
+    case 128 * 4 + 2: e = launch_d<128, 32, 8, 2>(p, shared, a.rope_dims, treat, g, dn, stream); break;
+    case 256 * 4 + 1: e = launch_d<256, 32, 4, 1>(p, shared, a.rope_dims, treat, g, dn, stream); break;
+    case 256 * 4 + 2: e = launch_d<256, 32, 4, 2>(p, shared, a.rope_dims, treat, g, dn, stream); break;
+    case 512 * 4 + 2: e = launch_d<512, 16, 4, 2>(p, shared, a.rope_dims, treat, g, dn, stream); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || plan.splits == 1) return e;
@@ -1030,10 +1099,16 @@ hipError_t launch_decode(const lbca_decode_args& a, const DecodePlan& plan, void
 // ---------------------------------------------------------------------------
 // Fused decode step: the decode launch of launch_decode with the cache rows'
 // workgroups appended (plus the merge when the rows are split).
+// dn: every tensor of the call dense (instances that work the strides out from the sizes).
 template <int D, int DS, typename TZ>
-static void launch_step_d(const StepParams& sp, bool spec, unsigned grid, hipStream_t s) {
-  if (spec) decode_step_kernel<D, 32, 8, DS, true, TZ><<<grid, 512, 0, s>>>(sp);
-  else decode_step_kernel<D, 32, 8, DS, false, TZ><<<grid, 512, 0, s>>>(sp);
+static void launch_step_d(const StepParams& sp, bool spec, bool dn, unsigned grid, hipStream_t s) {
+  if (dn) {
+    if (spec) decode_step_kernel<D, 32, 8, DS, true, TZ, true><<<grid, 512, 0, s>>>(sp);
+    else decode_step_kernel<D, 32, 8, DS, false, TZ, true><<<grid, 512, 0, s>>>(sp);
+  } else {
+    if (spec) decode_step_kernel<D, 32, 8, DS, true, TZ, false><<<grid, 512, 0, s>>>(sp);
+    else decode_step_kernel<D, 32, 8, DS, false, TZ, false><<<grid, 512, 0, s>>>(sp);
+  }
 }
 
 hipError_t launch_decode_step(const lbca_decode_args& da, const lbca_cache_args& ca, const DecodePlan& plan,
@@ -1048,8 +1123,11 @@ hipError_t launch_decode_step(const lbca_decode_args& da, const lbca_cache_args&
   p.rv = static_cast<const bf16_t*>(da.raw_v);
   p.pos = da.pos; p.rpb = nullptr; p.sel = nullptr; p.sink = da.sink;
   p.out = da.out; p.lse = da.lse;
+  set_strides(p, da, 1);
   p.tk = static_cast<const bf16_t*>(ca.x_new);
   p.tv = static_cast<const bf16_t*>(ca.v_new);
+  p.tk_st = ca.x_new_st;
+  p.tv_st = ca.v_new_st;
   p.ring = ca.ring;
   const size_t units = (size_t)da.batch * da.kv_heads * plan.head_groups;
   if (plan.splits > 1) {
@@ -1073,20 +1151,28 @@ hipError_t launch_decode_step(const lbca_decode_args& da, const lbca_cache_args&
   c.lanes_per_row = (int)(ca.dim / 8);
   c.log2_lanes = __builtin_ctz((unsigned)c.lanes_per_row);
   c.eps = -1.f;
+  set_cache_strides(c, ca);
   const size_t pairs = units * plan.splits;
   const int ds = plan.dim_splits;
   const unsigned grid = (unsigned)(ds == 1 ? pairs : (pairs + 7) / 8 * 8 * ds);
   const bool spec = plan.splits == 1;
   const bool zf = ca.z_dtype == LBCA_F32;
+  const int64_t B = ca.batch, H = ca.heads, R = 2 * ca.ring, d = ca.dim;
+  const bool dn = decode_dense(da, 1) && dense_strides(ca.x_new, ca.x_new_st, {B, H}, d) &&
+                  dense_strides(ca.v_new, ca.v_new_st, {B, H}, d) && dense_strides(ca.z_new, ca.z_new_st, {B, H}, d) &&
+                  dense_strides(ca.raw_z, ca.raw_z_st, {B, H, R}, d);
   switch (da.dim * 4 + ds) {
     case 64 * 4 + 1:
-      zf ? launch_step_d<64, 1, float>(sp, spec, grid, stream) : launch_step_d<64, 1, bf16_t>(sp, spec, grid, stream);
+      zf ? launch_step_d<64, 1, float>(sp, spec, dn, grid, stream)
+         : launch_step_d<64, 1, bf16_t>(sp, spec, dn, grid, stream);
       break;
     case 128 * 4 + 1:
-      zf ? launch_step_d<128, 1, float>(sp, spec, grid, stream) : launch_step_d<128, 1, bf16_t>(sp, spec, grid, stream);
+      zf ? launch_step_d<128, 1, float>(sp, spec, dn, grid, stream)
+         : launch_step_d<128, 1, bf16_t>(sp, spec, dn, grid, stream);
       break;
     case 128 * 4 + 2:
-      zf ? launch_step_d<128, 2, float>(sp, spec, grid, stream) : launch_step_d<128, 2, bf16_t>(sp, spec, grid, stream);
+      zf ? launch_step_d<128, 2, float>(sp, spec, dn, grid, stream)
+         : launch_step_d<128, 2, bf16_t>(sp, spec, dn, grid, stream);
       break;
     default: return hipErrorInvalidValue;
   }

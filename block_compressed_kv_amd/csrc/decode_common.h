@@ -35,7 +35,17 @@ struct DecodeParams {
   const bf16_t* tk;
   const bf16_t* tv;
   int64_t ring;  // > 0 only in the fused step
+  // element strides.  q_st, o_st: {sequence, query of a chunk, head} (query
+  // row b is query b % qrows of sequence b / qrows); pk/pv/rk/rv:
+  // {sequence, KV head, row}; tk, tv: {sequence, KV head}
+  Str q_st, o_st, pk_st, pv_st, rk_st, rv_st, tk_st, tv_st;
 };
+
+// Element offset of head h of query row b in q (q_st) or out (o_st).
+__device__ __forceinline__ int64_t qrow_off(Str st, int qrows, int64_t b, int64_t h) {
+  if (qrows > 1) return (b / qrows) * st.s0 + (b % qrows) * st.s1 + h * st.s2;
+  return b * st.s0 + h * st.s2;
+}
 
 // Puts the argument fields a decode prologue needs into registers before its
 // first branch.  Left to itself the compiler loads kernel arguments one basic
@@ -46,6 +56,32 @@ __device__ __forceinline__ void preload_params(const DecodeParams& p) {
   asm volatile("" ::"s"(p.q), "s"(p.pk), "s"(p.pv), "s"(p.rk), "s"(p.rv), "s"(p.pos), "s"(p.rpb), "s"(p.sel),
                "s"(p.hq), "s"(p.hkv), "s"(p.G), "s"(p.entries), "s"(p.raw_rows), "s"(p.k_sel), "s"(p.m), "s"(p.W),
                "s"(p.mode), "s"(p.splits), "s"(p.head_groups), "s"(p.units), "s"(p.wide_twins));
+}
+// The strides that place the query and the cache slices (strided calls).
+__device__ __forceinline__ void preload_strides(const DecodeParams& p) {
+  asm volatile("" ::"s"(p.q_st.s0), "s"(p.q_st.s1), "s"(p.q_st.s2), "s"(p.pk_st.s0), "s"(p.pk_st.s1),
+               "s"(p.pk_st.s2), "s"(p.pv_st.s0), "s"(p.pv_st.s1), "s"(p.pv_st.s2), "s"(p.rk_st.s0),
+               "s"(p.rk_st.s1), "s"(p.rk_st.s2), "s"(p.rv_st.s0), "s"(p.rv_st.s1), "s"(p.rv_st.s2));
+}
+
+// The strides a decode workgroup places its rows with: the arguments', or,
+// when every tensor of the call is dense (DN), the row-major ones worked out
+// from the sizes, which leaves the stride arguments unread.
+struct DecStr {
+  Str q, o, pk, pv, rk, rv, tk, tv;
+};
+// (qrows: the query rows per cache sequence, 1 outside a query chunk)
+template <bool DN, int D>
+__device__ __forceinline__ DecStr dec_strides(const DecodeParams& p, int qrows) {
+  if constexpr (DN) {
+    const Str qs{(int64_t)qrows * p.hq * D, p.hq * D, D};
+    const Str ps{p.hkv * p.entries * D, p.entries * D, D};
+    const Str rs{p.hkv * p.raw_rows * D, p.raw_rows * D, D};
+    const Str ts{p.hkv * D, D, 0};
+    return DecStr{qs, qs, ps, ps, rs, rs, ts, ts};
+  } else {
+    return DecStr{p.q_st, p.o_st, p.pk_st, p.pv_st, p.rk_st, p.rv_st, p.tk_st, p.tv_st};
+  }
 }
 
 // A uniform value (a position, a raw base) requested before the row loads
@@ -105,7 +141,8 @@ __device__ __forceinline__ SeqView seq_view(const DecodeParams& p, int64_t b) {
 
 // Wide-row MQA decode (512 dims, shared series, query heads in blocks of 32
 // per KV head): launched by launch_decode when the plan selects it.
-hipError_t launch_decode_wide(const DecodeParams& p, int rope_dims, bool treat, int head_blocks,
+// dn: every tensor of the call dense (instances that work the strides out from the sizes).
+hipError_t launch_decode_wide(const DecodeParams& p, int rope_dims, bool treat, int head_blocks, bool dn,
                               hipStream_t stream);
 // norm: the partials are the wide path's normalised bf16 outputs (ws_o).
 void launch_decode_merge(const DecodeParams& p, int64_t batch, int64_t dim, bool norm, hipStream_t stream);

@@ -173,7 +173,7 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 }  // namespace
 
-template <int HB, int RD, bool TREAT, bool SEL>
+template <int HB, int RD, bool TREAT, bool SEL, bool DN>
 __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
   static_assert(HB == 1 || HB == 2, "one or two 32-head blocks");
   static_assert(RD == 0 || RD == 64 || RD == 128, "rotated dims");
@@ -188,6 +188,8 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
   __shared__ double s_freq[RD > 0 ? RD / 2 : 1];
 
   preload_params(p);
+  if constexpr (!DN) preload_strides(p);
+  const DecStr ST = dec_strides<DN, WD>(p, p.qrows);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = wave & 3, hb = wave >> 2;  // dim quarter, head block
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
   // not depend on the position, so they load alongside it
   uint4 qb[WKST];
   {
-    const bf16_t* qrow = p.q + (b * p.hq + head0 + n) * WD + WQ * q + 8 * g;
+    const bf16_t* qrow = p.q + qrow_off(ST.q, p.qrows, b, head0 + n) + WQ * q + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < WKST; ++ks) qb[ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks);
   }
@@ -245,9 +247,10 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
 
   // ---- tile copies: the waves of quarter q copy its 32 rows between them ----
   const int64_t cb = p.qrows > 1 ? (int64_t)((unsigned)b / (unsigned)p.qrows) : b;  // cache sequence
-  const uintptr_t pk_slice = reinterpret_cast<uintptr_t>(p.pk) + (uint64_t)((cb * p.hkv + kvh) * p.entries) * (WD * 2);
-  const uintptr_t rk_slice = reinterpret_cast<uintptr_t>(p.rk) + (uint64_t)((cb * p.hkv + kvh) * p.raw_rows) * (WD * 2);
-  const uintptr_t dummy = reinterpret_cast<uintptr_t>(p.q + (b * p.hq + kvh * p.G) * WD);  // 1 KB, cached
+  const uintptr_t pk_slice = reinterpret_cast<uintptr_t>(p.pk + cb * ST.pk.s0 + kvh * ST.pk.s1);
+  const uintptr_t rk_slice = reinterpret_cast<uintptr_t>(p.rk + cb * ST.rk.s0 + kvh * ST.rk.s1);
+  const uint32_t pks = 2u * (uint32_t)ST.pk.s2, rks = 2u * (uint32_t)ST.rk.s2;  // row strides, bytes
+  const uintptr_t dummy = reinterpret_cast<uintptr_t>(p.q + qrow_off(ST.q, p.qrows, b, kvh * p.G));  // 1 KB, cached
   const int rq = lane >> 4, c_lane = lane & 15;  // row within 4 and LDS chunk this lane writes
   // Row v of the tile's part of the list -> (valid, buffer row).
   auto locate = [&](bool raw, int v, int64_t& row) __attribute__((always_inline)) -> bool {
@@ -269,25 +272,31 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
   auto tile_full = [&](bool raw, int v0) __attribute__((always_inline)) {
     return raw ? v0 + WTR <= sv.n_raw : (!SEL && v0 + WTR <= sv.n_sel);
   };
-  // byte offset within a row run of this lane's copy j (row 4(hb*NI + j) + rq)
+  // byte offset of this lane's copy j (row 4(hb*NI + j) + rq) within its row,
+  // plus (dense rows) the row's offset within a run of rows
   uint32_t lane_off[NI];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     const int r = 4 * (hb * NI + j) + rq;
-    lane_off[j] = (uint32_t)(r * WD * 2 + WQ * 2 * q) + 16u * (uint32_t)(c_lane ^ wswz(r));
+    lane_off[j] = (DN ? (uint32_t)(r * WD * 2) : 0u) + (uint32_t)(WQ * 2 * q) + 16u * (uint32_t)(c_lane ^ wswz(r));
   }
+  // a run's row offset of copy j for row stride rs (strided rows)
+  auto run_off = [&](int j, uint32_t rs) __attribute__((always_inline)) -> uint64_t {
+    return DN ? 0 : (uint64_t)(uint32_t)(4 * (hb * NI + j) + rq) * rs;
+  };
   // Issues this wave's NI copies of `tile` into ring slot `slot`.
   auto issue = [&](int tile, int slot) __attribute__((always_inline)) {
     const bool raw = tile >= tiles_p;
     const int v0 = raw ? (tile - tiles_p) * WTR : tile * WTR;
     const uintptr_t sb = raw ? rk_slice : pk_slice;
+    const uint32_t rs = raw ? rks : pks;
     uint8_t* dst0 = ring + slot * (4 * WQB) + q * WQB + hb * NI * 1024;
     if (tile_full(raw, v0)) {  // consecutive rows, all in the list
-      const uintptr_t base = sb + (uint64_t)(raw ? sv.raw_row0 + v0 : (int64_t)v0) * (WD * 2);
+      const uintptr_t base = sb + (uint64_t)(raw ? sv.raw_row0 + v0 : (int64_t)v0) * rs;
 #pragma unroll
       for (int j = 0; j < NI; ++j)
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(base + lane_off[j]), (lds_void*)(dst0 + j * 1024),
-                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(base + run_off(j, rs) + lane_off[j]),
+                                         (lds_void*)(dst0 + j * 1024), 16, 0, 0);
       return;
     }
 #pragma unroll
@@ -296,7 +305,7 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
       int64_t row;
       const bool ok = locate(raw, v0 + r, row);
       const uint32_t coff = (uint32_t)(WQ * 2 * q) + 16u * (uint32_t)(c_lane ^ wswz(r));
-      const uintptr_t ga = (ok ? sb + (uint64_t)row * (WD * 2) : dummy) + coff;
+      const uintptr_t ga = (ok ? sb + (uint64_t)row * rs : dummy) + coff;
       __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(ga), (lds_void*)(dst0 + j * 1024), 16, 0, 0);
     }
   };
@@ -306,11 +315,11 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
     const int v0 = tile * WTR;
     uint8_t* dst0 = ring + slot * (4 * WQB) + q * WQB + hb * NI * 1024;
     if (!SEL && v0 + WTR <= cap_sel) {
-      const uintptr_t base = pk_slice + (uint64_t)v0 * (WD * 2);
+      const uintptr_t base = pk_slice + (uint64_t)v0 * pks;
 #pragma unroll
       for (int j = 0; j < NI; ++j)
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(base + lane_off[j]), (lds_void*)(dst0 + j * 1024),
-                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(base + run_off(j, pks) + lane_off[j]),
+                                         (lds_void*)(dst0 + j * 1024), 16, 0, 0);
       return;
     }
 #pragma unroll
@@ -325,7 +334,7 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
         ok = ok && id >= 0 && id < p.entries;
       }
       const uint32_t coff = (uint32_t)(WQ * 2 * q) + 16u * (uint32_t)(c_lane ^ wswz(r));
-      const uintptr_t ga = (ok ? pk_slice + (uint64_t)id * (WD * 2) : dummy) + coff;
+      const uintptr_t ga = (ok ? pk_slice + (uint64_t)id * pks : dummy) + coff;
       __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(ga), (lds_void*)(dst0 + j * 1024), 16, 0, 0);
     }
   };
@@ -341,7 +350,8 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
     vm_wait<0>();
     if (split == 0) {
       const int64_t h0 = kvh * p.G + 32 * HB * (int)tw;
-      for (int i = tid; i < 32 * HB * WD; i += 256 * HB) p.out[(b * p.hq + h0) * WD + i] = __builtin_nanf("");
+      for (int i = tid; i < 32 * HB * WD; i += 256 * HB)
+        p.out[qrow_off(ST.o, p.qrows, b, h0 + i / WD) + i % WD] = __builtin_nanf("");
       if (p.lse && tid < 32 * HB) p.lse[b * p.hq + h0 + tid] = __builtin_nanf("");
     }
     return;
@@ -684,7 +694,7 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
           }
       }
     }
-    float* o = p.out + (b * p.hq + head) * WD + WQ * q + 4 * g;
+    float* o = p.out + qrow_off(ST.o, p.qrows, b, head) + WQ * q + 4 * g;
 #pragma unroll
     for (int db = 0; db < WDB; ++db)
 #pragma unroll
@@ -713,7 +723,7 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
   }
 }
 
-hipError_t launch_decode_wide(const DecodeParams& p, int rope_dims, bool treat, int head_blocks,
+hipError_t launch_decode_wide(const DecodeParams& p, int rope_dims, bool treat, int head_blocks, bool dn,
                               hipStream_t stream) {
   const unsigned pairs = (unsigned)(p.units / p.head_groups) * (unsigned)p.splits;  // (sequence, KV head, split)
   const dim3 grid(p.wide_twins > 1 ? (pairs + 7) / 8 * 8 * (unsigned)p.wide_twins : pairs);
@@ -722,18 +732,26 @@ hipError_t launch_decode_wide(const DecodeParams& p, int rope_dims, bool treat, 
     kern<<<grid, 256 * hb, 0, stream>>>(p);
     return hipGetLastError();
   };
-  auto pick = [&](auto hbc) -> hipError_t {
+  auto pick = [&](auto hbc, auto dnc) -> hipError_t {
     constexpr int HB = decltype(hbc)::value;
-    if (!treat) return sel ? go(decode_wide_kernel<HB, 0, false, true>, HB) : go(decode_wide_kernel<HB, 0, false, false>, HB);
+    constexpr bool DN = decltype(dnc)::value;
+    if (!treat)
+      return sel ? go(decode_wide_kernel<HB, 0, false, true, DN>, HB) : go(decode_wide_kernel<HB, 0, false, false, DN>, HB);
     switch (rope_dims) {
-      case 0: return sel ? go(decode_wide_kernel<HB, 0, true, true>, HB) : go(decode_wide_kernel<HB, 0, true, false>, HB);
-      case 64: return sel ? go(decode_wide_kernel<HB, 64, true, true>, HB) : go(decode_wide_kernel<HB, 64, true, false>, HB);
-      case 128: return sel ? go(decode_wide_kernel<HB, 128, true, true>, HB) : go(decode_wide_kernel<HB, 128, true, false>, HB);
+      case 0:
+        return sel ? go(decode_wide_kernel<HB, 0, true, true, DN>, HB) : go(decode_wide_kernel<HB, 0, true, false, DN>, HB);
+      case 64:
+        return sel ? go(decode_wide_kernel<HB, 64, true, true, DN>, HB) : go(decode_wide_kernel<HB, 64, true, false, DN>, HB);
+      case 128:
+        return sel ? go(decode_wide_kernel<HB, 128, true, true, DN>, HB)
+                   : go(decode_wide_kernel<HB, 128, true, false, DN>, HB);
       default: return hipErrorInvalidValue;
     }
   };
-  if (head_blocks == 2) return pick(std::integral_constant<int, 2>{});
-  if (head_blocks == 1) return pick(std::integral_constant<int, 1>{});
+  using T = std::true_type;
+  using F = std::false_type;
+  if (head_blocks == 2) return dn ? pick(std::integral_constant<int, 2>{}, T{}) : pick(std::integral_constant<int, 2>{}, F{});
+  if (head_blocks == 1) return dn ? pick(std::integral_constant<int, 1>{}, T{}) : pick(std::integral_constant<int, 1>{}, F{});
   return hipErrorInvalidValue;
 }
 

@@ -36,6 +36,8 @@ struct IndexParams {
   int slices;                            // two-stage selection: slices of kSliceLen entries
   int64_t cstride;                       // candidates per sequence, rounded up to 4
   int64_t qrows;                         // chunk scoring: query rows per key sequence
+  // element strides: queries {sequence, query of a chunk, head}, keys {sequence, entry}
+  Str q_st, k_st;
 };
 
 __device__ __forceinline__ int64_t n_visible(const IndexParams& p, int64_t b) {
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexParams p) {
   const int64_t key0 = ((int64_t)blockIdx.x * 4 + wave) * 64;
   if (key0 >= nv) return;  // whole wave beyond the visible keys
   const bool head_ok = n < p.heads;
-  const bf16_t* qrow = p.q + (b * p.heads + (head_ok ? n : 0)) * DI + 8 * kq;
+  const bf16_t* qrow = p.q + b * p.q_st.s0 + (head_ok ? n : 0) * p.q_st.s2 + 8 * kq;
   uint4 qr[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) qr[s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexParams p) {
   for (int hh = 0; hh < 4; ++hh) {
     int64_t key = key0 + 16 * hh + n;
     key = key < nv ? key : nv - 1;
-    const bf16_t* krow = p.keys + (b * p.entries + key) * DI + 8 * kq;
+    const bf16_t* krow = p.keys + b * p.k_st.s0 + key * p.k_st.s1 + 8 * kq;
 #pragma unroll
     for (int s = 0; s < KS; ++s) kv[hh][s] = *reinterpret_cast<const uint4*>(krow + 32 * s);
   }
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(256) void index_score_chunk_kernel(IndexParams p) {
   for (int hh = 0; hh < 4; ++hh) {
     int64_t key = key0 + 16 * hh + n;
     key = key < nv_last ? key : nv_last - 1;
-    const bf16_t* krow = p.keys + (seq * p.entries + key) * DI + 8 * kq;
+    const bf16_t* krow = p.keys + seq * p.k_st.s0 + key * p.k_st.s1 + 8 * kq;
 #pragma unroll
     for (int s = 0; s < KS; ++s) kv[hh][s] = *reinterpret_cast<const uint4*>(krow + 32 * s);
   }
@@ -156,10 +158,13 @@ __global__ __launch_bounds__(256) void index_score_chunk_kernel(IndexParams p) {
   const int hsafe = head_ok ? hd : 0;
   // query slot i + qo of the group: its row (clamped into the group), rows and weight
   auto row_of = [&](int64_t i) { return r0 + (i + qo < qn ? i + qo : i); };
+  // query row r (query r - seq * qrows of the sequence), this lane's head
+  const bf16_t* qseq = p.q + seq * p.q_st.s0 + hsafe * p.q_st.s2 + 8 * kq;
+  auto qrow_of = [&](int64_t rr) { return qseq + (rr - seq * p.qrows) * p.q_st.s1; };
   uint4 qr[KS];
   int64_t r = row_of(0);
 #pragma unroll
-  for (int s = 0; s < KS; ++s) qr[s] = *reinterpret_cast<const uint4*>(p.q + (r * p.heads + hsafe) * DI + 8 * kq + 32 * s);
+  for (int s = 0; s < KS; ++s) qr[s] = *reinterpret_cast<const uint4*>(qrow_of(r) + 32 * s);
   float wv = p.w[r * p.heads + hsafe];
   int64_t tpos = p.pos[r];
   for (int64_t i = 0; i < qn; i += QP) {
@@ -168,7 +173,7 @@ __global__ __launch_bounds__(256) void index_score_chunk_kernel(IndexParams p) {
     uint4 qn_r[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      qn_r[s] = *reinterpret_cast<const uint4*>(p.q + (rn * p.heads + hsafe) * DI + 8 * kq + 32 * s);
+      qn_r[s] = *reinterpret_cast<const uint4*>(qrow_of(rn) + 32 * s);
     const float wn = p.w[rn * p.heads + hsafe];
     const int64_t tn = p.pos[rn];
     const bool q_ok = i + qo < qn;
@@ -554,6 +559,8 @@ static IndexParams index_params(const csa_index_args& a, void* ws) {
     p.cand_id = reinterpret_cast<int32_t*>(p.cand_key + a.batch * p.cstride);
   }
   p.qrows = 1;
+  p.q_st = lbca_strides{{a.q_idx_st.s[0], 0, a.q_idx_st.s[1]}};  // [batch, heads, dim]
+  p.k_st = a.keys_st;
   return p;
 }
 
@@ -582,6 +589,7 @@ hipError_t launch_index_topk_chunk(const csa_index_args& a, int64_t q_len, int64
   IndexParams p = index_params(a, ws);
   p.pos = pos_ws;
   p.qrows = q_len;
+  p.q_st = a.q_idx_st;  // a query chunk's rows: {sequence, query, head}
   if (a.entries > 0) {
     const dim3 grid((unsigned)((a.entries + 255) / 256), (unsigned)((q_len + kChunkQ - 1) / kChunkQ),
                     (unsigned)(a.batch / q_len));

@@ -2,9 +2,38 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include <initializer_list>
+
 #include "lbca.h"
 
 namespace lbca {
+
+// Element strides of one tensor argument as the kernels hold them,
+// outermost dimension first: the outermost (sequence) stride in 64 bits, the
+// other two in 32 (the entry points reject inner strides of 2^31 elements or
+// more), which keeps the kernels' scalar registers free.
+struct Str {
+  int64_t s0;
+  int32_t s1, s2;
+  Str() = default;
+  Str(const lbca_strides& a) : s0(a.s[0]), s1((int32_t)a.s[1]), s2((int32_t)a.s[2]) {}
+  __host__ __device__ constexpr Str(int64_t a, int64_t b, int64_t c) : s0(a), s1((int32_t)b), s2((int32_t)c) {}
+};
+
+// Whether the strides of a tensor with outer extents ext (outermost first) and
+// feature dim d are the dense row-major ones (dimensions of extent 1 aside,
+// whose strides are never used).  An absent tensor counts as dense.
+inline bool dense_strides(const void* ptr, const lbca_strides& st, std::initializer_list<int64_t> ext, int64_t d) {
+  if (!ptr) return true;
+  const int n = (int)ext.size();
+  const int64_t* e = ext.begin();
+  int64_t s = d;
+  for (int i = n - 1; i >= 0; --i) {
+    if (e[i] > 1 && st.s[i] != s) return false;
+    s *= e[i] > 0 ? e[i] : 1;
+  }
+  return true;
+}
 
 // Host validation has already run when these are called; they only pick the
 // kernel instance and launch it on `stream`.

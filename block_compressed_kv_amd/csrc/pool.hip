@@ -41,6 +41,7 @@ struct PoolParams {
   const float* bias_b;
   void* out_x;
   void* out_v;
+  Str x_st, v_st, z_st, xb_st, zb_st, ox_st, ov_st;  // {sequence, head, row}
   int64_t heads, tokens, dim, m, entries, block_begin, n_blocks, pos_base, total_rows;
   int lanes_per_row;  // L = dim / 8, a power of two <= 64
   int log2_lanes;
@@ -50,8 +51,25 @@ struct PoolParams {
   double log2_base;
 };
 
-template <typename TX, typename TZ, bool DUAL, bool HAS_V, bool TREAT>
+// The strides of a pooling pass: the arguments', or, when every tensor of the
+// call is dense (DN), the row-major ones worked out from the sizes.
+struct PoolStr {
+  Str x, v, z, xb, zb, ox, ov;
+};
+template <bool DN>
+__device__ __forceinline__ PoolStr pool_strides(const PoolParams& p) {
+  if constexpr (DN) {
+    const Str tok{p.heads * p.tokens * p.dim, p.tokens * p.dim, p.dim};
+    const Str ent{p.heads * p.entries * p.dim, p.entries * p.dim, p.dim};
+    return PoolStr{tok, tok, tok, tok, tok, ent, ent};
+  } else {
+    return PoolStr{p.x_st, p.v_st, p.z_st, p.xb_st, p.zb_st, p.ox_st, p.ov_st};
+  }
+}
+
+template <typename TX, typename TZ, bool DUAL, bool HAS_V, bool TREAT, bool DN>
 __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
+  const PoolStr S = pool_strides<DN>(p);
   __shared__ float part[32][256];  // [state value][thread], used when P > 1
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -68,46 +86,50 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
 
   const int64_t j = p.block_begin + rr % p.n_blocks;  // entry index
   const int64_t bh = rr / p.n_blocks;                // sequence * heads + head
-  const int64_t h = bh % p.heads;
+  const int64_t h = bh % p.heads, b = bh / p.heads;
   const int64_t dim = p.dim;
   const int64_t c0 = (int64_t)li * 8;
-  const int64_t series = bh * p.tokens * dim + c0;
+  auto at = [&](Str st, int64_t r) { return b * st.s0 + h * st.s1 + r * st.s2 + c0; };
   const float* bias_h = p.bias + h * p.m * dim + c0;
 
   PoolAcc<TX, TZ, HAS_V> acc;
   acc.init();
   if (active) {
     const int64_t r0 = j * p.m - p.pos_base;  // token row of the entry's own block
-    acc.run(static_cast<const TX*>(p.x) + series + r0 * dim,
-            HAS_V ? static_cast<const TX*>(p.v) + series + r0 * dim : nullptr,
-            static_cast<const TZ*>(p.z) + series + r0 * dim, bias_h, phase, P, p.m, dim);
+    acc.run(static_cast<const TX*>(p.x) + at(S.x, r0), HAS_V ? static_cast<const TX*>(p.v) + at(S.v, r0) : nullptr,
+            static_cast<const TZ*>(p.z) + at(S.z, r0), bias_h, phase, P, p.m, dim, RowPitch{S.x.s2, S.v.s2, S.z.s2});
     if (DUAL && j > 0) {
       const int64_t rb = r0 - p.m;  // preceding block, b-series
-      acc.run(static_cast<const TX*>(p.xb) + series + rb * dim, nullptr,
-              static_cast<const TZ*>(p.zb) + series + rb * dim, p.bias_b + h * p.m * dim + c0,
-              phase, P, p.m, dim);
+      acc.run(static_cast<const TX*>(p.xb) + at(S.xb, rb), nullptr, static_cast<const TZ*>(p.zb) + at(S.zb, rb),
+              p.bias_b + h * p.m * dim + c0, phase, P, p.m, dim, RowPitch{S.xb.s2, 0, S.zb.s2});
     }
   }
 
-  const int64_t o = (bh * p.entries + j) * dim + c0;
   finish_entry<TX, TZ, HAS_V, TREAT>(acc, part, L, P, phase, active, dim, c0, j * p.m,
-                                     EntryTreat{p.eps, p.rope_dims, p.log2_base}, static_cast<TX*>(p.out_x) + o,
-                                     HAS_V ? static_cast<TX*>(p.out_v) + o : nullptr);
+                                     EntryTreat{p.eps, p.rope_dims, p.log2_base},
+                                     static_cast<TX*>(p.out_x) + at(S.ox, j),
+                                     HAS_V ? static_cast<TX*>(p.out_v) + at(S.ov, j) : nullptr);
+}
+
+template <typename TX, typename TZ, bool DN>
+static hipError_t launch_typed_d(const PoolParams& p, bool dual, bool has_v, bool treat, dim3 grid, hipStream_t s) {
+  if (dual) {
+    if (treat) pool_kernel<TX, TZ, true, false, true, DN><<<grid, 256, 0, s>>>(p);
+    else pool_kernel<TX, TZ, true, false, false, DN><<<grid, 256, 0, s>>>(p);
+  } else if (has_v) {
+    pool_kernel<TX, TZ, false, true, false, DN><<<grid, 256, 0, s>>>(p);
+  } else {
+    if (treat) pool_kernel<TX, TZ, false, false, true, DN><<<grid, 256, 0, s>>>(p);
+    else pool_kernel<TX, TZ, false, false, false, DN><<<grid, 256, 0, s>>>(p);
+  }
+  return hipGetLastError();
 }
 
 template <typename TX, typename TZ>
-static hipError_t launch_typed(const PoolParams& p, bool dual, bool has_v, bool treat, dim3 grid,
+static hipError_t launch_typed(const PoolParams& p, bool dual, bool has_v, bool treat, dim3 grid, bool dn,
                                hipStream_t s) {
-  if (dual) {
-    if (treat) pool_kernel<TX, TZ, true, false, true><<<grid, 256, 0, s>>>(p);
-    else pool_kernel<TX, TZ, true, false, false><<<grid, 256, 0, s>>>(p);
-  } else if (has_v) {
-    pool_kernel<TX, TZ, false, true, false><<<grid, 256, 0, s>>>(p);
-  } else {
-    if (treat) pool_kernel<TX, TZ, false, false, true><<<grid, 256, 0, s>>>(p);
-    else pool_kernel<TX, TZ, false, false, false><<<grid, 256, 0, s>>>(p);
-  }
-  return hipGetLastError();
+  return dn ? launch_typed_d<TX, TZ, true>(p, dual, has_v, treat, grid, s)
+            : launch_typed_d<TX, TZ, false>(p, dual, has_v, treat, grid, s);
 }
 
 hipError_t launch_pool(const lbca_pool_args& a, hipStream_t stream) {
@@ -115,6 +137,8 @@ hipError_t launch_pool(const lbca_pool_args& a, hipStream_t stream) {
   p.x = a.x; p.v = a.v; p.z = a.z; p.bias = a.bias;
   p.xb = a.xb; p.zb = a.zb; p.bias_b = a.bias_b;
   p.out_x = a.out_x; p.out_v = a.out_v;
+  p.x_st = a.x_st; p.v_st = a.v_st; p.z_st = a.z_st; p.xb_st = a.xb_st; p.zb_st = a.zb_st;
+  p.ox_st = a.out_x_st; p.ov_st = a.out_v_st;
   p.heads = a.heads; p.tokens = a.tokens; p.dim = a.dim; p.m = a.block; p.entries = a.entries;
   p.block_begin = a.block_begin; p.n_blocks = a.block_end - a.block_begin;
   p.pos_base = a.pos_base;
@@ -136,12 +160,17 @@ hipError_t launch_pool(const lbca_pool_args& a, hipStream_t stream) {
   dim3 grid((unsigned)((p.total_rows + rows_per_wg - 1) / rows_per_wg));
   const bool dual = a.xb != nullptr, has_v = a.v != nullptr;
   const bool treat = a.rmsnorm_eps >= 0.f || a.rope_dims > 0;
+  const int64_t B = a.batch, H = a.heads, T = a.tokens, N = a.entries, d = a.dim;
+  const bool dn = dense_strides(a.x, a.x_st, {B, H, T}, d) && dense_strides(a.v, a.v_st, {B, H, T}, d) &&
+                  dense_strides(a.z, a.z_st, {B, H, T}, d) && dense_strides(a.xb, a.xb_st, {B, H, T}, d) &&
+                  dense_strides(a.zb, a.zb_st, {B, H, T}, d) && dense_strides(a.out_x, a.out_x_st, {B, H, N}, d) &&
+                  dense_strides(a.out_v, a.out_v_st, {B, H, N}, d);
   if (a.x_dtype == LBCA_BF16) {
-    if (a.z_dtype == LBCA_BF16) return launch_typed<bf16_t, bf16_t>(p, dual, has_v, treat, grid, stream);
-    return launch_typed<bf16_t, float>(p, dual, has_v, treat, grid, stream);
+    if (a.z_dtype == LBCA_BF16) return launch_typed<bf16_t, bf16_t>(p, dual, has_v, treat, grid, dn, stream);
+    return launch_typed<bf16_t, float>(p, dual, has_v, treat, grid, dn, stream);
   }
-  if (a.z_dtype == LBCA_BF16) return launch_typed<float, bf16_t>(p, dual, has_v, treat, grid, stream);
-  return launch_typed<float, float>(p, dual, has_v, treat, grid, stream);
+  if (a.z_dtype == LBCA_BF16) return launch_typed<float, bf16_t>(p, dual, has_v, treat, grid, dn, stream);
+  return launch_typed<float, float>(p, dual, has_v, treat, grid, dn, stream);
 }
 
 }  // namespace lbca

@@ -12,6 +12,11 @@
 
 namespace lbca {
 
+// Row strides (elements) of the token series a pooling pass reads.
+struct RowPitch {
+  int64_t x, v, z;
+};
+
 template <typename TX, typename TZ, bool HAS_V>
 struct PoolAcc {
   float mx[8], l[8], ax[8], av[8];
@@ -21,24 +26,25 @@ struct PoolAcc {
     for (int c = 0; c < 8; ++c) { mx[c] = kNegInf; l[c] = 0.f; ax[c] = 0.f; av[c] = 0.f; }
   }
 
-  // Fold NT tokens, `stride` rows apart, into the state (bias rows stride apart too).
+  // Fold NT tokens into the state: token i at xs + i * st.x, vs + i * st.v,
+  // zs + i * st.z, its bias row at bs + i * sb.
   template <int NT>
   __device__ __forceinline__ void fold(const TX* xs, const TX* vs, const TZ* zs, const float* bs,
-                                       int64_t stride) {
+                                       const RowPitch& st, int64_t sb) {
     float a[NT][8];
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       float zz[8], bb[8];
-      load8(zs + i * stride, zz);
-      load8(bs + i * stride, bb);
+      load8(zs + i * st.z, zz);
+      load8(bs + i * sb, bb);
 #pragma unroll
       for (int c = 0; c < 8; ++c) a[i][c] = (zz[c] + bb[c]) * kLog2e;
     }
     float xv[NT][8], vv[NT][8];
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      load8(xs + i * stride, xv[i]);
-      if constexpr (HAS_V) load8(vs + i * stride, vv[i]);
+      load8(xs + i * st.x, xv[i]);
+      if constexpr (HAS_V) load8(vs + i * st.v, vv[i]);
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -63,15 +69,16 @@ struct PoolAcc {
   }
 
   // Fold tokens first, first+P, ... (< count) of a block whose token 0 is at
-  // xs/vs/zs (row pitch dim) and whose bias row 0 is at bs.
+  // xs/vs/zs (row strides rp) and whose bias row 0 is at bs (row pitch dim).
   __device__ __forceinline__ void run(const TX* xs, const TX* vs, const TZ* zs, const float* bs,
-                                      int64_t first, int64_t P, int64_t count, int64_t dim) {
-    const int64_t stride = P * dim;
+                                      int64_t first, int64_t P, int64_t count, int64_t dim, const RowPitch& rp) {
+    const RowPitch st{P * rp.x, P * rp.v, P * rp.z};
+    const int64_t sb = P * dim;
     int64_t i = first;
     for (; i + 3 * P < count; i += 4 * P)
-      fold<4>(xs + i * dim, HAS_V ? vs + i * dim : nullptr, zs + i * dim, bs + i * dim, stride);
+      fold<4>(xs + i * rp.x, HAS_V ? vs + i * rp.v : nullptr, zs + i * rp.z, bs + i * dim, st, sb);
     for (; i < count; i += P)
-      fold<1>(xs + i * dim, HAS_V ? vs + i * dim : nullptr, zs + i * dim, bs + i * dim, stride);
+      fold<1>(xs + i * rp.x, HAS_V ? vs + i * rp.v : nullptr, zs + i * rp.z, bs + i * dim, st, sb);
   }
 
   // Combine channel c of two partial states, lower token phase first

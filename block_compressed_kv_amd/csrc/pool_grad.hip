@@ -51,6 +51,8 @@ struct PoolGradParams {
   int64_t batch, heads, tokens, dim, m, entries, block_begin, n_blocks, pos_base;
   int chunks, per_chunk;  // workgroups per head, blocks per workgroup
   int log2_lanes;
+  // element strides {sequence, head, row}: token rows and their gradients, entry gradients
+  Str x_st, v_st, z_st, xb_st, zb_st, dx_st, dv_st, dz_st, dxb_st, dzb_st, gx_st, gv_st;
 };
 
 constexpr int kGradNT = 256;  // threads per workgroup (4 waves)
@@ -64,19 +66,19 @@ template <typename TX, typename TZ, bool HAS_V>
 struct BlockRows {
   static constexpr int NX = (int)(sizeof(TX) * 8 / 16), NZ = (int)(sizeof(TZ) * 8 / 16);
   uint4 x[kGradTPL][NX], v[kGradTPL][HAS_V ? NX : 1], z[kGradTPL][NZ];
-  // token slot k's rows at element offset off[k] of its series (a or b per slot)
-  __device__ __forceinline__ void load(const TX* const* xs, const TX* vs, const TZ* const* zs, const int64_t* off,
+  // token slot k's rows at xp[k], vp[k], zp[k]
+  __device__ __forceinline__ void load(const TX* const* xp, const TX* const* vp, const TZ* const* zp,
                                        const bool* present) {
 #pragma unroll
     for (int k = 0; k < kGradTPL; ++k) {
       if (!present[k]) continue;
 #pragma unroll
       for (int i = 0; i < NX; ++i) {
-        x[k][i] = reinterpret_cast<const uint4*>(xs[k] + off[k])[i];
-        if constexpr (HAS_V) v[k][i] = reinterpret_cast<const uint4*>(vs + off[k])[i];
+        x[k][i] = reinterpret_cast<const uint4*>(xp[k])[i];
+        if constexpr (HAS_V) v[k][i] = reinterpret_cast<const uint4*>(vp[k])[i];
       }
 #pragma unroll
-      for (int i = 0; i < NZ; ++i) z[k][i] = reinterpret_cast<const uint4*>(zs[k] + off[k])[i];
+      for (int i = 0; i < NZ; ++i) z[k][i] = reinterpret_cast<const uint4*>(zp[k])[i];
     }
   }
 };
@@ -255,34 +257,48 @@ __global__ __launch_bounds__(kGradNT) void pool_grad_kernel(PoolGradParams p) {
   // slots u >= m (dual mode) are block j-1 of the b-series
   bool has[kGradTPL], is_b[kGradTPL];
   int64_t uoff[kGradTPL];  // row offset from the entry's own block start
-  const TX* xser[kGradTPL];
-  const TZ* zser[kGradTPL];
 #pragma unroll
   for (int k = 0; k < kGradTPL; ++k) {
     const int64_t u = phase + (int64_t)P * k;
     has[k] = u < M2;
     is_b[k] = DUAL && u >= m;
     uoff[k] = is_b[k] ? u - 2 * m : u;
-    xser[k] = static_cast<const TX*>(is_b[k] ? p.xb : p.x);
-    zser[k] = static_cast<const TZ*>(is_b[k] ? p.zb : p.z);
   }
-  auto block_of = [&](int64_t kk, int64_t& bh, int64_t& j, int64_t (&off)[kGradTPL], bool (&present)[kGradTPL]) {
-    const int64_t b = kk / p.n_blocks;
+  // element offset of this lane's channels of token row r of sequence b
+  auto at = [&](Str st, int64_t b, int64_t r) __attribute__((always_inline)) {
+    return b * st.s0 + (int64_t)h * st.s1 + r * st.s2 + c0;
+  };
+  // (sequence, entry) of list item kk and the token rows of this lane's slots
+  auto block_of = [&](int64_t kk, int64_t& b, int64_t& j, int64_t (&row)[kGradTPL], bool (&present)[kGradTPL]) {
+    b = kk / p.n_blocks;
     j = p.block_begin + kk % p.n_blocks;
-    bh = b * p.heads + h;
-    const int64_t row0 = bh * p.tokens + j * m - p.pos_base;
 #pragma unroll
     for (int k = 0; k < kGradTPL; ++k) {
-      off[k] = (row0 + uoff[k]) * dim + c0;
+      row[k] = j * m - p.pos_base + uoff[k];
       present[k] = has[k] && !(is_b[k] && j == 0);  // entry 0 has no b-part
     }
   };
+  auto load_rows = [&](BlockRows<TX, TZ, HAS_V>& br, int64_t b, const int64_t (&row)[kGradTPL],
+                       const bool (&present)[kGradTPL]) __attribute__((always_inline)) {
+    const TX* xp[kGradTPL];
+    const TX* vp[kGradTPL];
+    const TZ* zp[kGradTPL];
+#pragma unroll
+    for (int k = 0; k < kGradTPL; ++k) {
+      xp[k] = is_b[k] ? static_cast<const TX*>(p.xb) + at(p.xb_st, b, row[k])
+                      : static_cast<const TX*>(p.x) + at(p.x_st, b, row[k]);
+      vp[k] = HAS_V ? static_cast<const TX*>(p.v) + at(p.v_st, b, row[k]) : nullptr;
+      zp[k] = is_b[k] ? static_cast<const TZ*>(p.zb) + at(p.zb_st, b, row[k])
+                      : static_cast<const TZ*>(p.z) + at(p.z_st, b, row[k]);
+    }
+    br.load(xp, vp, zp, present);
+  };
   BlockRows<TX, TZ, HAS_V> cur;
   {
-    int64_t bh, j, off[kGradTPL];
+    int64_t b, j, row[kGradTPL];
     bool present[kGradTPL];
-    block_of(k0, bh, j, off, present);
-    cur.load(xser, static_cast<const TX*>(p.v), zser, off, present);
+    block_of(k0, b, j, row, present);
+    load_rows(cur, b, row, present);
   }
   if constexpr (TREAT) {
     if (tid < p.rope_dims / 2) s_freq[tid] = rope_turns_per_pos(tid, p.rope_dims, p.log2_base);
@@ -301,13 +317,12 @@ __global__ __launch_bounds__(kGradNT) void pool_grad_kernel(PoolGradParams p) {
     for (int c = 0; c < 8; ++c) db[k][c] = 0.f;
 
   for (int64_t kk = k0; kk < k1; ++kk) {
-    int64_t bh, j, off[kGradTPL];
+    int64_t b, j, row[kGradTPL];
     bool present[kGradTPL];
-    block_of(kk, bh, j, off, present);
-    const int64_t eo = (bh * p.entries + j) * dim + c0;
+    block_of(kk, b, j, row, present);
     float g[8], gvv[8];
-    load8(static_cast<const TX*>(p.gx) + eo, g);
-    if constexpr (HAS_V) load8(static_cast<const TX*>(p.gv) + eo, gvv);
+    load8(static_cast<const TX*>(p.gx) + at(p.gx_st, b, j), g);
+    if constexpr (HAS_V) load8(static_cast<const TX*>(p.gv) + at(p.gv_st, b, j), gvv);
     // logits (log2 units) of this lane's tokens, then the next block's rows go out
     float a[kGradTPL][8];
 #pragma unroll
@@ -321,10 +336,10 @@ __global__ __launch_bounds__(kGradNT) void pool_grad_kernel(PoolGradParams p) {
     }
     BlockRows<TX, TZ, HAS_V> nxt;
     if (kk + 1 < k1) {
-      int64_t bhn, jn, offn[kGradTPL];
+      int64_t bn, jn, rown[kGradTPL];
       bool presn[kGradTPL];
-      block_of(kk + 1, bhn, jn, offn, presn);
-      nxt.load(xser, static_cast<const TX*>(p.v), zser, offn, presn);
+      block_of(kk + 1, bn, jn, rown, presn);
+      load_rows(nxt, bn, rown, presn);
     }
     // this lane's state, then the block's
     GradState st;
@@ -387,9 +402,11 @@ __global__ __launch_bounds__(kGradNT) void pool_grad_kernel(PoolGradParams p) {
         oz[c] = w * da;
         db[k][c] += oz[c];
       }
-      store8(static_cast<TX*>(is_b[k] ? p.dxb : p.dx) + off[k], ox);
-      if constexpr (HAS_V) store8(static_cast<TX*>(p.dv) + off[k], ov);
-      store8(static_cast<TZ*>(is_b[k] ? p.dzb : p.dz) + off[k], oz);
+      store8(is_b[k] ? static_cast<TX*>(p.dxb) + at(p.dxb_st, b, row[k]) : static_cast<TX*>(p.dx) + at(p.dx_st, b, row[k]),
+             ox);
+      if constexpr (HAS_V) store8(static_cast<TX*>(p.dv) + at(p.dv_st, b, row[k]), ov);
+      store8(is_b[k] ? static_cast<TZ*>(p.dzb) + at(p.dzb_st, b, row[k]) : static_cast<TZ*>(p.dz) + at(p.dz_st, b, row[k]),
+             oz);
     }
     cur = nxt;
   }
@@ -453,6 +470,9 @@ hipError_t launch_pool_grad(const lbca_pool_grad_args& a, void* ws, hipStream_t 
   p.batch = a.batch; p.heads = a.heads; p.tokens = a.tokens; p.dim = a.dim; p.m = a.block;
   p.entries = a.entries; p.block_begin = a.block_begin; p.n_blocks = a.block_end - a.block_begin;
   p.pos_base = a.pos_base;
+  p.x_st = a.x_st; p.v_st = a.v_st; p.z_st = a.z_st; p.xb_st = a.xb_st; p.zb_st = a.zb_st;
+  p.dx_st = a.dx_st; p.dv_st = a.dv_st; p.dz_st = a.dz_st; p.dxb_st = a.dxb_st; p.dzb_st = a.dzb_st;
+  p.gx_st = a.grad_x_st; p.gv_st = a.grad_v_st;
   grad_plan(a, &p.chunks, &p.per_chunk);
   p.log2_lanes = __builtin_ctz((unsigned)(a.dim / 8));
   const bool dual = a.xb != nullptr;

@@ -47,7 +47,31 @@ struct PrefillParams {
   int64_t q_len, hq, hkv, G, entries, raw_rows, q_pos0, raw_pos_base, m, W;
   int mode, out_bf16, row_blocks;
   float scale_log2;
+  // element strides: q and out {sequence, query, head}; caches {sequence, KV head, row}
+  Str q_st, o_st, pk_st, pv_st, rk_st, rv_st;
 };
+
+// Element offset of (sequence b, query t, head h) in q (q_st) or out (o_st).
+__device__ __forceinline__ int64_t qoff(Str st, int64_t b, int64_t t, int64_t h) {
+  return b * st.s0 + t * st.s1 + h * st.s2;
+}
+
+// The strides a prefill workgroup uses: the arguments', or, when every tensor
+// of the call is dense (DN), the row-major ones worked out from the sizes.
+struct PreStr {
+  Str q, o, pk, pv, rk, rv;
+};
+template <bool DN, int D>
+__device__ __forceinline__ PreStr pre_strides(const PrefillParams& p) {
+  if constexpr (DN) {
+    const Str qs{p.q_len * p.hq * D, p.hq * D, D};
+    const Str ps{p.hkv * p.entries * D, p.entries * D, D};
+    const Str rs{p.hkv * p.raw_rows * D, p.raw_rows * D, D};
+    return PreStr{qs, qs, ps, ps, rs, rs};
+  } else {
+    return PreStr{p.q_st, p.o_st, p.pk_st, p.pv_st, p.rk_st, p.rv_st};
+  }
+}
 
 // Chunk swizzle of an LDS tile row (16-byte chunks): 8 consecutive rows read at
 // one chunk index, or 4 consecutive rows read at two adjacent chunks, hit
@@ -149,7 +173,7 @@ __device__ __forceinline__ void read_v_tiles(s16x4 (&r)[16], const bf16_t* vt, i
 #define LBCA_PREFILL_V1 0
 #endif
 
-template <int D, bool SHARED, int NWV, int QG>
+template <int D, bool SHARED, int NWV, int QG, bool DN>
 __global__ __launch_bounds__(NWV * 64, 1) void prefill_kernel(PrefillParams p) {
   constexpr int NT = NWV * 64;
   constexpr int KT = D <= 64 ? 64 : 32;  // keys per tile (registers bound it at 128 dims)
@@ -194,11 +218,12 @@ __global__ __launch_bounds__(NWV * 64, 1) void prefill_kernel(PrefillParams p) {
   const int row_last = row0 + ROWS - 1 < rows_total ? row0 + ROWS - 1 : rows_total - 1;
   const int q0 = (int)p.q_pos0;
   const int p_first = q0 + row0 / G, p_last = q0 + row_last / G;
+  const PreStr ST = pre_strides<DN, D>(p);
 
   // this wave's 16-row query groups: B operands and per-row visibility
   uint4 qr[QG][KS];
   int my_np[QG], my_rb[QG], my_pos[QG];
-  int64_t my_out[QG];
+  int my_rr[QG];  // flat row (position in the chunk * G + head in the group)
   bool my_ok[QG];
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
@@ -212,8 +237,8 @@ __global__ __launch_bounds__(NWV * 64, 1) void prefill_kernel(PrefillParams p) {
     my_rb[g] = (int)rb;
     my_pos[g] = q0 + pl;
     my_ok[g] = ok;
-    my_out[g] = (((int64_t)b * p.q_len + pl) * p.hq + (int64_t)kvh * G + hg) * D;
-    const bf16_t* qrow = p.q + my_out[g] + 8 * kq;
+    my_rr[g] = rr;
+    const bf16_t* qrow = p.q + qoff(ST.q, b, pl, (int64_t)kvh * G + hg) + 8 * kq;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       qr[g][s] = ok ? *reinterpret_cast<const uint4*>(qrow + 32 * s) : make_uint4(0, 0, 0, 0);
@@ -228,10 +253,20 @@ __global__ __launch_bounds__(NWV * 64, 1) void prefill_kernel(PrefillParams p) {
   const int T = T1 + (p_last - RB + 1 + KT - 1) / KT;
   // slice bases as integers (a pointer select from the argument block would
   // become a private-memory lookup)
-  const uintptr_t pk_base = reinterpret_cast<uintptr_t>(p.pk) + ((int64_t)bh * p.entries) * (D * 2);
-  const uintptr_t pv_base = reinterpret_cast<uintptr_t>(SHARED ? p.pk : p.pv) + ((int64_t)bh * p.entries) * (D * 2);
-  const uintptr_t rk_base = reinterpret_cast<uintptr_t>(p.rk) + ((int64_t)bh * p.raw_rows - p.raw_pos_base) * (D * 2);
-  const uintptr_t rv_base = reinterpret_cast<uintptr_t>(SHARED ? p.rk : p.rv) + ((int64_t)bh * p.raw_rows - p.raw_pos_base) * (D * 2);
+  // row strides in bytes; a shared series reads values with the key strides
+  const uint32_t pks = 2u * (uint32_t)ST.pk.s2, rks = 2u * (uint32_t)ST.rk.s2;
+  const uint32_t pvs = SHARED ? pks : 2u * (uint32_t)ST.pv.s2, rvs = SHARED ? rks : 2u * (uint32_t)ST.rv.s2;
+  const int64_t b64 = b, kvh64 = kvh;
+  const uintptr_t pk_base = reinterpret_cast<uintptr_t>(p.pk + b64 * ST.pk.s0 + kvh64 * ST.pk.s1);
+  const uintptr_t pv_base =
+      SHARED ? pk_base : reinterpret_cast<uintptr_t>(p.pv + b64 * ST.pv.s0 + kvh64 * ST.pv.s1);
+  // raw bases at position 0 (row -raw_pos_base)
+  const uintptr_t rk_base = reinterpret_cast<uintptr_t>(p.rk + b64 * ST.rk.s0 + kvh64 * ST.rk.s1) -
+                            (uintptr_t)(p.raw_pos_base * rks);
+  const uintptr_t rv_base =
+      SHARED ? rk_base
+             : reinterpret_cast<uintptr_t>(p.rv + b64 * ST.rv.s0 + kvh64 * ST.rv.s1) -
+                   (uintptr_t)(p.raw_pos_base * rvs);
 
   // LDS layout: row r of a tile holds its 16-byte chunks in swizzled order,
   // chunk c at position c ^ swz(r), so that the 16-byte K reads of 8 rows and
@@ -245,16 +280,19 @@ __global__ __launch_bounds__(NWV * 64, 1) void prefill_kernel(PrefillParams p) {
     const int x0 = pooled ? tile * KT : RB + (tile - T1) * KT;
     const int lim = pooled ? NP : p_last + 1;
     const uintptr_t kb = pooled ? pk_base : rk_base, vb = pooled ? pv_base : rv_base;
+    const uint32_t ks = pooled ? pks : rks, vs = pooled ? pvs : rvs;
 #pragma unroll
     for (int i = 0; i < CALLS; ++i) {
       const int slot = i * NT + tid;
       const int r = slot / CH, pos = slot % CH;
       const int x = x0 + r < lim ? x0 + r : lim - 1;
-      const uint64_t off = (uint64_t)(int64_t)x * (D * 2) + 16u * (pos ^ swz<D>(r));
+      const uint32_t col = 16u * (pos ^ swz<D>(r));
       const int dst = (i * NT + wave * 64) * 8;  // bf16 elements, wave-uniform
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(kb + off), (lds_void*)(kbuf(bufc) + dst), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(kb + (uint64_t)(uint32_t)x * ks + col),
+                                       (lds_void*)(kbuf(bufc) + dst), 16, 0, 0);
       if constexpr (!SHARED)
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(vb + off), (lds_void*)(vbuf(bufc) + dst), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(vb + (uint64_t)(uint32_t)x * vs + col),
+                                         (lds_void*)(vbuf(bufc) + dst), 16, 0, 0);
     }
   };
 
@@ -432,11 +470,13 @@ __global__ __launch_bounds__(NWV * 64, 1) void prefill_kernel(PrefillParams p) {
     float l = xor16_sum(l_run[g]);
     l = xor32_sum(l);
     if (!my_ok[g]) continue;
-    const int64_t h = (my_out[g] / D) % p.hq;
+    const int pl = my_rr[g] / G;
+    const int64_t h = (int64_t)kvh * G + (my_rr[g] - pl * G);
+    const int64_t ooff = qoff(ST.o, b, pl, h);
     if (p.sink) l += fast_exp2(p.sink[h] * kLog2e - m_run[g]);
     const float inv = 1.f / l;
     if (p.out_bf16) {
-      bf16_t* o = static_cast<bf16_t*>(p.out) + my_out[g] + 4 * kq;
+      bf16_t* o = static_cast<bf16_t*>(p.out) + ooff + 4 * kq;
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         uint2 w;
@@ -445,13 +485,13 @@ __global__ __launch_bounds__(NWV * 64, 1) void prefill_kernel(PrefillParams p) {
         *reinterpret_cast<uint2*>(o + 16 * t) = w;
       }
     } else {
-      float* o = static_cast<float*>(p.out) + my_out[g] + 4 * kq;
+      float* o = static_cast<float*>(p.out) + ooff + 4 * kq;
 #pragma unroll
       for (int t = 0; t < DT; ++t)
         *reinterpret_cast<float4*>(o + 16 * t) =
             make_float4(acc[g][t][0] * inv, acc[g][t][1] * inv, acc[g][t][2] * inv, acc[g][t][3] * inv);
     }
-    if (p.lse && kq == 0) p.lse[my_out[g] / D] = (m_run[g] + log2f(l)) * 0.69314718055994531f;
+    if (p.lse && kq == 0) p.lse[((int64_t)b * p.q_len + pl) * p.hq + h] = (m_run[g] + log2f(l)) * 0.69314718055994531f;
   }
 }
 
@@ -487,7 +527,7 @@ __device__ __forceinline__ uint4 ldb16(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 // reads of V(t) and K(t+1), then the exponentials of tile t beside the Q.K
 // MFMAs of tile t+1, then P.V of tile t and the mask and max of tile t+1; the
 // (rare) accumulator rescale closes the step.
-template <bool SHARED>
+template <bool SHARED, bool DN>
 __global__ __launch_bounds__(512, 1) void prefill128_kernel(PrefillParams p) {
   constexpr int D = 128, NWV = 8, NT = 512, KT = 32, DC = D / 16, DB = D / 32, CH = 16;
   constexpr int ROWS = NWV * 32;  // 256
@@ -508,11 +548,12 @@ __global__ __launch_bounds__(512, 1) void prefill128_kernel(PrefillParams p) {
   const int row_last = row0 + ROWS - 1 < rows_total ? row0 + ROWS - 1 : rows_total - 1;
   const int q0 = (int)p.q_pos0;
   const int p_first = q0 + row0 / G, p_last = q0 + row_last / G;
+  const PreStr ST = pre_strides<DN, D>(p);
 
   // this lane's query row (B operand: dims 16c + 8h .. +8) and its visibility
   uint4 qr[DC];
   int my_np, my_rb, my_pos;
-  int64_t my_out;
+  int my_rr;  // flat row (position in the chunk * G + head in the group)
   bool my_ok;
   {
     const int r = row0 + wave * 32 + n;
@@ -524,8 +565,8 @@ __global__ __launch_bounds__(512, 1) void prefill128_kernel(PrefillParams p) {
     my_np = (int)np;
     my_rb = (int)rb;
     my_pos = q0 + pl;
-    my_out = (((int64_t)b * p.q_len + pl) * p.hq + (int64_t)kvh * G + hg) * D;
-    const bf16_t* qrow = p.q + my_out + 8 * h;
+    my_rr = rr;
+    const bf16_t* qrow = p.q + qoff(ST.q, b, pl, (int64_t)kvh * G + hg) + 8 * h;
 #pragma unroll
     for (int c = 0; c < DC; ++c)
       qr[c] = my_ok ? *reinterpret_cast<const uint4*>(qrow + 16 * c) : make_uint4(0, 0, 0, 0);
@@ -538,10 +579,20 @@ __global__ __launch_bounds__(512, 1) void prefill128_kernel(PrefillParams p) {
   const int NPmin = (int)t64a, RB = (int)t64b;
   const int T1 = (NP + KT - 1) / KT;
   const int T = T1 + (p_last - RB + 1 + KT - 1) / KT;
-  const uintptr_t pk_base = reinterpret_cast<uintptr_t>(p.pk) + ((int64_t)bh * p.entries) * (D * 2);
-  const uintptr_t pv_base = reinterpret_cast<uintptr_t>(SHARED ? p.pk : p.pv) + ((int64_t)bh * p.entries) * (D * 2);
-  const uintptr_t rk_base = reinterpret_cast<uintptr_t>(p.rk) + ((int64_t)bh * p.raw_rows - p.raw_pos_base) * (D * 2);
-  const uintptr_t rv_base = reinterpret_cast<uintptr_t>(SHARED ? p.rk : p.rv) + ((int64_t)bh * p.raw_rows - p.raw_pos_base) * (D * 2);
+  // row strides in bytes; a shared series reads values with the key strides
+  const uint32_t pks = 2u * (uint32_t)ST.pk.s2, rks = 2u * (uint32_t)ST.rk.s2;
+  const uint32_t pvs = SHARED ? pks : 2u * (uint32_t)ST.pv.s2, rvs = SHARED ? rks : 2u * (uint32_t)ST.rv.s2;
+  const int64_t b64 = b, kvh64 = kvh;
+  const uintptr_t pk_base = reinterpret_cast<uintptr_t>(p.pk + b64 * ST.pk.s0 + kvh64 * ST.pk.s1);
+  const uintptr_t pv_base =
+      SHARED ? pk_base : reinterpret_cast<uintptr_t>(p.pv + b64 * ST.pv.s0 + kvh64 * ST.pv.s1);
+  // raw bases at position 0 (row -raw_pos_base)
+  const uintptr_t rk_base = reinterpret_cast<uintptr_t>(p.rk + b64 * ST.rk.s0 + kvh64 * ST.rk.s1) -
+                            (uintptr_t)(p.raw_pos_base * rks);
+  const uintptr_t rv_base =
+      SHARED ? rk_base
+             : reinterpret_cast<uintptr_t>(p.rv + b64 * ST.rv.s0 + kvh64 * ST.rv.s1) -
+                   (uintptr_t)(p.raw_pos_base * rvs);
 
   // LDS tile layout: row r holds its 16-byte chunks in swizzled order, chunk
   // x at position x ^ swz(r); this thread's chunk of every tile is LDS slot
@@ -567,19 +618,36 @@ __global__ __launch_bounds__(512, 1) void prefill128_kernel(PrefillParams p) {
   // load is in flight (which would make the compiler wait for it), and rows
   // past the span's end (the last tile's tail) read as zeros without touching
   // memory.  Each span's limit is its last visible row.
-  const uint32_t st_voff = (uint32_t)(st_r * D * 2) + st_goff;
-  const int64_t raw_lim = ((int64_t)p_last + 1 - p.raw_pos_base) * (D * 2);
-  const __amdgpu_buffer_rsrc_t rs_pk = make_rsrc(pk_base, (int64_t)NP * (D * 2));
-  const __amdgpu_buffer_rsrc_t rs_pv = make_rsrc(pv_base, (int64_t)NP * (D * 2));
-  const __amdgpu_buffer_rsrc_t rs_rk = make_rsrc(rk_base + (uintptr_t)(p.raw_pos_base * (D * 2)), raw_lim);
-  const __amdgpu_buffer_rsrc_t rs_rv = make_rsrc(rv_base + (uintptr_t)(p.raw_pos_base * (D * 2)), raw_lim);
+  const int64_t raw_n = (int64_t)p_last + 1 - p.raw_pos_base;  // raw rows up to the last position
+  const uintptr_t rk_slice = rk_base + (uintptr_t)(p.raw_pos_base * rks);
+  const uintptr_t rv_slice = rv_base + (uintptr_t)(p.raw_pos_base * rvs);
+  const int64_t pk_lim = (int64_t)NP * pks, pv_lim = (int64_t)NP * pvs, rk_lim = raw_n * rks, rv_lim = raw_n * rvs;
+  const __amdgpu_buffer_rsrc_t rs_pk = make_rsrc(pk_base, pk_lim);
+  const __amdgpu_buffer_rsrc_t rs_pv = make_rsrc(pv_base, pv_lim);
+  const __amdgpu_buffer_rsrc_t rs_rk = make_rsrc(rk_slice, rk_lim);
+  const __amdgpu_buffer_rsrc_t rs_rv = make_rsrc(rv_slice, rv_lim);
+  const uint32_t st_voff = (uint32_t)(st_r * D * 2) + st_goff;  // (dense rows)
   auto fetch = [=, &stg_k, &stg_v](int u, auto slot) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot)::value;
     (void)stg_v;
     const bool pooled = u < T1;
-    const int soff = (pooled ? u * KT : RB - (int)p.raw_pos_base + (u - T1) * KT) * (D * 2);
-    stg_k[SL] = ldb16(pooled ? rs_pk : rs_rk, st_voff, soff);
-    if constexpr (!SHARED) stg_v[SL] = ldb16(pooled ? rs_pv : rs_rv, st_voff, soff);
+    const int r0 = pooled ? u * KT : RB - (int)p.raw_pos_base + (u - T1) * KT;  // first row of the tile
+    if constexpr (DN) {
+      const int soff = r0 * (D * 2);
+      stg_k[SL] = ldb16(pooled ? rs_pk : rs_rk, st_voff, soff);
+      if constexpr (!SHARED) stg_v[SL] = ldb16(pooled ? rs_pv : rs_rv, st_voff, soff);
+    } else {
+      // strided rows: the descriptor is built per tile from a selected base and
+      // limit (a select between two descriptors goes through private memory)
+      const uint32_t ks = pooled ? pks : rks;
+      stg_k[SL] = ldb16(make_rsrc(pooled ? pk_base : rk_slice, pooled ? pk_lim : rk_lim),
+                        (uint32_t)st_r * ks + st_goff, (int)(r0 * ks));
+      if constexpr (!SHARED) {
+        const uint32_t vs = pooled ? pvs : rvs;
+        stg_v[SL] = ldb16(make_rsrc(pooled ? pv_base : rv_slice, pooled ? pv_lim : rv_lim),
+                          (uint32_t)st_r * vs + st_goff, (int)(r0 * vs));
+      }
+    }
   };
   auto stash = [&](auto c, auto slot) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot)::value;
@@ -767,10 +835,13 @@ __global__ __launch_bounds__(512, 1) void prefill128_kernel(PrefillParams p) {
   // (n, h) writes dims 32 db + 8 j + 4 h .. +4 of its row
   float l = xor32_sum(l_run);
   if (!my_ok) return;
-  if (p.sink) l += fast_exp2(p.sink[(my_out / D) % p.hq] * kLog2e - m_run);
+  const int pl = my_rr / G;
+  const int64_t head = (int64_t)kvh * G + (my_rr - pl * G);
+  const int64_t ooff = qoff(ST.o, b, pl, head);
+  if (p.sink) l += fast_exp2(p.sink[head] * kLog2e - m_run);
   const float inv = 1.f / l;
   if (p.out_bf16) {
-    bf16_t* o = static_cast<bf16_t*>(p.out) + my_out + 4 * h;
+    bf16_t* o = static_cast<bf16_t*>(p.out) + ooff + 4 * h;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -781,7 +852,7 @@ __global__ __launch_bounds__(512, 1) void prefill128_kernel(PrefillParams p) {
         *reinterpret_cast<uint2*>(o + 32 * db + 8 * j) = w;
       }
   } else {
-    float* o = static_cast<float*>(p.out) + my_out + 4 * h;
+    float* o = static_cast<float*>(p.out) + ooff + 4 * h;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -790,7 +861,7 @@ __global__ __launch_bounds__(512, 1) void prefill128_kernel(PrefillParams p) {
             make_float4(acc[db][4 * j + 0] * inv, acc[db][4 * j + 1] * inv, acc[db][4 * j + 2] * inv,
                         acc[db][4 * j + 3] * inv);
   }
-  if (p.lse && h == 0) p.lse[my_out / D] = (m_run + log2f(l)) * 0.69314718055994531f;
+  if (p.lse && h == 0) p.lse[((int64_t)b * p.q_len + pl) * p.hq + head] = (m_run + log2f(l)) * 0.69314718055994531f;
 }
 
 hipError_t launch_prefill(const lbca_prefill_args& a, hipStream_t stream) {
@@ -809,7 +880,16 @@ hipError_t launch_prefill(const lbca_prefill_args& a, hipStream_t stream) {
   p.m = a.block; p.W = a.window; p.mode = a.mode;
   p.out_bf16 = a.out_dtype == LBCA_BF16;
   p.scale_log2 = a.scale * kLog2e;
+  p.q_st = a.q_st; p.o_st = a.out_st;
+  p.pk_st = a.pooled_k_st; p.pv_st = a.pooled_v_st; p.rk_st = a.raw_k_st; p.rv_st = a.raw_v_st;
   const bool shared = a.pooled_v == nullptr;
+  const int64_t B = a.batch, Hk = a.kv_heads, d = a.dim;
+  const bool dn = dense_strides(a.q, a.q_st, {B, a.q_len, a.q_heads}, d) &&
+                  dense_strides(a.out, a.out_st, {B, a.q_len, a.q_heads}, d) &&
+                  dense_strides(a.pooled_k, a.pooled_k_st, {B, Hk, a.entries}, d) &&
+                  dense_strides(a.pooled_v, a.pooled_v_st, {B, Hk, a.entries}, d) &&
+                  dense_strides(a.raw_k, a.raw_k_st, {B, Hk, a.raw_rows}, d) &&
+                  dense_strides(a.raw_v, a.raw_v_st, {B, Hk, a.raw_rows}, d);
   auto go = [&](auto kern, int waves, int rows) {
     p.row_blocks = (int)((a.q_len * p.G + rows - 1) / rows);
     const dim3 grid((unsigned)(a.batch * a.kv_heads * p.row_blocks));
@@ -817,19 +897,19 @@ hipError_t launch_prefill(const lbca_prefill_args& a, hipStream_t stream) {
   };
   switch (a.dim) {
     case 64:
-      if (shared) go(prefill_kernel<64, true, 8, 2>, 8, 256);
-      else go(prefill_kernel<64, false, 8, 2>, 8, 256);
+      if (shared) dn ? go(prefill_kernel<64, true, 8, 2, true>, 8, 256) : go(prefill_kernel<64, true, 8, 2, false>, 8, 256);
+      else dn ? go(prefill_kernel<64, false, 8, 2, true>, 8, 256) : go(prefill_kernel<64, false, 8, 2, false>, 8, 256);
       break;
     case 128:
 #if LBCA_PREFILL_V1
       {
         constexpr int W128 = LBCA_PREFILL_WAVES, Q128 = LBCA_PREFILL_QG;
-        if (shared) go(prefill_kernel<128, true, W128, Q128>, W128, W128 * Q128 * 16);
-        else go(prefill_kernel<128, false, W128, Q128>, W128, W128 * Q128 * 16);
+        if (shared) go(prefill_kernel<128, true, W128, Q128, false>, W128, W128 * Q128 * 16);
+        else go(prefill_kernel<128, false, W128, Q128, false>, W128, W128 * Q128 * 16);
       }
 #else
-      if (shared) go(prefill128_kernel<true>, 8, 256);
-      else go(prefill128_kernel<false>, 8, 256);
+      if (shared) dn ? go(prefill128_kernel<true, true>, 8, 256) : go(prefill128_kernel<true, false>, 8, 256);
+      else dn ? go(prefill128_kernel<false, true>, 8, 256) : go(prefill128_kernel<false, false>, 8, 256);
 #endif
       break;
     default: return hipErrorInvalidValue;

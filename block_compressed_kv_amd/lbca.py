@@ -1,8 +1,11 @@
 """Thin ctypes binding over liblbca.so (the C ABI in include/lbca.h).
 
 Argument marshalling only: every step of the method runs in the HIP kernels.
-PyTorch supplies device memory and the current HIP stream.  Tensors must
-already be contiguous and on the GPU; nothing is copied or converted here.
+PyTorch supplies device memory and the current HIP stream.  Tensors must be
+on the GPU.  Queries, keys, values, logits, outputs and their gradients may be
+strided views (their last dimension contiguous): their strides go to the
+library as they are.  Per-head and per-sequence vectors, positions, index
+lists and biases must be contiguous.  Nothing is copied or converted here.
 Missing outputs and workspaces are allocated with ``torch.empty`` (plumbing).
 If ``liblbca.so`` has not been built, the first call raises ``RuntimeError``.
 """
@@ -26,13 +29,22 @@ EXCLUSIVE, OVERLAP = 0, 1
 _i64, _i32, _f32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 
 
+class Strides(ctypes.Structure):
+    """lbca_strides: element strides of every dimension but the last, outermost first."""
+    _fields_ = [("s", _i64 * 3)]
+
+
+def _stf(*names):
+    return [(n, Strides) for n in names]
+
+
 class PoolArgs(ctypes.Structure):
     _fields_ = [("x", _vp), ("v", _vp), ("z", _vp), ("bias", _vp), ("xb", _vp), ("zb", _vp),
                 ("bias_b", _vp), ("out_x", _vp), ("out_v", _vp),
                 ("batch", _i64), ("heads", _i64), ("tokens", _i64), ("dim", _i64), ("block", _i64),
                 ("entries", _i64), ("block_begin", _i64), ("block_end", _i64), ("pos_base", _i64),
                 ("x_dtype", _i32), ("z_dtype", _i32), ("rmsnorm_eps", _f32), ("rope_dims", _i32),
-                ("rope_base", _f32)]
+                ("rope_base", _f32)] + _stf("x_st", "v_st", "z_st", "xb_st", "zb_st", "out_x_st", "out_v_st")
 
 
 class PoolGradArgs(ctypes.Structure):
@@ -42,7 +54,8 @@ class PoolGradArgs(ctypes.Structure):
                 ("entries", _i64), ("block_begin", _i64), ("block_end", _i64), ("pos_base", _i64),
                 ("x_dtype", _i32), ("z_dtype", _i32), ("rmsnorm_eps", _f32), ("rope_dims", _i32),
                 ("rope_base", _f32), ("xb", _vp), ("zb", _vp), ("bias_b", _vp), ("dxb", _vp), ("dzb", _vp),
-                ("dbias_b", _vp)]
+                ("dbias_b", _vp)] + _stf("x_st", "v_st", "z_st", "grad_x_st", "grad_v_st", "dx_st", "dv_st",
+                                          "dz_st", "xb_st", "zb_st", "dxb_st", "dzb_st")
 
 
 class CacheArgs(ctypes.Structure):
@@ -52,7 +65,9 @@ class CacheArgs(ctypes.Structure):
                 ("batch", _i64), ("heads", _i64), ("dim", _i64), ("block", _i64), ("window", _i64),
                 ("ring", _i64), ("entries", _i64), ("mode", _i32), ("x_dtype", _i32), ("z_dtype", _i32),
                 ("rmsnorm_eps", _f32), ("rope_dims", _i32), ("rope_base", _f32),
-                ("xb_new", _vp), ("zb_new", _vp), ("raw_xb", _vp), ("raw_zb", _vp), ("bias_b", _vp)]
+                ("xb_new", _vp), ("zb_new", _vp), ("raw_xb", _vp), ("raw_zb", _vp), ("bias_b", _vp)] + _stf(
+                    "x_new_st", "v_new_st", "z_new_st", "raw_x_st", "raw_v_st", "raw_z_st", "out_x_st", "out_v_st",
+                    "xb_new_st", "zb_new_st", "raw_xb_st", "raw_zb_st")
 
 
 class DecodeArgs(ctypes.Structure):
@@ -62,7 +77,8 @@ class DecodeArgs(ctypes.Structure):
                 ("batch", _i64), ("q_heads", _i64), ("kv_heads", _i64), ("dim", _i64), ("entries", _i64),
                 ("raw_rows", _i64), ("k_sel", _i64), ("block", _i64), ("window", _i64),
                 ("mode", _i32), ("dtype", _i32), ("scale", _f32), ("rmsnorm_eps", _f32),
-                ("rope_dims", _i32), ("rope_base", _f32)]
+                ("rope_dims", _i32), ("rope_base", _f32)] + _stf("q_st", "pooled_k_st", "pooled_v_st", "raw_k_st",
+                                                                  "raw_v_st", "out_st")
 
 
 class PrefillArgs(ctypes.Structure):
@@ -71,7 +87,7 @@ class PrefillArgs(ctypes.Structure):
                 ("batch", _i64), ("q_len", _i64), ("q_heads", _i64), ("kv_heads", _i64), ("dim", _i64),
                 ("entries", _i64), ("raw_rows", _i64), ("q_pos0", _i64), ("raw_pos_base", _i64),
                 ("block", _i64), ("window", _i64), ("mode", _i32), ("dtype", _i32), ("out_dtype", _i32),
-                ("scale", _f32)]
+                ("scale", _f32)] + _stf("q_st", "pooled_k_st", "pooled_v_st", "raw_k_st", "raw_v_st", "out_st")
 
 
 class PrefillGradArgs(ctypes.Structure):
@@ -82,7 +98,9 @@ class PrefillGradArgs(ctypes.Structure):
                 ("batch", _i64), ("q_len", _i64), ("q_heads", _i64), ("kv_heads", _i64), ("dim", _i64),
                 ("entries", _i64), ("raw_rows", _i64), ("q_pos0", _i64), ("raw_pos_base", _i64),
                 ("block", _i64), ("window", _i64), ("mode", _i32), ("dtype", _i32), ("out_dtype", _i32),
-                ("accumulate", _i32), ("scale", _f32)]
+                ("accumulate", _i32), ("scale", _f32)] + _stf(
+                    "q_st", "pooled_k_st", "pooled_v_st", "raw_k_st", "raw_v_st", "out_st", "grad_out_st",
+                    "grad_q_st", "grad_pooled_k_st", "grad_pooled_v_st", "grad_raw_k_st", "grad_raw_v_st")
 
 
 class StepArgs(ctypes.Structure):
@@ -91,14 +109,15 @@ class StepArgs(ctypes.Structure):
                 ("raw_pos_base", _vp), ("sink", _vp), ("out", _vp), ("lse", _vp),
                 ("batch", _i64), ("q_heads", _i64), ("kv_heads", _i64), ("dim", _i64), ("block", _i64),
                 ("window", _i64), ("ring", _i64), ("entries", _i64), ("dtype", _i32), ("z_dtype", _i32),
-                ("scale", _f32)]
+                ("scale", _f32)] + _stf("q_st", "k_new_st", "v_new_st", "z_new_st", "raw_k_st", "raw_v_st",
+                                        "raw_z_st", "pooled_k_st", "pooled_v_st", "out_st")
 
 
 class IndexArgs(ctypes.Structure):
     _fields_ = [("q_idx", _vp), ("head_w", _vp), ("keys", _vp), ("pos", _vp), ("out_idx", _vp),
                 ("out_score", _vp),
                 ("batch", _i64), ("heads", _i64), ("dim", _i64), ("entries", _i64), ("k", _i64),
-                ("block", _i64), ("dtype", _i32)]
+                ("block", _i64), ("dtype", _i32)] + _stf("q_idx_st", "keys_st")
 
 
 class CsaPrefillArgs(ctypes.Structure):
@@ -108,7 +127,8 @@ class CsaPrefillArgs(ctypes.Structure):
                 ("q_heads", _i64), ("dim", _i64), ("n_entries", _i64), ("raw_rows", _i64), ("k", _i64),
                 ("q_pos0", _i64), ("raw_pos_base", _i64), ("block", _i64), ("window", _i64),
                 ("dtype", _i32), ("scale", ctypes.c_float), ("rmsnorm_eps", ctypes.c_float),
-                ("rope_dims", _i32), ("rope_base", ctypes.c_float)]
+                ("rope_dims", _i32), ("rope_base", ctypes.c_float)] + _stf(
+                    "q_idx_st", "idx_keys_st", "q_st", "entries_st", "raw_st", "out_st")
 
 
 class GemmArgs(ctypes.Structure):
@@ -160,7 +180,7 @@ def lib():
         L.lbca_grouped_gemm.argtypes = [ctypes.POINTER(GemmArgs), _vp]
         for name in exported_names():
             getattr(L, name).restype = ctypes.c_int if name != "lbca_status_string" else ctypes.c_char_p
-        if L.lbca_abi_version() != 1:
+        if L.lbca_abi_version() != 2:
             raise RuntimeError("liblbca ABI version mismatch")
         _lib = L
     return _lib
@@ -201,8 +221,6 @@ def _dt(t):
 def _need(t, name, ndim=None):
     if t is None:
         return
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
 
@@ -210,20 +228,43 @@ def _need(t, name, ndim=None):
 _FLOAT = (torch.float32, torch.bfloat16)
 
 
-def _expect(t, name, shape, dtypes=_FLOAT, device=None):
+def _expect(t, name, shape, dtypes=_FLOAT, device=None, strided=False):
     """The library sees raw pointers only, so every buffer's full shape, dtype and
     device are checked here: a short buffer would otherwise be read or written
-    past its end."""
+    past its end.  strided: a view whose last dimension is contiguous (its
+    strides are passed with it), else a contiguous tensor."""
     if t is None:
         return
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if t.dtype not in dtypes:
         raise ValueError(f"{name} must be one of {dtypes}, got {t.dtype}")
-    if not t.is_contiguous():
+    if strided:
+        if t.dim() > 0 and t.shape[-1] > 1 and t.stride(-1) != 1:
+            raise ValueError(f"{name} must have a contiguous last dimension")
+        if t.numel() > 1 and all(st == 0 for st, n in zip(t.stride()[:-1], t.shape[:-1]) if n > 1) and \
+                any(n > 1 for n in t.shape[:-1]):
+            raise ValueError(f"{name}: a view that repeats one row everywhere is not accepted")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if device is not None and t.device != device:
         raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _st(t):
+    """lbca_strides of t: its element strides but the last (0 for dimensions of extent 1)."""
+    st = Strides()
+    if t is not None:
+        for i, (n, s) in enumerate(zip(t.shape[:-1], t.stride()[:-1])):
+            st.s[i] = s if n > 1 else 0
+    return st
+
+
+def _set_st(a, **tensors):
+    """Fills the named stride fields of the argument struct a from the tensors."""
+    for name, t in tensors.items():
+        setattr(a, name + "_st", _st(t))
+    return a
 
 
 def _stream(stream):
@@ -248,19 +289,20 @@ def pool_blocks(x, z, bias, block, block_begin, block_end, out_x, v=None, out_v=
     _need(out_x, "out_x", 4)
     B, H, T, d = x.shape
     N, dev, xt = out_x.shape[2], x.device, (x.dtype,)
-    _expect(x, "x", (B, H, T, d))
-    _expect(z, "z", (B, H, T, d), device=dev)
+    _expect(x, "x", (B, H, T, d), strided=True)
+    _expect(z, "z", (B, H, T, d), device=dev, strided=True)
     for t, n in ((v, "v"), (xb, "xb")):
-        _expect(t, n, (B, H, T, d), xt, dev)
-    _expect(zb, "zb", (B, H, T, d), (z.dtype,), dev)
+        _expect(t, n, (B, H, T, d), xt, dev, strided=True)
+    _expect(zb, "zb", (B, H, T, d), (z.dtype,), dev, strided=True)
     for t, n in ((out_x, "out_x"), (out_v, "out_v")):
-        _expect(t, n, (B, H, N, d), xt, dev)
+        _expect(t, n, (B, H, N, d), xt, dev, strided=True)
     for t, n in ((bias, "bias"), (bias_b, "bias_b")):
         _expect(t, n, (H, block, d), (torch.float32,), dev)
     a = PoolArgs(_p(x), _p(v), _p(z), _p(bias), _p(xb), _p(zb), _p(bias_b), _p(out_x), _p(out_v),
                  B, H, T, d, block, out_x.shape[2], block_begin, block_end, pos_base,
                  _dt(x), _dt(z), -1.0 if rmsnorm_eps is None else float(rmsnorm_eps), int(rope_dims),
                  float(rope_base))
+    _set_st(a, x=x, v=v, z=z, xb=xb, zb=zb, out_x=out_x, out_v=out_v)
     _check(lib().lbca_pool_blocks(ctypes.byref(a), _stream(stream)), "lbca_pool_blocks")
     return out_x if out_v is None else (out_x, out_v)
 
@@ -272,20 +314,22 @@ def _pool_grad_args(x, z, bias, block, block_begin, block_end, grad_x, dx, dz, d
     _need(grad_x, "grad_x", 4)
     B, H, T, d = x.shape
     N, dev, xt, zt = grad_x.shape[2], x.device, (x.dtype,), (z.dtype,)
-    _expect(x, "x", (B, H, T, d))
-    _expect(z, "z", (B, H, T, d), device=dev)
+    _expect(x, "x", (B, H, T, d), strided=True)
+    _expect(z, "z", (B, H, T, d), device=dev, strided=True)
     for t, n in ((v, "v"), (dx, "dx"), (dv, "dv"), (xb, "xb"), (dxb, "dxb")):
-        _expect(t, n, (B, H, T, d), xt, dev)
+        _expect(t, n, (B, H, T, d), xt, dev, strided=True)
     for t, n in ((dz, "dz"), (zb, "zb"), (dzb, "dzb")):
-        _expect(t, n, (B, H, T, d), zt, dev)
+        _expect(t, n, (B, H, T, d), zt, dev, strided=True)
     for t, n in ((grad_x, "grad_x"), (grad_v, "grad_v")):
-        _expect(t, n, (B, H, N, d), xt, dev)
+        _expect(t, n, (B, H, N, d), xt, dev, strided=True)
     for t, n in ((bias, "bias"), (dbias, "dbias"), (bias_b, "bias_b"), (dbias_b, "dbias_b")):
         _expect(t, n, (H, block, d), (torch.float32,), dev)
-    return PoolGradArgs(_p(x), _p(v), _p(z), _p(bias), _p(grad_x), _p(grad_v), _p(dx), _p(dv), _p(dz),
-                        _p(dbias), B, H, T, d, block, grad_x.shape[2], block_begin, block_end, pos_base,
-                        _dt(x), _dt(z), -1.0 if rmsnorm_eps is None else float(rmsnorm_eps), int(rope_dims),
-                        float(rope_base), _p(xb), _p(zb), _p(bias_b), _p(dxb), _p(dzb), _p(dbias_b))
+    a = PoolGradArgs(_p(x), _p(v), _p(z), _p(bias), _p(grad_x), _p(grad_v), _p(dx), _p(dv), _p(dz),
+                     _p(dbias), B, H, T, d, block, grad_x.shape[2], block_begin, block_end, pos_base,
+                     _dt(x), _dt(z), -1.0 if rmsnorm_eps is None else float(rmsnorm_eps), int(rope_dims),
+                     float(rope_base), _p(xb), _p(zb), _p(bias_b), _p(dxb), _p(dzb), _p(dbias_b))
+    return _set_st(a, x=x, v=v, z=z, grad_x=grad_x, grad_v=grad_v, dx=dx, dv=dv, dz=dz, xb=xb, zb=zb, dxb=dxb,
+                   dzb=dzb)
 
 
 def pool_blocks_backward(x, z, bias, block, block_begin, block_end, grad_x, v=None, grad_v=None, dx=None,
@@ -342,17 +386,17 @@ def cache_append(x_new, z_new, raw_x, raw_z, bias, pos, raw_pos_base, block, win
     if raw_x.shape[2] % 2:
         raise ValueError("raw buffers hold 2 * ring rows")
     R2, N, dev, xt, zt = raw_x.shape[2], out_x.shape[2], x_new.device, (x_new.dtype,), (z_new.dtype,)
-    _expect(x_new, "x_new", (B, H, d))
+    _expect(x_new, "x_new", (B, H, d), strided=True)
     for t, n in ((v_new, "v_new"), (xb_new, "xb_new")):
-        _expect(t, n, (B, H, d), xt, dev)
+        _expect(t, n, (B, H, d), xt, dev, strided=True)
     for t, n in ((z_new, "z_new"), (zb_new, "zb_new")):
-        _expect(t, n, (B, H, d), zt, dev)
+        _expect(t, n, (B, H, d), zt, dev, strided=True)
     for t, n in ((raw_x, "raw_x"), (raw_v, "raw_v"), (raw_xb, "raw_xb")):
-        _expect(t, n, (B, H, R2, d), xt, dev)
+        _expect(t, n, (B, H, R2, d), xt, dev, strided=True)
     for t, n in ((raw_z, "raw_z"), (raw_zb, "raw_zb")):
-        _expect(t, n, (B, H, R2, d), zt, dev)
+        _expect(t, n, (B, H, R2, d), zt, dev, strided=True)
     for t, n in ((out_x, "out_x"), (out_v, "out_v")):
-        _expect(t, n, (B, H, N, d), xt, dev)
+        _expect(t, n, (B, H, N, d), xt, dev, strided=True)
     for t, n in ((bias, "bias"), (bias_b, "bias_b")):
         _expect(t, n, (H, block, d), (torch.float32,), dev)
     for t, n in ((pos, "pos"), (raw_pos_base, "raw_pos_base")):
@@ -362,6 +406,8 @@ def cache_append(x_new, z_new, raw_x, raw_z, bias, pos, raw_pos_base, block, win
                   out_x.shape[2], mode, _dt(x_new), _dt(z_new),
                   -1.0 if rmsnorm_eps is None else float(rmsnorm_eps), int(rope_dims), float(rope_base),
                   _p(xb_new), _p(zb_new), _p(raw_xb), _p(raw_zb), _p(bias_b))
+    _set_st(a, x_new=x_new, v_new=v_new, z_new=z_new, raw_x=raw_x, raw_v=raw_v, raw_z=raw_z, out_x=out_x,
+            out_v=out_v, xb_new=xb_new, zb_new=zb_new, raw_xb=raw_xb, raw_zb=raw_zb)
     _check(lib().lbca_cache_append(ctypes.byref(a), _stream(stream)), "lbca_cache_append")
 
 
@@ -380,26 +426,28 @@ def decode_step(q, k_new, v_new, z_new, raw_k, raw_v, raw_z, bias, pooled_k, poo
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    _expect(q, "q", (B, Hq, d))
+    _expect(q, "q", (B, Hq, d), strided=True)
     for t, n in ((k_new, "k_new"), (v_new, "v_new")):
-        _expect(t, n, (B, Hkv, d), qt, dev)
-    _expect(z_new, "z_new", (B, Hkv, d), device=dev)
+        _expect(t, n, (B, Hkv, d), qt, dev, strided=True)
+    _expect(z_new, "z_new", (B, Hkv, d), device=dev, strided=True)
     for t, n in ((raw_k, "raw_k"), (raw_v, "raw_v")):
-        _expect(t, n, (B, Hkv, R2, d), qt, dev)
-    _expect(raw_z, "raw_z", (B, Hkv, R2, d), zt, dev)
+        _expect(t, n, (B, Hkv, R2, d), qt, dev, strided=True)
+    _expect(raw_z, "raw_z", (B, Hkv, R2, d), zt, dev, strided=True)
     _expect(bias, "bias", (Hkv, block, d), (torch.float32,), dev)
     for t, n in ((pooled_k, "pooled_k"), (pooled_v, "pooled_v")):
-        _expect(t, n, (B, Hkv, N, d), qt, dev)
+        _expect(t, n, (B, Hkv, N, d), qt, dev, strided=True)
     for t, n in ((pos, "pos"), (raw_pos_base, "raw_pos_base")):
         _expect(t, n, (B,), (torch.int64,), dev)
     _expect(sink, "sink", (Hq,), (torch.float32,), dev)
-    _expect(out, "out", (B, Hq, d), (torch.float32,), dev)
+    _expect(out, "out", (B, Hq, d), (torch.float32,), dev, strided=True)
     _expect(lse, "lse", (B, Hq), (torch.float32,), dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     a = StepArgs(_p(q), _p(k_new), _p(v_new), _p(z_new), _p(raw_k), _p(raw_v), _p(raw_z), _p(bias), _p(pooled_k),
                  _p(pooled_v), _p(pos), _p(raw_pos_base), _p(sink), _p(out), _p(lse), B, Hq, Hkv, d, block,
                  window, R2 // 2, N, _dt(q), _dt(z_new), float(scale))
+    _set_st(a, q=q, k_new=k_new, v_new=v_new, z_new=z_new, raw_k=raw_k, raw_v=raw_v, raw_z=raw_z,
+            pooled_k=pooled_k, pooled_v=pooled_v, out=out)
     need = ctypes.c_size_t()
     _check(lib().lbca_decode_step_workspace(ctypes.byref(a), ctypes.byref(need)), "lbca_decode_step_workspace")
     if workspace is None and need.value > 0:
@@ -415,27 +463,29 @@ def _decode_args(q, pooled_k, raw_k, pos, block, window, mode, out, lse, pooled_
         _need(t, n, nd)
     B, Hq, d = q.shape
     Hkv, N, R, dev, qt = pooled_k.shape[1], pooled_k.shape[2], raw_k.shape[2], q.device, (q.dtype,)
-    _expect(q, "q", (B, Hq, d))
+    _expect(q, "q", (B, Hq, d), strided=True)
     for t, n in ((pooled_k, "pooled_k"), (pooled_v, "pooled_v")):
-        _expect(t, n, (B, Hkv, N, d), qt, dev)
+        _expect(t, n, (B, Hkv, N, d), qt, dev, strided=True)
     for t, n in ((raw_k, "raw_k"), (raw_v, "raw_v")):
-        _expect(t, n, (B, Hkv, R, d), qt, dev)
+        _expect(t, n, (B, Hkv, R, d), qt, dev, strided=True)
     for t, n in ((pos, "pos"), (raw_pos_base, "raw_pos_base")):
         _expect(t, n, (B,), (torch.int64,), dev)
     if sel_idx is not None:
         _expect(sel_idx, "sel_idx", (B, sel_idx.shape[1]), (torch.int32,), dev)
     _expect(sink, "sink", (Hq,), (torch.float32,), dev)
     if check_out:
-        _expect(out, "out", (B, Hq, d), (torch.float32,), dev)
+        _expect(out, "out", (B, Hq, d), (torch.float32,), dev, strided=True)
         _expect(lse, "lse", (B, Hq), (torch.float32,), dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    return DecodeArgs(_p(q), _p(pooled_k), _p(pooled_v), _p(raw_k), _p(raw_v), _p(pos),
-                      _p(raw_pos_base), _p(sel_idx), _p(sink), _p(out), _p(lse),
-                      B, Hq, Hkv, d, N, raw_k.shape[2], 0 if sel_idx is None else sel_idx.shape[1],
-                      block, window, mode, _dt(q), float(scale),
-                      -1.0 if rmsnorm_eps is None else float(rmsnorm_eps), int(rope_dims),
-                      float(rope_base))
+    a = DecodeArgs(_p(q), _p(pooled_k), _p(pooled_v), _p(raw_k), _p(raw_v), _p(pos),
+                   _p(raw_pos_base), _p(sel_idx), _p(sink), _p(out), _p(lse),
+                   B, Hq, Hkv, d, N, raw_k.shape[2], 0 if sel_idx is None else sel_idx.shape[1],
+                   block, window, mode, _dt(q), float(scale),
+                   -1.0 if rmsnorm_eps is None else float(rmsnorm_eps), int(rope_dims),
+                   float(rope_base))
+    return _set_st(a, q=q, pooled_k=pooled_k, pooled_v=pooled_v, raw_k=raw_k, raw_v=raw_v,
+                   out=out if check_out else None)
 
 
 def decode_workspace_bytes(q, pooled_k, raw_k, pos, block, window, mode, **kw):
@@ -495,19 +545,20 @@ def attend_prefill(q, q_pos0, pooled_k, raw_k, raw_pos_base, block, window, mode
         out = torch.empty((B, Tq, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
-    _expect(q, "q", (B, Tq, Hq, d))
+    _expect(q, "q", (B, Tq, Hq, d), strided=True)
     for t, n in ((pooled_k, "pooled_k"), (pooled_v, "pooled_v")):
-        _expect(t, n, (B, Hkv, N, d), qt, dev)
+        _expect(t, n, (B, Hkv, N, d), qt, dev, strided=True)
     for t, n in ((raw_k, "raw_k"), (raw_v, "raw_v")):
-        _expect(t, n, (B, Hkv, R, d), qt, dev)
+        _expect(t, n, (B, Hkv, R, d), qt, dev, strided=True)
     _expect(sink, "sink", (Hq,), (torch.float32,), dev)
-    _expect(out, "out", (B, Tq, Hq, d), device=dev)
+    _expect(out, "out", (B, Tq, Hq, d), device=dev, strided=True)
     _expect(lse, "lse", (B, Tq, Hq), (torch.float32,), dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     a = PrefillArgs(_p(q), _p(pooled_k), _p(pooled_v), _p(raw_k), _p(raw_v), _p(sink), _p(out), _p(lse),
                     B, Tq, Hq, pooled_k.shape[1], d, pooled_k.shape[2], raw_k.shape[2], q_pos0,
                     raw_pos_base, block, window, mode, _dt(q), _dt(out), float(scale))
+    _set_st(a, q=q, pooled_k=pooled_k, pooled_v=pooled_v, raw_k=raw_k, raw_v=raw_v, out=out)
     _check(lib().lbca_attend_prefill(ctypes.byref(a), _stream(stream)), "lbca_attend_prefill")
     return out, lse
 
@@ -545,20 +596,20 @@ def attend_prefill_backward(q, q_pos0, pooled_k, raw_k, raw_pos_base, block, win
         raise ValueError("one shared K/V series has no separate value gradients")
     if sink is not None and grad_sink is None:
         grad_sink = new((Hq,))
-    _expect(q, "q", (B, Tq, Hq, d))
-    _expect(grad_out, "grad_out", (B, Tq, Hq, d), qt, dev)
+    _expect(q, "q", (B, Tq, Hq, d), strided=True)
+    _expect(grad_out, "grad_out", (B, Tq, Hq, d), qt, dev, strided=True)
     for t, n in ((pooled_k, "pooled_k"), (pooled_v, "pooled_v")):
-        _expect(t, n, (B, Hkv, N, d), qt, dev)
+        _expect(t, n, (B, Hkv, N, d), qt, dev, strided=True)
     for t, n in ((raw_k, "raw_k"), (raw_v, "raw_v")):
-        _expect(t, n, (B, Hkv, R, d), qt, dev)
+        _expect(t, n, (B, Hkv, R, d), qt, dev, strided=True)
     _expect(sink, "sink", (Hq,), (f32,), dev)
-    _expect(out, "out", (B, Tq, Hq, d), device=dev)
+    _expect(out, "out", (B, Tq, Hq, d), device=dev, strided=True)
     _expect(lse, "lse", (B, Tq, Hq), (f32,), dev)
-    _expect(grad_q, "grad_q", (B, Tq, Hq, d), (f32,), dev)
+    _expect(grad_q, "grad_q", (B, Tq, Hq, d), (f32,), dev, strided=True)
     for t, n in ((grad_pooled_k, "grad_pooled_k"), (grad_pooled_v, "grad_pooled_v")):
-        _expect(t, n, (B, Hkv, N, d), (f32,), dev)
+        _expect(t, n, (B, Hkv, N, d), (f32,), dev, strided=True)
     for t, n in ((grad_raw_k, "grad_raw_k"), (grad_raw_v, "grad_raw_v")):
-        _expect(t, n, (B, Hkv, R, d), (f32,), dev)
+        _expect(t, n, (B, Hkv, R, d), (f32,), dev, strided=True)
     _expect(grad_sink, "grad_sink", (Hq,), (f32,), dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -566,6 +617,9 @@ def attend_prefill_backward(q, q_pos0, pooled_k, raw_k, raw_pos_base, block, win
                         _p(grad_out), _p(grad_q), _p(grad_pooled_k), _p(grad_pooled_v), _p(grad_raw_k),
                         _p(grad_raw_v), _p(grad_sink), B, Tq, Hq, Hkv, d, N, R, q_pos0, raw_pos_base, block,
                         window, mode, _dt(q), _dt(out), int(bool(accumulate)), float(scale))
+    _set_st(a, q=q, pooled_k=pooled_k, pooled_v=pooled_v, raw_k=raw_k, raw_v=raw_v, out=out, grad_out=grad_out,
+            grad_q=grad_q, grad_pooled_k=grad_pooled_k, grad_pooled_v=grad_pooled_v, grad_raw_k=grad_raw_k,
+            grad_raw_v=grad_raw_v)
     need = ctypes.c_size_t()
     _check(lib().lbca_attend_prefill_backward_workspace(ctypes.byref(a), ctypes.byref(need)),
            "lbca_attend_prefill_backward_workspace")
@@ -598,9 +652,9 @@ def attend_prefill_backward_workspace_bytes(q_shape, q_pos0, kv_heads, entries, 
 def _check_index(q_idx, head_w, keys, pos):
     B, HI, dI = q_idx.shape
     dev = q_idx.device
-    _expect(q_idx, "q_idx", (B, HI, dI))
+    _expect(q_idx, "q_idx", (B, HI, dI), strided=True)
     _expect(head_w, "head_w", (B, HI), (torch.float32,), dev)
-    _expect(keys, "keys", (B, keys.shape[1], dI), (q_idx.dtype,), dev)
+    _expect(keys, "keys", (B, keys.shape[1], dI), (q_idx.dtype,), dev, strided=True)
     _expect(pos, "pos", (B,), (torch.int64,), dev)
 
 
@@ -612,6 +666,7 @@ def index_workspace_bytes(q_idx, head_w, keys, pos, block, k):
     B, HI, dI = q_idx.shape
     a = IndexArgs(_p(q_idx), _p(head_w), _p(keys), _p(pos), _p(q_idx), None,
                   B, HI, dI, keys.shape[1], k, block, _dt(q_idx))
+    _set_st(a, q_idx=q_idx, keys=keys)
     need = ctypes.c_size_t()
     _check(lib().csa_index_topk_workspace(ctypes.byref(a), ctypes.byref(need)), "csa_index_topk_workspace")
     return need.value
@@ -632,6 +687,7 @@ def csa_index_topk(q_idx, head_w, keys, pos, block, k, out_idx=None, out_score=N
     _expect(out_score, "out_score", (B, k), (torch.float32,), q_idx.device)
     a = IndexArgs(_p(q_idx), _p(head_w), _p(keys), _p(pos), _p(out_idx), _p(out_score),
                   B, HI, dI, keys.shape[1], k, block, _dt(q_idx))
+    _set_st(a, q_idx=q_idx, keys=keys)
     need = ctypes.c_size_t()
     _check(lib().csa_index_topk_workspace(ctypes.byref(a), ctypes.byref(need)), "csa_index_topk_workspace")
     if workspace is None and need.value > 0:
@@ -649,23 +705,25 @@ def _csa_prefill_args(q_idx, head_w, idx_keys, q, entries, raw, q_pos0, raw_pos_
     B, Tq, Hq, d = q.shape
     HI, dI = q_idx.shape[2], q_idx.shape[3]
     N, R, dev, qt = entries.shape[1], raw.shape[1], q.device, (q.dtype,)
-    _expect(q, "q", (B, Tq, Hq, d))
-    _expect(q_idx, "q_idx", (B, Tq, HI, dI), qt, dev)
+    _expect(q, "q", (B, Tq, Hq, d), strided=True)
+    _expect(q_idx, "q_idx", (B, Tq, HI, dI), qt, dev, strided=True)
     _expect(head_w, "head_w", (B, Tq, HI), (torch.float32,), dev)
-    _expect(idx_keys, "idx_keys", (B, N, dI), qt, dev)
-    _expect(entries, "entries", (B, N, d), qt, dev)
-    _expect(raw, "raw", (B, R, d), qt, dev)
+    _expect(idx_keys, "idx_keys", (B, N, dI), qt, dev, strided=True)
+    _expect(entries, "entries", (B, N, d), qt, dev, strided=True)
+    _expect(raw, "raw", (B, R, d), qt, dev, strided=True)
     _expect(sink, "sink", (Hq,), (torch.float32,), dev)
     if out is not q:  # the workspace query passes q in place of an absent output
-        _expect(out, "out", (B, Tq, Hq, d), (torch.float32,), dev)
+        _expect(out, "out", (B, Tq, Hq, d), (torch.float32,), dev, strided=True)
     _expect(lse, "lse", (B, Tq, Hq), (torch.float32,), dev)
     _expect(out_idx, "out_idx", (B, Tq, k), (torch.int32,), dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    return CsaPrefillArgs(_p(q_idx), _p(head_w), _p(idx_keys), _p(q), _p(entries), _p(raw), _p(sink), _p(out),
-                          _p(lse), _p(out_idx), B, Tq, HI, dI, Hq, d, entries.shape[1], raw.shape[1], k,
-                          q_pos0, raw_pos_base, block, window, _dt(q), float(scale),
-                          -1.0 if rmsnorm_eps is None else float(rmsnorm_eps), int(rope_dims), float(rope_base))
+    a = CsaPrefillArgs(_p(q_idx), _p(head_w), _p(idx_keys), _p(q), _p(entries), _p(raw), _p(sink), _p(out),
+                       _p(lse), _p(out_idx), B, Tq, HI, dI, Hq, d, entries.shape[1], raw.shape[1], k,
+                       q_pos0, raw_pos_base, block, window, _dt(q), float(scale),
+                       -1.0 if rmsnorm_eps is None else float(rmsnorm_eps), int(rope_dims), float(rope_base))
+    return _set_st(a, q_idx=q_idx, idx_keys=idx_keys, q=q, entries=entries, raw=raw,
+                   out=None if out is q else out)
 
 
 def csa_sparse_prefill_workspace_bytes(q_idx, head_w, idx_keys, q, entries, raw, q_pos0, raw_pos_base, block,

@@ -18,11 +18,19 @@
  * kernels: a sequence whose position does not fit the buffers it was given
  * gets NaN outputs instead of out-of-bounds accesses.
  *
- * Layout conventions: every tensor is dense row-major with the shape given
- * (last dimension contiguous), element type given by a dtype field
- * (LBCA_F32 = IEEE float32, LBCA_BF16 = bfloat16 bit patterns).  Device
- * pointers to bf16/f32 data must be 16-byte aligned.  Positions are 0-based
- * token indices (int64).
+ * Layout conventions: a tensor has the shape given, its last (feature)
+ * dimension contiguous, and its element type given by a dtype field
+ * (LBCA_F32 = IEEE float32, LBCA_BF16 = bfloat16 bit patterns).  Every
+ * tensor with a feature dimension (queries, keys, values, logits, outputs
+ * and their gradients) also takes an lbca_strides field (named after it
+ * with an _st suffix): int64 element strides of its other dimensions, so a
+ * slice of a longer cache, a head-interleaved [batch, rows, heads, dim]
+ * buffer seen as [batch, heads, rows, dim], or the query part of a fused
+ * projection output is passed in place.  A zeroed lbca_strides means dense
+ * row-major.  Per-head or per-sequence scalars (lse, sink, head_w),
+ * positions, index lists and the pooling biases are dense.  Device pointers
+ * to bf16/f32 data must be 16-byte aligned.  Positions are 0-based token
+ * indices (int64).
  *
  * Method (pages cited by title and section):
  *  - "mSeek: learned KV-cache compression in a 3B model" (mSeek), section
@@ -50,7 +58,7 @@
 extern "C" {
 #endif
 
-#define LBCA_ABI_VERSION 1
+#define LBCA_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define LBCA_API __attribute__((visibility("default")))
@@ -76,6 +84,22 @@ extern "C" {
                             unpooled token .. t (W .. W+m-1 tokens). */
 #define LBCA_OVERLAP 1   /* HCA/CSA: every complete block is visible; the raw
                             window is the last W tokens [max(0,t-W+1), t]. */
+
+/* Element strides of one tensor argument: s[i] is the distance, in
+ * elements, between neighbours along dimension i, outermost first, for every
+ * dimension but the last (which is contiguous); a tensor of rank r uses
+ * s[0 .. r-2] and the rest are ignored.  All zero: dense row-major for the
+ * documented shape.  Rules (INVALID_ARG otherwise): strides >= 0; each
+ * stride times the element size a multiple of 16 bytes (rows stay aligned for
+ * 16-byte loads); an output's elements must not overlap one another (for the
+ * dimensions of extent > 1, sorted by stride, each stride covers the extent
+ * of everything inside it).  Every stride but the outermost must be below 2^31
+ * elements, dense defaults included (UNSUPPORTED otherwise), and the calls
+ * that address cache rows with 32-bit offsets state their own bound on a
+ * slice's span. */
+typedef struct lbca_strides {
+  int64_t s[3];
+} lbca_strides;
 
 LBCA_API int lbca_abi_version(void);
 
@@ -141,6 +165,7 @@ typedef struct lbca_pool_args {
   float rmsnorm_eps; /* < 0: off */
   int32_t rope_dims; /* 0: off */
   float rope_base;
+  lbca_strides x_st, v_st, z_st, xb_st, zb_st, out_x_st, out_v_st;
 } lbca_pool_args;
 
 LBCA_API int lbca_pool_blocks(const lbca_pool_args* a, void* stream);
@@ -205,6 +230,7 @@ typedef struct lbca_pool_grad_args {
   void* dxb;
   void* dzb;
   float* dbias_b;
+  lbca_strides x_st, v_st, z_st, grad_x_st, grad_v_st, dx_st, dv_st, dz_st, xb_st, zb_st, dxb_st, dzb_st;
 } lbca_pool_grad_args;
 
 LBCA_API int lbca_pool_blocks_backward_workspace(const lbca_pool_grad_args* a, size_t* bytes);
@@ -278,6 +304,8 @@ typedef struct lbca_cache_args {
   void* raw_xb;
   void* raw_zb;
   const float* bias_b;
+  lbca_strides x_new_st, v_new_st, z_new_st, raw_x_st, raw_v_st, raw_z_st, out_x_st, out_v_st;
+  lbca_strides xb_new_st, zb_new_st, raw_xb_st, raw_zb_st;
 } lbca_cache_args;
 
 LBCA_API int lbca_cache_append(const lbca_cache_args* a, void* stream);
@@ -339,6 +367,8 @@ typedef struct lbca_step_args {
   int64_t batch, q_heads, kv_heads, dim, block, window, ring, entries;
   int32_t dtype, z_dtype;
   float scale;
+  lbca_strides q_st, k_new_st, v_new_st, z_new_st, raw_k_st, raw_v_st, raw_z_st, pooled_k_st, pooled_v_st,
+      out_st;
 } lbca_step_args;
 
 LBCA_API int lbca_decode_step_workspace(const lbca_step_args* a, size_t* bytes);
@@ -401,6 +431,7 @@ typedef struct lbca_decode_args {
   float rmsnorm_eps; /* < 0: off */
   int32_t rope_dims; /* 0: off */
   float rope_base;
+  lbca_strides q_st, pooled_k_st, pooled_v_st, raw_k_st, raw_v_st, out_st;
 } lbca_decode_args;
 
 LBCA_API int lbca_attend_decode_workspace(const lbca_decode_args* a, size_t* bytes);
@@ -456,6 +487,7 @@ typedef struct lbca_prefill_args {
   int64_t q_pos0, raw_pos_base, block, window;
   int32_t mode, dtype, out_dtype;
   float scale;
+  lbca_strides q_st, pooled_k_st, pooled_v_st, raw_k_st, raw_v_st, out_st;
 } lbca_prefill_args;
 
 LBCA_API int lbca_attend_prefill(const lbca_prefill_args* a, void* stream);
@@ -520,6 +552,8 @@ typedef struct lbca_prefill_grad_args {
   int64_t q_pos0, raw_pos_base, block, window;
   int32_t mode, dtype, out_dtype, accumulate;
   float scale;
+  lbca_strides q_st, pooled_k_st, pooled_v_st, raw_k_st, raw_v_st, out_st, grad_out_st;
+  lbca_strides grad_q_st, grad_pooled_k_st, grad_pooled_v_st, grad_raw_k_st, grad_raw_v_st;
 } lbca_prefill_grad_args;
 
 LBCA_API int lbca_attend_prefill_backward_workspace(const lbca_prefill_grad_args* a, size_t* bytes);
@@ -557,6 +591,7 @@ typedef struct csa_index_args {
   float* out_score;
   int64_t batch, heads, dim, entries, k, block;
   int32_t dtype;
+  lbca_strides q_idx_st, keys_st;
 } csa_index_args;
 
 LBCA_API int csa_index_topk_workspace(const csa_index_args* a, size_t* bytes);
@@ -610,6 +645,7 @@ typedef struct csa_prefill_args {
   float rmsnorm_eps; /* < 0: off */
   int32_t rope_dims; /* 0: off */
   float rope_base;
+  lbca_strides q_idx_st, idx_keys_st, q_st, entries_st, raw_st, out_st;
 } csa_prefill_args;
 
 LBCA_API int csa_sparse_prefill_workspace(const csa_prefill_args* a, size_t* bytes);

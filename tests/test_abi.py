@@ -491,3 +491,75 @@ def test_gemm_validation(kw, code):
 @fake_ptr
 def test_gemm_empty_is_ok_without_gpu():
     assert _gemm(groups=0) == 0 and _gemm(m=0) == 0 and _gemm(n=0) == 0
+
+
+# --- element strides (lbca_strides) ------------------------------------------
+def _st(*s):
+    st = lbca.Strides()
+    for i, v in enumerate(s):
+        st.s[i] = v
+    return st
+
+
+@fake_ptr
+@pytest.mark.parametrize("kw,code", [
+    (dict(), 0),
+    # q as the query part of a fused [batch, 40 heads, 128] projection output
+    (dict(q_st=_st(40 * 128, 128)), 0),
+    # caches as slices of longer [batch, kv_heads, 4096, 128] buffers, and a
+    # head-interleaved raw cache [batch, rows, kv_heads, 128]
+    (dict(pooled_k_st=_st(8 * 4096 * 128, 4096 * 128, 128), raw_k_st=_st(256 * 8 * 128, 128, 8 * 128)), 0),
+    (dict(out_st=_st(24 * 256, 256)), 0),                 # output rows padded to 256
+    (dict(q_st=_st(24 * 128, 4)), -1),                    # 8-byte stride: rows not 16-byte aligned
+    (dict(raw_v_st=_st(-256 * 8 * 128, 128, 8 * 128)), -1),  # negative stride
+    (dict(out_st=_st(24 * 128, 0)), -1),                  # every head of a sequence on one row
+    (dict(out_st=_st(128, 128)), -1),                     # sequences overlap each other's heads
+    (dict(out_st=_st(24 * 128, 64)), -1),                 # heads overlap (64 < 128 dims)
+    (dict(q_st=_st(0, 128)), 0),                          # an input may repeat across sequences
+    (dict(pooled_k_st=_st(0, 0, 1 << 23)), -2),           # a pooled slice beyond 2 GiB at this row stride
+])
+def test_decode_strides(kw, code):
+    st, _, _ = _decode(**kw)
+    assert st == code, kw
+
+
+@fake_ptr
+@pytest.mark.parametrize("kw,code", [
+    (dict(), 0),
+    (dict(q_st=_st(2048 * 40 * 128, 40 * 128, 128), out_st=_st(2048 * 24 * 128, 24 * 128, 128)), 0),
+    (dict(raw_k_st=_st(16384 * 8 * 128, 128, 8 * 128)), 0),                 # head-interleaved raw rows
+    (dict(raw_k_st=_st(0, 0, 1 << 20)), -2),                                # raw slice beyond 2 GiB
+    (dict(out_st=_st(2048 * 24 * 128, 24 * 128, 24 * 128)), -1),            # heads of a query share a row
+    (dict(pooled_v_st=_st(1016 * 128, 1016 * 128 * 8, 12)), -1),            # 24-byte row stride
+])
+def test_prefill_strides(kw, code):
+    if code == 0:  # a call with no queries validates the inputs' strides and launches nothing
+        assert _prefill(q_len=0, **kw) == 0
+    else:
+        assert _prefill(**kw) == code
+
+
+@fake_ptr
+def test_pool_and_cache_strides():
+    assert _pool(batch=0, out_x_st=_st(0, 0, 0)) == 0
+    assert _pool(out_x_st=_st(2 * 4 * 128, 4 * 128, 64)) == -1     # entries overlap
+    assert _pool(z_st=_st(2 * 64 * 128, 64 * 128, 2)) == -1         # z rows 8 bytes apart (fp32): misaligned
+    assert _cache(raw_x_st=_st(1, 0, 0)) == -1
+    assert _index(keys_st=_st(-1, 64))[0] == -1
+    assert _csap(entries_st=_st(0, 1 << 21))[0] == -2               # entry slice beyond 2 GiB
+    assert _csap(out_st=_st(100 * 64 * 512, 64 * 512, 0))[0] == -1  # heads of a query share a row
+
+
+def test_binding_passes_view_strides():
+    x = torch.zeros((2, 5, 3, 16))
+    v = x.permute(0, 2, 1, 3)                                        # [2, 3, 5, 16] head-interleaved view
+    st = lbca._st(v)
+    assert list(st.s) == [5 * 3 * 16, 16, 3 * 16]
+    assert list(lbca._st(x[:, :1]).s) == [5 * 3 * 16, 0, 16]         # extent-1 dims carry stride 0
+    with pytest.raises(ValueError, match="contiguous last"):
+        lbca._expect(x.transpose(2, 3), "x", (2, 5, 16, 3), strided=True)
+    with pytest.raises(ValueError, match="repeats one row"):
+        lbca._expect(torch.zeros(16).expand(2, 3, 16), "x", (2, 3, 16), strided=True)
+    lbca._expect(v, "v", (2, 3, 5, 16), strided=True)
+    with pytest.raises(ValueError, match="contiguous"):
+        lbca._expect(v, "lse", (2, 3, 5, 16))                        # dense-only arguments stay dense

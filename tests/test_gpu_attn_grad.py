@@ -94,7 +94,7 @@ def test_chunked_backward_accumulates(lib):
     dq = torch.empty((B, Tq, Hq, d), dtype=torch.float32, device=DEV)
     bufs = None
     for c0, c1 in ((0, 250), (250, Tq)):
-        sub = lambda t: t[:, c0:c1].contiguous()
+        sub = lambda t: t[:, c0:c1] if t.dim() == 4 else t[:, c0:c1].contiguous()  # lse stays dense
         kw = {} if bufs is None else dict(zip(("grad_pooled_k", "grad_pooled_v", "grad_raw_k", "grad_raw_v",
                                                "grad_sink"), bufs))
         g = lib.attend_prefill_backward(sub(x["q"]), c0, x["pk"], x["rk"], 0, m, W, mode, sub(o), sub(lse),

@@ -51,16 +51,16 @@ def _loop(lib, series, z, bias, m, W, mode, ring, entries, offsets, steps, check
     if dual is not None:  # (xb, zb, bias_b): the b-series of dual (CSA) pooling
         xb, zb, bias_b = dual
         raw_xb, raw_zb = torch.full_like(raw_x, float("nan")), torch.full_like(raw_z, float("nan"))
-        dual_kw = lambda ti: dict(xb_new=xb[bidx, :, ti].contiguous(), zb_new=zb[bidx, :, ti].contiguous(),
+        dual_kw = lambda ti: dict(xb_new=xb[bidx, :, ti], zb_new=zb[bidx, :, ti],
                                   raw_xb=raw_xb, raw_zb=raw_zb, bias_b=bias_b)
     for step in range(steps):
         t_list = [step - o for o in offsets]
         assert max(t_list) < T, "the history covers every appended position"
         pos = torch.tensor(t_list, dtype=torch.int64, device=DEV)
         ti = pos.clamp(min=0)
-        x_new = series[bidx, :, ti].contiguous()
-        z_new = z[bidx, :, ti].contiguous()
-        v_new = None if v is None else v[bidx, :, ti].contiguous()
+        x_new = series[bidx, :, ti]
+        z_new = z[bidx, :, ti]
+        v_new = None if v is None else v[bidx, :, ti]
         lib.cache_append(x_new, z_new, raw_x, raw_z, bias, pos, rpb, m, W, mode, out_x, v_new=v_new,
                          raw_v=raw_v, out_v=out_v, **treat, **(dual_kw(ti) if dual is not None else {}))
         if step in check_at:
@@ -268,7 +268,7 @@ def _run_steps(lib, L, qs, offsets, m, W, first_step, steps, fused, plain, check
         t_list = [step - o for o in offsets]
         pos = torch.tensor(t_list, dtype=torch.int64, device=DEV)
         ti = pos.clamp(min=0)
-        k_new, v_new, z_new = (x[bidx, :, ti].contiguous() for x in (k, v, z))
+        k_new, v_new, z_new = (x[bidx, :, ti] for x in (k, v, z))
         q = qs[step % qs.shape[0]]
         of, lf = lib.decode_step(q, k_new, v_new, z_new, fused["rk"], fused["rv"], fused["rz"], bias, fused["pk"],
                                  fused["pv"], pos, fused["rpb"], m, W)

@@ -51,7 +51,7 @@ def test_llama_decode_32k_batch16(lib):
     pv = torch.empty_like(pk)
     say("pool 510 blocks, decode at t=32767")
     lib.pool_blocks(L["k"], L["z"], L["bias"], m, 0, N, pk, v=L["v"], out_v=pv)
-    q = L["q"][:, 0].contiguous()
+    q = L["q"][:, 0]
     pos = torch.full((B,), T - 1, dtype=torch.int64, device=DEV)
     o, lse = lib.attend_decode(q, pk, L["k"], pos, m, W, O.EXCLUSIVE, pooled_v=pv, raw_v=L["v"])
     torch.cuda.synchronize()
@@ -82,7 +82,7 @@ def test_llama_chunked_prefill_16k(lib):
         need, _ = O.visible_range(c0 + chunk - 1, m, W, O.EXCLUSIVE)
         lib.pool_blocks(L["k"], L["z"], L["bias"], m, done, need, pk, v=L["v"], out_v=pv)
         done = need
-        qc = L["q"][:, c0:c0 + chunk].contiguous()
+        qc = L["q"][:, c0:c0 + chunk]
         lib.attend_prefill(qc, c0, pk, L["k"], 0, m, W, O.EXCLUSIVE, out=out[:, c0:c0 + chunk],
                             lse=lse[:, c0:c0 + chunk], pooled_v=pv, raw_v=L["v"])
     torch.cuda.synchronize()
@@ -230,7 +230,7 @@ def test_csa_sparse_prefill_128k_chunk_batch2(lib):
     lib.pool_blocks(C["ca"], C["za"], C["bias_a"], m, 0, N, ent, xb=C["cb"], zb=C["zb"],
                     bias_b=C["bias_b"], **treat)
     rbase = t0 - W + 1
-    raw = C["ca"][:, 0, rbase:].contiguous()
+    raw = C["ca"][:, 0, rbase:]
     say("sparse prefill of the chunk")
     o, lse, idx = lib.csa_sparse_prefill(C["qi"], C["w"], keys, C["q"], ent[:, 0], raw, t0, rbase, m, W, k,
                                          sink=C["sink"], **treat)

@@ -53,7 +53,7 @@ def test_pool_pos_base_window(lib):
     B, H, T, d, m = 1, 2, 2048, 128, 64
     L = _dev(synth.lbca_layer("pool-base", B, H, H, T, d, m, "bf16", "f32"))
     base = 640
-    sub = {k: L[k][:, :, base:].contiguous() for k in ("k", "v", "z")}
+    sub = {k: L[k][:, :, base:] for k in ("k", "v", "z")}
     ok = torch.zeros((B, H, 32, d), dtype=torch.bfloat16, device=DEV)
     ov = torch.zeros_like(ok)
     lib.pool_blocks(sub["k"], sub["z"], L["bias"], m, 10, 20, ok, v=sub["v"], out_v=ov, pos_base=base)
@@ -110,7 +110,7 @@ def test_pool_backward(lib, xdt, zdt, B, H, T, d, m, b0, b1, pb, with_v):
     N = T // m
     g = lambda n: synth.normal((B, H, N, d), synth.seed_of("pool-grad", xdt, d, m, n), dtype=xdt, device=DEV)
     gx, gv = g("gx"), (g("gv") if with_v else None)
-    sub = lambda t: t[:, :, pb:].contiguous()
+    sub = lambda t: t[:, :, pb:]
     x, z = sub(L["k"]), sub(L["z"])
     v = sub(L["v"]) if with_v else None
     dx, dz = torch.full_like(x, 7.0), torch.full_like(z, 7.0)
@@ -192,7 +192,7 @@ def test_decode_tiny_fp32_layer(lib):
     pk = torch.zeros((1, 1, 64, 64), device=DEV)
     pv = torch.zeros_like(pk)
     lib.pool_blocks(L["k"], L["z"], L["bias"], m, 0, n_p, pk, v=L["v"], out_v=pv)
-    q = L["q"][:, 0].contiguous()
+    q = L["q"][:, 0]
     pos = torch.tensor([t], device=DEV)
     for sink in (None, torch.tensor([0.3, -1.1], device=DEV)):
         o, lse = lib.attend_decode(q, pk, L["k"], pos, m, W, O.EXCLUSIVE, pooled_v=pv, raw_v=L["v"],
@@ -501,7 +501,7 @@ def test_prefill_chunked_bf16(lib, chunk):
         if need > done:
             lib.pool_blocks(L["k"], L["z"], L["bias"], m, done, need, pk, v=L["v"], out_v=pv)
             done = need
-        lib.attend_prefill(L["q"][:, c0:c1].contiguous(), c0, pk, L["k"], 0, m, W, O.EXCLUSIVE,
+        lib.attend_prefill(L["q"][:, c0:c1], c0, pk, L["k"], 0, m, W, O.EXCLUSIVE,
                            out=out[:, c0:c1], lse=lse[:, c0:c1], pooled_v=pv, raw_v=L["v"])
     ro, rl = O.prefill_chunked(host(L["q"]), host(L["k"]), host(L["v"]), host(L["z"]), host(L["bias"]),
                                m, W, 400, 1 / math.sqrt(d))
@@ -520,7 +520,7 @@ def test_prefill_tiny_chunks(lib, q0, q_len):
     pv = torch.zeros_like(pk)
     if need > 0:
         lib.pool_blocks(L["k"], L["z"], L["bias"], m, 0, need, pk, v=L["v"], out_v=pv)
-    q = L["q"][:, q0:q0 + q_len].contiguous()
+    q = L["q"][:, q0:q0 + q_len]
     o, lse = lib.attend_prefill(q, q0, pk, L["k"], 0, m, W, O.EXCLUSIVE, pooled_v=pv, raw_v=L["v"],
                                 out_dtype=torch.float32)
     rpk, rpv = O.pool_single(host(L["k"]), host(L["z"]), host(L["bias"]), m, 0, T // m, values=host(L["v"]))
