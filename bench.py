@@ -641,9 +641,10 @@ PJ_T, PJ_H, PJ_C, PJ_DC, PJ_HI, PJ_DI, PJ_G, PJ_DG, PJ_DM = 4096, 64, 512, 1024,
 
 
 def run_projections(reps):
-    """Low-rank indexer queries (d_c = 1024 -> 8 x 64) and the grouped output
-    projection (64 heads x 512 in 8 groups to 1024 each, then to 4096) of 4096
-    tokens, as three lbca_grouped_gemm launches captured in one graph."""
+    """Low-rank indexer queries (d_c = 1024 -> 8 x 64), the grouped output
+    projection (64 heads x 512 in 8 groups to 1024 each, then to 4096) and the
+    pooling logits of CSA's two series (4096 -> 2 x 512, fp32) of 4096 tokens,
+    each lbca_grouped_gemm launch captured in a graph of its own."""
     dev = "cuda"
     sd = lambda n: synth.seed_of("bench-proj", n)
     cq = synth.normal((PJ_T, PJ_DC), sd("cq"), dtype="bf16", device=dev)
@@ -662,9 +663,14 @@ def run_projections(reps):
                           2 * PJ_T * PJ_H * PJ_C * PJ_DG),
         "output_model": (lambda: lbca.grouped_gemm(mid, wo, out=y), 2 * PJ_T * PJ_G * PJ_DG * PJ_DM),
     }
+    h = synth.normal((PJ_T, PJ_DM), sd("h"), dtype="bf16", device=dev)
+    wz = synth.normal((2 * PJ_C, PJ_DM), sd("wz"), std=PJ_DM ** -0.5, dtype="bf16", device=dev)
+    z = torch.empty((PJ_T, 2 * PJ_C), dtype=torch.float32, device=dev)
+    parts["pooling_logits"] = (lambda: lbca.grouped_gemm(h, wz, out=z), 2 * PJ_T * PJ_DM * 2 * PJ_C)
     res = {"workload": f"{PJ_T} tokens: indexer queries {PJ_DC} -> {PJ_HI} x {PJ_DI}; output projection "
                        f"{PJ_H} heads x {PJ_C} in {PJ_G} groups -> {PJ_G} x {PJ_DG} -> {PJ_DM} "
-                       f"(fp32 attention output rounded to bf16 on load)"}
+                       f"(fp32 attention output rounded to bf16 on load); pooling logits of two series "
+                       f"{PJ_DM} -> 2 x {PJ_C} (fp32)"}
     tot_ms, tot_fl = 0.0, 0
     for name, (fn, fl) in parts.items():
         g = capture(fn)

@@ -106,6 +106,13 @@ __device__ __forceinline__ int64_t uniform_value(EarlyI64 e) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// a % b for a >= 0, b > 0, in 32-bit arithmetic when both fit (the 64-bit
+// remainder is a long instruction sequence).
+__device__ __forceinline__ int64_t mod_nonneg(int64_t a, int64_t b) {
+  if (((uint64_t)a | (uint64_t)b) < (uint64_t(1) << 32)) return (int64_t)((uint32_t)a % (uint32_t)b);
+  return a % b;
+}
+
 struct SeqView {
   int64_t t, raw_begin, raw_row0;
   int n_pooled, n_sel, n_raw;
@@ -134,7 +141,7 @@ __device__ __forceinline__ SeqView seq_view(const DecodeParams& p, int64_t b) {
   if (p.ring > 0 && t >= 0) {  // fused cache step: the base it writes for t
     int64_t np, rb;
     visible_range(t, p.m, p.W, p.mode, &np, &rb);
-    base = rb - rb % p.ring;
+    base = rb - mod_nonneg(rb, p.ring);
   }
   return seq_view(p, b, t, base);
 }

@@ -793,6 +793,15 @@ def indexer_queries(c_q, w_uq, heads, out=None, stream=None):
     return res.reshape(*lead, heads, w_uq.shape[0] // heads)
 
 
+def pooling_logits(h, w_z, dim, out=None, stream=None):
+    """Pooling logits of the series: h [..., d_model] (fp32 or bf16), w_z [series * dim,
+    d_model] bf16 (series stacked) -> fp32 [..., series, dim] (one grouped_gemm call)."""
+    lead = h.shape[:-1]
+    flat = h.reshape(-1, h.shape[-1])
+    z = grouped_gemm(flat, w_z, out=out, out_dtype=torch.float32, stream=stream)
+    return z.reshape(*lead, w_z.shape[0] // dim, dim)
+
+
 def output_projection(o, w_groups, w_out, mid=None, out=None, out_dtype=torch.float32, stream=None):
     """Grouped output projection: o [T, H, c] (fp32 or bf16, heads consecutive),
     w_groups [g, d_g, (H/g) * c] bf16, w_out [d_model, g * d_g] bf16 -> [T, d_model]

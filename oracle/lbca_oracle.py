@@ -587,6 +587,10 @@ def csa_sparse_prefill(qi, w, ki, q, entries, raw, raw_pos_base, q_pos0, m, W, k
 #   * low-rank indexer queries: q^I_t = W^IUQ c^Q_t, where c^Q_t is the query's
 #     low-rank latent (d_c dims) and W^IUQ maps it to all indexer heads at once
 #     ([heads * head_dim, d_c]); the result is split into heads;
+#   * pooling logits: the content-dependent pooling weights of a series
+#     ([CSA] "What is implemented", first item: Z^a, Z^b beside C^a, C^b; [HCA]
+#     the same for its single series) are a linear map of the token's hidden
+#     state, z_t = W^Z h_t, one row of logits per pooled channel;
 #   * grouped output projection: the attention output of a token (all query
 #     heads concatenated) is cut into g groups of consecutive heads; group i is
 #     projected by its own matrix W_i to an intermediate width, the g results are
@@ -614,6 +618,13 @@ def indexer_queries(c_q, w_uq, heads):
     [..., heads, d_I]."""
     q = _f64(c_q) @ _f64(w_uq).T
     return q.reshape(q.shape[:-1] + (heads, q.shape[-1] // heads))
+
+
+def pooling_logits(h, w_z, dim):
+    """Pooling logits of hidden states h [..., d_model]: w_z [series * dim,
+    d_model] (series stacked, e.g. Z^a then Z^b) -> [..., series, dim]."""
+    z = _f64(h) @ _f64(w_z).T
+    return z.reshape(z.shape[:-1] + (z.shape[-1] // dim, dim))
 
 
 def output_projection(o, w_groups, w_out):

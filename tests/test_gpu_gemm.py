@@ -94,3 +94,11 @@ def test_projections_csa_shapes(lib):
     # stage 1 itself within its bound
     mid_gpu = lib.grouped_gemm(o.reshape(T, -1), wg, groups=g)
     _check(host(mid_gpu)[rows], o_used, host(wg), mid, True, "output projection stage 1")
+    # pooling logits of CSA's two series (Z^a, Z^b: 512 channels each) from the hidden state
+    h = synth.normal((T, dm), seed("h"), dtype="bf16", device=DEV)
+    wz = synth.normal((2 * c, dm), seed("wz"), std=dm ** -0.5, dtype="bf16", device=DEV)
+    z = lib.pooling_logits(h, wz, c)
+    torch.cuda.synchronize()
+    assert z.shape == (T, 2, c) and z.dtype == torch.float32
+    rz = O.pooling_logits(host(h), host(wz), c)
+    _check(host(z).reshape(T, -1), host(h), host(wz)[None], rz.reshape(T, -1), False, "pooling logits")

@@ -69,3 +69,22 @@ def test_indexer_queries_split_into_heads():
     assert q.shape == (2, 5, HI, dI)
     for h in range(HI):
         np.testing.assert_allclose(q[:, :, h], c @ w[h * dI:(h + 1) * dI].T, atol=1e-12)
+
+
+def test_pooling_logits_closed_forms():
+    # a one-hot hidden state returns one column of W^Z, split into the series;
+    # a stacked pair of maps is the pair of single maps
+    dm, dim = 10, 4
+    w = rng.standard_normal((2 * dim, dm))
+    h = np.zeros((3, dm))
+    for i, c in enumerate((0, 4, 9)):
+        h[i, c] = 1.0
+    z = O.pooling_logits(h, w, dim)
+    assert z.shape == (3, 2, dim)
+    for i, c in enumerate((0, 4, 9)):
+        np.testing.assert_array_equal(z[i, 0], w[:dim, c])
+        np.testing.assert_array_equal(z[i, 1], w[dim:, c])
+    h2 = rng.standard_normal((5, dm))
+    za = O.pooling_logits(h2, w[:dim], dim)[:, 0]
+    zb = O.pooling_logits(h2, w[dim:], dim)[:, 0]
+    np.testing.assert_allclose(O.pooling_logits(h2, w, dim), np.stack([za, zb], axis=1), atol=1e-12)
