@@ -227,6 +227,7 @@ __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, 
   __shared__ float s_ml[NW][16][2];
   __shared__ float s_w[NW][16];
   __shared__ float s_M[16], s_L[16], s_inv[16], s_lse[16];
+  __shared__ float s_sink[16];  // sink logits of the head slots (the one-barrier merge)
   __shared__ double s_freq[RD > 0 ? RD / 2 : 1];  // RoPE turns per position, pair k
   __shared__ int s_ids[SPEC ? 1 : kSelLds];        // selected ids of this workgroup's range
 
@@ -590,38 +591,114 @@ __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, 
   l_run = xor32_sum(l_run);
 
   // ---- merge the NW waves (fixed order) ----
-  if (kq == 0) {
-    s_ml[wave][n][0] = m_run;
-    s_ml[wave][n][1] = l_run;
-  }
-  __syncthreads();  // every wave is done with its stage: the LDS is free
-  if (tid < 16) {
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][tid][0]);
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float sw = s_ml[w][tid][0] == kNegInf ? 0.f : fast_exp2(s_ml[w][tid][0] - M);
-      s_w[w][tid] = sw;
-      L = fmaf(s_ml[w][tid][1], sw, L);
-    }
-    s_M[tid] = M;
-    s_L[tid] = L;
-  }
-  __syncthreads();
   float* buf = reinterpret_cast<float*>(lds);
-  if constexpr (PAR_MERGE) {  // every wave writes its scaled acc to its own slice
+  if constexpr (PAR_MERGE) {
+    // the sink logits of the head slots (requested now: the loads overlap the
+    // barrier's wait)
+    const float sink_r = p.sink && wave == 0 && kq == 0 ? p.sink[head0 + (head_ok ? n : 0)] : 0.f;
+    // Every wave leaves its (max, sum) and its unscaled acc in its own stage
+    // (a wave's LDS operations complete in order, so its last reads of the
+    // stage are done), one barrier publishes them, and each output thread
+    // forms the wave weights of its slot itself.
+    if (kq == 0) {
+      s_ml[wave][n][0] = m_run;
+      s_ml[wave][n][1] = l_run;
+      if (wave == 0) s_sink[n] = sink_r;
+    }
     if (head_ok) {
-      const float sw = s_w[wave][n];
-      float* dst = buf + (wave * 16 + n) * DV + 4 * kq;
+      float* dst = reinterpret_cast<float*>(vt) + n * DV + 4 * kq;
 #pragma unroll
       for (int t = 0; t < DT; ++t)
-        *reinterpret_cast<float4*>(dst + 16 * t) =
-            make_float4(acc[t][0] * sw, acc[t][1] * sw, acc[t][2] * sw, acc[t][3] * sw);
+        *reinterpret_cast<float4*>(dst + 16 * t) = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
     }
     __syncthreads();
-  } else {  // accumulate into one buffer, wave after wave
+    // weights exp2(m_w - M) of the waves for slot sl, M and L = sum_w l_w sw_w
+    auto weights = [&](int sl, float (&sw)[NW], float& M, float& L) __attribute__((always_inline)) {
+      M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][sl][0]);
+      L = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        sw[w] = s_ml[w][sl][0] == kNegInf ? 0.f : fast_exp2(s_ml[w][sl][0] - M);
+        L = fmaf(s_ml[w][sl][1], sw[w], L);
+      }
+    };
+    auto merged = [&](int sl, int dl, const float (&sw)[NW]) __attribute__((always_inline)) {
+      float o = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) o = fmaf(buf[w * (STAGE / 2) + sl * DV + dl], sw[w], o);
+      return o;
+    };
+    if (p.splits == 1) {
+      constexpr int r = RD, half = RD / 2;
+      const bool rot = RD > 0 && (int)dh == DS - 1;
+      const int per_slot = rot ? DV - half : DV;
+      const int items = nvalid * per_slot;
+      for (int i = tid; i < items; i += blockDim.x) {
+        const int sl = i / per_slot, dl = i % per_slot;
+        float sw[NW], M, L;
+        weights(sl, sw, M, L);
+        if (p.sink) L += exp2f(s_sink[sl] * kLog2e - M);
+        const float inv = 1.f / L;
+        const int d = dv0 + dl;
+        float* o = p.out + b * ST.o.s0 + (head0 + sl) * ST.o.s2;
+        if (!rot || d < D - r) {
+          o[d] = merged(sl, dl, sw) * inv;
+        } else if constexpr (RD > 0) {
+          const int k = d - (D - r);
+          const float x1 = merged(sl, dl, sw) * inv, x2 = merged(sl, dl + half, sw) * inv;
+          float c, sn;
+          rope_cos_sin_turns(-(double)sv.t * s_freq[k], &c, &sn);
+          o[d] = x1 * c - x2 * sn;
+          o[d + half] = x2 * c + x1 * sn;
+        }
+      }
+      if (p.lse && dh == 0 && tid < nvalid) {
+        float sw[NW], M, L;
+        weights(tid, sw, M, L);
+        if (p.sink) L += exp2f(s_sink[tid] * kLog2e - M);
+        p.lse[b * p.hq + head0 + tid] = (M + log2f(L)) * 0.69314718055994531f;
+      }
+      return own_row;
+    }
+    // split partial to the workspace; decode_merge_kernel combines the splits
+    const int64_t part = (int64_t)unit * p.splits + split;
+    for (int i = tid; i < nvalid * DV; i += blockDim.x) {
+      float sw[NW], M, L;
+      weights(i / DV, sw, M, L);
+      p.ws_acc[(part * 16 + i / DV) * D + dv0 + i % DV] = merged(i / DV, i % DV, sw);
+    }
+    if (dh == 0 && tid < nvalid) {
+      float sw[NW], M, L;
+      weights(tid, sw, M, L);
+      p.ws_ml[(part * 16 + tid) * 2] = M;
+      p.ws_ml[(part * 16 + tid) * 2 + 1] = L;
+    }
+    return own_row;
+  } else {
+    // the waves' acc summed into one buffer, wave after wave (the stages are
+    // too small for a slice per wave)
+    if (kq == 0) {
+      s_ml[wave][n][0] = m_run;
+      s_ml[wave][n][1] = l_run;
+    }
+    __syncthreads();  // every wave is done with its stage: the LDS is free
+    if (tid < 16) {
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][tid][0]);
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float sw = s_ml[w][tid][0] == kNegInf ? 0.f : fast_exp2(s_ml[w][tid][0] - M);
+        s_w[w][tid] = sw;
+        L = fmaf(s_ml[w][tid][1], sw, L);
+      }
+      s_M[tid] = M;
+      s_L[tid] = L;
+    }
+    __syncthreads();
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       if (wave == w && head_ok) {
@@ -639,59 +716,45 @@ __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, 
       }
       __syncthreads();
     }
-  }
-  auto merged = [&](int sl, int dl) {  // combined unnormalised acc of slot sl, local dim dl
-    if constexpr (PAR_MERGE) {
-      float o = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) o += buf[(w * 16 + sl) * DV + dl];
-      return o;
-    } else {
-      return buf[sl * DV + dl];
-    }
-  };
-
-  if (p.splits == 1) {
-    if (tid < nvalid) {
-      float L = s_L[tid];
-      const float M = s_M[tid];
-      if (p.sink) L += exp2f(p.sink[head0 + tid] * kLog2e - M);
-      s_inv[tid] = 1.f / L;
-      s_lse[tid] = (M + log2f(L)) * 0.69314718055994531f;
-    }
-    __syncthreads();
-    // local dims: plain ones, and for the slice holding the rotated dims one
-    // item per rotate-half pair (k, k + RD/2)
-    constexpr int r = RD, half = RD / 2;
-    const bool rot = RD > 0 && (int)dh == DS - 1;
-    const int per_slot = rot ? DV - half : DV;
-    const int items = nvalid * per_slot;
-    for (int i = tid; i < items; i += blockDim.x) {
-      const int sl = i / per_slot, dl = i % per_slot;
-      const int d = dv0 + dl;
-      float* o = p.out + b * ST.o.s0 + (head0 + sl) * ST.o.s2;
-      const float inv = s_inv[sl];
-      if (!rot || d < D - r) {
-        o[d] = merged(sl, dl) * inv;
-      } else if constexpr (RD > 0) {
-        const int k = d - (D - r);
-        const float x1 = merged(sl, dl) * inv, x2 = merged(sl, dl + half) * inv;
-        float c, sn;
-        rope_cos_sin_turns(-(double)sv.t * s_freq[k], &c, &sn);
-        o[d] = x1 * c - x2 * sn;
-        o[d + half] = x2 * c + x1 * sn;
+    if (p.splits == 1) {
+      if (tid < nvalid) {
+        float L = s_L[tid];
+        const float M = s_M[tid];
+        if (p.sink) L += exp2f(p.sink[head0 + tid] * kLog2e - M);
+        s_inv[tid] = 1.f / L;
+        s_lse[tid] = (M + log2f(L)) * 0.69314718055994531f;
       }
+      __syncthreads();
+      constexpr int r = RD, half = RD / 2;
+      const bool rot = RD > 0 && (int)dh == DS - 1;
+      const int per_slot = rot ? DV - half : DV;
+      const int items = nvalid * per_slot;
+      for (int i = tid; i < items; i += blockDim.x) {
+        const int sl = i / per_slot, dl = i % per_slot;
+        const int d = dv0 + dl;
+        float* o = p.out + b * ST.o.s0 + (head0 + sl) * ST.o.s2;
+        const float inv = s_inv[sl];
+        if (!rot || d < D - r) {
+          o[d] = buf[sl * DV + dl] * inv;
+        } else if constexpr (RD > 0) {
+          const int k = d - (D - r);
+          const float x1 = buf[sl * DV + dl] * inv, x2 = buf[sl * DV + dl + half] * inv;
+          float c, sn;
+          rope_cos_sin_turns(-(double)sv.t * s_freq[k], &c, &sn);
+          o[d] = x1 * c - x2 * sn;
+          o[d + half] = x2 * c + x1 * sn;
+        }
+      }
+      if (p.lse && dh == 0 && tid < nvalid) p.lse[b * p.hq + head0 + tid] = s_lse[tid];
+      return own_row;
     }
-    if (p.lse && dh == 0 && tid < nvalid) p.lse[b * p.hq + head0 + tid] = s_lse[tid];
-    return own_row;
-  }
-  // ---- split partial to the workspace; decode_merge_kernel combines the splits ----
-  const int64_t part = (int64_t)unit * p.splits + split;
-  for (int i = tid; i < nvalid * DV; i += blockDim.x)
-    p.ws_acc[(part * 16 + i / DV) * D + dv0 + i % DV] = merged(i / DV, i % DV);
-  if (dh == 0 && tid < nvalid) {
-    p.ws_ml[(part * 16 + tid) * 2] = s_M[tid];
-    p.ws_ml[(part * 16 + tid) * 2 + 1] = s_L[tid];
+    const int64_t part = (int64_t)unit * p.splits + split;
+    for (int i = tid; i < nvalid * DV; i += blockDim.x)
+      p.ws_acc[(part * 16 + i / DV) * D + dv0 + i % DV] = buf[(i / DV) * DV + i % DV];
+    if (dh == 0 && tid < nvalid) {
+      p.ws_ml[(part * 16 + tid) * 2] = s_M[tid];
+      p.ws_ml[(part * 16 + tid) * 2 + 1] = s_L[tid];
+    }
   }
   return own_row;
 }
