@@ -930,8 +930,10 @@ static int waves_per_wg(int64_t dim) { return dim <= 128 ? 8 : 4; }
 // workgroups per (sequence, KV head) along the row list.  Enough splits to
 // give about LBCA_WIDE_TARGET_WGS row ranges (one CU streams only about
 // 40 GB/s), but at least LBCA_WIDE_MIN_TILES 32-row tiles per range (a
-// split's bf16 partial, 32 KB per head block, stays below the rows it reads),
-// and enough that each range's selected ids fit the LDS stage.  With 64 query
+// split's bf16 partial, 32 KB per head block, stays at most the rows it
+// reads; with few rows, as in a CSA step over its selection, one tile per
+// range measured 16.9 against 18.8 us for two), and enough that each range's
+// selected ids fit the LDS stage.  With 64 query
 // heads each range is worked by two 4-wave "twin" workgroups, one per 32-head
 // block (LBCA_WIDE_TWINS), rather than one 8-wave workgroup for both.
 #ifndef LBCA_WIDE_TWINS
@@ -941,7 +943,7 @@ static int waves_per_wg(int64_t dim) { return dim <= 128 ? 8 : 4; }
 #define LBCA_WIDE_TARGET_WGS 128
 #endif
 #ifndef LBCA_WIDE_MIN_TILES
-#define LBCA_WIDE_MIN_TILES 2
+#define LBCA_WIDE_MIN_TILES 1
 #endif
 constexpr int kWideSelLds = 1024;  // matches the wide kernel's id stage
 

@@ -349,7 +349,26 @@ __global__ __launch_bounds__(1024) void topk_kernel(IndexParams p) {
   }
 
   uint32_t key[KPT];
-  if constexpr (STAGE > 0) {
+  int32_t cidr[MODE == 2 ? KPT : 1];  // second stage: the candidates' entry ids, requested with their keys
+  // Up to 8 keys per thread go straight to registers while the first pass's
+  // histogram is cleared; more are staged through the LDS in 16-byte copies.
+  constexpr bool DIRECT = KPT <= 8;
+  if constexpr (DIRECT) {
+    uint32_t rk[KPT];
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const int i = r * 1024 + tid;
+      const int j = i < nv ? i : 0;  // a clamped index: every thread issues every load
+      rk[r] = MODE == 2 ? ck[j] : __float_as_uint(sc[j]);
+      if constexpr (MODE == 2) cidr[r] = cid[j];
+    }
+    for (int i = tid; i < 4096; i += 1024) *reinterpret_cast<int4*>(&hist[4 * i]) = make_int4(0, 0, 0, 0);
+    if (tid == 0) s_nc = 0;
+#pragma unroll
+    for (int r = 0; r < KPT; ++r)
+      key[r] = r * 1024 + tid < nv ? (MODE == 2 ? rk[r] : order_key(__uint_as_float(rk[r]))) : 0u;
+    __syncthreads();  // histogram cleared
+  } else if constexpr (STAGE > 0) {
     // 16-byte copies of the visible scores to LDS (lane i of a wave writes
     // bytes 16 i of the wave's 1 KB), the last nv % 4 scores one by one
     // (MODE 2: the candidates' keys, 4 bytes each as well)
@@ -362,6 +381,13 @@ __global__ __launch_bounds__(1024) void topk_kernel(IndexParams p) {
                                          (lds_void*)(stage + 4 * c0), 16, 0, 0);
     }
     if (tid < nv - 4 * nc) stage[4 * nc + tid] = src[4 * nc + tid];
+    if constexpr (MODE == 2) {
+#pragma unroll
+      for (int r = 0; r < KPT; ++r) {
+        const int i = r * 1024 + tid;
+        cidr[r] = cid[i < nv ? i : 0];
+      }
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies landed
     __syncthreads();
 #pragma unroll
@@ -375,6 +401,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(IndexParams p) {
     for (int r = 0; r < KPT; ++r) {
       const int i = r * 1024 + tid;
       key[r] = i < nv ? (MODE == 2 ? ck[i] : order_key(sc[i])) : 0u;
+      if constexpr (MODE == 2) cidr[r] = cid[i < nv ? i : 0];
     }
   }
 
@@ -388,16 +415,19 @@ __global__ __launch_bounds__(1024) void topk_kernel(IndexParams p) {
     const int4 h = *reinterpret_cast<const int4*>(&hist[4 * bin]);
     return h.x + h.y + h.z + h.w;
   };
-#pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
+  // One block-wide radix pass over the keys still matching the digits chosen
+  // so far (from the compacted list when there is one).
+  auto block_pass = [&](int pass) __attribute__((always_inline)) {
     const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
     const int nb = pass == 0 ? 4096 : 1024;
-    for (int i = tid; i < nb; i += 1024) *reinterpret_cast<int4*>(&hist[4 * i]) = make_int4(0, 0, 0, 0);
-    __syncthreads();
+    if (!(DIRECT && pass == 0)) {  // (the direct load cleared the first histogram)
+      for (int i = tid; i < nb; i += 1024) *reinterpret_cast<int4*>(&hist[4 * i]) = make_int4(0, 0, 0, 0);
+      __syncthreads();
+    }
     // Keys past the visible entries are 0 and every visible key is at least
     // 2^23 (order image of a finite float), so they fall in bin 0 of the first
     // pass (never the chosen one) and never match a later prefix.
-    if (pass > 0 && n_cand >= 0) {  // the chosen first-pass bin's keys, compacted
+    if (pass > 0 && n_cand >= 0) {
       for (int c = tid; c < n_cand; c += 1024) {
         const uint32_t k = cand[c];
         if ((k & pmask) == prefix) atomicAdd(&hist[4 * ((k >> shift) & (uint32_t)(nb - 1)) + (lane & 3)], 1);
@@ -423,43 +453,89 @@ __global__ __launch_bounds__(1024) void topk_kernel(IndexParams p) {
       int l16 = 0;
 #pragma unroll
       for (int j = 0; j < 16; ++j) l16 += s_part[16 * lane + j];
-      int base;
-      const int L = wave_crossing(l16, remaining, 0, &base);  // lane holding the crossing
+      int bs;
+      const int L = wave_crossing(l16, remaining, 0, &bs);  // lane holding the crossing
       const int tv = lane < 16 ? s_part[16 * L + lane] : 0;
-      const int J = wave_crossing(tv, remaining, base, &base);
+      const int J = wave_crossing(tv, remaining, bs, &bs);
       const int t = 16 * L + J;
       const int bv = lane < per ? count(nb - 1 - t * per - lane) : 0;
-      const int jb = wave_crossing(bv, remaining, base, &base);
+      const int jb = wave_crossing(bv, remaining, bs, &bs);
       if (lane == 0) {
         s_pick[0] = nb - 1 - t * per - jb;
-        s_pick[1] = remaining - base;
+        s_pick[1] = remaining - bs;
       }
     }
     __syncthreads();
     prefix |= (uint32_t)s_pick[0] << shift;
     pmask |= (uint32_t)(nb - 1) << shift;
     remaining = s_pick[1];
-    if (pass == 0) {  // compact the chosen bin's keys (if they fit) for the later passes
-      const int nbin = count(s_pick[0]);
-      __syncthreads();  // every wave has read the count; the list may overwrite LDS past the histogram
-      if (nbin <= kCandMax) {
+  };
+
+  block_pass(0);
+  {  // compact the chosen bin's keys (if they fit) for the later passes
+    const int nbin = count(s_pick[0]);
+    __syncthreads();  // every wave has read the count; the list may overwrite LDS past the histogram
+    if (nbin <= kCandMax) {
+      if constexpr (!DIRECT) {
         if (tid == 0) s_nc = 0;
         __syncthreads();
-        // one LDS atomic per wave: lane offsets from a scan of per-thread counts
-        int mine = 0;
+      }
+      // one LDS atomic per wave: lane offsets from a scan of per-thread counts
+      int mine = 0;
 #pragma unroll
-        for (int r = 0; r < KPT; ++r) mine += (key[r] & pmask) == prefix;
-        const int incl = wave_incl_scan(mine);
-        int base = 0;
-        if (lane == 63) base = atomicAdd(&s_nc, incl);
-        int at = __builtin_amdgcn_readlane(base, 63) + incl - mine;
+      for (int r = 0; r < KPT; ++r) mine += (key[r] & pmask) == prefix;
+      const int incl = wave_incl_scan(mine);
+      int wb = 0;
+      if (lane == 63) wb = atomicAdd(&s_nc, incl);
+      int at = __builtin_amdgcn_readlane(wb, 63) + incl - mine;
 #pragma unroll
-        for (int r = 0; r < KPT; ++r)
-          if ((key[r] & pmask) == prefix) cand[at++] = key[r];
-        __syncthreads();
-        n_cand = s_nc;
+      for (int r = 0; r < KPT; ++r)
+        if ((key[r] & pmask) == prefix) cand[at++] = key[r];
+      __syncthreads();
+      n_cand = s_nc;
+    }
+  }
+  if (n_cand >= 0) {
+    // The two 10-bit passes over the compacted list in wave 0 alone (no
+    // workgroup barriers): a private 1024-bin histogram, lane L counting the
+    // descending bins 1023 - 16 L .. 1008 - 16 L.  A wave's LDS operations
+    // complete in order, so each clear, count and read sees the one before.
+    if (wave == 0) {
+#pragma unroll
+      for (int pass = 1; pass < 3; ++pass) {
+        const int shift = pass == 1 ? 10 : 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<int4*>(&hist[16 * lane + 4 * j]) = make_int4(0, 0, 0, 0);
+        for (int c = lane; c < n_cand; c += 64) {
+          const uint32_t k = cand[c];
+          if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 1023u], 1);
+        }
+        const int blk = 63 - lane;  // storage block of this lane's descending bins
+        int sum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int4 h = *reinterpret_cast<const int4*>(&hist[16 * blk + 4 * j]);
+          sum += (h.x + h.y) + (h.z + h.w);
+        }
+        int bs;
+        const int L = wave_crossing(sum, remaining, 0, &bs);
+        const int bv = lane < 16 ? hist[16 * (63 - L) + 15 - lane] : 0;
+        const int J = wave_crossing(bv, remaining, bs, &bs);
+        prefix |= (uint32_t)(16 * (63 - L) + 15 - J) << shift;
+        pmask |= 1023u << shift;
+        remaining -= bs;
+      }
+      if (lane == 0) {
+        s_pick[0] = (int)prefix;
+        s_pick[1] = remaining;
       }
     }
+    __syncthreads();
+    prefix = (uint32_t)s_pick[0];
+    remaining = s_pick[1];
+  } else {
+    block_pass(1);
+    block_pass(2);
   }
   const uint32_t thr = prefix;       // key of the k-th largest score
   const int need_eq = remaining;     // keys equal to it to take, lowest index first
@@ -516,7 +592,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(IndexParams p) {
         wk[slot] = key[r];
         wi[slot] = (int32_t)(base + i);
       } else {
-        oi[slot] = cid[i];
+        oi[slot] = cidr[r];
         if (os) os[slot] = key_score(key[r]);
       }
     }
