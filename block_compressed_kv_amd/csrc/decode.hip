@@ -210,9 +210,9 @@ __device__ __forceinline__ void load_tile(Tile<D, R, DS, SHARED>& T, const int* 
 // the raw row at the position is read from the new token's input and the raw
 // base follows from the position; the workgroup that owns split 0 of a
 // (sequence, KV head) also appends the token to the ring (cp): its rows are
-// requested first and stored once the position is known; it returns that
-// cache row (else -1) so the caller can pool a completed block after the
-// decode.
+// requested first and stored once the position is known; when the token
+// completes a block it returns that cache row (else -1), so the caller pools
+// the block after the decode.
 template <int D, int R, int NW, int DS, bool SHARED, int RD, bool TREAT, bool SPEC, bool FUSED, bool DN,
           typename TZ = float>
 __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, const CacheParams* cp = nullptr) {
@@ -374,6 +374,14 @@ __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, 
     base = p.rpb ? uniform_value(e_base) : 0;
   }
   const SeqView sv = seq_view(p, b, uniform_value(e_pos), base);
+  // fused step: the cache row is handed back only when the token completes a
+  // block that fits the pooled buffer (the caller then pools it), so the other
+  // steps end without the cache step reading the position again
+  int pool_row = -1;
+  if constexpr (FUSED) {
+    const int64_t x = sv.t + 1;
+    if (own_row >= 0 && sv.t >= 0 && x % cp->m == 0 && x / cp->m - 1 < cp->entries) pool_row = own_row;
+  }
   // Fused step: the token into both ring rows of its slot, and the raw base
   // (lbca_cache_append's rule), once the position is known.  (Stored after
   // the decode work instead, the stores lengthen the owner workgroups' tails:
@@ -406,7 +414,7 @@ __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, 
         p.out[b * ST.o.s0 + (head0 + i / DV) * ST.o.s2 + dv0 + i % DV] = __builtin_nanf("");
       if (p.lse && dh == 0 && tid < nvalid) p.lse[b * p.hq + head0 + tid] = __builtin_nanf("");
     }
-    return own_row;
+    return pool_row;
   }
   if constexpr (TREAT) {
     if constexpr (RD > 0) {
@@ -660,7 +668,7 @@ __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, 
         if (p.sink) L += exp2f(s_sink[tid] * kLog2e - M);
         p.lse[b * p.hq + head0 + tid] = (M + log2f(L)) * 0.69314718055994531f;
       }
-      return own_row;
+      return pool_row;
     }
     // split partial to the workspace; decode_merge_kernel combines the splits
     const int64_t part = (int64_t)unit * p.splits + split;
@@ -675,7 +683,7 @@ __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, 
       p.ws_ml[(part * 16 + tid) * 2] = M;
       p.ws_ml[(part * 16 + tid) * 2 + 1] = L;
     }
-    return own_row;
+    return pool_row;
   } else {
     // the waves' acc summed into one buffer, wave after wave (the stages are
     // too small for a slice per wave)
@@ -746,7 +754,7 @@ __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, 
         }
       }
       if (p.lse && dh == 0 && tid < nvalid) p.lse[b * p.hq + head0 + tid] = s_lse[tid];
-      return own_row;
+      return pool_row;
     }
     const int64_t part = (int64_t)unit * p.splits + split;
     for (int i = tid; i < nvalid * DV; i += blockDim.x)
@@ -756,7 +764,7 @@ __device__ __forceinline__ int decode_body(const DecodeParams& p, unsigned bid, 
       p.ws_ml[(part * 16 + tid) * 2 + 1] = s_L[tid];
     }
   }
-  return own_row;
+  return pool_row;
 }
 
 // Combine the splits of one unit (16 query-head slots) over one chunk of CK
