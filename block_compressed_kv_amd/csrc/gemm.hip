@@ -19,8 +19,8 @@
 // or N read zeros; an fp32 A is rounded to bf16 on the way) while the current
 // step's are multiplied from LDS, then stored into the other LDS buffer; one
 // barrier per step.  LDS rows hold their 16-byte chunks in swizzled order so
-// that each MFMA operand read (one chunk of 32 consecutive rows) hits distinct
-// banks.  Two workgroups fit on a CU (64 KB of LDS each).
+// that each MFMA operand read (one chunk of 32 consecutive rows, 16 lanes per
+// pass) hits distinct banks.  Two workgroups fit on a CU (64 KB of LDS each).
 #include "device_util.h"
 #include "lbca_internal.h"
 
@@ -46,9 +46,10 @@ __device__ __forceinline__ uint4 ldb(__amdgpu_buffer_rsrc_t r, uint32_t voff, in
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0));
 }
 // position of chunk x of LDS row r: a 128-byte row spans half the banks, so
-// rows of one parity share a bank half; the xor spreads 4 rows of a parity
-// over the 4 chunk slots an 8-lane read group needs
-__device__ __forceinline__ int gswz(int r, int x) { return x ^ ((r >> 1) & 3); }
+// rows of one parity share a bank half; a 16-byte read serves 16 lanes per
+// pass, 16 consecutive rows, so the xor spreads the 8 rows of each parity over
+// all 8 chunk slots
+__device__ __forceinline__ int gswz(int r, int x) { return x ^ ((r >> 1) & 7); }
 
 template <bool AF32, bool CF32>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {

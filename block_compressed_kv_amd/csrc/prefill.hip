@@ -73,12 +73,14 @@ __device__ __forceinline__ PreStr pre_strides(const PrefillParams& p) {
   }
 }
 
-// Chunk swizzle of an LDS tile row (16-byte chunks): 8 consecutive rows read at
-// one chunk index, or 4 consecutive rows read at two adjacent chunks, hit
-// distinct banks.  Unchanged when the row moves by 16.
+// Chunk swizzle of an LDS tile row (16-byte chunks).  A 16-byte read serves
+// 16 lanes per pass over the 64 banks, so at 128 dims (a row spans all 64
+// banks) 16 consecutive rows read at one chunk index, and 4 consecutive rows
+// read at 4 aligned chunks (the transposing V reads), must land on 16 distinct
+// chunk positions.  Unchanged when the row moves by 16.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return (2 * r) & 15;
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
   else return (2 * (r >> 1)) & 7;
 }
 
