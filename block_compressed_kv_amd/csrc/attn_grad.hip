@@ -331,6 +331,11 @@ __global__ __launch_bounds__(512, 1) void attn_grad_kernel(GradParams p, GradStr
       }
     }
     __syncthreads();
+    // The next tile into the other buffer (free since the last barrier) before
+    // this tile's dQ atomics: the store waits for the tile's loads, and
+    // vector-memory operations complete in order, so placed after the atomics
+    // it would wait for them too.
+    if (more) stash(it + 1, buf ^ 1);
 
     // dQ (rows x this wave's 32 dims) = dS K over its key range; K^T from LDS
     if (do_dq) {
@@ -356,7 +361,6 @@ __global__ __launch_bounds__(512, 1) void attn_grad_kernel(GradParams p, GradStr
         if (tp + r < t_end) unsafeAtomicAdd(dqrow + r * rstride, dqa[e]);
       }
     }
-    if (more) stash(it + 1, buf ^ 1);
     __syncthreads();
   }
 
