@@ -271,17 +271,20 @@ constexpr int kSliceLen = 4096;
 // Every thread keeps KPT scores (as order-preserving
 // 32-bit keys) of entries r * 1024 + tid in registers.  The k-th largest key is
 // found by a radix select over 12 + 10 + 10 bits: each pass counts the keys
-// that still match the digits chosen so far into an LDS histogram, and a
-// block-wide scan from the top bin finds the bin holding the k-th largest.
+// that still match the digits chosen so far into an LDS histogram, and a scan
+// from the top bin finds the bin holding the k-th largest.  The first pass is
+// workgroup-wide; the keys of its chosen bin are then compacted, and wave 0
+// alone runs the other two passes over that list (no workgroup barriers).
 // The selection then takes every key above it and the lowest-index keys equal
 // to it: each element's output slot is the number of selected elements before
 // it in index order, from per-(round, wave) counts scanned across the block.
 template <int KPT, int MODE>
 __global__ __launch_bounds__(1024) void topk_kernel(IndexParams p) {
   static_assert(MODE != 1 || KPT * 1024 == kSliceLen, "a first-stage workgroup holds one slice");
-  // LDS: first the scores (copied straight from global memory), then the
-  // histograms (4 interleaved copies per bin, so lanes of one wave that hit
-  // the same bin mostly hit different words)
+  // LDS: the scores when more than 8 per thread are staged there (copied
+  // straight from global memory), then the histograms (4 interleaved copies
+  // per bin in the workgroup-wide passes, so lanes of one wave that hit the
+  // same bin mostly hit different words)
   constexpr int STAGE = KPT <= 32 ? KPT * 1024 : 0;
   constexpr int LDS_WORDS = STAGE > 4096 * 5 ? STAGE : 4096 * 5;  // histogram + candidate list
   __shared__ __attribute__((aligned(16))) int lds_words[LDS_WORDS];
