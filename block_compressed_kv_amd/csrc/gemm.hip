@@ -21,6 +21,7 @@
 // barrier per step.  LDS rows hold their 16-byte chunks in swizzled order so
 // that each MFMA operand read (one chunk of 32 consecutive rows, 16 lanes per
 // pass) hits distinct banks.  Two workgroups fit on a CU (64 KB of LDS each).
+#include <type_traits>
 #include "device_util.h"
 #include "lbca_internal.h"
 
@@ -75,23 +76,16 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
   // staging: each thread moves 4 A chunks and 4 W chunks (8 bf16 each) per step;
   // chunk s of this thread: tile row (tid / 8) + 32 s, chunk tid % 8
   const int st_x = tid & 7, st_r = tid >> 3;
+  // bf16 A: the chunks are stored to the LDS as loaded; a chunk past K is
+  // zeroed in a branch that only the tail step takes.
   uint4 stg_a[4], stg_w[4];
-  auto fetch = [&](int64_t k0) __attribute__((always_inline)) {
+  auto fetch16 = [&](int64_t k0) __attribute__((always_inline)) {
     const bool tail = k0 + BK > p.k;
     const bool live = !tail || k0 + 8 * st_x < p.k;  // K is a multiple of 8
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int r = st_r + 32 * s;
-      if constexpr (AF32) {
-        const uint32_t off = (uint32_t)(((int64_t)r * p.lda + k0 + 8 * st_x) * 4);
-        const uint4 lo = ldb(ra, off, 0), hi = ldb(ra, off + 16, 0);
-        stg_a[s] = make_uint4(pack_bf16x2(__uint_as_float(lo.x), __uint_as_float(lo.y)),
-                              pack_bf16x2(__uint_as_float(lo.z), __uint_as_float(lo.w)),
-                              pack_bf16x2(__uint_as_float(hi.x), __uint_as_float(hi.y)),
-                              pack_bf16x2(__uint_as_float(hi.z), __uint_as_float(hi.w)));
-      } else {
-        stg_a[s] = ldb(ra, (uint32_t)(((int64_t)r * p.lda + k0 + 8 * st_x) * 2), 0);
-      }
+      stg_a[s] = ldb(ra, (uint32_t)(((int64_t)r * p.lda + k0 + 8 * st_x) * 2), 0);
       stg_w[s] = ldb(rw, (uint32_t)(((int64_t)r * p.ldw + k0 + 8 * st_x) * 2), 0);
       if (!live) {
         stg_a[s] = make_uint4(0, 0, 0, 0);
@@ -99,12 +93,65 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
       }
     }
   };
-  auto stash = [&](int buf) __attribute__((always_inline)) {
+  auto stash16 = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int r = st_r + 32 * s;
       *reinterpret_cast<uint4*>(&sa[buf][r * BK + 8 * gswz(r, st_x)]) = stg_a[s];
       *reinterpret_cast<uint4*>(&sw[buf][r * BK + 8 * gswz(r, st_x)]) = stg_w[s];
+    }
+  };
+  // fp32 A: the loaded words are kept until the stash, which rounds them to
+  // bf16 and, on the one step that runs past K (a uniform branch), zeroes the
+  // chunks beyond K, so every load of the next step stays in flight while this
+  // step's MFMAs run (rounding right after the load would wait for it there).
+  uint4 f32_lo[4], f32_hi[4], f32_w[4];
+  bool f32_tail = false;
+  uint32_t f32_keep = ~0u;  // all ones, or zero for a chunk past K
+  auto fetch32 = [&](int64_t k0) __attribute__((always_inline)) {
+    f32_tail = k0 + BK > p.k;
+    f32_keep = k0 + 8 * st_x < p.k ? ~0u : 0u;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int r = st_r + 32 * s;
+      const uint32_t off = (uint32_t)(((int64_t)r * p.lda + k0 + 8 * st_x) * 4);
+      f32_lo[s] = ldb(ra, off, 0);
+      f32_hi[s] = ldb(ra, off + 16, 0);
+      f32_w[s] = ldb(rw, (uint32_t)(((int64_t)r * p.ldw + k0 + 8 * st_x) * 2), 0);
+    }
+  };
+  auto stash32_as = [&](int buf, uint32_t m, auto masked) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int r = st_r + 32 * s;
+      const uint4 lo = f32_lo[s], hi = f32_hi[s];
+      uint4 a = make_uint4(pack_bf16x2(__uint_as_float(lo.x), __uint_as_float(lo.y)),
+                           pack_bf16x2(__uint_as_float(lo.z), __uint_as_float(lo.w)),
+                           pack_bf16x2(__uint_as_float(hi.x), __uint_as_float(hi.y)),
+                           pack_bf16x2(__uint_as_float(hi.z), __uint_as_float(hi.w)));
+      uint4 w = f32_w[s];
+      if constexpr (decltype(masked)::value) {
+        a = make_uint4(a.x & m, a.y & m, a.z & m, a.w & m);
+        w = make_uint4(w.x & m, w.y & m, w.z & m, w.w & m);
+      }
+      *reinterpret_cast<uint4*>(&sa[buf][r * BK + 8 * gswz(r, st_x)]) = a;
+      *reinterpret_cast<uint4*>(&sw[buf][r * BK + 8 * gswz(r, st_x)]) = w;
+    }
+  };
+  auto fetch = [&](int64_t k0) __attribute__((always_inline)) {
+    if constexpr (AF32)
+      fetch32(k0);
+    else
+      fetch16(k0);
+  };
+  auto stash = [&](int buf) __attribute__((always_inline)) {
+    if constexpr (AF32) {
+      if (f32_tail)
+        stash32_as(buf, f32_keep, std::true_type{});
+      else
+        stash32_as(buf, ~0u, std::false_type{});
+    } else {
+      stash16(buf);
     }
   };
 

@@ -33,6 +33,8 @@ def _check(got, a_used, w, ref, c_bf16, what):
     (3, 129, 130, 200, "f32", "bf16"),      # K tail (200 = 3 x 64 + 8), fp32 A rounded on load
     (2, 1, 257, 64, "bf16", "bf16"),        # one row
     (4, 513, 96, 1024, "f32", "f32"),
+    (2, 70, 140, 136, "bf16", "f32"),       # bf16 K tail (136 = 2 x 64 + 8)
+    (1, 65, 64, 40, "bf16", "bf16"),        # K below one step: the only step is the tail
 ])
 def test_grouped_gemm(lib, G, M, N, K, a_dt, c_dt):
     say(f"grouped gemm G={G} M={M} N={N} K={K} a={a_dt} c={c_dt}")
