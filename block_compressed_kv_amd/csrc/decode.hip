@@ -991,6 +991,12 @@ static DecodePlan plan_decode_wide(const lbca_decode_args& a, int64_t G) {
     if (s < need) s = need;
   }
   if (s < 1) s = 1;
+  // ranges hold ceil(tiles / s) tiles each; drop the splits that would get none
+  // (260 tiles over 32 splits leave three empty), so no workgroup writes an
+  // empty partial and the merge reads fewer.  The range size is unchanged, so
+  // the selected ids per range still fit.
+  const int64_t per = (tiles + s - 1) / s;
+  if (per > 0) s = (tiles + per - 1) / per;
   pl.splits = (int)s;
   if (s == 1) return pl;
   const size_t u = (size_t)(a.batch * a.kv_heads * pl.head_groups);

@@ -31,7 +31,7 @@ import torch
 from block_compressed_kv_amd import synth
 from oracle import lbca_oracle as O
 
-from parity_util import check_bf16, host, index_score_bound, say, topk_matches
+from parity_util import check_bf16, host, index_score_bound, index_ws_scores, say, topk_matches
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -182,19 +182,23 @@ def test_csa_decode_128k_batch2(lib):
     lib.pool_blocks(C["ca"], C["za"], C["bias_a"], m, 0, N, ent, xb=C["cb"], zb=C["zb"],
                      bias_b=C["bias_b"], **treat)
     pos = torch.full((B,), T - 1, dtype=torch.int64, device=DEV)
-    idx, _ = lib.csa_index_topk(C["qi"], C["w"], keys, pos, m, k)
+    ws = torch.empty(lib.index_workspace_bytes(C["qi"], C["w"], keys, pos, m, k), dtype=torch.uint8, device=DEV)
+    idx, _ = lib.csa_index_topk(C["qi"], C["w"], keys, pos, m, k, workspace=ws)
     o, lse = lib.attend_decode(C["q"], ent, C["ca"], pos, m, W, O.OVERLAP, sel_idx=idx, sink=C["sink"],
                                 **treat)
     torch.cuda.synchronize()
     gidx = _cpu(idx).numpy()
+    gs = index_ws_scores(ws, B, N)
     qi, w, kh = _cpu(C["qi"]), _cpu(C["w"]), _cpu(keys)
     sel = np.zeros((B, k), dtype=np.int64)
     for b in range(B):
         say(f"oracle indexer sequence {b}")
         s = O.index_scores(qi[b], w[b], kh[b], N)
-        margin, band = topk_matches(gidx[b], s, k, f"CSA top-k b={b}", index_score_bound(qi[b], w[b], kh[b], N))
-        say(f"top-512 of sequence {b}: margin {margin:.3e}" + (" (in the fp32 tie band: validity checked)"
-                                                              if band else " (set exact)"))
+        margin, band = topk_matches(gidx[b], s, k, f"CSA top-k b={b}", index_score_bound(qi[b], w[b], kh[b], N),
+                                    gpu_scores=gs[b])
+        say(f"top-512 of sequence {b}: margin {margin:.3e}" +
+            (" (in the fp32 tie band: exact against the kernel's own fp32 scores, which are within their bounds)"
+             if band else " (set exact)"))
         sel[b] = gidx[b] if band else O.topk_select(s, k)
     # oracle entries for the selected ids only (entry i: a-block i and b-block i-1)
     pooled = np.zeros((B, 1, N, d))
@@ -245,7 +249,8 @@ def test_csa_sparse_prefill_128k_chunk_batch2(lib):
             say(f"oracle: sequence {b} query {i} (t = {t})")
             s = O.index_scores(_cpu(C["qi"][b, i]), _cpu(C["w"][b, i]), kh[b], n_vis)
             _, band = topk_matches(gidx[b, i], s, k, f"sparse prefill top-k b={b} i={i}",
-                                   index_score_bound(_cpu(C["qi"][b, i]), _cpu(C["w"][b, i]), kh[b], n_vis))
+                                   index_score_bound(_cpu(C["qi"][b, i]), _cpu(C["w"][b, i]), kh[b], n_vis),
+                                   allow_band=True)
             if band:
                 say(f"sequence {b} query {i}: selection in the fp32 tie band (validity checked)")
             sel = gidx[b, i]

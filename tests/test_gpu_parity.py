@@ -14,7 +14,7 @@ import torch
 from block_compressed_kv_amd import synth
 from oracle import lbca_oracle as O
 
-from parity_util import check, check_bf16, check_f32_rows, host, index_score_bound, say, topk_matches
+from parity_util import check, check_bf16, check_f32_rows, host, index_score_bound, index_ws_scores, say, topk_matches
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -422,7 +422,7 @@ def test_decode_merge_64_splits(lib, path):
                                  1 / math.sqrt(d), raw_pos_base=[rb])
     else:
         Hq, d, m, W = 64, 512, 4, 128
-        T = 4 * 4200 + 3
+        T = 4 * 6016 + 3  # 188 + 4 tiles of 32 rows: 64 ranges of 3
         N = T // m
         H = _dev(synth.hca_layer("dec-64splits-mqa", 1, Hq, T, d, m))
         entries = torch.zeros((1, 1, N, d), dtype=torch.bfloat16, device=DEV)
@@ -562,13 +562,16 @@ def test_index_topk(lib, N, k, t_list):
     qi, keys = g("qi", (B, HI, dI)), g("k", (B, N, dI))
     w = synth.uniform((B, HI), synth.seed_of("idx", N, "w"), device=DEV)
     pos = torch.tensor(t_list, device=DEV)
-    idx, score = lib.csa_index_topk(qi, w, keys, pos, m, k)
+    ws = torch.empty(lib.index_workspace_bytes(qi, w, keys, pos, m, k), dtype=torch.uint8, device=DEV)
+    idx, score = lib.csa_index_topk(qi, w, keys, pos, m, k, workspace=ws)
     idx, score = idx.cpu().numpy(), score.cpu().numpy()
+    gs = index_ws_scores(ws, B, N)
     for b, t in enumerate(t_list):
         n_vis = min((t + 1) // m, N)
         s = O.index_scores(host(qi[b]), host(w[b]), host(keys[b]), n_vis)
         margin, band = topk_matches(idx[b], s, k, f"top-k seq {b}",
-                                    index_score_bound(host(qi[b]), host(w[b]), host(keys[b]), n_vis))
+                                    index_score_bound(host(qi[b]), host(w[b]), host(keys[b]), n_vis),
+                                    gpu_scores=gs[b, :n_vis] if n_vis > k else None)
         say(f"top-k seq {b}: n_vis={n_vis} k={k} margin={margin:.3e}" + (" in the fp32 tie band" if band else ""))
         sel = idx[b][idx[b] >= 0]
         np.testing.assert_allclose(score[b][:sel.size], s[sel], rtol=1e-5, atol=1e-5)
@@ -666,7 +669,8 @@ def test_csa_sparse_prefill(lib, B, Tq, p0, HI, dI, k, treated):
             t = p0 + i
             n_vis = min((t + 1) // m, N)
             band_rows += topk_matches(idx[b, i], O.index_scores(qi[b, i], w[b, i], ki[b], n_vis), k,
-                                      f"seq {b} query {i}", index_score_bound(qi[b, i], w[b, i], ki[b], n_vis))[1]
+                                      f"seq {b} query {i}", index_score_bound(qi[b, i], w[b, i], ki[b], n_vis),
+                                      allow_band=True)[1]
             # the attention over the GPU's (valid) selection
             oo, ll = O.attend_decode(q[b, i][None], pooled[b][None], None, raw[b][None], None, [t], m, W,
                                      O.OVERLAP, 1 / math.sqrt(d), raw_pos_base=[0], sel_idx=idx[b, i][None],
@@ -697,7 +701,7 @@ def test_csa_sparse_prefill_two_stage_selection(lib, Tq, N):
         t = p0 + i
         n_vis = min((t + 1) // m, N)
         topk_matches(idx[0, i], O.index_scores(qh[0, i], wh[0, i], kh[0], n_vis), k, f"query {i}",
-                     index_score_bound(qh[0, i], wh[0, i], kh[0], n_vis))
+                     index_score_bound(qh[0, i], wh[0, i], kh[0], n_vis), allow_band=True)
         oo, ll = O.attend_decode(host(q)[0, i][None], eh[0][None, None], None, rh[0][None, None], None, [t], m, W,
                                  O.OVERLAP, 1 / math.sqrt(d), raw_pos_base=[base], sel_idx=idx[0, i][None])
         ro[i], rl[i] = oo[0], ll[0]

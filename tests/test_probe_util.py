@@ -83,3 +83,31 @@ def test_codes_name_rows():
     ids = (digits * (8 ** np.arange(7))).sum(axis=1)
     assert (ids == np.arange(300000)).all()
     assert (c[:, 0] == 0).all() and (c[:, 8] == 1).all() and (c[:, 9] == 3).all() and (c[:, 10] == 5).all()
+
+
+def test_topk_tie_band_fails_unless_allowed():
+    """The selection check: a clear margin demands the exact set; a k-th/(k+1)-th
+    pair closer than its fp32 bounds fails unless the test opts in, and then only
+    a top-k of scores within the bounds passes."""
+    from parity_util import topk_matches
+    s = np.array([5.0, 1.0, 3.0, 2.0, 4.0])
+    err = np.full(5, 1e-3)
+    margin, band = topk_matches(np.array([0, 2, 4, -1]), s, 3, "clear", err)
+    assert not band and margin == pytest.approx(1.0)
+    with pytest.raises(AssertionError):
+        topk_matches(np.array([0, 3, 4]), s, 3, "wrong set", err)
+    s2 = np.array([5.0, 3.0004, 3.0, 2.0, 4.0])  # 2nd and 3rd of the top-3 within 2e-3
+    with pytest.raises(AssertionError, match="tie band"):
+        topk_matches(np.array([0, 1, 4]), s2, 3, "band", err)
+    _, band = topk_matches(np.array([0, 2, 4]), s2, 3, "band", err, allow_band=True)  # the other tie order
+    assert band
+    with pytest.raises(AssertionError):
+        topk_matches(np.array([0, 3, 4]), s2, 3, "band", err, allow_band=True)  # 2.0 is not within the bounds
+    # with the kernel's own fp32 scores the band case is exact: those scores within
+    # their bounds, and the set their top-k (ties to the lower index)
+    own = np.array([5.0, 2.9999, 3.0, 2.0, 4.0], dtype=np.float32)
+    assert topk_matches(np.array([0, 2, 4]), s2, 3, "band", err, gpu_scores=own)[1]
+    with pytest.raises(AssertionError, match="own fp32 scores"):
+        topk_matches(np.array([0, 1, 4]), s2, 3, "band", err, gpu_scores=own)
+    with pytest.raises(AssertionError, match="outside their fp32 bound"):
+        topk_matches(np.array([0, 2, 4]), s2, 3, "band", err, gpu_scores=own + np.float32(0.01))
