@@ -90,14 +90,17 @@ def test_llama_chunked_prefill_16k(lib):
     check_bf16(host(pk[:, :, :done]), rk, "pooled K")
     check_bf16(host(pv[:, :, :done]), rv, "pooled V")
     rng = np.random.default_rng(16384)
+    # the chunk and window edges plus 500 random positions (every query head of each)
     ts = sorted({0, 1, 127, 128, 2047, 2048, 4095, 8191, 8192 + 77, 14335, 14336, 16383,
-                 *rng.integers(0, T, 4).tolist()})
+                 *rng.integers(0, T, 500).tolist()})
+    say(f"oracle prefill at {len(ts)} query positions")
     q = _cpu(L["q"])
+    oh, lh = host(out), host(lse)
     for t in ts:
         ro, rl = O.attend_prefill(q[:, t:t + 1], t, rk, rv, ks, vs, 0, m, W, O.EXCLUSIVE,
                                   1 / math.sqrt(d))
-        check_bf16(host(out[:, t:t + 1]), ro, f"prefill out t={t}")
-        check_bf16(host(lse[:, t:t + 1]), rl, f"prefill lse t={t}")
+        check_bf16(oh[:, t:t + 1], ro, f"prefill out t={t}")
+        check_bf16(lh[:, t:t + 1], rl, f"prefill lse t={t}")
 
 
 def test_llama_attention_backward_16k(lib):
@@ -147,24 +150,24 @@ def test_hca_decode_1m_batch4(lib):
     o, lse = lib.attend_decode(H["q"], ent, H["c"], pos, m, W, O.OVERLAP, sink=H["sink"],
                                 rmsnorm_eps=EPS, rope_dims=RD, rope_base=BASE)
     torch.cuda.synchronize()
-    b = 2
-    say(f"oracle: stream sequence {b} ({N} blocks)")
     bias = _cpu(H["bias"])
-    parts = []
-    step = 1024
-    for j0 in range(0, N, step):
-        cs = _cpu(H["c"][b:b + 1, :, j0 * m:(j0 + step) * m])
-        zs = _cpu(H["z"][b:b + 1, :, j0 * m:(j0 + step) * m])
-        parts.append(O.pool_single(cs, zs, bias, m, 0, step))
-    pooled = np.concatenate(parts, axis=2)                       # [1, 1, N, d]
-    treated = O.rope(O.rmsnorm(pooled, EPS), np.arange(N) * m, RD, BASE)
-    check_bf16(host(ent[b:b + 1]), treated, "treated HCA entries")
-    raw = _cpu(H["c"][b:b + 1, :, T - W:])
-    ro, rl = O.attend_decode(_cpu(H["q"][b:b + 1]), pooled, None, raw, None, [T - 1], m, W, O.OVERLAP,
-                             1 / math.sqrt(d), raw_pos_base=[T - W], sink=_cpu(H["sink"]),
-                             rmsnorm_eps=EPS, rope_dims=RD, rope_base=BASE)
-    check_bf16(host(o[b:b + 1]), ro, "HCA decode out")
-    check_bf16(host(lse[b:b + 1]), rl, "HCA decode lse")
+    for b in range(B):  # every sequence, its history streamed through the oracle 1024 blocks at a time
+        say(f"oracle: stream sequence {b} ({N} blocks)")
+        parts = []
+        step = 1024
+        for j0 in range(0, N, step):
+            cs = _cpu(H["c"][b:b + 1, :, j0 * m:(j0 + step) * m])
+            zs = _cpu(H["z"][b:b + 1, :, j0 * m:(j0 + step) * m])
+            parts.append(O.pool_single(cs, zs, bias, m, 0, step))
+        pooled = np.concatenate(parts, axis=2)                       # [1, 1, N, d]
+        treated = O.rope(O.rmsnorm(pooled, EPS), np.arange(N) * m, RD, BASE)
+        check_bf16(host(ent[b:b + 1]), treated, f"treated HCA entries b={b}")
+        raw = _cpu(H["c"][b:b + 1, :, T - W:])
+        ro, rl = O.attend_decode(_cpu(H["q"][b:b + 1]), pooled, None, raw, None, [T - 1], m, W, O.OVERLAP,
+                                 1 / math.sqrt(d), raw_pos_base=[T - W], sink=_cpu(H["sink"]),
+                                 rmsnorm_eps=EPS, rope_dims=RD, rope_base=BASE)
+        check_bf16(host(o[b:b + 1]), ro, f"HCA decode out b={b}")
+        check_bf16(host(lse[b:b + 1]), rl, f"HCA decode lse b={b}")
 
 
 def test_csa_decode_128k_batch2(lib):
