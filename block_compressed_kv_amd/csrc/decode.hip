@@ -994,9 +994,19 @@ static DecodePlan plan_decode_wide(const lbca_decode_args& a, int64_t G) {
   // ranges hold ceil(tiles / s) tiles each; drop the splits that would get none
   // (260 tiles over 32 splits leave three empty), so no workgroup writes an
   // empty partial and the merge reads fewer.  The range size is unchanged, so
-  // the selected ids per range still fit.
+  // the selected ids per range still fit.  With treated rows and more than
+  // one tile per range (no selection) a raw tile counts twice (it is
+  // normalised and rotated in LDS first), and the ranges split that cost;
+  // decode_wide_kernel applies the same rule (wide_ranges).
   const int64_t per = (tiles + s - 1) / s;
-  if (per > 0) s = (tiles + per - 1) / per;
+  const bool treat = a.rmsnorm_eps >= 0.f || a.rope_dims > 0;
+  if (treat && !a.sel_idx && per >= 2) {
+    const int64_t tiles_r = (raw_max + 31) / 32;
+    const int64_t cost = tiles + tiles_r, pc = (cost + s - 1) / s;
+    s = (cost + pc - 1) / pc;
+  } else if (per > 0) {
+    s = (tiles + per - 1) / per;
+  }
   pl.splits = (int)s;
   if (s == 1) return pl;
   const size_t u = (size_t)(a.batch * a.kv_heads * pl.head_groups);

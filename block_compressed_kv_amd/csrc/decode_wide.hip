@@ -231,10 +231,21 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
   const int64_t raw_span = p.mode == 0 ? p.W + p.m - 1 : p.W;
   const int cap_raw = (int)(raw_span < p.raw_rows ? raw_span : p.raw_rows);
   const int tiles_p = (cap_sel + WTR - 1) / WTR;
-  const int tiles = tiles_p + (cap_raw + WTR - 1) / WTR;
-  const int per = (tiles + S - 1) / S;
-  const int t0 = split * per < tiles ? split * per : tiles;
-  const int t1 = t0 + per < tiles ? t0 + per : tiles;
+  const int tiles_r = (cap_raw + WTR - 1) / WTR;
+  const int tiles = tiles_p + tiles_r;
+  int t0, t1;
+  if (TREAT && !SEL && S < tiles) {
+    // ranges split a cost in which a raw tile (treated in LDS) counts twice;
+    // a range takes the tiles whose cost starts inside it
+    const int cost = tiles + tiles_r, pc = (cost + S - 1) / S;
+    const int c0 = split * pc < cost ? split * pc : cost, c1 = c0 + pc < cost ? c0 + pc : cost;
+    t0 = c0 <= tiles_p ? c0 : tiles_p + (c0 - tiles_p + 1) / 2;
+    t1 = c1 <= tiles_p ? c1 : tiles_p + (c1 - tiles_p + 1) / 2;
+  } else {
+    const int per = (tiles + S - 1) / S;
+    t0 = split * per < tiles ? split * per : tiles;
+    t1 = t0 + per < tiles ? t0 + per : tiles;
+  }
   const int r0 = t0 * WTR;  // first list position of the range
 
   if constexpr (!SEL) {

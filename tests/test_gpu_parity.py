@@ -422,7 +422,7 @@ def test_decode_merge_64_splits(lib, path):
                                  1 / math.sqrt(d), raw_pos_base=[rb])
     else:
         Hq, d, m, W = 64, 512, 4, 128
-        T = 4 * 6016 + 3  # 188 + 4 tiles of 32 rows: 64 ranges of 3
+        T = 4 * 5888 + 3  # 184 + 4 tiles of 32 rows, raw tiles counting twice: 64 ranges of cost 3
         N = T // m
         H = _dev(synth.hca_layer("dec-64splits-mqa", 1, Hq, T, d, m))
         entries = torch.zeros((1, 1, N, d), dtype=torch.bfloat16, device=DEV)
