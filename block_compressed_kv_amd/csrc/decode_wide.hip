@@ -236,11 +236,11 @@ __global__ __launch_bounds__(256 * HB) void decode_wide_kernel(DecodeParams p) {
   int t0, t1;
   if (TREAT && !SEL && S < tiles) {
     // ranges split a cost in which a raw tile (treated in LDS) counts twice;
-    // a range takes the tiles whose cost starts inside it
+    // a range takes the tiles whose cost ends inside it
     const int cost = tiles + tiles_r, pc = (cost + S - 1) / S;
     const int c0 = split * pc < cost ? split * pc : cost, c1 = c0 + pc < cost ? c0 + pc : cost;
-    t0 = c0 <= tiles_p ? c0 : tiles_p + (c0 - tiles_p + 1) / 2;
-    t1 = c1 <= tiles_p ? c1 : tiles_p + (c1 - tiles_p + 1) / 2;
+    t0 = c0 <= tiles_p ? c0 : tiles_p + (c0 - tiles_p) / 2;
+    t1 = c1 <= tiles_p ? c1 : tiles_p + (c1 - tiles_p) / 2;
   } else {
     const int per = (tiles + S - 1) / S;
     t0 = split * per < tiles ? split * per : tiles;
